@@ -1,0 +1,337 @@
+/*
+ * Grouped Query Experts (GQE) attention, forward (prefill) pass: the plain CPU oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct definition that the
+ * GPU library is checked against.  Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark may load it.  It shares no code, header or constant with the HIP
+ * library under sparse_moe_query_amd/, and nothing in the product path calls it.
+ *
+ * Sources (the web pages on GQE; cited by page title and section):
+ *  [R]  "GQE: Grouped Query Experts" repository README, sections "Algorithm Overview",
+ *       "Usage" and "Parameters" (the authors' own description).
+ *  [T]  "Grouped Query Experts: Mixture-of-Experts on GQA Self-Attention", gist.science
+ *       explainer, "Technical Summary" -> "Architecture and Routing", "Training and Loss".
+ *  [M]  "Grouped-query attention and mixture of experts" tutorial (cseroadmap), sections
+ *       "Multi-head, multi-query and grouped-query attention" and "Mixture of experts (MoE)"
+ *       (the moe_layer sketch and its tested properties).
+ *
+ * Arithmetic: every input arrives as double (the caller widens the fp32 or bf16-rounded
+ * values exactly); every dot product, softmax sum and output accumulation is done in
+ * double, in plain sequential loop order.  There is no blocking, no fusion and no
+ * reordering beyond the definition.  OpenMP only splits independent tokens.
+ *
+ * Notation (README "Parameters"): d = dim, N = num_query_experts, G = num_kv_heads,
+ * k = top_k, dh = head_dim; n = N/G experts per group; expert e belongs to group
+ * g = e / n with local index j = e % n (contiguous grouping, as in GQA where each
+ * group of query heads shares one KV head [M]).
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - top-k is taken on the logits (softmax is strictly monotone, so the selected set
+ *    is the one "softmax then top-k" gives); equal logits -> lower local index first;
+ *    rank order within the selection is descending logit, then ascending index.
+ *  - renormalised weights w = p_sel / sum(p_sel) over the k selected experts [T], [M].
+ *  - "hard concat": each selected expert's head output goes through its own d_h x d
+ *    slice of the output projection (MHA concat with unselected slots zero).
+ *  - "renormalised weighted-sum slot": one extra d_h slot per group with its own
+ *    projection W_oR[g], fed with sum_r w_r * o_r.
+ *  - weighted_concat: the selected expert's slot is scaled by its in-group softmax
+ *    probability p (not renormalised).
+ *  - the shared head (a flag, default on) attends to KV group shared_kv_group.
+ *  - attention scale 1/sqrt(dh); causal mask keeps keys s' <= s; no positional
+ *    encoding, no projection biases.
+ *  - aux loss (Switch style, [R] "Algorithm Overview", [T] "Training and Loss"):
+ *    f_e = count_e/(T k), P_e = mean_t p[t,e], L_g = n * sum_{e in g} f_e P_e,
+ *    aux = mean_g L_g; unscaled (the caller multiplies by 0.01, [R] "Usage").
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    int32_t dim;             /* d   */
+    int32_t num_query_experts; /* N */
+    int32_t num_kv_heads;    /* G   */
+    int32_t top_k;           /* k   */
+    int32_t head_dim;        /* dh  */
+    int32_t variant;         /* 0 gqe, 1 weighted_concat, 2 hard_concat */
+    int32_t shared_head;     /* 1 = one always-on shared query head */
+    int32_t shared_kv_group; /* KV group the shared head reads */
+} oracle_cfg;
+
+/* ---------------------------------------------------------------------------------
+ * Router, for one token: logits, in-group softmax, top-k, renormalised weights.
+ * [R] "Algorithm Overview": softmax over experts inside each GQA group, then top-k.
+ * [M] moe_layer: probs = softmax(x @ router_w); keep the best top_k; mix by
+ * renormalised router weights.
+ *   logits[e] = sum_i x[i] * Wr[i][e] + br[e]
+ *   p[e]      = exp(logits[e] - m_g) / sum_{j in g} exp(logits[j] - m_g)
+ *   idx[g][r] = r-th best expert of group g (global id), w[g][r] = p / sum_sel p
+ *   gap[g]    = logit of the k-th choice minus logit of the (k+1)-th (+inf if k = n)
+ * --------------------------------------------------------------------------------- */
+static void router_token(const oracle_cfg* c, const double* x, const double* Wr,
+                         const double* br, double* logits, double* p, int32_t* idx,
+                         double* w, double* gap)
+{
+    const int d = c->dim, N = c->num_query_experts, G = c->num_kv_heads, k = c->top_k;
+    const int n = N / G;
+    for (int e = 0; e < N; ++e) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += x[i] * Wr[(size_t)i * N + e];
+        logits[e] = acc + (br ? br[e] : 0.0);
+    }
+    for (int g = 0; g < G; ++g) {
+        const double* lg = logits + g * n;
+        double m = lg[0];
+        for (int j = 1; j < n; ++j) if (lg[j] > m) m = lg[j];
+        double den = 0.0;
+        for (int j = 0; j < n; ++j) den += exp(lg[j] - m);
+        for (int j = 0; j < n; ++j) p[g * n + j] = exp(lg[j] - m) / den;
+
+        /* top-k by repeated selection of the best remaining local index */
+        int taken[64];
+        for (int j = 0; j < n; ++j) taken[j] = 0;
+        int sel[64];
+        for (int r = 0; r < k; ++r) {
+            int best = -1;
+            for (int j = 0; j < n; ++j) {
+                if (taken[j]) continue;
+                if (best < 0 || lg[j] > lg[best]) best = j; /* strict: lower j wins ties */
+            }
+            taken[best] = 1;
+            sel[r] = best;
+        }
+        if (k < n) {
+            int next = -1;
+            for (int j = 0; j < n; ++j) {
+                if (taken[j]) continue;
+                if (next < 0 || lg[j] > lg[next]) next = j;
+            }
+            gap[g] = lg[sel[k - 1]] - lg[next];
+        } else {
+            gap[g] = INFINITY;
+        }
+        double psum = 0.0;
+        for (int r = 0; r < k; ++r) psum += p[g * n + sel[r]];
+        for (int r = 0; r < k; ++r) {
+            idx[g * k + r] = g * n + sel[r];
+            w[g * k + r] = p[g * n + sel[r]] / psum;
+        }
+    }
+}
+
+/* x: [T, d]; outputs per token: logits/p [T, N], idx/w [T, G, k], gap [T, G]. */
+int gqe_oracle_router(const oracle_cfg* c, int64_t T, const double* x, const double* Wr,
+                      const double* br, double* logits, double* p, int32_t* idx, double* w,
+                      double* gap)
+{
+    const int d = c->dim, N = c->num_query_experts, G = c->num_kv_heads, k = c->top_k;
+    if (N <= 0 || G <= 0 || N % G != 0 || k < 1 || k > N / G || N / G > 64) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        router_token(c, x + t * d, Wr, br, logits + t * N, p + t * N, idx + t * G * k,
+                     w + t * G * k, gap + t * G);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------
+ * Load-balancing statistics ([R] "Algorithm Overview": Switch-style auxiliary loss;
+ * [T] "Training and Loss": encourage even use of the experts within each group).
+ *   count_e = #tokens that selected e;  P_e = (1/T) sum_t p[t,e]
+ *   f_e = count_e / (T k);  L_g = n sum_{e in g} f_e P_e;  aux = (1/G) sum_g L_g
+ *   active_heads = G k + (shared head ? 1 : 0)   ([R] "Algorithm Overview": 9 of 16)
+ * --------------------------------------------------------------------------------- */
+int gqe_oracle_aux(const oracle_cfg* c, int64_t T, const double* p, const int32_t* idx,
+                   int64_t* counts, double* mean_prob, double* aux, int32_t* active_heads)
+{
+    const int N = c->num_query_experts, G = c->num_kv_heads, k = c->top_k;
+    const int n = N / G;
+    for (int e = 0; e < N; ++e) { counts[e] = 0; mean_prob[e] = 0.0; }
+    for (int64_t t = 0; t < T; ++t) {
+        for (int a = 0; a < G * k; ++a) counts[idx[t * G * k + a]] += 1;
+        for (int e = 0; e < N; ++e) mean_prob[e] += p[t * N + e];
+    }
+    for (int e = 0; e < N; ++e) mean_prob[e] /= (double)T;
+    double total = 0.0;
+    for (int g = 0; g < G; ++g) {
+        double Lg = 0.0;
+        for (int j = 0; j < n; ++j) {
+            const int e = g * n + j;
+            const double f = (double)counts[e] / ((double)T * (double)k);
+            Lg += f * mean_prob[e];
+        }
+        total += (double)n * Lg;
+    }
+    *aux = total / (double)G;
+    *active_heads = G * k + (c->shared_head ? 1 : 0);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------
+ * Dense KV path ([R] "Algorithm Overview": all KV heads remain dense and unchanged;
+ * [T] "Dense KV Path").  For every token and every group g:
+ *   K[t][g][:] = x[t] @ Wk[:, g dh:(g+1) dh],  V likewise.   Wk, Wv: [d, G dh]
+ * Output layout K, V: [T, G, dh].
+ * --------------------------------------------------------------------------------- */
+int gqe_oracle_kv(const oracle_cfg* c, int64_t T, const double* x, const double* Wk,
+                  const double* Wv, double* K, double* V)
+{
+    const int d = c->dim, G = c->num_kv_heads, dh = c->head_dim;
+    const int W = G * dh;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int col = 0; col < W; ++col) {
+            double ak = 0.0, av = 0.0;
+            for (int i = 0; i < d; ++i) {
+                ak += x[t * d + i] * Wk[(size_t)i * W + col];
+                av += x[t * d + i] * Wv[(size_t)i * W + col];
+            }
+            K[t * W + col] = ak;
+            V[t * W + col] = av;
+        }
+    }
+    return 0;
+}
+
+/* Causal softmax attention of one query row over keys 0..s of one sequence and one
+ * KV group (two passes: the maximum, then the exponential sums).
+ * Kseq/Vseq point at position 0 of the sequence; row stride between positions is
+ * G*dh, and the group's dh values start at offset g*dh. */
+static void attend(int s, int dh, int G, int g, const double* q, const double* Kseq,
+                   const double* Vseq, double* o)
+{
+    const double scale = 1.0 / sqrt((double)dh);
+    double m = -INFINITY;
+    for (int j = 0; j <= s; ++j) {
+        const double* kj = Kseq + (size_t)j * G * dh + (size_t)g * dh;
+        double sc = 0.0;
+        for (int i = 0; i < dh; ++i) sc += q[i] * kj[i];
+        sc *= scale;
+        if (sc > m) m = sc;
+    }
+    double den = 0.0;
+    for (int i = 0; i < dh; ++i) o[i] = 0.0;
+    for (int j = 0; j <= s; ++j) {
+        const double* kj = Kseq + (size_t)j * G * dh + (size_t)g * dh;
+        const double* vj = Vseq + (size_t)j * G * dh + (size_t)g * dh;
+        double sc = 0.0;
+        for (int i = 0; i < dh; ++i) sc += q[i] * kj[i];
+        sc *= scale;
+        const double a = exp(sc - m);
+        den += a;
+        for (int i = 0; i < dh; ++i) o[i] += a * vj[i];
+    }
+    for (int i = 0; i < dh; ++i) o[i] /= den;
+}
+
+/* ---------------------------------------------------------------------------------
+ * One output token of the layer, given the routing of that token.
+ *  - routed queries: q_{g,r} = x[t] @ Wq[idx[g][r]]  (only the selected experts are
+ *    computed: [R] "Algorithm Overview", only the active query-head computation);
+ *  - shared query:   q_s = x[t] @ Wqs, always on ([R], [T] "Always-On Shared Head");
+ *  - each query attends causally to its group's dense K/V ([T] "Dense KV Path");
+ *  - output construction by variant ([R] "Parameters"/"Ablations", [T] "Output
+ *    Construction"):
+ *      hard_concat:     y = sum_g sum_r o_{g,r} Wo[e] + o_s Wos
+ *      weighted_concat: y = sum_g sum_r p_e o_{g,r} Wo[e] + o_s Wos
+ *      gqe:             y = sum_g sum_r o_{g,r} Wo[e] + sum_g (sum_r w_r o_{g,r}) WoR[g]
+ *                           + o_s Wos
+ *    (o_s terms only when the shared head is on.)
+ * w is recomputed from p and the given selection (renormalisation over the selected).
+ * Shapes: Wq [N, d, dh], Wqs [d, dh], Wo [N, dh, d], WoR [G, dh, d], Wos [dh, d];
+ * Kseq/Vseq: [S, G, dh] of the token's sequence; s = position of the token.
+ * q_out/o_out (optional) receive [H_act, dh] in virtual-head order v = g k + r, then
+ * the shared head.
+ * --------------------------------------------------------------------------------- */
+static void token_output(const oracle_cfg* c, int s, const double* xt, const double* pt,
+                         const int32_t* idxt, const double* Wq, const double* Wqs,
+                         const double* Kseq, const double* Vseq, const double* Wo,
+                         const double* WoR, const double* Wos, double* yt, double* q_out,
+                         double* o_out)
+{
+    const int d = c->dim, N = c->num_query_experts, G = c->num_kv_heads, k = c->top_k;
+    const int dh = c->head_dim;
+    (void)N;
+    double* q = (double*)malloc(sizeof(double) * dh);
+    double* o = (double*)malloc(sizeof(double) * dh);
+    double* slot = (double*)malloc(sizeof(double) * dh);
+    for (int i = 0; i < d; ++i) yt[i] = 0.0;
+
+    for (int g = 0; g < G; ++g) {
+        double psel = 0.0;
+        for (int r = 0; r < k; ++r) psel += pt[idxt[g * k + r]];
+        for (int i = 0; i < dh; ++i) slot[i] = 0.0;
+        for (int r = 0; r < k; ++r) {
+            const int e = idxt[g * k + r];
+            for (int j = 0; j < dh; ++j) {
+                double a = 0.0;
+                for (int i = 0; i < d; ++i) a += xt[i] * Wq[((size_t)e * d + i) * dh + j];
+                q[j] = a;
+            }
+            attend(s, dh, G, g, q, Kseq, Vseq, o);
+            if (q_out) memcpy(q_out + (size_t)(g * k + r) * dh, q, sizeof(double) * dh);
+            if (o_out) memcpy(o_out + (size_t)(g * k + r) * dh, o, sizeof(double) * dh);
+            double coef = 1.0;
+            if (c->variant == 1) coef = pt[e];
+            for (int col = 0; col < d; ++col) {
+                double a = 0.0;
+                for (int j = 0; j < dh; ++j) a += o[j] * Wo[((size_t)e * dh + j) * d + col];
+                yt[col] += coef * a;
+            }
+            const double wr = pt[e] / psel;
+            for (int j = 0; j < dh; ++j) slot[j] += wr * o[j];
+        }
+        if (c->variant == 0) {
+            for (int col = 0; col < d; ++col) {
+                double a = 0.0;
+                for (int j = 0; j < dh; ++j) a += slot[j] * WoR[((size_t)g * dh + j) * d + col];
+                yt[col] += a;
+            }
+        }
+    }
+    if (c->shared_head) {
+        for (int j = 0; j < dh; ++j) {
+            double a = 0.0;
+            for (int i = 0; i < d; ++i) a += xt[i] * Wqs[(size_t)i * dh + j];
+            q[j] = a;
+        }
+        attend(s, dh, G, c->shared_kv_group, q, Kseq, Vseq, o);
+        if (q_out) memcpy(q_out + (size_t)(G * k) * dh, q, sizeof(double) * dh);
+        if (o_out) memcpy(o_out + (size_t)(G * k) * dh, o, sizeof(double) * dh);
+        for (int col = 0; col < d; ++col) {
+            double a = 0.0;
+            for (int j = 0; j < dh; ++j) a += o[j] * Wos[(size_t)j * d + col];
+            yt[col] += a;
+        }
+    }
+    free(q);
+    free(o);
+    free(slot);
+}
+
+/* Layer output for a list of tokens (global ids t = b*S + s in [0, B*S)).
+ * x [B*S, d]; p [B*S, N]; idx [B*S, G, k]; K, V [B*S, G, dh] from gqe_oracle_kv.
+ * y [nrows, d]; q_out, o_out optional [nrows, H_act, dh]. */
+int gqe_oracle_rows(const oracle_cfg* c, int64_t B, int64_t S, const double* x,
+                    const double* p, const int32_t* idx, const double* Wq, const double* Wqs,
+                    const double* K, const double* V, const double* Wo, const double* WoR,
+                    const double* Wos, const int64_t* rows, int64_t nrows, double* y,
+                    double* q_out, double* o_out)
+{
+    const int d = c->dim, N = c->num_query_experts, G = c->num_kv_heads, k = c->top_k;
+    const int dh = c->head_dim;
+    const int Hact = G * k + (c->shared_head ? 1 : 0);
+    if (c->shared_head && (c->shared_kv_group < 0 || c->shared_kv_group >= G)) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t t = rows[r];
+        if (t < 0 || t >= B * S) continue;
+        const int64_t b = t / S, s = t % S;
+        const double* Kseq = K + (size_t)b * S * G * dh;
+        const double* Vseq = V + (size_t)b * S * G * dh;
+        token_output(c, (int)s, x + t * d, p + t * N, idx + t * G * k, Wq, Wqs, Kseq, Vseq,
+                     Wo, WoR, Wos, y + r * d, q_out ? q_out + r * Hact * dh : NULL,
+                     o_out ? o_out + r * Hact * dh : NULL);
+    }
+    return 0;
+}
