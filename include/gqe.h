@@ -1,0 +1,181 @@
+/*
+ * gqe.h -- C ABI of the MI355X (gfx950) forward (prefill) pass of the Grouped Query Experts
+ * (GQE) attention layer.
+ *
+ * The layer (GQE README, "Algorithm Overview"; gist.science explainer, "Technical Summary"
+ * -> "Architecture and Routing"): N query-head experts are split into G GQA groups of
+ * n = N/G experts.  Inside each group a router takes a softmax over the group's experts and
+ * keeps the top-k per token.  The k routed query heads of every group, plus one always-on
+ * shared query head, attend causally to the G dense, unchanged KV heads.  The output is built
+ * by the "gqe" variant (hard concatenation + renormalised weighted-sum slot + shared head) or
+ * by the "weighted_concat" / "hard_concat" ablations (README "Parameters", "Ablations").
+ *
+ * Conventions for every entry point:
+ *  - Return value: GQE_OK (0) or a negative GQE_ERR_* code.  A thread-local message is then
+ *    available from gqe_last_error().  No C++ exception crosses this boundary and nothing
+ *    aborts.  Every argument check is done on the host before any device call.
+ *  - Device pointers are plain addresses in the memory of the current HIP device.  All
+ *    tensors are dense and row-major in the "x @ W" convention; shapes are given per argument.
+ *  - Ownership: the caller owns every device buffer (x, y, weights, packed weights, workspace,
+ *    routing outputs) and the stream.  The library owns only the opaque host handle.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
+ *    enqueued asynchronously; only gqe_aux_stats synchronises.
+ *  - A handle is not re-entrant: calls that use one handle (or one workspace) must not overlap
+ *    on different streams.
+ */
+#ifndef GQE_H_
+#define GQE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status codes */
+#define GQE_OK 0
+#define GQE_ERR_INVALID_CONFIG (-1) /* config violates the method's constraints          */
+#define GQE_ERR_NULL_POINTER (-2)   /* a required pointer is NULL                        */
+#define GQE_ERR_MISALIGNED (-3)     /* a device pointer is not 16-byte aligned           */
+#define GQE_ERR_UNSUPPORTED (-4)    /* valid for the method, not implemented for gfx950 */
+#define GQE_ERR_WORKSPACE (-5)      /* workspace / packed-weight buffer too small        */
+#define GQE_ERR_SHAPE (-6)          /* batch or seq out of range                         */
+#define GQE_ERR_HIP (-7)            /* a HIP runtime call or kernel launch failed        */
+#define GQE_ERR_STATE (-8)          /* call order violated (e.g. forward before packing)  */
+
+/* ------------------------------------------------------------------ enums */
+#define GQE_VARIANT_GQE 0             /* README "Ablations": "gqe", the full method       */
+#define GQE_VARIANT_WEIGHTED_CONCAT 1 /* "weighted_concat": no renormalised slot          */
+#define GQE_VARIANT_HARD_CONCAT 2     /* "hard_concat": hard concat only                  */
+
+#define GQE_DTYPE_F32 0  /* x, weights (except the router), y in float32                */
+#define GQE_DTYPE_BF16 1 /* x, weights (except the router), y in bfloat16 (RNE-rounded) */
+
+/* ------------------------------------------------------------------ configuration
+ * Mirrors GQEAttention(dim, num_query_experts=16, num_kv_heads=8, top_k=1, head_dim=None,
+ * variant="gqe") (README "Usage" and "Parameters").
+ *  dim               d, the hidden size; required, > 0.
+ *  num_query_experts N, routed query-head experts; must be divisible by num_kv_heads
+ *                    (README "Parameters").  N <= 64.
+ *  num_kv_heads      G, GQA groups = dense KV heads.
+ *  top_k             k, experts activated per group, 1 <= k <= N/G.
+ *  head_dim          d_h; 0 means dim / N (README "Parameters": defaults to dim // N).
+ *  variant           GQE_VARIANT_*.
+ *  shared_head       1 = one always-on shared query head (README "Algorithm Overview"),
+ *                    0 = none.
+ *  shared_kv_group   the KV group the shared head attends to (0 <= . < G).
+ *  dtype             GQE_DTYPE_*.
+ *  causal            must be 1 (prefill of a decoder: key s' attends only if s' <= s).
+ *  dense_gqa         0 = GQE.  1 = the all-active GQA baseline on the same kernels: every
+ *                    expert is a head (requires top_k == N/G, hard_concat, shared_head == 0);
+ *                    no router runs.
+ */
+typedef struct {
+    int32_t dim;
+    int32_t num_query_experts;
+    int32_t num_kv_heads;
+    int32_t top_k;
+    int32_t head_dim;
+    int32_t variant;
+    int32_t shared_head;
+    int32_t shared_kv_group;
+    int32_t dtype;
+    int32_t causal;
+    int32_t dense_gqa;
+} gqe_config_t;
+
+/* ------------------------------------------------------------------ weights
+ * Device pointers, row-major, "x @ W" orientation (tutorial moe_layer: x @ router_w).
+ * The router is always float32; all other weights are in cfg.dtype.
+ *  w_router   [d, N]       router projection (README "Algorithm Overview": per-group router)
+ *  b_router   [N] or NULL  router bias
+ *  w_q        [N, d, d_h]  routed query-head experts
+ *  w_q_shared [d, d_h]     shared query head (required iff shared_head)
+ *  w_k, w_v   [d, G*d_h]   dense KV projections; head g uses columns g*d_h .. g*d_h+d_h-1
+ *  w_o        [N, d_h, d]  output projection slice of every expert slot ("hard concat")
+ *  w_o_rslot  [G, d_h, d]  renormalised weighted-sum slot of every group (variant gqe only)
+ *  w_o_shared [d_h, d]     output projection of the shared head (required iff shared_head)
+ * The pointers are stored by gqe_init and read by gqe_pack_weights (and, for float32, by
+ * gqe_forward); they must stay valid for as long as the handle uses them.
+ */
+typedef struct {
+    const float* w_router;
+    const float* b_router;
+    const void* w_q;
+    const void* w_q_shared;
+    const void* w_k;
+    const void* w_v;
+    const void* w_o;
+    const void* w_o_rslot;
+    const void* w_o_shared;
+} gqe_weights_t;
+
+typedef struct gqe_handle gqe_handle_t;
+
+/* Validates cfg and the weight pointers on the host (no device call) and creates a handle.
+ * Errors: GQE_ERR_NULL_POINTER, GQE_ERR_INVALID_CONFIG (e.g. "num_query_experts must be
+ * divisible by num_kv_heads"), GQE_ERR_UNSUPPORTED, GQE_ERR_MISALIGNED. */
+int gqe_init(const gqe_config_t* cfg, const gqe_weights_t* weights, gqe_handle_t** out);
+
+/* Bytes of the caller-owned device buffer that holds the weights in the kernels' layouts
+ * (transposed head blocks, the router widened to float64, the stacked output projection). */
+int gqe_packed_weights_bytes(const gqe_handle_t* h, size_t* bytes);
+
+/* Enqueues the repacking of the weights given to gqe_init into `packed` (device, >= the size
+ * above, 256-byte aligned) and records `packed` in the handle.  Call once after gqe_init and
+ * again whenever the weights change.  Layout change only: no arithmetic of the layer. */
+int gqe_pack_weights(gqe_handle_t* h, void* packed, size_t bytes, void* stream);
+
+/* Bytes of scratch that gqe_forward needs for a [batch, seq] input (routing decisions,
+ * per-expert statistics, Q/K/V and head outputs).  batch >= 1, seq >= 1. */
+int gqe_workspace_bytes(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t* bytes);
+
+/* The forward pass y = GQE(x) (README "Usage": y = attn(x)).
+ *  x          [batch, seq, d] device, cfg.dtype; not aliased with y.
+ *  y          [batch, seq, d] device, cfg.dtype (written).
+ *  workspace  device, >= gqe_workspace_bytes(batch, seq), 256-byte aligned; also holds the
+ *             routing statistics read later by gqe_aux_stats.
+ *  route_idx  optional [batch, seq, G, k] int32: global expert id of the r-th choice of each
+ *             group (descending router logit; ties -> lower id).  NULL to skip.
+ *  route_w    optional [batch, seq, G, k] float32: renormalised weight p / sum(p_selected)
+ *             of each choice.  NULL to skip.
+ * Enqueues all kernels on `stream` and returns.  Requires gqe_pack_weights first (else
+ * GQE_ERR_STATE).  Errors: NULL/misaligned pointers, GQE_ERR_SHAPE, GQE_ERR_WORKSPACE,
+ * GQE_ERR_HIP (launch failure). */
+int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t seq,
+                void* workspace, size_t ws_bytes, void* stream, int32_t* route_idx,
+                float* route_w);
+
+/* Load-balancing statistics of the last gqe_forward on this handle (README "Algorithm
+ * Overview": Switch-style auxiliary loss; "Usage": loss = lm_loss + 0.01 *
+ * collect_aux_loss(attn)).  Synchronises `stream`, then copies to host memory:
+ *  counts[N]     number of tokens that selected each expert (exact)
+ *  mean_prob[N]  mean over tokens of the in-group router probability of each expert
+ *  aux_loss      (1/G) sum_g n sum_{e in g} (count_e / (T k)) mean_prob_e -- unscaled; the
+ *                caller applies the 0.01 coefficient
+ *  active_heads  G*k + shared_head (README: 9 of 16 heads at N=16, G=8, k=1)
+ * Any output pointer may be NULL.  In dense_gqa mode counts are T per expert, mean_prob 1/n.
+ * Errors: GQE_ERR_STATE if no forward ran. */
+int gqe_aux_stats(gqe_handle_t* h, void* stream, int64_t* counts, double* mean_prob,
+                  double* aux_loss, int32_t* active_heads);
+
+/* Byte offsets of the intermediates inside the workspace of a [batch, seq] forward, for
+ * stage-by-stage checks:  offs[0] Q_act [B, H_act, S, d_h], offs[1] K [B, G, S_pad, d_h],
+ * offs[2] V^T [B, G, d_h, S_pad] (keys permuted inside every 32-key block, see DESIGN),
+ * offs[3] O_act [B, S, H_act, d_h], offs[4] route_idx [T, G, k] int32, offs[5] route_w
+ * [T, G, k] f32, offs[6] p_sel [T, G, k] f32; dims[0] = H_act, dims[1] = S_pad. */
+int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t offs[8],
+                         int64_t dims[4]);
+
+/* Destroys the handle (host memory only).  NULL is ignored. */
+void gqe_destroy(gqe_handle_t* h);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* gqe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQE_H_ */

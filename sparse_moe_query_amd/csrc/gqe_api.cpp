@@ -1,0 +1,284 @@
+// C ABI of libgqe: argument validation, workspace planning and launch order.
+// Every check runs on the host before any device call; no exception leaves this file.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "gqe_common.h"
+#include "gqe_internal.h"
+
+#ifndef MFMA_PATH_ENABLED
+#define MFMA_PATH_ENABLED 0
+#endif
+
+static thread_local char g_err[512] = "";
+
+static int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+static int ok() {
+    g_err[0] = 0;
+    return GQE_OK;
+}
+static bool misaligned(const void* p, size_t a) { return ((uintptr_t)p) % a != 0; }
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S) {
+    WorkPlan P;
+    P.B = B;
+    P.S = S;
+    P.T = B * S;
+    P.S_pad = round_up(S, GQE_KV_TILE);
+    P.nblk_router = ceil_div(P.T, 64);
+    const size_t es = D.dtype == GQE_DTYPE_BF16 ? 2 : 4;
+    const size_t gk = (size_t)P.T * D.G * D.k;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    P.idx = take(gk * 4);
+    P.wsel = take(gk * 4);
+    P.psel = take(gk * 4);
+    P.part_cnt = take((size_t)P.nblk_router * D.N * 4);
+    P.part_psum = take((size_t)P.nblk_router * D.N * 8);
+    P.stats = take((size_t)D.N * 16 + 64);
+    P.q = take((size_t)B * D.H * S * D.dh * es);
+    P.kk = take((size_t)B * D.G * P.S_pad * D.dh * es);
+    P.vt = take((size_t)B * D.G * D.dh * P.S_pad * es);
+    P.o = take((size_t)B * S * D.H * D.dh * es);
+    P.total = off;
+    return P;
+}
+
+PackedLayout make_packed_layout(const GqeDims& D, bool mfma) {
+    PackedLayout L;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    L.wr64 = take((size_t)D.d * D.N * 8);
+    L.br64 = take((size_t)D.N * 8);
+    L.hb_total = 2 * D.G + D.s + D.N;
+    L.slots = D.dense ? D.N : D.N + (D.variant == GQE_VARIANT_GQE ? D.G : 0) + D.s;
+    if (mfma) {
+        L.wproj = take((size_t)L.hb_total * D.dh * D.d * 2);
+        L.wo = take((size_t)D.d * L.slots * D.dh * 2);
+    } else {
+        L.wproj = L.wo = 0;
+    }
+    L.total = off;
+    return L;
+}
+
+// The matrix-core path covers bf16 with head dims that tile by 16 and hidden sizes that tile
+// by 64; everything else the method allows runs on the scalar path.
+static bool mfma_supported(const GqeDims& D) {
+    if (MFMA_PATH_ENABLED == 0) return false;
+    if (D.dtype != GQE_DTYPE_BF16) return false;
+    if (!(D.dh == 32 || D.dh == 48 || D.dh == 64)) return false;
+    if (D.d % 64 != 0) return false;
+    if (D.N > 64 || D.n > 16) return false;
+    if (!D.dense && 8 * D.k + D.n > 24) return false;
+    if (D.H > 64) return false;
+    return true;
+}
+
+extern "C" {
+
+const char* gqe_last_error(void) { return g_err; }
+
+int gqe_init(const gqe_config_t* cfg, const gqe_weights_t* w, gqe_handle_t** out) {
+    if (!cfg || !w || !out) return fail(GQE_ERR_NULL_POINTER, "gqe_init: cfg, weights and out must be non-NULL");
+    *out = nullptr;
+    const gqe_config_t& c = *cfg;
+    if (c.dim <= 0) return fail(GQE_ERR_INVALID_CONFIG, "dim must be positive (got %d)", c.dim);
+    if (c.num_query_experts <= 0 || c.num_kv_heads <= 0)
+        return fail(GQE_ERR_INVALID_CONFIG, "num_query_experts and num_kv_heads must be positive");
+    if (c.num_query_experts % c.num_kv_heads != 0)
+        return fail(GQE_ERR_INVALID_CONFIG, "num_query_experts must be divisible by num_kv_heads (%d %% %d != 0)",
+                    c.num_query_experts, c.num_kv_heads);
+    const int n = c.num_query_experts / c.num_kv_heads;
+    if (c.top_k < 1 || c.top_k > n)
+        return fail(GQE_ERR_INVALID_CONFIG, "top_k must be in [1, num_query_experts/num_kv_heads = %d] (got %d)", n, c.top_k);
+    if (c.head_dim < 0) return fail(GQE_ERR_INVALID_CONFIG, "head_dim must be >= 0 (0 = dim // num_query_experts)");
+    const int dh = c.head_dim ? c.head_dim : c.dim / c.num_query_experts;
+    if (dh <= 0) return fail(GQE_ERR_INVALID_CONFIG, "dim // num_query_experts is 0; give head_dim explicitly");
+    if (c.variant < 0 || c.variant > 2) return fail(GQE_ERR_INVALID_CONFIG, "unknown variant %d", c.variant);
+    if (c.dtype != GQE_DTYPE_F32 && c.dtype != GQE_DTYPE_BF16) return fail(GQE_ERR_INVALID_CONFIG, "unknown dtype %d", c.dtype);
+    if (c.shared_head != 0 && c.shared_head != 1) return fail(GQE_ERR_INVALID_CONFIG, "shared_head must be 0 or 1");
+    if (c.shared_head && (c.shared_kv_group < 0 || c.shared_kv_group >= c.num_kv_heads))
+        return fail(GQE_ERR_INVALID_CONFIG, "shared_kv_group must be in [0, num_kv_heads)");
+    if (c.dense_gqa != 0 && c.dense_gqa != 1) return fail(GQE_ERR_INVALID_CONFIG, "dense_gqa must be 0 or 1");
+    if (c.dense_gqa && (c.top_k != n || c.variant != GQE_VARIANT_HARD_CONCAT || c.shared_head))
+        return fail(GQE_ERR_INVALID_CONFIG, "dense_gqa requires top_k == num_query_experts/num_kv_heads, variant hard_concat and no shared head");
+    if (c.causal != 1) return fail(GQE_ERR_UNSUPPORTED, "only causal prefill (causal = 1) is implemented");
+    if (c.num_query_experts > 64) return fail(GQE_ERR_UNSUPPORTED, "num_query_experts > 64 is not supported");
+    if (dh > 128) return fail(GQE_ERR_UNSUPPORTED, "head_dim > 128 is not supported");
+
+    if (!c.dense_gqa && !w->w_router) return fail(GQE_ERR_NULL_POINTER, "w_router is required");
+    if (!w->w_q || !w->w_k || !w->w_v || !w->w_o) return fail(GQE_ERR_NULL_POINTER, "w_q, w_k, w_v and w_o are required");
+    if (c.shared_head && (!w->w_q_shared || !w->w_o_shared))
+        return fail(GQE_ERR_NULL_POINTER, "w_q_shared and w_o_shared are required when shared_head = 1");
+    if (c.variant == GQE_VARIANT_GQE && !c.dense_gqa && !w->w_o_rslot)
+        return fail(GQE_ERR_NULL_POINTER, "w_o_rslot is required for variant gqe");
+    const void* ptrs[] = {w->w_router, w->b_router, w->w_q, w->w_q_shared, w->w_k, w->w_v, w->w_o, w->w_o_rslot, w->w_o_shared};
+    for (const void* p : ptrs)
+        if (p && misaligned(p, 16)) return fail(GQE_ERR_MISALIGNED, "weight pointers must be 16-byte aligned");
+
+    gqe_handle* h = new (std::nothrow) gqe_handle();
+    if (!h) return fail(GQE_ERR_INVALID_CONFIG, "out of host memory");
+    h->cfg = c;
+    h->w = *w;
+    GqeDims& D = h->D;
+    D.d = c.dim;
+    D.N = c.num_query_experts;
+    D.G = c.num_kv_heads;
+    D.k = c.top_k;
+    D.n = n;
+    D.dh = dh;
+    D.s = c.shared_head;
+    D.H = D.G * D.k + D.s;
+    D.variant = c.variant;
+    D.dtype = c.dtype;
+    D.skv = c.shared_head ? c.shared_kv_group : 0;
+    D.dense = c.dense_gqa;
+    h->mfma = mfma_supported(D);
+    h->pl = make_packed_layout(D, h->mfma);
+    h->packed = nullptr;
+    h->ran = false;
+    h->last_ws = nullptr;
+    *out = h;
+    return ok();
+}
+
+int gqe_packed_weights_bytes(const gqe_handle_t* h, size_t* bytes) {
+    if (!h || !bytes) return fail(GQE_ERR_NULL_POINTER, "handle and bytes must be non-NULL");
+    *bytes = h->pl.total;
+    return ok();
+}
+
+int gqe_pack_weights(gqe_handle_t* h, void* packed, size_t bytes, void* stream) {
+    if (!h || !packed) return fail(GQE_ERR_NULL_POINTER, "handle and packed must be non-NULL");
+    if (misaligned(packed, 256)) return fail(GQE_ERR_MISALIGNED, "packed buffer must be 256-byte aligned");
+    if (bytes < h->pl.total) return fail(GQE_ERR_WORKSPACE, "packed buffer too small: %zu < %zu", bytes, h->pl.total);
+    hipError_t e = launch_pack(h->D, h->w, h->pl, packed, h->mfma, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GQE_ERR_HIP, "weight packing failed: %s", hipGetErrorString(e));
+    h->packed = packed;
+    return ok();
+}
+
+int gqe_workspace_bytes(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t* bytes) {
+    if (!h || !bytes) return fail(GQE_ERR_NULL_POINTER, "handle and bytes must be non-NULL");
+    if (batch < 1 || seq < 1 || batch * seq > ((int64_t)1 << 28))
+        return fail(GQE_ERR_SHAPE, "batch and seq must be >= 1 with batch*seq <= 2^28");
+    *bytes = make_plan(h->D, batch, seq).total;
+    return ok();
+}
+
+int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t offs[8], int64_t dims[4]) {
+    if (!h || !offs || !dims) return fail(GQE_ERR_NULL_POINTER, "handle, offs and dims must be non-NULL");
+    if (batch < 1 || seq < 1 || batch * seq > ((int64_t)1 << 28)) return fail(GQE_ERR_SHAPE, "bad batch/seq");
+    WorkPlan P = make_plan(h->D, batch, seq);
+    offs[0] = P.q;
+    offs[1] = P.kk;
+    offs[2] = P.vt;
+    offs[3] = P.o;
+    offs[4] = P.idx;
+    offs[5] = P.wsel;
+    offs[6] = P.psel;
+    offs[7] = P.stats;
+    dims[0] = h->D.H;
+    dims[1] = P.S_pad;
+    dims[2] = h->mfma ? 1 : 0;
+    dims[3] = 0;
+    return ok();
+}
+
+int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t seq, void* workspace,
+                size_t ws_bytes, void* stream, int32_t* route_idx, float* route_w) {
+    if (!h || !x || !y || !workspace) return fail(GQE_ERR_NULL_POINTER, "handle, x, y and workspace must be non-NULL");
+    if (!h->packed) return fail(GQE_ERR_STATE, "gqe_pack_weights must run before gqe_forward");
+    if (batch < 1 || seq < 1 || batch * seq > ((int64_t)1 << 28))
+        return fail(GQE_ERR_SHAPE, "batch and seq must be >= 1 with batch*seq <= 2^28 (got %lld x %lld)",
+                    (long long)batch, (long long)seq);
+    if (misaligned(x, 16) || misaligned(y, 16)) return fail(GQE_ERR_MISALIGNED, "x and y must be 16-byte aligned");
+    if (misaligned(workspace, 256)) return fail(GQE_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    if ((route_idx && misaligned(route_idx, 4)) || (route_w && misaligned(route_w, 4)))
+        return fail(GQE_ERR_MISALIGNED, "routing outputs must be 4-byte aligned");
+    const GqeDims& D = h->D;
+    const size_t es = D.dtype == GQE_DTYPE_BF16 ? 2 : 4;
+    const size_t xbytes = (size_t)batch * seq * D.d * es;
+    const char* xb = (const char*)x;
+    const char* yb = (const char*)y;
+    if (xb < yb + xbytes && yb < xb + xbytes) return fail(GQE_ERR_INVALID_CONFIG, "x and y must not alias");
+    WorkPlan P = make_plan(D, batch, seq);
+    if (ws_bytes < P.total) return fail(GQE_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, P.total);
+    hipStream_t st = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    hipError_t e = hipSuccess;
+    if (!D.dense) e = launch_router(D, P, x, h->packed, h->pl, ws, route_idx, route_w, st);
+    if (e == hipSuccess) {
+        if (h->mfma) {
+            e = launch_proj_mfma(D, P, x, h->packed, h->pl, ws, st);
+            if (e == hipSuccess) e = launch_attn_mfma(D, P, ws, st);
+            if (e == hipSuccess) e = launch_combine_mfma(D, P, h->packed, h->pl, y, ws, st);
+        } else {
+            e = launch_simple_forward(D, P, h->w, x, y, ws, st);
+        }
+    }
+    if (e != hipSuccess) return fail(GQE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    h->ran = true;
+    h->last_ws = workspace;
+    h->last_plan = P;
+    return ok();
+}
+
+int gqe_aux_stats(gqe_handle_t* h, void* stream, int64_t* counts, double* mean_prob, double* aux_loss,
+                  int32_t* active_heads) {
+    if (!h) return fail(GQE_ERR_NULL_POINTER, "handle must be non-NULL");
+    if (!h->ran) return fail(GQE_ERR_STATE, "no forward has run on this handle");
+    const GqeDims& D = h->D;
+    if (active_heads) *active_heads = D.H;
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return fail(GQE_ERR_HIP, "stream synchronisation failed: %s", hipGetErrorString(e));
+    const WorkPlan& P = h->last_plan;
+    if (D.dense) {
+        // all-active GQA: every expert sees every token with in-group probability 1/n
+        for (int i = 0; i < D.N; ++i) {
+            if (counts) counts[i] = P.T;
+            if (mean_prob) mean_prob[i] = 1.0 / D.n;
+        }
+        if (aux_loss) *aux_loss = 1.0;
+        return ok();
+    }
+    const char* st = (const char*)h->last_ws + P.stats;
+    if (counts) {
+        e = hipMemcpy(counts, st, sizeof(int64_t) * D.N, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return fail(GQE_ERR_HIP, "copy of counts failed: %s", hipGetErrorString(e));
+    }
+    if (mean_prob) {
+        e = hipMemcpy(mean_prob, st + 8 * D.N, sizeof(double) * D.N, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return fail(GQE_ERR_HIP, "copy of mean_prob failed: %s", hipGetErrorString(e));
+    }
+    if (aux_loss) {
+        e = hipMemcpy(aux_loss, st + 16 * D.N, sizeof(double), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return fail(GQE_ERR_HIP, "copy of aux_loss failed: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
+void gqe_destroy(gqe_handle_t* h) { delete h; }
+
+}  // extern "C"

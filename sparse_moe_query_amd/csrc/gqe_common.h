@@ -1,0 +1,51 @@
+// Internal helpers shared by the HIP kernels of libgqe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- element type traits
+// Storage is either float32 or bfloat16 (raw 16-bit patterns); arithmetic is float32.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) {
+    return __uint_as_float(((uint32_t)v.bits) << 16);
+}
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// float32 -> bfloat16, round to nearest even (finite inputs; NaN stays NaN).
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return bf16_t{(uint16_t)((u >> 16) | 0x40)};
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return bf16_t{(uint16_t)(u >> 16)};
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)from_f32<bf16_t>(lo).bits | ((uint32_t)from_f32<bf16_t>(hi).bits << 16);
+}
+
+// Position, inside its 32-key block, at which key offset o (0..31) of V^T is stored.
+// Groups of four keys are interleaved so that one 16-byte LDS read hands every lane of the
+// P.V matrix-core step exactly the eight keys its probability registers hold (see k_attn).
+__host__ __device__ __forceinline__ int vt_slot(int o) {
+    const int c = o >> 2;
+    return ((((c & 1) << 2) | (c >> 1)) << 2) | (o & 3);
+}
+__host__ __device__ __forceinline__ int64_t vt_pos(int64_t s) {
+    return (s & ~(int64_t)31) | vt_slot((int)(s & 31));
+}
+
+__host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ __forceinline__ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+#define GQE_KV_TILE 64  // keys per attention tile; K and V^T are padded to a multiple of this

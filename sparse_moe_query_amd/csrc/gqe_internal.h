@@ -1,0 +1,65 @@
+// Internal declarations of libgqe: the handle, the workspace plan and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gqe.h"
+
+struct GqeDims {
+    int d, N, G, k, n, dh, H, s;  // s = shared head on; H = active heads per token
+    int variant, dtype, skv, dense;
+};
+
+// Byte offsets into the caller's packed-weights buffer.
+struct PackedLayout {
+    size_t wr64, br64;   // router weights [d][N] and bias [N] widened to float64
+    size_t wproj;        // bf16 path: head blocks [HB][dh][d] (K_g, V_g, shared Q, W_q[e])
+    size_t wo;           // bf16 path: stacked output projection [d][Ktot], Ktot = slots * dh
+    size_t total;
+    int hb_total;        // number of projection head blocks
+    int slots;           // output-projection slots (expert slots, renormalised slots, shared)
+};
+
+// Byte offsets into the caller's workspace for one [B, S] forward.
+struct WorkPlan {
+    int64_t B, S, T, S_pad;
+    int64_t nblk_router;
+    size_t idx, wsel, psel;           // [T, G, k] int32 / f32 / f32
+    size_t part_cnt, part_psum;       // [nblk_router, N] int32 / f64
+    size_t stats;                     // counts [N] i64, mean [N] f64, aux f64
+    size_t q, kk, vt, o;              // Q_act, K, V^T, O_act
+    size_t total;
+};
+
+struct gqe_handle {
+    gqe_config_t cfg;
+    gqe_weights_t w;
+    GqeDims D;
+    bool mfma;             // bf16 matrix-core path available for this config
+    PackedLayout pl;
+    void* packed;          // set by gqe_pack_weights
+    // last forward (for gqe_aux_stats)
+    bool ran;
+    void* last_ws;
+    WorkPlan last_plan;
+};
+
+WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S);
+PackedLayout make_packed_layout(const GqeDims& D, bool mfma);
+
+// ---------------------------------------------------------------- launchers (return hipError_t)
+hipError_t launch_pack(const GqeDims& D, const gqe_weights_t& w, const PackedLayout& pl,
+                       void* packed, bool mfma, hipStream_t st);
+hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, const void* packed,
+                         const PackedLayout& pl, char* ws, int32_t* route_idx, float* route_w,
+                         hipStream_t st);
+hipError_t launch_simple_forward(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w,
+                                 const void* x, void* y, char* ws, hipStream_t st);
+hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x,
+                            const void* packed, const PackedLayout& pl, char* ws,
+                            hipStream_t st);
+hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st);
+hipError_t launch_combine_mfma(const GqeDims& D, const WorkPlan& P, const void* packed,
+                               const PackedLayout& pl, void* y, char* ws, hipStream_t st);

@@ -1,0 +1,96 @@
+// Weight repacking (layout only, no arithmetic of the layer):
+//  - the router projection and bias widened to float64 (exact) for the float64 logit sums;
+//  - bf16 path: every projection head block transposed to [d_h][d] so that each matrix-core
+//    lane reads eight consecutive hidden-dimension values with one 16-byte load;
+//  - bf16 path: the output projections stacked into one [d][slots * d_h] matrix, slot order
+//    per group g: its n expert slots, then (variant gqe) its renormalised slot; then the shared
+//    head's slot.
+#include "gqe_common.h"
+#include "gqe_internal.h"
+
+namespace {
+
+__global__ void widen_router_kernel(const float* __restrict__ w, const float* __restrict__ b,
+                                    int64_t dn, int N, double* __restrict__ w64,
+                                    double* __restrict__ b64) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < dn) w64[i] = w ? (double)w[i] : 0.0;
+    if (i < N) b64[i] = b ? (double)b[i] : 0.0;
+}
+
+// dst[hb][j][i] = src_hb[i * ld + col0 + j]   (16-bit elements)
+struct HeadBlockSrc {
+    const uint16_t* base;
+    int64_t ld;
+    int64_t col0;
+};
+
+__global__ void pack_proj_kernel(const uint16_t* __restrict__ wk, const uint16_t* __restrict__ wv,
+                                 const uint16_t* __restrict__ wqs, const uint16_t* __restrict__ wq,
+                                 int d, int G, int dh, int s, int N, uint16_t* __restrict__ dst) {
+    const int64_t per = (int64_t)dh * d;
+    const int64_t total = (int64_t)(2 * G + s + N) * per;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const int hb = (int)(q / per);
+        const int64_t r = q % per;
+        const int j = (int)(r / d), i = (int)(r % d);
+        uint16_t v;
+        if (hb < G) v = wk[(int64_t)i * G * dh + (int64_t)hb * dh + j];
+        else if (hb < 2 * G) v = wv[(int64_t)i * G * dh + (int64_t)(hb - G) * dh + j];
+        else if (s && hb == 2 * G) v = wqs[(int64_t)i * dh + j];
+        else {
+            const int e = hb - 2 * G - s;
+            v = wq[((int64_t)e * d + i) * dh + j];
+        }
+        dst[q] = v;
+    }
+}
+
+// dst[col][slot * dh + j] = W_slot[j][col]
+__global__ void pack_wo_kernel(const uint16_t* __restrict__ wo, const uint16_t* __restrict__ wor,
+                               const uint16_t* __restrict__ wos, int d, int G, int n, int dh,
+                               int rslot, int s, int slots, uint16_t* __restrict__ dst) {
+    const int64_t K = (int64_t)slots * dh;
+    const int64_t total = (int64_t)d * K;
+    const int per_group = n + rslot;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const int col = (int)(q / K);
+        const int64_t kk = q % K;
+        const int slot = (int)(kk / dh), j = (int)(kk % dh);
+        uint16_t v;
+        if (slot < G * per_group) {
+            const int g = slot / per_group, u = slot % per_group;
+            if (u < n) v = wo[((int64_t)(g * n + u) * dh + j) * d + col];
+            else v = wor[((int64_t)g * dh + j) * d + col];
+        } else {
+            (void)s;
+            v = wos[(int64_t)j * d + col];
+        }
+        dst[q] = v;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_pack(const GqeDims& D, const gqe_weights_t& w, const PackedLayout& pl,
+                       void* packed, bool mfma, hipStream_t st) {
+    char* pk = (char*)packed;
+    const int64_t dn = (int64_t)D.d * D.N;
+    const int64_t m = dn > D.N ? dn : D.N;
+    widen_router_kernel<<<(unsigned)ceil_div(m, 256), 256, 0, st>>>(
+        w.w_router, w.b_router, dn, D.N, (double*)(pk + pl.wr64), (double*)(pk + pl.br64));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !mfma) return e;
+    pack_proj_kernel<<<1024, 256, 0, st>>>((const uint16_t*)w.w_k, (const uint16_t*)w.w_v,
+                                           (const uint16_t*)w.w_q_shared, (const uint16_t*)w.w_q,
+                                           D.d, D.G, D.dh, D.s, D.N, (uint16_t*)(pk + pl.wproj));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int rslot = (!D.dense && D.variant == GQE_VARIANT_GQE) ? 1 : 0;
+    pack_wo_kernel<<<1024, 256, 0, st>>>((const uint16_t*)w.w_o, (const uint16_t*)w.w_o_rslot,
+                                         (const uint16_t*)w.w_o_shared, D.d, D.G, D.n, D.dh, rslot,
+                                         D.s, pl.slots, (uint16_t*)(pk + pl.wo));
+    return hipGetLastError();
+}

@@ -1,0 +1,268 @@
+"""Thin ctypes binding of libgqe (C ABI in include/gqe.h).
+
+Argument marshalling only: every step of the forward pass runs in the library's HIP kernels.
+PyTorch supplies device memory and streams.  The functions keep the C names; ``GQEAttention``
+and ``collect_aux_loss`` wrap them in the shape of the README's usage example
+(``attn = GQEAttention(dim=768, num_query_experts=16, num_kv_heads=8, top_k=1)``,
+``y = attn(x)``, ``collect_aux_loss(attn)``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgqe.so")
+
+VARIANTS = {"gqe": 0, "weighted_concat": 1, "hard_concat": 2}
+DTYPES = {"f32": 0, "bf16": 1}
+TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+ERRORS = {0: "GQE_OK", -1: "GQE_ERR_INVALID_CONFIG", -2: "GQE_ERR_NULL_POINTER",
+          -3: "GQE_ERR_MISALIGNED", -4: "GQE_ERR_UNSUPPORTED", -5: "GQE_ERR_WORKSPACE",
+          -6: "GQE_ERR_SHAPE", -7: "GQE_ERR_HIP", -8: "GQE_ERR_STATE"}
+EXPORTS = ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights", "gqe_workspace_bytes",
+           "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_destroy",
+           "gqe_last_error")
+
+
+class GqeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "dim", "num_query_experts", "num_kv_heads", "top_k", "head_dim", "variant",
+        "shared_head", "shared_kv_group", "dtype", "causal", "dense_gqa")]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w_router", "b_router", "w_q", "w_q_shared", "w_k", "w_v", "w_o", "w_o_rslot",
+        "w_o_shared")]
+
+
+_lib = None
+
+
+def lib():
+    """Load libgqe.so; fails loudly when the HIP library has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(hipcc for gfx950); there is no fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        L.gqe_init.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), ctypes.POINTER(P)]
+        L.gqe_packed_weights_bytes.argtypes = [P, ctypes.POINTER(SZ)]
+        L.gqe_pack_weights.argtypes = [P, P, SZ, P]
+        L.gqe_workspace_bytes.argtypes = [P, I64, I64, ctypes.POINTER(SZ)]
+        L.gqe_forward.argtypes = [P, P, P, I64, I64, P, SZ, P, P, P]
+        L.gqe_aux_stats.argtypes = [P, P, P, P, P, P]
+        L.gqe_workspace_layout.argtypes = [P, I64, I64, P, P]
+        L.gqe_destroy.argtypes = [P]
+        L.gqe_destroy.restype = None
+        L.gqe_last_error.argtypes = []
+        L.gqe_last_error.restype = ctypes.c_char_p
+        for f in ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights",
+                  "gqe_workspace_bytes", "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise GqeError(rc, gqe_last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ------------------------------------------------------------------------- C names
+def gqe_last_error() -> str:
+    return lib().gqe_last_error().decode()
+
+
+def gqe_init(cfg: Config, weights: Weights) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(lib().gqe_init(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(h)))
+    return h
+
+
+def gqe_packed_weights_bytes(h) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().gqe_packed_weights_bytes(h, ctypes.byref(n)))
+    return n.value
+
+
+def gqe_pack_weights(h, packed: torch.Tensor, stream=None):
+    _check(lib().gqe_pack_weights(h, _ptr(packed), packed.numel() * packed.element_size(),
+                                  _stream(stream)))
+
+
+def gqe_workspace_bytes(h, batch: int, seq: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().gqe_workspace_bytes(h, batch, seq, ctypes.byref(n)))
+    return n.value
+
+
+def gqe_forward(h, x: torch.Tensor, y: torch.Tensor, batch: int, seq: int,
+                workspace: torch.Tensor, stream=None, route_idx=None, route_w=None):
+    _check(lib().gqe_forward(h, _ptr(x), _ptr(y), batch, seq, _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream),
+                             _ptr(route_idx), _ptr(route_w)))
+
+
+def gqe_aux_stats(h, n_experts: int, stream=None) -> dict:
+    counts = np.zeros(n_experts, np.int64)
+    mean = np.zeros(n_experts, np.float64)
+    aux = np.zeros(1, np.float64)
+    heads = np.zeros(1, np.int32)
+    _check(lib().gqe_aux_stats(h, _stream(stream), counts.ctypes.data_as(ctypes.c_void_p),
+                               mean.ctypes.data_as(ctypes.c_void_p),
+                               aux.ctypes.data_as(ctypes.c_void_p),
+                               heads.ctypes.data_as(ctypes.c_void_p)))
+    return dict(counts=counts, mean_prob=mean, aux=float(aux[0]), active_heads=int(heads[0]))
+
+
+def gqe_workspace_layout(h, batch: int, seq: int):
+    offs = (ctypes.c_size_t * 8)()
+    dims = (ctypes.c_int64 * 4)()
+    _check(lib().gqe_workspace_layout(h, batch, seq, offs, dims))
+    return list(offs), list(dims)
+
+
+def gqe_destroy(h):
+    if h:
+        lib().gqe_destroy(h)
+
+
+# ------------------------------------------------------------------------- module wrapper
+class GQEAttention:
+    """GQEAttention(dim, num_query_experts=16, num_kv_heads=8, top_k=1, head_dim=None,
+    variant="gqe") as in the README; weights are device tensors in the C ABI layouts."""
+
+    WEIGHT_KEYS = ("w_router", "b_router", "w_q", "w_q_shared", "w_k", "w_v", "w_o",
+                   "w_o_rslot", "w_o_shared")
+
+    def __init__(self, dim: int, num_query_experts: int = 16, num_kv_heads: int = 8,
+                 top_k: int = 1, head_dim: int | None = None, variant: str = "gqe",
+                 shared_head: bool = True, shared_kv_group: int = 0, dtype: str = "bf16",
+                 dense_gqa: bool = False, weights: dict | None = None, stream=None):
+        if weights is None:
+            raise ValueError("weights (device tensors) are required")
+        self.dtype = dtype
+        self.N = num_query_experts
+        self.G = num_kv_heads
+        self.k = top_k
+        self.dim = dim
+        self.cfg = Config(dim, num_query_experts, num_kv_heads, top_k, head_dim or 0,
+                          VARIANTS[variant], int(shared_head), shared_kv_group, DTYPES[dtype], 1,
+                          int(dense_gqa))
+        self._w = {k: weights.get(k) for k in self.WEIGHT_KEYS}   # keep alive
+        self.weights = Weights(*[_ptr(self._w[k]) for k in self.WEIGHT_KEYS])
+        self.h = gqe_init(self.cfg, self.weights)
+        dev = next(v.device for v in self._w.values() if v is not None)
+        self.device = dev
+        self.packed = torch.empty(max(gqe_packed_weights_bytes(self.h), 256), dtype=torch.uint8,
+                                  device=dev)
+        gqe_pack_weights(self.h, self.packed, stream)
+        self._ws = None
+        self._ws_shape = None
+
+    def workspace(self, batch: int, seq: int) -> torch.Tensor:
+        nbytes = gqe_workspace_bytes(self.h, batch, seq)
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def __call__(self, x: torch.Tensor, y: torch.Tensor | None = None, stream=None,
+                 route_idx=None, route_w=None) -> torch.Tensor:
+        B, S, d = x.shape
+        if d != self.dim or x.dtype != TORCH_DTYPES[self.dtype] or not x.is_contiguous():
+            raise ValueError("x must be a contiguous [B, S, dim] tensor of the layer's dtype")
+        if y is None:
+            y = torch.empty_like(x)
+        ws = self.workspace(B, S)
+        gqe_forward(self.h, x, y, B, S, ws, stream, route_idx, route_w)
+        return y
+
+    def aux_stats(self, stream=None) -> dict:
+        return gqe_aux_stats(self.h, self.N, stream)
+
+    def intermediates(self, batch: int, seq: int) -> dict:
+        """Views of Q_act, K, V^T, O_act and the routing buffers inside the workspace."""
+        offs, dims = gqe_workspace_layout(self.h, batch, seq)
+        H, S_pad = dims[0], dims[1]
+        es = 2 if self.dtype == "bf16" else 4
+        td = TORCH_DTYPES[self.dtype]
+        dh = int(self.cfg.head_dim or self.dim // self.N)
+        ws = self._ws
+        T = batch * seq
+
+        def view(off, shape, dt, esz):
+            n = int(np.prod(shape))
+            return ws[off:off + n * esz].view(dt).reshape(shape)
+
+        return dict(
+            q=view(offs[0], (batch, H, seq, dh), td, es),
+            k=view(offs[1], (batch, self.G, S_pad, dh), td, es),
+            vt=view(offs[2], (batch, self.G, dh, S_pad), td, es),
+            o=view(offs[3], (batch, seq, H, dh), td, es),
+            idx=view(offs[4], (T, self.G, self.k), torch.int32, 4),
+            w=view(offs[5], (T, self.G, self.k), torch.float32, 4),
+            psel=view(offs[6], (T, self.G, self.k), torch.float32, 4),
+            matrix_core=bool(dims[2]),
+        )
+
+    def close(self):
+        if self.h:
+            gqe_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def collect_aux_loss(attn: GQEAttention, stream=None) -> float:
+    """README 'Usage': the load-balancing loss of the last forward (unscaled)."""
+    return attn.aux_stats(stream)["aux"]
+
+
+def vt_unpermute(vt: torch.Tensor) -> torch.Tensor:
+    """Undo the key slotting of V^T (inner 32-key blocks) -> [..., d_h, S_pad] in key order."""
+    S_pad = vt.shape[-1]
+    pos = np.arange(S_pad)
+    o = pos & 31
+    c = o >> 2
+    slot = ((((c & 1) << 2) | (c >> 1)) << 2) | (o & 3)
+    src = (pos & ~31) | slot
+    return vt[..., torch.as_tensor(src, device=vt.device)]
+
+
+def upload_weights(w: dict, device, dtype: str) -> dict:
+    """Host arrays from inputs.make_inputs -> device tensors of the ABI dtypes."""
+    td = TORCH_DTYPES[dtype]
+    out = {}
+    for k, v in w.items():
+        if k == "x":
+            continue
+        t = torch.from_numpy(np.ascontiguousarray(v))
+        out[k] = t.to(device=device, dtype=torch.float32 if k in ("w_router", "b_router") else td)
+    return out

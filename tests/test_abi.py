@@ -1,0 +1,107 @@
+"""The C ABI without a GPU: the library loads, exports every entry point declared in
+include/gqe.h, and rejects bad arguments on the host before any device call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_moe_query_amd import gqe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "gqe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("gqe_init", "gqe_forward", "gqe_aux_stats", "gqe_workspace_bytes",
+              "gqe_pack_weights", "gqe_destroy", "gqe_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = gqe.lib()
+    for n in _declared():
+        assert hasattr(L, n), n
+    assert set(_declared()) == set(gqe.EXPORTS)
+
+
+def _cfg(**kw):
+    base = dict(dim=768, num_query_experts=16, num_kv_heads=8, top_k=1, head_dim=0, variant=0,
+                shared_head=1, shared_kv_group=0, dtype=1, causal=1, dense_gqa=0)
+    base.update(kw)
+    return gqe.Config(*[base[f] for f, _ in gqe.Config._fields_])
+
+
+def _weights(**kw):
+    # fake but aligned addresses: gqe_init only validates them and never dereferences
+    base = {f: 0x10000 * (i + 1) for i, (f, _) in enumerate(gqe.Weights._fields_)}
+    base.update(kw)
+    return gqe.Weights(*[base[f] for f, _ in gqe.Weights._fields_])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(num_query_experts=12, num_kv_heads=8), -1, "divisible"),
+    (dict(top_k=0), -1, "top_k"),
+    (dict(top_k=3), -1, "top_k"),
+    (dict(dim=0), -1, "dim"),
+    (dict(dim=8, num_query_experts=16), -1, "head_dim"),
+    (dict(head_dim=-2), -1, "head_dim"),
+    (dict(variant=3), -1, "variant"),
+    (dict(dtype=7), -1, "dtype"),
+    (dict(shared_kv_group=8), -1, "shared_kv_group"),
+    (dict(causal=0), -4, "causal"),
+    (dict(dense_gqa=1), -1, "dense_gqa"),
+    (dict(num_query_experts=128, num_kv_heads=8), -4, "64"),
+    (dict(head_dim=256), -4, "head_dim"),
+])
+def test_init_rejects_bad_configs(kw, code, msg):
+    with pytest.raises(gqe.GqeError) as e:
+        gqe.gqe_init(_cfg(**kw), _weights())
+    assert e.value.code == code
+    assert msg in str(e.value)
+
+
+def test_init_rejects_null_and_misaligned_weights():
+    with pytest.raises(gqe.GqeError) as e:
+        gqe.gqe_init(_cfg(), _weights(w_router=None))
+    assert e.value.code == -2
+    with pytest.raises(gqe.GqeError) as e:
+        gqe.gqe_init(_cfg(), _weights(w_o_rslot=None))
+    assert e.value.code == -2
+    with pytest.raises(gqe.GqeError) as e:
+        gqe.gqe_init(_cfg(), _weights(w_k=0x10008))
+    assert e.value.code == -3
+    # hard_concat needs no renormalised-slot projection, no shared head needs no shared weights
+    h = gqe.gqe_init(_cfg(variant=2, shared_head=0), _weights(w_o_rslot=None, w_q_shared=None,
+                                                              w_o_shared=None))
+    gqe.gqe_destroy(h)
+
+
+def test_host_side_sizes_and_state_errors():
+    h = gqe.gqe_init(_cfg(), _weights())
+    try:
+        ws = gqe.gqe_workspace_bytes(h, 8, 2048)
+        assert ws > 8 * 2048 * 9 * 48 * 2 * 2   # at least Q_act and O_act
+        assert gqe.gqe_packed_weights_bytes(h) >= 768 * 16 * 8
+        with pytest.raises(gqe.GqeError) as e:
+            gqe.gqe_workspace_bytes(h, 0, 10)
+        assert e.value.code == -6
+        offs, dims = gqe.gqe_workspace_layout(h, 2, 100)
+        assert dims[0] == 9 and dims[1] == 128
+        assert len(set(offs)) == 8
+        # forward before the weights are packed -> state error, no device call
+        L = gqe.lib()
+        rc = L.gqe_forward(h, ctypes.c_void_p(0x1000), ctypes.c_void_p(0x200000), 1, 1,
+                           ctypes.c_void_p(0x400000), 1 << 30, None, None, None)
+        assert rc == -8
+        rc = L.gqe_aux_stats(h, None, None, None, None, None)
+        assert rc == -8
+    finally:
+        gqe.gqe_destroy(h)
+    assert gqe.gqe_last_error() == "" or isinstance(gqe.gqe_last_error(), str)
