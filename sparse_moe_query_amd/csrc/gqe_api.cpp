@@ -13,6 +13,8 @@
 #ifndef MFMA_PATH_ENABLED
 #define MFMA_PATH_ENABLED 0
 #endif
+#define MFMA_PROJ_READY 0
+#define MFMA_COMBINE_READY 0
 
 static thread_local char g_err[512] = "";
 
@@ -155,6 +157,9 @@ int gqe_init(const gqe_config_t* cfg, const gqe_weights_t* w, gqe_handle_t** out
     D.skv = c.shared_head ? c.shared_kv_group : 0;
     D.dense = c.dense_gqa;
     h->mfma = mfma_supported(D);
+    h->mfma_attn = D.dtype == GQE_DTYPE_BF16 && (dh == 32 || dh == 48 || dh == 64) && D.H <= 64;
+    h->mfma_proj = h->mfma && MFMA_PROJ_READY;
+    h->mfma_combine = h->mfma && MFMA_COMBINE_READY;
     h->pl = make_packed_layout(D, h->mfma);
     h->packed = nullptr;
     h->ran = false;
@@ -201,7 +206,7 @@ int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size
     offs[7] = P.stats;
     dims[0] = h->D.H;
     dims[1] = P.S_pad;
-    dims[2] = h->mfma ? 1 : 0;
+    dims[2] = (h->mfma_proj ? 1 : 0) | (h->mfma_attn ? 2 : 0) | (h->mfma_combine ? 4 : 0);
     dims[3] = 0;
     return ok();
 }
@@ -230,13 +235,12 @@ int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t 
     hipError_t e = hipSuccess;
     if (!D.dense) e = launch_router(D, P, x, h->packed, h->pl, ws, route_idx, route_w, st);
     if (e == hipSuccess) {
-        if (h->mfma) {
-            e = launch_proj_mfma(D, P, x, h->packed, h->pl, ws, st);
-            if (e == hipSuccess) e = launch_attn_mfma(D, P, ws, st);
-            if (e == hipSuccess) e = launch_combine_mfma(D, P, h->packed, h->pl, y, ws, st);
-        } else {
-            e = launch_simple_forward(D, P, h->w, x, y, ws, st);
-        }
+        e = h->mfma_proj ? launch_proj_mfma(D, P, x, h->packed, h->pl, ws, st)
+                         : launch_proj_simple(D, P, h->w, x, ws, st);
+        if (e == hipSuccess) e = h->mfma_attn ? launch_attn_mfma(D, P, ws, st) : launch_attn_simple(D, P, ws, st);
+        if (e == hipSuccess)
+            e = h->mfma_combine ? launch_combine_mfma(D, P, h->packed, h->pl, y, ws, st)
+                                : launch_combine_simple(D, P, h->w, y, ws, st);
     }
     if (e != hipSuccess) return fail(GQE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     h->ran = true;

@@ -38,6 +38,7 @@ struct gqe_handle {
     gqe_weights_t w;
     GqeDims D;
     bool mfma;             // bf16 matrix-core path available for this config
+    bool mfma_proj, mfma_attn, mfma_combine;  // per stage
     PackedLayout pl;
     void* packed;          // set by gqe_pack_weights
     // last forward (for gqe_aux_stats)
@@ -55,8 +56,11 @@ hipError_t launch_pack(const GqeDims& D, const gqe_weights_t& w, const PackedLay
 hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, const void* packed,
                          const PackedLayout& pl, char* ws, int32_t* route_idx, float* route_w,
                          hipStream_t st);
-hipError_t launch_simple_forward(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w,
-                                 const void* x, void* y, char* ws, hipStream_t st);
+hipError_t launch_proj_simple(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w,
+                              const void* x, char* ws, hipStream_t st);
+hipError_t launch_attn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st);
+hipError_t launch_combine_simple(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w,
+                                 void* y, char* ws, hipStream_t st);
 hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x,
                             const void* packed, const PackedLayout& pl, char* ws,
                             hipStream_t st);

@@ -5,7 +5,6 @@
 hipError_t launch_proj_mfma(const GqeDims&, const WorkPlan&, const void*, const void*, const PackedLayout&, char*, hipStream_t) {
     return hipErrorNotSupported;
 }
-hipError_t launch_attn_mfma(const GqeDims&, const WorkPlan&, char*, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_combine_mfma(const GqeDims&, const WorkPlan&, const void*, const PackedLayout&, void*, char*, hipStream_t) {
     return hipErrorNotSupported;
 }

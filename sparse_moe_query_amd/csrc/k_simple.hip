@@ -139,32 +139,49 @@ __global__ void combine_simple_kernel(Args a, const T* __restrict__ O, const int
 }
 
 template <typename T>
-hipError_t run(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w, const void* x, void* y,
-               char* ws, hipStream_t st) {
-    Args a{P.B, P.S, P.T, P.S_pad, D.d, D.N, D.G, D.k, D.n, D.dh, D.H, D.s, D.skv, D.variant, D.dense};
-    T* Q = (T*)(ws + P.q);
-    T* K = (T*)(ws + P.kk);
-    T* Vt = (T*)(ws + P.vt);
-    T* O = (T*)(ws + P.o);
-    const int32_t* idx = (const int32_t*)(ws + P.idx);
+Args make_args(const GqeDims& D, const WorkPlan& P) {
+    return Args{P.B, P.S, P.T, P.S_pad, D.d, D.N, D.G, D.k, D.n, D.dh, D.H, D.s, D.skv, D.variant, D.dense};
+}
+
+template <typename T>
+hipError_t proj(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w, const void* x, char* ws,
+                hipStream_t st) {
+    const Args a = make_args<T>(D, P);
     const int64_t C = (int64_t)(2 * D.G + D.s + D.G * D.k) * D.dh;
     proj_simple_kernel<T><<<(unsigned)ceil_div(P.T * C, 256), 256, 0, st>>>(
-        a, (const T*)x, (const T*)w.w_k, (const T*)w.w_v, (const T*)w.w_q_shared, (const T*)w.w_q, idx, Q, K, Vt);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    attn_simple_kernel<T><<<(unsigned)ceil_div(P.B * D.H * P.S, 128), 128, 0, st>>>(a, Q, K, Vt, O);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+        a, (const T*)x, (const T*)w.w_k, (const T*)w.w_v, (const T*)w.w_q_shared, (const T*)w.w_q,
+        (const int32_t*)(ws + P.idx), (T*)(ws + P.q), (T*)(ws + P.kk), (T*)(ws + P.vt));
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t attn(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st) {
+    const Args a = make_args<T>(D, P);
+    attn_simple_kernel<T><<<(unsigned)ceil_div(P.B * D.H * P.S, 128), 128, 0, st>>>(
+        a, (const T*)(ws + P.q), (const T*)(ws + P.kk), (const T*)(ws + P.vt), (T*)(ws + P.o));
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t combine(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w, void* y, char* ws,
+                   hipStream_t st) {
+    const Args a = make_args<T>(D, P);
     combine_simple_kernel<T><<<(unsigned)ceil_div(P.T * D.d, 256), 256, 0, st>>>(
-        a, O, idx, (const float*)(ws + P.wsel), (const float*)(ws + P.psel), (const T*)w.w_o,
-        (const T*)w.w_o_rslot, (const T*)w.w_o_shared, (T*)y);
+        a, (const T*)(ws + P.o), (const int32_t*)(ws + P.idx), (const float*)(ws + P.wsel),
+        (const float*)(ws + P.psel), (const T*)w.w_o, (const T*)w.w_o_rslot, (const T*)w.w_o_shared, (T*)y);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_simple_forward(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w,
-                                 const void* x, void* y, char* ws, hipStream_t st) {
-    if (D.dtype == GQE_DTYPE_BF16) return run<bf16_t>(D, P, w, x, y, ws, st);
-    return run<float>(D, P, w, x, y, ws, st);
+hipError_t launch_proj_simple(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w, const void* x,
+                              char* ws, hipStream_t st) {
+    return D.dtype == GQE_DTYPE_BF16 ? proj<bf16_t>(D, P, w, x, ws, st) : proj<float>(D, P, w, x, ws, st);
+}
+hipError_t launch_attn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st) {
+    return D.dtype == GQE_DTYPE_BF16 ? attn<bf16_t>(D, P, ws, st) : attn<float>(D, P, ws, st);
+}
+hipError_t launch_combine_simple(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w, void* y,
+                                 char* ws, hipStream_t st) {
+    return D.dtype == GQE_DTYPE_BF16 ? combine<bf16_t>(D, P, w, y, ws, st) : combine<float>(D, P, w, y, ws, st);
 }
