@@ -168,6 +168,14 @@ int gqe_aux_stats(gqe_handle_t* h, void* stream, int64_t* counts, double* mean_p
 int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t offs[8],
                          int64_t dims[4]);
 
+/* Stage timing for measurement.  While enabled, gqe_forward records HIP events on its stream
+ * around each of its kernels (stage 0 router, 1 projections, 2 attention, 3 combine + output
+ * projection).  gqe_profile_read waits for the recorded events, returns the summed milliseconds
+ * per stage and the number of forwards they cover, and starts a new accumulation.
+ * Not re-entrant; costs four event records per forward while enabled. */
+int gqe_profile_enable(gqe_handle_t* h, int enable);
+int gqe_profile_read(gqe_handle_t* h, double stage_ms[4], int64_t* forwards);
+
 /* Destroys the handle (host memory only).  NULL is ignored. */
 void gqe_destroy(gqe_handle_t* h);
 

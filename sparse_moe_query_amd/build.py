@@ -16,7 +16,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU instructions.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-munsafe-fp-atomics", "-DMFMA_PATH_ENABLED=%d" % int(os.environ.get("GQE_BUILD_MFMA", "0"))]
+         "-munsafe-fp-atomics", "-DMFMA_PATH_ENABLED=%d" % int(os.environ.get("GQE_BUILD_MFMA", "1"))]
 
 
 def _compile(src: str) -> str:

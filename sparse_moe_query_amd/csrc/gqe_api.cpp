@@ -13,8 +13,7 @@
 #ifndef MFMA_PATH_ENABLED
 #define MFMA_PATH_ENABLED 0
 #endif
-#define MFMA_PROJ_READY 0
-#define MFMA_COMBINE_READY 0
+
 
 static thread_local char g_err[512] = "";
 
@@ -74,9 +73,10 @@ PackedLayout make_packed_layout(const GqeDims& D, bool mfma) {
     L.br64 = take((size_t)D.N * 8);
     L.hb_total = 2 * D.G + D.s + D.N;
     L.slots = D.dense ? D.N : D.N + (D.variant == GQE_VARIANT_GQE ? D.G : 0) + D.s;
+    L.ktot_pad = (int)round_up((int64_t)L.slots * D.dh, 32);
     if (mfma) {
         L.wproj = take((size_t)L.hb_total * D.dh * D.d * 2);
-        L.wo = take((size_t)D.d * L.slots * D.dh * 2);
+        L.wo = take((size_t)D.d * L.ktot_pad * 2);
     } else {
         L.wproj = L.wo = 0;
     }
@@ -158,8 +158,8 @@ int gqe_init(const gqe_config_t* cfg, const gqe_weights_t* w, gqe_handle_t** out
     D.dense = c.dense_gqa;
     h->mfma = mfma_supported(D);
     h->mfma_attn = D.dtype == GQE_DTYPE_BF16 && (dh == 32 || dh == 48 || dh == 64) && D.H <= 64;
-    h->mfma_proj = h->mfma && MFMA_PROJ_READY;
-    h->mfma_combine = h->mfma && MFMA_COMBINE_READY;
+    h->mfma_proj = h->mfma;
+    h->mfma_combine = h->mfma && D.d % 128 == 0;
     h->pl = make_packed_layout(D, h->mfma);
     h->packed = nullptr;
     h->ran = false;
@@ -233,15 +233,35 @@ int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t 
     hipStream_t st = (hipStream_t)stream;
     char* ws = (char*)workspace;
     hipError_t e = hipSuccess;
+    hipEvent_t* ev = nullptr;
+    if (h->prof) {
+        if (h->prof_used + 5 > h->prof_ev.size()) {
+            for (int i = 0; i < 5 && e == hipSuccess; ++i) {
+                hipEvent_t x0;
+                e = hipEventCreate(&x0);
+                if (e == hipSuccess) h->prof_ev.push_back(x0);
+            }
+            if (e != hipSuccess) return fail(GQE_ERR_HIP, "event creation failed: %s", hipGetErrorString(e));
+        }
+        ev = &h->prof_ev[h->prof_used];
+        h->prof_used += 5;
+    }
+    auto mark = [&](int i) {
+        if (ev && e == hipSuccess) e = hipEventRecord(ev[i], st);
+    };
+    mark(0);
     if (!D.dense) e = launch_router(D, P, x, h->packed, h->pl, ws, route_idx, route_w, st);
-    if (e == hipSuccess) {
+    mark(1);
+    if (e == hipSuccess)
         e = h->mfma_proj ? launch_proj_mfma(D, P, x, h->packed, h->pl, ws, st)
                          : launch_proj_simple(D, P, h->w, x, ws, st);
-        if (e == hipSuccess) e = h->mfma_attn ? launch_attn_mfma(D, P, ws, st) : launch_attn_simple(D, P, ws, st);
-        if (e == hipSuccess)
-            e = h->mfma_combine ? launch_combine_mfma(D, P, h->packed, h->pl, y, ws, st)
-                                : launch_combine_simple(D, P, h->w, y, ws, st);
-    }
+    mark(2);
+    if (e == hipSuccess) e = h->mfma_attn ? launch_attn_mfma(D, P, ws, st) : launch_attn_simple(D, P, ws, st);
+    mark(3);
+    if (e == hipSuccess)
+        e = h->mfma_combine ? launch_combine_mfma(D, P, h->packed, h->pl, y, ws, st)
+                            : launch_combine_simple(D, P, h->w, y, ws, st);
+    mark(4);
     if (e != hipSuccess) return fail(GQE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     h->ran = true;
     h->last_ws = workspace;
@@ -283,6 +303,37 @@ int gqe_aux_stats(gqe_handle_t* h, void* stream, int64_t* counts, double* mean_p
     return ok();
 }
 
-void gqe_destroy(gqe_handle_t* h) { delete h; }
+int gqe_profile_enable(gqe_handle_t* h, int enable) {
+    if (!h) return fail(GQE_ERR_NULL_POINTER, "handle must be non-NULL");
+    h->prof = enable != 0;
+    h->prof_used = 0;
+    return ok();
+}
+
+int gqe_profile_read(gqe_handle_t* h, double stage_ms[4], int64_t* forwards) {
+    if (!h || !stage_ms) return fail(GQE_ERR_NULL_POINTER, "handle and stage_ms must be non-NULL");
+    for (int i = 0; i < 4; ++i) stage_ms[i] = 0.0;
+    const size_t n = h->prof_used / 5;
+    for (size_t f = 0; f < n; ++f) {
+        hipEvent_t* ev = &h->prof_ev[5 * f];
+        hipError_t e = hipEventSynchronize(ev[4]);
+        if (e != hipSuccess) return fail(GQE_ERR_HIP, "event wait failed: %s", hipGetErrorString(e));
+        for (int i = 0; i < 4; ++i) {
+            float ms = 0.f;
+            e = hipEventElapsedTime(&ms, ev[i], ev[i + 1]);
+            if (e != hipSuccess) return fail(GQE_ERR_HIP, "event timing failed: %s", hipGetErrorString(e));
+            stage_ms[i] += ms;
+        }
+    }
+    if (forwards) *forwards = (int64_t)n;
+    h->prof_used = 0;
+    return ok();
+}
+
+void gqe_destroy(gqe_handle_t* h) {
+    if (!h) return;
+    for (hipEvent_t e : h->prof_ev) (void)hipEventDestroy(e);
+    delete h;
+}
 
 }  // extern "C"

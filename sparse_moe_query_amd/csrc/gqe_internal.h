@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "../../include/gqe.h"
 
 struct GqeDims {
@@ -20,6 +22,7 @@ struct PackedLayout {
     size_t total;
     int hb_total;        // number of projection head blocks
     int slots;           // output-projection slots (expert slots, renormalised slots, shared)
+    int ktot_pad;        // slots * dh rounded up to 32 (zero columns past the last slot)
 };
 
 // Byte offsets into the caller's workspace for one [B, S] forward.
@@ -45,6 +48,10 @@ struct gqe_handle {
     bool ran;
     void* last_ws;
     WorkPlan last_plan;
+    // stage timing (gqe_profile_enable)
+    bool prof = false;
+    std::vector<hipEvent_t> prof_ev;  // 5 events per recorded forward
+    size_t prof_used = 0;
 };
 
 WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S);

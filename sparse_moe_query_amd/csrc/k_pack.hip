@@ -50,8 +50,8 @@ __global__ void pack_proj_kernel(const uint16_t* __restrict__ wk, const uint16_t
 // dst[col][slot * dh + j] = W_slot[j][col]
 __global__ void pack_wo_kernel(const uint16_t* __restrict__ wo, const uint16_t* __restrict__ wor,
                                const uint16_t* __restrict__ wos, int d, int G, int n, int dh,
-                               int rslot, int s, int slots, uint16_t* __restrict__ dst) {
-    const int64_t K = (int64_t)slots * dh;
+                               int rslot, int s, int slots, int ktot_pad, uint16_t* __restrict__ dst) {
+    const int64_t K = ktot_pad;
     const int64_t total = (int64_t)d * K;
     const int per_group = n + rslot;
     for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
@@ -60,7 +60,9 @@ __global__ void pack_wo_kernel(const uint16_t* __restrict__ wo, const uint16_t* 
         const int64_t kk = q % K;
         const int slot = (int)(kk / dh), j = (int)(kk % dh);
         uint16_t v;
-        if (slot < G * per_group) {
+        if (slot >= slots) {
+            v = 0;  // padding up to a multiple of 32 columns
+        } else if (slot < G * per_group) {
             const int g = slot / per_group, u = slot % per_group;
             if (u < n) v = wo[((int64_t)(g * n + u) * dh + j) * d + col];
             else v = wor[((int64_t)g * dh + j) * d + col];
@@ -91,6 +93,6 @@ hipError_t launch_pack(const GqeDims& D, const gqe_weights_t& w, const PackedLay
     const int rslot = (!D.dense && D.variant == GQE_VARIANT_GQE) ? 1 : 0;
     pack_wo_kernel<<<1024, 256, 0, st>>>((const uint16_t*)w.w_o, (const uint16_t*)w.w_o_rslot,
                                          (const uint16_t*)w.w_o_shared, D.d, D.G, D.n, D.dh, rslot,
-                                         D.s, pl.slots, (uint16_t*)(pk + pl.wo));
+                                         D.s, pl.slots, pl.ktot_pad, (uint16_t*)(pk + pl.wo));
     return hipGetLastError();
 }

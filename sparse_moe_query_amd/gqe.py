@@ -24,8 +24,9 @@ ERRORS = {0: "GQE_OK", -1: "GQE_ERR_INVALID_CONFIG", -2: "GQE_ERR_NULL_POINTER",
           -3: "GQE_ERR_MISALIGNED", -4: "GQE_ERR_UNSUPPORTED", -5: "GQE_ERR_WORKSPACE",
           -6: "GQE_ERR_SHAPE", -7: "GQE_ERR_HIP", -8: "GQE_ERR_STATE"}
 EXPORTS = ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights", "gqe_workspace_bytes",
-           "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_destroy",
-           "gqe_last_error")
+           "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_profile_enable",
+           "gqe_profile_read", "gqe_destroy", "gqe_last_error")
+STAGES = ("router", "projection", "attention", "combine")
 
 
 class GqeError(RuntimeError):
@@ -65,12 +66,15 @@ def lib():
         L.gqe_forward.argtypes = [P, P, P, I64, I64, P, SZ, P, P, P]
         L.gqe_aux_stats.argtypes = [P, P, P, P, P, P]
         L.gqe_workspace_layout.argtypes = [P, I64, I64, P, P]
+        L.gqe_profile_enable.argtypes = [P, ctypes.c_int]
+        L.gqe_profile_read.argtypes = [P, P, P]
         L.gqe_destroy.argtypes = [P]
         L.gqe_destroy.restype = None
         L.gqe_last_error.argtypes = []
         L.gqe_last_error.restype = ctypes.c_char_p
         for f in ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights",
-                  "gqe_workspace_bytes", "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout"):
+                  "gqe_workspace_bytes", "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout",
+                  "gqe_profile_enable", "gqe_profile_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -143,6 +147,17 @@ def gqe_workspace_layout(h, batch: int, seq: int):
     dims = (ctypes.c_int64 * 4)()
     _check(lib().gqe_workspace_layout(h, batch, seq, offs, dims))
     return list(offs), list(dims)
+
+
+def gqe_profile_enable(h, enable: bool):
+    _check(lib().gqe_profile_enable(h, int(enable)))
+
+
+def gqe_profile_read(h):
+    ms = (ctypes.c_double * 4)()
+    n = ctypes.c_int64()
+    _check(lib().gqe_profile_read(h, ms, ctypes.byref(n)))
+    return dict(zip(STAGES, list(ms))), n.value
 
 
 def gqe_destroy(h):
