@@ -69,7 +69,7 @@ PackedLayout make_packed_layout(const GqeDims& D, bool mfma) {
         off = align256(off + bytes);
         return o;
     };
-    L.wr64 = take((size_t)D.d * D.N * 8);
+    L.wr64 = take((size_t)D.d * round_up(D.N, 16) * 8);
     L.br64 = take((size_t)D.N * 8);
     L.hb_total = 2 * D.G + D.s + D.N;
     L.slots = D.dense ? D.N : D.N + (D.variant == GQE_VARIANT_GQE ? D.G : 0) + D.s;

@@ -16,7 +16,7 @@ struct GqeDims {
 
 // Byte offsets into the caller's packed-weights buffer.
 struct PackedLayout {
-    size_t wr64, br64;   // router weights [d][N] and bias [N] widened to float64
+    size_t wr64, br64;   // router weights in float64 (d x N rounded up to 16) and biases
     size_t wproj;        // bf16 path: head blocks [HB][dh][d] (K_g, V_g, shared Q, W_q[e])
     size_t wo;           // bf16 path: stacked output projection [d][Ktot], Ktot = slots * dh
     size_t total;
@@ -55,6 +55,7 @@ struct gqe_handle {
 };
 
 WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S);
+bool router_uses_mfma(const GqeDims& D);
 PackedLayout make_packed_layout(const GqeDims& D, bool mfma);
 
 // ---------------------------------------------------------------- launchers (return hipError_t)

@@ -1,5 +1,5 @@
 // Weight repacking (layout only, no arithmetic of the layer):
-//  - the router projection and bias widened to float64 (exact) for the float64 logit sums;
+//  - the router weights widened to float64 (exact) in the lane order of the router kernel;
 //  - bf16 path: every projection head block transposed to [d_h][d] so that each matrix-core
 //    lane reads eight consecutive hidden-dimension values with one 16-byte load;
 //  - bf16 path: the output projections stacked into one [d][slots * d_h] matrix, slot order
@@ -10,20 +10,34 @@
 
 namespace {
 
-__global__ void widen_router_kernel(const float* __restrict__ w, const float* __restrict__ b,
-                                    int64_t dn, int N, double* __restrict__ w64,
-                                    double* __restrict__ b64) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < dn) w64[i] = w ? (double)w[i] : 0.0;
-    if (i < N) b64[i] = b ? (double)b[i] : 0.0;
+// Router weights in float64 (exact widening of float32), zero-padded to Np = 16*NB columns:
+//  lane order (matrix-core router): dst[o][cb][c][s] = W_r[8o + s][16cb + c]
+//  plain (generic router):          dst[i][c]        = W_r[i][c]
+__global__ void pack_router_kernel(const float* __restrict__ w, const float* __restrict__ b, int d,
+                                   int N, int Np, int lane_order, double* __restrict__ dst,
+                                   double* __restrict__ bd) {
+    const int64_t total = (int64_t)d * Np;
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q < total) {
+        int i, c;
+        if (lane_order) {
+            const int s = (int)(q % 8);
+            const int64_t r = q / 8;
+            const int col = (int)(r % 16);
+            const int64_t r2 = r / 16;
+            const int NB = Np / 16;
+            const int cb = (int)(r2 % NB);
+            const int o = (int)(r2 / NB);
+            i = 8 * o + s;
+            c = 16 * cb + col;
+        } else {
+            i = (int)(q / Np);
+            c = (int)(q % Np);
+        }
+        dst[q] = (w && c < N) ? (double)w[(int64_t)i * N + c] : 0.0;
+    }
+    if (q < N) bd[q] = b ? (double)b[q] : 0.0;
 }
-
-// dst[hb][j][i] = src_hb[i * ld + col0 + j]   (16-bit elements)
-struct HeadBlockSrc {
-    const uint16_t* base;
-    int64_t ld;
-    int64_t col0;
-};
 
 __global__ void pack_proj_kernel(const uint16_t* __restrict__ wk, const uint16_t* __restrict__ wv,
                                  const uint16_t* __restrict__ wqs, const uint16_t* __restrict__ wq,
@@ -79,10 +93,11 @@ __global__ void pack_wo_kernel(const uint16_t* __restrict__ wo, const uint16_t* 
 hipError_t launch_pack(const GqeDims& D, const gqe_weights_t& w, const PackedLayout& pl,
                        void* packed, bool mfma, hipStream_t st) {
     char* pk = (char*)packed;
-    const int64_t dn = (int64_t)D.d * D.N;
-    const int64_t m = dn > D.N ? dn : D.N;
-    widen_router_kernel<<<(unsigned)ceil_div(m, 256), 256, 0, st>>>(
-        w.w_router, w.b_router, dn, D.N, (double*)(pk + pl.wr64), (double*)(pk + pl.br64));
+    const int Np = (int)round_up(D.N, 16);
+    const int64_t m = (int64_t)D.d * Np + D.N;
+    pack_router_kernel<<<(unsigned)ceil_div(m, 256), 256, 0, st>>>(
+        w.w_router, w.b_router, D.d, D.N, Np, router_uses_mfma(D) ? 1 : 0, (double*)(pk + pl.wr64),
+        (double*)(pk + pl.br64));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !mfma) return e;
     pack_proj_kernel<<<1024, 256, 0, st>>>((const uint16_t*)w.w_k, (const uint16_t*)w.w_v,

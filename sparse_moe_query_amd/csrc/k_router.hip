@@ -5,22 +5,50 @@
 // a Switch-style load-balancing auxiliary loss.  Tutorial "Mixture of experts (MoE)": the router
 // scores are x @ router_w; the chosen experts are mixed by renormalised router weights.
 //
-// Precision: the routing decision is an integer result decided by floating point, so the logits
-// are accumulated in float64 (fp64 FMA is full rate on gfx950); the selection compares float64
-// logits (softmax is monotone, so top-k of the logits is top-k of the probabilities).  Equal
-// logits resolve to the lower local index.
+// The routing decision is an integer result decided by floating point, so the logits are summed
+// in float64; top-k compares the float64 logits (softmax is monotone) and equal logits resolve to
+// the lower local index.
+//
+// Fast path (d % 64 == 0, N <= 16): v_mfma_f64_16x16x4_f64 (full-rate fp64 on gfx950).  A block
+// owns 64 tokens; wave w of 8 sums the w-th eighth of the hidden dimension for all of them.  Each lane
+// loads eight consecutive hidden values of one token with one 16-byte load; the k index of the
+// MFMA is permuted accordingly (k-step s of lane group q covers hidden index 8q + s), and the
+// router weights are pre-permuted into exactly that lane order ([octet of 8 hidden indices]
+// [column][8], by gqe_pack_weights), so the B operands are 64 contiguous bytes per lane.  The
+// eight partial sums are added in a fixed order.
+// Generic path (any d, N <= 64): one token per lane, float64 FMAs with the weights as wave-uniform
+// scalar operands.
 #include "gqe_common.h"
 #include "gqe_internal.h"
 
 namespace {
 
-constexpr int kTok = 64;     // tokens per block (one per lane)
-constexpr int kEChunk = 16;  // experts accumulated per pass over x
+constexpr int kTok = 64;  // tokens per block
+
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+// Read-only, wave-uniform weights: the constant address space lets them come through the scalar
+// cache as SGPR operands.
+typedef const __attribute__((address_space(4))) double* const_f64_ptr;
+
+struct RouterArgs {
+    const void* x;
+    const double* wr;    // generic: [d][Np] zero padded; fast: lane-ordered blocks
+    const double* br;    // [N]
+    int64_t T;
+    int d, N, G, k, n, Np;  // Np = N rounded up to 16
+    int32_t* idx;
+    float* wsel;
+    float* psel;
+    int32_t* ridx;
+    float* rw;
+    int32_t* part_cnt;
+    double* part_psum;
+};
 
 template <typename Tin>
-__device__ __forceinline__ void load8(const Tin* p, double* v);
+__device__ __forceinline__ void widen8(const Tin* p, double* v);
 template <>
-__device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, double* v) {
+__device__ __forceinline__ void widen8<bf16_t>(const bf16_t* p, double* v) {
     const u32x4_t q = *reinterpret_cast<const u32x4_t*>(p);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -29,7 +57,7 @@ __device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, double* v) {
     }
 }
 template <>
-__device__ __forceinline__ void load8<float>(const float* p, double* v) {
+__device__ __forceinline__ void widen8<float>(const float* p, double* v) {
     const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
     const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
 #pragma unroll
@@ -39,139 +67,191 @@ __device__ __forceinline__ void load8<float>(const float* p, double* v) {
     }
 }
 
-// Block: 256 threads = 4 waves; 64 tokens (lane = token); wave w accumulates the w-th quarter of
-// the hidden dimension, the four partial sums are added in a fixed order.
-template <typename Tin, bool kVec>
-__global__ void __launch_bounds__(256) router_kernel(
-    const Tin* __restrict__ x, const double* __restrict__ wr, const double* __restrict__ br,
-    int64_t T, int d, int N, int G, int k, int32_t* __restrict__ idx, float* __restrict__ wsel,
-    float* __restrict__ psel, int32_t* __restrict__ ridx, float* __restrict__ rw,
-    int32_t* __restrict__ part_cnt, double* __restrict__ part_psum) {
-    __shared__ double red[4][kTok][kEChunk + 1];
+// Softmax, top-k and weights for the block's tokens; logits in lg[tok][e] (bias included).
+// The selection compares the float64 logits; the probabilities are formed from the float64
+// differences l - max with the float32 exponential (relative error ~1e-7), and overwrite the
+// logits of the same (token, group).  Per-block statistics follow.
+__device__ void select_and_stats(const RouterArgs& a, double (*lg)[65], int* cnt, int64_t t0, int nthreads) {
+    const int n = a.n, G = a.G, k = a.k;
+    for (int q = threadIdx.x; q < kTok * G; q += nthreads) {
+        const int tok = q / G, g = q % G;
+        const int64_t tt = t0 + tok;
+        if (tt >= a.T) continue;
+        double* l = &lg[tok][g * n];
+        double m = l[0];
+        for (int j = 1; j < n; ++j) m = fmax(m, l[j]);
+        uint64_t taken = 0, sel = 0;  // sel: 4 bits per rank (n <= 16)
+        for (int r = 0; r < k; ++r) {
+            int best = -1;
+            for (int j = 0; j < n; ++j)
+                if (!((taken >> j) & 1) && (best < 0 || l[j] > l[best])) best = j;
+            taken |= (uint64_t)1 << best;
+            sel |= (uint64_t)best << (4 * r);
+        }
+        float den = 0.f;
+        for (int j = 0; j < n; ++j) den += expf((float)(l[j] - m));
+        const float inv = 1.0f / den;
+        for (int j = 0; j < n; ++j) l[j] = (double)(expf((float)(l[j] - m)) * inv);  // probabilities
+        double ps = 0.0;
+        for (int r = 0; r < k; ++r) ps += l[(sel >> (4 * r)) & 15];
+        const int64_t o = (tt * G + g) * k;
+        for (int r = 0; r < k; ++r) {
+            const int j = (int)((sel >> (4 * r)) & 15);
+            const int e = g * n + j;
+            const double p = l[j];
+            a.idx[o + r] = e;
+            a.wsel[o + r] = (float)(p / ps);
+            a.psel[o + r] = (float)p;
+            if (a.ridx) a.ridx[o + r] = e;
+            if (a.rw) a.rw[o + r] = (float)(p / ps);
+            atomicAdd(&cnt[e], 1);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < a.N) {
+        const int e = threadIdx.x;
+        double s = 0.0;
+        for (int tok = 0; tok < kTok; ++tok)
+            if (t0 + tok < a.T) s += lg[tok][e];
+        a.part_psum[(int64_t)blockIdx.x * a.N + e] = s;
+        a.part_cnt[(int64_t)blockIdx.x * a.N + e] = cnt[e];
+    }
+}
+
+template <typename Tin>
+__global__ void __launch_bounds__(512) router_mfma_kernel(RouterArgs a) {
+    constexpr int kW = 8;  // waves; wave w sums the w-th eighth of the hidden dimension
+    __shared__ double red[kW][kTok][17];
+    __shared__ double lg[kTok][65];
+    __shared__ int cnt[64];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t t0 = (int64_t)blockIdx.x * kTok;
+    if (threadIdx.x < 64) cnt[threadIdx.x] = 0;
+
+    const int dq = a.d / kW;            // multiple of 8 (d % 64 == 0)
+    const int nchunk = (dq + 31) / 32;  // 32-wide hidden chunks of this wave's share
+    f64x4_t acc[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) acc[tb] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    const Tin* xb = reinterpret_cast<const Tin*>(a.x);
+    for (int c = 0; c < nchunk; ++c) {
+        const int i0 = wv * dq + 32 * c;          // first hidden index of the chunk
+        const int ivalid = min(32, dq - 32 * c);  // hidden values of the chunk inside this share
+        double xv[4][8];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            int64_t t = t0 + 16 * tb + (lane & 15);
+            if (t >= a.T) t = a.T - 1;
+            if (8 * (lane >> 4) < ivalid) {
+                widen8<Tin>(xb + t * a.d + i0 + 8 * (lane >> 4), xv[tb]);
+            } else {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) xv[tb][s] = 0.0;
+            }
+        }
+        // lane-ordered weights [octet][column][8]: this lane's octet of hidden indices is
+        // i0/8 + (lane >> 4) (clamped: past the end x is zero), its column lane & 15
+        const int oct = min(i0 / 8 + (lane >> 4), a.d / 8 - 1);
+        const f64x4_t* wp = reinterpret_cast<const f64x4_t*>(a.wr + ((int64_t)oct * 16 + (lane & 15)) * 8);
+        const f64x4_t w0 = wp[0], w1 = wp[1];
+        const double wv8[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                acc[tb] = __builtin_amdgcn_mfma_f64_16x16x4f64(xv[tb][s], wv8[s], acc[tb], 0, 0, 0);
+    }
+    // C layout of v_mfma_f64_16x16x4: lane holds rows (lane >> 4) + 4i, column lane & 15
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wv][16 * tb + (lane >> 4) + 4 * i][lane & 15] = acc[tb][i];
+    __syncthreads();
+    for (int q = threadIdx.x; q < kTok * a.N; q += 64 * kW) {
+        const int tok = q / a.N, e = q % a.N;
+        double v = red[0][tok][e];
+#pragma unroll
+        for (int w = 1; w < kW; ++w) v += red[w][tok][e];
+        lg[tok][e] = v + a.br[e];
+    }
+    __syncthreads();
+    select_and_stats(a, lg, cnt, t0, 64 * kW);
+}
+
+template <typename Tin>
+__global__ void __launch_bounds__(256) router_valu_kernel(RouterArgs a) {
+    __shared__ double red[4][kTok][17];
     __shared__ double lg[kTok][65];
     __shared__ int cnt[64];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t t0 = (int64_t)blockIdx.x * kTok;
     const int64_t t = t0 + lane;
-    const bool valid = t < T;
-    const int n = N / G;
+    const bool valid = t < a.T;
     if (threadIdx.x < 64) cnt[threadIdx.x] = 0;
-
-    const int dq = kVec ? d / 4 : (d + 3) / 4;
-    const int i0 = min(d, wv * dq), i1 = min(d, i0 + dq);
-    const Tin* xr = x + (valid ? t : (int64_t)0) * d;
-
-    for (int e0 = 0; e0 < N; e0 += kEChunk) {
-        double acc[kEChunk];
+    const int dq = (a.d + 3) / 4;
+    const int i0 = min(a.d, wv * dq), i1 = min(a.d, i0 + dq);
+    const Tin* xr = reinterpret_cast<const Tin*>(a.x) + (valid ? t : (int64_t)0) * a.d;
+    for (int e0 = 0; e0 < a.Np; e0 += 16) {
+        double acc[16];
 #pragma unroll
-        for (int j = 0; j < kEChunk; ++j) acc[j] = 0.0;
-        if (kVec) {
-            for (int i = i0; i < i1; i += 8) {
-                double xv[8];
-                load8<Tin>(xr + i, xv);
+        for (int j = 0; j < 16; ++j) acc[j] = 0.0;
+        for (int i = i0; i < i1; ++i) {
+            const double xv = (double)to_f32(xr[i]);
+            const_f64_ptr wrow = (const_f64_ptr)(a.wr + (int64_t)i * a.Np + e0);
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const double* wrow = wr + (size_t)(i + u) * N + e0;
-#pragma unroll
-                    for (int j = 0; j < kEChunk; ++j)
-                        if (e0 + j < N) acc[j] = __builtin_fma(xv[u], wrow[j], acc[j]);
-                }
-            }
-        } else {
-            for (int i = i0; i < i1; ++i) {
-                const double xv = (double)to_f32(xr[i]);
-                const double* wrow = wr + (size_t)i * N + e0;
-#pragma unroll
-                for (int j = 0; j < kEChunk; ++j)
-                    if (e0 + j < N) acc[j] = __builtin_fma(xv, wrow[j], acc[j]);
-            }
+            for (int j = 0; j < 16; ++j) acc[j] = __builtin_fma(xv, wrow[j], acc[j]);
         }
 #pragma unroll
-        for (int j = 0; j < kEChunk; ++j) red[wv][lane][j] = acc[j];
+        for (int j = 0; j < 16; ++j) red[wv][lane][j] = acc[j];
         __syncthreads();
-        for (int q = threadIdx.x; q < kTok * kEChunk; q += 256) {
-            const int tok = q / kEChunk, j = q % kEChunk;
-            if (e0 + j < N)
-                lg[tok][e0 + j] = ((red[0][tok][j] + red[1][tok][j]) + red[2][tok][j]) + red[3][tok][j] +
-                                  (br ? br[e0 + j] : 0.0);
+        for (int q = threadIdx.x; q < kTok * 16; q += 256) {
+            const int tok = q / 16, j = q % 16;
+            if (e0 + j < a.N)
+                lg[tok][e0 + j] = ((red[0][tok][j] + red[1][tok][j]) + red[2][tok][j]) + red[3][tok][j] + a.br[e0 + j];
         }
         __syncthreads();
     }
-
-    // one (token, group) pair per thread: softmax, top-k, renormalised weights
-    for (int q = threadIdx.x; q < kTok * G; q += 256) {
-        const int tok = q / G, g = q % G;
-        const int64_t tt = t0 + tok;
-        if (tt >= T) continue;
-        const double* l = &lg[tok][g * n];
-        double m = l[0];
-        for (int j = 1; j < n; ++j) m = fmax(m, l[j]);
-        double den = 0.0;
-        for (int j = 0; j < n; ++j) den += exp(l[j] - m);
-        uint64_t taken = 0;
-        double ps = 0.0;
-        for (int r = 0; r < k; ++r) {
-            int best = -1;
-            for (int j = 0; j < n; ++j)
-                if (!((taken >> j) & 1) && (best < 0 || l[j] > l[best])) best = j;
-            taken |= (uint64_t)1 << best;
-            ps += exp(l[best] - m) / den;
-        }
-        taken = 0;
-        const int64_t o = (tt * G + g) * k;
-        for (int r = 0; r < k; ++r) {
-            int best = -1;
-            for (int j = 0; j < n; ++j)
-                if (!((taken >> j) & 1) && (best < 0 || l[j] > l[best])) best = j;
-            taken |= (uint64_t)1 << best;
-            const double p = exp(l[best] - m) / den;
-            const int e = g * n + best;
-            idx[o + r] = e;
-            wsel[o + r] = (float)(p / ps);
-            psel[o + r] = (float)p;
-            if (ridx) ridx[o + r] = e;
-            if (rw) rw[o + r] = (float)(p / ps);
-            atomicAdd(&cnt[e], 1);
-        }
-        // keep the probabilities for the statistics (only this thread touches group g of tok)
-        for (int j = 0; j < n; ++j) {
-            const double pj = exp(l[j] - m) / den;
-            lg[tok][g * n + j] = pj;
-        }
-    }
-    __syncthreads();
-    if (threadIdx.x < N) {
-        const int e = threadIdx.x;
-        double s = 0.0;
-        for (int tok = 0; tok < kTok; ++tok)
-            if (t0 + tok < T) s += lg[tok][e];
-        part_psum[(int64_t)blockIdx.x * N + e] = s;
-        part_cnt[(int64_t)blockIdx.x * N + e] = cnt[e];
-    }
+    select_and_stats(a, lg, cnt, t0, 256);
 }
 
-// Sums the per-block partials in block order (deterministic) and forms the balance loss.
+// Sums the per-block partials in a fixed order (deterministic) and forms the balance loss.
+// Thread (slice j, expert e) sums blocks j, j + J, ...; the J slice sums are then added in order.
 __global__ void __launch_bounds__(256) stats_finalize_kernel(const int32_t* __restrict__ part_cnt,
                                                              const double* __restrict__ part_psum,
                                                              int64_t nblk, int64_t T, int N, int G,
                                                              int k, char* __restrict__ stats) {
+    __shared__ double ps[256];
+    __shared__ int64_t pc[256];
     __shared__ double fp[64];
     int64_t* counts = reinterpret_cast<int64_t*>(stats);
     double* mean = reinterpret_cast<double*>(stats + 8 * N);
     double* aux = reinterpret_cast<double*>(stats + 16 * N);
-    const int e = threadIdx.x;
-    if (e < N) {
-        int64_t c = 0;
-        double s = 0.0;
-        for (int64_t b = 0; b < nblk; ++b) {
+    const int J = 256 / N;
+    const int e = threadIdx.x % N, j = threadIdx.x / N;
+    double s = 0.0;
+    int64_t c = 0;
+    if (j < J) {
+        for (int64_t b = j; b < nblk; b += J) {
             c += part_cnt[b * N + e];
             s += part_psum[b * N + e];
         }
-        counts[e] = c;
-        const double P = s / (double)T;
-        mean[e] = P;
-        fp[e] = ((double)c / ((double)T * (double)k)) * P;
+    }
+    ps[threadIdx.x] = s;
+    pc[threadIdx.x] = c;
+    __syncthreads();
+    if (threadIdx.x < N) {
+        double tot = 0.0;
+        int64_t ct = 0;
+        for (int jj = 0; jj < J; ++jj) {
+            tot += ps[jj * N + threadIdx.x];
+            ct += pc[jj * N + threadIdx.x];
+        }
+        counts[threadIdx.x] = ct;
+        const double P = tot / (double)T;
+        mean[threadIdx.x] = P;
+        fp[threadIdx.x] = ((double)ct / ((double)T * (double)k)) * P;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -179,7 +259,7 @@ __global__ void __launch_bounds__(256) stats_finalize_kernel(const int32_t* __re
         double tot = 0.0;
         for (int g = 0; g < G; ++g) {
             double Lg = 0.0;
-            for (int j = 0; j < n; ++j) Lg += fp[g * n + j];
+            for (int jj = 0; jj < n; ++jj) Lg += fp[g * n + jj];
             tot += (double)n * Lg;
         }
         *aux = tot / (double)G;
@@ -188,36 +268,42 @@ __global__ void __launch_bounds__(256) stats_finalize_kernel(const int32_t* __re
 
 }  // namespace
 
+bool router_uses_mfma(const GqeDims& D) { return D.d % 64 == 0 && D.N <= 16; }
+
 hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, const void* packed,
                          const PackedLayout& pl, char* ws, int32_t* route_idx, float* route_w,
                          hipStream_t st) {
     const char* pk = (const char*)packed;
-    const double* wr = (const double*)(pk + pl.wr64);
-    const double* br = (const double*)(pk + pl.br64);
-    int32_t* idx = (int32_t*)(ws + P.idx);
-    float* wsel = (float*)(ws + P.wsel);
-    float* psel = (float*)(ws + P.psel);
-    int32_t* pc = (int32_t*)(ws + P.part_cnt);
-    double* pp = (double*)(ws + P.part_psum);
+    RouterArgs a{};
+    a.x = x;
+    a.wr = (const double*)(pk + pl.wr64);
+    a.br = (const double*)(pk + pl.br64);
+    a.T = P.T;
+    a.d = D.d;
+    a.N = D.N;
+    a.G = D.G;
+    a.k = D.k;
+    a.n = D.n;
+    a.Np = (int)round_up(D.N, 16);
+    a.idx = (int32_t*)(ws + P.idx);
+    a.wsel = (float*)(ws + P.wsel);
+    a.psel = (float*)(ws + P.psel);
+    a.ridx = route_idx;
+    a.rw = route_w;
+    a.part_cnt = (int32_t*)(ws + P.part_cnt);
+    a.part_psum = (double*)(ws + P.part_psum);
     const dim3 grid((unsigned)P.nblk_router);
-    const bool vec = D.d % 32 == 0;
-    if (D.dtype == GQE_DTYPE_BF16) {
-        if (vec)
-            router_kernel<bf16_t, true><<<grid, 256, 0, st>>>((const bf16_t*)x, wr, br, P.T, D.d, D.N, D.G, D.k,
-                                                               idx, wsel, psel, route_idx, route_w, pc, pp);
-        else
-            router_kernel<bf16_t, false><<<grid, 256, 0, st>>>((const bf16_t*)x, wr, br, P.T, D.d, D.N, D.G, D.k,
-                                                                idx, wsel, psel, route_idx, route_w, pc, pp);
+    const bool bf = D.dtype == GQE_DTYPE_BF16;
+    if (router_uses_mfma(D)) {
+        if (bf) router_mfma_kernel<bf16_t><<<grid, 512, 0, st>>>(a);
+        else router_mfma_kernel<float><<<grid, 512, 0, st>>>(a);
     } else {
-        if (vec)
-            router_kernel<float, true><<<grid, 256, 0, st>>>((const float*)x, wr, br, P.T, D.d, D.N, D.G, D.k,
-                                                              idx, wsel, psel, route_idx, route_w, pc, pp);
-        else
-            router_kernel<float, false><<<grid, 256, 0, st>>>((const float*)x, wr, br, P.T, D.d, D.N, D.G, D.k,
-                                                               idx, wsel, psel, route_idx, route_w, pc, pp);
+        if (bf) router_valu_kernel<bf16_t><<<grid, 256, 0, st>>>(a);
+        else router_valu_kernel<float><<<grid, 256, 0, st>>>(a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    stats_finalize_kernel<<<1, 256, 0, st>>>(pc, pp, P.nblk_router, P.T, D.N, D.G, D.k, ws + P.stats);
+    stats_finalize_kernel<<<1, 256, 0, st>>>(a.part_cnt, a.part_psum, P.nblk_router, P.T, D.N, D.G, D.k,
+                                             ws + P.stats);
     return hipGetLastError();
 }
