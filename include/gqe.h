@@ -161,7 +161,8 @@ int gqe_aux_stats(gqe_handle_t* h, void* stream, int64_t* counts, double* mean_p
                   double* aux_loss, int32_t* active_heads);
 
 /* Byte offsets of the intermediates inside the workspace of a [batch, seq] forward, for
- * stage-by-stage checks:  offs[0] Q_act [B, H_act, S, d_h], offs[1] K [B, G, S_pad, d_h],
+ * stage-by-stage checks:  offs[0] Q_act [B, H_act, S, d_h] (stored multiplied by
+ * log2(e)/sqrt(d_h), the attention scale in log2 units), offs[1] K [B, G, S_pad, d_h],
  * offs[2] V^T [B, G, d_h, S_pad] (keys permuted inside every 32-key block, see DESIGN),
  * offs[3] O_act [B, S, H_act, d_h], offs[4] route_idx [T, G, k] int32, offs[5] route_w
  * [T, G, k] f32, offs[6] p_sel [T, G, k] f32; dims[0] = H_act, dims[1] = S_pad. */

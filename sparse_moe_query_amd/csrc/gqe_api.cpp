@@ -57,6 +57,10 @@ WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S) {
     P.kk = take((size_t)B * D.G * P.S_pad * D.dh * es);
     P.vt = take((size_t)B * D.G * D.dh * P.S_pad * es);
     P.o = take((size_t)B * S * D.H * D.dh * es);
+    P.kn = take((size_t)B * D.G * P.S_pad * 4);
+    attn_plan(D, B, S, &P.attn_items, &P.attn_ncmax, &P.attn_kch);
+    P.attn_part = take(attn_partial_bytes(D, P.attn_items, P.attn_ncmax));
+    P.attn_cnt = take((size_t)P.attn_items * 4);
     P.total = off;
     return P;
 }
@@ -255,6 +259,7 @@ int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t 
     if (e == hipSuccess)
         e = h->mfma_proj ? launch_proj_mfma(D, P, x, h->packed, h->pl, ws, st)
                          : launch_proj_simple(D, P, h->w, x, ws, st);
+    if (e == hipSuccess && !h->mfma_proj && h->mfma_attn) e = launch_kn_simple(D, P, ws, st);
     mark(2);
     if (e == hipSuccess) e = h->mfma_attn ? launch_attn_mfma(D, P, ws, st) : launch_attn_simple(D, P, ws, st);
     mark(3);

@@ -30,8 +30,12 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
     u += 0x7fffu + ((u >> 16) & 1u);
     return bf16_t{(uint16_t)(u >> 16)};
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Two float32 -> two bfloat16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)from_f32<bf16_t>(lo).bits | ((uint32_t)from_f32<bf16_t>(hi).bits << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Position, inside its 32-key block, at which key offset o (0..31) of V^T is stored.

@@ -5,20 +5,25 @@
 // positions); its 256 query columns are all (position, head) pairs of the group's active heads, so
 // every K/V tile staged in LDS serves the k routed heads (+ the shared head for its group) at once.
 //
-// Per wave: 64 query columns (two 32-column tiles).
-//   S^T = K Q^T       v_mfma_f32_32x32x16_bf16 (d_h = 48 needs no padding: 3 k-steps of 16)
-//   online softmax    per lane: one query column, 16 keys per 32-key subtile; the row maximum
-//                     of a tile is the lane maximum combined with lane l^32 (v_permlane32_swap);
-//                     the running maximum is only raised when it grows by more than 2^8 (lazy
-//                     rescale), so the O rescale is rare
-//   P -> B operand    probabilities are packed to bf16 and two v_permlane16_swap per register pair
-//                     turn the 32x32 accumulator layout into the 16x16x32 B-operand layout; V^T is
-//                     stored with keys slotted (vt_pos) so that one 16-byte LDS read gives each
-//                     lane the eight keys its probabilities hold
-//   O^T += V^T P^T    v_mfma_f32_16x16x32_bf16, d_h in 16-row blocks
-//
-// Work order: items sorted by causal key range, longest first (an in-kernel closed-form rank:
-// every item has the same number of query columns, so its cost is its key range).
+// Per wave: 64 query columns (two 32-column tiles), 64-key tiles.
+//   S^T = K Q^T     v_mfma_f32_32x32x16_bf16 (d_h = 48 needs no padding: 3 k-steps of 16).  The
+//                   queries arrive pre-scaled by log2(e)/sqrt(d_h), so S is in log2 units.
+//   softmax         per lane: one query column, 16 keys per 32-key subtile.  Fast tiles: when the
+//                   Cauchy-Schwarz bound max|q| * max|k| <= 64 holds for the wave and tile (the
+//                   key norms come from the projection) and the running offset is 0, P = exp2(S)
+//                   directly (no maximum, no subtraction: one exp2 and half a convert per score).
+//                   Otherwise the standard online softmax runs (lane maximum combined with lane
+//                   l^32 by v_permlane32_swap; the offset is raised lazily, only when it grows by
+//                   more than 2^8, so O is rarely rescaled).
+//   P -> B operand  bf16-packed and re-laid by two v_permlane16_swap per register pair into the
+//                   16x16x32 B layout; V^T is stored with keys slotted (vt_pos) so that one 16-byte
+//                   LDS read gives each lane the eight keys its probabilities hold.
+//   O^T += V^T P^T  v_mfma_f32_16x16x32_bf16 over d_h in 16-row blocks plus one block whose first
+//                   row is all ones: the matrix core also forms the row sums, from the same
+//                   bf16 P that multiplies V.
+// Long causal ranges are split into KV chunks (separate work items); each chunk stores its
+// unnormalised O, row sum and offset, and the chunk that finishes last (per-item atomic counter,
+// no waiting) merges them.  Work order: items by causal range, longest first.
 #include "gqe_common.h"
 #include "gqe_internal.h"
 
@@ -28,16 +33,21 @@ constexpr int kWaves = 4;
 constexpr int kQW = 64;                // query columns per wave
 constexpr int kCols = kWaves * kQW;    // query columns per work item
 constexpr int kBN = GQE_KV_TILE;       // keys per LDS tile
-constexpr float kLazy = 8.0f;          // raise the running max only when it grows by > 2^8
+constexpr float kLazy = 8.0f;          // raise the running offset only when it grows by > 2^8
+constexpr float kFastBound = 64.0f;    // |S| <= 64 (log2 units) keeps exp2 in range without offset
 
 struct AttnArgs {
     const bf16_t* Q;
     const bf16_t* K;
     const bf16_t* Vt;
+    const float* kn;      // per-key norms [B][G][S_pad]
     bf16_t* O;
+    float* part;          // split-KV partials
+    int* counters;        // split-KV arrival counters, one per item
     int64_t S, S_pad;
     int B, G, H, k, skv, s;
-    float scale_log2;  // log2(e) / sqrt(d_h)
+    int kch;              // tiles per KV chunk
+    int ncmax;            // chunks of the longest item (grid = items * ncmax)
     // schedule: up to two classes of groups (heads per group NH, positions per item P)
     int ncls;
     int nh[2], P[2], m[2], J[2], ngr[2];
@@ -93,66 +103,106 @@ __device__ __forceinline__ float fmax3(float a, float b, float c) {
     return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 
+__global__ void zero_ints_kernel(int* p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
 template <int DH>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
     constexpr int KS = DH / 16;        // k-steps of the 32x32x16 QK^T product
     constexpr int DB = DH / 16;        // 16-row blocks of d_h in the PV product
+    constexpr int DBX = DB + 1;        // plus the row-sum block
     constexpr int KP = DH + 8;         // LDS row pitch of K (elements)
     constexpr int VP = kBN + 8;        // LDS row pitch of V^T (elements)
     constexpr int KCH = kBN * DH / 8;  // 16-byte chunks per K tile
     constexpr int VCH = DH * kBN / 8;  // 16-byte chunks per V^T tile
     constexpr int LCH = (KCH + 255) / 256;
+    constexpr int NREG = 2 * 2 * DBX * 4;  // partial O floats per lane
     __shared__ __align__(16) uint16_t ks_lds[2][kBN * KP];
-    __shared__ __align__(16) uint16_t vs_lds[2][DH * VP];
+    __shared__ __align__(16) uint16_t vs_lds[2][(DH + 16) * VP];
+    __shared__ int last_flag;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const Item it = decode_item(a, blockIdx.x);
+    const int64_t rank = blockIdx.x / a.ncmax;
+    const int chunk = blockIdx.x % a.ncmax;
+    const Item it = decode_item(a, rank);
     const int NH = it.nh;
     const int64_t S = a.S;
     const int64_t last_pos = min((int64_t)it.p0 + it.np, S) - 1;  // last query position of the item
-    const int ntiles = (int)(last_pos / kBN) + 1;
+    const int ntiles_item = (int)(last_pos / kBN) + 1;
+    const int nchunks = (ntiles_item + a.kch - 1) / a.kch;
+    if (chunk >= nchunks) return;  // uniform for the whole block
+    const int kt_begin = chunk * a.kch;
+    const int kt_end = min(ntiles_item, kt_begin + a.kch);
 
     const bf16_t* Kg = a.K + ((int64_t)it.b * a.G + it.g) * a.S_pad * DH;
     const bf16_t* Vg = a.Vt + ((int64_t)it.b * a.G + it.g) * (int64_t)DH * a.S_pad;
+    const float* kng = a.kn + ((int64_t)it.b * a.G + it.g) * a.S_pad;
 
     // ---------------------------------------------------------------- query columns of the lane
     int64_t posq[2];
-    bool qvalid[2];
-    int vhead[2];
     bf16x8_t qf[2][KS];
+    float qsq[2];  // sum of squares of the lane's half of the query column's dims
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
         const int c = w * kQW + qt * 32 + (lane & 31);
         const int p = c / NH, h = c % NH;
         const int64_t pos = (int64_t)it.p0 + p;
-        qvalid[qt] = (p < it.np) && (pos < S);
-        posq[qt] = qvalid[qt] ? pos : S - 1;
-        vhead[qt] = h < a.k ? it.g * a.k + h : a.G * a.k;
-        const bf16_t* qr = a.Q + (((int64_t)it.b * a.H + vhead[qt]) * S + posq[qt]) * DH + 8 * (lane >> 5);
+        const bool valid = (p < it.np) && (pos < S);
+        posq[qt] = valid ? pos : S - 1;
+        const int vh = h < a.k ? it.g * a.k + h : a.G * a.k;
+        const bf16_t* qr = a.Q + (((int64_t)it.b * a.H + vh) * S + posq[qt]) * DH + 8 * (lane >> 5);
+        float ss = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) qf[qt][kk] = *reinterpret_cast<const bf16x8_t*>(qr + 16 * kk);
+        for (int kk = 0; kk < KS; ++kk) {
+            qf[qt][kk] = *reinterpret_cast<const bf16x8_t*>(qr + 16 * kk);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = (float)qf[qt][kk][e];
+                ss += v * v;
+            }
+        }
+        qsq[qt] = ss;
     }
+    // |q|^2 = (this half) + (other half) <= 2 max(half): a bound on every query norm of the wave
+    const float qmax_w = sqrtf(wave_max(__builtin_fmaxf(qsq[0], qsq[1]) * 2.0f));
     // key range of this wave
     const int cfirst = w * kQW, clast = w * kQW + kQW - 1;
     const int64_t wfirst = min((int64_t)it.p0 + cfirst / NH, S - 1);
     const int64_t wlast = min(min((int64_t)it.p0 + min(clast / NH, it.np - 1), S - 1), last_pos);
     const int wtiles = (int)(wlast / kBN) + 1;
 
-    f32x4_t oacc[2][2][DB];
+    f32x4_t oacc[2][2][DBX];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[qt][hf][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int db = 0; db < DBX; ++db) oacc[qt][hf][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float mrun[2] = {-INFINITY, -INFINITY};
-    float lsum[2] = {0.f, 0.f};
+    bool offset_zero = true;  // wave-uniform: every lane's offset is 0 or unset
+
+    // row-sum block of V^T: first row ones, the rest zeros (both buffers, written once)
+    for (int i = tid; i < 2 * 16 * kBN; i += 256) {
+        const int buf = i / (16 * kBN), r = (i / kBN) % 16, c = i % kBN;
+        vs_lds[buf][(DH + r) * VP + c] = r == 0 ? (uint16_t)0x3f80 : (uint16_t)0;
+    }
 
     // ---------------------------------------------------------------- tile loader
     u32x4_t kreg[LCH], vreg[LCH];
+    float kn_next = 0.f;  // norm of key kt*64 + lane of the tile being prefetched
     auto gload = [&](int kt) {
+        const int64_t kl = (int64_t)kt * kBN + lane;
+        kn_next = kl < S ? kng[kl] : 0.f;
 #pragma unroll
         for (int u = 0; u < LCH; ++u) {
             const int ch = tid + 256 * u;
@@ -195,80 +245,89 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
         }
     };
 
-    gload(0);
+    gload(kt_begin);
     lstore(0);
+    // largest key norm of the current tile (wave-uniform); the next tile's is formed while this
+    // tile computes, so neither the load nor the cross-lane maximum sits on the critical path
+    float kmax_cur = wave_max(kn_next);
     __syncthreads();
 
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < ntiles) gload(kt + 1);
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+        const int buf = (kt - kt_begin) & 1;
+        if (kt + 1 < kt_end) gload(kt + 1);
         if (kt < wtiles) {
             const uint16_t* kb = ks_lds[buf];
             const uint16_t* vb = vs_lds[buf];
-            // S^T tiles: [key subtile][query tile]
-            f32x16_t sacc[2][2];
+            const bool fast = offset_zero && (qmax_w * kmax_cur * 1.02f <= kFastBound);
+            // K fragments of both 32-key subtiles (shared by the two query tiles)
+            bf16x8_t kf[2][KS];
 #pragma unroll
-            for (int kst = 0; kst < 2; ++kst) {
-                bf16x8_t kf[KS];
+            for (int kst = 0; kst < 2; ++kst)
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk)
-                    kf[kk] = *reinterpret_cast<const bf16x8_t*>(kb + (32 * kst + (lane & 31)) * KP + 16 * kk + 8 * (lane >> 5));
-#pragma unroll
-                for (int qt = 0; qt < 2; ++qt) {
-                    f32x16_t acc = {};
-#pragma unroll
-                    for (int kk = 0; kk < KS; ++kk)
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[qt][kk], acc, 0, 0, 0);
-                    sacc[kst][qt] = acc;
-                }
-            }
+                    kf[kst][kk] = *reinterpret_cast<const bf16x8_t*>(kb + (32 * kst + (lane & 31)) * KP + 16 * kk + 8 * (lane >> 5));
             const bool diag = (int64_t)kt * kBN + kBN - 1 > wfirst;
             uint32_t pb[2][2][8];  // packed bf16 probabilities [qt][kst][reg]
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
+                // S^T tiles of this query tile: [key subtile]
+                f32x16_t sacc[2];
+#pragma unroll
+                for (int kst = 0; kst < 2; ++kst) {
+                    f32x16_t acc = {};
+#pragma unroll
+                    for (int kk = 0; kk < KS; ++kk)
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kst][kk], qf[qt][kk], acc, 0, 0, 0);
+                    sacc[kst] = acc;
+                }
                 if (diag) {
 #pragma unroll
                     for (int kst = 0; kst < 2; ++kst)
 #pragma unroll
                         for (int j = 0; j < 16; ++j) {
                             const int64_t kidx = (int64_t)kt * kBN + 32 * kst + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-                            if (kidx > posq[qt]) sacc[kst][qt][j] = -INFINITY;
+                            if (kidx > posq[qt]) sacc[kst][j] = -INFINITY;
                         }
                 }
-                float mx = -INFINITY;
+                float nm = 0.f;
+                if (fast) {
+                    mrun[qt] = 0.f;  // from unset (nothing accumulated) or already 0
+                } else {
+                    float mx = -INFINITY;
 #pragma unroll
-                for (int kst = 0; kst < 2; ++kst)
+                    for (int kst = 0; kst < 2; ++kst)
 #pragma unroll
-                    for (int j = 0; j < 16; j += 2) mx = fmax3(mx, sacc[kst][qt][j], sacc[kst][qt][j + 1]);
-                {
-                    const uint32_t mb = __float_as_uint(mx);
-                    auto sw = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
-                    mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-                }
-                const float cand = mx * a.scale_log2;
-                const bool need = cand > mrun[qt] + kLazy;
-                if (__builtin_amdgcn_ballot_w64(need)) {
-                    const float mnew = need ? cand : mrun[qt];
-                    const float alpha = need ? __builtin_amdgcn_exp2f(mrun[qt] - mnew) : 1.0f;
-                    mrun[qt] = mnew;
-                    lsum[qt] *= alpha;
-                    const float aa = __shfl(alpha, lane & 15);
-                    const float ab = __shfl(alpha, 16 + (lane & 15));
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        oacc[qt][0][db] *= aa;
-                        oacc[qt][1][db] *= ab;
+                        for (int j = 0; j < 16; j += 2) mx = fmax3(mx, sacc[kst][j], sacc[kst][j + 1]);
+                    {
+                        const uint32_t mb = __float_as_uint(mx);
+                        auto sw = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
+                        mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
                     }
+                    const bool need = mx > mrun[qt] + kLazy;
+                    if (__builtin_amdgcn_ballot_w64(need)) {
+                        const float mnew = need ? mx : mrun[qt];
+                        const float alpha = (need && mrun[qt] != -INFINITY) ? __builtin_amdgcn_exp2f(mrun[qt] - mnew)
+                                                                             : (need ? 0.f : 1.f);
+                        mrun[qt] = mnew;
+                        const float aa = __shfl(alpha, lane & 15);
+                        const float ab = __shfl(alpha, 16 + (lane & 15));
+#pragma unroll
+                        for (int db = 0; db < DBX; ++db) {
+                            oacc[qt][0][db] *= aa;
+                            oacc[qt][1][db] *= ab;
+                        }
+                    }
+                    nm = mrun[qt] == -INFINITY ? 0.f : -mrun[qt];
                 }
-                const float nm = -mrun[qt];
-                float ls = 0.f;
 #pragma unroll
                 for (int kst = 0; kst < 2; ++kst) {
                     float pv[16];
+                    if (fast) {
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kst][qt][j], a.scale_log2, nm));
-                        ls += pv[j];
+                        for (int j = 0; j < 16; ++j) pv[j] = __builtin_amdgcn_exp2f(sacc[kst][j]);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) pv[j] = __builtin_amdgcn_exp2f(sacc[kst][j] + nm);
                     }
                     uint32_t X[4], Y[4];
 #pragma unroll
@@ -283,13 +342,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
                         pb[qt][kst][4 + i] = r[1];  // query block 32qt + 16..31
                     }
                 }
-                lsum[qt] += ls;
             }
-            // O^T += V^T P^T
+            if (!fast) offset_zero = !__builtin_amdgcn_ballot_w64(mrun[0] != 0.f && mrun[0] != -INFINITY) &&
+                                     !__builtin_amdgcn_ballot_w64(mrun[1] != 0.f && mrun[1] != -INFINITY);
+            // O^T += V^T P^T (last block: row sums)
 #pragma unroll
             for (int kst = 0; kst < 2; ++kst) {
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
+                for (int db = 0; db < DBX; ++db) {
                     const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vb + (16 * db + (lane & 15)) * VP + 32 * kst + 8 * (lane >> 4));
 #pragma unroll
                     for (int qt = 0; qt < 2; ++qt) {
@@ -301,21 +361,80 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
                 }
             }
         }
-        if (kt + 1 < ntiles) lstore(buf ^ 1);
+        if (kt + 1 < kt_end) {
+            lstore(buf ^ 1);
+            kmax_cur = wave_max(kn_next);
+        }
         __syncthreads();
+    }
+
+    // offsets in the O layout: lane holds column (lane & 15) of block (qt, hf); the S layout lane
+    // holding that column is 16 hf + (lane & 15)
+    float mo[2][2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) mo[qt][hf] = __shfl(mrun[qt], 16 * hf + (lane & 15));
+
+    if (nchunks > 1) {
+        // ---------------------------------------------------------- split-KV: store, count, merge
+        const int64_t slot_base = rank * (int64_t)a.ncmax;
+        float* mine = a.part + ((slot_base + chunk) * 256 + w * 64 + lane) * (NREG + 4);
+        int r = 0;
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+                for (int db = 0; db < DBX; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mine[r++] = oacc[qt][hf][db][i];
+                mine[NREG + 2 * qt + hf] = mo[qt][hf];
+            }
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) {
+            const int prev = atomicAdd(&a.counters[rank], 1);
+            last_flag = (prev == nchunks - 1) ? 1 : 0;
+        }
+        __syncthreads();
+        if (!last_flag) return;
+        __threadfence();
+        // merge every chunk's partial into oacc (max offset, rescale, add)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                float M = -INFINITY;
+                for (int c = 0; c < nchunks; ++c) {
+                    const float* pc = a.part + ((slot_base + c) * 256 + w * 64 + lane) * (NREG + 4);
+                    M = __builtin_fmaxf(M, pc[NREG + 2 * qt + hf]);
+                }
+                if (M == -INFINITY) M = 0.f;
+#pragma unroll
+                for (int db = 0; db < DBX; ++db) oacc[qt][hf][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int c = 0; c < nchunks; ++c) {
+                    const float* pc = a.part + ((slot_base + c) * 256 + w * 64 + lane) * (NREG + 4);
+                    const float mc = pc[NREG + 2 * qt + hf];
+                    const float sc = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+                    const int base = (qt * 2 + hf) * DBX * 4;
+#pragma unroll
+                    for (int db = 0; db < DBX; ++db)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) oacc[qt][hf][db][i] += sc * pc[base + db * 4 + i];
+                }
+            }
+        if (tid == 0) a.counters[rank] = 0;  // ready for the next forward
     }
 
     // ---------------------------------------------------------------- normalise and store
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-        const uint32_t lb = __float_as_uint(lsum[qt]);
-        auto sw = __builtin_amdgcn_permlane32_swap(lb, lb, false, false);
-        const float ltot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        const float inv = 1.0f / ltot;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            const int src = 16 * hf + (lane & 15);  // S-layout lane holding this O column
-            const float sc = __shfl(inv, src);
+            // row sum: row 0 of the last block, held by the lane of this column in lane group 0
+            const float lsum = __shfl(oacc[qt][hf][DB][0], lane & 15);
+            const float sc = 1.0f / lsum;
             const int c = w * kQW + qt * 32 + 16 * hf + (lane & 15);
             const int p = c / NH, h = c % NH;
             const int64_t pos = (int64_t)it.p0 + p;
@@ -334,12 +453,49 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
 
 }  // namespace
 
+// Workspace needs of the attention kernel for one forward (split-KV partials and counters).
+void attn_plan(const GqeDims& D, int64_t B, int64_t S, int64_t* items, int* ncmax, int* kch) {
+    int64_t total = 0, tiles = 0;
+    auto cls = [&](int nh, int ngroups) {
+        const int P = kCols / nh;
+        const int64_t J = ceil_div(S, P);
+        total += B * ngroups * J;
+        for (int64_t j = 0; j < J; ++j) {
+            const int64_t E = std::min<int64_t>((j + 1) * P, S);
+            tiles += B * ngroups * ceil_div(E, kBN);
+        }
+    };
+    if (D.s) {
+        cls(D.k + 1, 1);
+        if (D.G > 1) cls(D.k, D.G - 1);
+    } else {
+        cls(D.k, D.G);
+    }
+    // chunk length: at least 32 tiles, else about a quarter of the average load of one of the 512
+    // concurrent work items (2 per CU), so that the longest item no longer dominates
+    const int64_t slots = 512;
+    const int64_t c = std::max<int64_t>(32, tiles / (slots * 4) * 2);
+    const int64_t longest = ceil_div(S, kBN);
+    *kch = (int)std::min<int64_t>(c, longest);
+    *ncmax = (int)ceil_div(longest, *kch);
+    *items = total;
+}
+
+size_t attn_partial_bytes(const GqeDims& D, int64_t items, int ncmax) {
+    if (ncmax <= 1) return 0;
+    const int DBX = D.dh / 16 + 1;
+    return (size_t)items * ncmax * 256 * (2 * 2 * DBX * 4 + 4) * sizeof(float);
+}
+
 hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st) {
     AttnArgs a{};
     a.Q = (const bf16_t*)(ws + P.q);
     a.K = (const bf16_t*)(ws + P.kk);
     a.Vt = (const bf16_t*)(ws + P.vt);
+    a.kn = (const float*)(ws + P.kn);
     a.O = (bf16_t*)(ws + P.o);
+    a.part = (float*)(ws + P.attn_part);
+    a.counters = (int*)(ws + P.attn_cnt);
     a.S = P.S;
     a.S_pad = P.S_pad;
     a.B = (int)P.B;
@@ -348,7 +504,8 @@ hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipSt
     a.k = D.k;
     a.skv = D.skv;
     a.s = D.s;
-    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D.dh));
+    a.kch = P.attn_kch;
+    a.ncmax = P.attn_ncmax;
     int64_t total = 0;
     auto add_class = [&](int nh, int ngroups, bool single) {
         const int c = a.ncls++;
@@ -366,11 +523,17 @@ hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipSt
     } else {
         add_class(D.k, D.G, false);
     }
-    if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
+    const int64_t grid = total * a.ncmax;
+    if (total != P.attn_items || grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
+    if (a.ncmax > 1) {
+        zero_ints_kernel<<<(unsigned)ceil_div(total, 256), 256, 0, st>>>(a.counters, total);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     switch (D.dh) {
-        case 32: attn_fwd_kernel<32><<<(unsigned)total, 256, 0, st>>>(a); break;
-        case 48: attn_fwd_kernel<48><<<(unsigned)total, 256, 0, st>>>(a); break;
-        case 64: attn_fwd_kernel<64><<<(unsigned)total, 256, 0, st>>>(a); break;
+        case 32: attn_fwd_kernel<32><<<(unsigned)grid, 256, 0, st>>>(a); break;
+        case 48: attn_fwd_kernel<48><<<(unsigned)grid, 256, 0, st>>>(a); break;
+        case 64: attn_fwd_kernel<64><<<(unsigned)grid, 256, 0, st>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

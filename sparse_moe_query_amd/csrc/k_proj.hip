@@ -15,6 +15,9 @@
 //   products   v_mfma_f32_16x16x32_bf16; K/Q blocks compute C^T = W^T x^T so each lane stores four
 //              consecutive head-dim values; V blocks compute C = x W so each lane stores four
 //              consecutive keys of V^T (slotted by vt_pos, see k_attn)
+//   epilogue   queries are stored multiplied by log2(e)/sqrt(d_h) (the attention scale, folded in
+//              before the single rounding to bf16); every key's norm is stored for the attention
+//              kernel's range test
 #include "gqe_common.h"
 #include "gqe_internal.h"
 
@@ -31,6 +34,8 @@ struct ProjArgs {
     bf16_t* Q;             // [B][H][S][DH]
     bf16_t* K;             // [B][G][S_pad][DH]
     bf16_t* Vt;            // [B][G][DH][S_pad]
+    float* kn;             // [B][G][S_pad] key norms
+    float qscale;          // log2(e) / sqrt(d_h): queries are stored pre-scaled
     int64_t T, S, S_pad;
     int d, G, k, n, H, s, dense, HB, njobs, ntiles;
 };
@@ -69,6 +74,9 @@ __global__ void __launch_bounds__(256, 2) proj_kernel(ProjArgs a) {
     // ---- rows of this wave (tile-local bucketing for a routed expert)
     int nrows;
     if (is_expert && !a.dense) {
+        // padding entries (past the slice) point at row 0 so every LDS read stays in the tile
+        rows[w][lane] = 0;
+        rows[w][lane + 64] = 0;
         int base = 0;
         for (int half = 0; half < kBM / 64; ++half) {
             const int row = half * 64 + lane;
@@ -176,18 +184,39 @@ __global__ void __launch_bounds__(256, 2) proj_kernel(ProjArgs a) {
         if (!is_v) {
             // C^T tile: lane holds token column (lane & 15), head dims 16cb + 4(lane>>4) + 0..3
             const int li = 16 * rb + (lane & 15);
-            if (li >= nrows) continue;
-            const int packed = rows[w][li];
+            const bool ok = li < nrows;
+            const int packed = rows[w][li & (kBM - 1)];
             const int row = packed & 0xff, rank = packed >> 8;
             const int64_t t = t0 + row;
             const int64_t b = t / S, sp = t % S;
+            if (hb < GD) {
+                // key: also its norm (the four lane groups hold complementary dims)
+                float ss = 0.f;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ss += acc[rb][cb][i] * acc[rb][cb][i];
+                ss += __shfl_xor(ss, 16);
+                ss += __shfl_xor(ss, 32);
+                if (!ok) continue;
+                if ((lane >> 4) == 0) a.kn[((int64_t)b * a.G + hb) * a.S_pad + sp] = sqrtf(ss);
+                bf16_t* dst = a.K + (((int64_t)b * a.G + hb) * a.S_pad + sp) * DH;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const f32x4_t v = acc[rb][cb];
+                    u32x2_t pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                    *reinterpret_cast<u32x2_t*>(dst + 16 * cb + 4 * (lane >> 4)) = pk;
+                }
+                continue;
+            }
+            if (!ok) continue;
             bf16_t* dst;
-            if (hb < GD) dst = a.K + (((int64_t)b * a.G + hb) * a.S_pad + sp) * DH;
-            else if (!is_expert) dst = a.Q + (((int64_t)b * a.H + a.G * a.k) * S + sp) * DH;  // shared head
+            if (!is_expert) dst = a.Q + (((int64_t)b * a.H + a.G * a.k) * S + sp) * DH;  // shared head
             else dst = a.Q + (((int64_t)b * a.H + g_of * a.k + rank) * S + sp) * DH;
+            const float qs = a.qscale;
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
-                const f32x4_t v = acc[rb][cb];
+                const f32x4_t v = acc[rb][cb] * qs;
                 u32x2_t pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
                 *reinterpret_cast<u32x2_t*>(dst + 16 * cb + 4 * (lane >> 4)) = pk;
             }
@@ -231,6 +260,8 @@ hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x, 
     a.Q = (bf16_t*)(ws + P.q);
     a.K = (bf16_t*)(ws + P.kk);
     a.Vt = (bf16_t*)(ws + P.vt);
+    a.kn = (float*)(ws + P.kn);
+    a.qscale = (float)(1.4426950408889634 / std::sqrt((double)D.dh));
     a.T = P.T;
     a.S = P.S;
     a.S_pad = P.S_pad;

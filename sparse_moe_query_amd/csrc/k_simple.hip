@@ -55,7 +55,8 @@ __global__ void proj_simple_kernel(Args a, const T* __restrict__ x, const T* __r
         w = wq + (int64_t)e * a.d * a.dh;
     }
     for (int i = 0; i < a.d; ++i) acc += to_f32(xr[i]) * to_f32(w[(int64_t)i * a.dh + j]);
-    Q[((b * a.H + v) * a.S + s) * a.dh + j] = from_f32<T>(acc);
+    // stored pre-scaled by log2(e)/sqrt(d_h): the attention works in log2 units
+    Q[((b * a.H + v) * a.S + s) * a.dh + j] = from_f32<T>(acc * (1.44269504088896341f / sqrtf((float)a.dh)));
 }
 
 // Causal attention of one query row (online softmax over keys 0..s of its group).
@@ -74,17 +75,15 @@ __global__ void attn_simple_kernel(Args a, const T* __restrict__ Q, const T* __r
         qv[j] = to_f32(qr[j]);
         o[j] = 0.f;
     }
-    const float scale = 1.0f / sqrtf((float)a.dh);
-    float m = -INFINITY, l = 0.f;
+    float m = -INFINITY, l = 0.f;  // scores are already in log2 units
     const T* Kg = K + (b * a.G + g) * a.S_pad * a.dh;
     const T* Vg = Vt + (b * a.G + g) * a.dh * a.S_pad;
     for (int64_t kk = 0; kk <= s; ++kk) {
         float sc = 0.f;
         for (int j = 0; j < a.dh; ++j) sc += qv[j] * to_f32(Kg[kk * a.dh + j]);
-        sc *= scale;
         const float mn = fmaxf(m, sc);
-        const float alpha = __expf(m - mn);
-        const float p = __expf(sc - mn);
+        const float alpha = exp2f(m - mn);
+        const float p = exp2f(sc - mn);
         l = l * alpha + p;
         const int64_t pos = vt_pos(kk);
         for (int j = 0; j < a.dh; ++j) o[j] = o[j] * alpha + p * to_f32(Vg[(int64_t)j * a.S_pad + pos]);
@@ -93,6 +92,18 @@ __global__ void attn_simple_kernel(Args a, const T* __restrict__ Q, const T* __r
     T* orow = O + ((b * a.S + s) * a.H + v) * a.dh;
     const float inv = 1.0f / l;
     for (int j = 0; j < a.dh; ++j) orow[j] = from_f32<T>(o[j] * inv);
+}
+
+// Key norms for the matrix-core attention kernel's range test (when the projection ran here).
+template <typename T>
+__global__ void kn_simple_kernel(Args a, const T* __restrict__ K, float* __restrict__ kn) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= a.B * a.G * a.S) return;
+    const int64_t s = q % a.S, bg = q / a.S;
+    const T* kr = K + (bg * a.S_pad + s) * a.dh;
+    float ss = 0.f;
+    for (int j = 0; j < a.dh; ++j) ss += to_f32(kr[j]) * to_f32(kr[j]);
+    kn[bg * a.S_pad + s] = sqrtf(ss) * 1.01f;  // margin for the float32 rounding of the sum
 }
 
 // Output construction (README "Parameters"/"Ablations"; explainer "Output Construction").
@@ -180,6 +191,16 @@ hipError_t launch_proj_simple(const GqeDims& D, const WorkPlan& P, const gqe_wei
 }
 hipError_t launch_attn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st) {
     return D.dtype == GQE_DTYPE_BF16 ? attn<bf16_t>(D, P, ws, st) : attn<float>(D, P, ws, st);
+}
+hipError_t launch_kn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st) {
+    const Args a = make_args<bf16_t>(D, P);
+    if (D.dtype == GQE_DTYPE_BF16)
+        kn_simple_kernel<bf16_t><<<(unsigned)ceil_div(P.B * D.G * P.S, 256), 256, 0, st>>>(
+            a, (const bf16_t*)(ws + P.kk), (float*)(ws + P.kn));
+    else
+        kn_simple_kernel<float><<<(unsigned)ceil_div(P.B * D.G * P.S, 256), 256, 0, st>>>(
+            a, (const float*)(ws + P.kk), (float*)(ws + P.kn));
+    return hipGetLastError();
 }
 hipError_t launch_combine_simple(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w, void* y,
                                  char* ws, hipStream_t st) {

@@ -62,7 +62,9 @@ def test_small_every_token_and_stage(wl):
     vg = vt_unpermute(inter["vt"]).float().cpu().numpy()[:, :, :, :S].transpose(0, 1, 3, 2)
     assert parity.within_rounding(kg, K, wl.dtype), parity.rel_err_rows(kg, K)
     assert parity.within_rounding(vg, V, wl.dtype), parity.rel_err_rows(vg, V)
-    qg = inter["q"].float().cpu().numpy().transpose(0, 2, 1, 3).reshape(B * S, H, dh)
+    # Q_act is stored pre-scaled by log2(e)/sqrt(d_h) (the attention works in log2 units)
+    qscale = np.float32(1.4426950408889634 / np.sqrt(dh))
+    qg = inter["q"].float().cpu().numpy().transpose(0, 2, 1, 3).reshape(B * S, H, dh) / qscale
     og = inter["o"].float().cpu().numpy().reshape(B * S, H, dh)
     assert parity.within_rounding(qg, rep["q_ref"], wl.dtype), parity.rel_err_rows(qg, rep["q_ref"])
     assert parity.rel_err_rows(og, rep["o_ref"]) <= (1e-4 if wl.dtype == "f32" else 2e-2)
