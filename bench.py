@@ -111,6 +111,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="main workload only (for profilers)")
+    ap.add_argument("--profile-workload", default=None,
+                    help="run only this named workload (inputs.WORKLOADS, or NAME_gqa for its "
+                         "all-active GQA baseline) for --steps forwards; for profilers")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
@@ -124,6 +127,12 @@ def main():
     from sparse_moe_query_amd.inputs import WORKLOADS, gqa_of
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.profile_workload:
+        name = args.profile_workload
+        wl = gqa_of(WORKLOADS[name[:-4]]) if name.endswith("_gqa") else WORKLOADS[name]
+        ms, stage_ms, _ = run_workload(wl, args.steps, args.warmup)
+        print(json.dumps({"workload": wl.name, "ms_per_step": ms, "stage_ms": stage_ms}), flush=True)
+        return
     main_wl = WORKLOADS["main_b8_s2048"]
     log(f"[bench] main workload {main_wl.name}: warmup {args.warmup}, steps {args.steps}")
     ms, stage_ms, path = run_workload(main_wl, args.steps, args.warmup)

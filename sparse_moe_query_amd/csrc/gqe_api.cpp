@@ -58,9 +58,7 @@ WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S) {
     P.vt = take((size_t)B * D.G * D.dh * P.S_pad * es);
     P.o = take((size_t)B * S * D.H * D.dh * es);
     P.kn = take((size_t)B * D.G * P.S_pad * 4);
-    attn_plan(D, B, S, &P.attn_items, &P.attn_ncmax, &P.attn_kch);
-    P.attn_part = take(attn_partial_bytes(D, P.attn_items, P.attn_ncmax));
-    P.attn_cnt = take((size_t)P.attn_items * 4);
+    P.knt = take((size_t)B * D.G * (P.S_pad / GQE_KV_TILE) * 4);
     P.total = off;
     return P;
 }

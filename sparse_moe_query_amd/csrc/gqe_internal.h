@@ -34,9 +34,7 @@ struct WorkPlan {
     size_t stats;                     // counts [N] i64, mean [N] f64, aux f64
     size_t q, kk, vt, o;              // Q_act, K, V^T, O_act
     size_t kn;                        // per-key norms [B][G][S_pad] f32
-    size_t attn_part, attn_cnt;       // split-KV partials and arrival counters
-    int64_t attn_items;
-    int attn_ncmax, attn_kch;
+    size_t knt;                       // per-64-key-tile maximum norm [B][G][S_pad/64] f32
     size_t total;
 };
 
@@ -59,8 +57,6 @@ struct gqe_handle {
 };
 
 WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S);
-void attn_plan(const GqeDims& D, int64_t B, int64_t S, int64_t* items, int* ncmax, int* kch);
-size_t attn_partial_bytes(const GqeDims& D, int64_t items, int ncmax);
 hipError_t launch_kn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st);
 bool router_uses_mfma(const GqeDims& D);
 PackedLayout make_packed_layout(const GqeDims& D, bool mfma);

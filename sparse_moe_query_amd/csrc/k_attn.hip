@@ -21,9 +21,7 @@
 //   O^T += V^T P^T  v_mfma_f32_16x16x32_bf16 over d_h in 16-row blocks plus one block whose first
 //                   row is all ones: the matrix core also forms the row sums, from the same
 //                   bf16 P that multiplies V.
-// Long causal ranges are split into KV chunks (separate work items); each chunk stores its
-// unnormalised O, row sum and offset, and the chunk that finishes last (per-item atomic counter,
-// no waiting) merges them.  Work order: items by causal range, longest first.
+// Work order: items by causal range, longest first (LPT over the concurrent work-group slots).
 #include "gqe_common.h"
 #include "gqe_internal.h"
 
@@ -36,18 +34,16 @@ constexpr int kBN = GQE_KV_TILE;       // keys per LDS tile
 constexpr float kLazy = 8.0f;          // raise the running offset only when it grows by > 2^8
 constexpr float kFastBound = 64.0f;    // |S| <= 64 (log2 units) keeps exp2 in range without offset
 
+
 struct AttnArgs {
     const bf16_t* Q;
     const bf16_t* K;
     const bf16_t* Vt;
     const float* kn;      // per-key norms [B][G][S_pad]
+    const float* knt;     // per-tile maximum key norm [B][G][S_pad / 64]
     bf16_t* O;
-    float* part;          // split-KV partials
-    int* counters;        // split-KV arrival counters, one per item
     int64_t S, S_pad;
     int B, G, H, k, skv, s;
-    int kch;              // tiles per KV chunk
-    int ncmax;            // chunks of the longest item (grid = items * ncmax)
     // schedule: up to two classes of groups (heads per group NH, positions per item P)
     int ncls;
     int nh[2], P[2], m[2], J[2], ngr[2];
@@ -58,35 +54,36 @@ struct Item {
     int b, g, p0, np, nh;
 };
 
-__device__ __forceinline__ int64_t count_ge(const AttnArgs& a, int64_t e) {
-    // number of items whose key range end E >= e (1 <= e <= S)
-    int64_t n = 0;
-    for (int c = 0; c < a.ncls; ++c) n += (int64_t)a.m[c] * (a.J[c] - (e - 1) / a.P[c]);
+__device__ __forceinline__ int count_ge(const AttnArgs& a, int e) {
+    // number of items whose key range end E >= e (1 <= e <= S); 32-bit: items and S fit easily
+    int n = 0;
+    for (int c = 0; c < a.ncls; ++c) n += a.m[c] * (a.J[c] - (int)((uint32_t)(e - 1) / (uint32_t)a.P[c]));
     return n;
 }
 
-__device__ Item decode_item(const AttnArgs& a, int64_t r) {
-    int64_t lo = 1, hi = a.S;
+__device__ Item decode_item(const AttnArgs& a, int r) {
+    const int S = (int)a.S;
+    int lo = 1, hi = S;
     while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) / 2;
+        const int mid = (lo + hi + 1) / 2;
         if (count_ge(a, mid) > r) lo = mid;
         else hi = mid - 1;
     }
-    const int64_t E = lo;
-    int64_t o = r - (E == a.S ? 0 : count_ge(a, E + 1));
+    const int E = lo;
+    int o = r - (E == S ? 0 : count_ge(a, E + 1));
     Item it{0, 0, 0, 0, 1};
     for (int c = 0; c < a.ncls; ++c) {
-        const bool has = (E == a.S) || (E % a.P[c] == 0);
+        const bool has = (E == S) || ((uint32_t)E % (uint32_t)a.P[c] == 0);
         if (!has) continue;
         if (o < a.m[c]) {
-            const int j = (E == a.S) ? a.J[c] - 1 : (int)(E / a.P[c]) - 1;
-            const int pair = (int)o;
+            const int j = (E == S) ? a.J[c] - 1 : (int)((uint32_t)E / (uint32_t)a.P[c]) - 1;
+            const int pair = o;
             if (a.single_group[c]) {
                 it.b = pair;
                 it.g = a.skv;
             } else {
-                it.b = pair / a.ngr[c];
-                const int gi = pair % a.ngr[c];
+                it.b = (int)((uint32_t)pair / (uint32_t)a.ngr[c]);
+                const int gi = pair - it.b * a.ngr[c];
                 it.g = (a.s && a.ncls == 2 && gi >= a.skv) ? gi + 1 : gi;
             }
             it.nh = a.nh[c];
@@ -103,10 +100,49 @@ __device__ __forceinline__ float fmax3(float a, float b, float c) {
     return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 
-__global__ void zero_ints_kernel(int* p, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0;
+// Per forward, before the attention kernel: the largest key norm of every 64-key tile (keys past
+// the sequence end excluded), and zero V^T at the padding keys [S, S_pad) so that P = 0 there
+// meets finite values.
+__global__ void __launch_bounds__(256) attn_prep_kernel(const float* __restrict__ kn, float* __restrict__ knt,
+                                                       bf16_t* __restrict__ Vt, int64_t BG, int64_t S,
+                                                       int64_t S_pad, int dh) {
+    const int64_t ntile = S_pad / 64;
+    const int64_t pad = S_pad - S;
+    const int64_t n1 = BG * ntile, n2 = BG * dh * pad;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n1 + n2;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        if (i < n1) {
+            const int64_t bg = i / ntile, t = i % ntile;
+            const f32x4_t* p = reinterpret_cast<const f32x4_t*>(kn + bg * S_pad + t * 64);
+            float m = 0.f;
+#pragma unroll 4
+            for (int q = 0; q < 16; ++q) {
+                const f32x4_t v = p[q];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (t * 64 + 4 * q + e < S) m = fmaxf(m, v[e]);
+            }
+            knt[i] = m;
+        } else {
+            const int64_t j = i - n1;
+            const int64_t row = j / pad, s = S + j % pad;  // row = bg * dh + head dim
+            Vt[row * S_pad + vt_pos(s)] = bf16_t{0};
+        }
+    }
 }
+
+// XOR swizzle of the 16-byte chunks of a key row in LDS, chosen per head dim so that the
+// fragment reads of eight consecutive rows (same logical chunk) fall into distinct bank groups.
+template <int DH>
+__device__ __forceinline__ int kswz(int r) {
+    if constexpr (DH == 64) return r & 7;
+    else if constexpr (DH == 32) return (r >> 2) & 3;
+    else return 0;  // d_h = 48: a 96-byte pitch already spreads eight rows over distinct groups
+}
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory operations are
+// outstanding and leaves the other counters unconstrained.
+constexpr int vmcnt_wait(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -119,30 +155,27 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
     constexpr int KS = DH / 16;        // k-steps of the 32x32x16 QK^T product
     constexpr int DB = DH / 16;        // 16-row blocks of d_h in the PV product
     constexpr int DBX = DB + 1;        // plus the row-sum block
-    constexpr int KP = DH + 8;         // LDS row pitch of K (elements)
-    constexpr int VP = kBN + 8;        // LDS row pitch of V^T (elements)
-    constexpr int KCH = kBN * DH / 8;  // 16-byte chunks per K tile
-    constexpr int VCH = DH * kBN / 8;  // 16-byte chunks per V^T tile
-    constexpr int LCH = (KCH + 255) / 256;
-    constexpr int NREG = 2 * 2 * DBX * 4;  // partial O floats per lane
-    __shared__ __align__(16) uint16_t ks_lds[2][kBN * KP];
-    __shared__ __align__(16) uint16_t vs_lds[2][(DH + 16) * VP];
-    __shared__ int last_flag;
+    constexpr int KC8 = DH / 8;        // 16-byte chunks per key row
+    constexpr int TILE_K = kBN * DH;   // elements of a K tile (unpadded, chunk-swizzled)
+    constexpr int TILE_V = DH * kBN;   // elements of a V^T tile (unpadded, chunk-swizzled)
+    constexpr int SEGK = TILE_K * 2 / 1024;  // 1 KB segments per tile (one wave-wide load each)
+    constexpr int SEGV = TILE_V * 2 / 1024;
+    constexpr int LK = (SEGK + 3) / 4;       // direct loads per wave per tile (same for every wave)
+    constexpr int LV = (SEGV + 3) / 4;
+    constexpr int NSTAGE = 3;
+    __shared__ __align__(1024) uint16_t ks_lds[NSTAGE][TILE_K];
+    __shared__ __align__(1024) uint16_t vs_lds[NSTAGE][TILE_V];
+    __shared__ __align__(1024) uint16_t sum_lds[16 * kBN];  // row-sum block: row 0 ones
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t rank = blockIdx.x / a.ncmax;
-    const int chunk = blockIdx.x % a.ncmax;
-    const Item it = decode_item(a, rank);
+    const Item it = decode_item(a, (int)blockIdx.x);
     const int NH = it.nh;
     const int64_t S = a.S;
     const int64_t last_pos = min((int64_t)it.p0 + it.np, S) - 1;  // last query position of the item
-    const int ntiles_item = (int)(last_pos / kBN) + 1;
-    const int nchunks = (ntiles_item + a.kch - 1) / a.kch;
-    if (chunk >= nchunks) return;  // uniform for the whole block
-    const int kt_begin = chunk * a.kch;
-    const int kt_end = min(ntiles_item, kt_begin + a.kch);
+    const int kt_begin = 0;
+    const int kt_end = (int)(last_pos / kBN) + 1;
 
     const bf16_t* Kg = a.K + ((int64_t)it.b * a.G + it.g) * a.S_pad * DH;
     const bf16_t* Vg = a.Vt + ((int64_t)it.b * a.G + it.g) * (int64_t)DH * a.S_pad;
@@ -191,81 +224,77 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
     float mrun[2] = {-INFINITY, -INFINITY};
     bool offset_zero = true;  // wave-uniform: every lane's offset is 0 or unset
 
-    // row-sum block of V^T: first row ones, the rest zeros (both buffers, written once)
-    for (int i = tid; i < 2 * 16 * kBN; i += 256) {
-        const int buf = i / (16 * kBN), r = (i / kBN) % 16, c = i % kBN;
-        vs_lds[buf][(DH + r) * VP + c] = r == 0 ? (uint16_t)0x3f80 : (uint16_t)0;
+    // row-sum block (read like a V^T block): row 0 all ones, rows 1..15 zero
+    for (int i = tid; i < 16 * kBN; i += 256) sum_lds[i] = (i < kBN) ? (uint16_t)0x3f80 : (uint16_t)0;
+
+    // Tiles go straight from global memory into LDS (global_load_lds_dwordx4: each wave-wide load
+    // fills one contiguous 1 KB segment, lane i its 16 bytes at 16 i).  Every lane therefore loads
+    // the global chunk that belongs at its LDS position; the chunk order inside a row is XOR
+    // swizzled so that the fragment reads of eight consecutive rows hit distinct banks.
+    // Three stages: while tile kt computes, tile kt+1 has landed or is landing and tile kt+2 is
+    // in flight.  Every wave issues the same number of loads per tile (segments past the end are
+    // re-issued, same bytes), so the wait is a compile-time vmcnt.
+    auto dma16 = [&](const void* gsrc, const uint16_t* ldst) {
+        // One wave-wide 16-byte-per-lane load straight into LDS at m0 + 16 * lane.  Written as
+        // inline assembly so that the compiler does not order every later LDS read behind it; the
+        // loop waits for these loads itself (vmcnt) before the barrier that publishes a stage.
+        const uint32_t m0v = (uint32_t)(uintptr_t)ldst;
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_nop 4"
+                     :
+                     : "s"(m0v), "v"(gsrc)
+                     : "memory", "m0");
+    };
+    auto issue = [&](int kt, int stage) {
+        const int64_t key0 = (int64_t)kt * kBN;
+#pragma unroll
+        for (int i = 0; i < LK; ++i) {
+            const int seg = min(w + 4 * i, SEGK - 1);
+            const int q = seg * 64 + lane;          // chunk position in the tile
+            const int r = q / KC8, cpos = q % KC8;  // key row, swizzled chunk slot
+            const int c = cpos ^ kswz<DH>(r);
+            dma16(Kg + (key0 + r) * DH + 8 * c, &ks_lds[stage][seg * 512]);
+        }
+#pragma unroll
+        for (int i = 0; i < LV; ++i) {
+            const int seg = min(w + 4 * i, SEGV - 1);
+            const int q = seg * 64 + lane;
+            const int r = q / 8, cpos = q % 8;      // V^T row (head dim), swizzled chunk slot
+            const int c = cpos ^ (r & 7);
+            dma16(Vg + (int64_t)r * a.S_pad + key0 + 8 * c, &vs_lds[stage][seg * 512]);
+        }
+    };
+    // per-tile maximum key norm: a wave-uniform scalar load (not on the vector-memory counter)
+    typedef const __attribute__((address_space(4))) float* const_f32_ptr;
+    const_f32_ptr kntg = (const_f32_ptr)(a.knt + ((int64_t)it.b * a.G + it.g) * (a.S_pad / kBN));
+    constexpr int NLOAD = LK + LV;  // vector-memory operations issued per tile per wave
+
+    issue(kt_begin, 0);
+    if (kt_begin + 1 < kt_end) {
+        issue(kt_begin + 1, 1);
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(NLOAD));
+    } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
     }
-
-    // ---------------------------------------------------------------- tile loader
-    u32x4_t kreg[LCH], vreg[LCH];
-    float kn_next = 0.f;  // norm of key kt*64 + lane of the tile being prefetched
-    auto gload = [&](int kt) {
-        const int64_t kl = (int64_t)kt * kBN + lane;
-        kn_next = kl < S ? kng[kl] : 0.f;
-#pragma unroll
-        for (int u = 0; u < LCH; ++u) {
-            const int ch = tid + 256 * u;
-            if (ch < KCH) {
-                const int r = ch / (DH / 8), c8 = ch % (DH / 8);
-                kreg[u] = *reinterpret_cast<const u32x4_t*>(Kg + ((int64_t)kt * kBN + r) * DH + 8 * c8);
-            }
-            if (ch < VCH) {
-                const int r = ch / (kBN / 8), c8 = ch % (kBN / 8);
-                vreg[u] = *reinterpret_cast<const u32x4_t*>(Vg + (int64_t)r * a.S_pad + (int64_t)kt * kBN + 8 * c8);
-                if ((int64_t)(kt + 1) * kBN > S) {
-                    // keys past the sequence end hold no data: zero them (their P is 0)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int q = (8 * c8 + e) & 31;
-                        const int sl = q >> 2;
-                        const int key = (((sl & 3) << 1) | (sl >> 2)) * 4 + (q & 3);
-                        const int64_t kidx = (int64_t)kt * kBN + ((8 * c8 + e) & ~31) + key;
-                        if (kidx >= S) {
-                            const uint32_t msk = (e & 1) ? 0x0000ffffu : 0xffff0000u;
-                            vreg[u][e >> 1] &= msk;
-                        }
-                    }
-                }
-            }
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < LCH; ++u) {
-            const int ch = tid + 256 * u;
-            if (ch < KCH) {
-                const int r = ch / (DH / 8), c8 = ch % (DH / 8);
-                *reinterpret_cast<u32x4_t*>(&ks_lds[buf][r * KP + 8 * c8]) = kreg[u];
-            }
-            if (ch < VCH) {
-                const int r = ch / (kBN / 8), c8 = ch % (kBN / 8);
-                *reinterpret_cast<u32x4_t*>(&vs_lds[buf][r * VP + 8 * c8]) = vreg[u];
-            }
-        }
-    };
-
-    gload(kt_begin);
-    lstore(0);
-    // largest key norm of the current tile (wave-uniform); the next tile's is formed while this
-    // tile computes, so neither the load nor the cross-lane maximum sits on the critical path
-    float kmax_cur = wave_max(kn_next);
     __syncthreads();
 
     for (int kt = kt_begin; kt < kt_end; ++kt) {
-        const int buf = (kt - kt_begin) & 1;
-        if (kt + 1 < kt_end) gload(kt + 1);
+        const int stage = (kt - kt_begin) % NSTAGE;
+        const bool ahead = kt + 2 < kt_end;
+        if (ahead) issue(kt + 2, (kt + 2 - kt_begin) % NSTAGE);
+        const float kmax_cur = kntg[kt];
         if (kt < wtiles) {
-            const uint16_t* kb = ks_lds[buf];
-            const uint16_t* vb = vs_lds[buf];
+            const uint16_t* kb = ks_lds[stage];
+            const uint16_t* vb = vs_lds[stage];
             const bool fast = offset_zero && (qmax_w * kmax_cur * 1.02f <= kFastBound);
             // K fragments of both 32-key subtiles (shared by the two query tiles)
             bf16x8_t kf[2][KS];
 #pragma unroll
             for (int kst = 0; kst < 2; ++kst)
 #pragma unroll
-                for (int kk = 0; kk < KS; ++kk)
-                    kf[kst][kk] = *reinterpret_cast<const bf16x8_t*>(kb + (32 * kst + (lane & 31)) * KP + 16 * kk + 8 * (lane >> 5));
+                for (int kk = 0; kk < KS; ++kk) {
+                    const int r = 32 * kst + (lane & 31), c = 2 * kk + (lane >> 5);
+                    kf[kst][kk] = *reinterpret_cast<const bf16x8_t*>(kb + (r * KC8 + (c ^ kswz<DH>(r))) * 8);
+                }
             const bool diag = (int64_t)kt * kBN + kBN - 1 > wfirst;
             uint32_t pb[2][2][8];  // packed bf16 probabilities [qt][kst][reg]
 #pragma unroll
@@ -350,7 +379,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
             for (int kst = 0; kst < 2; ++kst) {
 #pragma unroll
                 for (int db = 0; db < DBX; ++db) {
-                    const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vb + (16 * db + (lane & 15)) * VP + 32 * kst + 8 * (lane >> 4));
+                    const int r = 16 * db + (lane & 15), c = 4 * kst + (lane >> 4);
+                    const uint16_t* src = db < DB ? vb + (r * 8 + (c ^ (r & 7))) * 8
+                                                  : sum_lds + ((r - DH) * 8 + (c ^ (r & 7))) * 8;
+                    const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(src);
 #pragma unroll
                     for (int qt = 0; qt < 2; ++qt) {
                         u32x4_t ba = {pb[qt][kst][0], pb[qt][kst][1], pb[qt][kst][2], pb[qt][kst][3]};
@@ -362,69 +394,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
             }
         }
         if (kt + 1 < kt_end) {
-            lstore(buf ^ 1);
-            kmax_cur = wave_max(kn_next);
+            // tile kt+1 must have landed: only this step's loads (tile kt+2) may still be in flight
+            if (ahead) __builtin_amdgcn_s_waitcnt(vmcnt_wait(NLOAD));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
         }
         __syncthreads();
-    }
-
-    // offsets in the O layout: lane holds column (lane & 15) of block (qt, hf); the S layout lane
-    // holding that column is 16 hf + (lane & 15)
-    float mo[2][2];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) mo[qt][hf] = __shfl(mrun[qt], 16 * hf + (lane & 15));
-
-    if (nchunks > 1) {
-        // ---------------------------------------------------------- split-KV: store, count, merge
-        const int64_t slot_base = rank * (int64_t)a.ncmax;
-        float* mine = a.part + ((slot_base + chunk) * 256 + w * 64 + lane) * (NREG + 4);
-        int r = 0;
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-                for (int db = 0; db < DBX; ++db)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) mine[r++] = oacc[qt][hf][db][i];
-                mine[NREG + 2 * qt + hf] = mo[qt][hf];
-            }
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) {
-            const int prev = atomicAdd(&a.counters[rank], 1);
-            last_flag = (prev == nchunks - 1) ? 1 : 0;
-        }
-        __syncthreads();
-        if (!last_flag) return;
-        __threadfence();
-        // merge every chunk's partial into oacc (max offset, rescale, add)
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                float M = -INFINITY;
-                for (int c = 0; c < nchunks; ++c) {
-                    const float* pc = a.part + ((slot_base + c) * 256 + w * 64 + lane) * (NREG + 4);
-                    M = __builtin_fmaxf(M, pc[NREG + 2 * qt + hf]);
-                }
-                if (M == -INFINITY) M = 0.f;
-#pragma unroll
-                for (int db = 0; db < DBX; ++db) oacc[qt][hf][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                for (int c = 0; c < nchunks; ++c) {
-                    const float* pc = a.part + ((slot_base + c) * 256 + w * 64 + lane) * (NREG + 4);
-                    const float mc = pc[NREG + 2 * qt + hf];
-                    const float sc = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
-                    const int base = (qt * 2 + hf) * DBX * 4;
-#pragma unroll
-                    for (int db = 0; db < DBX; ++db)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) oacc[qt][hf][db][i] += sc * pc[base + db * 4 + i];
-                }
-            }
-        if (tid == 0) a.counters[rank] = 0;  // ready for the next forward
     }
 
     // ---------------------------------------------------------------- normalise and store
@@ -453,40 +427,6 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
 
 }  // namespace
 
-// Workspace needs of the attention kernel for one forward (split-KV partials and counters).
-void attn_plan(const GqeDims& D, int64_t B, int64_t S, int64_t* items, int* ncmax, int* kch) {
-    int64_t total = 0, tiles = 0;
-    auto cls = [&](int nh, int ngroups) {
-        const int P = kCols / nh;
-        const int64_t J = ceil_div(S, P);
-        total += B * ngroups * J;
-        for (int64_t j = 0; j < J; ++j) {
-            const int64_t E = std::min<int64_t>((j + 1) * P, S);
-            tiles += B * ngroups * ceil_div(E, kBN);
-        }
-    };
-    if (D.s) {
-        cls(D.k + 1, 1);
-        if (D.G > 1) cls(D.k, D.G - 1);
-    } else {
-        cls(D.k, D.G);
-    }
-    // chunk length: at least 32 tiles, else about a quarter of the average load of one of the 512
-    // concurrent work items (2 per CU), so that the longest item no longer dominates
-    const int64_t slots = 512;
-    const int64_t c = std::max<int64_t>(32, tiles / (slots * 4) * 2);
-    const int64_t longest = ceil_div(S, kBN);
-    *kch = (int)std::min<int64_t>(c, longest);
-    *ncmax = (int)ceil_div(longest, *kch);
-    *items = total;
-}
-
-size_t attn_partial_bytes(const GqeDims& D, int64_t items, int ncmax) {
-    if (ncmax <= 1) return 0;
-    const int DBX = D.dh / 16 + 1;
-    return (size_t)items * ncmax * 256 * (2 * 2 * DBX * 4 + 4) * sizeof(float);
-}
-
 hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st) {
     AttnArgs a{};
     a.Q = (const bf16_t*)(ws + P.q);
@@ -494,8 +434,6 @@ hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipSt
     a.Vt = (const bf16_t*)(ws + P.vt);
     a.kn = (const float*)(ws + P.kn);
     a.O = (bf16_t*)(ws + P.o);
-    a.part = (float*)(ws + P.attn_part);
-    a.counters = (int*)(ws + P.attn_cnt);
     a.S = P.S;
     a.S_pad = P.S_pad;
     a.B = (int)P.B;
@@ -504,8 +442,6 @@ hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipSt
     a.k = D.k;
     a.skv = D.skv;
     a.s = D.s;
-    a.kch = P.attn_kch;
-    a.ncmax = P.attn_ncmax;
     int64_t total = 0;
     auto add_class = [&](int nh, int ngroups, bool single) {
         const int c = a.ncls++;
@@ -523,10 +459,17 @@ hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipSt
     } else {
         add_class(D.k, D.G, false);
     }
-    const int64_t grid = total * a.ncmax;
-    if (total != P.attn_items || grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
-    if (a.ncmax > 1) {
-        zero_ints_kernel<<<(unsigned)ceil_div(total, 256), 256, 0, st>>>(a.counters, total);
+    const int64_t grid = total;
+    if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
+    a.knt = (const float*)(ws + P.knt);
+    {
+        const int64_t BG = P.B * D.G;
+        const int64_t work = BG * (P.S_pad / 64) + BG * D.dh * (P.S_pad - P.S);
+        const unsigned pg = (unsigned)std::min<int64_t>(ceil_div(work, 256), 1024);
+        attn_prep_kernel<<<pg, 256, 0, st>>>(a.kn, (float*)(ws + P.knt), (bf16_t*)(ws + P.vt), BG, P.S, P.S_pad,
+                                             D.dh);
+    }
+    {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
