@@ -53,3 +53,31 @@ __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { ret
 __host__ __device__ __forceinline__ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 #define GQE_KV_TILE 64  // keys per attention tile; K and V^T are padded to a multiple of this
+
+// ---------------------------------------------------------------- direct global -> LDS loads
+// One wave-wide global_load_lds_dwordx4: lane i's 16 bytes from gsrc land in LDS at
+// ldst + 16 i (ldst wave-uniform).  Written as inline assembly so that the compiler does not
+// order every later LDS read behind it; the kernels wait for these loads themselves (vmcnt)
+// before the barrier that publishes a stage.  No register of the asm is an output.
+__device__ __forceinline__ void dma16(const void* gsrc, const void* ldst) {
+    const uint32_t m0v = (uint32_t)(uintptr_t)ldst;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_nop 4"
+                 :
+                 : "s"(m0v), "v"(gsrc)
+                 : "memory", "m0");
+}
+
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, const void* ldst) {
+    const uint32_t m0v = (uint32_t)(uintptr_t)ldst;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_nop 4"
+                 :
+                 : "s"(m0v), "v"(voff), "s"(gbase)
+                 : "memory", "m0");
+}
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory operations are
+// outstanding and leaves the other counters unconstrained.
+__host__ __device__ constexpr int vmcnt_wait(int n) {
+    return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8);
+}

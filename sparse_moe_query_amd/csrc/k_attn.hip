@@ -140,10 +140,6 @@ __device__ __forceinline__ int kswz(int r) {
     else return 0;  // d_h = 48: a 96-byte pitch already spreads eight rows over distinct groups
 }
 
-// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory operations are
-// outstanding and leaves the other counters unconstrained.
-constexpr int vmcnt_wait(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o));
@@ -234,16 +230,6 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
     // Three stages: while tile kt computes, tile kt+1 has landed or is landing and tile kt+2 is
     // in flight.  Every wave issues the same number of loads per tile (segments past the end are
     // re-issued, same bytes), so the wait is a compile-time vmcnt.
-    auto dma16 = [&](const void* gsrc, const uint16_t* ldst) {
-        // One wave-wide 16-byte-per-lane load straight into LDS at m0 + 16 * lane.  Written as
-        // inline assembly so that the compiler does not order every later LDS read behind it; the
-        // loop waits for these loads itself (vmcnt) before the barrier that publishes a stage.
-        const uint32_t m0v = (uint32_t)(uintptr_t)ldst;
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_nop 4"
-                     :
-                     : "s"(m0v), "v"(gsrc)
-                     : "memory", "m0");
-    };
     auto issue = [&](int kt, int stage) {
         const int64_t key0 = (int64_t)kt * kBN;
 #pragma unroll

@@ -5,16 +5,19 @@
 // computed.  All of them read the same token rows, so one kernel does them all:
 //
 //   work item = (tile of 128 tokens, 4 head blocks); head block = d_h output columns of one of
-//               K_g, V_g, the shared query head, or routed expert e
-//   x tile     staged once in LDS per 32-wide slice of the hidden dimension, shared by the four
-//              waves (one wave per head block)
+//               K_g, V_g, the shared query head, or routed expert e; one wave per head block
+//   pipeline   per 64-wide slice of the hidden dimension, the x tile (128 x 64) and the four head
+//              blocks' weights (4 d_h x 64, pre-transposed by gqe_pack_weights) go straight from
+//              global memory into LDS (global_load_lds_dwordx4 into XOR-swizzled 16-byte chunks,
+//              so fragment reads are bank-conflict free); two LDS stages, the next slice in
+//              flight while the current one multiplies; the x tile is shared by the four waves
 //   routed     tile-local token-to-expert bucketing: for its expert e the wave scans the tile's
 //              routing decisions with a ballot (histogram = popcount, exclusive prefix = masked
 //              popcount) and gathers the matching rows into a contiguous LDS slice; only those
 //              rows are multiplied (no capacity, no dropped tokens; empty slices do no work)
-//   products   v_mfma_f32_16x16x32_bf16; K/Q blocks compute C^T = W^T x^T so each lane stores four
-//              consecutive head-dim values; V blocks compute C = x W so each lane stores four
-//              consecutive keys of V^T (slotted by vt_pos, see k_attn)
+//   products   v_mfma_f32_16x16x32_bf16 computing C^T = W^T x^T, one straight-line body for every
+//              wave; each lane ends with four consecutive head-dim values of one token (K/Q rows
+//              are stored as 8-byte vectors, V goes to V^T [dim][key], keys slotted by vt_pos)
 //   epilogue   queries are stored multiplied by log2(e)/sqrt(d_h) (the attention scale, folded in
 //              before the single rounding to bf16); every key's norm is stored for the attention
 //              kernel's range test
@@ -24,8 +27,7 @@
 namespace {
 
 constexpr int kBM = 128;   // tokens per tile
-constexpr int kKC = 32;    // hidden-dim slice per LDS stage
-constexpr int kXP = kKC + 8;  // LDS pitch of the x tile (elements)
+constexpr int kKC = 64;    // hidden-dim slice per LDS stage (8 chunks of 16 bytes per row)
 
 struct ProjArgs {
     const bf16_t* x;
@@ -40,12 +42,45 @@ struct ProjArgs {
     int d, G, k, n, H, s, dense, HB, njobs, ntiles;
 };
 
+// Element offset of (row, 16-byte chunk c) in an LDS stage of [rows][64] bf16 whose chunks are
+// XOR-swizzled by the row: the 16 rows one fragment read touches hit distinct bank groups.
+__device__ __forceinline__ int swz64(int row, int c) { return (row * 8 + (c ^ (row & 7))) * 8; }
+
+// One 64-wide slice of the hidden dimension for one wave: C^T += W^T x^T over the eight row
+// blocks myrow[] of the x stage and the wave's d_h weight rows.  Every wave runs this same
+// straight-line body (routed slices too, on their gathered rows; padding rows are not stored),
+// so the accumulators stay in place across the loop.
 template <int DH>
-__global__ void __launch_bounds__(256, 2) proj_kernel(ProjArgs a) {
+__device__ __forceinline__ void mma_slice(f32x4_t (&acc)[8][DH / 16], const uint16_t* xb, const uint16_t* wb,
+                                          const int (&xrow)[8], int wrow, int lane) {
     constexpr int CB = DH / 16;
-    __shared__ __align__(16) uint16_t xs[2][kBM * kXP];
-    __shared__ uint16_t rows[4][kBM];   // per wave: gathered tile rows (| rank << 8)
-    __shared__ int nrows_s[4];
+#pragma unroll
+    for (int ks = 0; ks < kKC / 32; ++ks) {
+        const int c = 4 * ks + (lane >> 4);
+        bf16x8_t wf[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+            wf[cb] = *reinterpret_cast<const bf16x8_t*>(wb + swz64(wrow + 16 * cb + (lane & 15), c));
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb) {
+            const bf16x8_t xf = *reinterpret_cast<const bf16x8_t*>(xb + swz64(xrow[rb], c));
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+                acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[cb], xf, acc[rb][cb], 0, 0, 0);
+        }
+    }
+}
+
+template <int DH>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) proj_kernel(ProjArgs a) {
+    constexpr int CB = DH / 16;
+    constexpr int LX = kBM * kKC * 2 / 1024 / 4;       // 1 KB x segments per wave per stage
+    constexpr int LW = 4 * DH * kKC * 2 / 1024 / 4;    // 1 KB weight segments per wave per stage
+    __shared__ __align__(1024) uint16_t xs[2][kBM * kKC];
+    __shared__ __align__(1024) uint16_t wls[2][4 * DH * kKC];
+    // per wave: gathered tile rows (| rank << 8); lives in x stage 1 until the first slice is
+    // loaded into it (each lane keeps the entries it needs in registers)
+    uint16_t (*rows)[kBM] = reinterpret_cast<uint16_t (*)[kBM]>(&xs[1][0]);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -60,6 +95,8 @@ __global__ void __launch_bounds__(256, 2) proj_kernel(ProjArgs a) {
         tile = L / a.njobs;
         job = L % a.njobs;
     }
+    tile = __builtin_amdgcn_readfirstlane(tile);  // keep the tile's addresses in scalar registers
+    job = __builtin_amdgcn_readfirstlane(job);
     const int64_t t0 = (int64_t)tile * kBM;
     const int hb = job * 4 + w;
     const bool active = hb < a.HB;
@@ -70,6 +107,35 @@ __global__ void __launch_bounds__(256, 2) proj_kernel(ProjArgs a) {
     const bool is_expert = active && hb >= ebase;
     const int e = hb - ebase;
     const int g_of = is_expert ? e / a.n : (hb < GD ? hb : hb - GD);
+
+    // ---- stage loader: each wave moves LX segments of the x tile (rows past the last token
+    // repeat it) and LW segments of the weights (a head block past the last one reads block 0)
+    // per-lane byte offsets are loop invariant; the slice index moves the (scalar) bases
+    const int hb0 = job * 4;
+    uint32_t xoff[LX], woff[LW];
+#pragma unroll
+    for (int i = 0; i < LX; ++i) {
+        const int q = (w + 4 * i) * 64 + lane;
+        const int r = q >> 3, c = (q & 7) ^ (r & 7);
+        const int64_t rem = a.T - 1 - t0;
+        xoff[i] = (uint32_t)(((r < rem ? r : rem) * a.d + 8 * c) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < LW; ++i) {
+        const int q = (w + 4 * i) * 64 + lane;
+        const int r = q >> 3, c = (q & 7) ^ (r & 7);
+        int h = hb0 + r / DH;
+        if (h >= a.HB) h = 0;
+        woff[i] = (uint32_t)(((h * DH + r % DH) * a.d + 8 * c) * 2);
+    }
+    const bf16_t* xbase = a.x + t0 * a.d;
+    auto issue = [&](int kc, int stage) {
+#pragma unroll
+        for (int i = 0; i < LX; ++i) dma16(xbase + kc * kKC, xoff[i], &xs[stage][(w + 4 * i) * 512]);
+#pragma unroll
+        for (int i = 0; i < LW; ++i) dma16(a.wproj + kc * kKC, woff[i], &wls[stage][(w + 4 * i) * 512]);
+    };
+    issue(0, 0);
 
     // ---- rows of this wave (tile-local bucketing for a routed expert)
     int nrows;
@@ -99,30 +165,8 @@ __global__ void __launch_bounds__(256, 2) proj_kernel(ProjArgs a) {
         const int rank = is_expert ? e % a.n : 0;  // all-active GQA: expert j of a group is head j
         for (int i = lane; i < kBM; i += 64) rows[w][i] = (uint16_t)(i | (rank << 8));
     }
-    if (lane == 0) nrows_s[w] = nrows;
     nrows = __builtin_amdgcn_readfirstlane(nrows);
     const int nrb = (nrows + 15) / 16;
-
-    // ---- x tile loader: 128 rows x 32 columns = 512 chunks of 16 bytes, 2 per thread
-    u32x4_t xr[2];
-    auto gload = [&](int kc) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int ch = tid + 256 * u;
-            const int r = ch >> 2, c = ch & 3;
-            int64_t t = t0 + r;
-            if (t >= a.T) t = a.T - 1;
-            xr[u] = *reinterpret_cast<const u32x4_t*>(a.x + t * a.d + (int64_t)kc * kKC + 8 * c);
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int ch = tid + 256 * u;
-            const int r = ch >> 2, c = ch & 3;
-            *reinterpret_cast<u32x4_t*>(&xs[buf][r * kXP + 8 * c]) = xr[u];
-        }
-    };
 
     f32x4_t acc[8][CB];
 #pragma unroll
@@ -130,121 +174,79 @@ __global__ void __launch_bounds__(256, 2) proj_kernel(ProjArgs a) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const bf16_t* wb = a.wproj + (int64_t)(active ? hb : 0) * DH * a.d;
     const int nk = a.d / kKC;
-    gload(0);
-    __syncthreads();  // rows[] visible
-    lstore(0);
-    __syncthreads();
-    // my gathered row indices for the 8 row blocks (lane's row = rows[16 rb + lane%16])
-    int myrow[8];
+    // my gathered entry for each row block (lane's row = rows[16 rb + lane % 16]); rows[] is
+    // written and read by its own wave only, the barrier below frees stage 1 for the loads
+    int myrow[8], xrow[8];  // row | rank << 8, and the row alone
 #pragma unroll
-    for (int rb = 0; rb < 8; ++rb) myrow[rb] = rows[w][(16 * rb + (lane & 15)) & (kBM - 1)] & 0xff;
+    for (int rb = 0; rb < 8; ++rb) {
+        myrow[rb] = rows[w][16 * rb + (lane & 15)];
+        xrow[rb] = myrow[rb] & 0xff;
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+    __syncthreads();  // stage 0 visible, stage 1 free
 
-    bf16x8_t wf[CB];
-    auto wload = [&](int kc) {
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-            wf[cb] = *reinterpret_cast<const bf16x8_t*>(wb + (int64_t)(16 * cb + (lane & 15)) * a.d + (int64_t)kc * kKC + 8 * (lane >> 4));
-    };
-    if (active) wload(0);
     for (int kc = 0; kc < nk; ++kc) {
-        const int buf = kc & 1;
-        if (kc + 1 < nk) gload(kc + 1);
-        bf16x8_t wcur[CB];
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) wcur[cb] = wf[cb];
-        if (active && kc + 1 < nk) wload(kc + 1);
-        if (active) {
-            const uint16_t* xb = xs[buf];
-#pragma unroll
-            for (int rb = 0; rb < 8; ++rb) {
-                if (rb < nrb) {
-                    const bf16x8_t xf = *reinterpret_cast<const bf16x8_t*>(xb + myrow[rb] * kXP + 8 * (lane >> 4));
-#pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) {
-                        if (is_v)
-                            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, wcur[cb], acc[rb][cb], 0, 0, 0);
-                        else
-                            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wcur[cb], xf, acc[rb][cb], 0, 0, 0);
-                    }
-                }
-            }
-        }
-        if (kc + 1 < nk) lstore(buf ^ 1);
+        const int stage = kc & 1;
+        if (kc + 1 < nk) issue(kc + 1, stage ^ 1);
+        mma_slice<DH>(acc, xs[stage], wls[stage], xrow, w * DH, lane);
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
         __syncthreads();
     }
     if (!active) return;
 
-    // ---- epilogue
-    const int64_t S = a.S;
+    // ---- epilogue: acc[rb][cb] lane holds row 16 rb + (lane & 15) of the slice, head dims
+    // 16 cb + 4 (lane >> 4) + 0..3
+    const uint32_t S = (uint32_t)a.S;  // the host limits a call to 2^28 tokens
 #pragma unroll
     for (int rb = 0; rb < 8; ++rb) {
         if (rb >= nrb) continue;
-        if (!is_v) {
-            // C^T tile: lane holds token column (lane & 15), head dims 16cb + 4(lane>>4) + 0..3
-            const int li = 16 * rb + (lane & 15);
-            const bool ok = li < nrows;
-            const int packed = rows[w][li & (kBM - 1)];
-            const int row = packed & 0xff, rank = packed >> 8;
-            const int64_t t = t0 + row;
-            const int64_t b = t / S, sp = t % S;
-            if (hb < GD) {
-                // key: also its norm (the four lane groups hold complementary dims)
-                float ss = 0.f;
+        const int li = 16 * rb + (lane & 15);
+        const bool ok = li < nrows;
+        const int row = myrow[rb] & 0xff, rank = myrow[rb] >> 8;
+        const uint32_t t = (uint32_t)(t0 + row);
+        const uint32_t b = t / S, sp = t - b * S;
+        if (hb < GD) {
+            // key: also its norm (the four lane groups hold complementary dims)
+            float ss = 0.f;
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
+            for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) ss += acc[rb][cb][i] * acc[rb][cb][i];
-                ss += __shfl_xor(ss, 16);
-                ss += __shfl_xor(ss, 32);
-                if (!ok) continue;
-                if ((lane >> 4) == 0) a.kn[((int64_t)b * a.G + hb) * a.S_pad + sp] = sqrtf(ss);
-                bf16_t* dst = a.K + (((int64_t)b * a.G + hb) * a.S_pad + sp) * DH;
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    const f32x4_t v = acc[rb][cb];
-                    u32x2_t pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                    *reinterpret_cast<u32x2_t*>(dst + 16 * cb + 4 * (lane >> 4)) = pk;
-                }
-                continue;
-            }
+                for (int i = 0; i < 4; ++i) ss += acc[rb][cb][i] * acc[rb][cb][i];
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
             if (!ok) continue;
-            bf16_t* dst;
-            if (!is_expert) dst = a.Q + (((int64_t)b * a.H + a.G * a.k) * S + sp) * DH;  // shared head
-            else dst = a.Q + (((int64_t)b * a.H + g_of * a.k + rank) * S + sp) * DH;
-            const float qs = a.qscale;
+            if ((lane >> 4) == 0) a.kn[((int64_t)b * a.G + hb) * a.S_pad + sp] = sqrtf(ss);
+            bf16_t* dst = a.K + (((int64_t)b * a.G + hb) * a.S_pad + sp) * DH;
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
-                const f32x4_t v = acc[rb][cb] * qs;
+                const f32x4_t v = acc[rb][cb];
                 u32x2_t pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
                 *reinterpret_cast<u32x2_t*>(dst + 16 * cb + 4 * (lane >> 4)) = pk;
             }
-        } else {
-            // C tile: lane holds head dim 16cb + (lane & 15), tokens 16rb + 4(lane>>4) + 0..3
+            continue;
+        }
+        if (!ok) continue;
+        if (is_v) {
+            // V^T [dim][key]: this lane's token is one key of four consecutive dim rows
             const int g = hb - GD;
-            const int r0 = 16 * rb + 4 * (lane >> 4);
-            const int64_t t = t0 + r0;
-            const int64_t b = t / S, sp = t % S;
-            const bool vec = (sp % 4 == 0) && (sp + 3 < S) && (t + 3 < a.T);
+            uint16_t* dst = reinterpret_cast<uint16_t*>(a.Vt) + ((int64_t)b * a.G + g) * DH * a.S_pad + vt_pos(sp);
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                const int dim = 16 * cb + (lane & 15);
-                const f32x4_t v = acc[rb][cb];
-                if (vec) {
-                    bf16_t* dst = a.Vt + (((int64_t)b * a.G + g) * DH + dim) * a.S_pad + vt_pos(sp);
-                    u32x2_t pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                    *reinterpret_cast<u32x2_t*>(dst) = pk;
-                } else {
+            for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int64_t ti = t + i;
-                        if (ti >= a.T) break;
-                        const int64_t bi = ti / S, si = ti % S;
-                        a.Vt[(((int64_t)bi * a.G + g) * DH + dim) * a.S_pad + vt_pos(si)] = from_f32<bf16_t>(v[i]);
-                    }
-                }
-            }
+                for (int i = 0; i < 4; ++i)
+                    dst[(int64_t)(16 * cb + 4 * (lane >> 4) + i) * a.S_pad] = from_f32<bf16_t>(acc[rb][cb][i]).bits;
+            continue;
+        }
+        bf16_t* dst;
+        if (!is_expert) dst = a.Q + (((int64_t)b * a.H + a.G * a.k) * S + sp) * DH;  // shared head
+        else dst = a.Q + (((int64_t)b * a.H + g_of * a.k + rank) * S + sp) * DH;
+        const float qs = a.qscale;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const f32x4_t v = acc[rb][cb] * qs;
+            u32x2_t pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            *reinterpret_cast<u32x2_t*>(dst + 16 * cb + 4 * (lane >> 4)) = pk;
         }
     }
 }
@@ -275,6 +277,7 @@ hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x, 
     a.HB = pl.hb_total;
     a.njobs = (a.HB + 3) / 4;
     a.ntiles = (int)ceil_div(P.T, kBM);
+    if (D.d % kKC != 0) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)((int64_t)a.ntiles * a.njobs);
     switch (D.dh) {
         case 32: proj_kernel<32><<<grid, 256, 0, st>>>(a); break;
