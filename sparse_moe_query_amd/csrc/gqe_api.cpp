@@ -75,12 +75,14 @@ PackedLayout make_packed_layout(const GqeDims& D, bool mfma) {
     L.br64 = take((size_t)D.N * 8);
     L.hb_total = 2 * D.G + D.s + D.N;
     L.slots = D.dense ? D.N : D.N + (D.variant == GQE_VARIANT_GQE ? D.G : 0) + D.s;
-    L.ktot_pad = (int)round_up((int64_t)L.slots * D.dh, 32);
+    L.wo_pitch = 0;
+    L.wproj = L.wo = 0;
     if (mfma) {
         L.wproj = take((size_t)L.hb_total * D.dh * D.d * 2);
-        L.wo = take((size_t)D.d * L.ktot_pad * 2);
-    } else {
-        L.wproj = L.wo = 0;
+        if (combine_mfma_supported(D)) {
+            L.wo_pitch = combine_stage_pitch(D.dh);
+            L.wo = take((size_t)D.d * L.slots * L.wo_pitch * 16);
+        }
     }
     L.total = off;
     return L;
@@ -161,7 +163,7 @@ int gqe_init(const gqe_config_t* cfg, const gqe_weights_t* w, gqe_handle_t** out
     h->mfma = mfma_supported(D);
     h->mfma_attn = D.dtype == GQE_DTYPE_BF16 && (dh == 32 || dh == 48 || dh == 64) && D.H <= 64;
     h->mfma_proj = h->mfma;
-    h->mfma_combine = h->mfma && D.d % 128 == 0;
+    h->mfma_combine = h->mfma && combine_mfma_supported(D);
     h->pl = make_packed_layout(D, h->mfma);
     h->packed = nullptr;
     h->ran = false;

@@ -18,11 +18,11 @@ struct GqeDims {
 struct PackedLayout {
     size_t wr64, br64;   // router weights in float64 (d x N rounded up to 16) and biases
     size_t wproj;        // bf16 path: head blocks [HB][dh][d] (K_g, V_g, shared Q, W_q[e])
-    size_t wo;           // bf16 path: stacked output projection [d][Ktot], Ktot = slots * dh
+    size_t wo;           // bf16 path: stacked output projection as per-(column tile, slot) stages
     size_t total;
     int hb_total;        // number of projection head blocks
     int slots;           // output-projection slots (expert slots, renormalised slots, shared)
-    int ktot_pad;        // slots * dh rounded up to 32 (zero columns past the last slot)
+    int wo_pitch;        // 16-byte chunks per output column of one W_stack stage (0: not packed)
 };
 
 // Byte offsets into the caller's workspace for one [B, S] forward.
@@ -76,5 +76,7 @@ hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x,
                             const void* packed, const PackedLayout& pl, char* ws,
                             hipStream_t st);
 hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st);
+bool combine_mfma_supported(const GqeDims& D);
+int combine_stage_pitch(int dh);
 hipError_t launch_combine_mfma(const GqeDims& D, const WorkPlan& P, const void* packed,
                                const PackedLayout& pl, void* y, char* ws, hipStream_t st);

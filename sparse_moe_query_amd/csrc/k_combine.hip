@@ -9,12 +9,23 @@
 //     A[t, rslot g]  = sum_r w_r O[t, (g, r)]            (gqe only)
 //     A[t, shared]   = O[t, shared]
 // the layer output is y = A @ W_stack, W_stack = [W_o[g*n..g*n+n-1]; W_oR[g] for g; W_os].
-// The weighted combine is fused into the GEMM: A is built tile by tile in LDS straight from
-// O_act and the routing decisions, never written to HBM.
+// A is never materialised: its fragments are formed in registers from the head outputs.
 //
-// Tile: 128 tokens x 128 output columns, K in 32-wide stages (two 16-wide pieces, each inside one
-// slot); four waves in 2 x 2, each 64 x 64 = 2 x 2 blocks of v_mfma_f32_32x32x16_bf16 computing
-// y^T = W_stack^T A^T so every lane stores four consecutive output columns.
+// Work item: 128 tokens x 128 output columns; four waves in 2 x 2, each 64 x 64 = 2 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16 computing y^T = W_stack^T A^T (every lane stores four consecutive
+// output columns).  The reduction runs slot by slot (one stage = d_h rows of W_stack):
+//   W_stack   pre-packed per (column tile, slot) as the exact LDS image ([128 cols][odd pitch]
+//             16-byte chunks, zero pad chunk) and copied by global_load_lds_dwordx4 into a ring
+//             of three stages, two slots ahead of the one being multiplied
+//   O         the rows of one unit (a group's k heads, or the shared head) for the 128 tokens are
+//             copied the same way into one of two buffers when the previous unit starts
+//   routing   the tile's choices (and coefficients where needed) are staged in LDS once; each
+//             lane keeps those of its two tokens for the current group in registers
+//   fragments a token fragment (8 consecutive head dims of one token) is the LDS chunk of the
+//             chosen head (copy), that chunk or zero (select), or a coefficient-weighted sum of
+//             the group's heads rounded once to bf16 (scale); with one choice per group the
+//             renormalised weight is exactly 1 (p / p), so the gqe slot is a copy
+// No compiler-visible global load sits in the loop, so every wait is an explicit vmcnt.
 #include "gqe_common.h"
 #include "gqe_internal.h"
 
@@ -22,33 +33,44 @@ namespace {
 
 constexpr int kBM = 128;
 constexpr int kBN = 128;
-constexpr int kKC = 32;
-constexpr int kAP = kKC + 8;  // LDS pitches (elements)
-constexpr int kBP = kKC + 8;
+constexpr int kGKMax = 16;  // routing entries per token staged in LDS (groups x choices)
+
+__host__ __device__ constexpr int odd_pitch(int chunks) { return (chunks & 1) ? chunks : chunks + 1; }
 
 struct CombArgs {
     const bf16_t* O;       // [T][H][DH]
-    const bf16_t* wo;      // [d][Ktot]
+    const bf16_t* wo;      // [d / 128][NS][128][PW * 8]
     const int32_t* idx;    // [T][G][k]
     const float* wsel;     // [T][G][k]
     const float* psel;     // [T][G][k]
     bf16_t* y;             // [T][d]
     int64_t T;
-    int d, G, k, n, H, s, dense, variant, slots, per_group, ktot;
+    int d, G, k, n, H, variant, dense, s;
+    int NS;        // stages (slots)
+    int PG;        // stages per unit (n + rslot; 1 when every head is its own unit)
+    int NUM;       // units before the shared head's
+    int KHU;       // heads per unit
 };
 
-template <int DH>
-__global__ void __launch_bounds__(256, 2) combine_kernel(CombArgs a) {
-    constexpr int PPS = DH / 16;  // 16-wide pieces per slot
-    __shared__ __align__(16) uint16_t as[2][kBM * kAP];
-    __shared__ __align__(16) uint16_t bs[2][kBN * kBP];
+template <int DH, int KH, bool COEF>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) combine_kernel(CombArgs a) {
+    constexpr int C8 = DH / 8;                // 16-byte chunks per head row
+    constexpr int PW = odd_pitch(C8);         // W_stack stage pitch (chunks per output column)
+    constexpr int PO = odd_pitch(KH * C8);    // O stage pitch (chunks per token)
+    constexpr int SEGW = kBN * PW * 16 / 1024, LW = (SEGW + 3) / 4;
+    constexpr int SEGO = kBM * PO * 16 / 1024, LO = (SEGO + 3) / 4;
+    constexpr int KS = DH / 16;
+    __shared__ __align__(1024) uint16_t wl[3][kBN * PW * 8];
+    __shared__ __align__(1024) uint16_t ol[2][kBM * PO * 8];
+    __shared__ uint8_t rj[kBM * kGKMax];          // expert index inside the group, per choice
+    __shared__ float rc[COEF ? kBM * kGKMax : 1]; // p (weighted_concat) or w (gqe) per choice
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w >> 1, wn = w & 1;
     const int ncol = a.d / kBN;
     const int ntile = (int)ceil_div(a.T, kBM);
-    // XCD-aware: the column tiles of one token tile run on one XCD (they share O_act rows)
+    // XCD-aware: the column tiles of one token tile run on one XCD (they share the O rows)
     int tile, ct;
     const int L = blockIdx.x;
     if (ntile % 8 == 0) {
@@ -59,77 +81,67 @@ __global__ void __launch_bounds__(256, 2) combine_kernel(CombArgs a) {
         tile = L / ncol;
         ct = L % ncol;
     }
+    tile = __builtin_amdgcn_readfirstlane(tile);
+    ct = __builtin_amdgcn_readfirstlane(ct);
     const int64_t t0 = (int64_t)tile * kBM;
-    const int c0 = ct * kBN;
+    const int NU = a.NUM + a.s;  // units, the shared head's last
 
-    // ---- A stage: 128 tokens x 2 pieces x 16 = 512 half-pieces of 8 elements, 2 per thread
-    u32x4_t ar[2];
-    auto build_a = [&](int kc) {
+    // ---- loaders
+    const bf16_t* wtile = a.wo + (int64_t)ct * a.NS * kBN * PW * 8;
+    auto issue_w = [&](int st) {
+        const bf16_t* src = wtile + (int64_t)st * kBN * PW * 8;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int task = tid + 256 * u;      // token = task >> 2, piece = (task >> 1) & 1, half = task & 1
-            const int row = task >> 2;
-            const int piece = kc * 2 + ((task >> 1) & 1);
-            const int half = task & 1;
-            const int slot = piece / PPS;
-            const int off = (piece % PPS) * 16 + 8 * half;
+        for (int i = 0; i < LW; ++i) {
+            const int seg = min(w + 4 * i, SEGW - 1);
+            dma16(src, (uint32_t)(seg * 1024 + 16 * lane), &wl[st % 3][seg * 512]);
+        }
+    };
+    // O rows: chunk slot q of the stage = (token row q / PO, chunk q % PO); rows past the last
+    // token repeat it, pad chunks repeat chunk 0
+    uint32_t orow[LO];
+    int ochk[LO];
+#pragma unroll
+    for (int i = 0; i < LO; ++i) {
+        const int q = min(w + 4 * i, SEGO - 1) * 64 + lane;
+        const int64_t rmax = a.T - 1 - t0;
+        const int r = q / PO;
+        orow[i] = (uint32_t)((r < rmax ? r : rmax) * a.H * DH * 2);
+        ochk[i] = q % PO;
+    }
+    auto issue_o = [&](int unit) {
+        const int nh = unit < a.NUM ? a.KHU : 1;
+        const bf16_t* base = a.O + (t0 * a.H + (int64_t)unit * a.KHU) * DH;
+#pragma unroll
+        for (int i = 0; i < LO; ++i) {
+            const int c = ochk[i] < nh * C8 ? ochk[i] : 0;
+            dma16(base, orow[i] + 16 * c, &ol[unit & 1][(min(w + 4 * i, SEGO - 1)) * 512]);
+        }
+    };
+
+    issue_o(0);
+    issue_w(0);
+    if (a.NS > 1) issue_w(1);
+
+    // ---- routing of the tile's tokens (routed mode): expert index inside the group per choice
+    if (!a.dense) {
+        const int GK = a.G * a.k;
+        for (int q = tid; q < kBM * GK; q += 256) {
+            const int row = q / GK, e = q % GK;
             const int64_t t = t0 + row;
-            float v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = 0.f;
+            uint8_t j = 0xff;
+            float c = 0.f;
             if (t < a.T) {
-                const bf16_t* ot = a.O + t * a.H * DH;
-                auto addrow = [&](int head, float c) {
-                    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(ot + head * DH + off);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        v[2 * i] += c * __uint_as_float(q[i] << 16);
-                        v[2 * i + 1] += c * __uint_as_float(q[i] & 0xffff0000u);
-                    }
-                };
-                if (slot < a.G * a.per_group) {
-                    const int g = slot / a.per_group, u2 = slot % a.per_group;
-                    const int64_t rb = (t * a.G + g) * a.k;
-                    if (u2 < a.n) {
-                        const int e = g * a.n + u2;
-                        if (a.dense) {
-                            addrow(g * a.k + u2, 1.f);
-                        } else {
-                            for (int r = 0; r < a.k; ++r)
-                                if (a.idx[rb + r] == e)
-                                    addrow(g * a.k + r, a.variant == GQE_VARIANT_WEIGHTED_CONCAT ? a.psel[rb + r] : 1.f);
-                        }
-                    } else {
-                        for (int r = 0; r < a.k; ++r) addrow(g * a.k + r, a.wsel[rb + r]);
-                    }
-                } else if (slot < a.slots) {
-                    addrow(a.G * a.k, 1.f);  // shared head
-                }                            // else: zero padding past the last slot
+                const int g = e / a.k;
+                j = (uint8_t)(a.idx[t * GK + e] - g * a.n);
+                if (COEF) c = a.variant == GQE_VARIANT_WEIGHTED_CONCAT ? a.psel[t * GK + e] : a.wsel[t * GK + e];
             }
-            ar[u] = u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                            pack_bf16x2(v[6], v[7])};
+            rj[row * kGKMax + e] = j;
+            if (COEF) rc[row * kGKMax + e] = c;
         }
-    };
-    // ---- B stage: 128 output columns x 32 k = 512 chunks, 2 per thread
-    u32x4_t br[2];
-    auto load_b = [&](int kc) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int ch = tid + 256 * u;
-            const int col = ch >> 2, c = ch & 3;
-            br[u] = *reinterpret_cast<const u32x4_t*>(a.wo + (int64_t)(c0 + col) * a.ktot + kc * kKC + 8 * c);
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int task = tid + 256 * u;
-            const int row = task >> 2, q = task & 3;  // q = 8-element column group (piece*2 + half)
-            *reinterpret_cast<u32x4_t*>(&as[buf][row * kAP + 8 * q]) = ar[u];
-            const int col = task >> 2;
-            *reinterpret_cast<u32x4_t*>(&bs[buf][col * kBP + 8 * q]) = br[u];
-        }
-    };
+    }
+    if (a.NS > 1) __builtin_amdgcn_s_waitcnt(vmcnt_wait(LW));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+    __syncthreads();
 
     f32x16_t acc[2][2];
 #pragma unroll
@@ -137,56 +149,156 @@ __global__ void __launch_bounds__(256, 2) combine_kernel(CombArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
-    const int nk = a.ktot / kKC;
-    build_a(0);
-    load_b(0);
-    lstore(0);
-    __syncthreads();
-    for (int kc = 0; kc < nk; ++kc) {
-        const int buf = kc & 1;
-        if (kc + 1 < nk) {
-            build_a(kc + 1);
-            load_b(kc + 1);
-        }
-        const uint16_t* ab = as[buf];
-        const uint16_t* bb = bs[buf];
+    const int trow0 = 64 * wm + (lane & 31);          // token rows trow0, trow0 + 32
+    const int wcol0 = 64 * wn + (lane & 31);          // output columns wcol0, wcol0 + 32
+    const int hsel = lane >> 5;                       // which 8 of the 16 reduction rows
+    int jr[2][KH];
+    float cr[2][KH];
 #pragma unroll
-        for (int ks = 0; ks < kKC / 16; ++ks) {
-            bf16x8_t af[2], bf[2];
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < KH; ++r) {
+            jr[i][r] = -1;
+            cr[i][r] = 0.f;
+        }
+
+    for (int st = 0; st < a.NS; ++st) {
+        int unit, u;
+        if (st < a.NUM * a.PG) {
+            unit = st / a.PG;
+            u = st - unit * a.PG;
+        } else {
+            unit = a.NUM;
+            u = 0;
+        }
+        // kind: 0 copy (head u of the unit in dense mode, the shared head, a gqe slot with one
+        // choice), 1 select (expert slot, coefficient 1), 2 scale (weighted expert slot, gqe slot
+        // with several choices)
+        int kind = 0;
+        if (unit < a.NUM && !a.dense) {
+            if (u == 0) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int r = 0; r < KH; ++r) {
+                        jr[i][r] = rj[(trow0 + 32 * i) * kGKMax + unit * KH + r];
+                        if (COEF) cr[i][r] = rc[(trow0 + 32 * i) * kGKMax + unit * KH + r];
+                    }
+            }
+            if (u < a.n) kind = a.variant == GQE_VARIANT_WEIGHTED_CONCAT ? 2 : 1;
+            else kind = KH == 1 ? 0 : 2;
+        }
+        // per-lane term of the select / scale kinds
+        int off[2];
+        bool valid[2];
+        float coef[2][KH];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            off[i] = 0;
+            valid[i] = true;
+            if (kind == 1) {
+                valid[i] = false;
+#pragma unroll
+                for (int r = 0; r < KH; ++r)
+                    if (jr[i][r] == u) {
+                        valid[i] = true;
+                        off[i] = r * C8;
+                    }
+            }
+#pragma unroll
+            for (int r = 0; r < KH; ++r)
+                coef[i][r] = (u < a.n) ? (jr[i][r] == u ? cr[i][r] : 0.f) : cr[i][r];
+        }
+
+        // issue: the next unit's rows when this unit starts, then the slot two ahead
+        if (u == 0 && unit + 1 < NU) issue_o(unit + 1);
+        const bool ahead = st + 2 < a.NS;
+        if (ahead) issue_w(st + 2);
+
+        const uint16_t* wb = wl[st % 3];
+        const uint16_t* ob = ol[unit & 1];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            bf16x8_t wf[2], tf[2];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+                wf[cb] = *reinterpret_cast<const bf16x8_t*>(wb + ((wcol0 + 32 * cb) * PW + 2 * kk + hsel) * 8);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                af[i] = *reinterpret_cast<const bf16x8_t*>(ab + (64 * wm + 32 * i + (lane & 31)) * kAP + 16 * ks + 8 * (lane >> 5));
-                bf[i] = *reinterpret_cast<const bf16x8_t*>(bb + (64 * wn + 32 * i + (lane & 31)) * kBP + 16 * ks + 8 * (lane >> 5));
+                const uint16_t* orow_p = ob + ((trow0 + 32 * i) * PO + 2 * kk + hsel) * 8;
+                if (!COEF || kind != 2) {
+                    u32x4_t v = *reinterpret_cast<const u32x4_t*>(orow_p + off[i] * 8);
+                    if (!valid[i]) v = u32x4_t{0u, 0u, 0u, 0u};
+                    tf[i] = __builtin_bit_cast(bf16x8_t, v);
+                } else {
+                    float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int r = 0; r < KH; ++r) {
+                        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(orow_p + r * C8 * 8);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            f[2 * e] += coef[i][r] * __uint_as_float(v[e] << 16);
+                            f[2 * e + 1] += coef[i][r] * __uint_as_float(v[e] & 0xffff0000u);
+                        }
+                    }
+                    const u32x4_t pk = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                                        pack_bf16x2(f[6], f[7])};
+                    tf[i] = __builtin_bit_cast(bf16x8_t, pk);
+                }
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+                for (int cb = 0; cb < 2; ++cb)
+                    acc[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb], tf[i], acc[i][cb], 0, 0, 0);
         }
-        if (kc + 1 < nk) lstore(buf ^ 1);
+        if (st + 1 < a.NS) {
+            // the next slot (and, at a unit's first slot, the next unit's rows) must have landed;
+            // only the slot issued two ahead may still be in flight
+            if (ahead) __builtin_amdgcn_s_waitcnt(vmcnt_wait(LW));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+        }
         __syncthreads();
     }
 
-    // ---- epilogue: acc[i][j] is y^T for tokens 64wm + 32i + (lane & 31), columns 64wn + 32j + rows
+    // ---- epilogue: acc[i][cb] is y^T for token trow0 + 32 i, columns 64 wn + 32 cb + rows
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int64_t t = t0 + 64 * wm + 32 * i + (lane & 31);
+        const int64_t t = t0 + trow0 + 32 * i;
         if (t >= a.T) continue;
-        bf16_t* yr = a.y + t * a.d + c0 + 64 * wn;
+        bf16_t* yr = a.y + t * a.d + ct * kBN + 64 * wn;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int col = 32 * j + 8 * q + 4 * (lane >> 5);
-                u32x2_t pk = {pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                              pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+                const int col = 32 * cb + 8 * q + 4 * hsel;
+                u32x2_t pk = {pack_bf16x2(acc[i][cb][4 * q], acc[i][cb][4 * q + 1]),
+                              pack_bf16x2(acc[i][cb][4 * q + 2], acc[i][cb][4 * q + 3])};
                 *reinterpret_cast<u32x2_t*>(yr + col) = pk;
             }
     }
 }
 
+template <int DH>
+hipError_t launch_dh(const CombArgs& a, bool coef, unsigned grid, hipStream_t st) {
+    if (a.KHU == 1) {
+        if (coef) combine_kernel<DH, 1, true><<<grid, 256, 0, st>>>(a);
+        else combine_kernel<DH, 1, false><<<grid, 256, 0, st>>>(a);
+    } else {
+        combine_kernel<DH, 2, true><<<grid, 256, 0, st>>>(a);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
+
+int combine_stage_pitch(int dh) { return odd_pitch(dh / 8); }
+
+bool combine_mfma_supported(const GqeDims& D) {
+    if (D.d % kBN != 0) return false;
+    if (!D.dense && (D.k > 2 || D.G * D.k > kGKMax)) return false;
+    return true;
+}
 
 hipError_t launch_combine_mfma(const GqeDims& D, const WorkPlan& P, const void* packed,
                                const PackedLayout& pl, void* y, char* ws, hipStream_t st) {
@@ -203,19 +315,28 @@ hipError_t launch_combine_mfma(const GqeDims& D, const WorkPlan& P, const void* 
     a.k = D.k;
     a.n = D.n;
     a.H = D.H;
-    a.s = D.s;
-    a.dense = D.dense;
     a.variant = D.variant;
-    a.slots = pl.slots;
-    a.per_group = D.n + ((!D.dense && D.variant == GQE_VARIANT_GQE) ? 1 : 0);
-    a.ktot = pl.ktot_pad;
-    if (a.d % kBN != 0 || a.ktot % kKC != 0) return hipErrorInvalidValue;
+    a.dense = D.dense;
+    a.s = D.s;
+    a.NS = pl.slots;
+    if (D.dense) {
+        // every head is its own unit (head e = expert e), one slot each
+        a.PG = 1;
+        a.NUM = D.N;
+        a.KHU = 1;
+    } else {
+        a.PG = D.n + (D.variant == GQE_VARIANT_GQE ? 1 : 0);
+        a.NUM = D.G;
+        a.KHU = D.k;
+    }
+    if (!combine_mfma_supported(D)) return hipErrorInvalidValue;
+    // coefficients are needed by weighted_concat and by gqe with several choices per group
+    const bool coef = !D.dense && (D.variant == GQE_VARIANT_WEIGHTED_CONCAT || (D.variant == GQE_VARIANT_GQE && D.k > 1));
     const unsigned grid = (unsigned)(ceil_div(P.T, kBM) * (a.d / kBN));
     switch (D.dh) {
-        case 32: combine_kernel<32><<<grid, 256, 0, st>>>(a); break;
-        case 48: combine_kernel<48><<<grid, 256, 0, st>>>(a); break;
-        case 64: combine_kernel<64><<<grid, 256, 0, st>>>(a); break;
+        case 32: return launch_dh<32>(a, coef, grid, st);
+        case 48: return launch_dh<48>(a, coef, grid, st);
+        case 64: return launch_dh<64>(a, coef, grid, st);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }

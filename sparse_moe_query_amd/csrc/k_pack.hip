@@ -62,27 +62,34 @@ __global__ void pack_proj_kernel(const uint16_t* __restrict__ wk, const uint16_t
 }
 
 // dst[col][slot * dh + j] = W_slot[j][col]
+// W_stack for the matrix-core combine, as the LDS image of each (128-column tile, slot) stage:
+// dst[((ct * slots + slot) * 128 + c) * pitch * 8 + j] = W_stack[slot * dh + j][ct * 128 + c] for
+// j < dh, zero for the pad chunk (pitch = d_h / 8 rounded up to odd, in 16-byte chunks).
+// Slot order: per group its n experts then (gqe) its weighted-sum slot; the shared head last.
 __global__ void pack_wo_kernel(const uint16_t* __restrict__ wo, const uint16_t* __restrict__ wor,
                                const uint16_t* __restrict__ wos, int d, int G, int n, int dh,
-                               int rslot, int s, int slots, int ktot_pad, uint16_t* __restrict__ dst) {
-    const int64_t K = ktot_pad;
-    const int64_t total = (int64_t)d * K;
+                               int rslot, int slots, int pitch, uint16_t* __restrict__ dst) {
+    const int64_t per_col = (int64_t)pitch * 8;
+    const int64_t total = (int64_t)d * slots * per_col;
     const int per_group = n + rslot;
     for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
          q += (int64_t)gridDim.x * blockDim.x) {
-        const int col = (int)(q / K);
-        const int64_t kk = q % K;
-        const int slot = (int)(kk / dh), j = (int)(kk % dh);
-        uint16_t v;
-        if (slot >= slots) {
-            v = 0;  // padding up to a multiple of 32 columns
-        } else if (slot < G * per_group) {
-            const int g = slot / per_group, u = slot % per_group;
-            if (u < n) v = wo[((int64_t)(g * n + u) * dh + j) * d + col];
-            else v = wor[((int64_t)g * dh + j) * d + col];
-        } else {
-            (void)s;
-            v = wos[(int64_t)j * d + col];
+        const int j = (int)(q % per_col);
+        const int64_t rest = q / per_col;
+        const int c = (int)(rest % 128);
+        const int64_t rest2 = rest / 128;
+        const int slot = (int)(rest2 % slots);
+        const int ct = (int)(rest2 / slots);
+        const int col = ct * 128 + c;
+        uint16_t v = 0;
+        if (j < dh) {
+            if (slot < G * per_group) {
+                const int g = slot / per_group, u = slot % per_group;
+                if (u < n) v = wo[((int64_t)(g * n + u) * dh + j) * d + col];
+                else v = wor[((int64_t)g * dh + j) * d + col];
+            } else {
+                v = wos[(int64_t)j * d + col];
+            }
         }
         dst[q] = v;
     }
@@ -106,8 +113,9 @@ hipError_t launch_pack(const GqeDims& D, const gqe_weights_t& w, const PackedLay
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int rslot = (!D.dense && D.variant == GQE_VARIANT_GQE) ? 1 : 0;
+    if (pl.wo_pitch == 0) return hipSuccess;  // combine on the scalar path
     pack_wo_kernel<<<1024, 256, 0, st>>>((const uint16_t*)w.w_o, (const uint16_t*)w.w_o_rslot,
                                          (const uint16_t*)w.w_o_shared, D.d, D.G, D.n, D.dh, rslot,
-                                         D.s, pl.slots, pl.ktot_pad, (uint16_t*)(pk + pl.wo));
+                                         pl.slots, pl.wo_pitch, (uint16_t*)(pk + pl.wo));
     return hipGetLastError();
 }

@@ -47,6 +47,10 @@ SMALL = [
     _small("dh32_f32", d=64, N=4, G=2, k=1, dh=32, B=1, S=70, dtype="f32", router_std=0.3),
     _small("gqa_small", B=2, S=150, k=2, variant="hard_concat", shared_head=False,
            dense_gqa=True),
+    _small("dh32_bf16_k2", d=256, N=8, G=4, k=2, dh=32, B=1, S=150, seed=5),
+    _small("dh32_weighted", d=384, N=8, G=4, k=1, dh=32, B=2, S=77, variant="weighted_concat", seed=6),
+    _small("n1_groups_hard", d=512, N=8, G=8, k=1, dh=64, B=1, S=140, variant="hard_concat", seed=7),
+    _small("weighted_k2", d=512, N=16, G=4, k=2, dh=48, B=1, S=129, variant="weighted_concat", seed=8),
 ]
 
 
