@@ -58,10 +58,11 @@ __host__ __device__ __forceinline__ int64_t round_up(int64_t a, int64_t b) { ret
 // One wave-wide global_load_lds_dwordx4: lane i's 16 bytes from gsrc land in LDS at
 // ldst + 16 i (ldst wave-uniform).  Written as inline assembly so that the compiler does not
 // order every later LDS read behind it; the kernels wait for these loads themselves (vmcnt)
-// before the barrier that publishes a stage.  No register of the asm is an output.
+// before the barrier that publishes a stage.  No register of the asm is an output.  The LDS
+// destination comes from M0, which needs one wait state between its SALU write and the load.
 __device__ __forceinline__ void dma16(const void* gsrc, const void* ldst) {
     const uint32_t m0v = (uint32_t)(uintptr_t)ldst;
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_nop 4"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_nop 4"
                  :
                  : "s"(m0v), "v"(gsrc)
                  : "memory", "m0");
@@ -70,7 +71,7 @@ __device__ __forceinline__ void dma16(const void* gsrc, const void* ldst) {
 // The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset.
 __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, const void* ldst) {
     const uint32_t m0v = (uint32_t)(uintptr_t)ldst;
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_nop 4"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_nop 4"
                  :
                  : "s"(m0v), "v"(voff), "s"(gbase)
                  : "memory", "m0");

@@ -62,7 +62,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
     constexpr int KS = DH / 16;
     __shared__ __align__(1024) uint16_t wl[3][kBN * PW * 8];
     __shared__ __align__(1024) uint16_t ol[2][kBM * PO * 8];
-    __shared__ uint8_t rj[kBM * kGKMax];          // expert index inside the group, per choice
+    __shared__ __align__(16) uint8_t rj[kBM * kGKMax];  // expert index inside the group, per choice
     __shared__ float rc[COEF ? kBM * kGKMax : 1]; // p (weighted_concat) or w (gqe) per choice
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -152,6 +152,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
     const int trow0 = 64 * wm + (lane & 31);          // token rows trow0, trow0 + 32
     const int wcol0 = 64 * wn + (lane & 31);          // output columns wcol0, wcol0 + 32
     const int hsel = lane >> 5;                       // which 8 of the 16 reduction rows
+    // the choices of the lane's two tokens for every group (one byte each), kept in registers
+    u32x4_t jw[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        jw[i] = a.dense ? u32x4_t{0u, 0u, 0u, 0u} : *reinterpret_cast<const u32x4_t*>(&rj[(trow0 + 32 * i) * kGKMax]);
     int jr[2][KH];
     float cr[2][KH];
 #pragma unroll
@@ -162,33 +167,27 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
             cr[i][r] = 0.f;
         }
 
+    int unit = 0, u = 0;  // position of the stage: unit, slot inside the unit (wave-uniform)
     for (int st = 0; st < a.NS; ++st) {
-        int unit, u;
-        if (st < a.NUM * a.PG) {
-            unit = st / a.PG;
-            u = st - unit * a.PG;
-        } else {
-            unit = a.NUM;
-            u = 0;
+        const bool routed = unit < a.NUM && !a.dense;
+        if (routed && u == 0) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < KH; ++r) {
+                    const int byte = unit * KH + r, q = byte >> 2;
+                    const uint32_t dw = q == 0 ? jw[i][0] : q == 1 ? jw[i][1] : q == 2 ? jw[i][2] : jw[i][3];
+                    jr[i][r] = (int)((dw >> (8 * (byte & 3))) & 0xffu);
+                    if (COEF) cr[i][r] = rc[(trow0 + 32 * i) * kGKMax + byte];
+                }
         }
-        // kind: 0 copy (head u of the unit in dense mode, the shared head, a gqe slot with one
-        // choice), 1 select (expert slot, coefficient 1), 2 scale (weighted expert slot, gqe slot
-        // with several choices)
+        // kind: 0 copy (dense head, shared head, gqe slot with one choice), 1 select (expert slot,
+        // coefficient 1), 2 scale (weighted expert slot, gqe slot with several choices)
         int kind = 0;
-        if (unit < a.NUM && !a.dense) {
-            if (u == 0) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int r = 0; r < KH; ++r) {
-                        jr[i][r] = rj[(trow0 + 32 * i) * kGKMax + unit * KH + r];
-                        if (COEF) cr[i][r] = rc[(trow0 + 32 * i) * kGKMax + unit * KH + r];
-                    }
-            }
+        if (routed) {
             if (u < a.n) kind = a.variant == GQE_VARIANT_WEIGHTED_CONCAT ? 2 : 1;
             else kind = KH == 1 ? 0 : 2;
         }
-        // per-lane term of the select / scale kinds
         int off[2];
         bool valid[2];
         float coef[2][KH];
@@ -210,11 +209,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
                 coef[i][r] = (u < a.n) ? (jr[i][r] == u ? cr[i][r] : 0.f) : cr[i][r];
         }
 
-        // issue: the next unit's rows when this unit starts, then the slot two ahead
-        if (u == 0 && unit + 1 < NU) issue_o(unit + 1);
+        // loads of this step, spread over its k-steps so that the transfers overlap the matrix
+        // work: the next unit's rows when this unit starts, then the slot two ahead
+        const bool o_next = u == 0 && unit + 1 < NU;
         const bool ahead = st + 2 < a.NS;
-        if (ahead) issue_w(st + 2);
-
         const uint16_t* wb = wl[st % 3];
         const uint16_t* ob = ol[unit & 1];
 #pragma unroll
@@ -251,14 +249,28 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb)
                     acc[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb], tf[i], acc[i][cb], 0, 0, 0);
+            if (kk == 0 && o_next) issue_o(unit + 1);
+            if (kk == 1 && ahead) issue_w(st + 2);
         }
         if (st + 1 < a.NS) {
-            // the next slot (and, at a unit's first slot, the next unit's rows) must have landed;
-            // only the slot issued two ahead may still be in flight
-            if (ahead) __builtin_amdgcn_s_waitcnt(vmcnt_wait(LW));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+            // the next slot must have landed, and the next unit's rows if the next slot starts
+            // it; loads of this step that the next slot does not read may stay in flight
+            const bool o_pending = o_next && unit < a.NUM && u + 1 < a.PG;
+            if (ahead) {
+                if (o_pending) __builtin_amdgcn_s_waitcnt(vmcnt_wait(LW + LO));
+                else __builtin_amdgcn_s_waitcnt(vmcnt_wait(LW));
+            } else {
+                if (o_pending) __builtin_amdgcn_s_waitcnt(vmcnt_wait(LO));
+                else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+            }
         }
         __syncthreads();
+        if (unit < a.NUM && u + 1 < a.PG) {
+            ++u;
+        } else {
+            ++unit;
+            u = 0;
+        }
     }
 
     // ---- epilogue: acc[i][cb] is y^T for token trow0 + 32 i, columns 64 wn + 32 cb + rows
