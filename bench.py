@@ -1,30 +1,42 @@
 """Benchmark of the GQE forward (prefill) pass on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-long] [--only-main]
+                [--profile-workload NAME] [--copy-calibration]
 
 One step = one gqe_forward over the main-setting workload (dim 768, N=16, G=8, k=1, head_dim 48,
 shared head, variant gqe, batch 8 x seq 2048, bf16) with x and the packed weights resident in HBM.
-Prints ONE JSON line (stdout): tokens/s of that workload, the roofline of its dominant kernel
-(stage times from HIP events recorded on the forward's stream during the timed steps), the CPU
-oracle timed on a bounded sample, and -- as extra fields -- the long-context runs (seq 16384 and
-32768) with the all-active GQA baseline on the same inputs and kernels.
+Prints ONE JSON line (stdout): tokens/s of that workload (K timed forwards, bracketed by device
+synchronisations); the roofline of its dominant kernel (its algorithmic work per launch over its
+average launch duration, from HIP events recorded on the forward's stream right before and after
+every kernel during K more forwards; HBM traffic from the committed rocprofv3 counter summary
+when it was taken on the current kernel source, else null); the CPU
+oracle timed on a bounded sample; and, as extra fields, the all-active GQA baseline and the
+long-context runs (seq 16384 and 32768).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
-
-import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2500.0   # TFLOP/s, MI355X dense bf16 matrix
-PEAK_FP64 = 78.6     # TFLOP/s, MI355X fp64 vector
+PEAK_FP64 = 78.6     # TFLOP/s, MI355X fp64 (matrix and vector)
 PEAK_HBM = 8000.0    # GB/s
+
+# kernel slot -> (source file of the kernel, stage of the algorithmic-work table)
+KERNEL_SOURCES = {
+    "router": ("k_router.hip", "router"),
+    "projection": ("k_proj.hip", "projection"),
+    "attention": ("k_attn.hip", "attention"),
+    "combine": ("k_combine.hip", "combine"),
+}
 
 
 def log(*a):
@@ -32,8 +44,9 @@ def log(*a):
 
 
 def algorithmic(wl) -> dict:
-    """Algorithmic work of one forward, per stage: flops (active heads only) and HBM bytes
-    (each tensor read or written once, bf16 = 2 bytes)."""
+    """Algorithmic work of one forward, per stage: flops (active heads only; causal attention
+    counts S(S+1)/2 score entries per head) and HBM bytes (each tensor read or written once,
+    bf16 = 2 bytes)."""
     T, d, N, G, dh = wl.tokens, wl.dim, wl.num_query_experts, wl.num_kv_heads, wl.dh
     k = wl.top_k
     H = G * k + (1 if wl.shared_head else 0)
@@ -43,10 +56,10 @@ def algorithmic(wl) -> dict:
     gk = G * k
     out = {
         "router": dict(flops=0.0 if wl.dense_gqa else 2.0 * T * d * N,
-                       bytes=0.0 if wl.dense_gqa else T * d * es + T * gk * 12.0),
+                       bytes=0.0 if wl.dense_gqa else T * d * es + d * N * 8 + T * gk * 12.0),
         "projection": dict(flops=2.0 * T * d * dh * (2 * G + H),
                            bytes=T * d * es + d * dh * (2 * G + (N if wl.dense_gqa else N + (1 if wl.shared_head else 0))) * es
-                           + T * (H + 2 * G) * dh * es),
+                           + T * (H + 2 * G) * dh * es + T * G * 4.0),
         "attention": dict(flops=4.0 * dh * H * B * S * (S + 1) / 2.0,
                           bytes=(B * H * S * dh + 2 * B * G * S * dh + T * H * dh) * es),
         "combine": dict(flops=2.0 * T * d * dh * slots,
@@ -54,6 +67,29 @@ def algorithmic(wl) -> dict:
     }
     out["layer_flops"] = sum(v["flops"] for v in out.values() if isinstance(v, dict))
     return out
+
+
+def source_hash(fname: str) -> str:
+    """Hash of a kernel source and the helpers it includes (ties counter summaries to code)."""
+    h = hashlib.sha256()
+    for f in (fname, "gqe_common.h"):
+        with open(os.path.join(ROOT, "sparse_moe_query_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of ``kernel`` on ``workload`` from profiles/traffic_<kernel>_<workload>.md,
+    if that summary was taken on the current source (its 'source hash' line matches)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source hash:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"HBM bytes per launch \(scaled\):\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(KERNEL_SOURCES[kernel][0]):
+        return None
+    return float(m_bytes.group(1))
 
 
 def run_workload(wl, steps, warmup, profile=True):
@@ -64,43 +100,84 @@ def run_workload(wl, steps, warmup, profile=True):
     y = torch.empty_like(x)
     for _ in range(warmup):
         layer(x, y)
-    torch.cuda.synchronize()
-    if profile:
-        gqe.gqe_profile_enable(layer.h, True)
+    # timed steps: nothing but the forwards on the stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         layer(x, y)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    stages, n = (gqe.gqe_profile_read(layer.h) if profile else ({}, 0))
-    if profile:
-        gqe.gqe_profile_enable(layer.h, False)
     ms = (t1 - t0) * 1e3 / steps
-    stage_ms = {k: v / max(n, 1) for k, v in stages.items()}
+    # the same number of steps again with HIP events around every kernel (per-kernel durations)
+    kern, n = {}, 0
+    if profile:
+        gqe.gqe_profile_enable(layer.h, True)
+        for _ in range(steps):
+            layer(x, y)
+        torch.cuda.synchronize()
+        kern, n = gqe.gqe_profile_read_kernels(layer.h)
+        gqe.gqe_profile_enable(layer.h, False)
+    kernel_ms = {k: v / max(n, 1) for k, v in kern.items()}
     path = layer.intermediates(wl.batch, wl.seq)["matrix_core"]
     layer.close()
     del layer, x, y
     torch.cuda.empty_cache()
-    return ms, stage_ms, path
+    return ms, kernel_ms, path
 
 
-def cpu_baseline(wl):
-    """The oracle as it stands, on one sequence of the workload (all of its tokens)."""
+def stages_of(kernel_ms: dict) -> dict:
+    g = kernel_ms.get
+    return {"router": g("router", 0) + g("router_stats", 0),
+            "projection": g("projection", 0) + g("key_norms", 0),
+            "attention": g("attention_prep", 0) + g("attention", 0),
+            "combine": g("combine", 0)}
+
+
+def roofline(kernel: str, ms: float, alg: dict, workload: str) -> dict:
+    stage = KERNEL_SOURCES[kernel][1]
+    f = alg[stage]["flops"] / (ms * 1e-3) / 1e12
+    peak = PEAK_FP64 if kernel == "router" else PEAK_BF16
+    r = dict(bound="mfma", achieved=f, peak=peak, unit="TFLOP/s", frac=f / peak)
+    r["kernel"] = kernel
+    r["kernel_ms"] = ms
+    r["traffic"] = committed_traffic(kernel, workload)
+    r["algorithmic_bytes"] = alg[stage]["bytes"]
+    r["algorithmic_hbm_frac"] = alg[stage]["bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM
+    return r
+
+
+def cpu_baseline(wl, min_seconds=10.0):
+    """The oracle as it stands, on whole sequences of the workload (all of their tokens), repeated
+    over the batch until at least ``min_seconds`` of CPU work have been timed."""
     from oracle import gqe_oracle as go
     from sparse_moe_query_amd.inputs import make_inputs
-    one = wl.with_(batch=1)
-    inp = make_inputs(one)
-    cfg = go.OracleConfig(one.dim, one.num_query_experts, one.num_kv_heads, one.top_k, one.dh,
-                          one.variant, one.shared_head, one.shared_kv_group)
+    inp = make_inputs(wl)
+    cfg = go.OracleConfig(wl.dim, wl.num_query_experts, wl.num_kv_heads, wl.top_k, wl.dh,
+                          wl.variant, wl.shared_head, wl.shared_kv_group)
     go.build(force=False)
-    t0 = time.perf_counter()
-    go.forward(cfg, 1, one.seq, inp["x"], inp)
-    t1 = time.perf_counter()
+    x = inp["x"].reshape(wl.batch, wl.seq, wl.dim)
+    done, elapsed, b = 0, 0.0, 0
+    while elapsed < min_seconds:
+        t0 = time.perf_counter()
+        go.forward(cfg, 1, wl.seq, x[b % wl.batch], inp)
+        elapsed += time.perf_counter() - t0
+        done += wl.seq
+        b += 1
     threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-    return dict(value=one.tokens / (t1 - t0), unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"one sequence of the workload: batch 1 x seq {one.seq} (all tokens), "
-                       f"fp64 plain loops, {t1 - t0:.1f} s")
+    return dict(value=done / elapsed, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{b} whole sequences of the workload (seq {wl.seq}, all tokens, cycling over its "
+                       f"batch of {wl.batch}), fp64 plain loops, {elapsed:.1f} s")
+
+
+def copy_calibration(nbytes=256 << 20, reps=3):
+    """A plain device copy of known size, for scaling the HBM byte counters of a profiled run."""
+    import torch
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {reps} copies of {nbytes} bytes (read {nbytes}, write {nbytes})")
 
 
 def main():
@@ -114,6 +191,8 @@ def main():
     ap.add_argument("--profile-workload", default=None,
                     help="run only this named workload (inputs.WORKLOADS, or NAME_gqa for its "
                          "all-active GQA baseline) for --steps forwards; for profilers")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="with --profile-workload: also run a plain 256 MiB device copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
@@ -130,28 +209,25 @@ def main():
     if args.profile_workload:
         name = args.profile_workload
         wl = gqa_of(WORKLOADS[name[:-4]]) if name.endswith("_gqa") else WORKLOADS[name]
-        ms, stage_ms, _ = run_workload(wl, args.steps, args.warmup)
-        print(json.dumps({"workload": wl.name, "ms_per_step": ms, "stage_ms": stage_ms}), flush=True)
+        if args.copy_calibration:
+            copy_calibration()
+        ms, kernel_ms, _ = run_workload(wl, args.steps, args.warmup)
+        print(json.dumps({"workload": wl.name, "ms_per_step": ms, "kernel_ms": kernel_ms,
+                          "source_hash": {k: source_hash(v[0]) for k, v in KERNEL_SOURCES.items()}}),
+              flush=True)
         return
     main_wl = WORKLOADS["main_b8_s2048"]
     log(f"[bench] main workload {main_wl.name}: warmup {args.warmup}, steps {args.steps}")
-    ms, stage_ms, path = run_workload(main_wl, args.steps, args.warmup)
+    ms, kernel_ms, path = run_workload(main_wl, args.steps, args.warmup)
     alg = algorithmic(main_wl)
     tokens_s = main_wl.tokens / (ms / 1e3)
-    dom = max(stage_ms, key=lambda k: stage_ms[k])
-    log(f"[bench] {ms:.3f} ms/step, {tokens_s:.3e} tokens/s; stages (ms) {stage_ms}")
-
-    def roof(stage, sms, a):
-        f = a[stage]["flops"] / (sms * 1e-3) / 1e12
-        if stage == "router":
-            return dict(bound="alu", achieved=f, peak=PEAK_FP64, unit="TFLOP/s", frac=f / PEAK_FP64)
-        return dict(bound="mfma", achieved=f, peak=PEAK_BF16, unit="TFLOP/s", frac=f / PEAK_BF16)
-
-    roofline = roof(dom, stage_ms[dom], alg)
-    roofline["kernel"] = dom
-    roofline["traffic"] = None
-    stages = {k: dict(ms=v, **{kk: vv for kk, vv in roof(k, v, alg).items() if kk in ("achieved", "frac", "bound")})
-              for k, v in stage_ms.items() if v > 0}
+    stage_ms = stages_of(kernel_ms)
+    log(f"[bench] {ms:.3f} ms/step, {tokens_s:.3e} tokens/s; kernels (ms) {kernel_ms}")
+    dom = max(KERNEL_SOURCES, key=lambda k: kernel_ms.get(k, 0.0))
+    rl = roofline(dom, kernel_ms[dom], alg, main_wl.name)
+    kernels = {k: roofline(k, kernel_ms[k], alg, main_wl.name) for k in KERNEL_SOURCES if kernel_ms.get(k, 0) > 0}
+    kernels = {k: {kk: v[kk] for kk in ("kernel_ms", "achieved", "frac", "algorithmic_hbm_frac", "traffic")}
+               for k, v in kernels.items()}
 
     result = {
         "metric": "GQE prefill tokens/s + attn TFLOP/s (% MFMA peak), d=768 N=16 G=8 k=1",
@@ -169,34 +245,35 @@ def main():
         "config": {"workload": main_wl.name, "dim": 768, "num_query_experts": 16, "num_kv_heads": 8,
                    "top_k": 1, "head_dim": 48, "shared_head": True, "variant": "gqe", "batch": 8,
                    "seq": 2048, "causal": True, "matrix_core_stages": path},
-        "roofline": roofline,
-        "attn_tflops": alg["attention"]["flops"] / (stage_ms["attention"] * 1e-3) / 1e12,
-        "stages": stages,
+        "roofline": rl,
+        "attn_tflops": alg["attention"]["flops"] / (kernel_ms["attention"] * 1e-3) / 1e12,
+        "kernels": kernels,
+        "stage_ms": stage_ms,
     }
     result["attn_frac_peak"] = result["attn_tflops"] / PEAK_BF16
 
     if not args.only_main:
         # the all-active GQA baseline at the main setting
-        g_ms, g_stage, _ = run_workload(gqa_of(main_wl), args.steps, args.warmup)
+        g_ms, g_kern, _ = run_workload(gqa_of(main_wl), args.steps, args.warmup)
         result["main_gqa"] = dict(ms_per_step=g_ms, speedup_layer=g_ms / ms,
-                                  speedup_attention=g_stage["attention"] / stage_ms["attention"])
+                                  speedup_attention=g_kern["attention"] / kernel_ms["attention"])
     if not args.no_long and not args.only_main:
         long = {}
         for name, steps in (("long_s16384", max(5, args.steps // 3)), ("long_s32768", max(3, args.steps // 6))):
             wl = WORKLOADS[name]
             log(f"[bench] {name}")
-            l_ms, l_stage, _ = run_workload(wl, steps, 2)
+            l_ms, l_kern, _ = run_workload(wl, steps, 2)
             log(f"[bench] {name} gqa")
-            g_ms, g_stage, _ = run_workload(gqa_of(wl), steps, 2)
+            g_ms, g_kern, _ = run_workload(gqa_of(wl), steps, 2)
             a = algorithmic(wl)
             ga = algorithmic(gqa_of(wl))
-            at = a["attention"]["flops"] / (l_stage["attention"] * 1e-3) / 1e12
-            gat = ga["attention"]["flops"] / (g_stage["attention"] * 1e-3) / 1e12
-            long[name] = dict(tokens_s=wl.tokens / (l_ms / 1e3), ms=l_ms, stage_ms=l_stage,
+            at = a["attention"]["flops"] / (l_kern["attention"] * 1e-3) / 1e12
+            gat = ga["attention"]["flops"] / (g_kern["attention"] * 1e-3) / 1e12
+            long[name] = dict(tokens_s=wl.tokens / (l_ms / 1e3), ms=l_ms, kernel_ms=l_kern,
                               attn_tflops=at, attn_frac_peak=at / PEAK_BF16,
-                              gqa_ms=g_ms, gqa_stage_ms=g_stage, gqa_attn_tflops=gat,
+                              gqa_ms=g_ms, gqa_kernel_ms=g_kern, gqa_attn_tflops=gat,
                               speedup_layer=g_ms / l_ms,
-                              speedup_attention=g_stage["attention"] / l_stage["attention"])
+                              speedup_attention=g_kern["attention"] / l_kern["attention"])
             log(f"[bench] {name}: {l_ms:.3f} ms (GQA {g_ms:.3f} ms) attn {at:.0f} TFLOP/s")
         result["long_context"] = long
     if not args.no_cpu and not args.only_main:

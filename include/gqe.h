@@ -169,13 +169,22 @@ int gqe_aux_stats(gqe_handle_t* h, void* stream, int64_t* counts, double* mean_p
 int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t offs[8],
                          int64_t dims[4]);
 
-/* Stage timing for measurement.  While enabled, gqe_forward records HIP events on its stream
- * around each of its kernels (stage 0 router, 1 projections, 2 attention, 3 combine + output
- * projection).  gqe_profile_read waits for the recorded events, returns the summed milliseconds
- * per stage and the number of forwards they cover, and starts a new accumulation.
- * Not re-entrant; costs four event records per forward while enabled. */
+/* Kernel timing for measurement.  While enabled, gqe_forward records a HIP event on its stream
+ * right before and right after each kernel it launches; a kernel's duration is the time between
+ * the two.  Kernel slots, in launch order:
+ *   0 router (logits, softmax, top-k, weights, per-block statistics)   1 router statistics
+ *   2 projections (routed + shared Q, K, V)                              3 key norms (only when the
+ *   projections run on the scalar path and attention on matrix cores)   4 attention preparation
+ *   5 attention                                                          6 combine + output projection
+ * gqe_profile_read_kernels waits for the recorded events, returns the summed milliseconds per
+ * kernel slot (0 for slots not launched) and the number of forwards they cover, and starts a new
+ * accumulation.  gqe_profile_read does the same summed per stage (0 router = slots 0+1,
+ * 1 projections = 2+3, 2 attention = 4+5, 3 combine = 6).  Not re-entrant; errors as
+ * GQE_ERR_NULL_POINTER / GQE_ERR_HIP. */
+#define GQE_PROF_KERNELS 7
 int gqe_profile_enable(gqe_handle_t* h, int enable);
 int gqe_profile_read(gqe_handle_t* h, double stage_ms[4], int64_t* forwards);
+int gqe_profile_read_kernels(gqe_handle_t* h, double kernel_ms[GQE_PROF_KERNELS], int64_t* forwards);
 
 /* Destroys the handle (host memory only).  NULL is ignored. */
 void gqe_destroy(gqe_handle_t* h);

@@ -237,36 +237,34 @@ int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t 
     hipStream_t st = (hipStream_t)stream;
     char* ws = (char*)workspace;
     hipError_t e = hipSuccess;
-    hipEvent_t* ev = nullptr;
+    KernelMarks marks;
+    KernelMarks* km = nullptr;
     if (h->prof) {
-        if (h->prof_used + 5 > h->prof_ev.size()) {
-            for (int i = 0; i < 5 && e == hipSuccess; ++i) {
-                hipEvent_t x0;
-                e = hipEventCreate(&x0);
-                if (e == hipSuccess) h->prof_ev.push_back(x0);
-            }
-            if (e != hipSuccess) return fail(GQE_ERR_HIP, "event creation failed: %s", hipGetErrorString(e));
+        const size_t need = (h->prof_used + 1) * (2 * KT_COUNT);
+        while (h->prof_ev.size() < need && e == hipSuccess) {
+            hipEvent_t x0;
+            e = hipEventCreate(&x0);
+            if (e == hipSuccess) h->prof_ev.push_back(x0);
         }
-        ev = &h->prof_ev[h->prof_used];
-        h->prof_used += 5;
+        if (e != hipSuccess) return fail(GQE_ERR_HIP, "event creation failed: %s", hipGetErrorString(e));
+        if (h->prof_mask.size() < h->prof_used + 1) h->prof_mask.resize(h->prof_used + 1);
+        marks.ev = &h->prof_ev[h->prof_used * (2 * KT_COUNT)];
+        marks.mask = &h->prof_mask[h->prof_used];
+        *marks.mask = 0;
+        marks.st = st;
+        h->prof_used += 1;
+        km = &marks;
     }
-    auto mark = [&](int i) {
-        if (ev && e == hipSuccess) e = hipEventRecord(ev[i], st);
-    };
-    mark(0);
-    if (!D.dense) e = launch_router(D, P, x, h->packed, h->pl, ws, route_idx, route_w, st);
-    mark(1);
+    if (!D.dense) e = launch_router(D, P, x, h->packed, h->pl, ws, route_idx, route_w, st, km);
     if (e == hipSuccess)
-        e = h->mfma_proj ? launch_proj_mfma(D, P, x, h->packed, h->pl, ws, st)
-                         : launch_proj_simple(D, P, h->w, x, ws, st);
-    if (e == hipSuccess && !h->mfma_proj && h->mfma_attn) e = launch_kn_simple(D, P, ws, st);
-    mark(2);
-    if (e == hipSuccess) e = h->mfma_attn ? launch_attn_mfma(D, P, ws, st) : launch_attn_simple(D, P, ws, st);
-    mark(3);
+        e = h->mfma_proj ? launch_proj_mfma(D, P, x, h->packed, h->pl, ws, st, km)
+                         : launch_proj_simple(D, P, h->w, x, ws, st, km);
+    if (e == hipSuccess && !h->mfma_proj && h->mfma_attn) e = launch_kn_simple(D, P, ws, st, km);
+    if (e == hipSuccess) e = h->mfma_attn ? launch_attn_mfma(D, P, ws, st, km) : launch_attn_simple(D, P, ws, st, km);
     if (e == hipSuccess)
-        e = h->mfma_combine ? launch_combine_mfma(D, P, h->packed, h->pl, y, ws, st)
-                            : launch_combine_simple(D, P, h->w, y, ws, st);
-    mark(4);
+        e = h->mfma_combine ? launch_combine_mfma(D, P, h->packed, h->pl, y, ws, st, km)
+                            : launch_combine_simple(D, P, h->w, y, ws, st, km);
+    if (e == hipSuccess && km && marks.err != hipSuccess) e = marks.err;
     if (e != hipSuccess) return fail(GQE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     h->ran = true;
     h->last_ws = workspace;
@@ -315,23 +313,36 @@ int gqe_profile_enable(gqe_handle_t* h, int enable) {
     return ok();
 }
 
-int gqe_profile_read(gqe_handle_t* h, double stage_ms[4], int64_t* forwards) {
-    if (!h || !stage_ms) return fail(GQE_ERR_NULL_POINTER, "handle and stage_ms must be non-NULL");
-    for (int i = 0; i < 4; ++i) stage_ms[i] = 0.0;
-    const size_t n = h->prof_used / 5;
-    for (size_t f = 0; f < n; ++f) {
-        hipEvent_t* ev = &h->prof_ev[5 * f];
-        hipError_t e = hipEventSynchronize(ev[4]);
-        if (e != hipSuccess) return fail(GQE_ERR_HIP, "event wait failed: %s", hipGetErrorString(e));
-        for (int i = 0; i < 4; ++i) {
+int gqe_profile_read_kernels(gqe_handle_t* h, double kernel_ms[GQE_PROF_KERNELS], int64_t* forwards) {
+    if (!h || !kernel_ms) return fail(GQE_ERR_NULL_POINTER, "handle and kernel_ms must be non-NULL");
+    for (int i = 0; i < KT_COUNT; ++i) kernel_ms[i] = 0.0;
+    for (size_t f = 0; f < h->prof_used; ++f) {
+        hipEvent_t* ev = &h->prof_ev[f * (2 * KT_COUNT)];
+        const uint32_t mask = h->prof_mask[f];
+        for (int k = 0; k < KT_COUNT; ++k) {
+            if (!((mask >> k) & 1)) continue;
+            hipError_t e = hipEventSynchronize(ev[2 * k + 1]);
+            if (e != hipSuccess) return fail(GQE_ERR_HIP, "event wait failed: %s", hipGetErrorString(e));
             float ms = 0.f;
-            e = hipEventElapsedTime(&ms, ev[i], ev[i + 1]);
+            e = hipEventElapsedTime(&ms, ev[2 * k], ev[2 * k + 1]);
             if (e != hipSuccess) return fail(GQE_ERR_HIP, "event timing failed: %s", hipGetErrorString(e));
-            stage_ms[i] += ms;
+            kernel_ms[k] += ms;
         }
     }
-    if (forwards) *forwards = (int64_t)n;
+    if (forwards) *forwards = (int64_t)h->prof_used;
     h->prof_used = 0;
+    return ok();
+}
+
+int gqe_profile_read(gqe_handle_t* h, double stage_ms[4], int64_t* forwards) {
+    if (!h || !stage_ms) return fail(GQE_ERR_NULL_POINTER, "handle and stage_ms must be non-NULL");
+    double k[KT_COUNT];
+    const int rc = gqe_profile_read_kernels(h, k, forwards);
+    if (rc != GQE_OK) return rc;
+    stage_ms[0] = k[KT_ROUTER] + k[KT_ROUTER_STATS];
+    stage_ms[1] = k[KT_PROJ] + k[KT_KEYNORM];
+    stage_ms[2] = k[KT_ATTN_PREP] + k[KT_ATTN];
+    stage_ms[3] = k[KT_COMBINE];
     return ok();
 }
 

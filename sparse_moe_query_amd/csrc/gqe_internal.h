@@ -50,14 +50,35 @@ struct gqe_handle {
     bool ran;
     void* last_ws;
     WorkPlan last_plan;
-    // stage timing (gqe_profile_enable)
+    // kernel timing (gqe_profile_enable)
     bool prof = false;
-    std::vector<hipEvent_t> prof_ev;  // 5 events per recorded forward
-    size_t prof_used = 0;
+    std::vector<hipEvent_t> prof_ev;     // 2 * KT_COUNT events per recorded forward
+    std::vector<uint32_t> prof_mask;     // kernel slots recorded by each forward
+    size_t prof_used = 0;                // forwards recorded
+};
+
+// Kernel timing slots, in launch order (GQE_PROF_KERNELS in gqe.h).
+enum { KT_ROUTER = 0, KT_ROUTER_STATS, KT_PROJ, KT_KEYNORM, KT_ATTN_PREP, KT_ATTN, KT_COMBINE, KT_COUNT };
+
+// Records events on the stream right before and right after each kernel a launcher enqueues
+// (when timing is on).
+struct KernelMarks {
+    hipEvent_t* ev = nullptr;  // 2 * KT_COUNT events: [2 slot] before, [2 slot + 1] after
+    uint32_t* mask = nullptr;
+    hipStream_t st = nullptr;
+    hipError_t err = hipSuccess;
+    void begin(int slot) {
+        if (ev && err == hipSuccess) err = hipEventRecord(ev[2 * slot], st);
+    }
+    void mark(int slot) {
+        if (!ev || err != hipSuccess) return;
+        err = hipEventRecord(ev[2 * slot + 1], st);
+        if (err == hipSuccess) *mask |= 1u << slot;
+    }
 };
 
 WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S);
-hipError_t launch_kn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st);
+hipError_t launch_kn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km);
 bool router_uses_mfma(const GqeDims& D);
 PackedLayout make_packed_layout(const GqeDims& D, bool mfma);
 
@@ -66,17 +87,17 @@ hipError_t launch_pack(const GqeDims& D, const gqe_weights_t& w, const PackedLay
                        void* packed, bool mfma, hipStream_t st);
 hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, const void* packed,
                          const PackedLayout& pl, char* ws, int32_t* route_idx, float* route_w,
-                         hipStream_t st);
+                         hipStream_t st, KernelMarks* km);
 hipError_t launch_proj_simple(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w,
-                              const void* x, char* ws, hipStream_t st);
-hipError_t launch_attn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st);
+                              const void* x, char* ws, hipStream_t st, KernelMarks* km);
+hipError_t launch_attn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km);
 hipError_t launch_combine_simple(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w,
-                                 void* y, char* ws, hipStream_t st);
+                                 void* y, char* ws, hipStream_t st, KernelMarks* km);
 hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x,
                             const void* packed, const PackedLayout& pl, char* ws,
-                            hipStream_t st);
-hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st);
+                            hipStream_t st, KernelMarks* km);
+hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km);
 bool combine_mfma_supported(const GqeDims& D);
 int combine_stage_pitch(int dh);
 hipError_t launch_combine_mfma(const GqeDims& D, const WorkPlan& P, const void* packed,
-                               const PackedLayout& pl, void* y, char* ws, hipStream_t st);
+                               const PackedLayout& pl, void* y, char* ws, hipStream_t st, KernelMarks* km);

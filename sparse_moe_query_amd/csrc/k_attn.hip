@@ -413,7 +413,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st) {
+hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km) {
     AttnArgs a{};
     a.Q = (const bf16_t*)(ws + P.q);
     a.K = (const bf16_t*)(ws + P.kk);
@@ -452,6 +452,7 @@ hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipSt
         const int64_t BG = P.B * D.G;
         const int64_t work = BG * (P.S_pad / 64) + BG * D.dh * (P.S_pad - P.S);
         const unsigned pg = (unsigned)std::min<int64_t>(ceil_div(work, 256), 1024);
+        if (km) km->begin(KT_ATTN_PREP);
         attn_prep_kernel<<<pg, 256, 0, st>>>(a.kn, (float*)(ws + P.knt), (bf16_t*)(ws + P.vt), BG, P.S, P.S_pad,
                                              D.dh);
     }
@@ -459,11 +460,14 @@ hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipSt
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (km) km->mark(KT_ATTN_PREP);
+    if (km) km->begin(KT_ATTN);
     switch (D.dh) {
         case 32: attn_fwd_kernel<32><<<(unsigned)grid, 256, 0, st>>>(a); break;
         case 48: attn_fwd_kernel<48><<<(unsigned)grid, 256, 0, st>>>(a); break;
         case 64: attn_fwd_kernel<64><<<(unsigned)grid, 256, 0, st>>>(a); break;
         default: return hipErrorInvalidValue;
     }
+    if (km) km->mark(KT_ATTN);
     return hipGetLastError();
 }

@@ -313,7 +313,7 @@ bool combine_mfma_supported(const GqeDims& D) {
 }
 
 hipError_t launch_combine_mfma(const GqeDims& D, const WorkPlan& P, const void* packed,
-                               const PackedLayout& pl, void* y, char* ws, hipStream_t st) {
+                               const PackedLayout& pl, void* y, char* ws, hipStream_t st, KernelMarks* km) {
     CombArgs a{};
     a.O = (const bf16_t*)(ws + P.o);
     a.wo = (const bf16_t*)((const char*)packed + pl.wo);
@@ -345,10 +345,14 @@ hipError_t launch_combine_mfma(const GqeDims& D, const WorkPlan& P, const void* 
     // coefficients are needed by weighted_concat and by gqe with several choices per group
     const bool coef = !D.dense && (D.variant == GQE_VARIANT_WEIGHTED_CONCAT || (D.variant == GQE_VARIANT_GQE && D.k > 1));
     const unsigned grid = (unsigned)(ceil_div(P.T, kBM) * (a.d / kBN));
+    hipError_t e;
+    if (km) km->begin(KT_COMBINE);
     switch (D.dh) {
-        case 32: return launch_dh<32>(a, coef, grid, st);
-        case 48: return launch_dh<48>(a, coef, grid, st);
-        case 64: return launch_dh<64>(a, coef, grid, st);
+        case 32: e = launch_dh<32>(a, coef, grid, st); break;
+        case 48: e = launch_dh<48>(a, coef, grid, st); break;
+        case 64: e = launch_dh<64>(a, coef, grid, st); break;
         default: return hipErrorInvalidValue;
     }
+    if (km) km->mark(KT_COMBINE);
+    return e;
 }

@@ -254,7 +254,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
 }  // namespace
 
 hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x, const void* packed,
-                            const PackedLayout& pl, char* ws, hipStream_t st) {
+                            const PackedLayout& pl, char* ws, hipStream_t st, KernelMarks* km) {
     ProjArgs a{};
     a.x = (const bf16_t*)x;
     a.wproj = (const bf16_t*)((const char*)packed + pl.wproj);
@@ -279,11 +279,13 @@ hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x, 
     a.ntiles = (int)ceil_div(P.T, kBM);
     if (D.d % kKC != 0) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)((int64_t)a.ntiles * a.njobs);
+    if (km) km->begin(KT_PROJ);
     switch (D.dh) {
         case 32: proj_kernel<32><<<grid, 256, 0, st>>>(a); break;
         case 48: proj_kernel<48><<<grid, 256, 0, st>>>(a); break;
         case 64: proj_kernel<64><<<grid, 256, 0, st>>>(a); break;
         default: return hipErrorInvalidValue;
     }
+    if (km) km->mark(KT_PROJ);
     return hipGetLastError();
 }

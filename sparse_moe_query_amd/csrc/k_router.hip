@@ -272,7 +272,7 @@ bool router_uses_mfma(const GqeDims& D) { return D.d % 64 == 0 && D.N <= 16; }
 
 hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, const void* packed,
                          const PackedLayout& pl, char* ws, int32_t* route_idx, float* route_w,
-                         hipStream_t st) {
+                         hipStream_t st, KernelMarks* km) {
     const char* pk = (const char*)packed;
     RouterArgs a{};
     a.x = x;
@@ -294,6 +294,7 @@ hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, con
     a.part_psum = (double*)(ws + P.part_psum);
     const dim3 grid((unsigned)P.nblk_router);
     const bool bf = D.dtype == GQE_DTYPE_BF16;
+    if (km) km->begin(KT_ROUTER);
     if (router_uses_mfma(D)) {
         if (bf) router_mfma_kernel<bf16_t><<<grid, 512, 0, st>>>(a);
         else router_mfma_kernel<float><<<grid, 512, 0, st>>>(a);
@@ -303,7 +304,10 @@ hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, con
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (km) km->mark(KT_ROUTER);
+    if (km) km->begin(KT_ROUTER_STATS);
     stats_finalize_kernel<<<1, 256, 0, st>>>(a.part_cnt, a.part_psum, P.nblk_router, P.T, D.N, D.G, D.k,
                                              ws + P.stats);
+    if (km) km->mark(KT_ROUTER_STATS);
     return hipGetLastError();
 }

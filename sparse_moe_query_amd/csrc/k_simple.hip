@@ -186,23 +186,34 @@ hipError_t combine(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w, 
 }  // namespace
 
 hipError_t launch_proj_simple(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w, const void* x,
-                              char* ws, hipStream_t st) {
-    return D.dtype == GQE_DTYPE_BF16 ? proj<bf16_t>(D, P, w, x, ws, st) : proj<float>(D, P, w, x, ws, st);
+                              char* ws, hipStream_t st, KernelMarks* km) {
+    if (km) km->begin(KT_PROJ);
+    const hipError_t e = D.dtype == GQE_DTYPE_BF16 ? proj<bf16_t>(D, P, w, x, ws, st) : proj<float>(D, P, w, x, ws, st);
+    if (km) km->mark(KT_PROJ);
+    return e;
 }
-hipError_t launch_attn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st) {
-    return D.dtype == GQE_DTYPE_BF16 ? attn<bf16_t>(D, P, ws, st) : attn<float>(D, P, ws, st);
+hipError_t launch_attn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km) {
+    if (km) km->begin(KT_ATTN);
+    const hipError_t e = D.dtype == GQE_DTYPE_BF16 ? attn<bf16_t>(D, P, ws, st) : attn<float>(D, P, ws, st);
+    if (km) km->mark(KT_ATTN);
+    return e;
 }
-hipError_t launch_kn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st) {
+hipError_t launch_kn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km) {
     const Args a = make_args<bf16_t>(D, P);
+    if (km) km->begin(KT_KEYNORM);
     if (D.dtype == GQE_DTYPE_BF16)
         kn_simple_kernel<bf16_t><<<(unsigned)ceil_div(P.B * D.G * P.S, 256), 256, 0, st>>>(
             a, (const bf16_t*)(ws + P.kk), (float*)(ws + P.kn));
     else
         kn_simple_kernel<float><<<(unsigned)ceil_div(P.B * D.G * P.S, 256), 256, 0, st>>>(
             a, (const float*)(ws + P.kk), (float*)(ws + P.kn));
+    if (km) km->mark(KT_KEYNORM);
     return hipGetLastError();
 }
 hipError_t launch_combine_simple(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w, void* y,
-                                 char* ws, hipStream_t st) {
-    return D.dtype == GQE_DTYPE_BF16 ? combine<bf16_t>(D, P, w, y, ws, st) : combine<float>(D, P, w, y, ws, st);
+                                 char* ws, hipStream_t st, KernelMarks* km) {
+    if (km) km->begin(KT_COMBINE);
+    const hipError_t e = D.dtype == GQE_DTYPE_BF16 ? combine<bf16_t>(D, P, w, y, ws, st) : combine<float>(D, P, w, y, ws, st);
+    if (km) km->mark(KT_COMBINE);
+    return e;
 }

@@ -25,8 +25,10 @@ ERRORS = {0: "GQE_OK", -1: "GQE_ERR_INVALID_CONFIG", -2: "GQE_ERR_NULL_POINTER",
           -6: "GQE_ERR_SHAPE", -7: "GQE_ERR_HIP", -8: "GQE_ERR_STATE"}
 EXPORTS = ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights", "gqe_workspace_bytes",
            "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_profile_enable",
-           "gqe_profile_read", "gqe_destroy", "gqe_last_error")
+           "gqe_profile_read", "gqe_profile_read_kernels", "gqe_destroy", "gqe_last_error")
 STAGES = ("router", "projection", "attention", "combine")
+# kernel timing slots of gqe_profile_read_kernels, in launch order
+KERNELS = ("router", "router_stats", "projection", "key_norms", "attention_prep", "attention", "combine")
 
 
 class GqeError(RuntimeError):
@@ -68,13 +70,14 @@ def lib():
         L.gqe_workspace_layout.argtypes = [P, I64, I64, P, P]
         L.gqe_profile_enable.argtypes = [P, ctypes.c_int]
         L.gqe_profile_read.argtypes = [P, P, P]
+        L.gqe_profile_read_kernels.argtypes = [P, P, P]
         L.gqe_destroy.argtypes = [P]
         L.gqe_destroy.restype = None
         L.gqe_last_error.argtypes = []
         L.gqe_last_error.restype = ctypes.c_char_p
         for f in ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights",
                   "gqe_workspace_bytes", "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout",
-                  "gqe_profile_enable", "gqe_profile_read"):
+                  "gqe_profile_enable", "gqe_profile_read", "gqe_profile_read_kernels"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -158,6 +161,13 @@ def gqe_profile_read(h):
     n = ctypes.c_int64()
     _check(lib().gqe_profile_read(h, ms, ctypes.byref(n)))
     return dict(zip(STAGES, list(ms))), n.value
+
+
+def gqe_profile_read_kernels(h):
+    ms = (ctypes.c_double * len(KERNELS))()
+    n = ctypes.c_int64()
+    _check(lib().gqe_profile_read_kernels(h, ms, ctypes.byref(n)))
+    return dict(zip(KERNELS, list(ms))), n.value
 
 
 def gqe_destroy(h):
