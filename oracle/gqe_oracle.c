@@ -168,6 +168,39 @@ int gqe_oracle_aux(const oracle_cfg* c, int64_t T, const double* p, const int32_
 }
 
 /* ---------------------------------------------------------------------------------
+ * Token-to-expert bucketing: the global gather that lets each routed expert read a
+ * contiguous list of its tokens ([R] "Algorithm Overview": a router selects k experts
+ * per token in every group, and only those experts' query heads are computed).
+ * Definition: the T*G*k assignments (t, g, r) with expert e = idx[t][g][r], sorted
+ * stably by e (tokens ascending inside each expert):
+ *   offs[e]           = number of assignments to experts below e   (offs[N] = T*G*k)
+ *   perm[offs[e] + i] = token of the i-th assignment to expert e
+ *   inv[t][g][r]      = position of assignment (t, g, r) in perm
+ * Written as a counting sort: count per expert, exclusive prefix, then one pass over
+ * the assignments in (t, g, r) order.
+ * --------------------------------------------------------------------------------- */
+int gqe_oracle_bucket(const oracle_cfg* c, int64_t T, const int32_t* idx, int64_t* offs,
+                      int64_t* perm, int64_t* inv)
+{
+    const int N = c->num_query_experts, G = c->num_kv_heads, k = c->top_k;
+    const int64_t A = T * G * k;
+    int64_t* next = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+    if (!next) return -1;
+    for (int e = 0; e <= N; ++e) offs[e] = 0;
+    for (int64_t a = 0; a < A; ++a) offs[idx[a] + 1] += 1;
+    for (int e = 0; e < N; ++e) offs[e + 1] += offs[e];
+    for (int e = 0; e < N; ++e) next[e] = offs[e];
+    for (int64_t a = 0; a < A; ++a) {
+        const int e = idx[a];
+        const int64_t pos = next[e]++;
+        perm[pos] = a / ((int64_t)G * k);
+        inv[a] = pos;
+    }
+    free(next);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------
  * Dense KV path ([R] "Algorithm Overview": all KV heads remain dense and unchanged;
  * [T] "Dense KV Path").  For every token and every group g:
  *   K[t][g][:] = x[t] @ Wk[:, g dh:(g+1) dh],  V likewise.   Wk, Wv: [d, G dh]

@@ -87,10 +87,11 @@ def _load():
         lib.gqe_oracle_router.argtypes = [C, I64, P, P, P, P, P, P, P, P]
         lib.gqe_oracle_aux.argtypes = [C, I64, P, P, P, P, P, P]
         lib.gqe_oracle_kv.argtypes = [C, I64, P, P, P, P, P]
+        lib.gqe_oracle_bucket.argtypes = [C, I64, P, P, P, P]
         lib.gqe_oracle_rows.argtypes = [C, I64, I64, P, P, P, P, P, P, P, P, P, P, P, I64, P,
                                         P, P]
         for f in (lib.gqe_oracle_router, lib.gqe_oracle_aux, lib.gqe_oracle_kv,
-                  lib.gqe_oracle_rows):
+                  lib.gqe_oracle_rows, lib.gqe_oracle_bucket):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -122,6 +123,22 @@ def router(cfg: OracleConfig, x, w_router, b_router=None) -> dict:
     if rc != 0:
         raise ValueError("oracle router: invalid configuration")
     return out
+
+
+def bucket(cfg: OracleConfig, idx) -> dict:
+    """Stable bucketing of the (t, g, r) assignments by expert: offs [N+1], perm [T*G*k]
+    (token ids), inv [T, G, k] (position of each assignment in perm)."""
+    lib = _load()
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    N, G, k = cfg.num_query_experts, cfg.num_kv_heads, cfg.top_k
+    T = idx.size // (G * k)
+    offs = np.zeros(N + 1, np.int64)
+    perm = np.zeros(T * G * k, np.int64)
+    inv = np.zeros((T, G, k), np.int64)
+    cc = cfg.c()
+    if lib.gqe_oracle_bucket(ctypes.byref(cc), T, _ptr(idx), _ptr(offs), _ptr(perm), _ptr(inv)) != 0:
+        raise MemoryError("oracle bucket")
+    return dict(offs=offs, perm=perm, inv=inv)
 
 
 def aux(cfg: OracleConfig, p, idx) -> dict:

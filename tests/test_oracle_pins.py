@@ -7,6 +7,9 @@ fails at least one of them:
 * router   -- numpy matmul + scipy softmax (library routines), brute force over k-subsets,
               the all-equal-logits tie case, k=1 => w=1, sum w = 1;
 * aux      -- closed forms (k = n => 1, collapse => n, uniform p => 1), count totals;
+* bucketing-- numpy's stable argsort of the expert ids (brute force), bucket sizes = counts,
+              perm o inv = identity, tokens ascending in every bucket, k = n => every bucket is
+              0..T-1;
 * attention-- S=1 => o = v_0; W_k = 0 => causal running mean of V;
 * layer    -- k = N/G + hard concat + no shared head is textbook GQA: torch's
               scaled_dot_product_attention (float64); label permutations of experts and groups;
@@ -136,6 +139,47 @@ def test_router_k1_weight_is_one_and_k_eq_n_gap_inf():
     wl2 = wl.with_(top_k=2)
     r2 = go.router(_cfg(wl2), w["x"], w["w_router"], w["b_router"])
     assert np.all(np.isinf(r2["gap"]))
+
+
+# ----------------------------------------------------------------------------- bucketing
+@pytest.mark.parametrize("N,G,k,T,seed", [(4, 2, 1, 37, 0), (16, 8, 1, 200, 1), (16, 4, 2, 150, 2),
+                                          (8, 8, 1, 20, 3), (32, 8, 3, 64, 4)])
+def test_bucket_is_stable_sort_by_expert(N, G, k, T, seed):
+    """Bucketing = stable sort of the (t, g, r) assignments by expert id: compared with numpy's
+    stable argsort (brute force); sizes equal the per-expert counts; perm o inv = identity;
+    tokens strictly ascending inside every bucket."""
+    rng = np.random.default_rng(seed)
+    n = N // G
+    idx = np.zeros((T, G, k), np.int32)
+    for t in range(T):
+        for g in range(G):
+            idx[t, g] = g * n + rng.permutation(n)[:k]
+    cfg = go.OracleConfig(64, N, G, k, 16)
+    b = go.bucket(cfg, idx)
+    flat = idx.reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    assert np.array_equal(b["perm"], order // (G * k))
+    pos = np.empty_like(order)
+    pos[order] = np.arange(order.size)
+    assert np.array_equal(b["inv"].reshape(-1), pos)
+    counts = np.bincount(flat, minlength=N)
+    assert np.array_equal(np.diff(b["offs"]), counts) and b["offs"][0] == 0
+    assert np.array_equal(b["perm"][b["inv"].reshape(-1)], np.repeat(np.arange(T), G * k))
+    for e in range(N):
+        seg = b["perm"][b["offs"][e]:b["offs"][e + 1]]
+        assert np.all(np.diff(seg) > 0)
+
+
+def test_bucket_all_experts_chosen_is_identity_per_bucket():
+    """k = n: every expert receives every token, so each bucket is 0..T-1 in order."""
+    N, G, T = 8, 4, 33
+    n = N // G
+    idx = np.zeros((T, G, n), np.int32)
+    for g in range(G):
+        idx[:, g, :] = g * n + np.arange(n)[::-1]   # rank order does not matter to the buckets
+    b = go.bucket(go.OracleConfig(64, N, G, n, 16), idx)
+    assert np.array_equal(b["offs"], np.arange(N + 1) * T)
+    assert np.array_equal(b["perm"], np.tile(np.arange(T), N))
 
 
 # ----------------------------------------------------------------------------- aux
