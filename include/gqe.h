@@ -169,6 +169,22 @@ int gqe_aux_stats(gqe_handle_t* h, void* stream, int64_t* counts, double* mean_p
 int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t offs[8],
                          int64_t dims[4]);
 
+/* Token-to-expert bucketing of the last forward's routing: the global form of the gather the
+ * routed query projections do tile by tile (GQE README "Algorithm Overview": a router selects k
+ * query-head experts per token in every GQA group and only those heads are computed).  The
+ * T*G*k assignments (token t, group g, rank r) are sorted stably by global expert id, tokens
+ * ascending inside each expert:
+ *   offs [N + 1] int32: offs[e] = position of expert e's first assignment, offs[N] = T*G*k
+ *   perm [T*G*k] int32: token id at each position
+ *   inv  [T][G][k] int32: position of assignment (t, g, r) in perm
+ * Device pointers, caller-owned, 4-byte aligned.  Enqueued on `stream` (asynchronous); reads
+ * the routing and the per-block expert counts in the last forward's workspace, which must be
+ * unchanged, and writes a small scratch area inside it.
+ * Errors: GQE_ERR_NULL_POINTER, GQE_ERR_STATE (no forward yet, or the all-active GQA
+ * configuration, which has no routing), GQE_ERR_MISALIGNED, GQE_ERR_SHAPE (T*G*k >= 2^31),
+ * GQE_ERR_HIP. */
+int gqe_bucket(gqe_handle_t* h, void* stream, int32_t* offs, int32_t* perm, int32_t* inv);
+
 /* Kernel timing for measurement.  While enabled, gqe_forward records a HIP event on its stream
  * right before and right after each kernel it launches; a kernel's duration is the time between
  * the two.  Kernel slots, in launch order:

@@ -52,6 +52,7 @@ WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S) {
     P.psel = take(gk * 4);
     P.part_cnt = take((size_t)P.nblk_router * D.N * 4);
     P.part_psum = take((size_t)P.nblk_router * D.N * 8);
+    P.bucket_boff = take((size_t)P.nblk_router * D.N * 4);
     P.stats = take((size_t)D.N * 16 + 64);
     P.q = take((size_t)B * D.H * S * D.dh * es);
     P.kk = take((size_t)B * D.G * P.S_pad * D.dh * es);
@@ -303,6 +304,20 @@ int gqe_aux_stats(gqe_handle_t* h, void* stream, int64_t* counts, double* mean_p
         e = hipMemcpy(aux_loss, st + 16 * D.N, sizeof(double), hipMemcpyDeviceToHost);
         if (e != hipSuccess) return fail(GQE_ERR_HIP, "copy of aux_loss failed: %s", hipGetErrorString(e));
     }
+    return ok();
+}
+
+int gqe_bucket(gqe_handle_t* h, void* stream, int32_t* offs, int32_t* perm, int32_t* inv) {
+    if (!h || !offs || !perm || !inv) return fail(GQE_ERR_NULL_POINTER, "handle, offs, perm and inv must be non-NULL");
+    if (!h->ran) return fail(GQE_ERR_STATE, "no forward has run on this handle");
+    const GqeDims& D = h->D;
+    if (D.dense) return fail(GQE_ERR_STATE, "the all-active GQA configuration has no routing to bucket");
+    if (misaligned(offs, 4) || misaligned(perm, 4) || misaligned(inv, 4))
+        return fail(GQE_ERR_MISALIGNED, "offs, perm and inv must be 4-byte aligned");
+    const WorkPlan& P = h->last_plan;
+    if (P.T * D.G * D.k >= ((int64_t)1 << 31)) return fail(GQE_ERR_SHAPE, "T*G*k must be below 2^31");
+    const hipError_t e = launch_bucket(D, P, (char*)h->last_ws, offs, perm, inv, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GQE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

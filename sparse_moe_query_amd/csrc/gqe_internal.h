@@ -31,6 +31,7 @@ struct WorkPlan {
     int64_t nblk_router;
     size_t idx, wsel, psel;           // [T, G, k] int32 / f32 / f32
     size_t part_cnt, part_psum;       // [nblk_router, N] int32 / f64
+    size_t bucket_boff;               // [nblk_router, N] int32 (gqe_bucket)
     size_t stats;                     // counts [N] i64, mean [N] f64, aux f64
     size_t q, kk, vt, o;              // Q_act, K, V^T, O_act
     size_t kn;                        // per-key norms [B][G][S_pad] f32
@@ -97,6 +98,8 @@ hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x,
                             const void* packed, const PackedLayout& pl, char* ws,
                             hipStream_t st, KernelMarks* km);
 hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km);
+hipError_t launch_bucket(const GqeDims& D, const WorkPlan& P, char* ws, int32_t* offs, int32_t* perm, int32_t* inv,
+                         hipStream_t st);
 bool combine_mfma_supported(const GqeDims& D);
 int combine_stage_pitch(int dh);
 hipError_t launch_combine_mfma(const GqeDims& D, const WorkPlan& P, const void* packed,

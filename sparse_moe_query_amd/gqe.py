@@ -24,7 +24,7 @@ ERRORS = {0: "GQE_OK", -1: "GQE_ERR_INVALID_CONFIG", -2: "GQE_ERR_NULL_POINTER",
           -3: "GQE_ERR_MISALIGNED", -4: "GQE_ERR_UNSUPPORTED", -5: "GQE_ERR_WORKSPACE",
           -6: "GQE_ERR_SHAPE", -7: "GQE_ERR_HIP", -8: "GQE_ERR_STATE"}
 EXPORTS = ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights", "gqe_workspace_bytes",
-           "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_profile_enable",
+           "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_bucket", "gqe_profile_enable",
            "gqe_profile_read", "gqe_profile_read_kernels", "gqe_destroy", "gqe_last_error")
 STAGES = ("router", "projection", "attention", "combine")
 # kernel timing slots of gqe_profile_read_kernels, in launch order
@@ -68,6 +68,7 @@ def lib():
         L.gqe_forward.argtypes = [P, P, P, I64, I64, P, SZ, P, P, P]
         L.gqe_aux_stats.argtypes = [P, P, P, P, P, P]
         L.gqe_workspace_layout.argtypes = [P, I64, I64, P, P]
+        L.gqe_bucket.argtypes = [P, P, P, P, P]
         L.gqe_profile_enable.argtypes = [P, ctypes.c_int]
         L.gqe_profile_read.argtypes = [P, P, P]
         L.gqe_profile_read_kernels.argtypes = [P, P, P]
@@ -76,7 +77,7 @@ def lib():
         L.gqe_last_error.argtypes = []
         L.gqe_last_error.restype = ctypes.c_char_p
         for f in ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights",
-                  "gqe_workspace_bytes", "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout",
+                  "gqe_workspace_bytes", "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_bucket",
                   "gqe_profile_enable", "gqe_profile_read", "gqe_profile_read_kernels"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -131,6 +132,10 @@ def gqe_forward(h, x: torch.Tensor, y: torch.Tensor, batch: int, seq: int,
     _check(lib().gqe_forward(h, _ptr(x), _ptr(y), batch, seq, _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream),
                              _ptr(route_idx), _ptr(route_w)))
+
+
+def gqe_bucket(h, offs: torch.Tensor, perm: torch.Tensor, inv: torch.Tensor, stream=None):
+    _check(lib().gqe_bucket(h, _stream(stream), _ptr(offs), _ptr(perm), _ptr(inv)))
 
 
 def gqe_aux_stats(h, n_experts: int, stream=None) -> dict:
@@ -227,6 +232,15 @@ class GQEAttention:
 
     def aux_stats(self, stream=None) -> dict:
         return gqe_aux_stats(self.h, self.N, stream)
+
+    def bucket(self, batch: int, seq: int, stream=None) -> dict:
+        """Global token-to-expert bucketing of the last forward (device int32 tensors)."""
+        G, k = self.cfg.num_kv_heads, self.cfg.top_k
+        offs = torch.empty(self.N + 1, dtype=torch.int32, device=self.device)
+        perm = torch.empty(batch * seq * G * k, dtype=torch.int32, device=self.device)
+        inv = torch.empty((batch * seq, G, k), dtype=torch.int32, device=self.device)
+        gqe_bucket(self.h, offs, perm, inv, stream)
+        return dict(offs=offs, perm=perm, inv=inv)
 
     def intermediates(self, batch: int, seq: int) -> dict:
         """Views of Q_act, K, V^T, O_act and the routing buffers inside the workspace."""

@@ -118,6 +118,56 @@ def test_abi_errors_on_device():
     assert e.value.code == -6
 
 
+BUCKET = [_small("bucket_main_ragged", B=2, S=200), _small("bucket_k2", d=1024, k=2, dh=64, B=1, S=333,
+                                                              router_std=2.70 / 32.0, router_bias_first=2.0),
+          _small("bucket_n4_k2", N=16, G=4, k=2, dh=64, d=512, B=1, S=150, seed=4),
+          _small("bucket_n1", d=512, N=8, G=8, k=1, dh=64, B=1, S=70, variant="hard_concat", seed=7),
+          WORKLOADS["main_b8_s2048"], WORKLOADS["k2_skew_b4_s4096"]]
+
+
+@pytest.mark.parametrize("wl", BUCKET, ids=[w.name for w in BUCKET])
+def test_bucket_bit_exact(wl):
+    """Global bucketing of the forward's routing = the oracle's stable counting sort of the same
+    decisions (integer result: bit-exact), on small ragged and full-size workloads."""
+    from oracle import gqe_oracle as go
+    from sparse_moe_query_amd.runner import build_layer, run_layer
+    print(f"[gpu] bucket {wl.name} B={wl.batch} S={wl.seq} N={wl.num_query_experts} G={wl.num_kv_heads} "
+          f"k={wl.top_k}", flush=True)
+    layer, x, _ = build_layer(wl)
+    run_layer(layer, x)
+    b = layer.bucket(wl.batch, wl.seq)
+    torch.cuda.synchronize()
+    idx = layer.intermediates(wl.batch, wl.seq)["idx"].cpu().numpy()
+    ref = go.bucket(parity.oracle_cfg(wl), idx)
+    assert np.array_equal(b["offs"].cpu().numpy().astype(np.int64), ref["offs"])
+    assert np.array_equal(b["perm"].cpu().numpy().astype(np.int64), ref["perm"])
+    assert np.array_equal(b["inv"].cpu().numpy().astype(np.int64), ref["inv"])
+    layer.close()
+
+
+def test_bucket_errors():
+    from sparse_moe_query_amd import gqe
+    from sparse_moe_query_amd.runner import build_layer, run_layer
+    wl = _small("bucket_errors", B=1, S=64)
+    layer, x, _ = build_layer(wl)
+    with pytest.raises(gqe.GqeError) as e:
+        layer.bucket(1, 64)
+    assert e.value.code == -8  # no forward yet
+    run_layer(layer, x)
+    t = torch.empty(4, dtype=torch.int32, device=x.device)
+    with pytest.raises(gqe.GqeError) as e:
+        gqe.gqe_bucket(layer.h, t, torch.empty(0), t)
+    assert e.value.code == -2  # empty tensor -> NULL pointer
+    layer.close()
+    g = gqa_of(_small("bucket_gqa", B=1, S=64, k=2, variant="hard_concat", shared_head=False))
+    layer, x, _ = build_layer(g)
+    run_layer(layer, x)
+    with pytest.raises(gqe.GqeError) as e:
+        layer.bucket(1, 64)
+    assert e.value.code == -8  # dense GQA has no routing
+    layer.close()
+
+
 FULL = [WORKLOADS[k] for k in ("main_b8_s2048", "long_s16384", "long_s32768",
                                "k2_skew_b4_s4096", "ablation_gqe_b2_s8192",
                                "ablation_weighted_b2_s8192", "ablation_hard_b2_s8192")]
