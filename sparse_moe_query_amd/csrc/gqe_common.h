@@ -38,15 +38,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// Position, inside its 32-key block, at which key offset o (0..31) of V^T is stored.
-// Groups of four keys are interleaved so that one 16-byte LDS read hands every lane of the
-// P.V matrix-core step exactly the eight keys its probability registers hold (see k_attn).
+// Position, inside its 16-key chunk, at which key offset o (0..15) of V^T is stored: bits 2 and 3
+// of the offset swapped, i.e. keys 0-3, 8-11, 4-7, 12-15.  A 32x32 matrix-core score tile leaves
+// each lane with keys {0-3, 8-11} (lanes 0-31) or {4-7, 12-15} (lanes 32-63) of every 16-key chunk;
+// with this order one 16-byte read of V^T gives each lane exactly those eight keys, so the
+// probabilities feed the P.V product straight from the score registers (see k_attn).
 __host__ __device__ __forceinline__ int vt_slot(int o) {
-    const int c = o >> 2;
-    return ((((c & 1) << 2) | (c >> 1)) << 2) | (o & 3);
+    return (o & ~12) | ((o & 4) << 1) | ((o & 8) >> 1);
 }
 __host__ __device__ __forceinline__ int64_t vt_pos(int64_t s) {
-    return (s & ~(int64_t)31) | vt_slot((int)(s & 31));
+    return (s & ~(int64_t)15) | vt_slot((int)(s & 15));
 }
 
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

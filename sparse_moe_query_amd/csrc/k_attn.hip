@@ -15,13 +15,14 @@
 //                   Otherwise the standard online softmax runs (lane maximum combined with lane
 //                   l^32 by v_permlane32_swap; the offset is raised lazily, only when it grows by
 //                   more than 2^8, so O is rarely rescaled).
-//   P -> B operand  bf16-packed and re-laid by two v_permlane16_swap per register pair into the
-//                   16x16x32 B layout; V^T is stored with keys slotted (vt_pos) so that one 16-byte
-//                   LDS read gives each lane the eight keys its probabilities hold.
-//   O^T += V^T P^T  v_mfma_f32_16x16x32_bf16 over d_h in 16-row blocks plus one block whose first
-//                   row is all ones: the matrix core also forms the row sums, from the same
-//                   bf16 P that multiplies V.
+//   P -> A operand  bf16-packed straight from the score registers: each lane holds, per 16-key
+//                   chunk, the eight keys that V^T's slotting (vt_pos) puts in one 16-byte read.
+//   O += P [V|1|0]  v_mfma_f32_32x32x16_bf16 over 32-wide column blocks of V (d_h = 48: two blocks,
+//                   the second's spare columns carry a column of ones), so the matrix core also
+//                   forms the row sums, from the same bf16 P that multiplies V.
 // Work order: items by causal range, longest first (LPT over the concurrent work-group slots).
+#include <type_traits>
+
 #include "gqe_common.h"
 #include "gqe_internal.h"
 
@@ -146,11 +147,72 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// softmax of one query tile's S^T (32 keys x 32 columns per kst, lane = column) -> P packed to
+// bf16 as A operands of the 32x32x16 P.V product: pa[2 kst + u] holds, for the lane's column, the
+// eight keys of 16-key chunk u of subtile kst that the score layout left in this lane (register
+// order = the key order of V^T's slotting).  FAST: P = exp2(S) (the range test holds and the offset
+// is 0).  diag: keys past the lane's position are masked.  Rescales the tile's O accumulators when
+// the offset rises (alpha of each accumulator row fetched from the lane that owns that column).
+template <int NCB, bool FAST>
+__device__ __forceinline__ void softmax_tile(f32x16_t (&sacc)[2], float& mrun, f32x16_t (&oacc)[NCB],
+                                             bf16x8_t (&pa)[4], bool diag, int key0, int pos, int lane) {
+    if (diag) {
+        // key index of register j: key0 + 32 kst + 8 (j / 4) + 4 (lane / 32) + j % 4
+        const int lim = pos - key0 - 4 * (lane >> 5);
+#pragma unroll
+        for (int kst = 0; kst < 2; ++kst)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (32 * kst + 8 * (j >> 2) + (j & 3) > lim) sacc[kst][j] = -INFINITY;
+    }
+    float nm = 0.f;
+    if (!FAST) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kst = 0; kst < 2; ++kst)
+#pragma unroll
+            for (int j = 0; j < 16; j += 2) mx = fmax3(mx, sacc[kst][j], sacc[kst][j + 1]);
+        {
+            const uint32_t mb = __float_as_uint(mx);
+            auto sw = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
+            mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const bool need = mx > mrun + kLazy;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float mnew = need ? mx : mrun;
+            const float alpha = (need && mrun != -INFINITY) ? __builtin_amdgcn_exp2f(mrun - mnew) : (need ? 0.f : 1.f);
+            mrun = mnew;
+            // accumulator register j of this lane is query row 8 (j / 4) + 4 (lane / 32) + j % 4,
+            // whose alpha lives in the lane of that column
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float aj = __shfl(alpha, 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3));
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) oacc[cb][j] *= aj;
+            }
+        }
+        nm = mrun == -INFINITY ? 0.f : -mrun;
+    } else {
+        mrun = 0.f;  // from unset (nothing accumulated) or already 0
+    }
+#pragma unroll
+    for (int kst = 0; kst < 2; ++kst) {
+        float pv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) pv[j] = __builtin_amdgcn_exp2f(FAST ? sacc[kst][j] : sacc[kst][j] + nm);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const u32x4_t pk = {pack_bf16x2(pv[8 * u + 0], pv[8 * u + 1]), pack_bf16x2(pv[8 * u + 2], pv[8 * u + 3]),
+                                pack_bf16x2(pv[8 * u + 4], pv[8 * u + 5]), pack_bf16x2(pv[8 * u + 6], pv[8 * u + 7])};
+            pa[2 * kst + u] = __builtin_bit_cast(bf16x8_t, pk);
+        }
+    }
+}
+
 template <int DH>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
     constexpr int KS = DH / 16;        // k-steps of the 32x32x16 QK^T product
-    constexpr int DB = DH / 16;        // 16-row blocks of d_h in the PV product
-    constexpr int DBX = DB + 1;        // plus the row-sum block
+    constexpr int NCB = DH / 32 + 1;   // 32-wide column blocks of [V | 1 | 0] in the P.V product
     constexpr int KC8 = DH / 8;        // 16-byte chunks per key row
     constexpr int TILE_K = kBN * DH;   // elements of a K tile (unpadded, chunk-swizzled)
     constexpr int TILE_V = DH * kBN;   // elements of a V^T tile (unpadded, chunk-swizzled)
@@ -159,33 +221,33 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
     constexpr int LK = (SEGK + 3) / 4;       // direct loads per wave per tile (same for every wave)
     constexpr int LV = (SEGV + 3) / 4;
     constexpr int NSTAGE = 3;
+    constexpr int XR = NCB * 32 - DH;        // rows of the last block past d_h: row DH is ones
     __shared__ __align__(1024) uint16_t ks_lds[NSTAGE][TILE_K];
     __shared__ __align__(1024) uint16_t vs_lds[NSTAGE][TILE_V];
-    __shared__ __align__(1024) uint16_t sum_lds[16 * kBN];  // row-sum block: row 0 ones
+    __shared__ __align__(1024) uint16_t one_lds[XR * kBN];  // rows DH.. of [V | 1 | 0]^T
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const Item it = decode_item(a, (int)blockIdx.x);
     const int NH = it.nh;
-    const int64_t S = a.S;
-    const int64_t last_pos = min((int64_t)it.p0 + it.np, S) - 1;  // last query position of the item
-    const int kt_begin = 0;
-    const int kt_end = (int)(last_pos / kBN) + 1;
+    const int S = (int)a.S;  // the host limits a call to 2^28 tokens
+    const int last_pos = min(it.p0 + it.np, S) - 1;  // last query position of the item
+    const int kt_end = last_pos / kBN + 1;
 
     const bf16_t* Kg = a.K + ((int64_t)it.b * a.G + it.g) * a.S_pad * DH;
     const bf16_t* Vg = a.Vt + ((int64_t)it.b * a.G + it.g) * (int64_t)DH * a.S_pad;
-    const float* kng = a.kn + ((int64_t)it.b * a.G + it.g) * a.S_pad;
 
     // ---------------------------------------------------------------- query columns of the lane
-    int64_t posq[2];
     bf16x8_t qf[2][KS];
+    int posq[2];
+    float mrun[2] = {-INFINITY, -INFINITY};
     float qsq[2];  // sum of squares of the lane's half of the query column's dims
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
         const int c = w * kQW + qt * 32 + (lane & 31);
         const int p = c / NH, h = c % NH;
-        const int64_t pos = (int64_t)it.p0 + p;
+        const int pos = it.p0 + p;
         const bool valid = (p < it.np) && (pos < S);
         posq[qt] = valid ? pos : S - 1;
         const int vh = h < a.k ? it.g * a.k + h : a.G * a.k;
@@ -206,29 +268,27 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
     const float qmax_w = sqrtf(wave_max(__builtin_fmaxf(qsq[0], qsq[1]) * 2.0f));
     // key range of this wave
     const int cfirst = w * kQW, clast = w * kQW + kQW - 1;
-    const int64_t wfirst = min((int64_t)it.p0 + cfirst / NH, S - 1);
-    const int64_t wlast = min(min((int64_t)it.p0 + min(clast / NH, it.np - 1), S - 1), last_pos);
-    const int wtiles = (int)(wlast / kBN) + 1;
+    const int wfirst = min(it.p0 + cfirst / NH, S - 1);
+    const int wlast = min(min(it.p0 + min(clast / NH, it.np - 1), S - 1), last_pos);
+    const int wtiles = wlast / kBN + 1;
 
-    f32x4_t oacc[2][2][DBX];
+    // O accumulators: [qt][column block], 32 query rows x 32 columns of [V | 1 | 0] each
+    f32x16_t oacc[2][NCB];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int db = 0; db < DBX; ++db) oacc[qt][hf][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float mrun[2] = {-INFINITY, -INFINITY};
+        for (int cb = 0; cb < NCB; ++cb) oacc[qt][cb] = f32x16_t{};
     bool offset_zero = true;  // wave-uniform: every lane's offset is 0 or unset
 
-    // row-sum block (read like a V^T block): row 0 all ones, rows 1..15 zero
-    for (int i = tid; i < 16 * kBN; i += 256) sum_lds[i] = (i < kBN) ? (uint16_t)0x3f80 : (uint16_t)0;
+    // rows DH.. of the [V | 1 | 0]^T operand: row DH all ones, the rest zero
+    for (int i = tid; i < XR * kBN; i += 256) one_lds[i] = (i < kBN) ? (uint16_t)0x3f80 : (uint16_t)0;
 
     // Tiles go straight from global memory into LDS (global_load_lds_dwordx4: each wave-wide load
     // fills one contiguous 1 KB segment, lane i its 16 bytes at 16 i).  Every lane therefore loads
     // the global chunk that belongs at its LDS position; the chunk order inside a row is XOR
     // swizzled so that the fragment reads of eight consecutive rows hit distinct banks.
-    // Three stages: while tile kt computes, tile kt+1 has landed or is landing and tile kt+2 is
-    // in flight.  Every wave issues the same number of loads per tile (segments past the end are
+    // Three stages: while tile kt computes, tile kt+1 has landed or is landing and tile kt+2 is in
+    // flight.  Every wave issues the same number of loads per tile (segments past the end are
     // re-issued, same bytes), so the wait is a compile-time vmcnt.
     auto issue = [&](int kt, int stage) {
         const int64_t key0 = (int64_t)kt * kBN;
@@ -254,129 +314,76 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
     const_f32_ptr kntg = (const_f32_ptr)(a.knt + ((int64_t)it.b * a.G + it.g) * (a.S_pad / kBN));
     constexpr int NLOAD = LK + LV;  // vector-memory operations issued per tile per wave
 
-    issue(kt_begin, 0);
-    if (kt_begin + 1 < kt_end) {
-        issue(kt_begin + 1, 1);
+    // [V | 1 | 0]^T fragment rows of this lane: row n = 32 cb + (lane & 31)
+    const int hsel = lane >> 5;
+    auto body = [&](auto fast_t, bool diag, int kt) {
+        constexpr bool FAST = decltype(fast_t)::value;
+        const int stage = kt % NSTAGE;
+        const uint16_t* kb = ks_lds[stage];
+        const uint16_t* vb = vs_lds[stage];
+        // K fragments of both 32-key subtiles (shared by the two query tiles)
+        bf16x8_t kf[2][KS];
+#pragma unroll
+        for (int kst = 0; kst < 2; ++kst)
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const int r = 32 * kst + (lane & 31), c = 2 * kk + hsel;
+                kf[kst][kk] = *reinterpret_cast<const bf16x8_t*>(kb + (r * KC8 + (c ^ kswz<DH>(r))) * 8);
+            }
+        bf16x8_t pa[2][4];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+            f32x16_t sacc[2];
+#pragma unroll
+            for (int kst = 0; kst < 2; ++kst) {
+                f32x16_t acc = {};
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kst][kk], qf[qt][kk], acc, 0, 0, 0);
+                sacc[kst] = acc;
+            }
+            softmax_tile<NCB, FAST>(sacc, mrun[qt], oacc[qt], pa[qt], diag, kt * kBN, posq[qt], lane);
+        }
+        // O += P [V | 1 | 0]: per 16-key chunk, one fragment of each column block serves both
+        // query tiles
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+            const int c = 2 * ch + hsel;  // 16-byte chunk of the slotted key order
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const int n = 32 * cb + (lane & 31);
+                const uint16_t* src = n < DH ? vb + (n * 8 + (c ^ (n & 7))) * 8
+                                             : one_lds + ((n - DH) * 8 + (c ^ (n & 7))) * 8;
+                const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(src);
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt)
+                    oacc[qt][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[qt][ch], vf, oacc[qt][cb], 0, 0, 0);
+            }
+        }
+    };
+
+    issue(0, 0);
+    if (kt_end > 1) {
+        issue(1, 1);
         __builtin_amdgcn_s_waitcnt(vmcnt_wait(NLOAD));
     } else {
         __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
     }
     __syncthreads();
 
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-        const int stage = (kt - kt_begin) % NSTAGE;
+    for (int kt = 0; kt < kt_end; ++kt) {
         const bool ahead = kt + 2 < kt_end;
-        if (ahead) issue(kt + 2, (kt + 2 - kt_begin) % NSTAGE);
+        if (ahead) issue(kt + 2, (kt + 2) % NSTAGE);
         const float kmax_cur = kntg[kt];
         if (kt < wtiles) {
-            const uint16_t* kb = ks_lds[stage];
-            const uint16_t* vb = vs_lds[stage];
             const bool fast = offset_zero && (qmax_w * kmax_cur * 1.02f <= kFastBound);
-            // K fragments of both 32-key subtiles (shared by the two query tiles)
-            bf16x8_t kf[2][KS];
-#pragma unroll
-            for (int kst = 0; kst < 2; ++kst)
-#pragma unroll
-                for (int kk = 0; kk < KS; ++kk) {
-                    const int r = 32 * kst + (lane & 31), c = 2 * kk + (lane >> 5);
-                    kf[kst][kk] = *reinterpret_cast<const bf16x8_t*>(kb + (r * KC8 + (c ^ kswz<DH>(r))) * 8);
-                }
-            const bool diag = (int64_t)kt * kBN + kBN - 1 > wfirst;
-            uint32_t pb[2][2][8];  // packed bf16 probabilities [qt][kst][reg]
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                // S^T tiles of this query tile: [key subtile]
-                f32x16_t sacc[2];
-#pragma unroll
-                for (int kst = 0; kst < 2; ++kst) {
-                    f32x16_t acc = {};
-#pragma unroll
-                    for (int kk = 0; kk < KS; ++kk)
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kst][kk], qf[qt][kk], acc, 0, 0, 0);
-                    sacc[kst] = acc;
-                }
-                if (diag) {
-#pragma unroll
-                    for (int kst = 0; kst < 2; ++kst)
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) {
-                            const int64_t kidx = (int64_t)kt * kBN + 32 * kst + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-                            if (kidx > posq[qt]) sacc[kst][j] = -INFINITY;
-                        }
-                }
-                float nm = 0.f;
-                if (fast) {
-                    mrun[qt] = 0.f;  // from unset (nothing accumulated) or already 0
-                } else {
-                    float mx = -INFINITY;
-#pragma unroll
-                    for (int kst = 0; kst < 2; ++kst)
-#pragma unroll
-                        for (int j = 0; j < 16; j += 2) mx = fmax3(mx, sacc[kst][j], sacc[kst][j + 1]);
-                    {
-                        const uint32_t mb = __float_as_uint(mx);
-                        auto sw = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
-                        mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-                    }
-                    const bool need = mx > mrun[qt] + kLazy;
-                    if (__builtin_amdgcn_ballot_w64(need)) {
-                        const float mnew = need ? mx : mrun[qt];
-                        const float alpha = (need && mrun[qt] != -INFINITY) ? __builtin_amdgcn_exp2f(mrun[qt] - mnew)
-                                                                             : (need ? 0.f : 1.f);
-                        mrun[qt] = mnew;
-                        const float aa = __shfl(alpha, lane & 15);
-                        const float ab = __shfl(alpha, 16 + (lane & 15));
-#pragma unroll
-                        for (int db = 0; db < DBX; ++db) {
-                            oacc[qt][0][db] *= aa;
-                            oacc[qt][1][db] *= ab;
-                        }
-                    }
-                    nm = mrun[qt] == -INFINITY ? 0.f : -mrun[qt];
-                }
-#pragma unroll
-                for (int kst = 0; kst < 2; ++kst) {
-                    float pv[16];
-                    if (fast) {
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) pv[j] = __builtin_amdgcn_exp2f(sacc[kst][j]);
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) pv[j] = __builtin_amdgcn_exp2f(sacc[kst][j] + nm);
-                    }
-                    uint32_t X[4], Y[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        X[i] = pack_bf16x2(pv[2 * i], pv[2 * i + 1]);
-                        Y[i] = pack_bf16x2(pv[8 + 2 * i], pv[9 + 2 * i]);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        auto r = __builtin_amdgcn_permlane16_swap(X[i], Y[i], false, false);
-                        pb[qt][kst][i] = r[0];      // query block 32qt + 0..15
-                        pb[qt][kst][4 + i] = r[1];  // query block 32qt + 16..31
-                    }
-                }
-            }
-            if (!fast) offset_zero = !__builtin_amdgcn_ballot_w64(mrun[0] != 0.f && mrun[0] != -INFINITY) &&
-                                     !__builtin_amdgcn_ballot_w64(mrun[1] != 0.f && mrun[1] != -INFINITY);
-            // O^T += V^T P^T (last block: row sums)
-#pragma unroll
-            for (int kst = 0; kst < 2; ++kst) {
-#pragma unroll
-                for (int db = 0; db < DBX; ++db) {
-                    const int r = 16 * db + (lane & 15), c = 4 * kst + (lane >> 4);
-                    const uint16_t* src = db < DB ? vb + (r * 8 + (c ^ (r & 7))) * 8
-                                                  : sum_lds + ((r - DH) * 8 + (c ^ (r & 7))) * 8;
-                    const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(src);
-#pragma unroll
-                    for (int qt = 0; qt < 2; ++qt) {
-                        u32x4_t ba = {pb[qt][kst][0], pb[qt][kst][1], pb[qt][kst][2], pb[qt][kst][3]};
-                        u32x4_t bb = {pb[qt][kst][4], pb[qt][kst][5], pb[qt][kst][6], pb[qt][kst][7]};
-                        oacc[qt][0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(bf16x8_t, ba), oacc[qt][0][db], 0, 0, 0);
-                        oacc[qt][1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(bf16x8_t, bb), oacc[qt][1][db], 0, 0, 0);
-                    }
-                }
+            const bool diag = kt * kBN + kBN - 1 > wfirst;
+            if (fast) {
+                body(std::true_type{}, diag, kt);
+            } else {
+                body(std::false_type{}, diag, kt);
+                offset_zero = !__builtin_amdgcn_ballot_w64(mrun[0] != 0.f && mrun[0] != -INFINITY) &&
+                              !__builtin_amdgcn_ballot_w64(mrun[1] != 0.f && mrun[1] != -INFINITY);
             }
         }
         if (kt + 1 < kt_end) {
@@ -388,24 +395,26 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
     }
 
     // ---------------------------------------------------------------- normalise and store
+    // accumulator register j of this lane: query row 8 (j / 4) + 4 (lane / 32) + j % 4 of the
+    // tile, column 32 cb + (lane & 31); the row sum is column DH, held by lane DH % 32 (+32)
+    constexpr int CBS = DH / 32, CS = DH % 32;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            // row sum: row 0 of the last block, held by the lane of this column in lane group 0
-            const float lsum = __shfl(oacc[qt][hf][DB][0], lane & 15);
+        for (int j = 0; j < 16; ++j) {
+            const int row = 8 * (j >> 2) + 4 * hsel + (j & 3);
+            const float lsum = __shfl(oacc[qt][CBS][j], CS + 32 * hsel);
             const float sc = 1.0f / lsum;
-            const int c = w * kQW + qt * 32 + 16 * hf + (lane & 15);
+            const int c = w * kQW + qt * 32 + row;
             const int p = c / NH, h = c % NH;
-            const int64_t pos = (int64_t)it.p0 + p;
+            const int pos = it.p0 + p;
             if (p >= it.np || pos >= S) continue;
             const int v = h < a.k ? it.g * a.k + h : a.G * a.k;
-            bf16_t* orow = a.O + (((int64_t)it.b * S + pos) * a.H + v) * DH + 4 * (lane >> 4);
+            bf16_t* orow = a.O + (((int64_t)it.b * S + pos) * a.H + v) * DH;
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const f32x4_t o = oacc[qt][hf][db] * sc;
-                u32x2_t pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-                *reinterpret_cast<u32x2_t*>(orow + 16 * db) = pk;
+            for (int cb = 0; cb < NCB; ++cb) {
+                const int n = 32 * cb + (lane & 31);
+                if (n < DH) orow[n] = from_f32<bf16_t>(oacc[qt][cb][j] * sc);
             }
         }
     }

@@ -285,13 +285,13 @@ def collect_aux_loss(attn: GQEAttention, stream=None) -> float:
 
 
 def vt_unpermute(vt: torch.Tensor) -> torch.Tensor:
-    """Undo the key slotting of V^T (inner 32-key blocks) -> [..., d_h, S_pad] in key order."""
+    """Undo the key slotting of V^T (bits 2 and 3 of the key offset inside every 16-key chunk
+    are swapped) -> [..., d_h, S_pad] in key order."""
     S_pad = vt.shape[-1]
     pos = np.arange(S_pad)
-    o = pos & 31
-    c = o >> 2
-    slot = ((((c & 1) << 2) | (c >> 1)) << 2) | (o & 3)
-    src = (pos & ~31) | slot
+    o = pos & 15
+    slot = (o & ~12) | ((o & 4) << 1) | ((o & 8) >> 1)
+    src = (pos & ~15) | slot
     return vt[..., torch.as_tensor(src, device=vt.device)]
 
 
