@@ -11,7 +11,10 @@ Bars (from the measurement plan):
     output is the token's d-vector.  A single RMS over all tokens is not a usable scale here:
     with causal averaging |y_t| shrinks like 1/sqrt(t), so at S = 2048 the largest outputs are
     ~60x the global RMS and the bf16 rounding of y alone exceeds 2e-2 of it.  The global figure
-    is still reported (``y_err_global``).
+    is still reported (``y_err_global``).  The bound is on the computation: a bf16 output
+    element is in addition allowed its own storage rounding, 2^-8 |y_ref_tj| (the same rule as
+    for the stored intermediates), since a token's largest elements are ~4x its RMS and half an
+    ulp of those is already up to ~1.5e-2 of the RMS.
 """
 from __future__ import annotations
 
@@ -21,6 +24,7 @@ from oracle import gqe_oracle as go
 
 NEAR_TIE = 1e-6
 Y_TOL = {"f32": 1e-4, "bf16": 2e-2}
+Y_STORAGE_U = {"f32": 0.0, "bf16": 2.0 ** -8}   # storage rounding of one output element
 
 
 def oracle_cfg(wl) -> go.OracleConfig:
@@ -46,12 +50,14 @@ def rel_err(got, ref) -> float:
     return float(np.max(np.abs(got - ref))) / max(rms, 1e-300)
 
 
-def rel_err_rows(got, ref) -> float:
-    """max over vectors (last axis) of max |got - ref| / RMS(ref of that vector)."""
+def rel_err_rows(got, ref, storage_u: float = 0.0) -> float:
+    """max over vectors (last axis) of max |got - ref| / RMS(ref of that vector); with storage_u,
+    each element's error is first reduced by its storage rounding allowance storage_u |ref|."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     rms = np.sqrt(np.mean(np.square(ref), axis=-1))
-    err = np.max(np.abs(got - ref), axis=-1)
+    d = np.maximum(np.abs(got - ref) - storage_u * np.abs(ref), 0.0)
+    err = np.max(d, axis=-1)
     return float(np.max(err / np.maximum(rms, 1e-30)))
 
 
@@ -112,9 +118,9 @@ def compare(wl, gpu: dict, inputs: dict, rows=None, want_qo=False) -> dict:
     rows = np.arange(T) if rows is None else np.asarray(rows)
     res = go.rows(cfg, B, S, x64, p, idx_used, inputs, K, V, rows, want_qo=want_qo)
     y_ref = res[0] if want_qo else res
-    err = rel_err_rows(gpu["y"][rows], y_ref)
-    rep.update(y_err=err, y_err_global=rel_err(gpu["y"][rows], y_ref), rows=int(len(rows)),
-               K=K, V=V)
+    err = rel_err_rows(gpu["y"][rows], y_ref, Y_STORAGE_U[wl.dtype])
+    rep.update(y_err=err, y_err_raw=rel_err_rows(gpu["y"][rows], y_ref),
+               y_err_global=rel_err(gpu["y"][rows], y_ref), rows=int(len(rows)), K=K, V=V)
     if want_qo:
         rep["q_ref"], rep["o_ref"] = res[1], res[2]
     assert np.all(np.isfinite(gpu["y"][rows])), "non-finite GPU output"

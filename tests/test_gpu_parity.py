@@ -51,6 +51,11 @@ SMALL = [
     _small("dh32_weighted", d=384, N=8, G=4, k=1, dh=32, B=2, S=77, variant="weighted_concat", seed=6),
     _small("n1_groups_hard", d=512, N=8, G=8, k=1, dh=64, B=1, S=140, variant="hard_concat", seed=7),
     _small("weighted_k2", d=512, N=16, G=4, k=2, dh=48, B=1, S=129, variant="weighted_concat", seed=8),
+    # several hundred positions: many key tiles per attention item, every token checked
+    _small("long_s1000", B=1, S=1000, seed=9),
+    _small("long_k2_dh64", d=1024, k=2, dh=64, B=1, S=700, seed=10),
+    _small("long_dh32_k2", d=256, N=8, G=4, k=2, dh=32, B=2, S=900, seed=11),
+    _small("long_gqa", B=1, S=800, k=2, variant="hard_concat", shared_head=False, dense_gqa=True, seed=12),
 ]
 
 
@@ -71,7 +76,7 @@ def test_small_every_token_and_stage(wl):
     qg = inter["q"].float().cpu().numpy().transpose(0, 2, 1, 3).reshape(B * S, H, dh) / qscale
     og = inter["o"].float().cpu().numpy().reshape(B * S, H, dh)
     assert parity.within_rounding(qg, rep["q_ref"], wl.dtype), parity.rel_err_rows(qg, rep["q_ref"])
-    assert parity.rel_err_rows(og, rep["o_ref"]) <= (1e-4 if wl.dtype == "f32" else 2e-2)
+    assert parity.rel_err_rows(og, rep["o_ref"], parity.Y_STORAGE_U[wl.dtype]) <= (1e-4 if wl.dtype == "f32" else 2e-2)
     print(f"[gpu] {wl.name}: y_err={rep['y_err']:.2e} (global {rep['y_err_global']:.2e}) "
           f"near_ties={rep['near_ties']}", flush=True)
 
