@@ -132,14 +132,20 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(const float* __restrict_
     }
 }
 
-// XOR swizzle of the 16-byte chunks of a key row in LDS, chosen per head dim so that the
-// fragment reads of eight consecutive rows (same logical chunk) fall into distinct bank groups.
+// LDS layout of a key row: pitch in 16-byte chunks and XOR swizzle of the chunk order, chosen per
+// head dim so that a fragment read (sixteen lanes per LDS cycle, sixteen consecutive rows, same
+// logical chunk) touches sixteen distinct 16-byte bank groups of the 256-byte bank row.
+template <int DH>
+__host__ __device__ constexpr int kpitch() { return DH == 48 ? 7 : DH / 8; }  // 48: odd pitch
 template <int DH>
 __device__ __forceinline__ int kswz(int r) {
-    if constexpr (DH == 64) return r & 7;
+    if constexpr (DH == 64) return (r >> 1) & 7;
     else if constexpr (DH == 32) return (r >> 2) & 3;
-    else return 0;  // d_h = 48: a 96-byte pitch already spreads eight rows over distinct groups
+    else return 0;
 }
+// V^T rows (128 bytes): rows 2m and 2m+1 sit in different halves of the bank row, the XOR spreads
+// eight such pairs
+__device__ __forceinline__ int vswz(int n) { return (n >> 1) & 7; }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -214,7 +220,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
     constexpr int KS = DH / 16;        // k-steps of the 32x32x16 QK^T product
     constexpr int NCB = DH / 32 + 1;   // 32-wide column blocks of [V | 1 | 0] in the P.V product
     constexpr int KC8 = DH / 8;        // 16-byte chunks per key row
-    constexpr int TILE_K = kBN * DH;   // elements of a K tile (unpadded, chunk-swizzled)
+    constexpr int KP = kpitch<DH>();   // LDS pitch of a key row in chunks (>= KC8)
+    constexpr int TILE_K = kBN * KP * 8;  // elements of a K tile in LDS (chunk-swizzled)
     constexpr int TILE_V = DH * kBN;   // elements of a V^T tile (unpadded, chunk-swizzled)
     constexpr int SEGK = TILE_K * 2 / 1024;  // 1 KB segments per tile (one wave-wide load each)
     constexpr int SEGV = TILE_V * 2 / 1024;
@@ -286,7 +293,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
     // Tiles go straight from global memory into LDS (global_load_lds_dwordx4: each wave-wide load
     // fills one contiguous 1 KB segment, lane i its 16 bytes at 16 i).  Every lane therefore loads
     // the global chunk that belongs at its LDS position; the chunk order inside a row is XOR
-    // swizzled so that the fragment reads of eight consecutive rows hit distinct banks.
+    // swizzled (and d_h = 48 key rows are padded to an odd pitch) so that fragment reads of
+    // sixteen consecutive rows hit distinct banks.
     // Three stages: while tile kt computes, tile kt+1 has landed or is landing and tile kt+2 is in
     // flight.  Every wave issues the same number of loads per tile (segments past the end are
     // re-issued, same bytes), so the wait is a compile-time vmcnt.
@@ -296,8 +304,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
         for (int i = 0; i < LK; ++i) {
             const int seg = min(w + 4 * i, SEGK - 1);
             const int q = seg * 64 + lane;          // chunk position in the tile
-            const int r = q / KC8, cpos = q % KC8;  // key row, swizzled chunk slot
-            const int c = cpos ^ kswz<DH>(r);
+            const int r = q / KP, cpos = q % KP;    // key row, swizzled chunk slot
+            const int c = cpos < KC8 ? cpos ^ kswz<DH>(r) : 0;  // pad slot: any chunk of the row
             dma16(Kg + (key0 + r) * DH + 8 * c, &ks_lds[stage][seg * 512]);
         }
 #pragma unroll
@@ -305,7 +313,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
             const int seg = min(w + 4 * i, SEGV - 1);
             const int q = seg * 64 + lane;
             const int r = q / 8, cpos = q % 8;      // V^T row (head dim), swizzled chunk slot
-            const int c = cpos ^ (r & 7);
+            const int c = cpos ^ vswz(r);
             dma16(Vg + (int64_t)r * a.S_pad + key0 + 8 * c, &vs_lds[stage][seg * 512]);
         }
     };
@@ -328,7 +336,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
                 const int r = 32 * kst + (lane & 31), c = 2 * kk + hsel;
-                kf[kst][kk] = *reinterpret_cast<const bf16x8_t*>(kb + (r * KC8 + (c ^ kswz<DH>(r))) * 8);
+                kf[kst][kk] = *reinterpret_cast<const bf16x8_t*>(kb + (r * KP + (c ^ kswz<DH>(r))) * 8);
             }
         bf16x8_t pa[2][4];
 #pragma unroll
@@ -352,8 +360,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 const int n = 32 * cb + (lane & 31);
-                const uint16_t* src = n < DH ? vb + (n * 8 + (c ^ (n & 7))) * 8
-                                             : one_lds + ((n - DH) * 8 + (c ^ (n & 7))) * 8;
+                const uint16_t* src = n < DH ? vb + (n * 8 + (c ^ vswz(n))) * 8
+                                             : one_lds + ((n - DH) * 8 + (c ^ vswz(n))) * 8;
                 const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(src);
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt)

@@ -43,8 +43,10 @@ struct ProjArgs {
 };
 
 // Element offset of (row, 16-byte chunk c) in an LDS stage of [rows][64] bf16 whose chunks are
-// XOR-swizzled by the row: the 16 rows one fragment read touches hit distinct bank groups.
-__device__ __forceinline__ int swz64(int row, int c) { return (row * 8 + (c ^ (row & 7))) * 8; }
+// XOR-swizzled by the row: rows 2m and 2m+1 fall in different halves of the 256-byte bank row and
+// the XOR spreads eight such pairs, so the 16 rows one fragment read serves per LDS cycle hit
+// distinct bank groups.
+__device__ __forceinline__ int swz64(int row, int c) { return (row * 8 + (c ^ ((row >> 1) & 7))) * 8; }
 
 // One 64-wide slice of the hidden dimension for one wave: C^T += W^T x^T over the eight row
 // blocks myrow[] of the x stage and the wave's d_h weight rows.  Every wave runs this same
@@ -116,14 +118,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
 #pragma unroll
     for (int i = 0; i < LX; ++i) {
         const int q = (w + 4 * i) * 64 + lane;
-        const int r = q >> 3, c = (q & 7) ^ (r & 7);
+        const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
         const int64_t rem = a.T - 1 - t0;
         xoff[i] = (uint32_t)(((r < rem ? r : rem) * a.d + 8 * c) * 2);
     }
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
         const int q = (w + 4 * i) * 64 + lane;
-        const int r = q >> 3, c = (q & 7) ^ (r & 7);
+        const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
         int h = hb0 + r / DH;
         if (h >= a.HB) h = 0;
         woff[i] = (uint32_t)(((h * DH + r % DH) * a.d + 8 * c) * 2);
