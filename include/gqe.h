@@ -163,10 +163,14 @@ int gqe_aux_stats(gqe_handle_t* h, void* stream, int64_t* counts, double* mean_p
 /* Byte offsets of the intermediates inside the workspace of a [batch, seq] forward, for
  * stage-by-stage checks:  offs[0] Q_act [B, H_act, S, d_h] (stored multiplied by
  * log2(e)/sqrt(d_h), the attention scale in log2 units), offs[1] K [B, G, S_pad, d_h],
- * offs[2] V^T [B, G, d_h, S_pad] (keys permuted inside every 32-key block, see DESIGN),
- * offs[3] O_act [B, S, H_act, d_h], offs[4] route_idx [T, G, k] int32, offs[5] route_w
- * [T, G, k] f32, offs[6] p_sel [T, G, k] f32; dims[0] = H_act, dims[1] = S_pad. */
-int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t offs[8],
+ * offs[2] V^T [B, G, d_h, S_pad] (inside every 16-key chunk, bits 2 and 3 of the key offset are
+ * swapped), offs[3] O_act [B, S, H_act, d_h], offs[4] route_idx [T, G, k] int32, offs[5]
+ * route_w [T, G, k] f32, offs[6] p_sel [T, G, k] f32, offs[7] statistics (counts [N] int64,
+ * mean probability [N] f64, aux f64), offs[8] key norms [B, G, S_pad] f32, offs[9] largest key
+ * norm of every 64-key tile [B, G, S_pad / 64] f32; dims[0] = H_act, dims[1] = S_pad,
+ * dims[2] = matrix-core stages (1 projection, 2 attention, 4 combine).  Errors:
+ * GQE_ERR_NULL_POINTER, GQE_ERR_SHAPE. */
+int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t offs[10],
                          int64_t dims[4]);
 
 /* Token-to-expert bucketing of the last forward's routing: the global form of the gather the

@@ -197,7 +197,7 @@ int gqe_workspace_bytes(const gqe_handle_t* h, int64_t batch, int64_t seq, size_
     return ok();
 }
 
-int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t offs[8], int64_t dims[4]) {
+int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t offs[10], int64_t dims[4]) {
     if (!h || !offs || !dims) return fail(GQE_ERR_NULL_POINTER, "handle, offs and dims must be non-NULL");
     if (batch < 1 || seq < 1 || batch * seq > ((int64_t)1 << 28)) return fail(GQE_ERR_SHAPE, "bad batch/seq");
     WorkPlan P = make_plan(h->D, batch, seq);
@@ -209,6 +209,8 @@ int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size
     offs[5] = P.wsel;
     offs[6] = P.psel;
     offs[7] = P.stats;
+    offs[8] = P.kn;
+    offs[9] = P.knt;
     dims[0] = h->D.H;
     dims[1] = P.S_pad;
     dims[2] = (h->mfma_proj ? 1 : 0) | (h->mfma_attn ? 2 : 0) | (h->mfma_combine ? 4 : 0);
@@ -256,12 +258,16 @@ int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t 
         h->prof_used += 1;
         km = &marks;
     }
-    if (!D.dense) e = launch_router(D, P, x, h->packed, h->pl, ws, route_idx, route_w, st, km);
+    // with the matrix-core projection, its last work group finalizes the router statistics and
+    // (S % 64 == 0) its key blocks write the per-tile key-norm maxima the attention reads
+    if (!D.dense) e = launch_router(D, P, x, h->packed, h->pl, ws, route_idx, route_w, st, km, !h->mfma_proj);
     if (e == hipSuccess)
         e = h->mfma_proj ? launch_proj_mfma(D, P, x, h->packed, h->pl, ws, st, km)
                          : launch_proj_simple(D, P, h->w, x, ws, st, km);
     if (e == hipSuccess && !h->mfma_proj && h->mfma_attn) e = launch_kn_simple(D, P, ws, st, km);
-    if (e == hipSuccess) e = h->mfma_attn ? launch_attn_mfma(D, P, ws, st, km) : launch_attn_simple(D, P, ws, st, km);
+    if (e == hipSuccess)
+        e = h->mfma_attn ? launch_attn_mfma(D, P, ws, st, km, !(h->mfma_proj && P.S % 64 == 0))
+                         : launch_attn_simple(D, P, ws, st, km);
     if (e == hipSuccess)
         e = h->mfma_combine ? launch_combine_mfma(D, P, h->packed, h->pl, y, ws, st, km)
                             : launch_combine_simple(D, P, h->w, y, ws, st, km);

@@ -88,7 +88,7 @@ hipError_t launch_pack(const GqeDims& D, const gqe_weights_t& w, const PackedLay
                        void* packed, bool mfma, hipStream_t st);
 hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, const void* packed,
                          const PackedLayout& pl, char* ws, int32_t* route_idx, float* route_w,
-                         hipStream_t st, KernelMarks* km);
+                         hipStream_t st, KernelMarks* km, bool finalize);
 hipError_t launch_proj_simple(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w,
                               const void* x, char* ws, hipStream_t st, KernelMarks* km);
 hipError_t launch_attn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km);
@@ -97,7 +97,8 @@ hipError_t launch_combine_simple(const GqeDims& D, const WorkPlan& P, const gqe_
 hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x,
                             const void* packed, const PackedLayout& pl, char* ws,
                             hipStream_t st, KernelMarks* km);
-hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km);
+hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km,
+                            bool prep);
 hipError_t launch_bucket(const GqeDims& D, const WorkPlan& P, char* ws, int32_t* offs, int32_t* perm, int32_t* inv,
                          hipStream_t st);
 bool combine_mfma_supported(const GqeDims& D);

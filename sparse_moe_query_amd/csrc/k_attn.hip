@@ -430,7 +430,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km) {
+hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km, bool prep) {
     AttnArgs a{};
     a.Q = (const bf16_t*)(ws + P.q);
     a.K = (const bf16_t*)(ws + P.kk);
@@ -465,19 +465,19 @@ hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipSt
     const int64_t grid = total;
     if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
     a.knt = (const float*)(ws + P.knt);
-    {
+    if (prep) {
         const int64_t BG = P.B * D.G;
         const int64_t work = BG * (P.S_pad / 64) + BG * D.dh * (P.S_pad - P.S);
         const unsigned pg = (unsigned)std::min<int64_t>(ceil_div(work, 256), 1024);
         if (km) km->begin(KT_ATTN_PREP);
         attn_prep_kernel<<<pg, 256, 0, st>>>(a.kn, (float*)(ws + P.knt), (bf16_t*)(ws + P.vt), BG, P.S, P.S_pad,
                                              D.dh);
+        if (km) km->mark(KT_ATTN_PREP);
     }
     {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (km) km->mark(KT_ATTN_PREP);
     if (km) km->begin(KT_ATTN);
     switch (D.dh) {
         case 32: attn_fwd_kernel<32><<<(unsigned)grid, 256, 0, st>>>(a); break;

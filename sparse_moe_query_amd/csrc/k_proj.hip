@@ -23,6 +23,7 @@
 //              kernel's range test
 #include "gqe_common.h"
 #include "gqe_internal.h"
+#include "gqe_stats.h"
 
 namespace {
 
@@ -37,9 +38,17 @@ struct ProjArgs {
     bf16_t* K;             // [B][G][S_pad][DH]
     bf16_t* Vt;            // [B][G][DH][S_pad]
     float* kn;             // [B][G][S_pad] key norms
+    float* knt;            // [B][G][S_pad / 64] largest key norm per 64-key tile (when knt_here)
     float qscale;          // log2(e) / sqrt(d_h): queries are stored pre-scaled
     int64_t T, S, S_pad;
     int d, G, k, n, H, s, dense, HB, njobs, ntiles;
+    int knt_here;          // S % 64 == 0: every 64-key tile is one half of a 128-token tile
+    // router statistics finalize, run by the last work group after its own tile (when stats_here)
+    int stats_here, N;
+    const int32_t* part_cnt;
+    const double* part_psum;
+    char* stats;
+    int64_t nblk_router;
 };
 
 // Element offset of (row, 16-byte chunk c) in an LDS stage of [rows][64] bf16 whose chunks are
@@ -188,6 +197,82 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
     __syncthreads();  // stage 0 visible, stage 1 free
 
+    // ---- epilogue: acc[rb][cb] lane holds row 16 rb + (lane & 15) of the slice, head dims
+    // 16 cb + 4 (lane >> 4) + 0..3
+    auto epilogue = [&](f32x4_t (&acc)[8][DH / 16], const int (&myrow)[8], int nrows, int nrb) {
+        const uint32_t S = (uint32_t)a.S;  // the host limits a call to 2^28 tokens
+        float kmx[2] = {0.f, 0.f};  // K blocks: largest squared norm of each 64-token half
+    #pragma unroll
+        for (int rb = 0; rb < 8; ++rb) {
+            if (rb >= nrb) continue;
+            const int li = 16 * rb + (lane & 15);
+            const bool ok = li < nrows;
+            const int row = myrow[rb] & 0xff, rank = myrow[rb] >> 8;
+            const uint32_t t = (uint32_t)(t0 + row);
+            const uint32_t b = t / S, sp = t - b * S;
+            if (hb < GD) {
+                // key: also its norm (the four lane groups hold complementary dims)
+                float ss = 0.f;
+    #pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) ss += acc[rb][cb][i] * acc[rb][cb][i];
+                ss += __shfl_xor(ss, 16);
+                ss += __shfl_xor(ss, 32);
+                if (!ok) continue;
+                kmx[rb >> 2] = __builtin_fmaxf(kmx[rb >> 2], ss);
+                if ((lane >> 4) == 0) a.kn[((int64_t)b * a.G + hb) * a.S_pad + sp] = sqrtf(ss);
+                bf16_t* dst = a.K + (((int64_t)b * a.G + hb) * a.S_pad + sp) * DH;
+    #pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const f32x4_t v = acc[rb][cb];
+                    u32x2_t pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                    *reinterpret_cast<u32x2_t*>(dst + 16 * cb + 4 * (lane >> 4)) = pk;
+                }
+                continue;
+            }
+            if (!ok) continue;
+            if (is_v) {
+                // V^T [dim][key]: this lane's token is one key of four consecutive dim rows
+                const int g = hb - GD;
+                uint16_t* dst = reinterpret_cast<uint16_t*>(a.Vt) + ((int64_t)b * a.G + g) * DH * a.S_pad + vt_pos(sp);
+    #pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+    #pragma unroll
+                    for (int i = 0; i < 4; i += 2) {
+                        const uint32_t pk = pack_bf16x2(acc[rb][cb][i], acc[rb][cb][i + 1]);
+                        dst[(int64_t)(16 * cb + 4 * (lane >> 4) + i) * a.S_pad] = (uint16_t)(pk & 0xffffu);
+                        dst[(int64_t)(16 * cb + 4 * (lane >> 4) + i + 1) * a.S_pad] = (uint16_t)(pk >> 16);
+                    }
+                continue;
+            }
+            bf16_t* dst;
+            if (!is_expert) dst = a.Q + (((int64_t)b * a.H + a.G * a.k) * S + sp) * DH;  // shared head
+            else dst = a.Q + (((int64_t)b * a.H + g_of * a.k + rank) * S + sp) * DH;
+            const float qs = a.qscale;
+    #pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const f32x4_t v = acc[rb][cb] * qs;
+                u32x2_t pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                *reinterpret_cast<u32x2_t*>(dst + 16 * cb + 4 * (lane >> 4)) = pk;
+            }
+        }
+        if (hb < GD && a.knt_here) {
+            // S % 64 == 0: the two 64-token halves of the tile are whole 64-key tiles
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float m = kmx[h];
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
+                const int64_t t = t0 + 64 * h;
+                if (lane == 0 && t < a.T) {
+                    const uint32_t b = (uint32_t)t / S, sp = (uint32_t)t - b * S;
+                    a.knt[((int64_t)b * a.G + hb) * (a.S_pad / 64) + sp / 64] = sqrtf(m);
+                }
+            }
+        }
+    };
+
     for (int kc = 0; kc < nk; ++kc) {
         const int stage = kc & 1;
         if (kc + 1 < nk) issue(kc + 1, stage ^ 1);
@@ -195,61 +280,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
         __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
         __syncthreads();
     }
-    if (!active) return;
-
-    // ---- epilogue: acc[rb][cb] lane holds row 16 rb + (lane & 15) of the slice, head dims
-    // 16 cb + 4 (lane >> 4) + 0..3
-    const uint32_t S = (uint32_t)a.S;  // the host limits a call to 2^28 tokens
-#pragma unroll
-    for (int rb = 0; rb < 8; ++rb) {
-        if (rb >= nrb) continue;
-        const int li = 16 * rb + (lane & 15);
-        const bool ok = li < nrows;
-        const int row = myrow[rb] & 0xff, rank = myrow[rb] >> 8;
-        const uint32_t t = (uint32_t)(t0 + row);
-        const uint32_t b = t / S, sp = t - b * S;
-        if (hb < GD) {
-            // key: also its norm (the four lane groups hold complementary dims)
-            float ss = 0.f;
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ss += acc[rb][cb][i] * acc[rb][cb][i];
-            ss += __shfl_xor(ss, 16);
-            ss += __shfl_xor(ss, 32);
-            if (!ok) continue;
-            if ((lane >> 4) == 0) a.kn[((int64_t)b * a.G + hb) * a.S_pad + sp] = sqrtf(ss);
-            bf16_t* dst = a.K + (((int64_t)b * a.G + hb) * a.S_pad + sp) * DH;
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                const f32x4_t v = acc[rb][cb];
-                u32x2_t pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                *reinterpret_cast<u32x2_t*>(dst + 16 * cb + 4 * (lane >> 4)) = pk;
-            }
-            continue;
-        }
-        if (!ok) continue;
-        if (is_v) {
-            // V^T [dim][key]: this lane's token is one key of four consecutive dim rows
-            const int g = hb - GD;
-            uint16_t* dst = reinterpret_cast<uint16_t*>(a.Vt) + ((int64_t)b * a.G + g) * DH * a.S_pad + vt_pos(sp);
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    dst[(int64_t)(16 * cb + 4 * (lane >> 4) + i) * a.S_pad] = from_f32<bf16_t>(acc[rb][cb][i]).bits;
-            continue;
-        }
-        bf16_t* dst;
-        if (!is_expert) dst = a.Q + (((int64_t)b * a.H + a.G * a.k) * S + sp) * DH;  // shared head
-        else dst = a.Q + (((int64_t)b * a.H + g_of * a.k + rank) * S + sp) * DH;
-        const float qs = a.qscale;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const f32x4_t v = acc[rb][cb] * qs;
-            u32x2_t pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-            *reinterpret_cast<u32x2_t*>(dst + 16 * cb + 4 * (lane >> 4)) = pk;
-        }
+    if (active) epilogue(acc, myrow, nrows, nrb);
+    if (a.stats_here && blockIdx.x == gridDim.x - 1) {
+        // the x stages are free now: LDS scratch of the statistics finalize
+        __syncthreads();
+        double* ps = reinterpret_cast<double*>(&xs[0][0]);
+        int64_t* pc = reinterpret_cast<int64_t*>(&xs[0][0] + 1024);
+        double* fp = reinterpret_cast<double*>(&xs[1][0]);
+        stats_finalize_block(a.part_cnt, a.part_psum, a.nblk_router, a.T, a.N, a.G, a.k, a.stats, ps, pc, fp);
     }
 }
 
@@ -265,6 +303,14 @@ hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x, 
     a.K = (bf16_t*)(ws + P.kk);
     a.Vt = (bf16_t*)(ws + P.vt);
     a.kn = (float*)(ws + P.kn);
+    a.knt = (float*)(ws + P.knt);
+    a.knt_here = (P.S % 64 == 0) ? 1 : 0;
+    a.stats_here = D.dense ? 0 : 1;
+    a.N = D.N;
+    a.part_cnt = (const int32_t*)(ws + P.part_cnt);
+    a.part_psum = (const double*)(ws + P.part_psum);
+    a.stats = ws + P.stats;
+    a.nblk_router = P.nblk_router;
     a.qscale = (float)(1.4426950408889634 / std::sqrt((double)D.dh));
     a.T = P.T;
     a.S = P.S;

@@ -20,6 +20,7 @@
 // scalar operands.
 #include "gqe_common.h"
 #include "gqe_internal.h"
+#include "gqe_stats.h"
 
 namespace {
 
@@ -225,45 +226,7 @@ __global__ void __launch_bounds__(256) stats_finalize_kernel(const int32_t* __re
     __shared__ double ps[256];
     __shared__ int64_t pc[256];
     __shared__ double fp[64];
-    int64_t* counts = reinterpret_cast<int64_t*>(stats);
-    double* mean = reinterpret_cast<double*>(stats + 8 * N);
-    double* aux = reinterpret_cast<double*>(stats + 16 * N);
-    const int J = 256 / N;
-    const int e = threadIdx.x % N, j = threadIdx.x / N;
-    double s = 0.0;
-    int64_t c = 0;
-    if (j < J) {
-        for (int64_t b = j; b < nblk; b += J) {
-            c += part_cnt[b * N + e];
-            s += part_psum[b * N + e];
-        }
-    }
-    ps[threadIdx.x] = s;
-    pc[threadIdx.x] = c;
-    __syncthreads();
-    if (threadIdx.x < N) {
-        double tot = 0.0;
-        int64_t ct = 0;
-        for (int jj = 0; jj < J; ++jj) {
-            tot += ps[jj * N + threadIdx.x];
-            ct += pc[jj * N + threadIdx.x];
-        }
-        counts[threadIdx.x] = ct;
-        const double P = tot / (double)T;
-        mean[threadIdx.x] = P;
-        fp[threadIdx.x] = ((double)ct / ((double)T * (double)k)) * P;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int n = N / G;
-        double tot = 0.0;
-        for (int g = 0; g < G; ++g) {
-            double Lg = 0.0;
-            for (int jj = 0; jj < n; ++jj) Lg += fp[g * n + jj];
-            tot += (double)n * Lg;
-        }
-        *aux = tot / (double)G;
-    }
+    stats_finalize_block(part_cnt, part_psum, nblk, T, N, G, k, stats, ps, pc, fp);
 }
 
 }  // namespace
@@ -272,7 +235,7 @@ bool router_uses_mfma(const GqeDims& D) { return D.d % 64 == 0 && D.N <= 16; }
 
 hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, const void* packed,
                          const PackedLayout& pl, char* ws, int32_t* route_idx, float* route_w,
-                         hipStream_t st, KernelMarks* km) {
+                         hipStream_t st, KernelMarks* km, bool finalize) {
     const char* pk = (const char*)packed;
     RouterArgs a{};
     a.x = x;
@@ -305,6 +268,7 @@ hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, con
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (km) km->mark(KT_ROUTER);
+    if (!finalize) return hipSuccess;  // the projection kernel's last work group finalizes
     if (km) km->begin(KT_ROUTER_STATS);
     stats_finalize_kernel<<<1, 256, 0, st>>>(a.part_cnt, a.part_psum, P.nblk_router, P.T, D.N, D.G, D.k,
                                              ws + P.stats);

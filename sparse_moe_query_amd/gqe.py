@@ -151,7 +151,7 @@ def gqe_aux_stats(h, n_experts: int, stream=None) -> dict:
 
 
 def gqe_workspace_layout(h, batch: int, seq: int):
-    offs = (ctypes.c_size_t * 8)()
+    offs = (ctypes.c_size_t * 10)()
     dims = (ctypes.c_int64 * 4)()
     _check(lib().gqe_workspace_layout(h, batch, seq, offs, dims))
     return list(offs), list(dims)
@@ -264,6 +264,8 @@ class GQEAttention:
             idx=view(offs[4], (T, self.G, self.k), torch.int32, 4),
             w=view(offs[5], (T, self.G, self.k), torch.float32, 4),
             psel=view(offs[6], (T, self.G, self.k), torch.float32, 4),
+            kn=view(offs[8], (batch, self.G, S_pad), torch.float32, 4),
+            knt=view(offs[9], (batch, self.G, S_pad // 64), torch.float32, 4),
             matrix_core=bool(dims[2]),
         )
 

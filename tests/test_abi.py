@@ -94,7 +94,7 @@ def test_host_side_sizes_and_state_errors():
         assert e.value.code == -6
         offs, dims = gqe.gqe_workspace_layout(h, 2, 100)
         assert dims[0] == 9 and dims[1] == 128
-        assert len(set(offs)) == 8
+        assert len(set(offs)) == 10
         # forward before the weights are packed -> state error, no device call
         L = gqe.lib()
         rc = L.gqe_forward(h, ctypes.c_void_p(0x1000), ctypes.c_void_p(0x200000), 1, 1,

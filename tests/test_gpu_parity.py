@@ -104,6 +104,27 @@ def test_deterministic_reruns():
     np.testing.assert_array_equal(a["mean_prob"], b["mean_prob"])
 
 
+@pytest.mark.parametrize("wl", [_small("knt_s128", B=2, S=128), _small("knt_s320", B=3, S=320, seed=2),
+                                _small("knt_ragged", B=2, S=200, seed=3)], ids=lambda w: w.name)
+def test_key_norm_tile_maxima(wl):
+    """The attention's range test reads the largest key norm of every 64-key tile: it must be
+    the maximum of that tile's key norms (bit-exact: the square root is monotone and correctly
+    rounded), and each key norm the norm of the stored-before-rounding key within float32."""
+    from sparse_moe_query_amd.runner import build_layer, run_layer
+    layer, x, _ = build_layer(wl)
+    run_layer(layer, x)
+    inter = layer.intermediates(wl.batch, wl.seq)
+    kn = inter["kn"].cpu().numpy()[:, :, :wl.seq]
+    knt = inter["knt"].cpu().numpy()
+    S = wl.seq
+    for j in range(knt.shape[2]):
+        ref = kn[:, :, 64 * j:min(64 * (j + 1), S)].max(axis=2)
+        np.testing.assert_array_equal(knt[:, :, j], ref)
+    kg = inter["k"].float().cpu().numpy()[:, :, :S]
+    np.testing.assert_allclose(kn, np.sqrt((kg.astype(np.float64) ** 2).sum(-1)), rtol=2e-2)
+    layer.close()
+
+
 def test_abi_errors_on_device():
     from sparse_moe_query_amd import gqe
     from sparse_moe_query_amd.runner import build_layer
