@@ -75,12 +75,18 @@ PackedLayout make_packed_layout(const GqeDims& D, bool mfma) {
     L.wr64 = take((size_t)D.d * round_up(D.N, 16) * 8);
     L.br64 = take((size_t)D.N * 8);
     L.hb_total = 2 * D.G + D.s + D.N;
-    L.slots = D.dense ? D.N : D.N + (D.variant == GQE_VARIANT_GQE ? D.G : 0) + D.s;
+    const bool rslot = !D.dense && D.variant == GQE_VARIANT_GQE;
+    L.slots = D.dense ? D.N : D.N + (rslot ? D.G : 0) + D.s;
     L.wo_pitch = 0;
+    L.rslot_fused = 0;
     L.wproj = L.wo = 0;
     if (mfma) {
         L.wproj = take((size_t)L.hb_total * D.dh * D.d * 2);
         if (combine_mfma_supported(D)) {
+            if (rslot && D.k == 1) {
+                L.rslot_fused = 1;
+                L.slots = D.N + D.s;
+            }
             L.wo_pitch = combine_stage_pitch(D.dh);
             L.wo = take((size_t)D.d * L.slots * L.wo_pitch * 16);
         }

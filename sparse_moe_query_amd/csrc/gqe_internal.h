@@ -23,6 +23,8 @@ struct PackedLayout {
     int hb_total;        // number of projection head blocks
     int slots;           // output-projection slots (expert slots, renormalised slots, shared)
     int wo_pitch;        // 16-byte chunks per output column of one W_stack stage (0: not packed)
+    int rslot_fused;     // variant gqe with one choice per group: each expert slot carries
+                         // W_o[e] + W_oR[g] (the renormalised weight is exactly 1), no own slot
 };
 
 // Byte offsets into the caller's workspace for one [B, S] forward.

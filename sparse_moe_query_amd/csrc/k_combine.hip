@@ -24,7 +24,8 @@
 //   fragments a token fragment (8 consecutive head dims of one token) is the LDS chunk of the
 //             chosen head (copy), that chunk or zero (select), or a coefficient-weighted sum of
 //             the group's heads rounded once to bf16 (scale); with one choice per group the
-//             renormalised weight is exactly 1 (p / p), so the gqe slot is a copy
+//             renormalised weight is exactly 1 (p / p): the gqe slot's weights are then folded
+//             into the group's expert slots when the weights are packed (one slot per expert)
 // No compiler-visible global load sits in the loop, so every wait is an explicit vmcnt.
 #include "gqe_common.h"
 #include "gqe_internal.h"
@@ -337,7 +338,7 @@ hipError_t launch_combine_mfma(const GqeDims& D, const WorkPlan& P, const void* 
         a.NUM = D.N;
         a.KHU = 1;
     } else {
-        a.PG = D.n + (D.variant == GQE_VARIANT_GQE ? 1 : 0);
+        a.PG = D.n + (D.variant == GQE_VARIANT_GQE && !pl.rslot_fused ? 1 : 0);
         a.NUM = D.G;
         a.KHU = D.k;
     }

@@ -1,10 +1,13 @@
-// Weight repacking (layout only, no arithmetic of the layer):
+// Weight repacking (layout, plus one addition for the fused output slots below):
 //  - the router weights widened to float64 (exact) in the lane order of the router kernel;
 //  - bf16 path: every projection head block transposed to [d_h][d] so that each matrix-core
 //    lane reads eight consecutive hidden-dimension values with one 16-byte load;
 //  - bf16 path: the output projections stacked into one [d][slots * d_h] matrix, slot order
 //    per group g: its n expert slots, then (variant gqe) its renormalised slot; then the shared
-//    head's slot.
+//    head's slot.  Variant gqe with one choice per group: the renormalised weight of the single
+//    choice is exactly 1, so the group's slot operand equals the chosen head's output and
+//    O W_o[e] + O W_oR[g] = O (W_o[e] + W_oR[g]); each expert slot then carries that sum (formed
+//    in float32, rounded once to bf16) and the renormalised slot is dropped.
 #include "gqe_common.h"
 #include "gqe_internal.h"
 
@@ -66,9 +69,10 @@ __global__ void pack_proj_kernel(const uint16_t* __restrict__ wk, const uint16_t
 // dst[((ct * slots + slot) * 128 + c) * pitch * 8 + j] = W_stack[slot * dh + j][ct * 128 + c] for
 // j < dh, zero for the pad chunk (pitch = d_h / 8 rounded up to odd, in 16-byte chunks).
 // Slot order: per group its n experts then (gqe) its weighted-sum slot; the shared head last.
+// fuse: no weighted-sum slot, W_oR[g] added into each expert slot of group g.
 __global__ void pack_wo_kernel(const uint16_t* __restrict__ wo, const uint16_t* __restrict__ wor,
                                const uint16_t* __restrict__ wos, int d, int G, int n, int dh,
-                               int rslot, int slots, int pitch, uint16_t* __restrict__ dst) {
+                               int rslot, int fuse, int slots, int pitch, uint16_t* __restrict__ dst) {
     const int64_t per_col = (int64_t)pitch * 8;
     const int64_t total = (int64_t)d * slots * per_col;
     const int per_group = n + rslot;
@@ -85,8 +89,16 @@ __global__ void pack_wo_kernel(const uint16_t* __restrict__ wo, const uint16_t* 
         if (j < dh) {
             if (slot < G * per_group) {
                 const int g = slot / per_group, u = slot % per_group;
-                if (u < n) v = wo[((int64_t)(g * n + u) * dh + j) * d + col];
-                else v = wor[((int64_t)g * dh + j) * d + col];
+                if (u < n) {
+                    v = wo[((int64_t)(g * n + u) * dh + j) * d + col];
+                    if (fuse) {
+                        const float f = __uint_as_float((uint32_t)v << 16) +
+                                        __uint_as_float((uint32_t)wor[((int64_t)g * dh + j) * d + col] << 16);
+                        v = from_f32<bf16_t>(f).bits;
+                    }
+                } else {
+                    v = wor[((int64_t)g * dh + j) * d + col];
+                }
             } else {
                 v = wos[(int64_t)j * d + col];
             }
@@ -112,10 +124,10 @@ hipError_t launch_pack(const GqeDims& D, const gqe_weights_t& w, const PackedLay
                                            D.d, D.G, D.dh, D.s, D.N, (uint16_t*)(pk + pl.wproj));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int rslot = (!D.dense && D.variant == GQE_VARIANT_GQE) ? 1 : 0;
+    const int rslot = (!D.dense && D.variant == GQE_VARIANT_GQE && !pl.rslot_fused) ? 1 : 0;
     if (pl.wo_pitch == 0) return hipSuccess;  // combine on the scalar path
     pack_wo_kernel<<<1024, 256, 0, st>>>((const uint16_t*)w.w_o, (const uint16_t*)w.w_o_rslot,
                                          (const uint16_t*)w.w_o_shared, D.d, D.G, D.n, D.dh, rslot,
-                                         pl.slots, pl.wo_pitch, (uint16_t*)(pk + pl.wo));
+                                         pl.rslot_fused, pl.slots, pl.wo_pitch, (uint16_t*)(pk + pl.wo));
     return hipGetLastError();
 }
