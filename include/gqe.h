@@ -17,7 +17,10 @@
  *  - Device pointers are plain addresses in the memory of the current HIP device.  All
  *    tensors are dense and row-major in the "x @ W" convention; shapes are given per argument.
  *  - Ownership: the caller owns every device buffer (x, y, weights, packed weights, workspace,
- *    routing outputs) and the stream.  The library owns only the opaque host handle.
+ *    routing outputs) and the stream.  The library owns the opaque host handle and, per
+ *    (device, batch, seq) it has run, a small device table of the attention work schedule
+ *    (8 int32 per work group), allocated and copied synchronously on the first gqe_forward of
+ *    that shape and freed by gqe_destroy.
  *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
  *    enqueued asynchronously; only gqe_aux_stats synchronises.
  *  - A handle is not re-entrant: calls that use one handle (or one workspace) must not overlap
@@ -128,7 +131,8 @@ int gqe_packed_weights_bytes(const gqe_handle_t* h, size_t* bytes);
 int gqe_pack_weights(gqe_handle_t* h, void* packed, size_t bytes, void* stream);
 
 /* Bytes of scratch that gqe_forward needs for a [batch, seq] input (routing decisions,
- * per-expert statistics, Q/K/V and head outputs).  batch >= 1, seq >= 1. */
+ * per-expert statistics, Q/K/V, head outputs and the float32 partial results of attention items
+ * that the schedule splits along the key range).  batch >= 1, seq >= 1.  Host only. */
 int gqe_workspace_bytes(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t* bytes);
 
 /* The forward pass y = GQE(x) (README "Usage": y = attn(x)).
@@ -189,6 +193,21 @@ int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size
  * GQE_ERR_HIP. */
 int gqe_bucket(gqe_handle_t* h, void* stream, int32_t* offs, int32_t* perm, int32_t* inv);
 
+/* The work schedule of the matrix-core attention for a [batch, seq] forward (host only, no device
+ * call; the same tables gqe_forward uploads).  The causal attention of item (batch b, group g,
+ * positions p0 .. p0+np-1, the nh active heads of the group at each position: 256 / nh positions
+ * per item) reads the key tiles 0 .. (last position)/64; long items are split into chunks of
+ * consecutive key tiles whose float32 partial results a merge kernel combines (online-softmax
+ * merge over disjoint key ranges).
+ *  jobs    NULL or [max_jobs][8] int32, dispatch order: b, g, nh, p0, np, kt0, kt1 (key tiles
+ *          [kt0, kt1)), partial slot (-1: the job covers the whole item and writes O itself)
+ *  merges  NULL or [max_merges][8] int32: b, g, nh, p0, np, first slot, chunks, 0
+ *  counts  [4]: jobs, merges, partial slots, chunk cap in key tiles (0: nothing split)
+ * Errors: GQE_ERR_NULL_POINTER, GQE_ERR_SHAPE, GQE_ERR_STATE (scalar attention path),
+ * GQE_ERR_WORKSPACE (a buffer smaller than the count). */
+int gqe_attention_schedule(const gqe_handle_t* h, int64_t batch, int64_t seq, int32_t* jobs,
+                           int64_t max_jobs, int32_t* merges, int64_t max_merges, int64_t counts[4]);
+
 /* Kernel timing for measurement.  While enabled, gqe_forward records a HIP event on its stream
  * right before and right after each kernel it launches; a kernel's duration is the time between
  * the two.  Kernel slots, in launch order:
@@ -199,14 +218,14 @@ int gqe_bucket(gqe_handle_t* h, void* stream, int32_t* offs, int32_t* perm, int3
  * gqe_profile_read_kernels waits for the recorded events, returns the summed milliseconds per
  * kernel slot (0 for slots not launched) and the number of forwards they cover, and starts a new
  * accumulation.  gqe_profile_read does the same summed per stage (0 router = slots 0+1,
- * 1 projections = 2+3, 2 attention = 4+5, 3 combine = 6).  Not re-entrant; errors as
+ * 1 projections = 2+3, 2 attention = 4+5+6, 3 combine = 7).  Not re-entrant; errors as
  * GQE_ERR_NULL_POINTER / GQE_ERR_HIP. */
-#define GQE_PROF_KERNELS 7
+#define GQE_PROF_KERNELS 8
 int gqe_profile_enable(gqe_handle_t* h, int enable);
 int gqe_profile_read(gqe_handle_t* h, double stage_ms[4], int64_t* forwards);
 int gqe_profile_read_kernels(gqe_handle_t* h, double kernel_ms[GQE_PROF_KERNELS], int64_t* forwards);
 
-/* Destroys the handle (host memory only).  NULL is ignored. */
+/* Destroys the handle and frees the device schedule tables it owns.  NULL is ignored. */
 void gqe_destroy(gqe_handle_t* h);
 
 /* Message of the last failing call on this thread ("" if none). */

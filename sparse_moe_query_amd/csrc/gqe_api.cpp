@@ -32,7 +32,7 @@ static bool misaligned(const void* p, size_t a) { return ((uintptr_t)p) % a != 0
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S) {
+WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S, int64_t attn_slots) {
     WorkPlan P;
     P.B = B;
     P.S = S;
@@ -60,6 +60,9 @@ WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S) {
     P.o = take((size_t)B * S * D.H * D.dh * es);
     P.kn = take((size_t)B * D.G * P.S_pad * 4);
     P.knt = take((size_t)B * D.G * (P.S_pad / GQE_KV_TILE) * 4);
+    P.nslots = attn_slots;
+    P.part_o = take((size_t)attn_slots * GQE_ATTN_COLS * D.dh * 4);
+    P.part_ml = take((size_t)attn_slots * GQE_ATTN_COLS * 2 * 4);
     P.total = off;
     return P;
 }
@@ -106,6 +109,46 @@ static bool mfma_supported(const GqeDims& D) {
     if (!D.dense && 8 * D.k + D.n > 24) return false;
     if (D.H > 64) return false;
     return true;
+}
+
+// Partial-result slots of the attention schedule for [B, S] (0 on the scalar attention path).
+static int64_t attn_slots(const gqe_handle* h, int64_t B, int64_t S) {
+    if (!h->mfma_attn) return 0;
+    for (const AttnSchedDev& c : h->sched)
+        if (c.B == B && c.S == S) return c.nslots;
+    return plan_attention(h->D, B, S, false).nslots;
+}
+
+// The device copy of the attention schedule for [B, S] on the current device: built on the host
+// and uploaded on first use (synchronous copy), then reused.
+static int attn_schedule(gqe_handle* h, int64_t B, int64_t S, const AttnSchedDev** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GQE_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    for (const AttnSchedDev& c : h->sched)
+        if (c.device == dev && c.B == B && c.S == S) {
+            *out = &c;
+            return GQE_OK;
+        }
+    const AttnSchedule sc = plan_attention(h->D, B, S, true);
+    AttnSchedDev d{dev, B, S, nullptr, nullptr, (int)sc.jobs.size(), (int)sc.merges.size(), sc.nslots};
+    if (sc.jobs.empty() || sc.jobs.size() > 0x7fffffffu)
+        return fail(GQE_ERR_SHAPE, "attention schedule has %zu jobs", sc.jobs.size());
+    e = hipMalloc((void**)&d.jobs, sc.jobs.size() * sizeof(AttnJob));
+    if (e == hipSuccess) e = hipMemcpy(d.jobs, sc.jobs.data(), sc.jobs.size() * sizeof(AttnJob), hipMemcpyHostToDevice);
+    if (e == hipSuccess && !sc.merges.empty()) {
+        e = hipMalloc((void**)&d.merges, sc.merges.size() * sizeof(AttnMerge));
+        if (e == hipSuccess)
+            e = hipMemcpy(d.merges, sc.merges.data(), sc.merges.size() * sizeof(AttnMerge), hipMemcpyHostToDevice);
+    }
+    if (e != hipSuccess) {
+        if (d.jobs) (void)hipFree(d.jobs);
+        if (d.merges) (void)hipFree(d.merges);
+        return fail(GQE_ERR_HIP, "upload of the attention schedule failed: %s", hipGetErrorString(e));
+    }
+    h->sched.push_back(d);
+    *out = &h->sched.back();
+    return GQE_OK;
 }
 
 extern "C" {
@@ -199,14 +242,14 @@ int gqe_workspace_bytes(const gqe_handle_t* h, int64_t batch, int64_t seq, size_
     if (!h || !bytes) return fail(GQE_ERR_NULL_POINTER, "handle and bytes must be non-NULL");
     if (batch < 1 || seq < 1 || batch * seq > ((int64_t)1 << 28))
         return fail(GQE_ERR_SHAPE, "batch and seq must be >= 1 with batch*seq <= 2^28");
-    *bytes = make_plan(h->D, batch, seq).total;
+    *bytes = make_plan(h->D, batch, seq, attn_slots(h, batch, seq)).total;
     return ok();
 }
 
 int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t offs[10], int64_t dims[4]) {
     if (!h || !offs || !dims) return fail(GQE_ERR_NULL_POINTER, "handle, offs and dims must be non-NULL");
     if (batch < 1 || seq < 1 || batch * seq > ((int64_t)1 << 28)) return fail(GQE_ERR_SHAPE, "bad batch/seq");
-    WorkPlan P = make_plan(h->D, batch, seq);
+    WorkPlan P = make_plan(h->D, batch, seq, attn_slots(h, batch, seq));
     offs[0] = P.q;
     offs[1] = P.kk;
     offs[2] = P.vt;
@@ -241,7 +284,12 @@ int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t 
     const char* xb = (const char*)x;
     const char* yb = (const char*)y;
     if (xb < yb + xbytes && yb < xb + xbytes) return fail(GQE_ERR_INVALID_CONFIG, "x and y must not alias");
-    WorkPlan P = make_plan(D, batch, seq);
+    const AttnSchedDev* sched = nullptr;
+    if (h->mfma_attn) {
+        const int rc = attn_schedule(h, batch, seq, &sched);
+        if (rc != GQE_OK) return rc;
+    }
+    WorkPlan P = make_plan(D, batch, seq, sched ? sched->nslots : 0);
     if (ws_bytes < P.total) return fail(GQE_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, P.total);
     hipStream_t st = (hipStream_t)stream;
     char* ws = (char*)workspace;
@@ -272,7 +320,7 @@ int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t 
                          : launch_proj_simple(D, P, h->w, x, ws, st, km);
     if (e == hipSuccess && !h->mfma_proj && h->mfma_attn) e = launch_kn_simple(D, P, ws, st, km);
     if (e == hipSuccess)
-        e = h->mfma_attn ? launch_attn_mfma(D, P, ws, st, km, !(h->mfma_proj && P.S % 64 == 0))
+        e = h->mfma_attn ? launch_attn_mfma(D, P, *sched, ws, st, km, !(h->mfma_proj && P.S % 64 == 0))
                          : launch_attn_simple(D, P, ws, st, km);
     if (e == hipSuccess)
         e = h->mfma_combine ? launch_combine_mfma(D, P, h->packed, h->pl, y, ws, st, km)
@@ -333,6 +381,29 @@ int gqe_bucket(gqe_handle_t* h, void* stream, int32_t* offs, int32_t* perm, int3
     return ok();
 }
 
+int gqe_attention_schedule(const gqe_handle_t* h, int64_t batch, int64_t seq, int32_t* jobs, int64_t max_jobs,
+                           int32_t* merges, int64_t max_merges, int64_t counts[4]) {
+    if (!h || !counts) return fail(GQE_ERR_NULL_POINTER, "handle and counts must be non-NULL");
+    if (batch < 1 || seq < 1 || batch * seq > ((int64_t)1 << 28)) return fail(GQE_ERR_SHAPE, "bad batch/seq");
+    if (!h->mfma_attn) return fail(GQE_ERR_STATE, "this configuration runs the scalar attention path (no schedule)");
+    const AttnSchedule sc = plan_attention(h->D, batch, seq, true);
+    counts[0] = (int64_t)sc.jobs.size();
+    counts[1] = (int64_t)sc.merges.size();
+    counts[2] = sc.nslots;
+    counts[3] = sc.chunk;
+    if (jobs) {
+        if (max_jobs < counts[0]) return fail(GQE_ERR_WORKSPACE, "jobs buffer holds %lld < %lld records",
+                                              (long long)max_jobs, (long long)counts[0]);
+        std::memcpy(jobs, sc.jobs.data(), sc.jobs.size() * sizeof(AttnJob));
+    }
+    if (merges) {
+        if (max_merges < counts[1]) return fail(GQE_ERR_WORKSPACE, "merges buffer holds %lld < %lld records",
+                                                (long long)max_merges, (long long)counts[1]);
+        std::memcpy(merges, sc.merges.data(), sc.merges.size() * sizeof(AttnMerge));
+    }
+    return ok();
+}
+
 int gqe_profile_enable(gqe_handle_t* h, int enable) {
     if (!h) return fail(GQE_ERR_NULL_POINTER, "handle must be non-NULL");
     h->prof = enable != 0;
@@ -368,7 +439,7 @@ int gqe_profile_read(gqe_handle_t* h, double stage_ms[4], int64_t* forwards) {
     if (rc != GQE_OK) return rc;
     stage_ms[0] = k[KT_ROUTER] + k[KT_ROUTER_STATS];
     stage_ms[1] = k[KT_PROJ] + k[KT_KEYNORM];
-    stage_ms[2] = k[KT_ATTN_PREP] + k[KT_ATTN];
+    stage_ms[2] = k[KT_ATTN_PREP] + k[KT_ATTN] + k[KT_ATTN_MERGE];
     stage_ms[3] = k[KT_COMBINE];
     return ok();
 }
@@ -376,6 +447,14 @@ int gqe_profile_read(gqe_handle_t* h, double stage_ms[4], int64_t* forwards) {
 void gqe_destroy(gqe_handle_t* h) {
     if (!h) return;
     for (hipEvent_t e : h->prof_ev) (void)hipEventDestroy(e);
+    for (AttnSchedDev& c : h->sched) {
+        int cur = 0;
+        const bool other = hipGetDevice(&cur) == hipSuccess && cur != c.device;
+        if (other) (void)hipSetDevice(c.device);
+        if (c.jobs) (void)hipFree(c.jobs);
+        if (c.merges) (void)hipFree(c.merges);
+        if (other) (void)hipSetDevice(cur);
+    }
     delete h;
 }
 

@@ -9,6 +9,9 @@
 
 #include "../../include/gqe.h"
 
+#define GQE_ATTN_COLS 256        // query columns (position, head) of one attention work item
+#define GQE_ATTN_MAX_CHUNKS 32   // key-range chunks an attention item may be split into
+
 struct GqeDims {
     int d, N, G, k, n, dh, H, s;  // s = shared head on; H = active heads per token
     int variant, dtype, skv, dense;
@@ -38,7 +41,38 @@ struct WorkPlan {
     size_t q, kk, vt, o;              // Q_act, K, V^T, O_act
     size_t kn;                        // per-key norms [B][G][S_pad] f32
     size_t knt;                       // per-64-key-tile maximum norm [B][G][S_pad/64] f32
+    size_t part_o, part_ml;           // attention partials [nslots][256][d_h] / [nslots][256][2] f32
+    int64_t nslots;
     size_t total;
+};
+
+// One attention work group: item (batch b, group g, nh heads per position, positions
+// [p0, p0 + np)) restricted to key tiles [kt0, kt1); part = partial-result slot, or -1 when the
+// job covers the whole item and writes O itself.  Eight int32 per job on the device.
+struct AttnJob {
+    int32_t b, g, nh, p0, np, kt0, kt1, part;
+};
+// One merge work group: the item's nc chunks sit in slots slot0 .. slot0 + nc - 1.
+struct AttnMerge {
+    int32_t b, g, nh, p0, np, slot0, nc, pad;
+};
+struct AttnSchedule {
+    std::vector<AttnJob> jobs;      // dispatch order
+    std::vector<AttnMerge> merges;
+    int64_t nslots = 0;             // partial-result slots
+    int chunk = 0;                  // chunk cap in key tiles (0: no item split)
+};
+// tables = false: only nslots and chunk (for workspace sizing)
+AttnSchedule plan_attention(const GqeDims& D, int64_t B, int64_t S, bool tables);
+
+// Device copy of a schedule, owned by the handle (one per (device, batch, seq) run).
+struct AttnSchedDev {
+    int device;
+    int64_t B, S;
+    AttnJob* jobs;
+    AttnMerge* merges;
+    int njobs, nmerges;
+    int64_t nslots;
 };
 
 struct gqe_handle {
@@ -58,10 +92,11 @@ struct gqe_handle {
     std::vector<hipEvent_t> prof_ev;     // 2 * KT_COUNT events per recorded forward
     std::vector<uint32_t> prof_mask;     // kernel slots recorded by each forward
     size_t prof_used = 0;                // forwards recorded
+    std::vector<AttnSchedDev> sched;     // attention schedules uploaded so far
 };
 
 // Kernel timing slots, in launch order (GQE_PROF_KERNELS in gqe.h).
-enum { KT_ROUTER = 0, KT_ROUTER_STATS, KT_PROJ, KT_KEYNORM, KT_ATTN_PREP, KT_ATTN, KT_COMBINE, KT_COUNT };
+enum { KT_ROUTER = 0, KT_ROUTER_STATS, KT_PROJ, KT_KEYNORM, KT_ATTN_PREP, KT_ATTN, KT_ATTN_MERGE, KT_COMBINE, KT_COUNT };
 
 // Records events on the stream right before and right after each kernel a launcher enqueues
 // (when timing is on).
@@ -80,7 +115,7 @@ struct KernelMarks {
     }
 };
 
-WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S);
+WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S, int64_t attn_slots);
 hipError_t launch_kn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km);
 bool router_uses_mfma(const GqeDims& D);
 PackedLayout make_packed_layout(const GqeDims& D, bool mfma);
@@ -99,8 +134,8 @@ hipError_t launch_combine_simple(const GqeDims& D, const WorkPlan& P, const gqe_
 hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x,
                             const void* packed, const PackedLayout& pl, char* ws,
                             hipStream_t st, KernelMarks* km);
-hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km,
-                            bool prep);
+hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, const AttnSchedDev& sc, char* ws, hipStream_t st,
+                            KernelMarks* km, bool prep);
 hipError_t launch_bucket(const GqeDims& D, const WorkPlan& P, char* ws, int32_t* offs, int32_t* perm, int32_t* inv,
                          hipStream_t st);
 bool combine_mfma_supported(const GqeDims& D);

@@ -25,10 +25,12 @@ ERRORS = {0: "GQE_OK", -1: "GQE_ERR_INVALID_CONFIG", -2: "GQE_ERR_NULL_POINTER",
           -6: "GQE_ERR_SHAPE", -7: "GQE_ERR_HIP", -8: "GQE_ERR_STATE"}
 EXPORTS = ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights", "gqe_workspace_bytes",
            "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_bucket", "gqe_profile_enable",
-           "gqe_profile_read", "gqe_profile_read_kernels", "gqe_destroy", "gqe_last_error")
+           "gqe_profile_read", "gqe_profile_read_kernels", "gqe_attention_schedule", "gqe_destroy",
+           "gqe_last_error")
 STAGES = ("router", "projection", "attention", "combine")
 # kernel timing slots of gqe_profile_read_kernels, in launch order
-KERNELS = ("router", "router_stats", "projection", "key_norms", "attention_prep", "attention", "combine")
+KERNELS = ("router", "router_stats", "projection", "key_norms", "attention_prep", "attention", "attention_merge",
+           "combine")
 
 
 class GqeError(RuntimeError):
@@ -72,13 +74,15 @@ def lib():
         L.gqe_profile_enable.argtypes = [P, ctypes.c_int]
         L.gqe_profile_read.argtypes = [P, P, P]
         L.gqe_profile_read_kernels.argtypes = [P, P, P]
+        L.gqe_attention_schedule.argtypes = [P, I64, I64, P, I64, P, I64, P]
         L.gqe_destroy.argtypes = [P]
         L.gqe_destroy.restype = None
         L.gqe_last_error.argtypes = []
         L.gqe_last_error.restype = ctypes.c_char_p
         for f in ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights",
                   "gqe_workspace_bytes", "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_bucket",
-                  "gqe_profile_enable", "gqe_profile_read", "gqe_profile_read_kernels"):
+                  "gqe_profile_enable", "gqe_profile_read", "gqe_profile_read_kernels",
+                  "gqe_attention_schedule"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -173,6 +177,19 @@ def gqe_profile_read_kernels(h):
     n = ctypes.c_int64()
     _check(lib().gqe_profile_read_kernels(h, ms, ctypes.byref(n)))
     return dict(zip(KERNELS, list(ms))), n.value
+
+
+def gqe_attention_schedule(h, batch: int, seq: int):
+    """The attention work schedule (host only): jobs [n, 8] and merges [m, 8] int32 (numpy), the
+    number of partial slots and the chunk cap in key tiles."""
+    import numpy as np
+    counts = (ctypes.c_int64 * 4)()
+    _check(lib().gqe_attention_schedule(h, batch, seq, None, 0, None, 0, counts))
+    jobs = np.zeros((max(counts[0], 1), 8), dtype=np.int32)
+    merges = np.zeros((max(counts[1], 1), 8), dtype=np.int32)
+    _check(lib().gqe_attention_schedule(h, batch, seq, jobs.ctypes.data_as(ctypes.c_void_p), jobs.shape[0],
+                                        merges.ctypes.data_as(ctypes.c_void_p), merges.shape[0], counts))
+    return jobs[:counts[0]], merges[:counts[1]], int(counts[2]), int(counts[3])
 
 
 def gqe_destroy(h):
