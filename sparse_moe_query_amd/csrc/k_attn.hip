@@ -217,6 +217,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
     const_i32_ptr jb = (const_i32_ptr)(a.jobs + 8 * (int64_t)blockIdx.x);
     const int ib = jb[0], ig = jb[1], NH = jb[2], p0 = jb[3], np = jb[4];
     const int kt0 = jb[5], kt_end = jb[6], part = jb[7];
+    if (kt_end <= kt0) return;  // padding of the schedule's XCD lists
     const int S = (int)a.S;  // the host limits a call to 2^28 tokens
     const int last_pos = min(p0 + np, S) - 1;  // last query position of the item
 

@@ -98,3 +98,4 @@ def test_long_items_are_split_at_16k():
         gqe.gqe_destroy(h)
     assert chunk > 0 and len(merges) > 0
     assert (jobs[:, 6] - jobs[:, 5]).max() < 256
+
