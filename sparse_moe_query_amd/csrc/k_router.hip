@@ -10,12 +10,13 @@
 // the lower local index.
 //
 // Fast path (d % 64 == 0, N <= 16): v_mfma_f64_16x16x4_f64 (full-rate fp64 on gfx950).  A block
-// owns 64 tokens; wave w of 8 sums the w-th eighth of the hidden dimension for all of them.  Each lane
+// owns 64 tokens; wave w of 4 sums the w-th quarter of the hidden dimension for all of them, its
+// x and weight loads issued three 32-wide chunks at a time ahead of the products.  Each lane
 // loads eight consecutive hidden values of one token with one 16-byte load; the k index of the
 // MFMA is permuted accordingly (k-step s of lane group q covers hidden index 8q + s), and the
 // router weights are pre-permuted into exactly that lane order ([octet of 8 hidden indices]
 // [column][8], by gqe_pack_weights), so the B operands are 64 contiguous bytes per lane.  The
-// eight partial sums are added in a fixed order.
+// four partial sums are added in a fixed order; two blocks fit one CU (68 KB of LDS each).
 // Generic path (any d, N <= 64): one token per lane, float64 FMAs with the weights as wave-uniform
 // scalar operands.
 #include "gqe_common.h"
@@ -109,19 +110,30 @@ __device__ void select_and_stats(const RouterArgs& a, double (*lg)[65], int* cnt
         }
     }
     __syncthreads();
+    // per-block probability sums of every expert, in a fixed order: thread (expert e, token
+    // group j) sums tokens j, j + kJ, ...; the kJ group sums are then added in order
+    constexpr int kJ = 8;  // token groups
+    __shared__ double gs[kJ][64];
+    for (int q = threadIdx.x; q < kJ * a.N; q += nthreads) {
+        const int e = q % a.N, j = q / a.N;
+        double s = 0.0;
+        for (int tok = j; tok < kTok; tok += kJ)
+            if (t0 + tok < a.T) s += lg[tok][e];
+        gs[j][e] = s;
+    }
+    __syncthreads();
     if (threadIdx.x < a.N) {
         const int e = threadIdx.x;
         double s = 0.0;
-        for (int tok = 0; tok < kTok; ++tok)
-            if (t0 + tok < a.T) s += lg[tok][e];
+        for (int j = 0; j < kJ; ++j) s += gs[j][e];
         a.part_psum[(int64_t)blockIdx.x * a.N + e] = s;
         a.part_cnt[(int64_t)blockIdx.x * a.N + e] = cnt[e];
     }
 }
 
 template <typename Tin>
-__global__ void __launch_bounds__(512) router_mfma_kernel(RouterArgs a) {
-    constexpr int kW = 8;  // waves; wave w sums the w-th eighth of the hidden dimension
+__global__ void __launch_bounds__(256) router_mfma_kernel(RouterArgs a) {
+    constexpr int kW = 4;  // waves; wave w sums the w-th quarter of the hidden dimension
     __shared__ double red[kW][kTok][17];
     __shared__ double lg[kTok][65];
     __shared__ int cnt[64];
@@ -136,32 +148,58 @@ __global__ void __launch_bounds__(512) router_mfma_kernel(RouterArgs a) {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) acc[tb] = f64x4_t{0.0, 0.0, 0.0, 0.0};
     const Tin* xb = reinterpret_cast<const Tin*>(a.x);
-    for (int c = 0; c < nchunk; ++c) {
-        const int i0 = wv * dq + 32 * c;          // first hidden index of the chunk
-        const int ivalid = min(32, dq - 32 * c);  // hidden values of the chunk inside this share
-        double xv[4][8];
+    // Chunks go in batches of kBatch whose x and weight loads are all issued before the first
+    // product of the batch (one memory latency per batch instead of one per chunk).
+    constexpr int kBatch = 3;
+    constexpr int XW = sizeof(Tin) * 2;  // 32-bit words of a lane's eight hidden values
+    for (int c0 = 0; c0 < nchunk; c0 += kBatch) {
+        uint32_t xr[kBatch][4][XW];
+        f64x4_t wr[kBatch][2];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            int64_t t = t0 + 16 * tb + (lane & 15);
-            if (t >= a.T) t = a.T - 1;
-            if (8 * (lane >> 4) < ivalid) {
-                widen8<Tin>(xb + t * a.d + i0 + 8 * (lane >> 4), xv[tb]);
-            } else {
+        for (int cc = 0; cc < kBatch; ++cc) {
+            const int c = c0 + cc;
+            const int i0 = wv * dq + 32 * c;  // first hidden index of the chunk
+            const bool in = c < nchunk && 8 * (lane >> 4) < dq - 32 * c;
 #pragma unroll
-                for (int s = 0; s < 8; ++s) xv[tb][s] = 0.0;
+            for (int tb = 0; tb < 4; ++tb) {
+                int64_t t = t0 + 16 * tb + (lane & 15);
+                if (t >= a.T) t = a.T - 1;
+                if (in) {
+                    const uint32_t* src = reinterpret_cast<const uint32_t*>(xb + t * a.d + i0 + 8 * (lane >> 4));
+#pragma unroll
+                    for (int q = 0; q < XW; q += 4) {
+                        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + q);
+                        xr[cc][tb][q] = v[0];
+                        xr[cc][tb][q + 1] = v[1];
+                        xr[cc][tb][q + 2] = v[2];
+                        xr[cc][tb][q + 3] = v[3];
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < XW; ++q) xr[cc][tb][q] = 0u;
+                }
+            }
+            // lane-ordered weights [octet][column][8]: this lane's octet of hidden indices is
+            // i0/8 + (lane >> 4) (clamped: past the end x is zero), its column lane & 15
+            const int oct = min(i0 / 8 + (lane >> 4), a.d / 8 - 1);
+            const f64x4_t* wp = reinterpret_cast<const f64x4_t*>(a.wr + ((int64_t)oct * 16 + (lane & 15)) * 8);
+            wr[cc][0] = wp[0];
+            wr[cc][1] = wp[1];
+        }
+#pragma unroll
+        for (int cc = 0; cc < kBatch; ++cc) {
+            if (c0 + cc >= nchunk) break;
+            const double wv8[8] = {wr[cc][0][0], wr[cc][0][1], wr[cc][0][2], wr[cc][0][3],
+                                   wr[cc][1][0], wr[cc][1][1], wr[cc][1][2], wr[cc][1][3]};
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                double xv[8];
+                widen8<Tin>(reinterpret_cast<const Tin*>(xr[cc][tb]), xv);
+#pragma unroll
+                for (int s = 0; s < 8; ++s)
+                    acc[tb] = __builtin_amdgcn_mfma_f64_16x16x4f64(xv[s], wv8[s], acc[tb], 0, 0, 0);
             }
         }
-        // lane-ordered weights [octet][column][8]: this lane's octet of hidden indices is
-        // i0/8 + (lane >> 4) (clamped: past the end x is zero), its column lane & 15
-        const int oct = min(i0 / 8 + (lane >> 4), a.d / 8 - 1);
-        const f64x4_t* wp = reinterpret_cast<const f64x4_t*>(a.wr + ((int64_t)oct * 16 + (lane & 15)) * 8);
-        const f64x4_t w0 = wp[0], w1 = wp[1];
-        const double wv8[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-                acc[tb] = __builtin_amdgcn_mfma_f64_16x16x4f64(xv[tb][s], wv8[s], acc[tb], 0, 0, 0);
     }
     // C layout of v_mfma_f64_16x16x4: lane holds rows (lane >> 4) + 4i, column lane & 15
 #pragma unroll
@@ -259,8 +297,8 @@ hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, con
     const bool bf = D.dtype == GQE_DTYPE_BF16;
     if (km) km->begin(KT_ROUTER);
     if (router_uses_mfma(D)) {
-        if (bf) router_mfma_kernel<bf16_t><<<grid, 512, 0, st>>>(a);
-        else router_mfma_kernel<float><<<grid, 512, 0, st>>>(a);
+        if (bf) router_mfma_kernel<bf16_t><<<grid, 256, 0, st>>>(a);
+        else router_mfma_kernel<float><<<grid, 256, 0, st>>>(a);
     } else {
         if (bf) router_valu_kernel<bf16_t><<<grid, 256, 0, st>>>(a);
         else router_valu_kernel<float><<<grid, 256, 0, st>>>(a);
