@@ -1,6 +1,6 @@
 """Benchmark of the GQE forward (prefill) pass on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-long] [--only-main]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-long] [--no-decode] [--only-main]
                 [--profile-workload NAME] [--copy-calibration]
 
 One step = one gqe_forward over the main-setting workload (dim 768, N=16, G=8, k=1, head_dim 48,
@@ -10,8 +10,9 @@ synchronisations); the roofline of its dominant kernel (its algorithmic work per
 average launch duration, from HIP events recorded on the forward's stream right before and after
 every kernel during K more forwards; HBM traffic from the committed rocprofv3 counter summary
 when it was taken on the current kernel source, else null); the CPU
-oracle timed on a bounded sample; and, as extra fields, the all-active GQA baseline and the
-long-context runs (seq 16384 and 32768).
+oracle timed on a bounded sample; and, as extra fields, the all-active GQA baseline, the
+long-context runs (seq 16384 and 32768) and a decode step with a dense KV cache (64 sequences with
+8192 cached positions each, same layer shape).
 """
 from __future__ import annotations
 
@@ -155,6 +156,83 @@ def roofline(kernel: str, ms: float, alg: dict, workload: str, merge_ms: float =
     return r
 
 
+# Decode: the main-setting layer, one new token for each of `batch` sequences with `ctx` cached positions.
+DECODE_WORKLOADS = {"decode_b64_ctx8192": ("main_b8_s2048", 64, 8192)}
+KV_STD = 0.02 * 768 ** 0.5   # std of x @ W_k for x ~ N(0, 1), W_k ~ N(0, 0.02^2), d = 768
+
+
+def decode_algorithmic(wl, batch: int, ctx: int) -> dict:
+    """Bytes the decode attention must move: the K and V cache rows of positions 0..ctx of every
+    (sequence, group), read once (the queries, partials and outputs are a few hundred KB)."""
+    es = 2 if wl.dtype == "bf16" else 4
+    kv = 2.0 * batch * wl.num_kv_heads * (ctx + 1) * wl.dh * es
+    return dict(attention_bytes=kv)
+
+
+def run_decode(name: str, steps: int, warmup: int, gqa: bool = False, profile: bool = True):
+    """Decode steps at a fixed position (the new token at position ctx; each step rewrites the same
+    cache slot with the same values): wall time per step and per-kernel HIP-event durations."""
+    import torch
+    from sparse_moe_query_amd import gqe
+    from sparse_moe_query_amd.inputs import WORKLOADS, gqa_of
+    from sparse_moe_query_amd.runner import build_layer
+    base, batch, ctx = DECODE_WORKLOADS[name]
+    wl = WORKLOADS[base].with_(name=name, batch=batch, seq=1)
+    if gqa:
+        wl = gqa_of(wl)
+    layer, x, _ = build_layer(wl)          # x [batch, 1, d]: the new tokens
+    x = x.reshape(batch, wl.dim)
+    kc, vc = layer.kv_cache(batch, ctx + 64)
+    gen = torch.Generator(device=x.device)
+    gen.manual_seed(1234)
+    kc.normal_(0.0, KV_STD, generator=gen)
+    vc.normal_(0.0, KV_STD, generator=gen)
+    pos = torch.full((batch,), ctx, dtype=torch.int32, device=x.device)
+    y = torch.empty_like(x)
+    for _ in range(warmup):
+        layer.decode(x, pos, kc, vc, y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.decode(x, pos, kc, vc, y)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    kern, n = {}, 0
+    if profile:
+        gqe.gqe_profile_enable(layer.h, True)
+        for _ in range(steps):
+            layer.decode(x, pos, kc, vc, y)
+        torch.cuda.synchronize()
+        kern, n = gqe.gqe_profile_read_kernels(layer.h)
+        gqe.gqe_profile_enable(layer.h, False)
+    kernel_ms = {k: v / max(n, 1) for k, v in kern.items() if v > 0}
+    assert torch.isfinite(y.float()).all(), "decode produced non-finite outputs"
+    layer.close()
+    del layer, x, y, kc, vc
+    torch.cuda.empty_cache()
+    return wl, batch, ctx, ms, kernel_ms
+
+
+def decode_report(steps: int, warmup: int) -> dict:
+    name = "decode_b64_ctx8192"
+    log(f"[bench] {name}")
+    wl, batch, ctx, ms, km = run_decode(name, steps, warmup)
+    log(f"[bench] {name} gqa")
+    _, _, _, g_ms, g_km = run_decode(name, steps, warmup, gqa=True)
+    a = decode_algorithmic(wl, batch, ctx)
+    att = km.get("decode_attention", 0.0) + km.get("decode_merge", 0.0)
+    g_att = g_km.get("decode_attention", 0.0) + g_km.get("decode_merge", 0.0)
+    gbs = a["attention_bytes"] / (att * 1e-3) / 1e9
+    log(f"[bench] {name}: {ms:.3f} ms/step (GQA {g_ms:.3f}), attention {gbs:.0f} GB/s; kernels {km}")
+    return dict(workload=name, batch=batch, cached_positions=ctx, ms_per_step=ms,
+                tokens_s=batch / (ms / 1e3), kernel_ms=km,
+                roofline=dict(bound="hbm", kernel="decode_attention", achieved=gbs, peak=PEAK_HBM,
+                              unit="GB/s", frac=gbs / PEAK_HBM, kernel_ms=km.get("decode_attention", 0.0),
+                              merge_ms=km.get("decode_merge", 0.0), algorithmic_bytes=a["attention_bytes"]),
+                gqa_ms_per_step=g_ms, gqa_kernel_ms=g_km, speedup_layer=g_ms / ms,
+                speedup_attention=g_att / att if att > 0 else None)
+
+
 def cpu_baseline(wl, min_seconds=10.0):
     """The oracle as it stands, on whole sequences of the workload (all of their tokens), repeated
     over the batch until at least ``min_seconds`` of CPU work have been timed."""
@@ -196,6 +274,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="main workload only (for profilers)")
     ap.add_argument("--profile-workload", default=None,
                     help="run only this named workload (inputs.WORKLOADS, or NAME_gqa for its "
@@ -215,6 +294,13 @@ def main():
     from sparse_moe_query_amd.inputs import WORKLOADS, gqa_of
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.profile_workload in DECODE_WORKLOADS or (args.profile_workload or "")[:-4] in DECODE_WORKLOADS:
+        name = args.profile_workload
+        gqa = name.endswith("_gqa")
+        wl, _, _, ms, kernel_ms = run_decode(name[:-4] if gqa else name, args.steps, args.warmup, gqa=gqa)
+        print(json.dumps({"workload": wl.name, "ms_per_step": ms, "kernel_ms": kernel_ms,
+                          "source_hash": source_hash("k_decode.hip")}), flush=True)
+        return
     if args.profile_workload:
         name = args.profile_workload
         wl = gqa_of(WORKLOADS[name[:-4]]) if name.endswith("_gqa") else WORKLOADS[name]
@@ -286,6 +372,8 @@ def main():
                               speedup_attention=attn_step_ms(g_kern) / attn_step_ms(l_kern))
             log(f"[bench] {name}: {l_ms:.3f} ms (GQA {g_ms:.3f} ms) attn {at:.0f} TFLOP/s")
         result["long_context"] = long
+    if not args.no_decode and not args.only_main:
+        result["decode"] = decode_report(max(10, args.steps), args.warmup)
     if not args.no_cpu and not args.only_main:
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(main_wl)

@@ -208,19 +208,71 @@ int gqe_bucket(gqe_handle_t* h, void* stream, int32_t* offs, int32_t* perm, int3
 int gqe_attention_schedule(const gqe_handle_t* h, int64_t batch, int64_t seq, int32_t* jobs,
                            int64_t max_jobs, int32_t* merges, int64_t max_merges, int64_t counts[4]);
 
-/* Kernel timing for measurement.  While enabled, gqe_forward records a HIP event on its stream
- * right before and right after each kernel it launches; a kernel's duration is the time between
- * the two.  Kernel slots, in launch order:
+/* ------------------------------------------------------------------ decode with a dense KV cache
+ * GQE README "Algorithm Overview" and the gist.science explainer ("Architecture and Routing",
+ * "Dense KV Path"): the KV projections and the KV cache stay dense and unchanged; only the
+ * query-head computation is routed.  A decode step takes one new token per sequence; its output
+ * is row p of the causal forward pass over positions 0..p of that sequence, where p is the
+ * token's position and positions 0..p-1 are read from the cache.
+ *
+ * Cache: kcache and vcache, each [cache_batch, G, s_max, d_h] in cfg.dtype, row-major, device,
+ * caller-owned, 16-byte aligned, not overlapping; head g of sequence b at position s is the d_h
+ * vector at [b, g, s, :] (the keys and values the forward pass computes: x @ W_k / x @ W_v,
+ * columns g*d_h ..).  Sequence b of a decode batch uses cache row b.
+ *
+ * Supported: d_h * element size a multiple of 16 bytes and d_h <= 128; at most 8 active query
+ * heads per KV group (top_k + shared head, or N/G for dense_gqa); at most 192 output slots and
+ * 8192 slot x head-dim values per token.  Otherwise GQE_ERR_UNSUPPORTED. */
+
+/* Copies the keys and values of every token of the last gqe_forward on this handle (batch B, seq S)
+ * into cache rows b0 .. b0+B-1, positions 0 .. S-1 (the prefill of the cache).  Reads the last
+ * forward's workspace, which must be unchanged.  Requires S <= s_max and b0 + B <= cache_batch.
+ * Enqueued on `stream`.  Errors: GQE_ERR_NULL_POINTER, GQE_ERR_STATE (no forward yet),
+ * GQE_ERR_MISALIGNED, GQE_ERR_SHAPE, GQE_ERR_INVALID_CONFIG (caches overlap), GQE_ERR_HIP. */
+int gqe_kv_export(gqe_handle_t* h, void* stream, void* kcache, void* vcache, int64_t cache_batch,
+                  int64_t s_max, int64_t b0);
+
+/* Bytes of scratch that gqe_decode needs for `batch` sequences with caches of s_max positions
+ * (routing of the new tokens, float32 queries, per-chunk partial attention results, merged head
+ * outputs).  1 <= batch <= 2^20, 1 <= s_max <= 2^28.  Host only.  Errors: GQE_ERR_NULL_POINTER,
+ * GQE_ERR_SHAPE, GQE_ERR_UNSUPPORTED. */
+int gqe_decode_workspace_bytes(const gqe_handle_t* h, int64_t batch, int64_t s_max, size_t* bytes);
+
+/* One decode step.
+ *  x          [batch, d] device, cfg.dtype: the new token of every sequence; not aliased with y.
+ *  y          [batch, d] device, cfg.dtype (written): the layer output of those tokens.
+ *  pos        [batch] device int32: position of sequence b's new token = number of its tokens
+ *             already in the cache.  The token's key and value are written to the cache at
+ *             [b, g, pos[b], :], then it attends to cache positions 0 .. pos[b].  A position
+ *             outside [0, s_max) is not processed: no cache write, and y[b, :] is NaN.
+ *  kcache, vcache  the cache, [batch, G, s_max, d_h] (see above).
+ *  workspace  device, >= gqe_decode_workspace_bytes(batch, s_max), 256-byte aligned.
+ *  route_idx, route_w  optional [batch, G, k] routing outputs as in gqe_forward (NULL to skip).
+ * Enqueues its kernels on `stream` and returns.  Requires gqe_pack_weights first (the router
+ * reads the packed weights); the other weights are read in their gqe_init layouts, so the pointers
+ * given to gqe_init must stay valid.  Does not change the statistics read by gqe_aux_stats.
+ * Errors: NULL/misaligned pointers, GQE_ERR_SHAPE, GQE_ERR_UNSUPPORTED, GQE_ERR_WORKSPACE,
+ * GQE_ERR_STATE, GQE_ERR_INVALID_CONFIG (aliasing), GQE_ERR_HIP. */
+int gqe_decode(gqe_handle_t* h, const void* x, void* y, int64_t batch, const int32_t* pos,
+               void* kcache, void* vcache, int64_t s_max, void* workspace, size_t ws_bytes,
+               void* stream, int32_t* route_idx, float* route_w);
+
+/* Kernel timing for measurement.  While enabled, gqe_forward and gqe_decode record a HIP event on
+ * their stream right before and right after each kernel they launch; a kernel's duration is the
+ * time between the two.  Kernel slots, in launch order:
  *   0 router (logits, softmax, top-k, weights, per-block statistics)   1 router statistics
  *   2 projections (routed + shared Q, K, V)                              3 key norms (only when the
  *   projections run on the scalar path and attention on matrix cores)   4 attention preparation
- *   5 attention                                                          6 combine + output projection
+ *   5 attention                                                          6 attention merge
+ *   7 combine + output projection
+ * and of gqe_decode (slot 0 is its router):
+ *   8 decode projections    9 decode attention    10 decode merge    11 decode combine
  * gqe_profile_read_kernels waits for the recorded events, returns the summed milliseconds per
  * kernel slot (0 for slots not launched) and the number of forwards they cover, and starts a new
  * accumulation.  gqe_profile_read does the same summed per stage (0 router = slots 0+1,
- * 1 projections = 2+3, 2 attention = 4+5+6, 3 combine = 7).  Not re-entrant; errors as
+ * 1 projections = 2+3+8, 2 attention = 4+5+6+9+10, 3 combine = 7+11).  Not re-entrant; errors as
  * GQE_ERR_NULL_POINTER / GQE_ERR_HIP. */
-#define GQE_PROF_KERNELS 8
+#define GQE_PROF_KERNELS 12
 int gqe_profile_enable(gqe_handle_t* h, int enable);
 int gqe_profile_read(gqe_handle_t* h, double stage_ms[4], int64_t* forwards);
 int gqe_profile_read_kernels(gqe_handle_t* h, double kernel_ms[GQE_PROF_KERNELS], int64_t* forwards);

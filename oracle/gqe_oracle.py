@@ -218,3 +218,33 @@ def forward(cfg: OracleConfig, B: int, S: int, x, w: dict, rows_list=None, want_
         out["y"] = res
     out["rows"] = np.asarray(rows_list)
     return out
+
+
+def decode(cfg: OracleConfig, x_hist, w: dict, pos, idx_new=None) -> dict:
+    """One decode step with a dense KV cache (README "Algorithm Overview": the KV heads stay dense
+    and unchanged, so GQA's KV cache is kept; explainer "Architecture and Routing", "Dense KV
+    Path").  The new token of sequence b sits at position pos[b] after the cached positions
+    0 .. pos[b]-1 of x_hist[b]; the cache holds exactly their keys and values, so the token's
+    output is row pos[b] of the causal forward pass over x_hist[b, :pos[b]+1].  That is how it is
+    computed here (no cache of its own: the definition, written out).
+
+    x_hist [B, >= max(pos)+1, d]; idx_new optional [B, G, k] routing of the new tokens that replaces
+    the oracle's (only where a decision is near-tied).  Returns y [B, d] and the new tokens'
+    logits, p, idx, w, gap."""
+    x_hist = np.asarray(x_hist)
+    B = x_hist.shape[0]
+    G, k = cfg.num_kv_heads, cfg.top_k
+    out = dict(y=np.zeros((B, cfg.dim)), logits=np.zeros((B, cfg.num_query_experts)),
+               p=np.zeros((B, cfg.num_query_experts)), idx=np.zeros((B, G, k), np.int32),
+               w=np.zeros((B, G, k)), gap=np.zeros((B, G)))
+    for b, p in enumerate(int(v) for v in pos):
+        xs = _f64(x_hist[b, :p + 1]).reshape(p + 1, cfg.dim)
+        override = None
+        if idx_new is not None:
+            override = router(cfg, xs, w["w_router"], w.get("b_router"))["idx"]
+            override[p] = np.asarray(idx_new)[b]
+        r = forward(cfg, 1, p + 1, xs, w, rows_list=[p], idx_override=override)
+        out["y"][b] = r["y"][0]
+        for key in ("logits", "p", "idx", "w", "gap"):
+            out[key][b] = r[key][p]
+    return out

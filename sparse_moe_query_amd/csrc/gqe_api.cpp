@@ -67,6 +67,60 @@ WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S, int64_t attn_slots) {
     return P;
 }
 
+// Decode workspace: the router's buffers for the B new tokens, then the float32 queries, chunk
+// partials and merged head outputs.
+static DecodePlan make_decode_plan(const GqeDims& D, int64_t B, int64_t s_max) {
+    DecodePlan P{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    WorkPlan& r = P.r;
+    r.B = B;
+    r.S = 1;
+    r.T = B;
+    r.S_pad = GQE_KV_TILE;
+    r.nblk_router = ceil_div(B, 64);
+    const size_t gk = (size_t)B * D.G * D.k;
+    r.idx = take(gk * 4);
+    r.wsel = take(gk * 4);
+    r.psel = take(gk * 4);
+    r.part_cnt = take((size_t)r.nblk_router * D.N * 4);
+    r.part_psum = take((size_t)r.nblk_router * D.N * 8);
+    r.stats = take((size_t)D.N * 16 + 64);
+    P.B = B;
+    P.s_max = s_max;
+    P.C = decode_chunk(D);
+    P.NC = ceil_div(s_max, P.C);
+    P.MH = (D.dense ? D.n : D.k) + D.s;
+    P.qd = take((size_t)B * D.H * D.dh * 4);
+    P.part = take((size_t)B * D.G * P.NC * P.MH * (D.dh + 2) * 4);
+    P.od = take((size_t)B * D.H * D.dh * 4);
+    P.total = off;
+    r.total = off;
+    return P;
+}
+
+// Shapes the decode kernels handle: 16-byte cache rows, d_h <= 128, a bounded number of active
+// heads per group and of output slots per token.
+static int decode_supported(const GqeDims& D) {
+    const int es = D.dtype == GQE_DTYPE_BF16 ? 2 : 4;
+    if ((D.dh * es) % 16 != 0 || D.dh > 128)
+        return fail(GQE_ERR_UNSUPPORTED, "decode needs head_dim * element size to be a multiple of 16 bytes and head_dim <= 128");
+    const int mh = (D.dense ? D.n : D.k) + D.s;
+    if (mh > GQE_DEC_MAX_HEADS) return fail(GQE_ERR_UNSUPPORTED, "decode handles at most %d active heads per group", GQE_DEC_MAX_HEADS);
+    const int slots = D.G * (D.dense ? D.n : D.k) + ((!D.dense && D.variant == GQE_VARIANT_GQE) ? D.G : 0) + D.s;
+    if (slots > GQE_DEC_MAX_SLOTS || slots * D.dh > GQE_DEC_MAX_SLOT_DIMS)
+        return fail(GQE_ERR_UNSUPPORTED, "decode handles at most %d output slots x head dims per token", GQE_DEC_MAX_SLOT_DIMS);
+    return GQE_OK;
+}
+
+static bool decode_shape_ok(int64_t batch, int64_t s_max) {
+    return batch >= 1 && batch <= ((int64_t)1 << 20) && s_max >= 1 && s_max <= ((int64_t)1 << 28);
+}
+
 PackedLayout make_packed_layout(const GqeDims& D, bool mfma) {
     PackedLayout L;
     size_t off = 0;
@@ -148,6 +202,25 @@ static int attn_schedule(gqe_handle* h, int64_t B, int64_t S, const AttnSchedDev
     }
     h->sched.push_back(d);
     *out = &h->sched.back();
+    return GQE_OK;
+}
+
+// Events of the next recorded call while kernel timing is on (gqe_profile_enable).
+static int prof_marks(gqe_handle* h, hipStream_t st, KernelMarks* marks) {
+    hipError_t e = hipSuccess;
+    const size_t need = (h->prof_used + 1) * (2 * KT_COUNT);
+    while (h->prof_ev.size() < need && e == hipSuccess) {
+        hipEvent_t x0;
+        e = hipEventCreate(&x0);
+        if (e == hipSuccess) h->prof_ev.push_back(x0);
+    }
+    if (e != hipSuccess) return fail(GQE_ERR_HIP, "event creation failed: %s", hipGetErrorString(e));
+    if (h->prof_mask.size() < h->prof_used + 1) h->prof_mask.resize(h->prof_used + 1);
+    marks->ev = &h->prof_ev[h->prof_used * (2 * KT_COUNT)];
+    marks->mask = &h->prof_mask[h->prof_used];
+    *marks->mask = 0;
+    marks->st = st;
+    h->prof_used += 1;
     return GQE_OK;
 }
 
@@ -297,19 +370,8 @@ int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t 
     KernelMarks marks;
     KernelMarks* km = nullptr;
     if (h->prof) {
-        const size_t need = (h->prof_used + 1) * (2 * KT_COUNT);
-        while (h->prof_ev.size() < need && e == hipSuccess) {
-            hipEvent_t x0;
-            e = hipEventCreate(&x0);
-            if (e == hipSuccess) h->prof_ev.push_back(x0);
-        }
-        if (e != hipSuccess) return fail(GQE_ERR_HIP, "event creation failed: %s", hipGetErrorString(e));
-        if (h->prof_mask.size() < h->prof_used + 1) h->prof_mask.resize(h->prof_used + 1);
-        marks.ev = &h->prof_ev[h->prof_used * (2 * KT_COUNT)];
-        marks.mask = &h->prof_mask[h->prof_used];
-        *marks.mask = 0;
-        marks.st = st;
-        h->prof_used += 1;
+        const int rc = prof_marks(h, st, &marks);
+        if (rc != GQE_OK) return rc;
         km = &marks;
     }
     // with the matrix-core projection, its last work group finalizes the router statistics and
@@ -404,6 +466,78 @@ int gqe_attention_schedule(const gqe_handle_t* h, int64_t batch, int64_t seq, in
     return ok();
 }
 
+int gqe_kv_export(gqe_handle_t* h, void* stream, void* kcache, void* vcache, int64_t cache_batch, int64_t s_max,
+                  int64_t b0) {
+    if (!h || !kcache || !vcache) return fail(GQE_ERR_NULL_POINTER, "handle, kcache and vcache must be non-NULL");
+    if (!h->ran) return fail(GQE_ERR_STATE, "no forward has run on this handle");
+    if (misaligned(kcache, 16) || misaligned(vcache, 16)) return fail(GQE_ERR_MISALIGNED, "caches must be 16-byte aligned");
+    const WorkPlan& P = h->last_plan;
+    if (!decode_shape_ok(cache_batch, s_max) || b0 < 0 || b0 + P.B > cache_batch || P.S > s_max)
+        return fail(GQE_ERR_SHAPE, "the last forward [%lld x %lld] does not fit cache rows %lld.. of [%lld x %lld]",
+                    (long long)P.B, (long long)P.S, (long long)b0, (long long)cache_batch, (long long)s_max);
+    if (h->D.dh > 128) return fail(GQE_ERR_UNSUPPORTED, "head_dim > 128");
+    const size_t cbytes = (size_t)cache_batch * h->D.G * s_max * h->D.dh * (h->D.dtype == GQE_DTYPE_BF16 ? 2 : 4);
+    const char* kb = (const char*)kcache;
+    const char* vb = (const char*)vcache;
+    if (kb < vb + cbytes && vb < kb + cbytes) return fail(GQE_ERR_INVALID_CONFIG, "kcache and vcache must not overlap");
+    const hipError_t e = launch_kv_export(h->D, P, (const char*)h->last_ws, kcache, vcache, s_max, b0, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GQE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int gqe_decode_workspace_bytes(const gqe_handle_t* h, int64_t batch, int64_t s_max, size_t* bytes) {
+    if (!h || !bytes) return fail(GQE_ERR_NULL_POINTER, "handle and bytes must be non-NULL");
+    if (!decode_shape_ok(batch, s_max)) return fail(GQE_ERR_SHAPE, "batch must be in [1, 2^20] and s_max in [1, 2^28]");
+    const int rc = decode_supported(h->D);
+    if (rc != GQE_OK) return rc;
+    *bytes = make_decode_plan(h->D, batch, s_max).total;
+    return ok();
+}
+
+int gqe_decode(gqe_handle_t* h, const void* x, void* y, int64_t batch, const int32_t* pos, void* kcache,
+               void* vcache, int64_t s_max, void* workspace, size_t ws_bytes, void* stream, int32_t* route_idx,
+               float* route_w) {
+    if (!h || !x || !y || !pos || !kcache || !vcache || !workspace)
+        return fail(GQE_ERR_NULL_POINTER, "handle, x, y, pos, kcache, vcache and workspace must be non-NULL");
+    if (!h->packed) return fail(GQE_ERR_STATE, "gqe_pack_weights must run before gqe_decode");
+    if (!decode_shape_ok(batch, s_max)) return fail(GQE_ERR_SHAPE, "batch must be in [1, 2^20] and s_max in [1, 2^28]");
+    const int rc = decode_supported(h->D);
+    if (rc != GQE_OK) return rc;
+    if (misaligned(x, 16) || misaligned(y, 16) || misaligned(kcache, 16) || misaligned(vcache, 16))
+        return fail(GQE_ERR_MISALIGNED, "x, y, kcache and vcache must be 16-byte aligned");
+    if (misaligned(pos, 4)) return fail(GQE_ERR_MISALIGNED, "pos must be 4-byte aligned");
+    if (misaligned(workspace, 256)) return fail(GQE_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    if ((route_idx && misaligned(route_idx, 4)) || (route_w && misaligned(route_w, 4)))
+        return fail(GQE_ERR_MISALIGNED, "routing outputs must be 4-byte aligned");
+    const GqeDims& D = h->D;
+    const size_t es = D.dtype == GQE_DTYPE_BF16 ? 2 : 4;
+    const size_t xbytes = (size_t)batch * D.d * es;
+    const char* xb = (const char*)x;
+    const char* yb = (const char*)y;
+    if (xb < yb + xbytes && yb < xb + xbytes) return fail(GQE_ERR_INVALID_CONFIG, "x and y must not alias");
+    const size_t cbytes = (size_t)batch * D.G * s_max * D.dh * es;
+    const char* kb = (const char*)kcache;
+    const char* vb = (const char*)vcache;
+    if (kb < vb + cbytes && vb < kb + cbytes) return fail(GQE_ERR_INVALID_CONFIG, "kcache and vcache must not overlap");
+    const DecodePlan P = make_decode_plan(D, batch, s_max);
+    if (ws_bytes < P.total) return fail(GQE_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, P.total);
+    hipStream_t st = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    KernelMarks marks;
+    KernelMarks* km = nullptr;
+    hipError_t e = hipSuccess;
+    if (h->prof) {
+        const int rc = prof_marks(h, st, &marks);
+        if (rc != GQE_OK) return rc;
+        km = &marks;
+    }
+    if (!D.dense) e = launch_router(D, P.r, x, h->packed, h->pl, ws, route_idx, route_w, st, km, false);
+    if (e == hipSuccess) e = launch_decode(D, P, h->w, x, y, pos, kcache, vcache, ws, st, km);
+    if (e == hipSuccess && km && marks.err != hipSuccess) e = marks.err;
+    if (e != hipSuccess) return fail(GQE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int gqe_profile_enable(gqe_handle_t* h, int enable) {
     if (!h) return fail(GQE_ERR_NULL_POINTER, "handle must be non-NULL");
     h->prof = enable != 0;
@@ -438,9 +572,9 @@ int gqe_profile_read(gqe_handle_t* h, double stage_ms[4], int64_t* forwards) {
     const int rc = gqe_profile_read_kernels(h, k, forwards);
     if (rc != GQE_OK) return rc;
     stage_ms[0] = k[KT_ROUTER] + k[KT_ROUTER_STATS];
-    stage_ms[1] = k[KT_PROJ] + k[KT_KEYNORM];
-    stage_ms[2] = k[KT_ATTN_PREP] + k[KT_ATTN] + k[KT_ATTN_MERGE];
-    stage_ms[3] = k[KT_COMBINE];
+    stage_ms[1] = k[KT_PROJ] + k[KT_KEYNORM] + k[KT_DEC_PROJ];
+    stage_ms[2] = k[KT_ATTN_PREP] + k[KT_ATTN] + k[KT_ATTN_MERGE] + k[KT_DEC_ATTN] + k[KT_DEC_MERGE];
+    stage_ms[3] = k[KT_COMBINE] + k[KT_DEC_COMBINE];
     return ok();
 }
 

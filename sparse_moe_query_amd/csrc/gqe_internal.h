@@ -11,6 +11,9 @@
 
 #define GQE_ATTN_COLS 256        // query columns (position, head) of one attention work item
 #define GQE_ATTN_MAX_CHUNKS 32   // key-range chunks an attention item may be split into
+#define GQE_DEC_MAX_HEADS 8      // decode: active query heads of one KV group
+#define GQE_DEC_MAX_SLOTS 192    // decode: output-projection slots of one token
+#define GQE_DEC_MAX_SLOT_DIMS 8192  // decode: slots x d_h of one token
 
 struct GqeDims {
     int d, N, G, k, n, dh, H, s;  // s = shared head on; H = active heads per token
@@ -43,6 +46,16 @@ struct WorkPlan {
     size_t knt;                       // per-64-key-tile maximum norm [B][G][S_pad/64] f32
     size_t part_o, part_ml;           // attention partials [nslots][256][d_h] / [nslots][256][2] f32
     int64_t nslots;
+    size_t total;
+};
+
+// Byte offsets into the caller's workspace for one decode step of B sequences with caches of
+// s_max positions.
+struct DecodePlan {
+    WorkPlan r;                       // routing buffers of the B new tokens (idx, wsel, psel, partials)
+    int64_t B, s_max, NC;             // NC = key chunks per cache row
+    int C, MH;                        // keys per chunk, largest active head count of a group
+    size_t qd, part, od;              // queries [B][H][dh], chunk partials [B][G][NC][MH][dh+2], O [B][H][dh] (f32)
     size_t total;
 };
 
@@ -96,7 +109,10 @@ struct gqe_handle {
 };
 
 // Kernel timing slots, in launch order (GQE_PROF_KERNELS in gqe.h).
-enum { KT_ROUTER = 0, KT_ROUTER_STATS, KT_PROJ, KT_KEYNORM, KT_ATTN_PREP, KT_ATTN, KT_ATTN_MERGE, KT_COMBINE, KT_COUNT };
+enum {
+    KT_ROUTER = 0, KT_ROUTER_STATS, KT_PROJ, KT_KEYNORM, KT_ATTN_PREP, KT_ATTN, KT_ATTN_MERGE, KT_COMBINE,
+    KT_DEC_PROJ, KT_DEC_ATTN, KT_DEC_MERGE, KT_DEC_COMBINE, KT_COUNT
+};
 
 // Records events on the stream right before and right after each kernel a launcher enqueues
 // (when timing is on).
@@ -136,6 +152,11 @@ hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x,
                             hipStream_t st, KernelMarks* km);
 hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, const AttnSchedDev& sc, char* ws, hipStream_t st,
                             KernelMarks* km, bool prep);
+int decode_chunk(const GqeDims& D);
+hipError_t launch_kv_export(const GqeDims& D, const WorkPlan& P, const char* ws, void* kc, void* vc, int64_t s_max,
+                            int64_t b0, hipStream_t st);
+hipError_t launch_decode(const GqeDims& D, const DecodePlan& P, const gqe_weights_t& w, const void* x, void* y,
+                         const int32_t* pos, void* kc, void* vc, char* ws, hipStream_t st, KernelMarks* km);
 hipError_t launch_bucket(const GqeDims& D, const WorkPlan& P, char* ws, int32_t* offs, int32_t* perm, int32_t* inv,
                          hipStream_t st);
 bool combine_mfma_supported(const GqeDims& D);

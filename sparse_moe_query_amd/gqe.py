@@ -25,12 +25,12 @@ ERRORS = {0: "GQE_OK", -1: "GQE_ERR_INVALID_CONFIG", -2: "GQE_ERR_NULL_POINTER",
           -6: "GQE_ERR_SHAPE", -7: "GQE_ERR_HIP", -8: "GQE_ERR_STATE"}
 EXPORTS = ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights", "gqe_workspace_bytes",
            "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_bucket", "gqe_profile_enable",
-           "gqe_profile_read", "gqe_profile_read_kernels", "gqe_attention_schedule", "gqe_destroy",
-           "gqe_last_error")
+           "gqe_profile_read", "gqe_profile_read_kernels", "gqe_attention_schedule", "gqe_kv_export",
+           "gqe_decode_workspace_bytes", "gqe_decode", "gqe_destroy", "gqe_last_error")
 STAGES = ("router", "projection", "attention", "combine")
 # kernel timing slots of gqe_profile_read_kernels, in launch order
 KERNELS = ("router", "router_stats", "projection", "key_norms", "attention_prep", "attention", "attention_merge",
-           "combine")
+           "combine", "decode_projection", "decode_attention", "decode_merge", "decode_combine")
 
 
 class GqeError(RuntimeError):
@@ -75,6 +75,9 @@ def lib():
         L.gqe_profile_read.argtypes = [P, P, P]
         L.gqe_profile_read_kernels.argtypes = [P, P, P]
         L.gqe_attention_schedule.argtypes = [P, I64, I64, P, I64, P, I64, P]
+        L.gqe_kv_export.argtypes = [P, P, P, P, I64, I64, I64]
+        L.gqe_decode_workspace_bytes.argtypes = [P, I64, I64, ctypes.POINTER(SZ)]
+        L.gqe_decode.argtypes = [P, P, P, I64, P, P, P, I64, P, SZ, P, P, P]
         L.gqe_destroy.argtypes = [P]
         L.gqe_destroy.restype = None
         L.gqe_last_error.argtypes = []
@@ -82,7 +85,7 @@ def lib():
         for f in ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights",
                   "gqe_workspace_bytes", "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_bucket",
                   "gqe_profile_enable", "gqe_profile_read", "gqe_profile_read_kernels",
-                  "gqe_attention_schedule"):
+                  "gqe_attention_schedule", "gqe_kv_export", "gqe_decode_workspace_bytes", "gqe_decode"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -192,6 +195,25 @@ def gqe_attention_schedule(h, batch: int, seq: int):
     return jobs[:counts[0]], merges[:counts[1]], int(counts[2]), int(counts[3])
 
 
+def gqe_kv_export(h, kcache: torch.Tensor, vcache: torch.Tensor, b0: int = 0, stream=None):
+    """Keys and values of the last forward -> cache rows b0 .. b0+B-1 ([rows, G, s_max, d_h])."""
+    _check(lib().gqe_kv_export(h, _stream(stream), _ptr(kcache), _ptr(vcache), kcache.shape[0],
+                               kcache.shape[2], b0))
+
+
+def gqe_decode_workspace_bytes(h, batch: int, s_max: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().gqe_decode_workspace_bytes(h, batch, s_max, ctypes.byref(n)))
+    return n.value
+
+
+def gqe_decode(h, x: torch.Tensor, y: torch.Tensor, pos: torch.Tensor, kcache: torch.Tensor,
+               vcache: torch.Tensor, workspace: torch.Tensor, stream=None, route_idx=None, route_w=None):
+    _check(lib().gqe_decode(h, _ptr(x), _ptr(y), x.shape[0], _ptr(pos), _ptr(kcache), _ptr(vcache),
+                            kcache.shape[2], _ptr(workspace), workspace.numel() * workspace.element_size(),
+                            _stream(stream), _ptr(route_idx), _ptr(route_w)))
+
+
 def gqe_destroy(h):
     if h:
         lib().gqe_destroy(h)
@@ -229,6 +251,8 @@ class GQEAttention:
         gqe_pack_weights(self.h, self.packed, stream)
         self._ws = None
         self._ws_shape = None
+        self._dws = None
+        self.dh = int(head_dim or dim // num_query_experts)
 
     def workspace(self, batch: int, seq: int) -> torch.Tensor:
         nbytes = gqe_workspace_bytes(self.h, batch, seq)
@@ -249,6 +273,48 @@ class GQEAttention:
 
     def aux_stats(self, stream=None) -> dict:
         return gqe_aux_stats(self.h, self.N, stream)
+
+    # ---- decode with a dense KV cache
+    def kv_cache(self, batch: int, s_max: int):
+        """Empty K and V caches [batch, G, s_max, d_h] of the layer's dtype."""
+        shape = (batch, self.G, s_max, self.dh)
+        td = TORCH_DTYPES[self.dtype]
+        return (torch.empty(shape, dtype=td, device=self.device),
+                torch.empty(shape, dtype=td, device=self.device))
+
+    def export_kv(self, kcache: torch.Tensor, vcache: torch.Tensor, b0: int = 0, stream=None):
+        """Writes the keys and values of the last forward into cache rows b0 .. b0+B-1."""
+        self._check_cache(kcache, vcache)
+        gqe_kv_export(self.h, kcache, vcache, b0, stream)
+
+    def decode(self, x: torch.Tensor, pos: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+               y: torch.Tensor | None = None, stream=None, route_idx=None, route_w=None) -> torch.Tensor:
+        """One decode step: x [B, dim] (new token of every sequence), pos [B] int32 on the device
+        (its position = tokens already cached); appends its K/V to the caches and returns y [B, dim]."""
+        B, d = x.shape
+        if d != self.dim or x.dtype != TORCH_DTYPES[self.dtype] or not x.is_contiguous():
+            raise ValueError("x must be a contiguous [B, dim] tensor of the layer's dtype")
+        if pos.dtype != torch.int32 or pos.shape != (B,) or not pos.is_contiguous():
+            raise ValueError("pos must be a contiguous int32 tensor [B]")
+        self._check_cache(kcache, vcache)
+        if kcache.shape[0] < B:
+            raise ValueError("the caches have fewer rows than the batch")
+        if y is None:
+            y = torch.empty_like(x)
+        nbytes = gqe_decode_workspace_bytes(self.h, B, kcache.shape[2])
+        if self._dws is None or self._dws.numel() < nbytes:
+            self._dws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        gqe_decode(self.h, x, y, pos, kcache, vcache, self._dws, stream, route_idx, route_w)
+        return y
+
+    def _check_cache(self, kcache, vcache):
+        td = TORCH_DTYPES[self.dtype]
+        for c in (kcache, vcache):
+            if (c.dim() != 4 or c.shape[1] != self.G or c.shape[3] != self.dh or c.dtype != td
+                    or not c.is_contiguous()):
+                raise ValueError("caches must be contiguous [rows, G, s_max, d_h] tensors of the layer's dtype")
+        if kcache.shape != vcache.shape:
+            raise ValueError("kcache and vcache must have the same shape")
 
     def bucket(self, batch: int, seq: int, stream=None) -> dict:
         """Global token-to-expert bucketing of the last forward (device int32 tensors)."""

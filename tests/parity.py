@@ -73,6 +73,33 @@ def within_rounding(got, ref, dtype: str) -> bool:
     return bool(np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-3 * rms))
 
 
+def check_routing(cfg, r: dict, gpu_idx, gpu_w):
+    """Routing of T tokens against the oracle's (``r`` = go.router output): indices bit-exact and
+    weights within float32 rounding, except near-tied decisions, where the GPU's choice is taken.
+    Returns (idx to use for the oracle's outputs, number of near-tied decisions that differ)."""
+    G, k = cfg.num_kv_heads, cfg.top_k
+    n = cfg.num_query_experts // G
+    T = r["idx"].shape[0]
+    diff = np.any(np.sort(gpu_idx, axis=2) != np.sort(r["idx"], axis=2), axis=2)  # [T,G]
+    order_diff = np.any(gpu_idx != r["idx"], axis=2)
+    # a decision is near-tied when any two adjacent logits among the top min(k+1, n) of
+    # the group are closer than NEAR_TIE (this covers the k-th/(k+1)-th gap and the rank
+    # order inside the selection)
+    srt = -np.sort(-r["logits"].reshape(T, G, n), axis=2)[:, :, :min(k + 1, n)]
+    near = (np.min(srt[:, :, :-1] - srt[:, :, 1:], axis=2, initial=np.inf) < NEAR_TIE) \
+        if srt.shape[2] > 1 else np.zeros((T, G), bool)
+    bad = (diff | order_diff) & ~near
+    assert not bad.any(), (f"{int(bad.sum())} routing decisions differ with gap >= {NEAR_TIE}; "
+                           f"first at {np.argwhere(bad)[:5].tolist()}")
+    idx_used = r["idx"].copy()
+    tie_pairs = np.argwhere(diff | order_diff)
+    for t, g in tie_pairs:
+        idx_used[t, g] = gpu_idx[t, g]
+    same = ~(diff | order_diff)
+    np.testing.assert_allclose(gpu_w[same], r["w"][same], rtol=2e-6, atol=1e-7)
+    return idx_used, int(len(tie_pairs))
+
+
 def compare(wl, gpu: dict, inputs: dict, rows=None, want_qo=False) -> dict:
     """Check a GPU forward (run_layer output) against the oracle; returns a report and raises
     AssertionError on any violation."""
@@ -89,24 +116,7 @@ def compare(wl, gpu: dict, inputs: dict, rows=None, want_qo=False) -> dict:
         assert np.all(gpu["counts"] == T)
     else:
         r = go.router(cfg, x64, inputs["w_router"], inputs["b_router"])
-        diff = np.any(np.sort(gpu["idx"], axis=2) != np.sort(r["idx"], axis=2), axis=2)  # [T,G]
-        order_diff = np.any(gpu["idx"] != r["idx"], axis=2)
-        # a decision is near-tied when any two adjacent logits among the top min(k+1, n) of
-        # the group are closer than NEAR_TIE (this covers the k-th/(k+1)-th gap and the rank
-        # order inside the selection)
-        srt = -np.sort(-r["logits"].reshape(T, G, n), axis=2)[:, :, :min(k + 1, n)]
-        near = (np.min(srt[:, :, :-1] - srt[:, :, 1:], axis=2, initial=np.inf) < NEAR_TIE) \
-            if srt.shape[2] > 1 else np.zeros((T, G), bool)
-        bad = (diff | order_diff) & ~near
-        assert not bad.any(), (f"{int(bad.sum())} routing decisions differ with gap >= {NEAR_TIE}; "
-                               f"first at {np.argwhere(bad)[:5].tolist()}")
-        idx_used = r["idx"].copy()
-        tie_pairs = np.argwhere(diff | order_diff)
-        rep["near_ties"] = int(len(tie_pairs))
-        for t, g in tie_pairs:
-            idx_used[t, g] = gpu["idx"][t, g]
-        same = ~(diff | order_diff)
-        np.testing.assert_allclose(gpu["w"][same], r["w"][same], rtol=2e-6, atol=1e-7)
+        idx_used, rep["near_ties"] = check_routing(cfg, r, gpu["idx"], gpu["w"])
         st = go.aux(cfg, r["p"], idx_used)
         np.testing.assert_array_equal(gpu["counts"], st["counts"])
         np.testing.assert_allclose(gpu["mean_prob"], st["mean_prob"], rtol=1e-6, atol=1e-12)
@@ -125,4 +135,25 @@ def compare(wl, gpu: dict, inputs: dict, rows=None, want_qo=False) -> dict:
         rep["q_ref"], rep["o_ref"] = res[1], res[2]
     assert np.all(np.isfinite(gpu["y"][rows])), "non-finite GPU output"
     assert err <= Y_TOL[wl.dtype], f"{wl.name}: y max-abs error {err:.3e} x token RMS > {Y_TOL[wl.dtype]}"
+    return rep
+
+
+def compare_decode(wl, y, idx, w, inputs: dict, pos) -> dict:
+    """One decode step (new token of sequence b at position pos[b], history inputs["x"][b]) against
+    the oracle's decode (row pos[b] of the causal forward over the prefix); same routing rules
+    and the same y bar as the forward."""
+    cfg = oracle_cfg(wl)
+    x = inputs["x"]
+    rep = dict(workload=wl.name, near_ties=0)
+    idx_new = None
+    if not wl.dense_gqa:
+        xs = np.stack([x[b, p] for b, p in enumerate(pos)]).astype(np.float64)
+        r = go.router(cfg, xs, inputs["w_router"], inputs["b_router"])
+        idx_new, rep["near_ties"] = check_routing(cfg, r, idx, w)
+    ref = go.decode(cfg, x, inputs, pos, idx_new=idx_new)
+    y = np.asarray(y, np.float64)
+    assert np.all(np.isfinite(y)), "non-finite GPU output"
+    err = rel_err_rows(y, ref["y"], Y_STORAGE_U[wl.dtype])
+    rep.update(y_err=err, y_err_raw=rel_err_rows(y, ref["y"]))
+    assert err <= Y_TOL[wl.dtype], f"{wl.name} decode: y max-abs error {err:.3e} x token RMS > {Y_TOL[wl.dtype]}"
     return rep

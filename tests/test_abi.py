@@ -105,3 +105,34 @@ def test_host_side_sizes_and_state_errors():
     finally:
         gqe.gqe_destroy(h)
     assert gqe.gqe_last_error() == "" or isinstance(gqe.gqe_last_error(), str)
+
+
+def test_decode_host_side_errors():
+    """Decode entry points check sizes, support and call order on the host."""
+    h = gqe.gqe_init(_cfg(), _weights())
+    try:
+        n = gqe.gqe_decode_workspace_bytes(h, 64, 8192)
+        # float32 queries and merged outputs, and per-chunk partials of every (sequence, group)
+        assert n >= 64 * 9 * 48 * 4 * 2 + 64 * 8 * 32 * 2 * 50 * 4
+        for bad in ((0, 10), (4, 0), (1 << 21, 8)):
+            with pytest.raises(gqe.GqeError) as e:
+                gqe.gqe_decode_workspace_bytes(h, *bad)
+            assert e.value.code == -6
+        L = gqe.lib()
+        P = ctypes.c_void_p
+        args = [P(0x1000), P(0x200000), 1, P(0x300000), P(0x400000), P(0x500000), 16, P(0x600000),
+                1 << 30, None, None, None]
+        assert L.gqe_decode(h, *args) == -8          # weights not packed yet
+        args[3] = None
+        assert L.gqe_decode(h, *args) == -2          # no positions
+        assert L.gqe_kv_export(h, None, P(0x400000), P(0x500000), 1, 16, 0) == -8  # no forward yet
+    finally:
+        gqe.gqe_destroy(h)
+    # head_dim 20 in bf16: 40-byte cache rows are not whole 16-byte units
+    h = gqe.gqe_init(_cfg(dim=320, head_dim=20), _weights())
+    try:
+        with pytest.raises(gqe.GqeError) as e:
+            gqe.gqe_decode_workspace_bytes(h, 2, 64)
+        assert e.value.code == -4
+    finally:
+        gqe.gqe_destroy(h)

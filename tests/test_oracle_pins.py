@@ -433,3 +433,34 @@ def test_inputs_are_seeded_and_ordered():
         np.testing.assert_array_equal(a[key], b[key])
     c = make_inputs(wl.with_(variant="hard_concat"))
     np.testing.assert_array_equal(a["w_o_shared"], c["w_o_shared"])
+
+
+@pytest.mark.parametrize("variant,k,shared", [("gqe", 1, True), ("weighted_concat", 2, True),
+                                              ("hard_concat", 2, False)])
+def test_decode_is_last_row_of_prefix_bruteforce(variant, k, shared):
+    """Decode with a dense KV cache (README "Algorithm Overview", explainer "Dense KV Path"): the
+    new token's output equals the last row of the independently written numpy brute force run
+    over the sequence's prefix, for ragged positions (0 = empty cache)."""
+    wl = _wl(d=24, N=8, G=2, k=k, dh=8, B=3, S=13, variant=variant, shared=shared, rstd=0.9, bias=0.3)
+    w = make_inputs(wl)
+    pos = [0, 5, 12]
+    dec = go.decode(_cfg(wl), w["x"], w, pos)
+    for b, p in enumerate(pos):
+        bf = bruteforce.layer(_cfg(wl), 1, p + 1, w["x"][b, :p + 1], w)
+        np.testing.assert_allclose(dec["y"][b], bf["y"][p], rtol=1e-11, atol=1e-13)
+        np.testing.assert_array_equal(dec["idx"][b], bf["idx"][p])
+
+
+def test_decode_ignores_tokens_after_its_position():
+    """Causality seen from the cache: a decode step reads positions 0 .. pos only, so whatever
+    follows pos in the history (future tokens, padding) does not change its output."""
+    wl = _wl(d=24, N=4, G=2, k=1, dh=8, B=2, S=10, rstd=1.0)
+    w = make_inputs(wl)
+    pos = [3, 9]
+    ref = go.decode(_cfg(wl), w["x"], w, pos)["y"]
+    x2 = w["x"].copy()
+    x2[0, 4:] = 100.0
+    got = go.decode(_cfg(wl), x2, w, pos)["y"]
+    np.testing.assert_array_equal(got, ref)
+    x2[1, 2] += 1.0   # a cached token of sequence 1 does change it
+    assert np.any(go.decode(_cfg(wl), x2, w, pos)["y"][1] != ref[1])
