@@ -98,6 +98,8 @@ static DecodePlan make_decode_plan(const GqeDims& D, int64_t B, int64_t s_max) {
     P.qd = take((size_t)B * D.H * D.dh * 4);
     P.part = take((size_t)B * D.G * P.NC * P.MH * (D.dh + 2) * 4);
     P.od = take((size_t)B * D.H * D.dh * 4);
+    P.NS = D.G * (D.dense ? D.n : D.k) + ((!D.dense && D.variant == GQE_VARIANT_GQE) ? D.G : 0) + D.s;
+    P.yp = take((size_t)B * P.NS * D.d * 4);
     P.total = off;
     r.total = off;
     return P;
@@ -109,6 +111,7 @@ static int decode_supported(const GqeDims& D) {
     const int es = D.dtype == GQE_DTYPE_BF16 ? 2 : 4;
     if ((D.dh * es) % 16 != 0 || D.dh > 128)
         return fail(GQE_ERR_UNSUPPORTED, "decode needs head_dim * element size to be a multiple of 16 bytes and head_dim <= 128");
+    if ((D.d * es) % 16 != 0) return fail(GQE_ERR_UNSUPPORTED, "decode needs dim * element size to be a multiple of 16 bytes");
     const int mh = (D.dense ? D.n : D.k) + D.s;
     if (mh > GQE_DEC_MAX_HEADS) return fail(GQE_ERR_UNSUPPORTED, "decode handles at most %d active heads per group", GQE_DEC_MAX_HEADS);
     const int slots = D.G * (D.dense ? D.n : D.k) + ((!D.dense && D.variant == GQE_VARIANT_GQE) ? D.G : 0) + D.s;

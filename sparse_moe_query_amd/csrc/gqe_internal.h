@@ -55,7 +55,9 @@ struct DecodePlan {
     WorkPlan r;                       // routing buffers of the B new tokens (idx, wsel, psel, partials)
     int64_t B, s_max, NC;             // NC = key chunks per cache row
     int C, MH;                        // keys per chunk, largest active head count of a group
-    size_t qd, part, od;              // queries [B][H][dh], chunk partials [B][G][NC][MH][dh+2], O [B][H][dh] (f32)
+    int NS;                           // output-projection slots of one token
+    size_t qd, part, od, yp;          // queries [B][H][dh], chunk partials [B][G][NC][MH][dh+2], O [B][H][dh],
+                                      // per-slot output rows [B][NS][d] (all f32)
     size_t total;
 };
 
@@ -152,6 +154,7 @@ hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x,
                             hipStream_t st, KernelMarks* km);
 hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, const AttnSchedDev& sc, char* ws, hipStream_t st,
                             KernelMarks* km, bool prep);
+int decode_units(const GqeDims& D);
 int decode_chunk(const GqeDims& D);
 hipError_t launch_kv_export(const GqeDims& D, const WorkPlan& P, const char* ws, void* kc, void* vc, int64_t s_max,
                             int64_t b0, hipStream_t st);

@@ -37,8 +37,9 @@
 
 namespace {
 
-constexpr int kTok = 8;     // tokens per projection work group
-constexpr int kDC = 512;    // hidden-dim chunk of the token rows staged in LDS by the projection
+constexpr int kTok = 8;     // tokens per projection / output-projection work group
+constexpr int kDC = 1024;   // hidden-dim chunk of the token rows staged in LDS by the projection
+constexpr int kKeysPerThread = 8;  // attention: keys per thread (chunk = 256 / units x 8 keys)
 constexpr int kMaxH = GQE_DEC_MAX_HEADS;
 
 struct DecArgs {
@@ -54,8 +55,10 @@ struct DecArgs {
     float* qd;     // [B][H][dh]
     float* part;   // [B][G][NC][MH][dh + 2]
     float* od;     // [B][H][dh]
+    float* yp;     // [B][NS][d]: a token's output row per slot
     int64_t s_max;
-    int B, d, N, G, k, n, dh, H, s, skv, variant, dense, NC, MH, C;
+    int B, d, N, G, k, n, dh, H, s, skv, variant, dense, NC, MH, C, NS;
+    int up;        // 16-byte units of a d_h row, rounded up to a power of two
     float qscale;
 };
 
@@ -109,80 +112,96 @@ __global__ void __launch_bounds__(256) kv_export_kernel(const T* __restrict__ K,
     for (int i = tid; i < ns * dh; i += 256) vd[i] = from_f32<T>(tile[i / dh][i % dh]);
 }
 
+// Tokens of work group `tg` among the tokens that use one weight block: every token (rank0 is
+// then their choice rank), or, for routed expert e of group g, the tokens that chose e, in
+// ascending order (ballot compaction over the batch).  list[i] = token | rank << 24.  Returns the
+// count (at most kTok, uniform over the work group); list is visible to the whole group.
+__device__ int token_group(const DecArgs& a, bool routed, int e, int g, int rank0, int tg, int* list,
+                           int* wcount) {
+    const int tid = threadIdx.x, nw = blockDim.x >> 6;
+    if (!routed) {
+        int ntok = a.B - kTok * tg;
+        ntok = ntok < kTok ? ntok : kTok;
+        if (tid < ntok) list[tid] = (kTok * tg + tid) | (rank0 << 24);
+        __syncthreads();
+        return ntok;
+    }
+    const int w = tid >> 6;
+    int base = 0;
+    for (int b0 = 0; b0 < a.B; b0 += blockDim.x) {
+        const int b = b0 + tid;
+        int rank = -1;
+        if (b < a.B) {
+            const int32_t* id = a.idx + ((int64_t)b * a.G + g) * a.k;
+            for (int r = 0; r < a.k; ++r)
+                if (id[r] == e) rank = r;
+        }
+        const uint64_t m = __builtin_amdgcn_ballot_w64(rank >= 0);
+        if ((tid & 63) == 0) wcount[w] = __builtin_popcountll(m);
+        __syncthreads();
+        int off = base, tot = 0;
+        for (int i = 0; i < nw; ++i) {
+            if (i < w) off += wcount[i];
+            tot += wcount[i];
+        }
+        const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        const int slot = off + pre - kTok * tg;
+        if (rank >= 0 && slot >= 0 && slot < kTok) list[slot] = b | (rank << 24);
+        base += tot;
+        __syncthreads();
+    }
+    const int ntok = base - kTok * tg;
+    return ntok < 0 ? 0 : (ntok < kTok ? ntok : kTok);
+}
+
+__device__ __forceinline__ u32x4_t load16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+
 // ---------------------------------------------------------------- projections of the new tokens
+// Thread (unit u of the d_h columns, row slice rs): 16-byte units of the weight rows rs, rs + RS,
+// ... (RS = 256 / UP slices, UP = units per row rounded up to a power of two) against the staged
+// token rows; partial sums reduced over the slices by lane exchanges inside a wave, then across
+// the four waves in LDS.
 template <typename T>
 __global__ void __launch_bounds__(256) dec_proj_kernel(DecArgs a) {
+    constexpr int E = 16 / (int)sizeof(T);
     __shared__ float xs[kTok][kDC];
-    __shared__ float red[256 * kTok];
+    __shared__ float wacc[4][kTok][128];
     __shared__ int list[kTok];
     __shared__ int wcount[4];
     const int hb = blockIdx.x, tg = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
     const int G = a.G, dh = a.dh, d = a.d;
     const int ebase = 2 * G + a.s;
     const bool is_exp = hb >= ebase;
     const int e = hb - ebase;
     const int g = is_exp ? e / a.n : (hb < G ? hb : hb - G);
-
-    // tokens of this work group: entries [8 tg, 8 tg + 8) of the tokens that use the head block
-    int ntok;
-    if (!is_exp || a.dense) {
-        const int r = is_exp ? e % a.n : 0;  // all-active GQA: expert j of a group is head j
-        ntok = a.B - kTok * tg;
-        ntok = ntok < kTok ? ntok : kTok;
-        if (tid < ntok) list[tid] = (kTok * tg + tid) | (r << 24);
-    } else {
-        // routed expert e: its tokens in ascending order (ballot compaction over the batch)
-        const int w = tid >> 6;
-        int base = 0;
-        for (int b0 = 0; b0 < a.B; b0 += 256) {
-            const int b = b0 + tid;
-            int rank = -1;
-            if (b < a.B) {
-                const int32_t* id = a.idx + ((int64_t)b * G + g) * a.k;
-                for (int r = 0; r < a.k; ++r)
-                    if (id[r] == e) rank = r;
-            }
-            const uint64_t m = __builtin_amdgcn_ballot_w64(rank >= 0);
-            if ((tid & 63) == 0) wcount[w] = __builtin_popcountll(m);
-            __syncthreads();
-            int off = base;
-            for (int i = 0; i < w; ++i) off += wcount[i];
-            const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-            const int slot = off + pre - kTok * tg;
-            if (rank >= 0 && slot >= 0 && slot < kTok) list[slot] = b | (rank << 24);
-            base += wcount[0] + wcount[1] + wcount[2] + wcount[3];
-            __syncthreads();
-        }
-        ntok = base - kTok * tg;
-        ntok = ntok < 0 ? 0 : (ntok < kTok ? ntok : kTok);
-    }
+    const int ntok = token_group(a, is_exp && !a.dense, e, g, is_exp ? e % a.n : 0, tg, list, wcount);
     if (ntok <= 0) return;  // uniform over the work group
-    __syncthreads();
-    int tok[kTok];
-#pragma unroll
-    for (int t = 0; t < kTok; ++t) tok[t] = t < ntok ? list[t] : list[0];
 
     const T* W;
-    int64_t rs;
+    int64_t rstride;
     if (hb < G) {
         W = (const T*)a.wk + hb * dh;
-        rs = (int64_t)G * dh;
+        rstride = (int64_t)G * dh;
     } else if (hb < 2 * G) {
         W = (const T*)a.wv + (hb - G) * dh;
-        rs = (int64_t)G * dh;
+        rstride = (int64_t)G * dh;
     } else if (!is_exp) {
         W = (const T*)a.wqs;
-        rs = dh;
+        rstride = dh;
     } else {
         W = (const T*)a.wq + (int64_t)e * d * dh;
-        rs = dh;
+        rstride = dh;
     }
-    const int nsl = 256 / dh;  // slices of the hidden dimension (dh <= 128)
-    const int j = tid % dh, sl = tid / dh;
-    const bool act = sl < nsl;
-    float acc[kTok];
+    const int U = dh / E;
+    const int UP = a.up, RS = 256 / UP;
+    const int u = tid & (UP - 1), rs = tid / UP;
+    const bool uact = u < U;
+    float acc[kTok][E];
 #pragma unroll
-    for (int t = 0; t < kTok; ++t) acc[t] = 0.f;
+    for (int t = 0; t < kTok; ++t)
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc[t][i] = 0.f;
     const T* X = (const T*)a.x;
     for (int c0 = 0; c0 < d; c0 += kDC) {
         const int nc = d - c0 < kDC ? d - c0 : kDC;
@@ -191,29 +210,49 @@ __global__ void __launch_bounds__(256) dec_proj_kernel(DecArgs a) {
             xs[t][c] = t < ntok ? to_f32(X[(int64_t)(list[t] & 0xffffff) * d + c0 + c]) : 0.f;
         }
         __syncthreads();
-        if (act) {
-            const T* wp = W + (int64_t)c0 * rs + j;
-            for (int i = sl; i < nc; i += nsl) {
-                const float wv = to_f32(wp[(int64_t)i * rs]);
+        if (uact) {
+            const T* wp = W + (int64_t)c0 * rstride + u * E;
+            auto rowfma = [&](const u32x4_t& wv, int i) {
+                float f[E];
+                widen16(wv, f);
 #pragma unroll
-                for (int t = 0; t < kTok; ++t) acc[t] += xs[t][i] * wv;
+                for (int t = 0; t < kTok; ++t) {
+                    const float xv = xs[t][i];
+#pragma unroll
+                    for (int q = 0; q < E; ++q) acc[t][q] += xv * f[q];
+                }
+            };
+            int i = rs;
+            for (; i + 3 * RS < nc; i += 4 * RS) {
+                const u32x4_t w0 = load16(wp + (int64_t)i * rstride);
+                const u32x4_t w1 = load16(wp + (int64_t)(i + RS) * rstride);
+                const u32x4_t w2 = load16(wp + (int64_t)(i + 2 * RS) * rstride);
+                const u32x4_t w3 = load16(wp + (int64_t)(i + 3 * RS) * rstride);
+                rowfma(w0, i);
+                rowfma(w1, i + RS);
+                rowfma(w2, i + 2 * RS);
+                rowfma(w3, i + 3 * RS);
             }
+            for (; i < nc; i += RS) rowfma(load16(wp + (int64_t)i * rstride), i);
         }
         __syncthreads();
     }
-    if (act) {
+    // sum over the row slices: inside the wave (lanes u, u + UP, ...), then over the waves
+    for (int off = UP; off < 64; off <<= 1)
 #pragma unroll
-        for (int t = 0; t < kTok; ++t) red[(sl * dh + j) * kTok + t] = acc[t];
-    }
+        for (int t = 0; t < kTok; ++t)
+#pragma unroll
+            for (int q = 0; q < E; ++q) acc[t][q] += __shfl_xor(acc[t][q], off);
+    if (lane < UP && uact)
+#pragma unroll
+        for (int t = 0; t < kTok; ++t)
+#pragma unroll
+            for (int q = 0; q < E; ++q) wacc[w][t][u * E + q] = acc[t][q];
     __syncthreads();
     for (int o = tid; o < ntok * dh; o += 256) {
         const int t = o / dh, jj = o - t * dh;
-        float v = 0.f;
-        for (int q = 0; q < nsl; ++q) v += red[(q * dh + jj) * kTok + t];
-        int tk = tok[0];
-#pragma unroll
-        for (int u = 1; u < kTok; ++u)
-            if (t == u) tk = tok[u];
+        const float v = (wacc[0][t][jj] + wacc[1][t][jj]) + (wacc[2][t][jj] + wacc[3][t][jj]);
+        const int tk = list[t];
         const int b = tk & 0xffffff, rank = tk >> 24;
         if (hb < 2 * G) {
             const int p = a.pos[b];
@@ -228,110 +267,144 @@ __global__ void __launch_bounds__(256) dec_proj_kernel(DecArgs a) {
 }
 
 // ---------------------------------------------------------------- attention over one cache chunk
-template <typename T>
+// Thread (unit u, key group kg): the 16-byte units u of keys kg, kg + KG, ... (KG = 256 / UP key
+// groups, KPT keys each) of K and of V, all loaded up front.  Scores: partial dot products over
+// the unit, summed over the UP lanes of a key by lane exchanges; softmax over the chunk; P.V:
+// each lane scales its V units by its keys' probabilities, summed over the key groups (lane
+// exchanges, then LDS across the waves).  MH bounds the active heads of a group.
+template <typename T, int MH>
 __global__ void __launch_bounds__(256) dec_attn_kernel(DecArgs a) {
-    constexpr int E16 = 16 / (int)sizeof(T);  // elements per 16-byte load
-    __shared__ __align__(16) unsigned char vbuf[32768];
-    __shared__ __align__(16) float qs[kMaxH * 128];
-    __shared__ float ps[kMaxH * 256];
-    __shared__ float red[2048];
-    __shared__ float wred[4][kMaxH];
+    constexpr int E = 16 / (int)sizeof(T);
+    constexpr int KPT = kKeysPerThread;
+    __shared__ float wred[4][MH];
+    __shared__ float osum[4][MH][128];
     const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int lane = tid & 63, w = tid >> 6;
     const int p = a.pos[b];
     if (!pos_ok(p, a.s_max)) return;
     const int64_t L = (int64_t)p + 1, c0 = (int64_t)chunk * a.C;
     if (c0 >= L) return;
     const int nk = (int)(L - c0 < a.C ? L - c0 : a.C);
-    const int dh = a.dh, G = a.G, C = a.C;
+    const int dh = a.dh, G = a.G;
     const int kr = a.dense ? a.n : a.k;
     const int m = kr + ((a.s && g == a.skv) ? 1 : 0);
-    for (int i = tid; i < m * dh; i += 256) {
-        const int h = i / dh, jj = i - h * dh;
-        const int hid = h < kr ? g * kr + h : G * kr;
-        qs[i] = a.qd[((int64_t)b * a.H + hid) * dh + jj];
-    }
+    const int U = dh / E, UP = a.up, KG = 256 / UP;
+    const int u = tid & (UP - 1), kg = tid / UP;
+    const bool uact = u < U;
     const int64_t row0 = ((int64_t)b * G + g) * a.s_max + c0;
-    {
-        const unsigned char* vsrc = (const unsigned char*)a.vc + row0 * dh * (int64_t)sizeof(T);
-        const int nbytes = nk * dh * (int)sizeof(T);
-        for (int o = tid * 16; o < nbytes; o += 256 * 16)
-            *reinterpret_cast<u32x4_t*>(vbuf + o) = *reinterpret_cast<const u32x4_t*>(vsrc + o);
+    const T* kb = (const T*)a.kc + row0 * dh + u * E;
+    const T* vb = (const T*)a.vc + row0 * dh + u * E;
+    // every lane loads (past the chunk or the row: a valid key's unit, then zeroed): no branches
+    u32x4_t kv[KPT], vv[KPT];
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+        const int i = kg + KG * r;
+        const int64_t off = (int64_t)(i < nk ? i : nk - 1) * dh - (uact ? 0 : u * E);
+        kv[r] = load16(kb + off);
+        vv[r] = load16(vb + off);
     }
-    __syncthreads();  // queries visible
-
-    // scores of key c0 + tid for every active head (log2 units: queries carry log2(e)/sqrt(d_h))
-    float sc[kMaxH];
 #pragma unroll
-    for (int h = 0; h < kMaxH; ++h) sc[h] = -INFINITY;
-    if (tid < nk) {
-#pragma unroll
-        for (int h = 0; h < kMaxH; ++h)
-            if (h < m) sc[h] = 0.f;
-        const u32x4_t* krow = reinterpret_cast<const u32x4_t*>((const T*)a.kc + (row0 + tid) * dh);
-        for (int u = 0; u < dh / E16; ++u) {
-            float f[E16];
-            widen16(krow[u], f);
-#pragma unroll
-            for (int h = 0; h < kMaxH; ++h) {
-                if (h >= m) break;
-                const float* q = qs + h * dh + u * E16;
-#pragma unroll
-                for (int i = 0; i < E16; ++i) sc[h] += q[i] * f[i];
-            }
+    for (int r = 0; r < KPT; ++r) {
+        if (!uact || kg + KG * r >= nk) {
+            kv[r] = u32x4_t{0u, 0u, 0u, 0u};
+            vv[r] = u32x4_t{0u, 0u, 0u, 0u};
         }
     }
-    float mx[kMaxH], ls[kMaxH];
+    float q[MH][E];
 #pragma unroll
-    for (int h = 0; h < kMaxH; ++h) {
-        const float v = wave_max(sc[h]);
-        if ((tid & 63) == 0) wred[w][h] = v;
-    }
-    __syncthreads();
+    for (int h = 0; h < MH; ++h) {
+        const int hid = h < m ? (h < kr ? g * kr + h : G * kr) : 0;
+        const f32x4_t* qp = reinterpret_cast<const f32x4_t*>(a.qd + ((int64_t)b * a.H + hid) * dh + (uact ? u * E : 0));
 #pragma unroll
-    for (int h = 0; h < kMaxH; ++h) mx[h] = fmaxf(fmaxf(wred[0][h], wred[1][h]), fmaxf(wred[2][h], wred[3][h]));
-    __syncthreads();
+        for (int i = 0; i < E; i += 4) {
+            const f32x4_t v = qp[i / 4];
 #pragma unroll
-    for (int h = 0; h < kMaxH; ++h) {
-        const float pr = (h < m && tid < nk) ? exp2f(sc[h] - mx[h]) : 0.f;
-        if (h < m && tid < C) ps[h * C + tid] = pr;
-        const float v = wave_sum(pr);
-        if ((tid & 63) == 0) wred[w][h] = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < kMaxH; ++h) ls[h] = (wred[0][h] + wred[1][h]) + (wred[2][h] + wred[3][h]);
-
-    // P.V: thread (dim j, key group kg) sums keys kg, kg + KG, ...
-    const int KG = 256 / dh;
-    const int j = tid % dh, kg = tid / dh;
-    if (kg < KG) {
-        float o[kMaxH];
-#pragma unroll
-        for (int h = 0; h < kMaxH; ++h) o[h] = 0.f;
-        const T* vb = reinterpret_cast<const T*>(vbuf);
-        for (int i = kg; i < nk; i += KG) {
-            const float v = to_f32(vb[i * dh + j]);
-#pragma unroll
-            for (int h = 0; h < kMaxH; ++h)
-                if (h < m) o[h] += ps[h * C + i] * v;
+            for (int z = 0; z < 4; ++z) q[h][i + z] = (h < m && uact) ? v[z] : 0.f;
         }
+    }
+    // scores (log2 units: the queries carry log2(e)/sqrt(d_h))
+    float sc[MH][KPT];
 #pragma unroll
-        for (int h = 0; h < kMaxH; ++h)
-            if (h < m) red[(kg * kMaxH + h) * dh + j] = o[h];
+    for (int r = 0; r < KPT; ++r) {
+        float f[E];
+        widen16(kv[r], f);
+#pragma unroll
+        for (int h = 0; h < MH; ++h) {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < E; ++i) s += q[h][i] * f[i];
+            sc[h][r] = s;
+        }
+    }
+    for (int off = 1; off < UP; off <<= 1)
+#pragma unroll
+        for (int h = 0; h < MH; ++h)
+#pragma unroll
+            for (int r = 0; r < KPT; ++r) sc[h][r] += __shfl_xor(sc[h][r], off);
+    float mx[MH];
+#pragma unroll
+    for (int h = 0; h < MH; ++h) {
+        float v = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < KPT; ++r)
+            if (kg + KG * r < nk) v = fmaxf(v, sc[h][r]);
+        v = wave_max(v);
+        if (lane == 0) wred[w][h] = v;
     }
     __syncthreads();
+#pragma unroll
+    for (int h = 0; h < MH; ++h) mx[h] = fmaxf(fmaxf(wred[0][h], wred[1][h]), fmaxf(wred[2][h], wred[3][h]));
+    __syncthreads();
+    float ls[MH];
+#pragma unroll
+    for (int h = 0; h < MH; ++h) {
+        float l = 0.f;
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+            const float pr = (h < m && kg + KG * r < nk) ? __builtin_amdgcn_exp2f(sc[h][r] - mx[h]) : 0.f;
+            sc[h][r] = pr;
+            l += pr;
+        }
+        l = wave_sum(u == 0 ? l : 0.f);  // one lane per key
+        if (lane == 0) wred[w][h] = l;
+    }
+    // P.V over my keys
+    float o[MH][E];
+#pragma unroll
+    for (int h = 0; h < MH; ++h)
+#pragma unroll
+        for (int i = 0; i < E; ++i) o[h][i] = 0.f;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+        float f[E];
+        widen16(vv[r], f);
+#pragma unroll
+        for (int h = 0; h < MH; ++h)
+#pragma unroll
+            for (int i = 0; i < E; ++i) o[h][i] += sc[h][r] * f[i];
+    }
+    for (int off = UP; off < 64; off <<= 1)
+#pragma unroll
+        for (int h = 0; h < MH; ++h)
+#pragma unroll
+            for (int i = 0; i < E; ++i) o[h][i] += __shfl_xor(o[h][i], off);
+    if (lane < UP && uact)
+#pragma unroll
+        for (int h = 0; h < MH; ++h)
+#pragma unroll
+            for (int i = 0; i < E; ++i) osum[w][h][u * E + i] = o[h][i];
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < MH; ++h) ls[h] = (wred[0][h] + wred[1][h]) + (wred[2][h] + wred[3][h]);
     float* dst = a.part + ((((int64_t)b * G + g) * a.NC + chunk) * a.MH) * (dh + 2);
     for (int i = tid; i < m * dh; i += 256) {
         const int h = i / dh, jj = i - h * dh;
-        float v = 0.f;
-        for (int q = 0; q < KG; ++q) v += red[(q * kMaxH + h) * dh + jj];
-        dst[h * (dh + 2) + jj] = v;
+        dst[h * (dh + 2) + jj] = (osum[0][h][jj] + osum[1][h][jj]) + (osum[2][h][jj] + osum[3][h][jj]);
     }
     if (tid < m) {
         float mv = mx[0], lv = ls[0];
 #pragma unroll
-        for (int h = 1; h < kMaxH; ++h)
+        for (int h = 1; h < MH; ++h)
             if (tid == h) {
                 mv = mx[h];
                 lv = ls[h];
@@ -342,7 +415,10 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecArgs a) {
 }
 
 // ---------------------------------------------------------------- merge of the chunk partials
+// One wave per (token, head): chunk weights 2^(m_c - M) / l from the lanes (64 chunks at a time),
+// then every lane sums its head dims over those chunks.
 __global__ void __launch_bounds__(64) dec_merge_kernel(DecArgs a) {
+    __shared__ float scl[64];
     const int hid = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
     const int dh = a.dh;
     float* out = a.od + ((int64_t)b * a.H + hid) * dh;
@@ -358,81 +434,161 @@ __global__ void __launch_bounds__(64) dec_merge_kernel(DecArgs a) {
     const int64_t cs = (int64_t)a.MH * (dh + 2);
     const float* base = a.part + (((int64_t)b * a.G + g) * a.NC * a.MH + h) * (dh + 2);
     float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, base[c * cs + dh]);
+    for (int c = lane; c < nch; c += 64) M = fmaxf(M, base[c * cs + dh]);
+    M = wave_max(M);
     float l = 0.f;
-    for (int c = 0; c < nch; ++c) l += base[c * cs + dh + 1] * exp2f(base[c * cs + dh] - M);
-    const float inv = 1.f / l;
-    for (int j = lane; j < dh; j += 64) {
-        float o = 0.f;
-        for (int c = 0; c < nch; ++c) o += base[c * cs + j] * exp2f(base[c * cs + dh] - M);
-        out[j] = o * inv;
+    for (int c = lane; c < nch; c += 64) l += base[c * cs + dh + 1] * exp2f(base[c * cs + dh] - M);
+    const float inv = 1.f / wave_sum(l);
+    float o0 = 0.f, o1 = 0.f;
+    for (int cb = 0; cb < nch; cb += 64) {
+        const int c = cb + lane;
+        scl[lane] = c < nch ? exp2f(base[c * cs + dh] - M) * inv : 0.f;
+        __syncthreads();
+        const int n = nch - cb < 64 ? nch - cb : 64;
+        const float* pc = base + cb * cs;
+        if (lane < dh) {
+#pragma unroll 8
+            for (int i = 0; i < n; ++i) o0 += pc[i * cs + lane] * scl[i];
+        }
+        if (lane + 64 < dh) {
+#pragma unroll 8
+            for (int i = 0; i < n; ++i) o1 += pc[i * cs + lane + 64] * scl[i];
+        }
+        __syncthreads();
     }
+    if (lane < dh) out[lane] = o0;
+    if (lane + 64 < dh) out[lane + 64] = o1;
 }
 
-// ---------------------------------------------------------------- output construction + W_o
+// ---------------------------------------------------------------- output projection per weight slot
+// Work group (one wave) = (weight slot, up to 8 tokens that use it, 64 column units of 16 bytes):
+// slot = W_o of routed expert e (the tokens that chose it), W_oR of group g (variant gqe) or the
+// shared head's W_os (every token).  Each token's slot vector (its head output, times the
+// raw router probability for weighted_concat; the renormalised mix sum_r w_r o_r for W_oR) times the
+// slot's d_h x d block, each weight row read once for the group of tokens.  Writes the token's
+// float32 partial row of that slot; dec_ysum_kernel adds a token's slots in a fixed order.
 template <typename T>
-__global__ void __launch_bounds__(256) dec_combine_kernel(DecArgs a) {
-    __shared__ float vec[GQE_DEC_MAX_SLOT_DIMS];
-    __shared__ const T* wsl[GQE_DEC_MAX_SLOTS];
-    const int b = blockIdx.y, tid = threadIdx.x;
-    const int c = blockIdx.x * 256 + tid;
-    const int dh = a.dh, G = a.G, d = a.d;
-    T* y = (T*)a.y + (int64_t)b * d;
-    if (!pos_ok(a.pos[b], a.s_max)) {
-        if (c < d) y[c] = from_f32<T>(__builtin_nanf(""));
-        return;
-    }
+__global__ void __launch_bounds__(64) dec_oproj_kernel(DecArgs a) {
+    constexpr int E = 16 / (int)sizeof(T);
+    __shared__ float vs[kTok][128];
+    __shared__ int list[kTok];
+    __shared__ int wcount[1];
+    const int sm = blockIdx.x, tg = blockIdx.y, lane = threadIdx.x;
+    const int G = a.G, dh = a.dh, d = a.d;
     const int kr = a.dense ? a.n : a.k;
     const bool rslot = !a.dense && a.variant == GQE_VARIANT_GQE;
     const int nr = G * kr;
-    const int nslot = nr + (rslot ? G : 0) + a.s;
-    const float* o = a.od + (int64_t)b * a.H * dh;
-    const int64_t sel = (int64_t)b * G * a.k;  // [b][g][r] of the routing buffers
-    for (int i = tid; i < nslot * dh; i += 256) {
-        const int sl = i / dh, jj = i - sl * dh;
-        float v;
-        if (sl < nr) {
-            const float coef = (!a.dense && a.variant == GQE_VARIANT_WEIGHTED_CONCAT) ? a.psel[sel + sl] : 1.f;
-            v = coef * o[sl * dh + jj];
-        } else if (rslot && sl < nr + G) {
-            const int g = sl - nr;
-            v = 0.f;
-            for (int r = 0; r < a.k; ++r) v += a.wsel[sel + g * a.k + r] * o[(g * a.k + r) * dh + jj];
-        } else {
-            v = o[nr * dh + jj];  // shared head
-        }
-        vec[i] = v;
+    int kind, g = 0, e = 0;  // 0 routed expert, 1 renormalised slot, 2 shared head
+    if (sm < a.N) {
+        kind = 0;
+        e = sm;
+        g = e / a.n;
+    } else if (rslot && sm < a.N + G) {
+        kind = 1;
+        g = sm - a.N;
+    } else {
+        kind = 2;
     }
-    for (int i = tid; i < nslot; i += 256) {
-        const T* wp;
-        if (i < nr) {
-            const int g = i / kr, r = i - g * kr;
-            const int e = a.dense ? g * a.n + r : a.idx[sel + g * a.k + r];
-            wp = (const T*)a.wo + (int64_t)e * dh * d;
-        } else if (rslot && i < nr + G) {
-            wp = (const T*)a.wor + (int64_t)(i - nr) * dh * d;
-        } else {
-            wp = (const T*)a.wos;
+    const int ntok = token_group(a, kind == 0 && !a.dense, e, g, kind == 0 ? e % a.n : 0, tg, list, wcount);
+    if (ntok <= 0) return;
+    for (int i = lane; i < kTok * dh; i += 64) {
+        const int t = i / dh, jj = i - t * dh;
+        float v = 0.f;
+        if (t < ntok) {
+            const int tk = list[t];
+            const int b = tk & 0xffffff, r = tk >> 24;
+            const float* o = a.od + (int64_t)b * a.H * dh;
+            const int64_t sel = ((int64_t)b * G + g) * a.k;
+            if (kind == 0) {
+                const float coef = (!a.dense && a.variant == GQE_VARIANT_WEIGHTED_CONCAT) ? a.psel[sel + r] : 1.f;
+                v = coef * o[(g * kr + r) * dh + jj];
+            } else if (kind == 1) {
+                for (int q = 0; q < a.k; ++q) v += a.wsel[sel + q] * o[(g * a.k + q) * dh + jj];
+            } else {
+                v = o[nr * dh + jj];
+            }
         }
-        wsl[i] = wp;
+        vs[t][jj] = v;
     }
     __syncthreads();
-    if (c >= d) return;
-    float acc = 0.f;
-    for (int sl = 0; sl < nslot; ++sl) {
-        const T* wp = wsl[sl] + c;
-        const float* v = vec + sl * dh;
-        for (int jj = 0; jj < dh; ++jj) acc += v[jj] * to_f32(wp[(int64_t)jj * d]);
+    const int cu = blockIdx.z * 64 + lane;  // column unit
+    if (cu * E >= d) return;
+    const T* W = kind == 0 ? (const T*)a.wo + (int64_t)e * dh * d
+                           : (kind == 1 ? (const T*)a.wor + (int64_t)g * dh * d : (const T*)a.wos);
+    const T* wp = W + cu * E;
+    float acc[kTok][E];
+#pragma unroll
+    for (int t = 0; t < kTok; ++t)
+#pragma unroll
+        for (int q = 0; q < E; ++q) acc[t][q] = 0.f;
+    auto rowfma = [&](const u32x4_t& wv, int j) {
+        float f[E];
+        widen16(wv, f);
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) {
+            const float x = vs[t][j];
+#pragma unroll
+            for (int q = 0; q < E; ++q) acc[t][q] += x * f[q];
+        }
+    };
+    int j = 0;
+    for (; j + 7 < dh; j += 8) {
+        u32x4_t wv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wv[i] = load16(wp + (int64_t)(j + i) * d);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rowfma(wv[i], j + i);
     }
-    y[c] = from_f32<T>(acc);
+    for (; j < dh; ++j) rowfma(load16(wp + (int64_t)j * d), j);
+    for (int t = 0; t < ntok; ++t) {
+        const int tk = list[t];
+        const int b = tk & 0xffffff, r = tk >> 24;
+        const int ls = kind == 0 ? g * kr + r : (kind == 1 ? nr + g : nr + (rslot ? G : 0));
+        float* dst = a.yp + ((int64_t)b * a.NS + ls) * d + cu * E;
+#pragma unroll
+        for (int q = 0; q < E; q += 4) {
+            float acc4[4];
+            for (int z = 0; z < 4; ++z) {
+                acc4[z] = acc[0][q + z];
+#pragma unroll
+                for (int tt = 1; tt < kTok; ++tt)
+                    if (t == tt) acc4[z] = acc[tt][q + z];
+            }
+            *reinterpret_cast<f32x4_t*>(dst + q) = f32x4_t{acc4[0], acc4[1], acc4[2], acc4[3]};
+        }
+    }
+}
+
+// y[b, :] = sum of the token's slot rows, in slot order (deterministic).
+template <typename T>
+__global__ void __launch_bounds__(256) dec_ysum_kernel(DecArgs a) {
+    const int b = blockIdx.y;
+    const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (c >= a.d) return;
+    T* y = (T*)a.y + (int64_t)b * a.d + c;
+    if (!pos_ok(a.pos[b], a.s_max)) {
+        for (int z = 0; z < 4; ++z) y[z] = from_f32<T>(__builtin_nanf(""));
+        return;
+    }
+    const int kr = a.dense ? a.n : a.k;
+    const int nslot = a.G * kr + ((!a.dense && a.variant == GQE_VARIANT_GQE) ? a.G : 0) + a.s;
+    const float* src = a.yp + (int64_t)b * a.NS * a.d + c;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int sl = 0; sl < nslot; ++sl) acc += *reinterpret_cast<const f32x4_t*>(src + (int64_t)sl * a.d);
+    for (int z = 0; z < 4; ++z) y[z] = from_f32<T>(acc[z]);
 }
 
 }  // namespace
 
-int decode_chunk(const GqeDims& D) {
-    const int row = D.dh * (D.dtype == GQE_DTYPE_BF16 ? 2 : 4);
-    return row <= 128 ? 256 : (row <= 256 ? 128 : 64);
+int decode_units(const GqeDims& D) {
+    const int u = D.dh * (D.dtype == GQE_DTYPE_BF16 ? 2 : 4) / 16;
+    int up = 1;
+    while (up < u) up <<= 1;
+    return up;
 }
+
+int decode_chunk(const GqeDims& D) { return 256 / decode_units(D) * kKeysPerThread; }
 
 hipError_t launch_kv_export(const GqeDims& D, const WorkPlan& P, const char* ws, void* kc, void* vc, int64_t s_max,
                             int64_t b0, hipStream_t st) {
@@ -467,6 +623,7 @@ hipError_t launch_decode(const GqeDims& D, const DecodePlan& P, const gqe_weight
     a.qd = (float*)(ws + P.qd);
     a.part = (float*)(ws + P.part);
     a.od = (float*)(ws + P.od);
+    a.yp = (float*)(ws + P.yp);
     a.s_max = P.s_max;
     a.B = (int)P.B;
     a.d = D.d;
@@ -483,34 +640,48 @@ hipError_t launch_decode(const GqeDims& D, const DecodePlan& P, const gqe_weight
     a.NC = (int)P.NC;
     a.MH = P.MH;
     a.C = P.C;
+    a.NS = P.NS;
+    a.up = decode_units(D);
     a.qscale = (float)(1.4426950408889634 / std::sqrt((double)D.dh));
     const bool bf = D.dtype == GQE_DTYPE_BF16;
-    const int HB = 2 * D.G + D.s + D.N;
+    const unsigned tgroups = (unsigned)ceil_div(P.B, kTok);
+    hipError_t e;
+    // projections of the new tokens (K/V into the cache)
     if (km) km->begin(KT_DEC_PROJ);
-    const dim3 gp((unsigned)HB, (unsigned)ceil_div(P.B, kTok));
+    const dim3 gp((unsigned)(2 * D.G + D.s + D.N), tgroups);
     if (bf) dec_proj_kernel<bf16_t><<<gp, 256, 0, st>>>(a);
     else dec_proj_kernel<float><<<gp, 256, 0, st>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (km) km->mark(KT_DEC_PROJ);
+    // attention over the cache chunks, then the merge
     if (km) km->begin(KT_DEC_ATTN);
     const dim3 ga((unsigned)P.NC, (unsigned)D.G, (unsigned)P.B);
-    if (bf) dec_attn_kernel<bf16_t><<<ga, 256, 0, st>>>(a);
-    else dec_attn_kernel<float><<<ga, 256, 0, st>>>(a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+#define GQE_DEC_ATTN(MHV)                                            \
+    if (bf) dec_attn_kernel<bf16_t, MHV><<<ga, 256, 0, st>>>(a);    \
+    else dec_attn_kernel<float, MHV><<<ga, 256, 0, st>>>(a);
+    if (P.MH <= 1) { GQE_DEC_ATTN(1) }
+    else if (P.MH <= 2) { GQE_DEC_ATTN(2) }
+    else if (P.MH <= 4) { GQE_DEC_ATTN(4) }
+    else { GQE_DEC_ATTN(8) }
+#undef GQE_DEC_ATTN
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (km) km->mark(KT_DEC_ATTN);
     if (km) km->begin(KT_DEC_MERGE);
     dec_merge_kernel<<<dim3((unsigned)D.H, (unsigned)P.B), 64, 0, st>>>(a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (km) km->mark(KT_DEC_MERGE);
+    // output construction + output projection: per weight slot, then the per-token sum
     if (km) km->begin(KT_DEC_COMBINE);
-    const dim3 gc((unsigned)ceil_div(D.d, 256), (unsigned)P.B);
-    if (bf) dec_combine_kernel<bf16_t><<<gc, 256, 0, st>>>(a);
-    else dec_combine_kernel<float><<<gc, 256, 0, st>>>(a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    const int E = bf ? 8 : 4;
+    const unsigned nsm = (unsigned)(D.N + ((!D.dense && D.variant == GQE_VARIANT_GQE) ? D.G : 0) + D.s);
+    const dim3 go(nsm, tgroups, (unsigned)ceil_div(D.d / E, 64));
+    if (bf) dec_oproj_kernel<bf16_t><<<go, 64, 0, st>>>(a);
+    else dec_oproj_kernel<float><<<go, 64, 0, st>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const dim3 gy((unsigned)ceil_div(D.d / 4, 256), (unsigned)P.B);
+    if (bf) dec_ysum_kernel<bf16_t><<<gy, 256, 0, st>>>(a);
+    else dec_ysum_kernel<float><<<gy, 256, 0, st>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (km) km->mark(KT_DEC_COMBINE);
     return hipSuccess;
 }
