@@ -534,7 +534,9 @@ int gqe_decode(gqe_handle_t* h, const void* x, void* y, int64_t batch, const int
         if (rc != GQE_OK) return rc;
         km = &marks;
     }
-    if (!D.dense) e = launch_router(D, P.r, x, h->packed, h->pl, ws, route_idx, route_w, st, km, false);
+    if (!D.dense)
+        e = launch_router_tokens(D, batch, x, h->packed, h->pl, (int32_t*)(ws + P.r.idx), (float*)(ws + P.r.wsel),
+                                 (float*)(ws + P.r.psel), route_idx, route_w, st, km);
     if (e == hipSuccess) e = launch_decode(D, P, h->w, x, y, pos, kcache, vcache, ws, st, km);
     if (e == hipSuccess && km && marks.err != hipSuccess) e = marks.err;
     if (e != hipSuccess) return fail(GQE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

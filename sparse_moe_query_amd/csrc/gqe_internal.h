@@ -144,6 +144,10 @@ hipError_t launch_pack(const GqeDims& D, const gqe_weights_t& w, const PackedLay
 hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, const void* packed,
                          const PackedLayout& pl, char* ws, int32_t* route_idx, float* route_w,
                          hipStream_t st, KernelMarks* km, bool finalize);
+// Router for a handful of tokens (one block per token; no balance statistics).
+hipError_t launch_router_tokens(const GqeDims& D, int64_t T, const void* x, const void* packed,
+                                const PackedLayout& pl, int32_t* idx, float* wsel, float* psel, int32_t* route_idx,
+                                float* route_w, hipStream_t st, KernelMarks* km);
 hipError_t launch_proj_simple(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w,
                               const void* x, char* ws, hipStream_t st, KernelMarks* km);
 hipError_t launch_attn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km);

@@ -73,41 +73,51 @@ __device__ __forceinline__ void widen8<float>(const float* p, double* v) {
 // The selection compares the float64 logits; the probabilities are formed from the float64
 // differences l - max with the float32 exponential (relative error ~1e-7), and overwrite the
 // logits of the same (token, group).  Per-block statistics follow.
+// The decision of one (token tt, group g) on the group's n logits l (overwritten with the
+// probabilities); counts the choice in cnt when given.
+__device__ void select_one(const RouterArgs& a, double* l, int64_t tt, int g, int* cnt) {
+    const int n = a.n, k = a.k;
+    double m = l[0];
+    for (int j = 1; j < n; ++j) m = fmax(m, l[j]);
+    uint64_t taken = 0, sel = 0;  // sel: 4 bits per rank (n <= 16)
+    for (int r = 0; r < k; ++r) {
+        int best = -1;
+        for (int j = 0; j < n; ++j)
+            if (!((taken >> j) & 1) && (best < 0 || l[j] > l[best])) best = j;
+        taken |= (uint64_t)1 << best;
+        sel |= (uint64_t)best << (4 * r);
+    }
+    float den = 0.f;
+    for (int j = 0; j < n; ++j) den += expf((float)(l[j] - m));
+    const float inv = 1.0f / den;
+    for (int j = 0; j < n; ++j) l[j] = (double)(expf((float)(l[j] - m)) * inv);  // probabilities
+    double ps = 0.0;
+    for (int r = 0; r < k; ++r) ps += l[(sel >> (4 * r)) & 15];
+    const int64_t o = (tt * a.G + g) * k;
+    for (int r = 0; r < k; ++r) {
+        const int j = (int)((sel >> (4 * r)) & 15);
+        const int e = g * n + j;
+        const double p = l[j];
+        a.idx[o + r] = e;
+        a.wsel[o + r] = (float)(p / ps);
+        a.psel[o + r] = (float)p;
+        if (a.ridx) a.ridx[o + r] = e;
+        if (a.rw) a.rw[o + r] = (float)(p / ps);
+        if (cnt) atomicAdd(&cnt[e], 1);
+    }
+}
+
+// Softmax, top-k and weights for the block's tokens; logits in lg[tok][e] (bias included).
+// The selection compares the float64 logits; the probabilities are formed from the float64
+// differences l - max with the float32 exponential (relative error ~1e-7), and overwrite the
+// logits of the same (token, group).  Per-block statistics follow.
 __device__ void select_and_stats(const RouterArgs& a, double (*lg)[65], int* cnt, int64_t t0, int nthreads) {
-    const int n = a.n, G = a.G, k = a.k;
+    const int G = a.G;
     for (int q = threadIdx.x; q < kTok * G; q += nthreads) {
         const int tok = q / G, g = q % G;
         const int64_t tt = t0 + tok;
         if (tt >= a.T) continue;
-        double* l = &lg[tok][g * n];
-        double m = l[0];
-        for (int j = 1; j < n; ++j) m = fmax(m, l[j]);
-        uint64_t taken = 0, sel = 0;  // sel: 4 bits per rank (n <= 16)
-        for (int r = 0; r < k; ++r) {
-            int best = -1;
-            for (int j = 0; j < n; ++j)
-                if (!((taken >> j) & 1) && (best < 0 || l[j] > l[best])) best = j;
-            taken |= (uint64_t)1 << best;
-            sel |= (uint64_t)best << (4 * r);
-        }
-        float den = 0.f;
-        for (int j = 0; j < n; ++j) den += expf((float)(l[j] - m));
-        const float inv = 1.0f / den;
-        for (int j = 0; j < n; ++j) l[j] = (double)(expf((float)(l[j] - m)) * inv);  // probabilities
-        double ps = 0.0;
-        for (int r = 0; r < k; ++r) ps += l[(sel >> (4 * r)) & 15];
-        const int64_t o = (tt * G + g) * k;
-        for (int r = 0; r < k; ++r) {
-            const int j = (int)((sel >> (4 * r)) & 15);
-            const int e = g * n + j;
-            const double p = l[j];
-            a.idx[o + r] = e;
-            a.wsel[o + r] = (float)(p / ps);
-            a.psel[o + r] = (float)p;
-            if (a.ridx) a.ridx[o + r] = e;
-            if (a.rw) a.rw[o + r] = (float)(p / ps);
-            atomicAdd(&cnt[e], 1);
-        }
+        select_one(a, &lg[tok][g * a.n], tt, g, cnt);
     }
     __syncthreads();
     // per-block probability sums of every expert, in a fixed order: thread (expert e, token
@@ -255,6 +265,42 @@ __global__ void __launch_bounds__(256) router_valu_kernel(RouterArgs a) {
     select_and_stats(a, lg, cnt, t0, 256);
 }
 
+// One token per block (few tokens, e.g. a decode step): thread (expert column e, hidden slice)
+// sums its slice of x . W_r[:, e] in float64; the slices are added in a fixed order, then the
+// same decision as the blocked kernels.  No balance statistics.  fast: the weights are in the
+// lane-ordered layout of router_mfma_kernel ([octet][column][8], 16 columns), else [d][Np].
+template <typename Tin>
+__global__ void __launch_bounds__(256) router_token_kernel(RouterArgs a, int fast) {
+    __shared__ double part[16][65];
+    __shared__ double lg[65];
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int np = a.Np, nsl = 256 / np;  // Np in {16, 32, 48, 64}: 16 .. 5 slices
+    const int e = tid % np, sl = tid / np;
+    if (sl < nsl) {
+        const int len = (a.d + nsl - 1) / nsl;
+        const int i0 = sl * len, i1 = min(a.d, i0 + len);
+        const Tin* xr = reinterpret_cast<const Tin*>(a.x) + t * a.d;
+        double acc = 0.0;
+        if (e < a.N) {
+#pragma unroll 8
+            for (int i = i0; i < i1; ++i) {
+                const double w = fast ? a.wr[((int64_t)(i >> 3) * 16 + e) * 8 + (i & 7)] : a.wr[(int64_t)i * np + e];
+                acc = __builtin_fma((double)to_f32(xr[i]), w, acc);
+            }
+        }
+        part[sl][e] = acc;
+    }
+    __syncthreads();
+    if (tid < a.N) {
+        double v = part[0][tid];
+        for (int q = 1; q < nsl; ++q) v += part[q][tid];
+        lg[tid] = v + a.br[tid];
+    }
+    __syncthreads();
+    if (tid < a.G) select_one(a, &lg[tid * a.n], t, tid, nullptr);
+}
+
 // Sums the per-block partials in a fixed order (deterministic) and forms the balance loss.
 // Thread (slice j, expert e) sums blocks j, j + J, ...; the J slice sums are then added in order.
 __global__ void __launch_bounds__(256) stats_finalize_kernel(const int32_t* __restrict__ part_cnt,
@@ -270,6 +316,36 @@ __global__ void __launch_bounds__(256) stats_finalize_kernel(const int32_t* __re
 }  // namespace
 
 bool router_uses_mfma(const GqeDims& D) { return D.d % 64 == 0 && D.N <= 16; }
+
+hipError_t launch_router_tokens(const GqeDims& D, int64_t T, const void* x, const void* packed,
+                                const PackedLayout& pl, int32_t* idx, float* wsel, float* psel, int32_t* route_idx,
+                                float* route_w, hipStream_t st, KernelMarks* km) {
+    const char* pk = (const char*)packed;
+    RouterArgs a{};
+    a.x = x;
+    a.wr = (const double*)(pk + pl.wr64);
+    a.br = (const double*)(pk + pl.br64);
+    a.T = T;
+    a.d = D.d;
+    a.N = D.N;
+    a.G = D.G;
+    a.k = D.k;
+    a.n = D.n;
+    a.Np = (int)round_up(D.N, 16);
+    a.idx = idx;
+    a.wsel = wsel;
+    a.psel = psel;
+    a.ridx = route_idx;
+    a.rw = route_w;
+    const int fast = router_uses_mfma(D) ? 1 : 0;
+    if (km) km->begin(KT_ROUTER);
+    if (D.dtype == GQE_DTYPE_BF16) router_token_kernel<bf16_t><<<dim3((unsigned)T), 256, 0, st>>>(a, fast);
+    else router_token_kernel<float><<<dim3((unsigned)T), 256, 0, st>>>(a, fast);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (km) km->mark(KT_ROUTER);
+    return hipSuccess;
+}
 
 hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, const void* packed,
                          const PackedLayout& pl, char* ws, int32_t* route_idx, float* route_w,
