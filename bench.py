@@ -79,7 +79,7 @@ def source_hash(fname: str) -> str:
     return h.hexdigest()[:16]
 
 
-def committed_traffic(kernel: str, workload: str):
+def committed_traffic(kernel: str, workload: str, source: str | None = None):
     """HBM bytes per launch of ``kernel`` on ``workload`` from profiles/traffic_<kernel>_<workload>.md,
     if that summary was taken on the current source (its 'source hash' line matches)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
@@ -88,7 +88,8 @@ def committed_traffic(kernel: str, workload: str):
     text = open(path).read()
     m_hash = re.search(r"source hash:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"HBM bytes per launch \(scaled\):\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(KERNEL_SOURCES[kernel][0]):
+    src = source or KERNEL_SOURCES[kernel][0]
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(src):
         return None
     return float(m_bytes.group(1))
 
@@ -228,7 +229,8 @@ def decode_report(steps: int, warmup: int) -> dict:
                 tokens_s=batch / (ms / 1e3), kernel_ms=km,
                 roofline=dict(bound="hbm", kernel="decode_attention", achieved=gbs, peak=PEAK_HBM,
                               unit="GB/s", frac=gbs / PEAK_HBM, kernel_ms=km.get("decode_attention", 0.0),
-                              merge_ms=km.get("decode_merge", 0.0), algorithmic_bytes=a["attention_bytes"]),
+                              merge_ms=km.get("decode_merge", 0.0), algorithmic_bytes=a["attention_bytes"],
+                              traffic=committed_traffic("decode_attention", name, "k_decode.hip")),
                 gqa_ms_per_step=g_ms, gqa_kernel_ms=g_km, speedup_layer=g_ms / ms,
                 speedup_attention=g_att / att if att > 0 else None)
 
@@ -297,6 +299,8 @@ def main():
     if args.profile_workload in DECODE_WORKLOADS or (args.profile_workload or "")[:-4] in DECODE_WORKLOADS:
         name = args.profile_workload
         gqa = name.endswith("_gqa")
+        if args.copy_calibration:
+            copy_calibration()
         wl, _, _, ms, kernel_ms = run_decode(name[:-4] if gqa else name, args.steps, args.warmup, gqa=gqa)
         print(json.dumps({"workload": wl.name, "ms_per_step": ms, "kernel_ms": kernel_ms,
                           "source_hash": source_hash("k_decode.hip")}), flush=True)

@@ -39,6 +39,7 @@ namespace {
 
 constexpr int kTok = 8;     // tokens per projection / output-projection work group
 constexpr int kDC = 1024;   // hidden-dim chunk of the token rows staged in LDS by the projection
+constexpr int kOprojRows = 12; // output projection: weight rows per batch (two batches in flight)
 constexpr int kKeysPerThread = 8;  // attention: keys per thread (chunk = 256 / units x 8 keys)
 constexpr int kMaxH = GQE_DEC_MAX_HEADS;
 
@@ -77,14 +78,86 @@ __device__ __forceinline__ void widen16(const u32x4_t& u, float (&f)[4]) {
     for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(u[i]);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
+// Lane exchanges without LDS: DPP row permutations and the gfx950 row swaps.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// v[lane] + v[lane ^ 16] and v[lane] + v[lane ^ 32] (the swap of a register with itself)
+__device__ __forceinline__ float add_x16(float v) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float add_x32(float v) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float max_x16(float v) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float max_x32(float v) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+
+// Sum over each aligned group of S lanes (S a power of two, wave-uniform), in every lane of the
+// group, for NV values at once: xor 1 and xor 2 inside quads, then mirrors of groups that are
+// already uniform.  Each step is one uniform branch over all values.
+template <int NV>
+__device__ __forceinline__ void group_sum(float* v, int S) {
+    if (S >= 2)
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+        for (int i = 0; i < NV; ++i) v[i] += dpp<0xB1>(v[i]);  // quad_perm [1,0,3,2]
+    if (S >= 4)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] += dpp<0x4E>(v[i]);  // quad_perm [2,3,0,1]
+    if (S >= 8)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] += dpp<0x141>(v[i]);  // row_half_mirror
+    if (S >= 16)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] += dpp<0x140>(v[i]);  // row_mirror
+    if (S >= 32)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] = add_x16(v[i]);
+    if (S >= 64)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] = add_x32(v[i]);
+}
+// Sum over the lanes congruent modulo S (S a power of two, wave-uniform), in every lane, for NV
+// values: rotations by S, 2S, .. 8 inside each 16-lane row, then across rows.
+template <int NV>
+__device__ __forceinline__ void stride_sum(float* v, int S) {
+    if (S <= 1)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] += dpp<0x121>(v[i]);  // row_ror:1
+    if (S <= 2)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] += dpp<0x122>(v[i]);  // row_ror:2
+    if (S <= 4)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] += dpp<0x124>(v[i]);  // row_ror:4
+    if (S <= 8)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] += dpp<0x128>(v[i]);  // row_ror:8
+    if (S <= 16)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] = add_x16(v[i]);
+    if (S <= 32)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] = add_x32(v[i]);
+}
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    v = max_x16(v);
+    return max_x32(v);
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    group_sum<1>(&v, 64);
     return v;
 }
 
@@ -161,7 +234,7 @@ __device__ __forceinline__ u32x4_t load16(const void* p) { return *reinterpret_c
 // ... (RS = 256 / UP slices, UP = units per row rounded up to a power of two) against the staged
 // token rows; partial sums reduced over the slices by lane exchanges inside a wave, then across
 // the four waves in LDS.
-template <typename T>
+template <typename T, int RPT>
 __global__ void __launch_bounds__(256) dec_proj_kernel(DecArgs a) {
     constexpr int E = 16 / (int)sizeof(T);
     __shared__ float xs[kTok][kDC];
@@ -175,8 +248,6 @@ __global__ void __launch_bounds__(256) dec_proj_kernel(DecArgs a) {
     const bool is_exp = hb >= ebase;
     const int e = hb - ebase;
     const int g = is_exp ? e / a.n : (hb < G ? hb : hb - G);
-    const int ntok = token_group(a, is_exp && !a.dense, e, g, is_exp ? e % a.n : 0, tg, list, wcount);
-    if (ntok <= 0) return;  // uniform over the work group
 
     const T* W;
     int64_t rstride;
@@ -195,54 +266,57 @@ __global__ void __launch_bounds__(256) dec_proj_kernel(DecArgs a) {
     }
     const int U = dh / E;
     const int UP = a.up, RS = 256 / UP;
+    const int CH = RS * RPT;  // rows per chunk (the launcher keeps it <= kDC)
     const int u = tid & (UP - 1), rs = tid / UP;
     const bool uact = u < U;
+    const T* wbase = W + (uact ? u * E : 0);
+    // the weight rows of a chunk: all loads issued at once (rows past the end repeat the last)
+    u32x4_t wv[RPT];
+    auto issue = [&](int c0) {
+        const int nc = d - c0 < CH ? d - c0 : CH;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            int i = rs + RS * r;
+            i = i < nc ? i : nc - 1;
+            wv[r] = load16(wbase + (int64_t)(c0 + i) * rstride);
+        }
+    };
+    issue(0);  // independent of the tokens: in flight during the token selection
+    const int ntok = token_group(a, is_exp && !a.dense, e, g, is_exp ? e % a.n : 0, tg, list, wcount);
+    if (ntok <= 0) return;  // uniform over the work group
+
     float acc[kTok][E];
 #pragma unroll
     for (int t = 0; t < kTok; ++t)
 #pragma unroll
         for (int i = 0; i < E; ++i) acc[t][i] = 0.f;
     const T* X = (const T*)a.x;
-    for (int c0 = 0; c0 < d; c0 += kDC) {
-        const int nc = d - c0 < kDC ? d - c0 : kDC;
-        for (int i = tid; i < kTok * nc; i += 256) {
-            const int t = i / nc, c = i - t * nc;
-            xs[t][c] = t < ntok ? to_f32(X[(int64_t)(list[t] & 0xffffff) * d + c0 + c]) : 0.f;
+    for (int c0 = 0; c0 < d; c0 += CH) {
+        const int nc = d - c0 < CH ? d - c0 : CH;
+        for (int i = tid; i < kTok * CH; i += 256) {
+            const int t = i / CH, c = i - t * CH;
+            xs[t][c] = (t < ntok && c < nc) ? to_f32(X[(int64_t)(list[t] & 0xffffff) * d + c0 + c]) : 0.f;
         }
         __syncthreads();
         if (uact) {
-            const T* wp = W + (int64_t)c0 * rstride + u * E;
-            auto rowfma = [&](const u32x4_t& wv, int i) {
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                const int i = rs + RS * r;  // rows past nc meet zero token values
                 float f[E];
-                widen16(wv, f);
+                widen16(wv[r], f);
 #pragma unroll
                 for (int t = 0; t < kTok; ++t) {
                     const float xv = xs[t][i];
 #pragma unroll
                     for (int q = 0; q < E; ++q) acc[t][q] += xv * f[q];
                 }
-            };
-            int i = rs;
-            for (; i + 3 * RS < nc; i += 4 * RS) {
-                const u32x4_t w0 = load16(wp + (int64_t)i * rstride);
-                const u32x4_t w1 = load16(wp + (int64_t)(i + RS) * rstride);
-                const u32x4_t w2 = load16(wp + (int64_t)(i + 2 * RS) * rstride);
-                const u32x4_t w3 = load16(wp + (int64_t)(i + 3 * RS) * rstride);
-                rowfma(w0, i);
-                rowfma(w1, i + RS);
-                rowfma(w2, i + 2 * RS);
-                rowfma(w3, i + 3 * RS);
             }
-            for (; i < nc; i += RS) rowfma(load16(wp + (int64_t)i * rstride), i);
         }
         __syncthreads();
+        if (c0 + CH < d) issue(c0 + CH);
     }
     // sum over the row slices: inside the wave (lanes u, u + UP, ...), then over the waves
-    for (int off = UP; off < 64; off <<= 1)
-#pragma unroll
-        for (int t = 0; t < kTok; ++t)
-#pragma unroll
-            for (int q = 0; q < E; ++q) acc[t][q] += __shfl_xor(acc[t][q], off);
+    stride_sum<kTok * E>(&acc[0][0], UP);
     if (lane < UP && uact)
 #pragma unroll
         for (int t = 0; t < kTok; ++t)
@@ -336,11 +410,7 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecArgs a) {
             sc[h][r] = s;
         }
     }
-    for (int off = 1; off < UP; off <<= 1)
-#pragma unroll
-        for (int h = 0; h < MH; ++h)
-#pragma unroll
-            for (int r = 0; r < KPT; ++r) sc[h][r] += __shfl_xor(sc[h][r], off);
+    group_sum<MH * KPT>(&sc[0][0], UP);
     float mx[MH];
 #pragma unroll
     for (int h = 0; h < MH; ++h) {
@@ -383,11 +453,7 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecArgs a) {
 #pragma unroll
             for (int i = 0; i < E; ++i) o[h][i] += sc[h][r] * f[i];
     }
-    for (int off = UP; off < 64; off <<= 1)
-#pragma unroll
-        for (int h = 0; h < MH; ++h)
-#pragma unroll
-            for (int i = 0; i < E; ++i) o[h][i] += __shfl_xor(o[h][i], off);
+    stride_sum<MH * E>(&o[0][0], UP);
     if (lane < UP && uact)
 #pragma unroll
         for (int h = 0; h < MH; ++h)
@@ -437,12 +503,12 @@ __global__ void __launch_bounds__(64) dec_merge_kernel(DecArgs a) {
     for (int c = lane; c < nch; c += 64) M = fmaxf(M, base[c * cs + dh]);
     M = wave_max(M);
     float l = 0.f;
-    for (int c = lane; c < nch; c += 64) l += base[c * cs + dh + 1] * exp2f(base[c * cs + dh] - M);
+    for (int c = lane; c < nch; c += 64) l += base[c * cs + dh + 1] * __builtin_amdgcn_exp2f(base[c * cs + dh] - M);
     const float inv = 1.f / wave_sum(l);
     float o0 = 0.f, o1 = 0.f;
     for (int cb = 0; cb < nch; cb += 64) {
         const int c = cb + lane;
-        scl[lane] = c < nch ? exp2f(base[c * cs + dh] - M) * inv : 0.f;
+        scl[lane] = c < nch ? __builtin_amdgcn_exp2f(base[c * cs + dh] - M) * inv : 0.f;
         __syncthreads();
         const int n = nch - cb < 64 ? nch - cb : 64;
         const float* pc = base + cb * cs;
@@ -470,7 +536,7 @@ __global__ void __launch_bounds__(64) dec_merge_kernel(DecArgs a) {
 template <typename T>
 __global__ void __launch_bounds__(64) dec_oproj_kernel(DecArgs a) {
     constexpr int E = 16 / (int)sizeof(T);
-    __shared__ float vs[kTok][128];
+    __shared__ float vs[kTok][128 + kOprojRows];
     __shared__ int list[kTok];
     __shared__ int wcount[1];
     const int sm = blockIdx.x, tg = blockIdx.y, lane = threadIdx.x;
@@ -489,12 +555,30 @@ __global__ void __launch_bounds__(64) dec_oproj_kernel(DecArgs a) {
     } else {
         kind = 2;
     }
+    const int cu = blockIdx.z * 64 + lane;  // column unit
+    const bool cact = cu * E < d;
+    const T* W = kind == 0 ? (const T*)a.wo + (int64_t)e * dh * d
+                           : (kind == 1 ? (const T*)a.wor + (int64_t)g * dh * d : (const T*)a.wos);
+    const T* wp = W + (cact ? cu * E : 0);
+    // weight rows in batches of kOprojRows, the next batch in flight while one is used; the
+    // first is issued before the token selection (rows past d_h repeat the last)
+    constexpr int RB = kOprojRows;
+    u32x4_t wv[2][RB];
+    auto issue = [&](int buf, int j0) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const int j = j0 + i < dh ? j0 + i : dh - 1;
+            wv[buf][i] = load16(wp + (int64_t)j * d);
+        }
+    };
+    issue(0, 0);
     const int ntok = token_group(a, kind == 0 && !a.dense, e, g, kind == 0 ? e % a.n : 0, tg, list, wcount);
     if (ntok <= 0) return;
-    for (int i = lane; i < kTok * dh; i += 64) {
-        const int t = i / dh, jj = i - t * dh;
+    constexpr int VW = 128 + kOprojRows;  // slot vector row (zero past d_h)
+    for (int i = lane; i < kTok * VW; i += 64) {
+        const int t = i / VW, jj = i - t * VW;
         float v = 0.f;
-        if (t < ntok) {
+        if (t < ntok && jj < dh) {
             const int tk = list[t];
             const int b = tk & 0xffffff, r = tk >> 24;
             const float* o = a.od + (int64_t)b * a.H * dh;
@@ -508,38 +592,34 @@ __global__ void __launch_bounds__(64) dec_oproj_kernel(DecArgs a) {
                 v = o[nr * dh + jj];
             }
         }
-        vs[t][jj] = v;
+        vs[t][jj] = v;  // rows past d_h are zero
     }
     __syncthreads();
-    const int cu = blockIdx.z * 64 + lane;  // column unit
-    if (cu * E >= d) return;
-    const T* W = kind == 0 ? (const T*)a.wo + (int64_t)e * dh * d
-                           : (kind == 1 ? (const T*)a.wor + (int64_t)g * dh * d : (const T*)a.wos);
-    const T* wp = W + cu * E;
+    if (!cact) return;
     float acc[kTok][E];
 #pragma unroll
     for (int t = 0; t < kTok; ++t)
 #pragma unroll
         for (int q = 0; q < E; ++q) acc[t][q] = 0.f;
-    auto rowfma = [&](const u32x4_t& wv, int j) {
-        float f[E];
-        widen16(wv, f);
+    auto use = [&](const u32x4_t (&wb)[RB], int j0) {
 #pragma unroll
-        for (int t = 0; t < kTok; ++t) {
-            const float x = vs[t][j];
+        for (int i = 0; i < RB; ++i) {
+            float f[E];
+            widen16(wb[i], f);
 #pragma unroll
-            for (int q = 0; q < E; ++q) acc[t][q] += x * f[q];
+            for (int t = 0; t < kTok; ++t) {
+                const float x = vs[t][j0 + i];
+#pragma unroll
+                for (int q = 0; q < E; ++q) acc[t][q] += x * f[q];
+            }
         }
     };
-    int j = 0;
-    for (; j + 7 < dh; j += 8) {
-        u32x4_t wv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) wv[i] = load16(wp + (int64_t)(j + i) * d);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) rowfma(wv[i], j + i);
+    for (int j0 = 0; j0 < dh; j0 += 2 * RB) {
+        if (j0 + RB < dh) issue(1, j0 + RB);
+        use(wv[0], j0);
+        if (j0 + 2 * RB < dh) issue(0, j0 + 2 * RB);
+        if (j0 + RB < dh) use(wv[1], j0 + RB);
     }
-    for (; j < dh; ++j) rowfma(load16(wp + (int64_t)j * d), j);
     for (int t = 0; t < ntok; ++t) {
         const int tk = list[t];
         const int b = tk & 0xffffff, r = tk >> 24;
@@ -648,9 +728,17 @@ hipError_t launch_decode(const GqeDims& D, const DecodePlan& P, const gqe_weight
     hipError_t e;
     // projections of the new tokens (K/V into the cache)
     if (km) km->begin(KT_DEC_PROJ);
+    // weight rows per thread and chunk, all loaded at once: 24 (a chunk of 768 rows) with 8 or more
+    // units per d_h row, fewer with fewer units so that the staged chunk stays within kDC rows
     const dim3 gp((unsigned)(2 * D.G + D.s + D.N), tgroups);
-    if (bf) dec_proj_kernel<bf16_t><<<gp, 256, 0, st>>>(a);
-    else dec_proj_kernel<float><<<gp, 256, 0, st>>>(a);
+#define GQE_DEC_PROJ(R)                                             \
+    if (bf) dec_proj_kernel<bf16_t, R><<<gp, 256, 0, st>>>(a);     \
+    else dec_proj_kernel<float, R><<<gp, 256, 0, st>>>(a);
+    if (a.up >= 8) { GQE_DEC_PROJ(24) }
+    else if (a.up == 4) { GQE_DEC_PROJ(16) }
+    else if (a.up == 2) { GQE_DEC_PROJ(8) }
+    else { GQE_DEC_PROJ(4) }
+#undef GQE_DEC_PROJ
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (km) km->mark(KT_DEC_PROJ);
     // attention over the cache chunks, then the merge

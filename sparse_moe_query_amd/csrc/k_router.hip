@@ -278,15 +278,29 @@ __global__ void __launch_bounds__(256) router_token_kernel(RouterArgs a, int fas
     const int np = a.Np, nsl = 256 / np;  // Np in {16, 32, 48, 64}: 16 .. 5 slices
     const int e = tid % np, sl = tid / np;
     if (sl < nsl) {
-        const int len = (a.d + nsl - 1) / nsl;
-        const int i0 = sl * len, i1 = min(a.d, i0 + len);
         const Tin* xr = reinterpret_cast<const Tin*>(a.x) + t * a.d;
         double acc = 0.0;
         if (e < a.N) {
+            if (fast) {
+                // d % 64 == 0: octets sl, sl + nsl, ... of eight hidden values, one 16-byte load of
+                // x and the 64 contiguous bytes of the lane-ordered weights each
+                const int noct = a.d / 8;
+#pragma unroll 4
+                for (int oc = sl; oc < noct; oc += nsl) {
+                    double xv[8];
+                    widen8<Tin>(xr + 8 * oc, xv);
+                    const f64x4_t* wp = reinterpret_cast<const f64x4_t*>(a.wr + ((int64_t)oc * 16 + e) * 8);
+                    const f64x4_t w0 = wp[0], w1 = wp[1];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc = __builtin_fma(xv[q], w0[q], acc);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc = __builtin_fma(xv[4 + q], w1[q], acc);
+                }
+            } else {
+                const int len = (a.d + nsl - 1) / nsl;
+                const int i0 = sl * len, i1 = min(a.d, i0 + len);
 #pragma unroll 8
-            for (int i = i0; i < i1; ++i) {
-                const double w = fast ? a.wr[((int64_t)(i >> 3) * 16 + e) * 8 + (i & 7)] : a.wr[(int64_t)i * np + e];
-                acc = __builtin_fma((double)to_f32(xr[i]), w, acc);
+                for (int i = i0; i < i1; ++i) acc = __builtin_fma((double)to_f32(xr[i]), a.wr[(int64_t)i * np + e], acc);
             }
         }
         part[sl][e] = acc;
