@@ -36,6 +36,20 @@ def layer(cfg, B, S, x, w):
     Wk = np.asarray(w["w_k"], np.float64).reshape(d, G, dh)
     Wv = np.asarray(w["w_v"], np.float64).reshape(d, G, dh)
     Kx = np.einsum("td,dgh->tgh", x, Wk).reshape(B, S, G, dh)
+    base = float(getattr(cfg, "rope_base", 0.0) or 0.0)
+    if base > 0:
+        # rotary position embedding as complex multiplication: the pair (v[2i], v[2i+1]) is the
+        # complex number v[2i] + i v[2i+1], multiplied by exp(i m base^(-2i/dh))
+        pos = getattr(cfg, "pos0", 0) + np.arange(S)
+        rot = np.exp(1j * pos[:, None] * base ** (-np.arange(0, dh, 2) / dh))   # [S, dh/2]
+
+        def rope(v):  # v [B, S, heads, dh]
+            z = (v[..., 0::2] + 1j * v[..., 1::2]) * rot[None, :, None, :]
+            out = np.empty_like(v)
+            out[..., 0::2], out[..., 1::2] = z.real, z.imag
+            return out
+        Kx = rope(Kx)
+        q_all = rope(q_all.reshape(B, S, N, dh)).reshape(T, N, dh)
     Vx = np.einsum("td,dgh->tgh", x, Wv).reshape(B, S, G, dh)
     mask = np.tril(np.ones((S, S), bool))
 
@@ -74,6 +88,8 @@ def layer(cfg, B, S, x, w):
     q_s = o_s = None
     if cfg.shared_head:
         q_s = x @ np.asarray(w["w_q_shared"], np.float64)
+        if base > 0:
+            q_s = rope(q_s.reshape(B, S, 1, dh)).reshape(T, dh)
         o_s = attn(q_s.reshape(B, S, dh), cfg.shared_kv_group).reshape(T, dh)
         y += o_s @ np.asarray(w["w_o_shared"], np.float64)
     return dict(y=y, logits=logits, p=pf, idx=idx.astype(np.int32), w=wts, o_all=o_all,

@@ -37,8 +37,11 @@
  *  - weighted_concat: the selected expert's slot is scaled by its in-group softmax
  *    probability p (not renormalised).
  *  - the shared head (a flag, default on) attends to KV group shared_kv_group.
- *  - attention scale 1/sqrt(dh); causal mask keeps keys s' <= s; no positional
- *    encoding, no projection biases.
+ *  - attention scale 1/sqrt(dh); causal mask keeps keys s' <= s; no projection biases.
+ *    Positional encoding: none on the pages; optionally (rope_base > 0) the rotary position
+ *    embedding of RoFormer (Su et al., "RoFormer: Enhanced Transformer with Rotary Position
+ *    Embedding"), read with interleaved pairs: the pair (v[2i], v[2i+1]) of every query and
+ *    key head vector at position m is rotated by the angle m * rope_base^(-2i/dh).
  *  - aux loss (Switch style, [R] "Algorithm Overview", [T] "Training and Loss"):
  *    f_e = count_e/(T k), P_e = mean_t p[t,e], L_g = n * sum_{e in g} f_e P_e,
  *    aux = mean_g L_g; unscaled (the caller multiplies by 0.01, [R] "Usage").
@@ -57,7 +60,25 @@ typedef struct {
     int32_t variant;         /* 0 gqe, 1 weighted_concat, 2 hard_concat */
     int32_t shared_head;     /* 1 = one always-on shared query head */
     int32_t shared_kv_group; /* KV group the shared head reads */
+    int32_t pos0;            /* position of the first token of every sequence (normally 0) */
+    int32_t pad_;
+    double rope_base;        /* rotary position embedding base; 0 = no positional encoding */
 } oracle_cfg;
+
+/* Rotary position embedding of one head vector at position m (see the readings above):
+ * (v[2i], v[2i+1]) -> (v[2i] cos a - v[2i+1] sin a, v[2i] sin a + v[2i+1] cos a),
+ * a = m * base^(-2i/dh).  No-op when base == 0. */
+static void rope(double* v, int dh, int64_t m, double base)
+{
+    if (base <= 0.0) return;
+    for (int i = 0; i < dh / 2; ++i) {
+        const double a = (double)m * pow(base, -2.0 * i / dh);
+        const double c = cos(a), s = sin(a);
+        const double x0 = v[2 * i], x1 = v[2 * i + 1];
+        v[2 * i] = x0 * c - x1 * s;
+        v[2 * i + 1] = x0 * s + x1 * c;
+    }
+}
 
 /* ---------------------------------------------------------------------------------
  * Router, for one token: logits, in-group softmax, top-k, renormalised weights.
@@ -204,9 +225,10 @@ int gqe_oracle_bucket(const oracle_cfg* c, int64_t T, const int32_t* idx, int64_
  * Dense KV path ([R] "Algorithm Overview": all KV heads remain dense and unchanged;
  * [T] "Dense KV Path").  For every token and every group g:
  *   K[t][g][:] = x[t] @ Wk[:, g dh:(g+1) dh],  V likewise.   Wk, Wv: [d, G dh]
- * Output layout K, V: [T, G, dh].
+ * then, with the rotary embedding, K[t][g] rotated at position pos0 + t % S (S = tokens per
+ * sequence).  Output layout K, V: [T, G, dh].
  * --------------------------------------------------------------------------------- */
-int gqe_oracle_kv(const oracle_cfg* c, int64_t T, const double* x, const double* Wk,
+int gqe_oracle_kv(const oracle_cfg* c, int64_t T, int64_t S, const double* x, const double* Wk,
                   const double* Wv, double* K, double* V)
 {
     const int d = c->dim, G = c->num_kv_heads, dh = c->head_dim;
@@ -222,6 +244,7 @@ int gqe_oracle_kv(const oracle_cfg* c, int64_t T, const double* x, const double*
             K[t * W + col] = ak;
             V[t * W + col] = av;
         }
+        for (int g = 0; g < G; ++g) rope(K + t * W + (size_t)g * dh, dh, c->pos0 + t % S, c->rope_base);
     }
     return 0;
 }
@@ -262,6 +285,7 @@ static void attend(int s, int dh, int G, int g, const double* q, const double* K
  *  - routed queries: q_{g,r} = x[t] @ Wq[idx[g][r]]  (only the selected experts are
  *    computed: [R] "Algorithm Overview", only the active query-head computation);
  *  - shared query:   q_s = x[t] @ Wqs, always on ([R], [T] "Always-On Shared Head");
+ *  - with the rotary embedding, every query rotated at position pos0 + s;
  *  - each query attends causally to its group's dense K/V ([T] "Dense KV Path");
  *  - output construction by variant ([R] "Parameters"/"Ablations", [T] "Output
  *    Construction"):
@@ -301,6 +325,7 @@ static void token_output(const oracle_cfg* c, int s, const double* xt, const dou
                 for (int i = 0; i < d; ++i) a += xt[i] * Wq[((size_t)e * d + i) * dh + j];
                 q[j] = a;
             }
+            rope(q, dh, c->pos0 + s, c->rope_base);
             attend(s, dh, G, g, q, Kseq, Vseq, o);
             if (q_out) memcpy(q_out + (size_t)(g * k + r) * dh, q, sizeof(double) * dh);
             if (o_out) memcpy(o_out + (size_t)(g * k + r) * dh, o, sizeof(double) * dh);
@@ -328,6 +353,7 @@ static void token_output(const oracle_cfg* c, int s, const double* xt, const dou
             for (int i = 0; i < d; ++i) a += xt[i] * Wqs[(size_t)i * dh + j];
             q[j] = a;
         }
+        rope(q, dh, c->pos0 + s, c->rope_base);
         attend(s, dh, G, c->shared_kv_group, q, Kseq, Vseq, o);
         if (q_out) memcpy(q_out + (size_t)(G * k) * dh, q, sizeof(double) * dh);
         if (o_out) memcpy(o_out + (size_t)(G * k) * dh, o, sizeof(double) * dh);

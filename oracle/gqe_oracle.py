@@ -41,7 +41,7 @@ def build(force: bool = True) -> str:
 class _Cfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "dim", "num_query_experts", "num_kv_heads", "top_k", "head_dim", "variant",
-        "shared_head", "shared_kv_group")]
+        "shared_head", "shared_kv_group", "pos0", "pad_")] + [("rope_base", ctypes.c_double)]
 
 
 @dataclass(frozen=True)
@@ -54,6 +54,8 @@ class OracleConfig:
     variant: str = "gqe"
     shared_head: bool = True
     shared_kv_group: int = 0
+    rope_base: float = 0.0        # rotary position embedding base (RoFormer); 0 = none
+    pos0: int = 0                 # position of the first token of every sequence
 
     @property
     def dh(self) -> int:
@@ -69,7 +71,8 @@ class OracleConfig:
 
     def c(self) -> _Cfg:
         return _Cfg(self.dim, self.num_query_experts, self.num_kv_heads, self.top_k, self.dh,
-                    VARIANTS[self.variant], int(self.shared_head), self.shared_kv_group)
+                    VARIANTS[self.variant], int(self.shared_head), self.shared_kv_group, self.pos0, 0,
+                    float(self.rope_base))
 
 
 _lib = None
@@ -86,7 +89,7 @@ def _load():
         C = ctypes.POINTER(_Cfg)
         lib.gqe_oracle_router.argtypes = [C, I64, P, P, P, P, P, P, P, P]
         lib.gqe_oracle_aux.argtypes = [C, I64, P, P, P, P, P, P]
-        lib.gqe_oracle_kv.argtypes = [C, I64, P, P, P, P, P]
+        lib.gqe_oracle_kv.argtypes = [C, I64, I64, P, P, P, P, P]
         lib.gqe_oracle_bucket.argtypes = [C, I64, P, P, P, P]
         lib.gqe_oracle_rows.argtypes = [C, I64, I64, P, P, P, P, P, P, P, P, P, P, P, I64, P,
                                         P, P]
@@ -159,8 +162,9 @@ def aux(cfg: OracleConfig, p, idx) -> dict:
                 active_heads=int(heads[0]))
 
 
-def kv(cfg: OracleConfig, x, w_k, w_v):
-    """Dense K and V for every token: [T, G, dh] each."""
+def kv(cfg: OracleConfig, x, w_k, w_v, S: int | None = None):
+    """Dense K and V for every token: [T, G, dh] each (sequences of S tokens; S = T when None:
+    the positions matter only with the rotary embedding)."""
     lib = _load()
     x = _f64(x).reshape(-1, cfg.dim)
     T = x.shape[0]
@@ -168,8 +172,8 @@ def kv(cfg: OracleConfig, x, w_k, w_v):
     K = np.zeros((T, G, dh))
     V = np.zeros((T, G, dh))
     cc = cfg.c()
-    lib.gqe_oracle_kv(ctypes.byref(cc), T, _ptr(x), _ptr(_f64(w_k)), _ptr(_f64(w_v)), _ptr(K),
-                      _ptr(V))
+    lib.gqe_oracle_kv(ctypes.byref(cc), T, T if S is None else S, _ptr(x), _ptr(_f64(w_k)),
+                      _ptr(_f64(w_v)), _ptr(K), _ptr(V))
     return K, V
 
 
@@ -204,7 +208,7 @@ def forward(cfg: OracleConfig, B: int, S: int, x, w: dict, rows_list=None, want_
     r = router(cfg, x, w["w_router"], w.get("b_router"))
     idx = r["idx"] if idx_override is None else np.ascontiguousarray(idx_override, np.int32)
     st = aux(cfg, r["p"], idx)
-    K, V = kv(cfg, x, w["w_k"], w["w_v"])
+    K, V = kv(cfg, x, w["w_k"], w["w_v"], S)
     if rows_list is None:
         rows_list = np.arange(B * S)
     res = rows(cfg, B, S, x, r["p"], idx, w, K, V, rows_list, want_qo=want_qo)

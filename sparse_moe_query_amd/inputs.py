@@ -50,6 +50,7 @@ class Workload:
     router_std: float | None = None   # None -> 1/sqrt(dim) (logits ~ N(0, 1))
     router_bias_first: float = 0.0    # added to local expert 0 of every group
     dense_gqa: bool = False           # all-active GQA baseline on the same weights
+    rope_base: float = 0.0            # rotary position embedding base (0: none, as on the pages)
 
     @property
     def dh(self) -> int:

@@ -29,7 +29,7 @@ Y_STORAGE_U = {"f32": 0.0, "bf16": 2.0 ** -8}   # storage rounding of one output
 
 def oracle_cfg(wl) -> go.OracleConfig:
     return go.OracleConfig(wl.dim, wl.num_query_experts, wl.num_kv_heads, wl.top_k, wl.dh,
-                           wl.variant, wl.shared_head, wl.shared_kv_group)
+                           wl.variant, wl.shared_head, wl.shared_kv_group, wl.rope_base)
 
 
 def sample_rows(B: int, S: int, n: int = 48, seed: int = 0) -> np.ndarray:
@@ -124,7 +124,7 @@ def compare(wl, gpu: dict, inputs: dict, rows=None, want_qo=False) -> dict:
         assert gpu["active_heads"] == st["active_heads"]
         p = r["p"]
         rep["top1_share_local0"] = float(np.mean(r["idx"][:, :, 0] % n == 0))
-    K, V = go.kv(cfg, x64, inputs["w_k"], inputs["w_v"])
+    K, V = go.kv(cfg, x64, inputs["w_k"], inputs["w_v"], S)
     rows = np.arange(T) if rows is None else np.asarray(rows)
     res = go.rows(cfg, B, S, x64, p, idx_used, inputs, K, V, rows, want_qo=want_qo)
     y_ref = res[0] if want_qo else res

@@ -464,3 +464,59 @@ def test_decode_ignores_tokens_after_its_position():
     np.testing.assert_array_equal(got, ref)
     x2[1, 2] += 1.0   # a cached token of sequence 1 does change it
     assert np.any(go.decode(_cfg(wl), x2, w, pos)["y"][1] != ref[1])
+
+
+def _rope_cfg(wl, base, pos0=0):
+    c = _cfg(wl)
+    return go.OracleConfig(c.dim, c.num_query_experts, c.num_kv_heads, c.top_k, c.head_dim, c.variant,
+                           c.shared_head, c.shared_kv_group, rope_base=base, pos0=pos0)
+
+
+@pytest.mark.parametrize("variant,k,base", [("gqe", 1, 10000.0), ("weighted_concat", 2, 500.0),
+                                            ("hard_concat", 1, 10.0)])
+def test_rope_c_oracle_matches_complex_bruteforce(variant, k, base):
+    """Rotary embedding (RoFormer; not on the pages, optional): the C oracle's real 2x2 rotations
+    agree with the brute force's complex multiplications by exp(i m base^(-2i/dh))."""
+    wl = _wl(d=24, N=8, G=2, k=k, dh=8, B=2, S=11, variant=variant, rstd=0.8)
+    w = make_inputs(wl)
+    cfg = _rope_cfg(wl, base)
+    out = go.forward(cfg, wl.batch, wl.seq, w["x"], w)
+    bf = bruteforce.layer(cfg, wl.batch, wl.seq, w["x"], w)
+    np.testing.assert_allclose(out["y"], bf["y"], rtol=1e-10, atol=1e-12)
+    plain = go.forward(_cfg(wl), wl.batch, wl.seq, w["x"], w)
+    # the rotation is not a no-op
+    assert np.max(np.abs(out["y"] - plain["y"])) > 1e-2 * np.sqrt(np.mean(plain["y"] ** 2))
+
+
+def test_rope_depends_only_on_relative_positions():
+    """q_m . k_n after the rotation depends on m - n only (RoFormer's defining property), so moving
+    every position of a sequence by the same offset leaves the layer output unchanged."""
+    wl = _wl(d=24, N=4, G=2, k=1, dh=8, B=1, S=12, rstd=1.0)
+    w = make_inputs(wl)
+    ref = go.forward(_rope_cfg(wl, 10000.0), 1, wl.seq, w["x"], w)["y"]
+    for off in (1, 777, 40000):
+        got = go.forward(_rope_cfg(wl, 10000.0, pos0=off), 1, wl.seq, w["x"], w)["y"]
+        np.testing.assert_allclose(got, ref, rtol=1e-9, atol=1e-11)
+    got = go.forward(_rope_cfg(wl, 10000.0, pos0=5), 1, wl.seq, w["x"], w)["K"]
+    k0 = go.forward(_rope_cfg(wl, 10000.0), 1, wl.seq, w["x"], w)["K"]
+    assert np.max(np.abs(got - k0)) > 1e-2 * np.sqrt(np.mean(k0 ** 2))   # the keys themselves move
+
+
+def test_rope_at_position_zero_is_identity():
+    """Position 0 rotates by angle 0: a one-token sequence is the same with and without RoPE."""
+    wl = _wl(d=24, N=4, G=2, k=1, dh=8, B=3, S=1, rstd=1.0)
+    w = make_inputs(wl)
+    a = go.forward(_rope_cfg(wl, 10000.0), wl.batch, 1, w["x"], w)["y"]
+    b = go.forward(_cfg(wl), wl.batch, 1, w["x"], w)["y"]
+    np.testing.assert_array_equal(a, b)
+
+
+def test_rope_decode_is_last_row_of_prefix_bruteforce():
+    wl = _wl(d=24, N=8, G=2, k=2, dh=8, B=2, S=9, rstd=0.9)
+    w = make_inputs(wl)
+    cfg = _rope_cfg(wl, 10000.0)
+    pos = [4, 8]
+    dec = go.decode(cfg, w["x"], w, pos)
+    for b, p in enumerate(pos):
+        bf = bruteforce.layer(cfg, 1, p + 1, w["x"][b, :p + 1], w)
+        np.testing.assert_allclose(dec["y"][b], bf["y"][p], rtol=1e-10, atol=1e-12)
