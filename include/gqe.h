@@ -73,6 +73,12 @@ extern "C" {
  *  dense_gqa         0 = GQE.  1 = the all-active GQA baseline on the same kernels: every
  *                    expert is a head (requires top_k == N/G, hard_concat, shared_head == 0);
  *                    no router runs.
+ *  rope_base         0 = no positional encoding (the pages describe none).  > 0: the rotary
+ *                    position embedding of RoFormer (Su et al.) on every query and key head,
+ *                    interleaved pairs: (v[2i], v[2i+1]) at position m is rotated by the angle
+ *                    m * rope_base^(-2i/head_dim) (10000 is the usual base); head_dim must be even.
+ *                    Positions count from 0 at the first token of every sequence (gqe_forward) or
+ *                    are given per sequence (gqe_decode); the cache holds rotated keys.
  */
 typedef struct {
     int32_t dim;
@@ -86,6 +92,7 @@ typedef struct {
     int32_t dtype;
     int32_t causal;
     int32_t dense_gqa;
+    float rope_base;
 } gqe_config_t;
 
 /* ------------------------------------------------------------------ weights

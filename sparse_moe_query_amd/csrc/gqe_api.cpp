@@ -134,6 +134,7 @@ PackedLayout make_packed_layout(const GqeDims& D, bool mfma) {
     };
     L.wr64 = take((size_t)D.d * round_up(D.N, 16) * 8);
     L.br64 = take((size_t)D.N * 8);
+    L.rope = take(64 * 8);
     L.hb_total = 2 * D.G + D.s + D.N;
     const bool rslot = !D.dense && D.variant == GQE_VARIANT_GQE;
     L.slots = D.dense ? D.N : D.N + (rslot ? D.G : 0) + D.s;
@@ -236,6 +237,8 @@ int gqe_init(const gqe_config_t* cfg, const gqe_weights_t* w, gqe_handle_t** out
     *out = nullptr;
     const gqe_config_t& c = *cfg;
     if (c.dim <= 0) return fail(GQE_ERR_INVALID_CONFIG, "dim must be positive (got %d)", c.dim);
+    if (!(c.rope_base >= 0.f) || c.rope_base > 3.0e38f)
+        return fail(GQE_ERR_INVALID_CONFIG, "rope_base must be finite and >= 0 (0 = no rotary embedding)");
     if (c.num_query_experts <= 0 || c.num_kv_heads <= 0)
         return fail(GQE_ERR_INVALID_CONFIG, "num_query_experts and num_kv_heads must be positive");
     if (c.num_query_experts % c.num_kv_heads != 0)
@@ -258,6 +261,7 @@ int gqe_init(const gqe_config_t* cfg, const gqe_weights_t* w, gqe_handle_t** out
     if (c.causal != 1) return fail(GQE_ERR_UNSUPPORTED, "only causal prefill (causal = 1) is implemented");
     if (c.num_query_experts > 64) return fail(GQE_ERR_UNSUPPORTED, "num_query_experts > 64 is not supported");
     if (dh > 128) return fail(GQE_ERR_UNSUPPORTED, "head_dim > 128 is not supported");
+    if (c.rope_base > 0.f && dh % 2 != 0) return fail(GQE_ERR_INVALID_CONFIG, "rope_base > 0 needs an even head_dim");
 
     if (!c.dense_gqa && !w->w_router) return fail(GQE_ERR_NULL_POINTER, "w_router is required");
     if (!w->w_q || !w->w_k || !w->w_v || !w->w_o) return fail(GQE_ERR_NULL_POINTER, "w_q, w_k, w_v and w_o are required");
@@ -286,6 +290,7 @@ int gqe_init(const gqe_config_t* cfg, const gqe_weights_t* w, gqe_handle_t** out
     D.dtype = c.dtype;
     D.skv = c.shared_head ? c.shared_kv_group : 0;
     D.dense = c.dense_gqa;
+    D.rope = c.rope_base;
     h->mfma = mfma_supported(D);
     h->mfma_attn = D.dtype == GQE_DTYPE_BF16 && (dh == 32 || dh == 48 || dh == 64) && D.H <= 64;
     h->mfma_proj = h->mfma;
@@ -382,7 +387,8 @@ int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t 
     if (!D.dense) e = launch_router(D, P, x, h->packed, h->pl, ws, route_idx, route_w, st, km, !h->mfma_proj);
     if (e == hipSuccess)
         e = h->mfma_proj ? launch_proj_mfma(D, P, x, h->packed, h->pl, ws, st, km)
-                         : launch_proj_simple(D, P, h->w, x, ws, st, km);
+                         : launch_proj_simple(D, P, h->w, x, (const double*)((const char*)h->packed + h->pl.rope), ws, st,
+                                              km);
     if (e == hipSuccess && !h->mfma_proj && h->mfma_attn) e = launch_kn_simple(D, P, ws, st, km);
     if (e == hipSuccess)
         e = h->mfma_attn ? launch_attn_mfma(D, P, *sched, ws, st, km, !(h->mfma_proj && P.S % 64 == 0))
@@ -537,7 +543,9 @@ int gqe_decode(gqe_handle_t* h, const void* x, void* y, int64_t batch, const int
     if (!D.dense)
         e = launch_router_tokens(D, batch, x, h->packed, h->pl, (int32_t*)(ws + P.r.idx), (float*)(ws + P.r.wsel),
                                  (float*)(ws + P.r.psel), route_idx, route_w, st, km);
-    if (e == hipSuccess) e = launch_decode(D, P, h->w, x, y, pos, kcache, vcache, ws, st, km);
+    if (e == hipSuccess)
+        e = launch_decode(D, P, h->w, (const double*)((const char*)h->packed + h->pl.rope), x, y, pos, kcache, vcache,
+                          ws, st, km);
     if (e == hipSuccess && km && marks.err != hipSuccess) e = marks.err;
     if (e != hipSuccess) return fail(GQE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -55,6 +55,28 @@ __host__ __device__ __forceinline__ int64_t round_up(int64_t a, int64_t b) { ret
 
 #define GQE_KV_TILE 64  // keys per attention tile; K and V^T are padded to a multiple of this
 
+// Rotary position embedding of one pair (a, b) of a query or key head vector at position pos:
+// rotation by the angle 2 pi * pos * rev, where rev = base^(-2i/d_h) / (2 pi) is the pair's
+// frequency in cycles per position (float64 table written by gqe_pack_weights).  The cycle count
+// is reduced to [-1/2, 1/2] in float64, so the float32 hardware sine and cosine (argument in
+// cycles) see a small argument at any position.
+__device__ __forceinline__ void rope_pair(float& a, float& b, int64_t pos, double rev) {
+    double f = (double)pos * rev;
+    f -= __builtin_rint(f);
+    const float ff = (float)f;
+    const float sn = __builtin_amdgcn_sinf(ff), cs = __builtin_amdgcn_cosf(ff);
+    const float a0 = a, b0 = b;
+    a = a0 * cs - b0 * sn;
+    b = a0 * sn + b0 * cs;
+}
+// The two pairs (v0, v1), (v2, v3) of four consecutive head dims.
+__device__ __forceinline__ void rope_quad(f32x4_t& v, int64_t pos, double rev0, double rev1) {
+    float a = v[0], b = v[1], c = v[2], d = v[3];
+    rope_pair(a, b, pos, rev0);
+    rope_pair(c, d, pos, rev1);
+    v = f32x4_t{a, b, c, d};
+}
+
 // ---------------------------------------------------------------- direct global -> LDS loads
 // One wave-wide global_load_lds_dwordx4: lane i's 16 bytes from gsrc land in LDS at
 // ldst + 16 i (ldst wave-uniform).  Written as inline assembly so that the compiler does not

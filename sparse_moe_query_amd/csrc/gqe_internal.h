@@ -18,6 +18,7 @@
 struct GqeDims {
     int d, N, G, k, n, dh, H, s;  // s = shared head on; H = active heads per token
     int variant, dtype, skv, dense;
+    float rope;                   // rotary embedding base (0: none)
 };
 
 // Byte offsets into the caller's packed-weights buffer.
@@ -25,6 +26,7 @@ struct PackedLayout {
     size_t wr64, br64;   // router weights in float64 (d x N rounded up to 16) and biases
     size_t wproj;        // bf16 path: head blocks [HB][dh][d] (K_g, V_g, shared Q, W_q[e])
     size_t wo;           // bf16 path: stacked output projection as per-(column tile, slot) stages
+    size_t rope;         // rotary embedding frequencies [64] f64, cycles per position (0 when off)
     size_t total;
     int hb_total;        // number of projection head blocks
     int slots;           // output-projection slots (expert slots, renormalised slots, shared)
@@ -149,7 +151,7 @@ hipError_t launch_router_tokens(const GqeDims& D, int64_t T, const void* x, cons
                                 const PackedLayout& pl, int32_t* idx, float* wsel, float* psel, int32_t* route_idx,
                                 float* route_w, hipStream_t st, KernelMarks* km);
 hipError_t launch_proj_simple(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w,
-                              const void* x, char* ws, hipStream_t st, KernelMarks* km);
+                              const void* x, const double* rope, char* ws, hipStream_t st, KernelMarks* km);
 hipError_t launch_attn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km);
 hipError_t launch_combine_simple(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w,
                                  void* y, char* ws, hipStream_t st, KernelMarks* km);
@@ -162,8 +164,9 @@ int decode_units(const GqeDims& D);
 int decode_chunk(const GqeDims& D);
 hipError_t launch_kv_export(const GqeDims& D, const WorkPlan& P, const char* ws, void* kc, void* vc, int64_t s_max,
                             int64_t b0, hipStream_t st);
-hipError_t launch_decode(const GqeDims& D, const DecodePlan& P, const gqe_weights_t& w, const void* x, void* y,
-                         const int32_t* pos, void* kc, void* vc, char* ws, hipStream_t st, KernelMarks* km);
+hipError_t launch_decode(const GqeDims& D, const DecodePlan& P, const gqe_weights_t& w, const double* rope,
+                         const void* x, void* y, const int32_t* pos, void* kc, void* vc, char* ws, hipStream_t st,
+                         KernelMarks* km);
 hipError_t launch_bucket(const GqeDims& D, const WorkPlan& P, char* ws, int32_t* offs, int32_t* perm, int32_t* inv,
                          hipStream_t st);
 bool combine_mfma_supported(const GqeDims& D);

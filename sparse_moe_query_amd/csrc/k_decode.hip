@@ -61,6 +61,7 @@ struct DecArgs {
     int B, d, N, G, k, n, dh, H, s, skv, variant, dense, NC, MH, C, NS;
     int up;        // 16-byte units of a d_h row, rounded up to a power of two
     float qscale;
+    const double* rope;  // rotary embedding frequencies (cycles per position), or null when off
 };
 
 __device__ __forceinline__ bool pos_ok(int p, int64_t s_max) { return p >= 0 && (int64_t)p < s_max; }
@@ -323,11 +324,19 @@ __global__ void __launch_bounds__(256) dec_proj_kernel(DecArgs a) {
 #pragma unroll
             for (int q = 0; q < E; ++q) wacc[w][t][u * E + q] = acc[t][q];
     __syncthreads();
+    const bool rot = a.rope != nullptr && (hb < G || hb >= 2 * G);  // queries and keys
     for (int o = tid; o < ntok * dh; o += 256) {
         const int t = o / dh, jj = o - t * dh;
-        const float v = (wacc[0][t][jj] + wacc[1][t][jj]) + (wacc[2][t][jj] + wacc[3][t][jj]);
+        float v = (wacc[0][t][jj] + wacc[1][t][jj]) + (wacc[2][t][jj] + wacc[3][t][jj]);
         const int tk = list[t];
         const int b = tk & 0xffffff, rank = tk >> 24;
+        if (rot) {
+            const int jp = jj ^ 1;  // pair partner
+            const float vp = (wacc[0][t][jp] + wacc[1][t][jp]) + (wacc[2][t][jp] + wacc[3][t][jp]);
+            float lo = (jj & 1) ? vp : v, hi = (jj & 1) ? v : vp;
+            rope_pair(lo, hi, a.pos[b], a.rope[jj >> 1]);
+            v = (jj & 1) ? hi : lo;
+        }
         if (hb < 2 * G) {
             const int p = a.pos[b];
             if (!pos_ok(p, a.s_max)) continue;
@@ -682,9 +691,11 @@ hipError_t launch_kv_export(const GqeDims& D, const WorkPlan& P, const char* ws,
     return hipGetLastError();
 }
 
-hipError_t launch_decode(const GqeDims& D, const DecodePlan& P, const gqe_weights_t& w, const void* x, void* y,
-                         const int32_t* pos, void* kc, void* vc, char* ws, hipStream_t st, KernelMarks* km) {
+hipError_t launch_decode(const GqeDims& D, const DecodePlan& P, const gqe_weights_t& w, const double* rope,
+                         const void* x, void* y, const int32_t* pos, void* kc, void* vc, char* ws, hipStream_t st,
+                         KernelMarks* km) {
     DecArgs a{};
+    a.rope = D.rope > 0.f ? rope : nullptr;
     a.x = x;
     a.y = y;
     a.pos = pos;

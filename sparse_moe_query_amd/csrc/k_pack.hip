@@ -107,6 +107,12 @@ __global__ void pack_wo_kernel(const uint16_t* __restrict__ wo, const uint16_t* 
     }
 }
 
+// Rotary embedding frequencies in cycles per position: rev[i] = base^(-2i/d_h) / (2 pi), float64.
+__global__ void rope_table_kernel(double base, int dh, double* __restrict__ rev) {
+    const int i = threadIdx.x;
+    if (i < 64) rev[i] = (base > 0.0 && 2 * i < dh) ? pow(base, -2.0 * i / dh) / 6.283185307179586476925 : 0.0;
+}
+
 }  // namespace
 
 hipError_t launch_pack(const GqeDims& D, const gqe_weights_t& w, const PackedLayout& pl,
@@ -118,6 +124,9 @@ hipError_t launch_pack(const GqeDims& D, const gqe_weights_t& w, const PackedLay
         w.w_router, w.b_router, D.d, D.N, Np, router_uses_mfma(D) ? 1 : 0, (double*)(pk + pl.wr64),
         (double*)(pk + pl.br64));
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    rope_table_kernel<<<1, 64, 0, st>>>((double)D.rope, D.dh, (double*)(pk + pl.rope));
+    e = hipGetLastError();
     if (e != hipSuccess || !mfma) return e;
     pack_proj_kernel<<<1024, 256, 0, st>>>((const uint16_t*)w.w_k, (const uint16_t*)w.w_v,
                                            (const uint16_t*)w.w_q_shared, (const uint16_t*)w.w_q,

@@ -40,6 +40,7 @@ struct ProjArgs {
     float* kn;             // [B][G][S_pad] key norms
     float* knt;            // [B][G][S_pad / 64] largest key norm per 64-key tile (when knt_here)
     float qscale;          // log2(e) / sqrt(d_h): queries are stored pre-scaled
+    const double* rope;    // rotary embedding frequencies (cycles per position), or null when off
     int64_t T, S, S_pad;
     int d, G, k, n, H, s, dense, HB, njobs, ntiles;
     int knt_here;          // S % 64 == 0: every 64-key tile is one half of a 128-token tile
@@ -202,6 +203,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
     auto epilogue = [&](f32x4_t (&acc)[8][DH / 16], const int (&myrow)[8], int nrows, int nrb) {
         const uint32_t S = (uint32_t)a.S;  // the host limits a call to 2^28 tokens
         float kmx[2] = {0.f, 0.f};  // K blocks: largest squared norm of each 64-token half
+        // rotary embedding of query and key blocks: this lane's pairs are head dims
+        // 16 cb + 4 (lane >> 4) + {0, 1} and {2, 3}, i.e. pairs 8 cb + 2 (lane >> 4) + {0, 1}
+        const bool rot = a.rope != nullptr && !is_v;
+        double rev[DH / 16][2];
+#pragma unroll
+        for (int cb = 0; cb < DH / 16; ++cb)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) rev[cb][p] = rot ? a.rope[8 * cb + 2 * (lane >> 4) + p] : 0.0;
     #pragma unroll
         for (int rb = 0; rb < 8; ++rb) {
             if (rb >= nrb) continue;
@@ -220,6 +229,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
                 ss += __shfl_xor(ss, 16);
                 ss += __shfl_xor(ss, 32);
                 if (!ok) continue;
+                if (rot)
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) rope_quad(acc[rb][cb], sp, rev[cb][0], rev[cb][1]);
                 kmx[rb >> 2] = __builtin_fmaxf(kmx[rb >> 2], ss);
                 if ((lane >> 4) == 0) a.kn[((int64_t)b * a.G + hb) * a.S_pad + sp] = sqrtf(ss);
                 bf16_t* dst = a.K + (((int64_t)b * a.G + hb) * a.S_pad + sp) * DH;
@@ -250,6 +262,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
             if (!is_expert) dst = a.Q + (((int64_t)b * a.H + a.G * a.k) * S + sp) * DH;  // shared head
             else dst = a.Q + (((int64_t)b * a.H + g_of * a.k + rank) * S + sp) * DH;
             const float qs = a.qscale;
+            if (rot)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) rope_quad(acc[rb][cb], sp, rev[cb][0], rev[cb][1]);
     #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
                 const f32x4_t v = acc[rb][cb] * qs;
@@ -312,6 +327,7 @@ hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x, 
     a.stats = ws + P.stats;
     a.nblk_router = P.nblk_router;
     a.qscale = (float)(1.4426950408889634 / std::sqrt((double)D.dh));
+    a.rope = D.rope > 0.f ? (const double*)((const char*)packed + pl.rope) : nullptr;
     a.T = P.T;
     a.S = P.S;
     a.S_pad = P.S_pad;

@@ -16,10 +16,12 @@ struct Args {
 
 // Projections (GQE README "Algorithm Overview": dense, unchanged K/V for every group; only the
 // selected query heads are computed; plus the always-on shared query head).
+// With the rotary embedding each query / key element also computes its pair partner (j ^ 1).
 template <typename T>
 __global__ void proj_simple_kernel(Args a, const T* __restrict__ x, const T* __restrict__ wk,
                                    const T* __restrict__ wv, const T* __restrict__ wqs,
                                    const T* __restrict__ wq, const int32_t* __restrict__ idx,
+                                   const double* __restrict__ rope, int use_rope,
                                    T* __restrict__ Q, T* __restrict__ K, T* __restrict__ Vt) {
     const int64_t C = (int64_t)(2 * a.G + a.s + a.G * a.k) * a.dh;
     const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -35,6 +37,13 @@ __global__ void proj_simple_kernel(Args a, const T* __restrict__ x, const T* __r
         const int cc = c % GD;
         for (int i = 0; i < a.d; ++i) acc += to_f32(xr[i]) * to_f32(w[(int64_t)i * GD + cc]);
         const int g = cc / a.dh, j = cc % a.dh;
+        if (c < GD && use_rope) {
+            float pr = 0.f;
+            for (int i = 0; i < a.d; ++i) pr += to_f32(xr[i]) * to_f32(w[(int64_t)i * GD + (cc ^ 1)]);
+            float lo = (j & 1) ? pr : acc, hi = (j & 1) ? acc : pr;
+            rope_pair(lo, hi, s, rope[j >> 1]);
+            acc = (j & 1) ? hi : lo;
+        }
         if (c < GD) K[((b * a.G + g) * a.S_pad + s) * a.dh + j] = from_f32<T>(acc);
         else Vt[((b * a.G + g) * a.dh + j) * a.S_pad + vt_pos(s)] = from_f32<T>(acc);
         return;
@@ -55,6 +64,13 @@ __global__ void proj_simple_kernel(Args a, const T* __restrict__ x, const T* __r
         w = wq + (int64_t)e * a.d * a.dh;
     }
     for (int i = 0; i < a.d; ++i) acc += to_f32(xr[i]) * to_f32(w[(int64_t)i * a.dh + j]);
+    if (use_rope) {
+        float pr = 0.f;
+        for (int i = 0; i < a.d; ++i) pr += to_f32(xr[i]) * to_f32(w[(int64_t)i * a.dh + (j ^ 1)]);
+        float lo = (j & 1) ? pr : acc, hi = (j & 1) ? acc : pr;
+        rope_pair(lo, hi, s, rope[j >> 1]);
+        acc = (j & 1) ? hi : lo;
+    }
     // stored pre-scaled by log2(e)/sqrt(d_h): the attention works in log2 units
     Q[((b * a.H + v) * a.S + s) * a.dh + j] = from_f32<T>(acc * (1.44269504088896341f / sqrtf((float)a.dh)));
 }
@@ -155,13 +171,14 @@ Args make_args(const GqeDims& D, const WorkPlan& P) {
 }
 
 template <typename T>
-hipError_t proj(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w, const void* x, char* ws,
-                hipStream_t st) {
+hipError_t proj(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w, const void* x, const double* rope,
+                char* ws, hipStream_t st) {
     const Args a = make_args<T>(D, P);
     const int64_t C = (int64_t)(2 * D.G + D.s + D.G * D.k) * D.dh;
     proj_simple_kernel<T><<<(unsigned)ceil_div(P.T * C, 256), 256, 0, st>>>(
         a, (const T*)x, (const T*)w.w_k, (const T*)w.w_v, (const T*)w.w_q_shared, (const T*)w.w_q,
-        (const int32_t*)(ws + P.idx), (T*)(ws + P.q), (T*)(ws + P.kk), (T*)(ws + P.vt));
+        (const int32_t*)(ws + P.idx), rope, D.rope > 0.f ? 1 : 0, (T*)(ws + P.q), (T*)(ws + P.kk),
+        (T*)(ws + P.vt));
     return hipGetLastError();
 }
 
@@ -186,9 +203,10 @@ hipError_t combine(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w, 
 }  // namespace
 
 hipError_t launch_proj_simple(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w, const void* x,
-                              char* ws, hipStream_t st, KernelMarks* km) {
+                              const double* rope, char* ws, hipStream_t st, KernelMarks* km) {
     if (km) km->begin(KT_PROJ);
-    const hipError_t e = D.dtype == GQE_DTYPE_BF16 ? proj<bf16_t>(D, P, w, x, ws, st) : proj<float>(D, P, w, x, ws, st);
+    const hipError_t e = D.dtype == GQE_DTYPE_BF16 ? proj<bf16_t>(D, P, w, x, rope, ws, st)
+                                                   : proj<float>(D, P, w, x, rope, ws, st);
     if (km) km->mark(KT_PROJ);
     return e;
 }

@@ -42,7 +42,7 @@ class GqeError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "dim", "num_query_experts", "num_kv_heads", "top_k", "head_dim", "variant",
-        "shared_head", "shared_kv_group", "dtype", "causal", "dense_gqa")]
+        "shared_head", "shared_kv_group", "dtype", "causal", "dense_gqa")] + [("rope_base", ctypes.c_float)]
 
 
 class Weights(ctypes.Structure):
@@ -230,7 +230,7 @@ class GQEAttention:
     def __init__(self, dim: int, num_query_experts: int = 16, num_kv_heads: int = 8,
                  top_k: int = 1, head_dim: int | None = None, variant: str = "gqe",
                  shared_head: bool = True, shared_kv_group: int = 0, dtype: str = "bf16",
-                 dense_gqa: bool = False, weights: dict | None = None, stream=None):
+                 dense_gqa: bool = False, weights: dict | None = None, stream=None, rope_base: float = 0.0):
         if weights is None:
             raise ValueError("weights (device tensors) are required")
         self.dtype = dtype
@@ -240,7 +240,7 @@ class GQEAttention:
         self.dim = dim
         self.cfg = Config(dim, num_query_experts, num_kv_heads, top_k, head_dim or 0,
                           VARIANTS[variant], int(shared_head), shared_kv_group, DTYPES[dtype], 1,
-                          int(dense_gqa))
+                          int(dense_gqa), float(rope_base))
         self._w = {k: weights.get(k) for k in self.WEIGHT_KEYS}   # keep alive
         self.weights = Weights(*[_ptr(self._w[k]) for k in self.WEIGHT_KEYS])
         self.h = gqe_init(self.cfg, self.weights)

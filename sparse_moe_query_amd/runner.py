@@ -23,7 +23,7 @@ def build_layer(wl: Workload, inputs: dict | None = None, device: str = "cuda:0"
         w["w_o_rslot"] = None
     layer = GQEAttention(wl.dim, wl.num_query_experts, wl.num_kv_heads, wl.top_k, wl.head_dim,
                          wl.variant, wl.shared_head, wl.shared_kv_group, wl.dtype, wl.dense_gqa,
-                         weights=w)
+                         weights=w, rope_base=wl.rope_base)
     x = torch.from_numpy(np.ascontiguousarray(inputs["x"])).to(device=device,
                                                                dtype=TORCH_DTYPES[wl.dtype])
     return layer, x, inputs

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def _cfg(**kw):
     base = dict(dim=768, num_query_experts=16, num_kv_heads=8, top_k=1, head_dim=0, variant=0,
-                shared_head=1, shared_kv_group=0, dtype=1, causal=1, dense_gqa=0)
+                shared_head=1, shared_kv_group=0, dtype=1, causal=1, dense_gqa=0, rope_base=0.0)
     base.update(kw)
     return gqe.Config(*[base[f] for f, _ in gqe.Config._fields_])
 
@@ -59,6 +59,9 @@ def _weights(**kw):
     (dict(dense_gqa=1), -1, "dense_gqa"),
     (dict(num_query_experts=128, num_kv_heads=8), -4, "64"),
     (dict(head_dim=256), -4, "head_dim"),
+    (dict(rope_base=-1.0), -1, "rope_base"),
+    (dict(rope_base=float("nan")), -1, "rope_base"),
+    (dict(rope_base=10000.0, dim=420, num_query_experts=12, num_kv_heads=4, head_dim=35), -1, "even"),
 ])
 def test_init_rejects_bad_configs(kw, code, msg):
     with pytest.raises(gqe.GqeError) as e:

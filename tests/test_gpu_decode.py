@@ -131,3 +131,18 @@ def test_decode_deterministic_and_invalid_positions():
     inp1["x"] = inp["x"][:1]
     parity.compare_decode(wl.with_(batch=1), y1[:1].float().cpu().numpy().astype(np.float64),
                           ridx[:1].cpu().numpy(), rw[:1].cpu().numpy(), inp1, [50])
+
+
+ROPE_CASES = [
+    (_wl("dec_rope_main", rope_base=10000.0, seed=30), [0, 63, 257, 300], 2, 320),
+    (_wl("dec_rope_k2", d=1024, k=2, dh=64, B=2, S=600, rope_base=10000.0, seed=31), [300, 555], 2, 600),
+    (Workload("dec_rope_f32", 64, 4, 2, 1, 16, 2, 40, dtype="f32", router_std=0.02, rope_base=500.0, seed=32),
+     [5, 30], 2, 40),
+]
+
+
+@pytest.mark.parametrize("wl,lens,steps,s_max", ROPE_CASES, ids=[c[0].name for c in ROPE_CASES])
+def test_decode_rope_matches_oracle(wl, lens, steps, s_max):
+    """Rotary embedding in decode: the new key is rotated at its position before it is cached; the
+    cached keys come rotated from the forward pass."""
+    _decode_steps(wl, lens, steps, s_max)

@@ -208,3 +208,25 @@ def test_full_size_sampled(wl):
           f"near_ties={rep['near_ties']}, top1 share of local expert 0="
           f"{rep.get('top1_share_local0', float('nan')):.3f}", flush=True)
     sys.stdout.flush()
+
+
+ROPE = [
+    _small("rope_main_ragged", B=2, S=200, rope_base=10000.0, seed=20),
+    _small("rope_k2_dh64", d=1024, k=2, dh=64, B=1, S=333, rope_base=10000.0, seed=21,
+           router_std=2.70 / 32.0, router_bias_first=2.0),
+    _small("rope_dh32_weighted", d=384, N=8, G=4, k=1, dh=32, B=2, S=130, variant="weighted_concat",
+           rope_base=500.0, seed=22),
+    _small("rope_f32_scalar", d=64, N=4, G=2, k=1, dh=16, B=1, S=70, dtype="f32", router_std=0.3,
+           rope_base=10000.0, seed=23),
+    _small("rope_gqa", B=1, S=150, k=2, variant="hard_concat", shared_head=False, dense_gqa=True,
+           rope_base=10000.0, seed=24),
+    # long positions: angles of thousands of radians per pair
+    _small("rope_long_s3000", B=1, S=3000, rope_base=10000.0, seed=25),
+]
+
+
+@pytest.mark.parametrize("wl", ROPE, ids=[w.name for w in ROPE])
+def test_rope_parity(wl):
+    """Optional rotary position embedding: every token against the oracle (rotation in float64)."""
+    rows = None if wl.tokens <= 1000 else parity.sample_rows(wl.batch, wl.seq, n=96, seed=3)
+    _run(wl, rows=rows)
