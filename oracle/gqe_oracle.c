@@ -394,3 +394,263 @@ int gqe_oracle_rows(const oracle_cfg* c, int64_t B, int64_t S, const double* x,
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------------------------
+ * Backward pass: gradients of  L = sum_t dy[t] . y[t] + aux_coef * aux  with respect to x and
+ * every weight, the routing decisions idx held fixed (top-k is piecewise constant; the loss
+ * of the README's "Usage" adds 0.01 * aux).  Each step is the chain rule applied to the
+ * forward definition above, in reverse order:
+ *  output construction   y += c o W_o[e]:  dW_o[e] += c o^T dy,  do += c dy W_o[e]^T;
+ *                        weighted_concat (c = p_e): dp_e += o . (dy W_o[e]^T)
+ *                        gqe slot y += (sum_r w_r o_r) W_oR[g]:  dW_oR[g] += slot^T dy,
+ *                        do_r += w_r dy W_oR[g]^T,  dw_r = o_r . (dy W_oR[g]^T)
+ *                        shared head y += o_s W_os:  dW_os += o_s^T dy,  do_s = dy W_os^T
+ *  renormalisation       w_r = p_r / P, P = sum_sel p:  dp_r += (dw_r - sum_r' w_r' dw_r') / P
+ *  aux loss              aux = (1/G) sum_g n sum_e f_e P_e, P_e = (1/T) sum_t p[t,e], f_e a
+ *                        count (constant):  dp[t,e] += aux_coef n f_e / (G T)
+ *  in-group softmax      dl_e = p_e (dp_e - sum_{e' in g} p_e' dp_e')
+ *  router logits         dW_r += x^T dl,  db_r += dl,  dx += dl W_r^T
+ *  attention             a_j = softmax_j(q . k_j / sqrt(dh)), j <= s:  dv_j += a_j do,
+ *                        dz_j = a_j (do . v_j - do . o),  dq = sum_j dz_j k_j / sqrt(dh),
+ *                        dk_j += dz_j q / sqrt(dh)
+ *  rotary embedding      orthogonal rotation: the gradient is rotated back (angle -m theta)
+ *  projections           dW_q[e] += x^T dq,  dx += dq W_q[e]^T;  likewise W_qs, W_k, W_v.
+ * Every gradient output is overwritten (dWqs / dWos may be NULL without the shared head,
+ * dWoR without the gqe slot).  Single-threaded: the key and value gradients of a token
+ * collect contributions from all later tokens.  Small shapes only.
+ * --------------------------------------------------------------------------------- */
+int gqe_oracle_backward(const oracle_cfg* c, int64_t B, int64_t S, const double* x,
+                        const double* Wr, const double* br, const double* Wq, const double* Wqs,
+                        const double* Wk, const double* Wv, const double* Wo, const double* WoR,
+                        const double* Wos, const int32_t* idx, const double* dy, double aux_coef,
+                        double* dx, double* dWr, double* dbr, double* dWq, double* dWqs,
+                        double* dWk, double* dWv, double* dWo, double* dWoR, double* dWos)
+{
+    const int d = c->dim, N = c->num_query_experts, G = c->num_kv_heads, k = c->top_k;
+    const int n = N / G, dh = c->head_dim, W = G * dh;
+    const int sh = c->shared_head ? 1 : 0, H = G * k + sh;
+    const int64_t T = B * S;
+    const double scale = 1.0 / sqrt((double)dh);
+    if (N <= 0 || G <= 0 || N % G != 0 || k < 1 || k > n || n > 64) return -1;
+
+    memset(dx, 0, sizeof(double) * T * d);
+    memset(dWr, 0, sizeof(double) * d * N);
+    memset(dbr, 0, sizeof(double) * N);
+    memset(dWq, 0, sizeof(double) * N * d * dh);
+    memset(dWk, 0, sizeof(double) * d * W);
+    memset(dWv, 0, sizeof(double) * d * W);
+    memset(dWo, 0, sizeof(double) * N * dh * d);
+    if (dWqs) memset(dWqs, 0, sizeof(double) * d * dh);
+    if (dWos) memset(dWos, 0, sizeof(double) * dh * d);
+    if (dWoR) memset(dWoR, 0, sizeof(double) * G * dh * d);
+
+    /* ---- forward quantities: router probabilities, K/V, per-head queries, attention weights, outputs */
+    double* logits = (double*)malloc(sizeof(double) * N);
+    double* p = (double*)malloc(sizeof(double) * T * N);
+    int32_t* tidx = (int32_t*)malloc(sizeof(int32_t) * G * k);
+    double* tw = (double*)malloc(sizeof(double) * G * k);
+    double* tgap = (double*)malloc(sizeof(double) * G);
+    for (int64_t t = 0; t < T; ++t) router_token(c, x + t * d, Wr, br, logits, p + t * N, tidx, tw, tgap);
+    double* K = (double*)malloc(sizeof(double) * T * W);
+    double* V = (double*)malloc(sizeof(double) * T * W);
+    gqe_oracle_kv(c, T, S, x, Wk, Wv, K, V);
+    double* q = (double*)calloc((size_t)T * H * dh, sizeof(double));
+    double* o = (double*)calloc((size_t)T * H * dh, sizeof(double));
+    double* a = (double*)calloc((size_t)T * H * S, sizeof(double));   /* a[t][h][j], j <= s */
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t b = t / S, s = t % S;
+        for (int h = 0; h < H; ++h) {
+            const int routed = h < G * k;
+            const int g = routed ? h / k : c->shared_kv_group;
+            const int e = routed ? idx[t * G * k + h] : -1;
+            double* qh = q + ((size_t)t * H + h) * dh;
+            for (int j = 0; j < dh; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < d; ++i)
+                    acc += x[t * d + i] * (routed ? Wq[((size_t)e * d + i) * dh + j] : Wqs[(size_t)i * dh + j]);
+                qh[j] = acc;
+            }
+            rope(qh, dh, c->pos0 + s, c->rope_base);
+            double* ah = a + ((size_t)t * H + h) * S;
+            double m = -INFINITY;
+            for (int64_t js = 0; js <= s; ++js) {
+                const double* kj = K + (size_t)(b * S + js) * W + (size_t)g * dh;
+                double sc = 0.0;
+                for (int i = 0; i < dh; ++i) sc += qh[i] * kj[i];
+                ah[js] = sc * scale;
+                if (ah[js] > m) m = ah[js];
+            }
+            double den = 0.0;
+            for (int64_t js = 0; js <= s; ++js) { ah[js] = exp(ah[js] - m); den += ah[js]; }
+            for (int64_t js = 0; js <= s; ++js) ah[js] /= den;
+            double* oh = o + ((size_t)t * H + h) * dh;
+            for (int64_t js = 0; js <= s; ++js) {
+                const double* vj = V + (size_t)(b * S + js) * W + (size_t)g * dh;
+                for (int i = 0; i < dh; ++i) oh[i] += ah[js] * vj[i];
+            }
+        }
+    }
+    int64_t* counts = (int64_t*)calloc(N, sizeof(int64_t));
+    for (int64_t t = 0; t < T; ++t)
+        for (int i = 0; i < G * k; ++i) counts[idx[t * G * k + i]] += 1;
+
+    /* ---- output construction, renormalisation, aux, softmax and router */
+    double* dob = (double*)calloc((size_t)T * H * dh, sizeof(double));
+    double* u = (double*)malloc(sizeof(double) * dh);
+    double* vg = (double*)malloc(sizeof(double) * dh);
+    double* slot = (double*)malloc(sizeof(double) * dh);
+    double* dp = (double*)malloc(sizeof(double) * N);
+    double* dw = (double*)malloc(sizeof(double) * k);
+    for (int64_t t = 0; t < T; ++t) {
+        const double* dyt = dy + t * d;
+        const double* pt = p + t * N;
+        for (int e = 0; e < N; ++e) dp[e] = 0.0;
+        for (int g = 0; g < G; ++g) {
+            double psel = 0.0;
+            for (int r = 0; r < k; ++r) psel += pt[idx[t * G * k + g * k + r]];
+            if (c->variant == 0) {
+                for (int j = 0; j < dh; ++j) {
+                    double acc = 0.0;
+                    for (int col = 0; col < d; ++col) acc += dyt[col] * WoR[((size_t)g * dh + j) * d + col];
+                    vg[j] = acc;
+                    slot[j] = 0.0;
+                }
+                for (int r = 0; r < k; ++r) {
+                    const double wr = pt[idx[t * G * k + g * k + r]] / psel;
+                    const double* orr = o + ((size_t)t * H + g * k + r) * dh;
+                    for (int j = 0; j < dh; ++j) slot[j] += wr * orr[j];
+                }
+                for (int j = 0; j < dh; ++j)
+                    for (int col = 0; col < d; ++col) dWoR[((size_t)g * dh + j) * d + col] += slot[j] * dyt[col];
+            }
+            for (int r = 0; r < k; ++r) {
+                const int e = idx[t * G * k + g * k + r];
+                const double* orr = o + ((size_t)t * H + g * k + r) * dh;
+                double* dorr = dob + ((size_t)t * H + g * k + r) * dh;
+                const double coef = c->variant == 1 ? pt[e] : 1.0;
+                double ou = 0.0, ov = 0.0;
+                for (int j = 0; j < dh; ++j) {
+                    double acc = 0.0;
+                    for (int col = 0; col < d; ++col) acc += dyt[col] * Wo[((size_t)e * dh + j) * d + col];
+                    u[j] = acc;
+                    ou += orr[j] * acc;
+                    for (int col = 0; col < d; ++col) dWo[((size_t)e * dh + j) * d + col] += coef * orr[j] * dyt[col];
+                    dorr[j] = coef * acc;
+                }
+                if (c->variant == 1) dp[e] += ou;
+                if (c->variant == 0) {
+                    const double wr = pt[e] / psel;
+                    for (int j = 0; j < dh; ++j) {
+                        dorr[j] += wr * vg[j];
+                        ov += orr[j] * vg[j];
+                    }
+                    dw[r] = ov;
+                }
+            }
+            if (c->variant == 0) {
+                double sw = 0.0;
+                for (int r = 0; r < k; ++r) sw += (pt[idx[t * G * k + g * k + r]] / psel) * dw[r];
+                for (int r = 0; r < k; ++r) dp[idx[t * G * k + g * k + r]] += (dw[r] - sw) / psel;
+            }
+        }
+        if (sh) {
+            const double* os = o + ((size_t)t * H + G * k) * dh;
+            double* dos = dob + ((size_t)t * H + G * k) * dh;
+            for (int j = 0; j < dh; ++j) {
+                double acc = 0.0;
+                for (int col = 0; col < d; ++col) {
+                    acc += dyt[col] * Wos[(size_t)j * d + col];
+                    dWos[(size_t)j * d + col] += os[j] * dyt[col];
+                }
+                dos[j] = acc;
+            }
+        }
+        for (int e = 0; e < N; ++e)
+            dp[e] += aux_coef * (double)n * ((double)counts[e] / ((double)T * (double)k)) / ((double)G * (double)T);
+        for (int g = 0; g < G; ++g) {
+            double sdp = 0.0;
+            for (int j = 0; j < n; ++j) sdp += pt[g * n + j] * dp[g * n + j];
+            for (int j = 0; j < n; ++j) {
+                const int e = g * n + j;
+                const double dl = pt[e] * (dp[e] - sdp);
+                dbr[e] += dl;
+                for (int i = 0; i < d; ++i) {
+                    dWr[(size_t)i * N + e] += x[t * d + i] * dl;
+                    dx[t * d + i] += Wr[(size_t)i * N + e] * dl;
+                }
+            }
+        }
+    }
+
+    /* ---- attention */
+    double* dq = (double*)calloc((size_t)T * H * dh, sizeof(double));
+    double* dK = (double*)calloc((size_t)T * W, sizeof(double));
+    double* dV = (double*)calloc((size_t)T * W, sizeof(double));
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t b = t / S, s = t % S;
+        for (int h = 0; h < H; ++h) {
+            const int g = h < G * k ? h / k : c->shared_kv_group;
+            const double* doh = dob + ((size_t)t * H + h) * dh;
+            const double* oh = o + ((size_t)t * H + h) * dh;
+            const double* qh = q + ((size_t)t * H + h) * dh;
+            const double* ah = a + ((size_t)t * H + h) * S;
+            double* dqh = dq + ((size_t)t * H + h) * dh;
+            double D = 0.0;
+            for (int i = 0; i < dh; ++i) D += doh[i] * oh[i];
+            for (int64_t js = 0; js <= s; ++js) {
+                const int64_t tj = b * S + js;
+                const double* kj = K + (size_t)tj * W + (size_t)g * dh;
+                const double* vj = V + (size_t)tj * W + (size_t)g * dh;
+                double dA = 0.0;
+                for (int i = 0; i < dh; ++i) dA += doh[i] * vj[i];
+                const double dz = ah[js] * (dA - D);
+                for (int i = 0; i < dh; ++i) {
+                    dqh[i] += dz * kj[i] * scale;
+                    dK[(size_t)tj * W + (size_t)g * dh + i] += dz * qh[i] * scale;
+                    dV[(size_t)tj * W + (size_t)g * dh + i] += ah[js] * doh[i];
+                }
+            }
+        }
+    }
+
+    /* ---- rotary embedding (rotate back), then the projections */
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t s = t % S;
+        for (int h = 0; h < H; ++h) rope(dq + ((size_t)t * H + h) * dh, dh, -(c->pos0 + s), c->rope_base);
+        for (int g = 0; g < G; ++g) rope(dK + (size_t)t * W + (size_t)g * dh, dh, -(c->pos0 + s), c->rope_base);
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        const double* xt = x + t * d;
+        for (int h = 0; h < H; ++h) {
+            const int routed = h < G * k;
+            const int e = routed ? idx[t * G * k + h] : -1;
+            const double* dqh = dq + ((size_t)t * H + h) * dh;
+            for (int i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < dh; ++j) {
+                    if (routed) {
+                        dWq[((size_t)e * d + i) * dh + j] += xt[i] * dqh[j];
+                        acc += Wq[((size_t)e * d + i) * dh + j] * dqh[j];
+                    } else {
+                        dWqs[(size_t)i * dh + j] += xt[i] * dqh[j];
+                        acc += Wqs[(size_t)i * dh + j] * dqh[j];
+                    }
+                }
+                dx[t * d + i] += acc;
+            }
+        }
+        for (int i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int col = 0; col < W; ++col) {
+                dWk[(size_t)i * W + col] += xt[i] * dK[(size_t)t * W + col];
+                dWv[(size_t)i * W + col] += xt[i] * dV[(size_t)t * W + col];
+                acc += Wk[(size_t)i * W + col] * dK[(size_t)t * W + col] + Wv[(size_t)i * W + col] * dV[(size_t)t * W + col];
+            }
+            dx[t * d + i] += acc;
+        }
+    }
+    free(logits); free(p); free(tidx); free(tw); free(tgap); free(K); free(V); free(q); free(o);
+    free(a); free(counts); free(dob); free(u); free(vg); free(slot); free(dp); free(dw); free(dq);
+    free(dK); free(dV);
+    return 0;
+}

@@ -93,8 +93,9 @@ def _load():
         lib.gqe_oracle_bucket.argtypes = [C, I64, P, P, P, P]
         lib.gqe_oracle_rows.argtypes = [C, I64, I64, P, P, P, P, P, P, P, P, P, P, P, I64, P,
                                         P, P]
+        lib.gqe_oracle_backward.argtypes = [C, I64, I64] + [P] * 12 + [ctypes.c_double] + [P] * 10
         for f in (lib.gqe_oracle_router, lib.gqe_oracle_aux, lib.gqe_oracle_kv,
-                  lib.gqe_oracle_rows, lib.gqe_oracle_bucket):
+                  lib.gqe_oracle_rows, lib.gqe_oracle_bucket, lib.gqe_oracle_backward):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -252,3 +253,45 @@ def decode(cfg: OracleConfig, x_hist, w: dict, pos, idx_new=None) -> dict:
         for key in ("logits", "p", "idx", "w", "gap"):
             out[key][b] = r[key][p]
     return out
+
+
+GRAD_KEYS = ("x", "w_router", "b_router", "w_q", "w_q_shared", "w_k", "w_v", "w_o", "w_o_rslot", "w_o_shared")
+
+
+def backward(cfg: OracleConfig, B: int, S: int, x, w: dict, dy, aux_coef: float = 0.0, idx=None) -> dict:
+    """Gradients of L = sum(dy * y) + aux_coef * aux with respect to x and every weight (the
+    training half of the method: README "Usage" trains with lm_loss + 0.01 * aux; the explainer's
+    "Output Construction" notes that the renormalised slot is the loss's differentiable path to the
+    router).  The routing ``idx`` [T, G, k] is held fixed (the oracle's own when None).
+    Returns a dict keyed like the weights, plus "x"."""
+    lib = _load()
+    T = B * S
+    d, N, G, k, dh = cfg.dim, cfg.num_query_experts, cfg.num_kv_heads, cfg.top_k, cfg.dh
+    x = _f64(x).reshape(T, d)
+    if idx is None:
+        idx = router(cfg, x, w["w_router"], w.get("b_router"))["idx"]
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    br = np.zeros(N) if w.get("b_router") is None else _f64(w["b_router"])
+    ins = [x, _f64(w["w_router"]), br, _f64(w["w_q"]), _f64(w["w_q_shared"]), _f64(w["w_k"]),
+           _f64(w["w_v"]), _f64(w["w_o"]), _f64(w["w_o_rslot"]), _f64(w["w_o_shared"])]
+    out = {"x": np.zeros((T, d)), "w_router": np.zeros((d, N)), "b_router": np.zeros(N),
+           "w_q": np.zeros((N, d, dh)), "w_q_shared": np.zeros((d, dh)), "w_k": np.zeros((d, G * dh)),
+           "w_v": np.zeros((d, G * dh)), "w_o": np.zeros((N, dh, d)), "w_o_rslot": np.zeros((G, dh, d)),
+           "w_o_shared": np.zeros((dh, d))}
+    cc = cfg.c()
+    rc = lib.gqe_oracle_backward(ctypes.byref(cc), B, S, *[_ptr(a) for a in ins[:9]], _ptr(ins[9]),
+                                 _ptr(idx), _ptr(_f64(dy).reshape(T, d)), float(aux_coef),
+                                 *[_ptr(out[kk]) for kk in GRAD_KEYS])
+    if rc != 0:
+        raise ValueError("oracle backward: invalid configuration")
+    return out
+
+
+def loss(cfg: OracleConfig, B: int, S: int, x, w: dict, dy, aux_coef: float, idx) -> float:
+    """L = sum(dy * y) + aux_coef * aux with the routing held at ``idx`` (for finite differences)."""
+    T = B * S
+    x = _f64(x).reshape(T, cfg.dim)
+    r = router(cfg, x, w["w_router"], w.get("b_router"))
+    out = forward(cfg, B, S, x, w, idx_override=idx)
+    st = aux(cfg, r["p"], idx)
+    return float(np.sum(_f64(dy).reshape(T, cfg.dim) * out["y"]) + aux_coef * st["aux"])

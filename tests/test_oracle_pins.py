@@ -520,3 +520,92 @@ def test_rope_decode_is_last_row_of_prefix_bruteforce():
     for b, p in enumerate(pos):
         bf = bruteforce.layer(cfg, 1, p + 1, w["x"][b, :p + 1], w)
         np.testing.assert_allclose(dec["y"][b], bf["y"][p], rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- backward pass
+def _fd_check(cfg, B, S, w, dy, aux_coef, n_coords=5, seed=0, eps=1e-5):
+    """Central finite differences of the oracle's loss against its analytic gradients, at random
+    coordinates of x and of every weight (the routing held at the unperturbed decision)."""
+    rng = np.random.default_rng(seed)
+    T = B * S
+    idx = go.router(cfg, np.asarray(w["x"], np.float64).reshape(T, cfg.dim), w["w_router"],
+                    w.get("b_router"))["idx"]
+    g = go.backward(cfg, B, S, w["x"], w, dy, aux_coef, idx)
+    worst = 0.0
+    for key in go.GRAD_KEYS:
+        if key == "w_q_shared" or key == "w_o_shared":
+            if not cfg.shared_head:
+                continue
+        if key == "w_o_rslot" and cfg.variant != "gqe":
+            continue
+        arr = np.asarray(w[key], np.float64)
+        for _ in range(n_coords):
+            pos = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            wp, wm = dict(w), dict(w)
+            ap, am = arr.copy(), arr.copy()
+            ap[pos] += eps
+            am[pos] -= eps
+            wp[key], wm[key] = ap, am
+            fd = (go.loss(cfg, B, S, wp["x"], wp, dy, aux_coef, idx)
+                  - go.loss(cfg, B, S, wm["x"], wm, dy, aux_coef, idx)) / (2 * eps)
+            an = g[key].reshape(arr.shape)[pos]
+            scale = max(1e-3, np.max(np.abs(g[key])))
+            worst = max(worst, abs(fd - an) / scale)
+            assert abs(fd - an) <= 1e-6 * scale, (key, pos, fd, an)
+    return g, worst
+
+
+@pytest.mark.parametrize("variant,k,shared,rope", [("gqe", 2, True, 0.0), ("gqe", 1, True, 10000.0),
+                                                   ("weighted_concat", 1, True, 0.0),
+                                                   ("weighted_concat", 2, False, 500.0),
+                                                   ("hard_concat", 2, True, 0.0)])
+def test_backward_matches_finite_differences(variant, k, shared, rope):
+    """Training half of the method (README "Usage": lm_loss + 0.01 * aux): the oracle's analytic
+    gradients of sum(dy * y) + 0.01 aux equal central finite differences of its own forward pass,
+    for every tensor, with the renormalised slot (k = 2), the weighted_concat probabilities, the
+    shared head and the rotary embedding exercised."""
+    wl = _wl(d=16, N=8, G=2, k=k, dh=4, B=2, S=5, variant=variant, shared=shared, rstd=1.0, bias=0.3)
+    w = make_inputs(wl)
+    cfg = _rope_cfg(wl, rope)
+    dy = np.random.default_rng(7).standard_normal((wl.tokens, wl.dim))
+    _fd_check(cfg, wl.batch, wl.seq, w, dy, 0.01)
+
+
+def test_backward_router_gradient_needs_more_than_one_choice():
+    """With one choice per group the renormalised weight is identically 1 and hard concat has no
+    router coefficient, so the LM loss sends no gradient to the router (only the aux loss does);
+    with two choices (gqe) or the raw probability (weighted_concat) it does."""
+    for variant, k, coef, zero in (("gqe", 1, 0.0, True), ("hard_concat", 2, 0.0, True),
+                                   ("gqe", 2, 0.0, False), ("weighted_concat", 1, 0.0, False),
+                                   ("gqe", 1, 0.01, False)):
+        wl = _wl(d=16, N=8, G=2, k=k, dh=4, B=1, S=6, variant=variant, rstd=1.0)
+        w = make_inputs(wl)
+        dy = np.random.default_rng(3).standard_normal((wl.tokens, wl.dim))
+        g = go.backward(_cfg(wl), 1, wl.seq, w["x"], w, dy, coef)
+        if zero:
+            assert np.all(g["w_router"] == 0) and np.all(g["b_router"] == 0), (variant, k)
+        else:
+            assert np.max(np.abs(g["w_router"])) > 1e-8, (variant, k, coef)
+
+
+def test_backward_gqa_case_matches_torch_autograd():
+    """k = N/G, hard concat, no shared head is textbook GQA: torch autograd (float64) of an
+    independently written GQA layer with scaled_dot_product_attention gives the same gradients."""
+    N, G, d, dh, S = 4, 2, 16, 4, 7
+    wl = _wl(d=d, N=N, G=G, k=N // G, dh=dh, B=1, S=S, variant="hard_concat", shared=False, rstd=1.0)
+    w = make_inputs(wl)
+    dy = np.random.default_rng(5).standard_normal((S, d))
+    g = go.backward(_cfg(wl), 1, S, w["x"], w, dy, 0.0)
+    t = {k: torch.tensor(np.asarray(w[k], np.float64), requires_grad=True)
+         for k in ("x", "w_q", "w_k", "w_v", "w_o")}
+    x = t["x"].reshape(S, d)
+    q = torch.einsum("sd,edh->esh", x, t["w_q"])                       # [N, S, dh]
+    kk = (x @ t["w_k"]).reshape(S, G, dh).permute(1, 0, 2)               # [G, S, dh]
+    vv = (x @ t["w_v"]).reshape(S, G, dh).permute(1, 0, 2)
+    rep = N // G
+    o = torch.nn.functional.scaled_dot_product_attention(
+        q, kk.repeat_interleave(rep, 0), vv.repeat_interleave(rep, 0), is_causal=True)
+    y = torch.einsum("esh,ehd->sd", o, t["w_o"])
+    (y * torch.tensor(dy)).sum().backward()
+    for key in ("x", "w_q", "w_k", "w_v", "w_o"):
+        np.testing.assert_allclose(g[key].reshape(t[key].shape), t[key].grad.numpy(), rtol=1e-9, atol=1e-12)
