@@ -264,6 +264,46 @@ int gqe_decode(gqe_handle_t* h, const void* x, void* y, int64_t batch, const int
                void* kcache, void* vcache, int64_t s_max, void* workspace, size_t ws_bytes,
                void* stream, int32_t* route_idx, float* route_w);
 
+/* ------------------------------------------------------------------ backward pass
+ * The training half of the method (README "Usage": loss = lm_loss + 0.01 * collect_aux_loss(attn);
+ * explainer "Output Construction": the renormalised weighted-sum slot gives the language-modelling
+ * loss a differentiable path to the router; "Training and Loss": the load-balancing loss).
+ * gqe_backward computes the gradients of  L = sum(dy * y) + aux_coef * aux  (dy = dL/dy of the
+ * caller's loss, aux the balance loss of gqe_aux_stats) with respect to x and every weight, the
+ * routing decisions of the forward pass held fixed (top-k is piecewise constant).
+ * All gradients are float32, row-major in the layouts of gqe_weights_t; every pointer is a device
+ * address, 4-byte aligned, and is overwritten (not accumulated into).  d_router and
+ * d_router_bias may be NULL only for dense_gqa; d_q_shared / d_o_shared may be NULL without the
+ * shared head, d_o_rslot unless variant gqe. */
+typedef struct {
+    float* dx;            /* [batch, seq, d] */
+    float* d_router;      /* [d, N] */
+    float* d_router_bias; /* [N] */
+    float* d_q;           /* [N, d, d_h] */
+    float* d_q_shared;    /* [d, d_h] */
+    float* d_k;           /* [d, G*d_h] */
+    float* d_v;           /* [d, G*d_h] */
+    float* d_o;           /* [N, d_h, d] */
+    float* d_o_rslot;     /* [G, d_h, d] */
+    float* d_o_shared;    /* [d_h, d] */
+} gqe_grads_t;
+
+/* Bytes of scratch gqe_backward needs for a [batch, seq] forward (per-slot projections of dy,
+ * head-output gradients, row statistics, router-logit gradients, dQ, dK, dV).  Host only.
+ * Errors: GQE_ERR_NULL_POINTER, GQE_ERR_SHAPE, GQE_ERR_UNSUPPORTED. */
+int gqe_backward_workspace_bytes(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t* bytes);
+
+/* The backward pass of the last gqe_forward on this handle.
+ *  x, dy          [batch, seq, d] device, cfg.dtype; x the forward's input, dy the loss gradient.
+ *  aux_coef       weight of the balance loss in L (the README's 0.01; 0 for none).
+ *  fwd_workspace  the workspace of that forward (routing, statistics, Q, K, V^T, O), unchanged.
+ *  workspace      device, >= gqe_backward_workspace_bytes(batch, seq), 256-byte aligned.
+ * Enqueued on `stream`.  Supported: n = N/G <= 16, head_dim a multiple of 16, head_dim <= 128.
+ * Errors: GQE_ERR_NULL_POINTER, GQE_ERR_STATE (no forward of this shape on this workspace),
+ * GQE_ERR_MISALIGNED, GQE_ERR_WORKSPACE, GQE_ERR_UNSUPPORTED, GQE_ERR_HIP. */
+int gqe_backward(gqe_handle_t* h, const void* x, const void* dy, int64_t batch, int64_t seq, double aux_coef,
+                 void* fwd_workspace, void* workspace, size_t ws_bytes, const gqe_grads_t* grads, void* stream);
+
 /* Kernel timing for measurement.  While enabled, gqe_forward and gqe_decode record a HIP event on
  * their stream right before and right after each kernel they launch; a kernel's duration is the
  * time between the two.  Kernel slots, in launch order:
@@ -274,12 +314,15 @@ int gqe_decode(gqe_handle_t* h, const void* x, void* y, int64_t batch, const int
  *   7 combine + output projection
  * and of gqe_decode (slot 0 is its router):
  *   8 decode projections    9 decode attention    10 decode merge    11 decode combine
+ * and of gqe_backward:
+ *   12 output-side gradients (dy W_slot^T, head outputs, router logits)   13 attention
+ *   14 weight gradients     15 input gradient dx
  * gqe_profile_read_kernels waits for the recorded events, returns the summed milliseconds per
  * kernel slot (0 for slots not launched) and the number of forwards they cover, and starts a new
  * accumulation.  gqe_profile_read does the same summed per stage (0 router = slots 0+1,
  * 1 projections = 2+3+8, 2 attention = 4+5+6+9+10, 3 combine = 7+11).  Not re-entrant; errors as
  * GQE_ERR_NULL_POINTER / GQE_ERR_HIP. */
-#define GQE_PROF_KERNELS 12
+#define GQE_PROF_KERNELS 16
 int gqe_profile_enable(gqe_handle_t* h, int enable);
 int gqe_profile_read(gqe_handle_t* h, double stage_ms[4], int64_t* forwards);
 int gqe_profile_read_kernels(gqe_handle_t* h, double kernel_ms[GQE_PROF_KERNELS], int64_t* forwards);

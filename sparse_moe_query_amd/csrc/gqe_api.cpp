@@ -551,6 +551,81 @@ int gqe_decode(gqe_handle_t* h, const void* x, void* y, int64_t batch, const int
     return ok();
 }
 
+static int backward_supported(const GqeDims& D) {
+    if (D.n > 16) return fail(GQE_ERR_UNSUPPORTED, "backward handles at most 16 experts per group");
+    if (D.dh % 16 != 0 || D.dh > 128) return fail(GQE_ERR_UNSUPPORTED, "backward needs head_dim a multiple of 16, <= 128");
+    return GQE_OK;
+}
+
+static BwdPlan make_bwd_plan(const GqeDims& D, int64_t B, int64_t S) {
+    BwdPlan P{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    const size_t T = (size_t)(B * S);
+    P.NS = D.G * D.k + ((!D.dense && D.variant == GQE_VARIANT_GQE) ? D.G : 0) + D.s;
+    P.U = take(T * P.NS * D.dh * 4);
+    P.dO = take(T * D.H * D.dh * 4);
+    P.Dd = take(T * D.H * 4);
+    P.lse = take(T * D.H * 4);
+    P.dl = take(T * D.N * 4);
+    P.cf = take(T * D.H * 4);
+    P.wn = take(T * D.H * 4);
+    P.dQ = take(T * D.H * D.dh * 4);
+    P.dK = take(T * D.G * D.dh * 4);
+    P.dV = take(T * D.G * D.dh * 4);
+    P.total = off;
+    return P;
+}
+
+int gqe_backward_workspace_bytes(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t* bytes) {
+    if (!h || !bytes) return fail(GQE_ERR_NULL_POINTER, "handle and bytes must be non-NULL");
+    if (batch < 1 || seq < 1 || batch * seq > ((int64_t)1 << 28)) return fail(GQE_ERR_SHAPE, "bad batch/seq");
+    const int rc = backward_supported(h->D);
+    if (rc != GQE_OK) return rc;
+    *bytes = make_bwd_plan(h->D, batch, seq).total;
+    return ok();
+}
+
+int gqe_backward(gqe_handle_t* h, const void* x, const void* dy, int64_t batch, int64_t seq, double aux_coef,
+                 void* fwd_workspace, void* workspace, size_t ws_bytes, const gqe_grads_t* grads, void* stream) {
+    if (!h || !x || !dy || !fwd_workspace || !workspace || !grads)
+        return fail(GQE_ERR_NULL_POINTER, "handle, x, dy, workspaces and grads must be non-NULL");
+    const GqeDims& D = h->D;
+    const gqe_grads_t& g = *grads;
+    if (!g.dx || !g.d_q || !g.d_k || !g.d_v || !g.d_o || (!D.dense && (!g.d_router || !g.d_router_bias)) ||
+        (D.s && (!g.d_q_shared || !g.d_o_shared)) || (!D.dense && D.variant == GQE_VARIANT_GQE && !g.d_o_rslot))
+        return fail(GQE_ERR_NULL_POINTER, "a required gradient pointer is NULL");
+    const float* gp[] = {g.dx, g.d_router, g.d_router_bias, g.d_q, g.d_q_shared, g.d_k, g.d_v, g.d_o, g.d_o_rslot, g.d_o_shared};
+    for (const float* p : gp)
+        if (p && misaligned(p, 4)) return fail(GQE_ERR_MISALIGNED, "gradient pointers must be 4-byte aligned");
+    if (misaligned(x, 16) || misaligned(dy, 16)) return fail(GQE_ERR_MISALIGNED, "x and dy must be 16-byte aligned");
+    if (misaligned(workspace, 256)) return fail(GQE_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    const int rc = backward_supported(D);
+    if (rc != GQE_OK) return rc;
+    if (!h->ran || h->last_ws != fwd_workspace || h->last_plan.B != batch || h->last_plan.S != seq)
+        return fail(GQE_ERR_STATE, "gqe_backward needs the last gqe_forward of this [batch, seq] and its workspace");
+    if (!(aux_coef == aux_coef)) return fail(GQE_ERR_INVALID_CONFIG, "aux_coef is NaN");
+    const BwdPlan BP = make_bwd_plan(D, batch, seq);
+    if (ws_bytes < BP.total) return fail(GQE_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, BP.total);
+    hipStream_t st = (hipStream_t)stream;
+    KernelMarks marks;
+    KernelMarks* km = nullptr;
+    if (h->prof) {
+        const int prc = prof_marks(h, st, &marks);
+        if (prc != GQE_OK) return prc;
+        km = &marks;
+    }
+    hipError_t e = launch_backward(D, h->last_plan, BP, h->w, h->packed, h->pl, x, dy, aux_coef,
+                                   (const char*)fwd_workspace, (char*)workspace, g, st, km);
+    if (e == hipSuccess && km && marks.err != hipSuccess) e = marks.err;
+    if (e != hipSuccess) return fail(GQE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int gqe_profile_enable(gqe_handle_t* h, int enable) {
     if (!h) return fail(GQE_ERR_NULL_POINTER, "handle must be non-NULL");
     h->prof = enable != 0;

@@ -63,6 +63,13 @@ struct DecodePlan {
     size_t total;
 };
 
+// Byte offsets into the caller's backward workspace for a [B, S] forward (all float32).
+struct BwdPlan {
+    int NS;                           // output-projection slots of one token
+    size_t U, dO, Dd, lse, dl, cf, wn, dQ, dK, dV;
+    size_t total;
+};
+
 // One attention work group: item (batch b, group g, nh heads per position, positions
 // [p0, p0 + np)) restricted to key tiles [kt0, kt1); part = partial-result slot, or -1 when the
 // job covers the whole item and writes O itself.  Eight int32 per job on the device.
@@ -115,7 +122,8 @@ struct gqe_handle {
 // Kernel timing slots, in launch order (GQE_PROF_KERNELS in gqe.h).
 enum {
     KT_ROUTER = 0, KT_ROUTER_STATS, KT_PROJ, KT_KEYNORM, KT_ATTN_PREP, KT_ATTN, KT_ATTN_MERGE, KT_COMBINE,
-    KT_DEC_PROJ, KT_DEC_ATTN, KT_DEC_MERGE, KT_DEC_COMBINE, KT_COUNT
+    KT_DEC_PROJ, KT_DEC_ATTN, KT_DEC_MERGE, KT_DEC_COMBINE,
+    KT_BWD_OUT, KT_BWD_ATTN, KT_BWD_WGRAD, KT_BWD_DX, KT_COUNT
 };
 
 // Records events on the stream right before and right after each kernel a launcher enqueues
@@ -167,6 +175,9 @@ hipError_t launch_kv_export(const GqeDims& D, const WorkPlan& P, const char* ws,
 hipError_t launch_decode(const GqeDims& D, const DecodePlan& P, const gqe_weights_t& w, const double* rope,
                          const void* x, void* y, const int32_t* pos, void* kc, void* vc, char* ws, hipStream_t st,
                          KernelMarks* km);
+hipError_t launch_backward(const GqeDims& D, const WorkPlan& P, const BwdPlan& BP, const gqe_weights_t& w,
+                           const void* packed, const PackedLayout& pl, const void* x, const void* dy, double aux_coef,
+                           const char* fws, char* ws, const gqe_grads_t& gr, hipStream_t st, KernelMarks* km);
 hipError_t launch_bucket(const GqeDims& D, const WorkPlan& P, char* ws, int32_t* offs, int32_t* perm, int32_t* inv,
                          hipStream_t st);
 bool combine_mfma_supported(const GqeDims& D);

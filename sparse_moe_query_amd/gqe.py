@@ -26,11 +26,15 @@ ERRORS = {0: "GQE_OK", -1: "GQE_ERR_INVALID_CONFIG", -2: "GQE_ERR_NULL_POINTER",
 EXPORTS = ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights", "gqe_workspace_bytes",
            "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_bucket", "gqe_profile_enable",
            "gqe_profile_read", "gqe_profile_read_kernels", "gqe_attention_schedule", "gqe_kv_export",
-           "gqe_decode_workspace_bytes", "gqe_decode", "gqe_destroy", "gqe_last_error")
+           "gqe_decode_workspace_bytes", "gqe_decode", "gqe_backward_workspace_bytes", "gqe_backward",
+           "gqe_destroy", "gqe_last_error")
 STAGES = ("router", "projection", "attention", "combine")
 # kernel timing slots of gqe_profile_read_kernels, in launch order
 KERNELS = ("router", "router_stats", "projection", "key_norms", "attention_prep", "attention", "attention_merge",
-           "combine", "decode_projection", "decode_attention", "decode_merge", "decode_combine")
+           "combine", "decode_projection", "decode_attention", "decode_merge", "decode_combine",
+           "backward_output", "backward_attention", "backward_weights", "backward_dx")
+GRAD_FIELDS = ("dx", "d_router", "d_router_bias", "d_q", "d_q_shared", "d_k", "d_v", "d_o", "d_o_rslot",
+               "d_o_shared")
 
 
 class GqeError(RuntimeError):
@@ -49,6 +53,10 @@ class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w_router", "b_router", "w_q", "w_q_shared", "w_k", "w_v", "w_o", "w_o_rslot",
         "w_o_shared")]
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_FIELDS]
 
 
 _lib = None
@@ -78,6 +86,8 @@ def lib():
         L.gqe_kv_export.argtypes = [P, P, P, P, I64, I64, I64]
         L.gqe_decode_workspace_bytes.argtypes = [P, I64, I64, ctypes.POINTER(SZ)]
         L.gqe_decode.argtypes = [P, P, P, I64, P, P, P, I64, P, SZ, P, P, P]
+        L.gqe_backward_workspace_bytes.argtypes = [P, I64, I64, ctypes.POINTER(SZ)]
+        L.gqe_backward.argtypes = [P, P, P, I64, I64, ctypes.c_double, P, P, SZ, ctypes.POINTER(Grads), P]
         L.gqe_destroy.argtypes = [P]
         L.gqe_destroy.restype = None
         L.gqe_last_error.argtypes = []
@@ -85,7 +95,8 @@ def lib():
         for f in ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights",
                   "gqe_workspace_bytes", "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_bucket",
                   "gqe_profile_enable", "gqe_profile_read", "gqe_profile_read_kernels",
-                  "gqe_attention_schedule", "gqe_kv_export", "gqe_decode_workspace_bytes", "gqe_decode"):
+                  "gqe_attention_schedule", "gqe_kv_export", "gqe_decode_workspace_bytes", "gqe_decode",
+                  "gqe_backward_workspace_bytes", "gqe_backward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -214,6 +225,20 @@ def gqe_decode(h, x: torch.Tensor, y: torch.Tensor, pos: torch.Tensor, kcache: t
                             _stream(stream), _ptr(route_idx), _ptr(route_w)))
 
 
+def gqe_backward_workspace_bytes(h, batch: int, seq: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().gqe_backward_workspace_bytes(h, batch, seq, ctypes.byref(n)))
+    return n.value
+
+
+def gqe_backward(h, x: torch.Tensor, dy: torch.Tensor, batch: int, seq: int, aux_coef: float,
+                 fwd_workspace: torch.Tensor, workspace: torch.Tensor, grads: dict, stream=None):
+    g = Grads(*[_ptr(grads.get(f)) for f in GRAD_FIELDS])
+    _check(lib().gqe_backward(h, _ptr(x), _ptr(dy), batch, seq, float(aux_coef), _ptr(fwd_workspace),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(), ctypes.byref(g),
+                              _stream(stream)))
+
+
 def gqe_destroy(h):
     if h:
         lib().gqe_destroy(h)
@@ -273,6 +298,30 @@ class GQEAttention:
 
     def aux_stats(self, stream=None) -> dict:
         return gqe_aux_stats(self.h, self.N, stream)
+
+    # ---- backward pass
+    def backward(self, x: torch.Tensor, dy: torch.Tensor, aux_coef: float = 0.0, stream=None) -> dict:
+        """Gradients of sum(dy * y) + aux_coef * aux for the last forward (which must have been on
+        this x): float32 tensors keyed like gqe_grads_t (dx, d_router, ..., d_o_shared)."""
+        B, S, d = x.shape
+        if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_contiguous():
+            raise ValueError("dy must be a contiguous tensor like x")
+        dh, N, G = self.dh, self.N, self.G
+        f32 = dict(dtype=torch.float32, device=self.device)
+        shapes = {"dx": (B, S, d), "d_router": (d, N), "d_router_bias": (N,), "d_q": (N, d, dh),
+                  "d_q_shared": (d, dh), "d_k": (d, G * dh), "d_v": (d, G * dh), "d_o": (N, dh, d),
+                  "d_o_rslot": (G, dh, d), "d_o_shared": (dh, d)}
+        if self.cfg.dense_gqa:
+            shapes.pop("d_router"), shapes.pop("d_router_bias")
+        if not self.cfg.shared_head:
+            shapes.pop("d_q_shared"), shapes.pop("d_o_shared")
+        if self.cfg.dense_gqa or self.cfg.variant != VARIANTS["gqe"]:
+            shapes.pop("d_o_rslot")
+        grads = {k: torch.empty(v, **f32) for k, v in shapes.items()}
+        nbytes = gqe_backward_workspace_bytes(self.h, B, S)
+        bws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        gqe_backward(self.h, x, dy, B, S, aux_coef, self._ws, bws, grads, stream)
+        return grads
 
     # ---- decode with a dense KV cache
     def kv_cache(self, batch: int, s_max: int):
