@@ -577,6 +577,9 @@ static BwdPlan make_bwd_plan(const GqeDims& D, int64_t B, int64_t S) {
     P.dQ = take(T * D.H * D.dh * 4);
     P.dK = take(T * D.G * D.dh * 4);
     P.dV = take(T * D.G * D.dh * 4);
+    P.offs = take((size_t)(D.N + 1) * 4);
+    P.perm = take(T * D.G * D.k * 4);
+    P.inv = take(T * D.G * D.k * 4);
     P.total = off;
     return P;
 }

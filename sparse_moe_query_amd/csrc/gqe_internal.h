@@ -67,6 +67,7 @@ struct DecodePlan {
 struct BwdPlan {
     int NS;                           // output-projection slots of one token
     size_t U, dO, Dd, lse, dl, cf, wn, dQ, dK, dV;
+    size_t offs, perm, inv;           // token lists of the routed experts (bucketing)
     size_t total;
 };
 

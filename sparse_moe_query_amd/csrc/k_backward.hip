@@ -7,22 +7,25 @@
 // Loss" adds the load-balancing loss.  The steps are the chain rule through the forward definition,
 // in reverse order:
 //
-//   bwd_u_kernel      U[t][slot] = dy_t W_slot^T for every output slot of the token (routed expert
-//                     e: W_o[e]; group g: W_oR[g]; shared head: W_os)
+//   ProbU             U[t][slot] = dy_t W_slot^T for every output slot of the token (routed expert
+//                     e: W_o[e], over its tokens; group g: W_oR[g]; shared head: W_os)
 //   bwd_route_kernel  per (token, group): head-output gradients do = c U_e + w U_g, D = do . o for
 //                     the attention, the router probabilities again (float64 logits, as in the
 //                     forward), the probability gradients (weighted_concat coefficient,
 //                     renormalisation w = p / sum_sel p, aux loss), and the logit gradients through
 //                     the in-group softmax
-//   bwd_lse_kernel    log-sum-exp of every query row (log2 units, from the stored queries and keys)
-//   bwd_dq_kernel     dq = sum_j p_j (do . v_j - D) k_j / sqrt(d_h), rotated back (rotary embedding)
-//   bwd_dkv_kernel    dk_j, dv_j summed over the later queries of every head of the group
-//   bwd_wgrad_kernels weight gradients as sums over the tokens that use each weight block
-//   bwd_dx_kernel     dx = sum over the token's head blocks of dq W^T (+ dk, dv, router logits)
+//   bwd_dq_kernel     per 64 queries of a head: the row log-sum-exp (log2 units, from the stored
+//                     queries and keys), then dq = sum_j p_j (do . v_j - D) k_j / sqrt(d_h),
+//                     rotated back (rotary embedding)
+//   bwd_dkv_kernel    per 64 keys of a group: dk_j, dv_j over every later query of every head
+//   ProbWo, ProbWx    weight gradients as sums over the tokens that use each weight block
+//   ProbDx*           dx = dense part (dk W_k^T, dv W_v^T, shared dq W_qs^T, router logits W_r^T),
+//                     then the routed dq W_q[e]^T per (group, rank)
 //
-// This is the first, scalar form of the backward pass: one thread per output element (or per
-// query / key row), float32 arithmetic over the forward's stored Q, K, V^T and O.  It reads the
-// forward pass's workspace (routing, statistics, Q, K, V^T, O), which must be unchanged.
+// The GEMM-shaped steps run through one tiled float32 kernel (tgemm_kernel) over gathered token
+// lists (the global bucketing of the forward's routing); the attention steps stage 64-row tiles in
+// LDS, four lanes per row.  Everything reads the forward pass's workspace (routing,
+// statistics, Q, K, V^T, O), which must be unchanged.
 #include <math.h>
 
 #include <cmath>
@@ -81,29 +84,6 @@ __device__ __forceinline__ int expert_of(const BwdArgs& a, int64_t t, int h) {
     return a.dense ? g * a.n + r : a.idx[(t * a.G + g) * a.k + r];
 }
 __device__ __forceinline__ int group_of(const BwdArgs& a, int h) { return h < a.G * a.k ? h / a.k : a.skv; }
-
-// ---------------------------------------------------------------- U = dy W_slot^T
-// slot ls of token t: routed (g, r) -> ls = g k + r (W_o[e]); group slot -> G k + g (W_oR[g]);
-// shared head -> G k + G (gqe) or G k
-template <typename T>
-__global__ void bwd_u_kernel(BwdArgs a) {
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t per = (int64_t)a.NS * a.dh;
-    if (q >= a.T * per) return;
-    const int64_t t = q / per;
-    const int ls = (int)((q % per) / a.dh), j = (int)(q % a.dh);
-    const int nr = a.G * a.k;
-    const bool rslot = !a.dense && a.variant == GQE_VARIANT_GQE;
-    const T* W;
-    if (ls < nr) W = (const T*)a.wo + (int64_t)expert_of(a, t, ls) * a.dh * a.d;
-    else if (rslot && ls < nr + a.G) W = (const T*)a.wor + (int64_t)(ls - nr) * a.dh * a.d;
-    else W = (const T*)a.wos;
-    const T* w = W + (int64_t)j * a.d;
-    const T* g = (const T*)a.dy + t * a.d;
-    float acc = 0.f;
-    for (int c = 0; c < a.d; ++c) acc += to_f32(g[c]) * to_f32(w[c]);
-    a.U[q] = acc;
-}
 
 // ---------------------------------------------------------------- head-output and router gradients
 // thread per (token, group); group 0 also handles the shared head.
@@ -207,235 +187,520 @@ __global__ void bwd_route_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- attention
+// Both kernels: four lanes per row, each holding a quarter of the head dims (DQ = d_h / 4); dot
+// products are summed over the four lanes with DPP quad permutations.  Tiles of 64 keys or queries
+// are staged in LDS as float32.
+
+__device__ __forceinline__ float quad_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));  // xor 1
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false));  // xor 2
+    return v;
+}
+
+constexpr int kDQ = 32;  // largest quarter of a head (d_h <= 128)
+
+// dq for a block of 64 queries of one (sequence, head): pass 1 recomputes each row's log-sum-exp
+// over the causal keys (online, log2 units), pass 2 sums dz_j k_j with dz_j = p_j (do . v_j - D).
 template <typename T>
-__global__ void bwd_lse_kernel(BwdArgs a) {
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= a.T * a.H) return;
-    const int64_t t = q / a.H;
-    const int h = (int)(q % a.H), g = group_of(a, h);
-    const int64_t b = t / a.S, s = t % a.S;
-    const int64_t qo = ((b * a.H + h) * a.S + s) * a.dh;
-    const int64_t kb = (b * a.G + g) * a.S_pad * a.dh;
+__global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
+    __shared__ float ks[64][129];
+    __shared__ float vs[64][129];
+    const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int g = group_of(a, h);
+    const int dh = a.dh, DQ = dh / 4;
+    const int qi = tid >> 2, qd = tid & 3, d0 = qd * DQ;
+    const int64_t s = (int64_t)qb * 64 + qi;
+    const bool valid = s < a.S;
+    const int64_t sq = valid ? s : a.S - 1;
+    const int64_t t = b * a.S + sq;
+    float q[kDQ], dov[kDQ], dq[kDQ];
+    const int64_t qo = ((b * a.H + h) * a.S + sq) * dh + d0;
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i) {
+        q[i] = i < DQ ? ld<T>(a.Q, qo + i) : 0.f;
+        dov[i] = i < DQ ? a.dO[(t * a.H + h) * dh + d0 + i] : 0.f;
+        dq[i] = 0.f;
+    }
+    const float D = a.Dd[t * a.H + h];
+    const int64_t kbase = (b * a.G + g) * a.S_pad * dh;
+    const int64_t vbase = (b * a.G + g) * dh * a.S_pad;
+    const int ntiles = qb + 1;  // causal: key tiles up to the diagonal
+    auto stage = [&](int kt, bool withv) {
+        __syncthreads();
+        for (int i = tid; i < 64 * dh; i += 256) {
+            const int kk = i / dh, c = i - kk * dh;
+            const int64_t kp = (int64_t)kt * 64 + kk;
+            ks[kk][c] = kp < a.S ? ld<T>(a.K, kbase + kp * dh + c) : 0.f;
+        }
+        if (withv)
+            for (int i = tid; i < 64 * dh; i += 256) {
+                const int c = i / 64, kk = i & 63;  // neighbouring threads: neighbouring keys of V^T
+                const int64_t kp = (int64_t)kt * 64 + kk;
+                vs[kk][c] = kp < a.S ? ld<T>(a.Vt, vbase + (int64_t)c * a.S_pad + vt_pos(kp)) : 0.f;
+            }
+        __syncthreads();
+    };
+    // pass 1: log-sum-exp of the row
     float m = -INFINITY, l = 0.f;
-    for (int64_t j = 0; j <= s; ++j) {
-        float sc = 0.f;
-        for (int i = 0; i < a.dh; ++i) sc += ld<T>(a.Q, qo + i) * ld<T>(a.K, kb + j * a.dh + i);
-        if (sc > m) {
-            l = l * exp2f(m - sc) + 1.f;
-            m = sc;
-        } else {
-            l += exp2f(sc - m);
+    for (int kt = 0; kt < ntiles; ++kt) {
+        stage(kt, false);
+        const int nk = (int)min<int64_t>(64, sq + 1 - (int64_t)kt * 64);
+        for (int kk = 0; kk < 64; ++kk) {
+            float p = 0.f;
+#pragma unroll
+            for (int i = 0; i < kDQ; ++i)
+                if (i < DQ) p += q[i] * ks[kk][d0 + i];
+            const float sc = quad_sum(p);
+            if (kk < nk) {
+                if (sc > m) {
+                    l = l * exp2f(m - sc) + 1.f;
+                    m = sc;
+                } else {
+                    l += exp2f(sc - m);
+                }
+            }
         }
     }
-    a.lse[q] = m + log2f(l);
-}
-
-__device__ __forceinline__ void rope_back(float* v, int n, int64_t pos, const double* rope, int j0) {
-    // rotation by the opposite angle: the rotation is orthogonal
-    for (int i = 0; i + 1 < n; i += 2) rope_pair(v[i], v[i + 1], -pos, rope[(j0 + i) >> 1]);
-}
-
-// thread per (query token, head): dq in registers (d_h <= 128)
-template <typename T>
-__global__ void bwd_dq_kernel(BwdArgs a) {
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= a.T * a.H) return;
-    const int64_t t = q / a.H;
-    const int h = (int)(q % a.H), g = group_of(a, h);
-    const int64_t b = t / a.S, s = t % a.S;
-    const int dh = a.dh;
-    const int64_t qo = ((b * a.H + h) * a.S + s) * dh;
-    const int64_t kb = (b * a.G + g) * a.S_pad * dh;
-    const int64_t vb = (b * a.G + g) * dh * a.S_pad;
-    const float L = a.lse[q], D = a.Dd[q];
-    const float* dov = a.dO + q * dh;
-    float dq[128];
-    for (int i = 0; i < dh; ++i) dq[i] = 0.f;
-    for (int64_t j = 0; j <= s; ++j) {
-        float sc = 0.f, dA = 0.f;
-        for (int i = 0; i < dh; ++i) {
-            sc += ld<T>(a.Q, qo + i) * ld<T>(a.K, kb + j * dh + i);
-            dA += dov[i] * ld<T>(a.Vt, vb + (int64_t)i * a.S_pad + vt_pos(j));
+    const float L = m + log2f(l);
+    // pass 2
+    for (int kt = 0; kt < ntiles; ++kt) {
+        stage(kt, true);
+        const int nk = (int)min<int64_t>(64, sq + 1 - (int64_t)kt * 64);
+        for (int kk = 0; kk < 64; ++kk) {
+            float p = 0.f, da = 0.f;
+#pragma unroll
+            for (int i = 0; i < kDQ; ++i)
+                if (i < DQ) {
+                    p += q[i] * ks[kk][d0 + i];
+                    da += dov[i] * vs[kk][d0 + i];
+                }
+            const float sc = quad_sum(p), dA = quad_sum(da);
+            const float dz = kk < nk ? exp2f(sc - L) * (dA - D) : 0.f;
+#pragma unroll
+            for (int i = 0; i < kDQ; ++i)
+                if (i < DQ) dq[i] += dz * ks[kk][d0 + i];
         }
-        const float pj = exp2f(sc - L);
-        const float dz = pj * (dA - D);  // gradient of the natural-log score q.k / sqrt(d_h)
-        for (int i = 0; i < dh; ++i) dq[i] += dz * ld<T>(a.K, kb + j * dh + i);
     }
+    if (!valid) return;
     const float sc = 1.f / sqrtf((float)dh);
-    for (int i = 0; i < dh; ++i) dq[i] *= sc;
-    if (a.rope) rope_back(dq, dh, s, a.rope, 0);
-    for (int i = 0; i < dh; ++i) a.dQ[q * dh + i] = dq[i];
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i) dq[i] *= sc;
+    if (a.rope)
+#pragma unroll
+        for (int i = 0; i < kDQ; i += 2)
+            if (i < DQ) rope_pair(dq[i], dq[i + 1], -s, a.rope[(d0 + i) >> 1]);
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i)
+        if (i < DQ) a.dQ[(t * a.H + h) * dh + d0 + i] = dq[i];
+    if (qd == 0) a.lse[t * a.H + h] = L;
 }
 
-// thread per (key token, group, 16 head dims): dk, dv of those dims over every later query and
-// every head of the group
+// dk, dv for a block of 64 keys of one (sequence, group): every later query of every head of the
+// group, query tiles of 64 staged in LDS with their log-sum-exp and D.
 template <typename T>
-__global__ void bwd_dkv_kernel(BwdArgs a) {
-    const int parts = a.dh / 16;
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= a.T * a.G * parts) return;
-    const int part = (int)(q % parts);
-    const int64_t tg = q / parts;
-    const int64_t t = tg / a.G;
-    const int g = (int)(tg % a.G);
-    const int64_t b = t / a.S, j = t % a.S;
-    const int dh = a.dh, j0 = 16 * part;
-    const int64_t kb = ((b * a.G + g) * a.S_pad + j) * dh;
-    const int64_t vb = (b * a.G + g) * dh * a.S_pad;
-    const float qs = 1.f / (kLog2e);  // stored queries carry log2(e)/sqrt(d_h): q/sqrt(d_h) = q~ / log2(e)
-    float dk[16], dv[16];
-    for (int i = 0; i < 16; ++i) dk[i] = dv[i] = 0.f;
+__global__ void __launch_bounds__(256) bwd_dkv_kernel(BwdArgs a) {
+    __shared__ float qs[64][129];
+    __shared__ float ds[64][129];
+    __shared__ float ls[64], dd[64];
+    const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int dh = a.dh, DQ = dh / 4;
+    const int kj = tid >> 2, qd = tid & 3, d0 = qd * DQ;
+    const int64_t j = (int64_t)kb * 64 + kj;
+    const bool valid = j < a.S;
+    const int64_t jk = valid ? j : a.S - 1;
+    float k[kDQ], v[kDQ], dk[kDQ], dv[kDQ];
+    const int64_t kbase = ((b * a.G + g) * a.S_pad + jk) * dh + d0;
+    const int64_t vbase = (b * a.G + g) * dh * a.S_pad;
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i) {
+        k[i] = i < DQ ? ld<T>(a.K, kbase + i) : 0.f;
+        v[i] = i < DQ ? ld<T>(a.Vt, vbase + (int64_t)(d0 + i) * a.S_pad + vt_pos(jk)) : 0.f;
+        dk[i] = dv[i] = 0.f;
+    }
+    const int nqt = (int)ceil_div(a.S, 64);
     for (int h = 0; h < a.H; ++h) {
-        if (group_of(a, h) != g) continue;
-        for (int64_t s = j; s < a.S; ++s) {
-            const int64_t qo = ((b * a.H + h) * a.S + s) * dh;
-            const int64_t qi = (b * a.S + s) * a.H + h;
-            const float* dov = a.dO + qi * dh;
-            float sc = 0.f, dA = 0.f;
-            for (int i = 0; i < dh; ++i) {
-                sc += ld<T>(a.Q, qo + i) * ld<T>(a.K, kb + i);
-                dA += dov[i] * ld<T>(a.Vt, vb + (int64_t)i * a.S_pad + vt_pos(j));
+        if (group_of(a, h) != g) continue;  // uniform over the work group
+        for (int qt = kb; qt < nqt; ++qt) {
+            __syncthreads();
+            for (int i = tid; i < 64 * dh; i += 256) {
+                const int qq = i / dh, c = i - qq * dh;
+                const int64_t sp = (int64_t)qt * 64 + qq;
+                const bool in = sp < a.S;
+                qs[qq][c] = in ? ld<T>(a.Q, ((b * a.H + h) * a.S + sp) * dh + c) : 0.f;
+                ds[qq][c] = in ? a.dO[((b * a.S + sp) * a.H + h) * dh + c] : 0.f;
             }
-            const float pj = exp2f(sc - a.lse[qi]);
-            const float dz = pj * (dA - a.Dd[qi]);
-            for (int i = 0; i < 16; ++i) {
-                dk[i] += dz * ld<T>(a.Q, qo + j0 + i) * qs;
-                dv[i] += pj * dov[j0 + i];
+            if (tid < 64) {
+                const int64_t sp = (int64_t)qt * 64 + tid;
+                const int64_t ti = (b * a.S + (sp < a.S ? sp : 0)) * a.H + h;
+                ls[tid] = a.lse[ti];
+                dd[tid] = a.Dd[ti];
+            }
+            __syncthreads();
+            for (int qq = 0; qq < 64; ++qq) {
+                const int64_t sp = (int64_t)qt * 64 + qq;
+                float p = 0.f, da = 0.f;
+#pragma unroll
+                for (int i = 0; i < kDQ; ++i)
+                    if (i < DQ) {
+                        p += qs[qq][d0 + i] * k[i];
+                        da += ds[qq][d0 + i] * v[i];
+                    }
+                const float sc = quad_sum(p), dA = quad_sum(da);
+                const bool on = sp < a.S && sp >= jk;
+                const float pj = on ? exp2f(sc - ls[qq]) : 0.f;
+                const float dz = pj * (dA - dd[qq]);
+#pragma unroll
+                for (int i = 0; i < kDQ; ++i)
+                    if (i < DQ) {
+                        dk[i] += dz * qs[qq][d0 + i];
+                        dv[i] += pj * ds[qq][d0 + i];
+                    }
             }
         }
     }
-    if (a.rope) rope_back(dk, 16, j, a.rope, j0);
-    for (int i = 0; i < 16; ++i) {
-        a.dK[(t * a.G + g) * dh + j0 + i] = dk[i];
-        a.dV[(t * a.G + g) * dh + j0 + i] = dv[i];
-    }
+    if (!valid) return;
+    // the stored queries carry log2(e)/sqrt(d_h): q / sqrt(d_h) = q~ / log2(e)
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i) dk[i] *= 1.f / kLog2e;
+    if (a.rope)
+#pragma unroll
+        for (int i = 0; i < kDQ; i += 2)
+            if (i < DQ) rope_pair(dk[i], dk[i + 1], -j, a.rope[(d0 + i) >> 1]);
+    const int64_t t = b * a.S + j;
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i)
+        if (i < DQ) {
+            a.dK[(t * a.G + g) * dh + d0 + i] = dk[i];
+            a.dV[(t * a.G + g) * dh + d0 + i] = dv[i];
+        }
 }
 
-// ---------------------------------------------------------------- weight gradients
-// W_o[e] / W_oR[g] / W_os: thread per (slot matrix, j, c), summed over the tokens in order
+// ---------------------------------------------------------------- tiled float32 GEMM
+// C[M][N] (=, +=) sum_k A(m, k) B(k, n) for a set of sub-problems (blockIdx.z): 64 x 64 tiles of C,
+// K in chunks of 16 staged in LDS, 256 threads with a 4 x 4 block each.  The problem type supplies
+// the sizes (possibly read on the device: gathered token lists), the element loaders and the
+// store; AK / BK say whether A / B are contiguous along k (then 16 neighbouring threads read 16
+// consecutive k of one row), else along m / n.
+template <class Prob, bool AK, bool BK>
+__global__ void __launch_bounds__(256) tgemm_kernel(Prob pr) {
+    __shared__ float As[16][68];
+    __shared__ float Bs[16][68];
+    typename Prob::Sub sp;
+    if (!pr.begin(blockIdx.z, sp)) return;
+    const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+    if (m0 >= sp.M || n0 >= sp.N) return;
+    const int tid = threadIdx.x, tm = tid >> 4, tn = tid & 15;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    for (int k0 = 0; k0 < sp.K; k0 += 16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = tid + 256 * q;
+            const int m = AK ? i >> 4 : i & 63, kk = AK ? i & 15 : i >> 6;
+            As[kk][m] = (m0 + m < sp.M && k0 + kk < sp.K) ? pr.lda(sp, m0 + m, k0 + kk) : 0.f;
+            const int n = BK ? i >> 4 : i & 63, kb = BK ? i & 15 : i >> 6;
+            Bs[kb][n] = (n0 + n < sp.N && k0 + kb < sp.K) ? pr.ldb(sp, k0 + kb, n0 + n) : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            const f32x4_t av = *reinterpret_cast<const f32x4_t*>(&As[kk][tm * 4]);
+            const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(&Bs[kk][tn * 4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] += av[i] * bv[j];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = m0 + tm * 4 + i, n = n0 + tn * 4 + j;
+            if (m < sp.M && n < sp.N) pr.store(sp, m, n, acc[i][j]);
+        }
+}
+
+// Token lists of the routed experts (global bucketing of the forward's routing): the m-th token of
+// expert e is perm[offs[e] + m]; its rank r is where e sits in idx[t][g].
+struct Lists {
+    const int32_t* offs;  // [N + 1]
+    const int32_t* perm;  // [T G k]
+};
+__device__ __forceinline__ int rank_of(const BwdArgs& a, int64_t t, int e) {
+    const int g = e / a.n;
+    const int32_t* id = a.idx + (t * a.G + g) * a.k;
+    int r = 0;
+    for (int q = 0; q < a.k; ++q)
+        if (id[q] == e) r = q;
+    return r;
+}
+
+// U[t][slot] = dy_t W_slot^T: sub-problem = slot matrix (expert e, group slot g, shared head);
+// M = its tokens, N = d_h, K = d.
 template <typename T>
-__global__ void bwd_wgrad_o_kernel(BwdArgs a) {
-    const bool rslot = !a.dense && a.variant == GQE_VARIANT_GQE;
-    const int nsm = a.N + (rslot ? a.G : 0) + a.s;
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t per = (int64_t)a.dh * a.d;
-    if (q >= nsm * per) return;
-    const int sm = (int)(q / per), j = (int)((q % per) / a.d), c = (int)(q % a.d);
-    const int nr = a.G * a.k;
-    float acc = 0.f;
-    for (int64_t t = 0; t < a.T; ++t) {
-        const float g = ld<T>(a.dy, t * a.d + c);
-        const int64_t ob = t * a.H * a.dh;  // O is token-major: [B][S][H][dh]
-        float v = 0.f;
-        if (sm < a.N) {
-            const int gg = sm / a.n;
-            for (int r = 0; r < a.k; ++r) {
-                const int h = gg * a.k + r;
-                if (expert_of(a, t, h) == sm) v += a.cf[t * a.H + h] * ld<T>(a.O, ob + h * a.dh + j);
+struct ProbU {
+    BwdArgs a;
+    Lists L;
+    struct Sub {
+        int M, N, K, kind, e, g, base;
+    };
+    __device__ bool begin(int z, Sub& s) const {
+        const bool rslot = !a.dense && a.variant == GQE_VARIANT_GQE;
+        s.N = a.dh;
+        s.K = a.d;
+        s.e = s.g = s.base = 0;
+        if (z < a.N) {
+            s.kind = 0;
+            s.e = z;
+            s.g = z / a.n;
+            if (a.dense) {
+                s.M = (int)a.T;
+            } else {
+                s.base = L.offs[z];
+                s.M = L.offs[z + 1] - s.base;
             }
-        } else if (rslot && sm < a.N + a.G) {
-            const int gg = sm - a.N;
+        } else if (rslot && z < a.N + a.G) {
+            s.kind = 1;
+            s.g = z - a.N;
+            s.M = (int)a.T;
+        } else {
+            s.kind = 2;
+            s.M = (int)a.T;
+        }
+        return s.M > 0;
+    }
+    __device__ int64_t tok(const Sub& s, int m) const { return (s.kind == 0 && !a.dense) ? L.perm[s.base + m] : m; }
+    __device__ float lda(const Sub& s, int m, int k) const { return ld<T>(a.dy, tok(s, m) * a.d + k); }
+    __device__ float ldb(const Sub& s, int k, int n) const {
+        const T* W = s.kind == 0 ? (const T*)a.wo + (int64_t)s.e * a.dh * a.d
+                                 : (s.kind == 1 ? (const T*)a.wor + (int64_t)s.g * a.dh * a.d : (const T*)a.wos);
+        return to_f32(W[(int64_t)n * a.d + k]);
+    }
+    __device__ void store(const Sub& s, int m, int n, float v) const {
+        const int64_t t = tok(s, m);
+        const bool rslot = !a.dense && a.variant == GQE_VARIANT_GQE;
+        int ls;
+        if (s.kind == 0) ls = s.g * a.k + (a.dense ? s.e % a.n : rank_of(a, t, s.e));
+        else if (s.kind == 1) ls = a.G * a.k + s.g;
+        else ls = a.G * a.k + (rslot ? a.G : 0);
+        a.U[(t * a.NS + ls) * a.dh + n] = v;
+    }
+};
+
+// weight gradients of the output slots: dW[j][c] = sum_t v_t[j] dy_t[c]; M = d_h, N = d, K = tokens
+template <typename T>
+struct ProbWo {
+    BwdArgs a;
+    Lists L;
+    typedef typename ProbU<T>::Sub Sub;
+    __device__ bool begin(int z, Sub& s) const {
+        ProbU<T> u{a, L};
+        if (!u.begin(z, s)) {
+            // no token: the gradient block is zero
+            s.K = 0;
+            s.M = a.dh;
+            s.N = a.d;
+            return true;
+        }
+        s.K = s.M;
+        s.M = a.dh;
+        s.N = a.d;
+        return true;
+    }
+    __device__ int64_t tok(const Sub& s, int k) const { return (s.kind == 0 && !a.dense) ? L.perm[s.base + k] : k; }
+    __device__ float lda(const Sub& s, int j, int k) const {
+        const int64_t t = tok(s, k);
+        const int64_t ob = t * a.H * a.dh;  // O is token-major
+        if (s.kind == 0) {
+            const int h = s.g * a.k + (a.dense ? s.e % a.n : rank_of(a, t, s.e));
+            return a.cf[t * a.H + h] * ld<T>(a.O, ob + h * a.dh + j);
+        }
+        if (s.kind == 1) {
+            float v = 0.f;
             for (int r = 0; r < a.k; ++r) {
-                const int h = gg * a.k + r;
+                const int h = s.g * a.k + r;
                 v += a.wn[t * a.H + h] * ld<T>(a.O, ob + h * a.dh + j);
             }
-        } else {
-            v = ld<T>(a.O, ob + nr * a.dh + j);
+            return v;
         }
-        acc += v * g;
+        return ld<T>(a.O, ob + a.G * a.k * a.dh + j);
     }
-    float* dst = sm < a.N ? a.dwo + (int64_t)sm * per
-                          : (rslot && sm < a.N + a.G ? a.dwor + (int64_t)(sm - a.N) * per : a.dwos);
-    dst[(int64_t)j * a.d + c] = acc;
-}
+    __device__ float ldb(const Sub& s, int k, int n) const { return ld<T>(a.dy, tok(s, k) * a.d + n); }
+    __device__ void store(const Sub& s, int m, int n, float v) const {
+        const int per = a.dh * a.d;
+        float* dst = s.kind == 0 ? a.dwo + (int64_t)s.e * per : (s.kind == 1 ? a.dwor + (int64_t)s.g * per : a.dwos);
+        dst[(int64_t)m * a.d + n] = v;
+    }
+};
 
-// W_k, W_v (per group), W_qs, W_q[e]: thread per (head block, i, j), summed over the tokens
+// input-side weight gradients dW[i][j] = sum_t x_t[i] g_t[j]: sub-problem = head block (K_g, V_g,
+// shared query, expert e) or the router (N columns, plus the bias as row i = d); M = d (+1),
+// N = d_h (N), K = tokens
 template <typename T>
-__global__ void bwd_wgrad_x_kernel(BwdArgs a) {
-    const int nhb = 2 * a.G + a.s + a.N;
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t per = (int64_t)a.d * a.dh;
-    if (q >= nhb * per) return;
-    const int hb = (int)(q / per), i = (int)((q % per) / a.dh), j = (int)(q % a.dh);
-    const int ebase = 2 * a.G + a.s, nr = a.G * a.k;
-    float acc = 0.f;
-    for (int64_t t = 0; t < a.T; ++t) {
-        const float xv = ld<T>(a.x, t * a.d + i);
-        float gv = 0.f;
-        if (hb < a.G) gv = a.dK[(t * a.G + hb) * a.dh + j];
-        else if (hb < 2 * a.G) gv = a.dV[(t * a.G + hb - a.G) * a.dh + j];
-        else if (hb < ebase) gv = a.dQ[(t * a.H + nr) * a.dh + j];
-        else {
-            const int e = hb - ebase, gg = e / a.n;
-            for (int r = 0; r < a.k; ++r) {
-                const int h = gg * a.k + r;
-                if (expert_of(a, t, h) == e) gv += a.dQ[(t * a.H + h) * a.dh + j];
+struct ProbWx {
+    BwdArgs a;
+    Lists L;
+    struct Sub {
+        int M, N, K, hb, e, g, base;
+    };
+    __device__ bool begin(int z, Sub& s) const {
+        const int ebase = 2 * a.G + a.s;
+        s.hb = z;
+        s.M = a.d;
+        s.N = a.dh;
+        s.K = (int)a.T;
+        s.e = s.g = s.base = 0;
+        if (z == ebase + a.N) {  // router
+            if (a.dense) return false;
+            s.M = a.d + 1;
+            s.N = a.N;
+        } else if (z >= ebase) {
+            s.e = z - ebase;
+            s.g = s.e / a.n;
+            if (!a.dense) {
+                s.base = L.offs[s.e];
+                s.K = L.offs[s.e + 1] - s.base;
             }
         }
-        acc += xv * gv;
+        return true;
     }
-    if (hb < a.G) a.dwk[(int64_t)i * a.G * a.dh + hb * a.dh + j] = acc;
-    else if (hb < 2 * a.G) a.dwv[(int64_t)i * a.G * a.dh + (hb - a.G) * a.dh + j] = acc;
-    else if (hb < ebase) a.dwqs[(int64_t)i * a.dh + j] = acc;
-    else a.dwq[((int64_t)(hb - ebase) * a.d + i) * a.dh + j] = acc;
-}
-
-// W_r (thread per (i, e)) and b_r (i == d)
-template <typename T>
-__global__ void bwd_wgrad_r_kernel(BwdArgs a) {
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= (int64_t)(a.d + 1) * a.N) return;
-    const int i = (int)(q / a.N), e = (int)(q % a.N);
-    float acc = 0.f;
-    for (int64_t t = 0; t < a.T; ++t) acc += (i < a.d ? ld<T>(a.x, t * a.d + i) : 1.f) * a.dl[t * a.N + e];
-    if (i < a.d) a.dwr[(int64_t)i * a.N + e] = acc;
-    else a.dbr[e] = acc;
-}
-
-// dx[t][i]: every head block of the token (dq W^T, dk W_k^T, dv W_v^T) and the router logits
-template <typename T>
-__global__ void bwd_dx_kernel(BwdArgs a) {
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= a.T * a.d) return;
-    const int64_t t = q / a.d;
-    const int i = (int)(q % a.d);
-    const int dh = a.dh, GD = a.G * dh, nr = a.G * a.k;
-    float acc = 0.f;
-    for (int h = 0; h < a.H; ++h) {
-        const float* g = a.dQ + (t * a.H + h) * dh;
-        const T* w = h < nr ? (const T*)a.wq + ((int64_t)expert_of(a, t, h) * a.d + i) * dh
-                            : (const T*)a.wqs + (int64_t)i * dh;
-        for (int j = 0; j < dh; ++j) acc += g[j] * to_f32(w[j]);
+    __device__ int64_t tok(const Sub& s, int k) const {
+        const int ebase = 2 * a.G + a.s;
+        return (s.hb >= ebase && s.hb < ebase + a.N && !a.dense) ? L.perm[s.base + k] : k;
     }
-    const T* wk = (const T*)a.wk + (int64_t)i * GD;
-    const T* wv = (const T*)a.wv + (int64_t)i * GD;
-    for (int c = 0; c < GD; ++c) acc += a.dK[t * GD + c] * to_f32(wk[c]) + a.dV[t * GD + c] * to_f32(wv[c]);
-    if (!a.dense)
-        for (int e = 0; e < a.N; ++e) acc += a.dl[t * a.N + e] * a.wr[(int64_t)i * a.N + e];
-    a.dx[q] = acc;
+    __device__ float lda(const Sub& s, int i, int k) const {
+        return i < a.d ? ld<T>(a.x, tok(s, k) * a.d + i) : 1.f;
+    }
+    __device__ float ldb(const Sub& s, int k, int j) const {
+        const int ebase = 2 * a.G + a.s;
+        const int64_t t = tok(s, k);
+        if (s.hb < a.G) return a.dK[(t * a.G + s.hb) * a.dh + j];
+        if (s.hb < 2 * a.G) return a.dV[(t * a.G + s.hb - a.G) * a.dh + j];
+        if (s.hb < ebase) return a.dQ[(t * a.H + a.G * a.k) * a.dh + j];
+        if (s.hb < ebase + a.N) {
+            const int h = s.g * a.k + (a.dense ? s.e % a.n : rank_of(a, t, s.e));
+            return a.dQ[(t * a.H + h) * a.dh + j];
+        }
+        return a.dl[t * a.N + j];
+    }
+    __device__ void store(const Sub& s, int i, int j, float v) const {
+        const int ebase = 2 * a.G + a.s;
+        if (s.hb < a.G) a.dwk[(int64_t)i * a.G * a.dh + s.hb * a.dh + j] = v;
+        else if (s.hb < 2 * a.G) a.dwv[(int64_t)i * a.G * a.dh + (s.hb - a.G) * a.dh + j] = v;
+        else if (s.hb < ebase) a.dwqs[(int64_t)i * a.dh + j] = v;
+        else if (s.hb < ebase + a.N) a.dwq[((int64_t)s.e * a.d + i) * a.dh + j] = v;
+        else if (i < a.d) a.dwr[(int64_t)i * a.N + j] = v;
+        else a.dbr[j] = v;
+    }
+};
+
+// dx, dense part (written): K = [dK (G d_h) | dV (G d_h) | shared dq (d_h) | router logits (N)]
+template <typename T>
+struct ProbDxDense {
+    BwdArgs a;
+    struct Sub {
+        int M, N, K;
+    };
+    __device__ bool begin(int, Sub& s) const {
+        s.M = (int)a.T;
+        s.N = a.d;
+        s.K = 2 * a.G * a.dh + a.s * a.dh + (a.dense ? 0 : a.N);
+        return true;
+    }
+    __device__ float lda(const Sub&, int t, int kk) const {
+        const int GD = a.G * a.dh;
+        if (kk < GD) return a.dK[(int64_t)t * GD + kk];
+        if (kk < 2 * GD) return a.dV[(int64_t)t * GD + kk - GD];
+        kk -= 2 * GD;
+        if (a.s && kk < a.dh) return a.dQ[((int64_t)t * a.H + a.G * a.k) * a.dh + kk];
+        kk -= a.s * a.dh;
+        return a.dl[(int64_t)t * a.N + kk];
+    }
+    __device__ float ldb(const Sub&, int kk, int i) const {
+        const int GD = a.G * a.dh;
+        if (kk < GD) return ld<T>(a.wk, (int64_t)i * GD + kk);
+        if (kk < 2 * GD) return ld<T>(a.wv, (int64_t)i * GD + kk - GD);
+        kk -= 2 * GD;
+        if (a.s && kk < a.dh) return ld<T>(a.wqs, (int64_t)i * a.dh + kk);
+        kk -= a.s * a.dh;
+        return a.wr[(int64_t)i * a.N + kk];
+    }
+    __device__ void store(const Sub&, int t, int i, float v) const { a.dx[(int64_t)t * a.d + i] = v; }
+};
+
+// dx, routed part (added): one launch per (group g, choice rank r), sub-problem = expert e of the
+// group; M = its tokens (those whose rank-r choice is another expert load zeros and store nothing),
+// N = d, K = d_h.  Inside one launch every token has exactly one such expert, so the adds never
+// collide; the launches follow each other on the stream.
+template <typename T>
+struct ProbDxRouted {
+    BwdArgs a;
+    Lists L;
+    int g, r;
+    struct Sub {
+        int M, N, K, e, base;
+    };
+    __device__ bool begin(int z, Sub& s) const {
+        s.e = g * a.n + z;
+        s.N = a.d;
+        s.K = a.dh;
+        if (a.dense) {
+            s.base = 0;
+            s.M = (z == r) ? (int)a.T : 0;
+        } else {
+            s.base = L.offs[s.e];
+            s.M = L.offs[s.e + 1] - s.base;
+        }
+        return s.M > 0;
+    }
+    __device__ int64_t tok(const Sub& s, int m) const { return a.dense ? m : L.perm[s.base + m]; }
+    __device__ bool mine(const Sub& s, int64_t t) const { return a.dense || rank_of(a, t, s.e) == r; }
+    __device__ float lda(const Sub& s, int m, int j) const {
+        const int64_t t = tok(s, m);
+        if (!mine(s, t)) return 0.f;
+        return a.dQ[(t * a.H + g * a.k + r) * a.dh + j];
+    }
+    __device__ float ldb(const Sub& s, int j, int i) const { return ld<T>(a.wq, ((int64_t)s.e * a.d + i) * a.dh + j); }
+    __device__ void store(const Sub& s, int m, int i, float v) const {
+        const int64_t t = tok(s, m);
+        if (mine(s, t)) a.dx[t * a.d + i] += v;
+    }
+};
+
+template <class Prob, bool AK, bool BK>
+void tgemm(const Prob& p, int maxM, int maxN, int nsub, hipStream_t st) {
+    const dim3 grid((unsigned)ceil_div(maxN, 64), (unsigned)ceil_div(maxM, 64), (unsigned)nsub);
+    tgemm_kernel<Prob, AK, BK><<<grid, 256, 0, st>>>(p);
 }
 
 template <typename T>
-hipError_t run(const BwdArgs& a, hipStream_t st, KernelMarks* km) {
+hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km) {
     auto blocks = [](int64_t n) { return (unsigned)ceil_div(n, 256); };
     const bool rslot = !a.dense && a.variant == GQE_VARIANT_GQE;
+    const int nsm = a.N + (rslot ? a.G : 0) + a.s;
+    const int nt = (int)a.T;
     if (km) km->begin(KT_BWD_OUT);
-    bwd_u_kernel<T><<<blocks(a.T * a.NS * a.dh), 256, 0, st>>>(a);
+    tgemm<ProbU<T>, true, true>(ProbU<T>{a, L}, nt, a.dh, nsm, st);
     bwd_route_kernel<T><<<blocks(a.T * a.G), 256, 0, st>>>(a);
     if (km) km->mark(KT_BWD_OUT);
     if (km) km->begin(KT_BWD_ATTN);
-    bwd_lse_kernel<T><<<blocks(a.T * a.H), 256, 0, st>>>(a);
-    bwd_dq_kernel<T><<<blocks(a.T * a.H), 256, 0, st>>>(a);
-    bwd_dkv_kernel<T><<<blocks(a.T * a.G * (a.dh / 16)), 256, 0, st>>>(a);
+    const unsigned nblk = (unsigned)ceil_div(a.S, 64);
+    bwd_dq_kernel<T><<<dim3(nblk, (unsigned)a.H, (unsigned)a.B), 256, 0, st>>>(a);
+    bwd_dkv_kernel<T><<<dim3(nblk, (unsigned)a.G, (unsigned)a.B), 256, 0, st>>>(a);
     if (km) km->mark(KT_BWD_ATTN);
     if (km) km->begin(KT_BWD_WGRAD);
-    const int nsm = a.N + (rslot ? a.G : 0) + a.s;
-    bwd_wgrad_o_kernel<T><<<blocks((int64_t)nsm * a.dh * a.d), 256, 0, st>>>(a);
-    bwd_wgrad_x_kernel<T><<<blocks((int64_t)(2 * a.G + a.s + a.N) * a.d * a.dh), 256, 0, st>>>(a);
-    if (!a.dense) bwd_wgrad_r_kernel<T><<<blocks((int64_t)(a.d + 1) * a.N), 256, 0, st>>>(a);
+    tgemm<ProbWo<T>, false, false>(ProbWo<T>{a, L}, a.dh, a.d, nsm, st);
+    tgemm<ProbWx<T>, false, false>(ProbWx<T>{a, L}, a.d + 1, a.dh > a.N ? a.dh : a.N, 2 * a.G + a.s + a.N + 1, st);
     if (km) km->mark(KT_BWD_WGRAD);
     if (km) km->begin(KT_BWD_DX);
-    bwd_dx_kernel<T><<<blocks(a.T * a.d), 256, 0, st>>>(a);
+    tgemm<ProbDxDense<T>, true, true>(ProbDxDense<T>{a}, nt, a.d, 1, st);
+    for (int g = 0; g < a.G; ++g)
+        for (int r = 0; r < a.k; ++r) tgemm<ProbDxRouted<T>, true, true>(ProbDxRouted<T>{a, L, g, r}, nt, a.d, a.n, st);
     if (km) km->mark(KT_BWD_DX);
     return hipGetLastError();
 }
@@ -504,5 +769,11 @@ hipError_t launch_backward(const GqeDims& D, const WorkPlan& P, const BwdPlan& B
     a.dense = D.dense;
     a.NS = BP.NS;
     a.Np = (int)round_up(D.N, 16);
-    return D.dtype == GQE_DTYPE_BF16 ? run<bf16_t>(a, st, km) : run<float>(a, st, km);
+    Lists L{(const int32_t*)(ws + BP.offs), (const int32_t*)(ws + BP.perm)};
+    if (!D.dense) {
+        const hipError_t e = launch_bucket(D, P, const_cast<char*>(fws), (int32_t*)(ws + BP.offs),
+                                           (int32_t*)(ws + BP.perm), (int32_t*)(ws + BP.inv), st);
+        if (e != hipSuccess) return e;
+    }
+    return D.dtype == GQE_DTYPE_BF16 ? run<bf16_t>(a, L, st, km) : run<float>(a, L, st, km);
 }
