@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16 = 2500.0   # TFLOP/s, MI355X dense bf16 matrix
 PEAK_FP64 = 78.6     # TFLOP/s, MI355X fp64 (matrix and vector)
 PEAK_HBM = 8000.0    # GB/s
+PEAK_FP32 = 157.3    # TFLOP/s, MI355X float32 vector (the backward's arithmetic)
 
 # kernel slot -> (source file of the kernel, stage of the algorithmic-work table)
 KERNEL_SOURCES = {
@@ -235,6 +236,64 @@ def decode_report(steps: int, warmup: int) -> dict:
                 speedup_attention=g_att / att if att > 0 else None)
 
 
+def backward_flops(wl) -> float:
+    """Multiply-add work of one backward pass, per the chain rule of the forward's contractions
+    (2 flops per multiply-add): every forward GEMM appears twice (input and weight gradient), the
+    causal attention five times over its S(S+1)/2 score entries per head (the recomputed scores,
+    the log-sum-exp pass, do . v, dq, dk and dv: 6 d_h-long products per entry, counted as 6)."""
+    alg = algorithmic(wl)
+    dh, B, S = wl.dh, wl.batch, wl.seq
+    H = wl.num_kv_heads * wl.top_k + (1 if wl.shared_head else 0)
+    att = 2.0 * dh * H * B * S * (S + 1) / 2.0 * 6
+    return 2 * (alg["projection"]["flops"] + alg["combine"]["flops"]) + att
+
+
+def run_backward(wl, steps, warmup, aux_coef=0.01):
+    """Forward once, then backward passes of sum(dy * y) + aux_coef * aux on the stored forward."""
+    import numpy as np
+    import torch
+    from sparse_moe_query_amd import gqe
+    from sparse_moe_query_amd.runner import build_layer
+    layer, x, _ = build_layer(wl)
+    gen = torch.Generator(device=x.device)
+    gen.manual_seed(4321)
+    dy = torch.empty_like(x).normal_(0.0, 1.0, generator=gen)
+    layer(x)
+    for _ in range(warmup):
+        layer.backward(x, dy, aux_coef)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g = layer.backward(x, dy, aux_coef)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    gqe.gqe_profile_enable(layer.h, True)
+    for _ in range(steps):
+        layer.backward(x, dy, aux_coef)
+    torch.cuda.synchronize()
+    kern, n = gqe.gqe_profile_read_kernels(layer.h)
+    gqe.gqe_profile_enable(layer.h, False)
+    km = {k: v / max(n, 1) for k, v in kern.items() if v > 0}
+    finite = all(bool(torch.isfinite(v).all()) for v in g.values())
+    layer.close()
+    del layer, x, dy, g
+    torch.cuda.empty_cache()
+    return ms, km, finite
+
+
+def backward_report(steps: int, warmup: int) -> dict:
+    from sparse_moe_query_amd.inputs import WORKLOADS
+    wl = WORKLOADS["main_b8_s2048"]
+    log("[bench] backward main_b8_s2048")
+    ms, km, finite = run_backward(wl, steps, warmup)
+    fl = backward_flops(wl)
+    tf = fl / (ms * 1e-3) / 1e12
+    log(f"[bench] backward: {ms:.3f} ms ({tf:.1f} TFLOP/s float32 vector); kernels {km}")
+    return dict(workload=wl.name, ms=ms, tokens_s=wl.tokens / (ms / 1e3), kernel_ms=km, finite=finite,
+                aux_coef=0.01, flops=fl,
+                roofline=dict(bound="alu", achieved=tf, peak=PEAK_FP32, unit="TFLOP/s", frac=tf / PEAK_FP32))
+
+
 def cpu_baseline(wl, min_seconds=10.0):
     """The oracle as it stands, on whole sequences of the workload (all of their tokens), repeated
     over the batch until at least ``min_seconds`` of CPU work have been timed."""
@@ -277,6 +336,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="main workload only (for profilers)")
     ap.add_argument("--profile-workload", default=None,
                     help="run only this named workload (inputs.WORKLOADS, or NAME_gqa for its "
@@ -304,6 +364,13 @@ def main():
         wl, _, _, ms, kernel_ms = run_decode(name[:-4] if gqa else name, args.steps, args.warmup, gqa=gqa)
         print(json.dumps({"workload": wl.name, "ms_per_step": ms, "kernel_ms": kernel_ms,
                           "source_hash": source_hash("k_decode.hip")}), flush=True)
+        return
+    if args.profile_workload == "backward_main_b8_s2048":
+        if args.copy_calibration:
+            copy_calibration()
+        ms, km, _ = run_backward(WORKLOADS["main_b8_s2048"], args.steps, args.warmup)
+        print(json.dumps({"workload": args.profile_workload, "ms_per_step": ms, "kernel_ms": km,
+                          "source_hash": source_hash("k_backward.hip")}), flush=True)
         return
     if args.profile_workload:
         name = args.profile_workload
@@ -378,6 +445,8 @@ def main():
         result["long_context"] = long
     if not args.no_decode and not args.only_main:
         result["decode"] = decode_report(max(10, args.steps), args.warmup)
+    if not args.no_backward and not args.only_main:
+        result["backward"] = backward_report(3, 1)
     if not args.no_cpu and not args.only_main:
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(main_wl)

@@ -67,7 +67,8 @@ struct DecodePlan {
 struct BwdPlan {
     int NS;                           // output-projection slots of one token
     size_t U, dO, Dd, lse, dl, cf, wn, dQ, dK, dV;
-    size_t offs, perm, inv;           // token lists of the routed experts (bucketing)
+    size_t offs, perm, inv, rank;     // token lists of the routed experts (bucketing) and choice ranks
+    size_t part;                      // split-K partial sums of the weight gradients
     size_t total;
 };
 

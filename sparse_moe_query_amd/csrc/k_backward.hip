@@ -36,6 +36,7 @@
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWgradSplits = 8;  // split-K pieces of the weight gradients (sums over the tokens)
 
 struct BwdArgs {
     const void* x;          // [T][d]
@@ -65,6 +66,7 @@ struct BwdArgs {
     float* dQ;              // [T][H][dh] (before the rotation)
     float* dK;              // [T][G][dh] (before the rotation)
     float* dV;              // [T][G][dh]
+    float* part;            // split-K partial sums of the weight gradients
     // outputs (float32)
     float *dx, *dwr, *dbr, *dwq, *dwqs, *dwk, *dwv, *dwo, *dwor, *dwos;
     double aux_coef;
@@ -197,28 +199,28 @@ __device__ __forceinline__ float quad_sum(float v) {
     return v;
 }
 
-constexpr int kDQ = 32;  // largest quarter of a head (d_h <= 128)
+constexpr int kPitch = 132;  // LDS row pitch (floats): 16-byte aligned rows, d_h <= 128
 
 // dq for a block of 64 queries of one (sequence, head): pass 1 recomputes each row's log-sum-exp
 // over the causal keys (online, log2 units), pass 2 sums dz_j k_j with dz_j = p_j (do . v_j - D).
-template <typename T>
+template <typename T, int DQ>
 __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
-    __shared__ float ks[64][129];
-    __shared__ float vs[64][129];
+    __shared__ __align__(16) float ks[64][kPitch];
+    __shared__ __align__(16) float vs[64][kPitch];
     const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int g = group_of(a, h);
-    const int dh = a.dh, DQ = dh / 4;
+    const int dh = a.dh;
     const int qi = tid >> 2, qd = tid & 3, d0 = qd * DQ;
     const int64_t s = (int64_t)qb * 64 + qi;
     const bool valid = s < a.S;
     const int64_t sq = valid ? s : a.S - 1;
     const int64_t t = b * a.S + sq;
-    float q[kDQ], dov[kDQ], dq[kDQ];
+    float q[DQ], dov[DQ], dq[DQ];
     const int64_t qo = ((b * a.H + h) * a.S + sq) * dh + d0;
 #pragma unroll
-    for (int i = 0; i < kDQ; ++i) {
-        q[i] = i < DQ ? ld<T>(a.Q, qo + i) : 0.f;
-        dov[i] = i < DQ ? a.dO[(t * a.H + h) * dh + d0 + i] : 0.f;
+    for (int i = 0; i < DQ; ++i) {
+        q[i] = ld<T>(a.Q, qo + i);
+        dov[i] = a.dO[(t * a.H + h) * dh + d0 + i];
         dq[i] = 0.f;
     }
     const float D = a.Dd[t * a.H + h];
@@ -248,73 +250,72 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
         for (int kk = 0; kk < 64; ++kk) {
             float p = 0.f;
 #pragma unroll
-            for (int i = 0; i < kDQ; ++i)
-                if (i < DQ) p += q[i] * ks[kk][d0 + i];
-            const float sc = quad_sum(p);
-            if (kk < nk) {
-                if (sc > m) {
-                    l = l * exp2f(m - sc) + 1.f;
-                    m = sc;
-                } else {
-                    l += exp2f(sc - m);
-                }
+            for (int i = 0; i < DQ; i += 4) {
+                const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(&ks[kk][d0 + i]);
+                p += q[i] * kv[0] + q[i + 1] * kv[1] + q[i + 2] * kv[2] + q[i + 3] * kv[3];
             }
+            const float sc = kk < nk ? quad_sum(p) : -INFINITY;
+            const float mn = fmaxf(m, sc);
+            l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(sc - mn);
+            m = mn;
         }
     }
-    const float L = m + log2f(l);
+    const float L = m + __builtin_amdgcn_logf(l);
     // pass 2
     for (int kt = 0; kt < ntiles; ++kt) {
         stage(kt, true);
         const int nk = (int)min<int64_t>(64, sq + 1 - (int64_t)kt * 64);
         for (int kk = 0; kk < 64; ++kk) {
             float p = 0.f, da = 0.f;
+            f32x4_t kr[DQ / 4];
 #pragma unroll
-            for (int i = 0; i < kDQ; ++i)
-                if (i < DQ) {
-                    p += q[i] * ks[kk][d0 + i];
-                    da += dov[i] * vs[kk][d0 + i];
+            for (int i = 0; i < DQ; i += 4) {
+                kr[i / 4] = *reinterpret_cast<const f32x4_t*>(&ks[kk][d0 + i]);
+                const f32x4_t vv = *reinterpret_cast<const f32x4_t*>(&vs[kk][d0 + i]);
+#pragma unroll
+                for (int z = 0; z < 4; ++z) {
+                    p += q[i + z] * kr[i / 4][z];
+                    da += dov[i + z] * vv[z];
                 }
+            }
             const float sc = quad_sum(p), dA = quad_sum(da);
-            const float dz = kk < nk ? exp2f(sc - L) * (dA - D) : 0.f;
+            const float dz = kk < nk ? __builtin_amdgcn_exp2f(sc - L) * (dA - D) : 0.f;
 #pragma unroll
-            for (int i = 0; i < kDQ; ++i)
-                if (i < DQ) dq[i] += dz * ks[kk][d0 + i];
+            for (int i = 0; i < DQ; ++i) dq[i] += dz * kr[i / 4][i % 4];
         }
     }
     if (!valid) return;
     const float sc = 1.f / sqrtf((float)dh);
 #pragma unroll
-    for (int i = 0; i < kDQ; ++i) dq[i] *= sc;
+    for (int i = 0; i < DQ; ++i) dq[i] *= sc;
     if (a.rope)
 #pragma unroll
-        for (int i = 0; i < kDQ; i += 2)
-            if (i < DQ) rope_pair(dq[i], dq[i + 1], -s, a.rope[(d0 + i) >> 1]);
+        for (int i = 0; i < DQ; i += 2) rope_pair(dq[i], dq[i + 1], -s, a.rope[(d0 + i) >> 1]);
 #pragma unroll
-    for (int i = 0; i < kDQ; ++i)
-        if (i < DQ) a.dQ[(t * a.H + h) * dh + d0 + i] = dq[i];
+    for (int i = 0; i < DQ; ++i) a.dQ[(t * a.H + h) * dh + d0 + i] = dq[i];
     if (qd == 0) a.lse[t * a.H + h] = L;
 }
 
 // dk, dv for a block of 64 keys of one (sequence, group): every later query of every head of the
 // group, query tiles of 64 staged in LDS with their log-sum-exp and D.
-template <typename T>
+template <typename T, int DQ>
 __global__ void __launch_bounds__(256) bwd_dkv_kernel(BwdArgs a) {
-    __shared__ float qs[64][129];
-    __shared__ float ds[64][129];
+    __shared__ __align__(16) float qs[64][kPitch];
+    __shared__ __align__(16) float ds[64][kPitch];
     __shared__ float ls[64], dd[64];
     const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-    const int dh = a.dh, DQ = dh / 4;
+    const int dh = a.dh;
     const int kj = tid >> 2, qd = tid & 3, d0 = qd * DQ;
     const int64_t j = (int64_t)kb * 64 + kj;
     const bool valid = j < a.S;
     const int64_t jk = valid ? j : a.S - 1;
-    float k[kDQ], v[kDQ], dk[kDQ], dv[kDQ];
+    float k[DQ], v[DQ], dk[DQ], dv[DQ];
     const int64_t kbase = ((b * a.G + g) * a.S_pad + jk) * dh + d0;
     const int64_t vbase = (b * a.G + g) * dh * a.S_pad;
 #pragma unroll
-    for (int i = 0; i < kDQ; ++i) {
-        k[i] = i < DQ ? ld<T>(a.K, kbase + i) : 0.f;
-        v[i] = i < DQ ? ld<T>(a.Vt, vbase + (int64_t)(d0 + i) * a.S_pad + vt_pos(jk)) : 0.f;
+    for (int i = 0; i < DQ; ++i) {
+        k[i] = ld<T>(a.K, kbase + i);
+        v[i] = ld<T>(a.Vt, vbase + (int64_t)(d0 + i) * a.S_pad + vt_pos(jk));
         dk[i] = dv[i] = 0.f;
     }
     const int nqt = (int)ceil_div(a.S, 64);
@@ -339,40 +340,42 @@ __global__ void __launch_bounds__(256) bwd_dkv_kernel(BwdArgs a) {
             for (int qq = 0; qq < 64; ++qq) {
                 const int64_t sp = (int64_t)qt * 64 + qq;
                 float p = 0.f, da = 0.f;
+                f32x4_t qr[DQ / 4], dr[DQ / 4];
 #pragma unroll
-                for (int i = 0; i < kDQ; ++i)
-                    if (i < DQ) {
-                        p += qs[qq][d0 + i] * k[i];
-                        da += ds[qq][d0 + i] * v[i];
+                for (int i = 0; i < DQ; i += 4) {
+                    qr[i / 4] = *reinterpret_cast<const f32x4_t*>(&qs[qq][d0 + i]);
+                    dr[i / 4] = *reinterpret_cast<const f32x4_t*>(&ds[qq][d0 + i]);
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) {
+                        p += qr[i / 4][z] * k[i + z];
+                        da += dr[i / 4][z] * v[i + z];
                     }
+                }
                 const float sc = quad_sum(p), dA = quad_sum(da);
                 const bool on = sp < a.S && sp >= jk;
-                const float pj = on ? exp2f(sc - ls[qq]) : 0.f;
+                const float pj = on ? __builtin_amdgcn_exp2f(sc - ls[qq]) : 0.f;
                 const float dz = pj * (dA - dd[qq]);
 #pragma unroll
-                for (int i = 0; i < kDQ; ++i)
-                    if (i < DQ) {
-                        dk[i] += dz * qs[qq][d0 + i];
-                        dv[i] += pj * ds[qq][d0 + i];
-                    }
+                for (int i = 0; i < DQ; ++i) {
+                    dk[i] += dz * qr[i / 4][i % 4];
+                    dv[i] += pj * dr[i / 4][i % 4];
+                }
             }
         }
     }
     if (!valid) return;
     // the stored queries carry log2(e)/sqrt(d_h): q / sqrt(d_h) = q~ / log2(e)
 #pragma unroll
-    for (int i = 0; i < kDQ; ++i) dk[i] *= 1.f / kLog2e;
+    for (int i = 0; i < DQ; ++i) dk[i] *= 1.f / kLog2e;
     if (a.rope)
 #pragma unroll
-        for (int i = 0; i < kDQ; i += 2)
-            if (i < DQ) rope_pair(dk[i], dk[i + 1], -j, a.rope[(d0 + i) >> 1]);
+        for (int i = 0; i < DQ; i += 2) rope_pair(dk[i], dk[i + 1], -j, a.rope[(d0 + i) >> 1]);
     const int64_t t = b * a.S + j;
 #pragma unroll
-    for (int i = 0; i < kDQ; ++i)
-        if (i < DQ) {
-            a.dK[(t * a.G + g) * dh + d0 + i] = dk[i];
-            a.dV[(t * a.G + g) * dh + d0 + i] = dv[i];
-        }
+    for (int i = 0; i < DQ; ++i) {
+        a.dK[(t * a.G + g) * dh + d0 + i] = dk[i];
+        a.dV[(t * a.G + g) * dh + d0 + i] = dv[i];
+    }
 }
 
 // ---------------------------------------------------------------- tiled float32 GEMM
@@ -382,27 +385,31 @@ __global__ void __launch_bounds__(256) bwd_dkv_kernel(BwdArgs a) {
 // store; AK / BK say whether A / B are contiguous along k (then 16 neighbouring threads read 16
 // consecutive k of one row), else along m / n.
 template <class Prob, bool AK, bool BK>
-__global__ void __launch_bounds__(256) tgemm_kernel(Prob pr) {
+__global__ void __launch_bounds__(256) tgemm_kernel(Prob pr, int splits, float* part, int64_t pstride) {
     __shared__ float As[16][68];
     __shared__ float Bs[16][68];
     typename Prob::Sub sp;
-    if (!pr.begin(blockIdx.z, sp)) return;
+    const int sub = blockIdx.z / splits, piece = blockIdx.z % splits;
+    if (!pr.begin(sub, sp)) return;
     const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
     if (m0 >= sp.M || n0 >= sp.N) return;
+    // split-K: this work group sums k in [kb, ke) (16-aligned pieces)
+    const int kc = ((sp.K + splits - 1) / splits + 15) & ~15;
+    const int kb = piece * kc, ke = min(sp.K, kb + kc);
     const int tid = threadIdx.x, tm = tid >> 4, tn = tid & 15;
     float acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-    for (int k0 = 0; k0 < sp.K; k0 += 16) {
+    for (int k0 = kb; k0 < ke; k0 += 16) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int i = tid + 256 * q;
             const int m = AK ? i >> 4 : i & 63, kk = AK ? i & 15 : i >> 6;
-            As[kk][m] = (m0 + m < sp.M && k0 + kk < sp.K) ? pr.lda(sp, m0 + m, k0 + kk) : 0.f;
-            const int n = BK ? i >> 4 : i & 63, kb = BK ? i & 15 : i >> 6;
-            Bs[kb][n] = (n0 + n < sp.N && k0 + kb < sp.K) ? pr.ldb(sp, k0 + kb, n0 + n) : 0.f;
+            As[kk][m] = (m0 + m < sp.M && k0 + kk < ke) ? pr.lda(sp, m0 + m, k0 + kk) : 0.f;
+            const int n = BK ? i >> 4 : i & 63, kq = BK ? i & 15 : i >> 6;
+            Bs[kq][n] = (n0 + n < sp.N && k0 + kq < ke) ? pr.ldb(sp, k0 + kq, n0 + n) : 0.f;
         }
         __syncthreads();
 #pragma unroll
@@ -421,23 +428,37 @@ __global__ void __launch_bounds__(256) tgemm_kernel(Prob pr) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int m = m0 + tm * 4 + i, n = n0 + tn * 4 + j;
-            if (m < sp.M && n < sp.N) pr.store(sp, m, n, acc[i][j]);
+            if (m >= sp.M || n >= sp.N) continue;
+            if (splits == 1) pr.store(sp, m, n, acc[i][j]);
+            else part[(int64_t)blockIdx.z * pstride + (int64_t)m * sp.N + n] = acc[i][j];
         }
+}
+
+// split-K: the pieces of every element added in piece order (deterministic), then stored
+template <class Prob>
+__global__ void __launch_bounds__(256) tgemm_reduce_kernel(Prob pr, int splits, const float* part, int64_t pstride) {
+    typename Prob::Sub sp;
+    const int sub = blockIdx.y;
+    if (!pr.begin(sub, sp)) return;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)sp.M * sp.N) return;
+    float v = 0.f;
+    for (int p = 0; p < splits; ++p) v += part[((int64_t)sub * splits + p) * pstride + e];
+    pr.store(sp, (int)(e / sp.N), (int)(e % sp.N), v);
 }
 
 // Token lists of the routed experts (global bucketing of the forward's routing): the m-th token of
 // expert e is perm[offs[e] + m]; its rank r is where e sits in idx[t][g].
 struct Lists {
     const int32_t* offs;  // [N + 1]
-    const int32_t* perm;  // [T G k]
+    const int32_t* perm;  // [T G k]: token of every list position
+    const int32_t* rank;  // [T G k]: choice rank of every list position
 };
-__device__ __forceinline__ int rank_of(const BwdArgs& a, int64_t t, int e) {
-    const int g = e / a.n;
-    const int32_t* id = a.idx + (t * a.G + g) * a.k;
-    int r = 0;
-    for (int q = 0; q < a.k; ++q)
-        if (id[q] == e) r = q;
-    return r;
+
+// rank of every list position, from the inverse map of the bucketing: thread per (t, g, r)
+__global__ void list_rank_kernel(const int32_t* __restrict__ inv, int64_t n, int k, int32_t* __restrict__ rank) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q < n) rank[inv[q]] = (int)(q % k);
 }
 
 // U[t][slot] = dy_t W_slot^T: sub-problem = slot matrix (expert e, group slot g, shared head);
@@ -485,7 +506,7 @@ struct ProbU {
         const int64_t t = tok(s, m);
         const bool rslot = !a.dense && a.variant == GQE_VARIANT_GQE;
         int ls;
-        if (s.kind == 0) ls = s.g * a.k + (a.dense ? s.e % a.n : rank_of(a, t, s.e));
+        if (s.kind == 0) ls = s.g * a.k + (a.dense ? s.e % a.n : L.rank[s.base + m]);
         else if (s.kind == 1) ls = a.G * a.k + s.g;
         else ls = a.G * a.k + (rslot ? a.G : 0);
         a.U[(t * a.NS + ls) * a.dh + n] = v;
@@ -517,7 +538,7 @@ struct ProbWo {
         const int64_t t = tok(s, k);
         const int64_t ob = t * a.H * a.dh;  // O is token-major
         if (s.kind == 0) {
-            const int h = s.g * a.k + (a.dense ? s.e % a.n : rank_of(a, t, s.e));
+            const int h = s.g * a.k + (a.dense ? s.e % a.n : L.rank[s.base + k]);
             return a.cf[t * a.H + h] * ld<T>(a.O, ob + h * a.dh + j);
         }
         if (s.kind == 1) {
@@ -583,7 +604,7 @@ struct ProbWx {
         if (s.hb < 2 * a.G) return a.dV[(t * a.G + s.hb - a.G) * a.dh + j];
         if (s.hb < ebase) return a.dQ[(t * a.H + a.G * a.k) * a.dh + j];
         if (s.hb < ebase + a.N) {
-            const int h = s.g * a.k + (a.dense ? s.e % a.n : rank_of(a, t, s.e));
+            const int h = s.g * a.k + (a.dense ? s.e % a.n : L.rank[s.base + k]);
             return a.dQ[(t * a.H + h) * a.dh + j];
         }
         return a.dl[t * a.N + j];
@@ -659,23 +680,26 @@ struct ProbDxRouted {
         return s.M > 0;
     }
     __device__ int64_t tok(const Sub& s, int m) const { return a.dense ? m : L.perm[s.base + m]; }
-    __device__ bool mine(const Sub& s, int64_t t) const { return a.dense || rank_of(a, t, s.e) == r; }
+    __device__ bool mine(const Sub& s, int m) const { return a.dense || L.rank[s.base + m] == r; }
     __device__ float lda(const Sub& s, int m, int j) const {
         const int64_t t = tok(s, m);
-        if (!mine(s, t)) return 0.f;
+        if (!mine(s, m)) return 0.f;
         return a.dQ[(t * a.H + g * a.k + r) * a.dh + j];
     }
     __device__ float ldb(const Sub& s, int j, int i) const { return ld<T>(a.wq, ((int64_t)s.e * a.d + i) * a.dh + j); }
     __device__ void store(const Sub& s, int m, int i, float v) const {
-        const int64_t t = tok(s, m);
-        if (mine(s, t)) a.dx[t * a.d + i] += v;
+        if (mine(s, m)) a.dx[tok(s, m) * a.d + i] += v;
     }
 };
 
 template <class Prob, bool AK, bool BK>
-void tgemm(const Prob& p, int maxM, int maxN, int nsub, hipStream_t st) {
-    const dim3 grid((unsigned)ceil_div(maxN, 64), (unsigned)ceil_div(maxM, 64), (unsigned)nsub);
-    tgemm_kernel<Prob, AK, BK><<<grid, 256, 0, st>>>(p);
+void tgemm(const Prob& p, int maxM, int maxN, int nsub, hipStream_t st, int splits = 1, float* part = nullptr) {
+    const int64_t pstride = (int64_t)maxM * maxN;
+    const dim3 grid((unsigned)ceil_div(maxN, 64), (unsigned)ceil_div(maxM, 64), (unsigned)(nsub * splits));
+    tgemm_kernel<Prob, AK, BK><<<grid, 256, 0, st>>>(p, splits, part, pstride);
+    if (splits > 1)
+        tgemm_reduce_kernel<Prob><<<dim3((unsigned)ceil_div(pstride, 256), (unsigned)nsub), 256, 0, st>>>(p, splits, part,
+                                                                                                           pstride);
 }
 
 template <typename T>
@@ -690,12 +714,27 @@ hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km
     if (km) km->mark(KT_BWD_OUT);
     if (km) km->begin(KT_BWD_ATTN);
     const unsigned nblk = (unsigned)ceil_div(a.S, 64);
-    bwd_dq_kernel<T><<<dim3(nblk, (unsigned)a.H, (unsigned)a.B), 256, 0, st>>>(a);
-    bwd_dkv_kernel<T><<<dim3(nblk, (unsigned)a.G, (unsigned)a.B), 256, 0, st>>>(a);
+    const dim3 gq(nblk, (unsigned)a.H, (unsigned)a.B), gk(nblk, (unsigned)a.G, (unsigned)a.B);
+#define GQE_BWD_ATTN(DQV)                                     \
+    bwd_dq_kernel<T, DQV><<<gq, 256, 0, st>>>(a);             \
+    bwd_dkv_kernel<T, DQV><<<gk, 256, 0, st>>>(a);
+    switch (a.dh / 4) {
+        case 4: GQE_BWD_ATTN(4) break;
+        case 8: GQE_BWD_ATTN(8) break;
+        case 12: GQE_BWD_ATTN(12) break;
+        case 16: GQE_BWD_ATTN(16) break;
+        case 20: GQE_BWD_ATTN(20) break;
+        case 24: GQE_BWD_ATTN(24) break;
+        case 28: GQE_BWD_ATTN(28) break;
+        default: GQE_BWD_ATTN(32) break;
+    }
+#undef GQE_BWD_ATTN
     if (km) km->mark(KT_BWD_ATTN);
     if (km) km->begin(KT_BWD_WGRAD);
-    tgemm<ProbWo<T>, false, false>(ProbWo<T>{a, L}, a.dh, a.d, nsm, st);
-    tgemm<ProbWx<T>, false, false>(ProbWx<T>{a, L}, a.d + 1, a.dh > a.N ? a.dh : a.N, 2 * a.G + a.s + a.N + 1, st);
+    // weight gradients reduce over the tokens: split-K pieces (kWgradSplits) summed in order
+    tgemm<ProbWo<T>, false, false>(ProbWo<T>{a, L}, a.dh, a.d, nsm, st, kWgradSplits, a.part);
+    tgemm<ProbWx<T>, false, false>(ProbWx<T>{a, L}, a.d + 1, a.dh > a.N ? a.dh : a.N, 2 * a.G + a.s + a.N + 1, st,
+                                   kWgradSplits, a.part);
     if (km) km->mark(KT_BWD_WGRAD);
     if (km) km->begin(KT_BWD_DX);
     tgemm<ProbDxDense<T>, true, true>(ProbDxDense<T>{a}, nt, a.d, 1, st);
@@ -741,6 +780,7 @@ hipError_t launch_backward(const GqeDims& D, const WorkPlan& P, const BwdPlan& B
     a.dQ = (float*)(ws + BP.dQ);
     a.dK = (float*)(ws + BP.dK);
     a.dV = (float*)(ws + BP.dV);
+    a.part = (float*)(ws + BP.part);
     a.dx = gr.dx;
     a.dwr = gr.d_router;
     a.dbr = gr.d_router_bias;
@@ -769,11 +809,15 @@ hipError_t launch_backward(const GqeDims& D, const WorkPlan& P, const BwdPlan& B
     a.dense = D.dense;
     a.NS = BP.NS;
     a.Np = (int)round_up(D.N, 16);
-    Lists L{(const int32_t*)(ws + BP.offs), (const int32_t*)(ws + BP.perm)};
+    Lists L{(const int32_t*)(ws + BP.offs), (const int32_t*)(ws + BP.perm), (const int32_t*)(ws + BP.rank)};
     if (!D.dense) {
-        const hipError_t e = launch_bucket(D, P, const_cast<char*>(fws), (int32_t*)(ws + BP.offs),
-                                           (int32_t*)(ws + BP.perm), (int32_t*)(ws + BP.inv), st);
+        hipError_t e = launch_bucket(D, P, const_cast<char*>(fws), (int32_t*)(ws + BP.offs), (int32_t*)(ws + BP.perm),
+                                     (int32_t*)(ws + BP.inv), st);
         if (e != hipSuccess) return e;
+        const int64_t n = P.T * D.G * D.k;
+        list_rank_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>((const int32_t*)(ws + BP.inv), n, D.k,
+                                                                     (int32_t*)(ws + BP.rank));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return D.dtype == GQE_DTYPE_BF16 ? run<bf16_t>(a, L, st, km) : run<float>(a, L, st, km);
 }
