@@ -588,6 +588,9 @@ static BwdPlan make_bwd_plan(const GqeDims& D, int64_t B, int64_t S) {
         const size_t out_side = (size_t)(D.N + D.G + D.s) * D.dh * D.d;
         P.part = take(8 * (in_side > out_side ? in_side : out_side) * 4);
     }
+    const size_t S_pad = (size_t)round_up(S, GQE_KV_TILE);
+    P.vr = take((size_t)B * D.G * S_pad * D.dh * 2);
+    P.dob = take((size_t)B * D.H * S_pad * D.dh * 2);
     P.total = off;
     return P;
 }

@@ -69,6 +69,7 @@ struct BwdPlan {
     size_t U, dO, Dd, lse, dl, cf, wn, dQ, dK, dV;
     size_t offs, perm, inv, rank;     // token lists of the routed experts (bucketing) and choice ranks
     size_t part;                      // split-K partial sums of the weight gradients
+    size_t vr, dob;                   // bf16 attention: row-major V and bf16 dO
     size_t total;
 };
 

@@ -67,6 +67,8 @@ struct BwdArgs {
     float* dK;              // [T][G][dh] (before the rotation)
     float* dV;              // [T][G][dh]
     float* part;            // split-K partial sums of the weight gradients
+    uint16_t* vr;           // bf16 path: V row-major [B][G][S_pad][dh]
+    uint16_t* dob;          // bf16 path: dO in bf16 [B][H][S_pad][dh]
     // outputs (float32)
     float *dx, *dwr, *dbr, *dwq, *dwqs, *dwk, *dwv, *dwo, *dwor, *dwos;
     double aux_coef;
@@ -376,6 +378,281 @@ __global__ void __launch_bounds__(256) bwd_dkv_kernel(BwdArgs a) {
         a.dK[(t * a.G + g) * dh + d0 + i] = dk[i];
         a.dV[(t * a.G + g) * dh + d0 + i] = dv[i];
     }
+}
+
+// ---------------------------------------------------------------- attention on matrix cores (bf16)
+// v_mfma_f32_16x16x16_bf16: A lane l = row l % 16, k 4 (l / 16) .. +3; B lane l = column l % 16, same
+// k; C lane l = column l % 16, rows 4 (l / 16) .. +3.  The C tile of S = Q K^T (rows = queries,
+// columns = keys) is, lane for lane, the A operand of a product whose rows are the keys and whose k
+// index runs over the queries (P^T dO, dS^T Q): probabilities and score gradients go from the
+// accumulators to the next product without any exchange; likewise S^T = K Q^T feeds dS K.  P and dS
+// are rounded to bf16 for the products (the forward pass feeds P to its P.V product the same way).
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mma16(const s16x4_t& a, const s16x4_t& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ s16x4_t pack4(const float (&v)[4]) {
+    return __builtin_bit_cast(s16x4_t, u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+}
+__device__ __forceinline__ s16x4_t lds8(const uint16_t* p) { return *reinterpret_cast<const s16x4_t*>(p); }
+__device__ __forceinline__ s16x4_t gld8(const uint16_t* p) { return *reinterpret_cast<const s16x4_t*>(p); }
+__device__ __forceinline__ float swap_x1(float v) {  // the value of lane ^ 1
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));
+}
+
+// row-major V and bf16 dO (rows past the sequence zero) for the matrix-core kernels
+__global__ void bwd_mprep_kernel(BwdArgs a, uint16_t* __restrict__ Vr, uint16_t* __restrict__ dOb) {
+    const int64_t nv = a.B * a.G * a.S_pad * a.dh, no = a.B * a.H * a.S_pad * a.dh;
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q < nv) {
+        const int c = (int)(q % a.dh);
+        const int64_t r = q / a.dh, s = r % a.S_pad, bg = r / a.S_pad;
+        Vr[q] = s < a.S ? reinterpret_cast<const uint16_t*>(a.Vt)[(bg * a.dh + c) * a.S_pad + vt_pos(s)] : 0;
+    } else if (q < nv + no) {
+        const int64_t i = q - nv;
+        const int c = (int)(i % a.dh);
+        const int64_t r = i / a.dh, s = r % a.S_pad, bh = r / a.S_pad, b = bh / a.H, h = bh % a.H;
+        dOb[i] = s < a.S ? (uint16_t)(pack_bf16x2(a.dO[((b * a.S + s) * a.H + h) * a.dh + c], 0.f) & 0xffffu) : 0;
+    }
+}
+
+// dk, dv of 64 keys (wave w: keys 16 w ..) of one (sequence, group) over the later queries of every
+// head of the group, query tiles of 64 staged in LDS row-major and transposed.
+template <int DH>
+__global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint16_t* __restrict__ Vr,
+                                                           const uint16_t* __restrict__ dOb) {
+    constexpr int NC = DH / 16, P1 = DH + 8, P2 = 72;
+    __shared__ __align__(16) uint16_t Qs[64 * P1], dOs[64 * P1], QsT[DH * P2], dOsT[DH * P2];
+    __shared__ float lss[64], dds[64];
+    const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, j4 = lane >> 4;
+    const int64_t S = a.S;
+    const int64_t key = (int64_t)kb * 64 + w * 16 + l16;  // this lane's key column
+    const bool kin = key < S;
+    const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + ((int64_t)(b * a.G + g) * a.S_pad) * DH;
+    const uint16_t* Vb = Vr + ((int64_t)(b * a.G + g) * a.S_pad) * DH;
+    s16x4_t kf[NC], vf[NC];
+    f32x4_t dk[NC], dv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        kf[c] = kin ? gld8(Kb + key * DH + 16 * c + 4 * j4) : s16x4_t{0, 0, 0, 0};
+        vf[c] = kin ? gld8(Vb + key * DH + 16 * c + 4 * j4) : s16x4_t{0, 0, 0, 0};
+        dk[c] = dv[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const int nqt = (int)ceil_div(S, 64);
+    const uint16_t* Qg = reinterpret_cast<const uint16_t*>(a.Q);
+    for (int h = 0; h < a.H; ++h) {
+        if (group_of(a, h) != g) continue;  // uniform over the work group
+        for (int qt = kb; qt < nqt; ++qt) {
+            __syncthreads();
+            for (int i = tid; i < 64 * (DH / 8); i += 256) {
+                const int q = i / (DH / 8), c8 = i % (DH / 8);
+                const int64_t qp = (int64_t)qt * 64 + q;
+                u32x4_t vq = {0u, 0u, 0u, 0u}, vd = {0u, 0u, 0u, 0u};
+                if (qp < S) {
+                    vq = *reinterpret_cast<const u32x4_t*>(Qg + (((int64_t)b * a.H + h) * S + qp) * DH + 8 * c8);
+                    vd = *reinterpret_cast<const u32x4_t*>(dOb + (((int64_t)b * a.H + h) * a.S_pad + qp) * DH + 8 * c8);
+                }
+                *reinterpret_cast<u32x4_t*>(&Qs[q * P1 + 8 * c8]) = vq;
+                *reinterpret_cast<u32x4_t*>(&dOs[q * P1 + 8 * c8]) = vd;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    QsT[(8 * c8 + e) * P2 + q] = (uint16_t)(vq[e >> 1] >> (16 * (e & 1)));
+                    dOsT[(8 * c8 + e) * P2 + q] = (uint16_t)(vd[e >> 1] >> (16 * (e & 1)));
+                }
+            }
+            if (tid < 64) {
+                const int64_t qp = (int64_t)qt * 64 + tid;
+                const int64_t ti = (b * S + (qp < S ? qp : 0)) * a.H + h;
+                lss[tid] = a.lse[ti];
+                dds[tid] = a.Dd[ti];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int qs = 0; qs < 4; ++qs) {
+                const int q0 = qs * 16;
+                f32x4_t sacc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    sacc = mma16(lds8(&Qs[(q0 + l16) * P1 + 16 * c + 4 * j4]), kf[c], sacc);
+                    dp = mma16(lds8(&dOs[(q0 + l16) * P1 + 16 * c + 4 * j4]), vf[c], dp);
+                }
+                float p[4], ds[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int qr = q0 + 4 * j4 + i;
+                    const int64_t qp = (int64_t)qt * 64 + qr;
+                    const bool on = kin && qp < S && qp >= key;
+                    p[i] = on ? __builtin_amdgcn_exp2f(sacc[i] - lss[qr]) : 0.f;
+                    ds[i] = on ? p[i] * (dp[i] - dds[qr]) : 0.f;
+                }
+                const s16x4_t pa = pack4(p), da = pack4(ds);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    dv[c] = mma16(pa, lds8(&dOsT[(16 * c + l16) * P2 + q0 + 4 * j4]), dv[c]);
+                    dk[c] = mma16(da, lds8(&QsT[(16 * c + l16) * P2 + q0 + 4 * j4]), dk[c]);
+                }
+            }
+        }
+    }
+    // C layout: lane column = head dim 16 c + l16, rows = keys 16 w + 4 j4 + i
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t kp = (int64_t)kb * 64 + w * 16 + 4 * j4 + i;
+            const int col = 16 * c + l16;
+            float kv = dk[c][i] * (1.f / kLog2e);
+            if (a.rope) {
+                const float other = swap_x1(kv);  // pair partner: the neighbouring column
+                float lo = (l16 & 1) ? other : kv, hi = (l16 & 1) ? kv : other;
+                rope_pair(lo, hi, -kp, a.rope[col >> 1]);
+                kv = (l16 & 1) ? hi : lo;
+            }
+            if (kp < S) {
+                a.dK[((b * S + kp) * a.G + g) * DH + col] = kv;
+                a.dV[((b * S + kp) * a.G + g) * DH + col] = dv[c][i];
+            }
+        }
+}
+
+// dq of 64 queries (wave w: queries 16 w ..) of one (sequence, head): pass 1 the row log-sum-exp,
+// pass 2 dS^T = P^T (dP^T - D) and dq += dS K over the causal key tiles.
+template <int DH>
+__global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint16_t* __restrict__ Vr,
+                                                          const uint16_t* __restrict__ dOb) {
+    constexpr int NC = DH / 16, P1 = DH + 8, P2 = 72;
+    __shared__ __align__(16) uint16_t Ks[64 * P1], Vs[64 * P1], KsT[DH * P2];
+    const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int g = group_of(a, h);
+    const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, j4 = lane >> 4;
+    const int64_t S = a.S;
+    const int64_t qpos = (int64_t)qb * 64 + w * 16 + l16;  // this lane's query column
+    const bool qin = qpos < S;
+    const uint16_t* Qg = reinterpret_cast<const uint16_t*>(a.Q);
+    s16x4_t qf[NC], df[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        qf[c] = qin ? gld8(Qg + (((int64_t)b * a.H + h) * S + qpos) * DH + 16 * c + 4 * j4) : s16x4_t{0, 0, 0, 0};
+        df[c] = qin ? gld8(dOb + (((int64_t)b * a.H + h) * a.S_pad + qpos) * DH + 16 * c + 4 * j4) : s16x4_t{0, 0, 0, 0};
+    }
+    const float Dq = qin ? a.Dd[(b * S + qpos) * a.H + h] : 0.f;
+    const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + ((int64_t)(b * a.G + g) * a.S_pad) * DH;
+    const uint16_t* Vb = Vr + ((int64_t)(b * a.G + g) * a.S_pad) * DH;
+    auto stage = [&](int kt, bool full) {
+        __syncthreads();
+        for (int i = tid; i < 64 * (DH / 8); i += 256) {
+            const int kk = i / (DH / 8), c8 = i % (DH / 8);
+            const int64_t kp = (int64_t)kt * 64 + kk;
+            u32x4_t vk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+            if (kp < S) {
+                vk = *reinterpret_cast<const u32x4_t*>(Kb + kp * DH + 8 * c8);
+                if (full) vv = *reinterpret_cast<const u32x4_t*>(Vb + kp * DH + 8 * c8);
+            }
+            *reinterpret_cast<u32x4_t*>(&Ks[kk * P1 + 8 * c8]) = vk;
+            if (full) {
+                *reinterpret_cast<u32x4_t*>(&Vs[kk * P1 + 8 * c8]) = vv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) KsT[(8 * c8 + e) * P2 + kk] = (uint16_t)(vk[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+        __syncthreads();
+    };
+    const int ntile = qb + 1;
+    // pass 1: each lane folds its four keys of every sub-tile into (m, l); then the four lanes of a
+    // query column are combined
+    float m = -INFINITY, l = 0.f;
+    for (int kt = 0; kt < ntile; ++kt) {
+        stage(kt, false);
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+            const int k0 = sub * 16;
+            f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) st = mma16(lds8(&Ks[(k0 + l16) * P1 + 16 * c + 4 * j4]), qf[c], st);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t kp = (int64_t)kt * 64 + k0 + 4 * j4 + i;
+                if (kp <= qpos && kp < S) {
+                    const float mn = fmaxf(m, st[i]);
+                    l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(st[i] - mn);
+                    m = mn;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+        float mo, lo;
+        if (o == 0) {
+            const auto sm = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+            const auto sl = __builtin_amdgcn_permlane16_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+            mo = (j4 & 1) ? __uint_as_float(sm[0]) : __uint_as_float(sm[1]);
+            lo = (j4 & 1) ? __uint_as_float(sl[0]) : __uint_as_float(sl[1]);
+        } else {
+            const auto sm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+            const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+            mo = (j4 & 2) ? __uint_as_float(sm[0]) : __uint_as_float(sm[1]);
+            lo = (j4 & 2) ? __uint_as_float(sl[0]) : __uint_as_float(sl[1]);
+        }
+        if (mo != -INFINITY) {
+            if (m == -INFINITY) {
+                m = mo;
+                l = lo;
+            } else {
+                const float mn = fmaxf(m, mo);
+                l = l * __builtin_amdgcn_exp2f(m - mn) + lo * __builtin_amdgcn_exp2f(mo - mn);
+                m = mn;
+            }
+        }
+    }
+    const float L = m + __builtin_amdgcn_logf(l);
+    // pass 2
+    f32x4_t dq[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) dq[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < ntile; ++kt) {
+        stage(kt, true);
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+            const int k0 = sub * 16;
+            f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                st = mma16(lds8(&Ks[(k0 + l16) * P1 + 16 * c + 4 * j4]), qf[c], st);
+                dpt = mma16(lds8(&Vs[(k0 + l16) * P1 + 16 * c + 4 * j4]), df[c], dpt);
+            }
+            float ds[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t kp = (int64_t)kt * 64 + k0 + 4 * j4 + i;
+                const bool on = qin && kp <= qpos && kp < S;
+                ds[i] = on ? __builtin_amdgcn_exp2f(st[i] - L) * (dpt[i] - Dq) : 0.f;
+            }
+            const s16x4_t da = pack4(ds);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) dq[c] = mma16(da, lds8(&KsT[(16 * c + l16) * P2 + k0 + 4 * j4]), dq[c]);
+        }
+    }
+    // C layout: lane column = head dim 16 c + l16, rows = queries 16 w + 4 j4 + i
+    const float sc = 1.f / sqrtf((float)DH);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t qr = (int64_t)qb * 64 + w * 16 + 4 * j4 + i;
+            const int col = 16 * c + l16;
+            float v = dq[c][i] * sc;
+            if (a.rope) {
+                const float other = swap_x1(v);
+                float lo = (l16 & 1) ? other : v, hi = (l16 & 1) ? v : other;
+                rope_pair(lo, hi, -qr, a.rope[col >> 1]);
+                v = (l16 & 1) ? hi : lo;
+            }
+            if (qr < S) a.dQ[((b * S + qr) * a.H + h) * DH + col] = v;
+        }
+    if (j4 == 0 && qin) a.lse[(b * S + qpos) * a.H + h] = L;
 }
 
 // ---------------------------------------------------------------- tiled float32 GEMM
@@ -715,6 +992,27 @@ hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km
     if (km) km->begin(KT_BWD_ATTN);
     const unsigned nblk = (unsigned)ceil_div(a.S, 64);
     const dim3 gq(nblk, (unsigned)a.H, (unsigned)a.B), gk(nblk, (unsigned)a.G, (unsigned)a.B);
+    if (sizeof(T) == 2) {
+        // bf16: matrix cores
+        const int64_t n = a.B * (a.G + a.H) * a.S_pad * a.dh;
+        bwd_mprep_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>(a, a.vr, a.dob);
+#define GQE_BWD_MFMA(DHV)                                                     \
+    bwd_dq_mfma_kernel<DHV><<<gq, 256, 0, st>>>(a, a.vr, a.dob);              \
+    bwd_dkv_mfma_kernel<DHV><<<gk, 256, 0, st>>>(a, a.vr, a.dob);
+        switch (a.dh / 16) {  // d_h: a multiple of 16, at most 128
+            case 1: GQE_BWD_MFMA(16) break;
+            case 2: GQE_BWD_MFMA(32) break;
+            case 3: GQE_BWD_MFMA(48) break;
+            case 4: GQE_BWD_MFMA(64) break;
+            case 5: GQE_BWD_MFMA(80) break;
+            case 6: GQE_BWD_MFMA(96) break;
+            case 7: GQE_BWD_MFMA(112) break;
+            default: GQE_BWD_MFMA(128) break;
+        }
+#undef GQE_BWD_MFMA
+        if (km) km->mark(KT_BWD_ATTN);
+        goto weights;
+    }
 #define GQE_BWD_ATTN(DQV)                                     \
     bwd_dq_kernel<T, DQV><<<gq, 256, 0, st>>>(a);             \
     bwd_dkv_kernel<T, DQV><<<gk, 256, 0, st>>>(a);
@@ -730,6 +1028,7 @@ hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km
     }
 #undef GQE_BWD_ATTN
     if (km) km->mark(KT_BWD_ATTN);
+weights:
     if (km) km->begin(KT_BWD_WGRAD);
     // weight gradients reduce over the tokens: split-K pieces (kWgradSplits) summed in order
     tgemm<ProbWo<T>, false, false>(ProbWo<T>{a, L}, a.dh, a.d, nsm, st, kWgradSplits, a.part);
@@ -781,6 +1080,8 @@ hipError_t launch_backward(const GqeDims& D, const WorkPlan& P, const BwdPlan& B
     a.dK = (float*)(ws + BP.dK);
     a.dV = (float*)(ws + BP.dV);
     a.part = (float*)(ws + BP.part);
+    a.vr = (uint16_t*)(ws + BP.vr);
+    a.dob = (uint16_t*)(ws + BP.dob);
     a.dx = gr.dx;
     a.dwr = gr.d_router;
     a.dbr = gr.d_router_bias;

@@ -79,6 +79,10 @@ CASES = [
     _wl("bwd_rope", k=2, B=1, S=80, rope_base=10000.0, seed=5),
     _wl("bwd_gqa", k=2, variant="hard_concat", shared_head=False, dense_gqa=True, B=1, S=60, seed=6),
     _wl("bwd_shared_group3", B=1, S=64, shared_kv_group=3, seed=7),
+    # several 64-row tiles with a ragged tail, other head widths
+    _wl("bwd_tiles_rope_dh64", k=2, dh=64, B=1, S=200, rope_base=10000.0, seed=13),
+    _wl("bwd_dh128", d=512, N=4, G=2, dh=128, B=1, S=150, seed=14),
+    _wl("bwd_dh16_k2", d=128, k=2, dh=16, B=2, S=130, seed=15),
     Workload("bwd_tiny_f32", 64, 4, 2, 1, 16, 1, 32, dtype="f32", router_std=0.5, seed=8),
     Workload("bwd_f32_k2_rope", 64, 8, 2, 2, 16, 2, 24, dtype="f32", router_std=0.5, rope_base=500.0, seed=9),
 ]
