@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16 = 2500.0   # TFLOP/s, MI355X dense bf16 matrix
 PEAK_FP64 = 78.6     # TFLOP/s, MI355X fp64 (matrix and vector)
 PEAK_HBM = 8000.0    # GB/s
-PEAK_FP32 = 157.3    # TFLOP/s, MI355X float32 vector (the backward's arithmetic)
+PEAK_FP32 = 157.3    # TFLOP/s, MI355X float32 vector (float32 layers' backward)
 
 # kernel slot -> (source file of the kernel, stage of the algorithmic-work table)
 KERNEL_SOURCES = {
@@ -281,6 +281,19 @@ def run_backward(wl, steps, warmup, aux_coef=0.01):
     return ms, km, finite
 
 
+def backward_stage_flops(wl) -> dict:
+    """Algorithmic flops of each timed backward stage (2 per multiply-add).  output: the per-slot
+    projections dy W_slot^T (the combine's contraction once); weights: every forward GEMM's weight
+    gradient (projection and combine contractions once each); dx: the projections' input gradient;
+    attention: six d_h-long products per causal score entry and head."""
+    alg = algorithmic(wl)
+    dh, B, S = wl.dh, wl.batch, wl.seq
+    H = wl.num_kv_heads * wl.top_k + (1 if wl.shared_head else 0)
+    pr, cb = alg["projection"]["flops"], alg["combine"]["flops"]
+    return {"backward_output": cb, "backward_attention": 2.0 * dh * H * B * S * (S + 1) / 2.0 * 6,
+            "backward_weights": pr + cb, "backward_dx": pr}
+
+
 def backward_report(steps: int, warmup: int) -> dict:
     from sparse_moe_query_amd.inputs import WORKLOADS
     wl = WORKLOADS["main_b8_s2048"]
@@ -288,10 +301,19 @@ def backward_report(steps: int, warmup: int) -> dict:
     ms, km, finite = run_backward(wl, steps, warmup)
     fl = backward_flops(wl)
     tf = fl / (ms * 1e-3) / 1e12
-    log(f"[bench] backward: {ms:.3f} ms ({tf:.1f} TFLOP/s float32 vector); kernels {km}")
+    # bf16 layers: every stage is matrix-core work except the router's float32 pieces
+    peak = PEAK_BF16 if wl.dtype == "bf16" else PEAK_FP32
+    bound = "mfma" if wl.dtype == "bf16" else "alu"
+    stages = {}
+    for k, f in backward_stage_flops(wl).items():
+        if k in km:
+            a = f / (km[k] * 1e-3) / 1e12
+            stages[k] = dict(bound=bound, achieved=a, peak=peak, unit="TFLOP/s", frac=a / peak, flops=f, ms=km[k])
+    dom = max(stages, key=lambda k: stages[k]["ms"]) if stages else None
+    log(f"[bench] backward: {ms:.3f} ms ({tf:.1f} TFLOP/s overall); kernels {km}")
+    roof = dict(stages[dom], kernel=dom) if dom else None
     return dict(workload=wl.name, ms=ms, tokens_s=wl.tokens / (ms / 1e3), kernel_ms=km, finite=finite,
-                aux_coef=0.01, flops=fl,
-                roofline=dict(bound="alu", achieved=tf, peak=PEAK_FP32, unit="TFLOP/s", frac=tf / PEAK_FP32))
+                aux_coef=0.01, flops=fl, tflops=tf, stages=stages, roofline=roof)
 
 
 def cpu_baseline(wl, min_seconds=10.0):

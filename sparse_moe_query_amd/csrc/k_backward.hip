@@ -724,6 +724,85 @@ __global__ void __launch_bounds__(256) tgemm_reduce_kernel(Prob pr, int splits, 
     pr.store(sp, (int)(e / sp.N), (int)(e % sp.N), v);
 }
 
+// The same sub-problems on matrix cores (bf16 layers): operands rounded once to bf16 as they are
+// staged (k chunks of 32, rows k-contiguous in LDS for both A and B), 16x16x16 products into float32
+// accumulators, wave w owning the 32 x 32 quarter (w / 2, w % 2) of the 64 x 64 tile.
+template <class Prob, bool AK, bool BK>
+__global__ void __launch_bounds__(256) tgemm_mfma_kernel(Prob pr, int splits, float* part, int64_t pstride) {
+    constexpr int KC = 32, KP = 40;  // k chunk; LDS row pitch in bf16 (80 bytes: 16 rows hit distinct banks)
+    __shared__ __align__(16) uint16_t As[64 * KP];  // [m][k]
+    __shared__ __align__(16) uint16_t Bs[64 * KP];  // [n][k]
+    typename Prob::Sub sp;
+    const int sub = blockIdx.z / splits, piece = blockIdx.z % splits;
+    if (!pr.begin(sub, sp)) return;
+    const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+    if (m0 >= sp.M || n0 >= sp.N) return;
+    const int kc = ((sp.K + splits - 1) / splits + KC - 1) / KC * KC;
+    const int kb = piece * kc, ke = min(sp.K, kb + kc);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, j4 = lane >> 4;
+    const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
+    f32x4_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = kb; k0 < ke; k0 += KC) {
+        // 64 x 32 of A and of B, two neighbouring k per thread and step
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = tid + 256 * q;
+            const int m = AK ? i >> 4 : i & 63, ka = AK ? (i & 15) * 2 : (i >> 6) * 2;
+            float a0 = 0.f, a1 = 0.f;
+            if (m0 + m < sp.M) {
+                if (k0 + ka < ke) a0 = pr.lda(sp, m0 + m, k0 + ka);
+                if (k0 + ka + 1 < ke) a1 = pr.lda(sp, m0 + m, k0 + ka + 1);
+            }
+            *reinterpret_cast<uint32_t*>(&As[m * KP + ka]) = pack_bf16x2(a0, a1);
+            const int n = BK ? i >> 4 : i & 63, kq = BK ? (i & 15) * 2 : (i >> 6) * 2;
+            float b0 = 0.f, b1 = 0.f;
+            if (n0 + n < sp.N) {
+                if (k0 + kq < ke) b0 = pr.ldb(sp, k0 + kq, n0 + n);
+                if (k0 + kq + 1 < ke) b1 = pr.ldb(sp, k0 + kq + 1, n0 + n);
+            }
+            *reinterpret_cast<uint32_t*>(&Bs[n * KP + kq]) = pack_bf16x2(b0, b1);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < KC; ks += 16) {
+            s16x4_t af[2], bq[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                af[t] = lds8(&As[(wm + 16 * t + l16) * KP + ks + 4 * j4]);
+                bq[t] = lds8(&Bs[(wn + 16 * t + l16) * KP + ks + 4 * j4]);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = mma16(af[i], bq[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+    // C layout: lane column n = l16 of each 16 x 16 block, rows 4 j4 .. 4 j4 + 3
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + wm + 16 * i + 4 * j4 + r, n = n0 + wn + 16 * j + l16;
+                if (m >= sp.M || n >= sp.N) continue;
+                if (splits == 1) pr.store(sp, m, n, acc[i][j][r]);
+                else part[(int64_t)blockIdx.z * pstride + (int64_t)m * sp.N + n] = acc[i][j][r];
+            }
+}
+
+// sub-problems z0, z0 + 1, ... of another problem set (a launch over part of its range)
+template <class P>
+struct ZShift : P {
+    int z0;
+    __device__ bool begin(int z, typename P::Sub& s) const { return P::begin(z + z0, s); }
+};
+
 // Token lists of the routed experts (global bucketing of the forward's routing): the m-th token of
 // expert e is perm[offs[e] + m]; its rank r is where e sits in idx[t][g].
 struct Lists {
@@ -897,20 +976,24 @@ struct ProbWx {
     }
 };
 
-// dx, dense part (written): K = [dK (G d_h) | dV (G d_h) | shared dq (d_h) | router logits (N)]
+// dx, dense part: K = [dK (G d_h) | dV (G d_h) | shared dq (d_h)] written (which = 0), then the
+// router logits' part, K = N, added (which = 1)
 template <typename T>
 struct ProbDxDense {
     BwdArgs a;
+    int which;
     struct Sub {
         int M, N, K;
     };
+    __device__ int kd() const { return 2 * a.G * a.dh + a.s * a.dh; }
     __device__ bool begin(int, Sub& s) const {
         s.M = (int)a.T;
         s.N = a.d;
-        s.K = 2 * a.G * a.dh + a.s * a.dh + (a.dense ? 0 : a.N);
-        return true;
+        s.K = which ? (a.dense ? 0 : a.N) : kd();
+        return s.K > 0;
     }
     __device__ float lda(const Sub&, int t, int kk) const {
+        if (which) kk += kd();
         const int GD = a.G * a.dh;
         if (kk < GD) return a.dK[(int64_t)t * GD + kk];
         if (kk < 2 * GD) return a.dV[(int64_t)t * GD + kk - GD];
@@ -920,6 +1003,7 @@ struct ProbDxDense {
         return a.dl[(int64_t)t * a.N + kk];
     }
     __device__ float ldb(const Sub&, int kk, int i) const {
+        if (which) kk += kd();
         const int GD = a.G * a.dh;
         if (kk < GD) return ld<T>(a.wk, (int64_t)i * GD + kk);
         if (kk < 2 * GD) return ld<T>(a.wv, (int64_t)i * GD + kk - GD);
@@ -928,7 +1012,10 @@ struct ProbDxDense {
         kk -= a.s * a.dh;
         return a.wr[(int64_t)i * a.N + kk];
     }
-    __device__ void store(const Sub&, int t, int i, float v) const { a.dx[(int64_t)t * a.d + i] = v; }
+    __device__ void store(const Sub&, int t, int i, float v) const {
+        if (which) a.dx[(int64_t)t * a.d + i] += v;
+        else a.dx[(int64_t)t * a.d + i] = v;
+    }
 };
 
 // dx, routed part (added): one launch per (group g, choice rank r), sub-problem = expert e of the
@@ -970,10 +1057,13 @@ struct ProbDxRouted {
 };
 
 template <class Prob, bool AK, bool BK>
-void tgemm(const Prob& p, int maxM, int maxN, int nsub, hipStream_t st, int splits = 1, float* part = nullptr) {
+void tgemm(bool mfma, const Prob& p, int maxM, int maxN, int nsub, hipStream_t st, int splits = 1,
+           float* part = nullptr) {
+    if (nsub <= 0) return;
     const int64_t pstride = (int64_t)maxM * maxN;
     const dim3 grid((unsigned)ceil_div(maxN, 64), (unsigned)ceil_div(maxM, 64), (unsigned)(nsub * splits));
-    tgemm_kernel<Prob, AK, BK><<<grid, 256, 0, st>>>(p, splits, part, pstride);
+    if (mfma) tgemm_mfma_kernel<Prob, AK, BK><<<grid, 256, 0, st>>>(p, splits, part, pstride);
+    else tgemm_kernel<Prob, AK, BK><<<grid, 256, 0, st>>>(p, splits, part, pstride);
     if (splits > 1)
         tgemm_reduce_kernel<Prob><<<dim3((unsigned)ceil_div(pstride, 256), (unsigned)nsub), 256, 0, st>>>(p, splits, part,
                                                                                                            pstride);
@@ -986,7 +1076,10 @@ hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km
     const int nsm = a.N + (rslot ? a.G : 0) + a.s;
     const int nt = (int)a.T;
     if (km) km->begin(KT_BWD_OUT);
-    tgemm<ProbU<T>, true, true>(ProbU<T>{a, L}, nt, a.dh, nsm, st);
+    // bf16 layers: the GEMM-shaped steps on matrix cores, except the router's (float32 weights and
+    // logit gradients stay float32)
+    const bool mm = sizeof(T) == 2;
+    tgemm<ProbU<T>, true, true>(mm, ProbU<T>{a, L}, nt, a.dh, nsm, st);
     bwd_route_kernel<T><<<blocks(a.T * a.G), 256, 0, st>>>(a);
     if (km) km->mark(KT_BWD_OUT);
     if (km) km->begin(KT_BWD_ATTN);
@@ -1031,14 +1124,19 @@ hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km
 weights:
     if (km) km->begin(KT_BWD_WGRAD);
     // weight gradients reduce over the tokens: split-K pieces (kWgradSplits) summed in order
-    tgemm<ProbWo<T>, false, false>(ProbWo<T>{a, L}, a.dh, a.d, nsm, st, kWgradSplits, a.part);
-    tgemm<ProbWx<T>, false, false>(ProbWx<T>{a, L}, a.d + 1, a.dh > a.N ? a.dh : a.N, 2 * a.G + a.s + a.N + 1, st,
-                                   kWgradSplits, a.part);
+    tgemm<ProbWo<T>, false, false>(mm, ProbWo<T>{a, L}, a.dh, a.d, nsm, st, kWgradSplits, a.part);
+    const int nwx = 2 * a.G + a.s + a.N;  // head blocks and experts; the router is sub-problem nwx
+    tgemm<ProbWx<T>, false, false>(mm, ProbWx<T>{a, L}, a.d, a.dh, nwx, st, kWgradSplits, a.part);
+    if (!a.dense)
+        tgemm<ZShift<ProbWx<T>>, false, false>(false, ZShift<ProbWx<T>>{{a, L}, nwx}, a.d + 1, a.N, 1, st,
+                                               kWgradSplits, a.part);
     if (km) km->mark(KT_BWD_WGRAD);
     if (km) km->begin(KT_BWD_DX);
-    tgemm<ProbDxDense<T>, true, true>(ProbDxDense<T>{a}, nt, a.d, 1, st);
+    tgemm<ProbDxDense<T>, true, true>(mm, ProbDxDense<T>{a, 0}, nt, a.d, 1, st);
+    if (!a.dense) tgemm<ProbDxDense<T>, true, true>(false, ProbDxDense<T>{a, 1}, nt, a.d, 1, st);
     for (int g = 0; g < a.G; ++g)
-        for (int r = 0; r < a.k; ++r) tgemm<ProbDxRouted<T>, true, true>(ProbDxRouted<T>{a, L, g, r}, nt, a.d, a.n, st);
+        for (int r = 0; r < a.k; ++r)
+            tgemm<ProbDxRouted<T>, true, true>(mm, ProbDxRouted<T>{a, L, g, r}, nt, a.d, a.n, st);
     if (km) km->mark(KT_BWD_DX);
     return hipGetLastError();
 }
