@@ -2,6 +2,7 @@
 // Every check runs on the host before any device call; no exception leaves this file.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -50,6 +51,7 @@ WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S, int64_t attn_slots) {
     P.idx = take(gk * 4);
     P.wsel = take(gk * 4);
     P.psel = take(gk * 4);
+    P.probs = take((size_t)P.T * D.N * 4);
     P.part_cnt = take((size_t)P.nblk_router * D.N * 4);
     P.part_psum = take((size_t)P.nblk_router * D.N * 8);
     P.bucket_boff = take((size_t)P.nblk_router * D.N * 4);
@@ -584,9 +586,10 @@ static BwdPlan make_bwd_plan(const GqeDims& D, int64_t B, int64_t S) {
     {
         // split-K partials: 8 pieces of every weight-gradient sub-problem, each at most (d + 1) x max(d_h, N)
         // (input side, 2G + s + N + 1 sub-problems) or d_h x d (output side, N + G + 1)
-        const size_t in_side = (size_t)(2 * D.G + D.s + D.N + 1) * (D.d + 1) * (D.dh > D.N ? D.dh : D.N);
+        const size_t in_side = (size_t)(2 * D.G + D.s + D.N) * D.d * D.dh;
         const size_t out_side = (size_t)(D.N + D.G + D.s) * D.dh * D.d;
-        P.part = take(8 * (in_side > out_side ? in_side : out_side) * 4);
+        const size_t router_side = (size_t)kRouterChunks * (D.d + 1) * D.N / 8 + 1;
+        P.part = take(8 * std::max(std::max(in_side, out_side), router_side) * 4);
     }
     const size_t S_pad = (size_t)round_up(S, GQE_KV_TILE);
     P.vr = take((size_t)B * D.G * S_pad * D.dh * 2);

@@ -11,6 +11,8 @@
 
 #define GQE_ATTN_COLS 256        // query columns (position, head) of one attention work item
 #define GQE_ATTN_MAX_CHUNKS 32   // key-range chunks an attention item may be split into
+// token chunks of the backward's router weight gradient (its partial sums share the split-K buffer)
+constexpr int kRouterChunks = 128;
 #define GQE_DEC_MAX_HEADS 8      // decode: active query heads of one KV group
 #define GQE_DEC_MAX_SLOTS 192    // decode: output-projection slots of one token
 #define GQE_DEC_MAX_SLOT_DIMS 8192  // decode: slots x d_h of one token
@@ -40,6 +42,7 @@ struct WorkPlan {
     int64_t B, S, T, S_pad;
     int64_t nblk_router;
     size_t idx, wsel, psel;           // [T, G, k] int32 / f32 / f32
+    size_t probs;                     // [T, N] f32 in-group router probabilities (for the backward)
     size_t part_cnt, part_psum;       // [nblk_router, N] int32 / f64
     size_t bucket_boff;               // [nblk_router, N] int32 (gqe_bucket)
     size_t stats;                     // counts [N] i64, mean [N] f64, aux f64

@@ -10,24 +10,28 @@
 //   ProbU             U[t][slot] = dy_t W_slot^T for every output slot of the token (routed expert
 //                     e: W_o[e], over its tokens; group g: W_oR[g]; shared head: W_os)
 //   bwd_route_kernel  per (token, group): head-output gradients do = c U_e + w U_g, D = do . o for
-//                     the attention, the router probabilities again (float64 logits, as in the
-//                     forward), the probability gradients (weighted_concat coefficient,
-//                     renormalisation w = p / sum_sel p, aux loss), and the logit gradients through
-//                     the in-group softmax
+//                     the attention; from the forward's stored router probabilities the
+//                     probability gradients (weighted_concat coefficient, renormalisation
+//                     w = p / sum_sel p, aux loss) and the logit gradients through the in-group
+//                     softmax
 //   bwd_dq_kernel     per 64 queries of a head: the row log-sum-exp (log2 units, from the stored
 //                     queries and keys), then dq = sum_j p_j (do . v_j - D) k_j / sqrt(d_h),
 //                     rotated back (rotary embedding)
 //   bwd_dkv_kernel    per 64 keys of a group: dk_j, dv_j over every later query of every head
 //   ProbWo, ProbWx    weight gradients as sums over the tokens that use each weight block
+//   bwd_router_wgrad  router weight and bias gradients (float32)
 //   ProbDx*           dx = dense part (dk W_k^T, dv W_v^T, shared dq W_qs^T, router logits W_r^T),
 //                     then the routed dq W_q[e]^T per (group, rank)
 //
-// The GEMM-shaped steps run through one tiled float32 kernel (tgemm_kernel) over gathered token
-// lists (the global bucketing of the forward's routing); the attention steps stage 64-row tiles in
-// LDS, four lanes per row.  Everything reads the forward pass's workspace (routing,
-// statistics, Q, K, V^T, O), which must be unchanged.
+// The GEMM-shaped steps run through one tiled kernel over gathered token lists (the global
+// bucketing of the forward's routing): on matrix cores for bf16 layers (tgemm_mfma_kernel), in
+// float32 FMAs otherwise (tgemm_kernel).  The attention steps of bf16 layers run on matrix cores
+// (bwd_*_mfma_kernel), those of float32 layers stage 64-row tiles in LDS, four lanes per row.
+// Everything reads the forward pass's workspace (routing, router probabilities, statistics, Q, K,
+// V^T, O), which must be unchanged.
 #include <math.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "gqe_common.h"
@@ -48,12 +52,10 @@ struct BwdArgs {
     const void* K;          // [B][G][S_pad][dh], rotated
     const void* Vt;         // [B][G][dh][S_pad], keys slotted
     const void* O;          // [B][S][H][dh]
-    // weights (gqe_init layouts) and the packed router / rotary tables
+    // weights (gqe_init layouts) and the packed rotary table
     const void *wq, *wqs, *wk, *wv, *wo, *wor, *wos;
     const float* wr;        // [d][N]
-    const double* wr64;     // packed router weights
-    const double* br64;     // [N]
-    int router_fast;        // lane-ordered packed router layout
+    const float* probs;     // [T][N] the forward's in-group router probabilities
     const double* rope;     // rotary frequencies (cycles per position) or null
     // backward workspace
     float* U;               // [T][NS][dh]
@@ -81,6 +83,23 @@ __device__ __forceinline__ float ld(const void* p, int64_t i) {
     return to_f32(reinterpret_cast<const T*>(p)[i]);
 }
 
+// four consecutive elements (16-byte aligned for float32, 8-byte for bf16) as float32
+template <typename T>
+__device__ __forceinline__ f32x4_t ld4(const void* p, int64_t i);
+template <>
+__device__ __forceinline__ f32x4_t ld4<float>(const void* p, int64_t i) {
+    return *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(p) + i);
+}
+template <>
+__device__ __forceinline__ f32x4_t ld4<bf16_t>(const void* p, int64_t i) {
+    const u32x2_t q = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const bf16_t*>(p) + i);
+    return f32x4_t{__uint_as_float(q[0] << 16), __uint_as_float(q[0] & 0xffff0000u), __uint_as_float(q[1] << 16),
+                   __uint_as_float(q[1] & 0xffff0000u)};
+}
+__device__ __forceinline__ float dot4(const f32x4_t& u, const f32x4_t& v) {
+    return u[0] * v[0] + u[1] * v[1] + u[2] * v[2] + u[3] * v[3];
+}
+
 // routed head h = g k + r of token t -> expert; the shared head -> -1
 __device__ __forceinline__ int expert_of(const BwdArgs& a, int64_t t, int h) {
     if (h >= a.G * a.k) return -1;
@@ -100,15 +119,18 @@ __global__ void bwd_route_kernel(BwdArgs a) {
     const int n = a.n, k = a.k, dh = a.dh, H = a.H, nr = a.G * a.k;
     const int64_t b = t / a.S, s = t % a.S;
     const bool rslot = !a.dense && a.variant == GQE_VARIANT_GQE;
+    // rows of d_h (a multiple of 16) read and written four elements at a time
     const float* Ut = a.U + t * a.NS * dh;
-    auto O_at = [&](int h, int j) { return ld<T>(a.O, ((b * a.S + s) * H + h) * dh + j); };
+    auto U4 = [&](int slot, int j) { return *reinterpret_cast<const f32x4_t*>(Ut + slot * dh + j); };
+    auto O4 = [&](int h, int j) { return ld4<T>(a.O, ((b * a.S + s) * H + h) * dh + j); };
+    auto dO4 = [&](int h, int j) -> f32x4_t& { return *reinterpret_cast<f32x4_t*>(a.dO + (t * H + h) * dh + j); };
     if (g == 0 && a.s) {  // shared head: do = dy W_os^T
         const int hs = nr, ls = nr + (rslot ? a.G : 0);
         float D = 0.f;
-        for (int j = 0; j < dh; ++j) {
-            const float v = Ut[ls * dh + j];
-            a.dO[(t * H + hs) * dh + j] = v;
-            D += v * O_at(hs, j);
+        for (int j = 0; j < dh; j += 4) {
+            const f32x4_t v = U4(ls, j);
+            dO4(hs, j) = v;
+            D += dot4(v, O4(hs, j));
         }
         a.Dd[t * H + hs] = D;
     }
@@ -116,10 +138,10 @@ __global__ void bwd_route_kernel(BwdArgs a) {
         for (int r = 0; r < k; ++r) {
             const int h = g * k + r;
             float D = 0.f;
-            for (int j = 0; j < dh; ++j) {
-                const float v = Ut[h * dh + j];
-                a.dO[(t * H + h) * dh + j] = v;
-                D += v * O_at(h, j);
+            for (int j = 0; j < dh; j += 4) {
+                const f32x4_t v = U4(h, j);
+                dO4(h, j) = v;
+                D += dot4(v, O4(h, j));
             }
             a.Dd[t * H + h] = D;
             a.cf[t * H + h] = 1.f;
@@ -127,27 +149,10 @@ __global__ void bwd_route_kernel(BwdArgs a) {
         }
         return;
     }
-    // router probabilities of the group, as the forward pass forms them
-    double l[16];
-    const T* xr = (const T*)a.x + t * a.d;
-    for (int jj = 0; jj < n; ++jj) {
-        const int e = g * n + jj;
-        double acc = 0.0;
-        for (int i = 0; i < a.d; ++i) {
-            const double w = a.router_fast ? a.wr64[((int64_t)(i >> 3) * 16 + e) * 8 + (i & 7)]
-                                           : a.wr64[(int64_t)i * a.Np + e];
-            acc = __builtin_fma((double)to_f32(xr[i]), w, acc);
-        }
-        l[jj] = acc + a.br64[e];
-    }
-    double m = l[0];
-    for (int jj = 1; jj < n; ++jj) m = fmax(m, l[jj]);
-    float den = 0.f;
-    for (int jj = 0; jj < n; ++jj) den += expf((float)(l[jj] - m));
-    const float inv = 1.0f / den;
+    // the group's router probabilities, as the forward pass formed them
     float p[16], dp[16];
     for (int jj = 0; jj < n; ++jj) {
-        p[jj] = expf((float)(l[jj] - m)) * inv;
+        p[jj] = a.probs[t * a.N + g * n + jj];
         dp[jj] = 0.f;
     }
     const int32_t* id = a.idx + (t * a.G + g) * k;
@@ -159,15 +164,15 @@ __global__ void bwd_route_kernel(BwdArgs a) {
         const float coef = a.variant == GQE_VARIANT_WEIGHTED_CONCAT ? p[jr] : 1.f;
         const float w = p[jr] / psel;
         float D = 0.f, ou = 0.f, ov = 0.f;
-        for (int j = 0; j < dh; ++j) {
-            const float u = Ut[h * dh + j];
-            const float v = rslot ? Ut[(nr + g) * dh + j] : 0.f;
-            const float o = O_at(h, j);
-            const float dov = coef * u + w * v;
-            a.dO[(t * H + h) * dh + j] = dov;
-            D += dov * o;
-            ou += o * u;
-            ov += o * v;
+        for (int j = 0; j < dh; j += 4) {
+            const f32x4_t u = U4(h, j);
+            const f32x4_t v = rslot ? U4(nr + g, j) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const f32x4_t o = O4(h, j);
+            const f32x4_t dov = coef * u + w * v;
+            dO4(h, j) = dov;
+            D += dot4(dov, o);
+            ou += dot4(o, u);
+            ov += dot4(o, v);
         }
         a.Dd[t * H + h] = D;
         a.cf[t * H + h] = coef;
@@ -796,13 +801,6 @@ __global__ void __launch_bounds__(256) tgemm_mfma_kernel(Prob pr, int splits, fl
             }
 }
 
-// sub-problems z0, z0 + 1, ... of another problem set (a launch over part of its range)
-template <class P>
-struct ZShift : P {
-    int z0;
-    __device__ bool begin(int z, typename P::Sub& s) const { return P::begin(z + z0, s); }
-};
-
 // Token lists of the routed experts (global bucketing of the forward's routing): the m-th token of
 // expert e is perm[offs[e] + m]; its rank r is where e sits in idx[t][g].
 struct Lists {
@@ -916,8 +914,7 @@ struct ProbWo {
 };
 
 // input-side weight gradients dW[i][j] = sum_t x_t[i] g_t[j]: sub-problem = head block (K_g, V_g,
-// shared query, expert e) or the router (N columns, plus the bias as row i = d); M = d (+1),
-// N = d_h (N), K = tokens
+// shared query, expert e); M = d, N = d_h, K = tokens
 template <typename T>
 struct ProbWx {
     BwdArgs a;
@@ -932,11 +929,7 @@ struct ProbWx {
         s.N = a.dh;
         s.K = (int)a.T;
         s.e = s.g = s.base = 0;
-        if (z == ebase + a.N) {  // router
-            if (a.dense) return false;
-            s.M = a.d + 1;
-            s.N = a.N;
-        } else if (z >= ebase) {
+        if (z >= ebase) {
             s.e = z - ebase;
             s.g = s.e / a.n;
             if (!a.dense) {
@@ -947,32 +940,24 @@ struct ProbWx {
         return true;
     }
     __device__ int64_t tok(const Sub& s, int k) const {
-        const int ebase = 2 * a.G + a.s;
-        return (s.hb >= ebase && s.hb < ebase + a.N && !a.dense) ? L.perm[s.base + k] : k;
+        return (s.hb >= 2 * a.G + a.s && !a.dense) ? L.perm[s.base + k] : k;
     }
-    __device__ float lda(const Sub& s, int i, int k) const {
-        return i < a.d ? ld<T>(a.x, tok(s, k) * a.d + i) : 1.f;
-    }
+    __device__ float lda(const Sub& s, int i, int k) const { return ld<T>(a.x, tok(s, k) * a.d + i); }
     __device__ float ldb(const Sub& s, int k, int j) const {
         const int ebase = 2 * a.G + a.s;
         const int64_t t = tok(s, k);
         if (s.hb < a.G) return a.dK[(t * a.G + s.hb) * a.dh + j];
         if (s.hb < 2 * a.G) return a.dV[(t * a.G + s.hb - a.G) * a.dh + j];
         if (s.hb < ebase) return a.dQ[(t * a.H + a.G * a.k) * a.dh + j];
-        if (s.hb < ebase + a.N) {
-            const int h = s.g * a.k + (a.dense ? s.e % a.n : L.rank[s.base + k]);
-            return a.dQ[(t * a.H + h) * a.dh + j];
-        }
-        return a.dl[t * a.N + j];
+        const int h = s.g * a.k + (a.dense ? s.e % a.n : L.rank[s.base + k]);
+        return a.dQ[(t * a.H + h) * a.dh + j];
     }
     __device__ void store(const Sub& s, int i, int j, float v) const {
         const int ebase = 2 * a.G + a.s;
         if (s.hb < a.G) a.dwk[(int64_t)i * a.G * a.dh + s.hb * a.dh + j] = v;
         else if (s.hb < 2 * a.G) a.dwv[(int64_t)i * a.G * a.dh + (s.hb - a.G) * a.dh + j] = v;
         else if (s.hb < ebase) a.dwqs[(int64_t)i * a.dh + j] = v;
-        else if (s.hb < ebase + a.N) a.dwq[((int64_t)s.e * a.d + i) * a.dh + j] = v;
-        else if (i < a.d) a.dwr[(int64_t)i * a.N + j] = v;
-        else a.dbr[j] = v;
+        else a.dwq[((int64_t)s.e * a.d + i) * a.dh + j] = v;
     }
 };
 
@@ -1056,6 +1041,59 @@ struct ProbDxRouted {
     }
 };
 
+// Router weight and bias gradients, dW_r[i][e] = sum_t x_t[i] dl_t[e] and db_r[e] = sum_t dl_t[e]
+// (row i = d, where x counts as 1), in float32: work group = (256 rows i, 16 experts, token chunk);
+// the chunk's logit gradients pass through LDS 128 tokens at a time and every lane reads them as
+// a broadcast; per-chunk partial sums are added in chunk order.
+constexpr int kRgTok = 128;
+template <typename T>
+__global__ void __launch_bounds__(256) bwd_router_wgrad_kernel(BwdArgs a, int nchunk, float* __restrict__ part) {
+    __shared__ __align__(16) float dls[kRgTok][16];
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int e0 = blockIdx.y * 16, ne = min(16, a.N - e0);
+    const int c = blockIdx.z;
+    const int64_t per = ceil_div(a.T, nchunk);
+    const int64_t t0 = (int64_t)c * per, t1 = min(a.T, t0 + per);
+    float acc[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int64_t tb = t0; tb < t1; tb += kRgTok) {
+        __syncthreads();
+        for (int q = threadIdx.x; q < kRgTok * 16; q += 256) {
+            const int tt = q >> 4, e = q & 15;
+            const int64_t t = tb + tt;
+            dls[tt][e] = (t < t1 && e < ne) ? a.dl[t * a.N + e0 + e] : 0.f;
+        }
+        __syncthreads();
+        const int nt = (int)min<int64_t>(kRgTok, t1 - tb);
+        if (i <= a.d)
+            for (int tt = 0; tt < nt; ++tt) {
+                const float xv = i < a.d ? ld<T>(a.x, (tb + tt) * a.d + i) : 1.f;
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&dls[tt][4 * e4]);
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) acc[4 * e4 + z] += xv * v[z];
+                }
+            }
+    }
+    if (i <= a.d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if (e < ne) part[((int64_t)c * (a.d + 1) + i) * a.N + e0 + e] = acc[e];
+}
+
+__global__ void bwd_router_wgrad_reduce(BwdArgs a, int nchunk, const float* __restrict__ part) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (i, e)
+    const int64_t n = (int64_t)(a.d + 1) * a.N;
+    if (q >= n) return;
+    float v = 0.f;
+    for (int c = 0; c < nchunk; ++c) v += part[(int64_t)c * n + q];
+    const int i = (int)(q / a.N), e = (int)(q % a.N);
+    if (i < a.d) a.dwr[(int64_t)i * a.N + e] = v;
+    else a.dbr[e] = v;
+}
+
 template <class Prob, bool AK, bool BK>
 void tgemm(bool mfma, const Prob& p, int maxM, int maxN, int nsub, hipStream_t st, int splits = 1,
            float* part = nullptr) {
@@ -1125,11 +1163,14 @@ weights:
     if (km) km->begin(KT_BWD_WGRAD);
     // weight gradients reduce over the tokens: split-K pieces (kWgradSplits) summed in order
     tgemm<ProbWo<T>, false, false>(mm, ProbWo<T>{a, L}, a.dh, a.d, nsm, st, kWgradSplits, a.part);
-    const int nwx = 2 * a.G + a.s + a.N;  // head blocks and experts; the router is sub-problem nwx
+    const int nwx = 2 * a.G + a.s + a.N;  // head blocks and experts (the router has its own kernel)
     tgemm<ProbWx<T>, false, false>(mm, ProbWx<T>{a, L}, a.d, a.dh, nwx, st, kWgradSplits, a.part);
-    if (!a.dense)
-        tgemm<ZShift<ProbWx<T>>, false, false>(false, ZShift<ProbWx<T>>{{a, L}, nwx}, a.d + 1, a.N, 1, st,
-                                               kWgradSplits, a.part);
+    if (!a.dense) {
+        const int nchunk = (int)std::min<int64_t>(kRouterChunks, ceil_div(a.T, kRgTok));
+        const dim3 gr((unsigned)ceil_div(a.d + 1, 256), (unsigned)ceil_div(a.N, 16), (unsigned)nchunk);
+        bwd_router_wgrad_kernel<T><<<gr, 256, 0, st>>>(a, nchunk, a.part);
+        bwd_router_wgrad_reduce<<<(unsigned)ceil_div((int64_t)(a.d + 1) * a.N, 256), 256, 0, st>>>(a, nchunk, a.part);
+    }
     if (km) km->mark(KT_BWD_WGRAD);
     if (km) km->begin(KT_BWD_DX);
     tgemm<ProbDxDense<T>, true, true>(mm, ProbDxDense<T>{a, 0}, nt, a.d, 1, st);
@@ -1163,9 +1204,7 @@ hipError_t launch_backward(const GqeDims& D, const WorkPlan& P, const BwdPlan& B
     a.wor = w.w_o_rslot;
     a.wos = w.w_o_shared;
     a.wr = w.w_router;
-    a.wr64 = (const double*)((const char*)packed + pl.wr64);
-    a.br64 = (const double*)((const char*)packed + pl.br64);
-    a.router_fast = router_uses_mfma(D) ? 1 : 0;
+    a.probs = (const float*)(fws + P.probs);
     a.rope = D.rope > 0.f ? (const double*)((const char*)packed + pl.rope) : nullptr;
     a.U = (float*)(ws + BP.U);
     a.dO = (float*)(ws + BP.dO);

@@ -41,6 +41,7 @@ struct RouterArgs {
     int32_t* idx;
     float* wsel;
     float* psel;
+    float* probs;  // [T][N] every expert's in-group probability, or null
     int32_t* ridx;
     float* rw;
     int32_t* part_cnt;
@@ -91,6 +92,8 @@ __device__ void select_one(const RouterArgs& a, double* l, int64_t tt, int g, in
     for (int j = 0; j < n; ++j) den += expf((float)(l[j] - m));
     const float inv = 1.0f / den;
     for (int j = 0; j < n; ++j) l[j] = (double)(expf((float)(l[j] - m)) * inv);  // probabilities
+    if (a.probs)
+        for (int j = 0; j < n; ++j) a.probs[tt * a.N + g * n + j] = (float)l[j];
     double ps = 0.0;
     for (int r = 0; r < k; ++r) ps += l[(sel >> (4 * r)) & 15];
     const int64_t o = (tt * a.G + g) * k;
@@ -379,6 +382,7 @@ hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, con
     a.idx = (int32_t*)(ws + P.idx);
     a.wsel = (float*)(ws + P.wsel);
     a.psel = (float*)(ws + P.psel);
+    a.probs = (float*)(ws + P.probs);
     a.ridx = route_idx;
     a.rw = route_w;
     a.part_cnt = (int32_t*)(ws + P.part_cnt);
