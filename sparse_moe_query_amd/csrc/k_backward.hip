@@ -96,6 +96,17 @@ __device__ __forceinline__ f32x4_t ld4<bf16_t>(const void* p, int64_t i) {
     return f32x4_t{__uint_as_float(q[0] << 16), __uint_as_float(q[0] & 0xffff0000u), __uint_as_float(q[1] << 16),
                    __uint_as_float(q[1] & 0xffff0000u)};
 }
+// eight consecutive elements (16-byte aligned for bf16, 32-byte for float32) as float32
+template <typename T>
+__device__ __forceinline__ void ld8(const void* p, int64_t i, float (&v)[8]) {
+    const f32x4_t a = ld4<T>(p, i), b = ld4<T>(p, i + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[e] = a[e];
+        v[4 + e] = b[e];
+    }
+}
+__device__ __forceinline__ void ld8f(const float* p, float (&v)[8]) { ld8<float>(p, 0, v); }
 __device__ __forceinline__ float dot4(const f32x4_t& u, const f32x4_t& v) {
     return u[0] * v[0] + u[1] * v[1] + u[2] * v[2] + u[3] * v[3];
 }
@@ -729,6 +740,11 @@ __global__ void __launch_bounds__(256) tgemm_reduce_kernel(Prob pr, int splits, 
     pr.store(sp, (int)(e / sp.N), (int)(e % sp.N), v);
 }
 
+__device__ __forceinline__ uint16_t bf16_bits(float v) { return (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu); }
+__device__ __forceinline__ u32x4_t pack8(const float (&v)[8]) {
+    return u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+}
+
 // The same sub-problems on matrix cores (bf16 layers): operands rounded once to bf16 as they are
 // staged (k chunks of 32, rows k-contiguous in LDS for both A and B), 16x16x16 products into float32
 // accumulators, wave w owning the 32 x 32 quarter (w / 2, w % 2) of the 64 x 64 tile.
@@ -752,24 +768,42 @@ __global__ void __launch_bounds__(256) tgemm_mfma_kernel(Prob pr, int splits, fl
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int k0 = kb; k0 < ke; k0 += KC) {
-        // 64 x 32 of A and of B, two neighbouring k per thread and step
+        // 64 x 32 of A and of B, eight elements per thread: a vector load where the problem
+        // offers one for the whole run (lda8 / ldb8), else element by element
+        {
+            float v[8];
+            if (AK) {
+                const int m = tid >> 2, ka = (tid & 3) * 8;
+                const bool in = m0 + m < sp.M;
+                if (!(in && k0 + ka + 8 <= ke && pr.lda8(sp, m0 + m, k0 + ka, v)))
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int i = tid + 256 * q;
-            const int m = AK ? i >> 4 : i & 63, ka = AK ? (i & 15) * 2 : (i >> 6) * 2;
-            float a0 = 0.f, a1 = 0.f;
-            if (m0 + m < sp.M) {
-                if (k0 + ka < ke) a0 = pr.lda(sp, m0 + m, k0 + ka);
-                if (k0 + ka + 1 < ke) a1 = pr.lda(sp, m0 + m, k0 + ka + 1);
+                    for (int e = 0; e < 8; ++e) v[e] = (in && k0 + ka + e < ke) ? pr.lda(sp, m0 + m, k0 + ka + e) : 0.f;
+                *reinterpret_cast<u32x4_t*>(&As[m * KP + ka]) = pack8(v);
+            } else {
+                const int ka = tid >> 3, m8 = (tid & 7) * 8;
+                const bool in = k0 + ka < ke;
+                if (!(in && m0 + m8 + 8 <= sp.M && pr.lda8(sp, m0 + m8, k0 + ka, v)))
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = (in && m0 + m8 + e < sp.M) ? pr.lda(sp, m0 + m8 + e, k0 + ka) : 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) As[(m8 + e) * KP + ka] = bf16_bits(v[e]);
             }
-            *reinterpret_cast<uint32_t*>(&As[m * KP + ka]) = pack_bf16x2(a0, a1);
-            const int n = BK ? i >> 4 : i & 63, kq = BK ? (i & 15) * 2 : (i >> 6) * 2;
-            float b0 = 0.f, b1 = 0.f;
-            if (n0 + n < sp.N) {
-                if (k0 + kq < ke) b0 = pr.ldb(sp, k0 + kq, n0 + n);
-                if (k0 + kq + 1 < ke) b1 = pr.ldb(sp, k0 + kq + 1, n0 + n);
+            if (BK) {
+                const int n = tid >> 2, kq = (tid & 3) * 8;
+                const bool in = n0 + n < sp.N;
+                if (!(in && k0 + kq + 8 <= ke && pr.ldb8(sp, k0 + kq, n0 + n, v)))
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = (in && k0 + kq + e < ke) ? pr.ldb(sp, k0 + kq + e, n0 + n) : 0.f;
+                *reinterpret_cast<u32x4_t*>(&Bs[n * KP + kq]) = pack8(v);
+            } else {
+                const int kq = tid >> 3, n8 = (tid & 7) * 8;
+                const bool in = k0 + kq < ke;
+                if (!(in && n0 + n8 + 8 <= sp.N && pr.ldb8(sp, k0 + kq, n0 + n8, v)))
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = (in && n0 + n8 + e < sp.N) ? pr.ldb(sp, k0 + kq, n0 + n8 + e) : 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) Bs[(n8 + e) * KP + kq] = bf16_bits(v[e]);
             }
-            *reinterpret_cast<uint32_t*>(&Bs[n * KP + kq]) = pack_bf16x2(b0, b1);
         }
         __syncthreads();
 #pragma unroll
@@ -851,10 +885,21 @@ struct ProbU {
     }
     __device__ int64_t tok(const Sub& s, int m) const { return (s.kind == 0 && !a.dense) ? L.perm[s.base + m] : m; }
     __device__ float lda(const Sub& s, int m, int k) const { return ld<T>(a.dy, tok(s, m) * a.d + k); }
-    __device__ float ldb(const Sub& s, int k, int n) const {
-        const T* W = s.kind == 0 ? (const T*)a.wo + (int64_t)s.e * a.dh * a.d
-                                 : (s.kind == 1 ? (const T*)a.wor + (int64_t)s.g * a.dh * a.d : (const T*)a.wos);
-        return to_f32(W[(int64_t)n * a.d + k]);
+    __device__ const T* wslot(const Sub& s) const {
+        return s.kind == 0 ? (const T*)a.wo + (int64_t)s.e * a.dh * a.d
+                           : (s.kind == 1 ? (const T*)a.wor + (int64_t)s.g * a.dh * a.d : (const T*)a.wos);
+    }
+    __device__ float ldb(const Sub& s, int k, int n) const { return to_f32(wslot(s)[(int64_t)n * a.d + k]); }
+    // k .. k + 7 (8-aligned; rows aligned when d % 8 == 0)
+    __device__ bool lda8(const Sub& s, int m, int k, float (&v)[8]) const {
+        if (a.d & 7) return false;
+        ld8<T>(a.dy, tok(s, m) * a.d + k, v);
+        return true;
+    }
+    __device__ bool ldb8(const Sub& s, int k, int n, float (&v)[8]) const {
+        if (a.d & 7) return false;
+        ld8<T>(wslot(s), (int64_t)n * a.d + k, v);
+        return true;
     }
     __device__ void store(const Sub& s, int m, int n, float v) const {
         const int64_t t = tok(s, m);
@@ -906,6 +951,37 @@ struct ProbWo {
         return ld<T>(a.O, ob + a.G * a.k * a.dh + j);
     }
     __device__ float ldb(const Sub& s, int k, int n) const { return ld<T>(a.dy, tok(s, k) * a.d + n); }
+    // j .. j + 7 of token k (d_h is a multiple of 16)
+    __device__ bool lda8(const Sub& s, int j, int k, float (&v)[8]) const {
+        const int64_t t = tok(s, k);
+        const int64_t ob = t * a.H * a.dh;
+        if (s.kind == 0) {
+            const int h = s.g * a.k + (a.dense ? s.e % a.n : L.rank[s.base + k]);
+            ld8<T>(a.O, ob + h * a.dh + j, v);
+            const float c = a.cf[t * a.H + h];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] *= c;
+        } else if (s.kind == 1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.f;
+            for (int r = 0; r < a.k; ++r) {
+                const int h = s.g * a.k + r;
+                float o[8];
+                ld8<T>(a.O, ob + h * a.dh + j, o);
+                const float c = a.wn[t * a.H + h];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] += c * o[e];
+            }
+        } else {
+            ld8<T>(a.O, ob + a.G * a.k * a.dh + j, v);
+        }
+        return true;
+    }
+    __device__ bool ldb8(const Sub& s, int k, int n, float (&v)[8]) const {
+        if (a.d & 7) return false;
+        ld8<T>(a.dy, tok(s, k) * a.d + n, v);
+        return true;
+    }
     __device__ void store(const Sub& s, int m, int n, float v) const {
         const int per = a.dh * a.d;
         float* dst = s.kind == 0 ? a.dwo + (int64_t)s.e * per : (s.kind == 1 ? a.dwor + (int64_t)s.g * per : a.dwos);
@@ -943,6 +1019,24 @@ struct ProbWx {
         return (s.hb >= 2 * a.G + a.s && !a.dense) ? L.perm[s.base + k] : k;
     }
     __device__ float lda(const Sub& s, int i, int k) const { return ld<T>(a.x, tok(s, k) * a.d + i); }
+    __device__ bool lda8(const Sub& s, int i, int k, float (&v)[8]) const {
+        if (a.d & 7) return false;
+        ld8<T>(a.x, tok(s, k) * a.d + i, v);
+        return true;
+    }
+    __device__ const float* grow(const Sub& s, int k) const {  // the gradient row of token list entry k
+        const int ebase = 2 * a.G + a.s;
+        const int64_t t = tok(s, k);
+        if (s.hb < a.G) return a.dK + (t * a.G + s.hb) * a.dh;
+        if (s.hb < 2 * a.G) return a.dV + (t * a.G + s.hb - a.G) * a.dh;
+        if (s.hb < ebase) return a.dQ + (t * a.H + a.G * a.k) * a.dh;
+        const int h = s.g * a.k + (a.dense ? s.e % a.n : L.rank[s.base + k]);
+        return a.dQ + (t * a.H + h) * a.dh;
+    }
+    __device__ bool ldb8(const Sub& s, int k, int j, float (&v)[8]) const {
+        ld8f(grow(s, k) + j, v);
+        return true;
+    }
     __device__ float ldb(const Sub& s, int k, int j) const {
         const int ebase = 2 * a.G + a.s;
         const int64_t t = tok(s, k);
@@ -997,6 +1091,23 @@ struct ProbDxDense {
         kk -= a.s * a.dh;
         return a.wr[(int64_t)i * a.N + kk];
     }
+    // kk .. kk + 7 inside one segment (segment lengths G d_h, d_h are multiples of 16)
+    __device__ bool lda8(const Sub&, int t, int kk, float (&v)[8]) const {
+        if (which) return false;
+        const int GD = a.G * a.dh;
+        if (kk < GD) ld8f(a.dK + (int64_t)t * GD + kk, v);
+        else if (kk < 2 * GD) ld8f(a.dV + (int64_t)t * GD + kk - GD, v);
+        else ld8f(a.dQ + ((int64_t)t * a.H + a.G * a.k) * a.dh + kk - 2 * GD, v);
+        return true;
+    }
+    __device__ bool ldb8(const Sub&, int kk, int i, float (&v)[8]) const {
+        if (which) return false;
+        const int GD = a.G * a.dh;
+        if (kk < GD) ld8<T>(a.wk, (int64_t)i * GD + kk, v);
+        else if (kk < 2 * GD) ld8<T>(a.wv, (int64_t)i * GD + kk - GD, v);
+        else ld8<T>(a.wqs, (int64_t)i * a.dh + kk - 2 * GD, v);
+        return true;
+    }
     __device__ void store(const Sub&, int t, int i, float v) const {
         if (which) a.dx[(int64_t)t * a.d + i] += v;
         else a.dx[(int64_t)t * a.d + i] = v;
@@ -1036,6 +1147,19 @@ struct ProbDxRouted {
         return a.dQ[(t * a.H + g * a.k + r) * a.dh + j];
     }
     __device__ float ldb(const Sub& s, int j, int i) const { return ld<T>(a.wq, ((int64_t)s.e * a.d + i) * a.dh + j); }
+    __device__ bool lda8(const Sub& s, int m, int j, float (&v)[8]) const {
+        if (!mine(s, m)) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        } else {
+            ld8f(a.dQ + (tok(s, m) * a.H + g * a.k + r) * a.dh + j, v);
+        }
+        return true;
+    }
+    __device__ bool ldb8(const Sub& s, int j, int i, float (&v)[8]) const {
+        ld8<T>(a.wq, ((int64_t)s.e * a.d + i) * a.dh + j, v);
+        return true;
+    }
     __device__ void store(const Sub& s, int m, int i, float v) const {
         if (mine(s, m)) a.dx[tok(s, m) * a.d + i] += v;
     }
