@@ -316,6 +316,70 @@ def backward_report(steps: int, warmup: int) -> dict:
                 aux_coef=0.01, flops=fl, tflops=tf, stages=stages, roofline=roof)
 
 
+def moe_flops(wl) -> dict:
+    """Algorithmic flops of the MoE-MLP's expert products (2 per multiply-add, only the chosen
+    experts' rows): up = T k d d_ff, down = T k d_ff d."""
+    f = 2.0 * wl.tokens * wl.top_k * wl.dim * wl.d_ff
+    return {"moe_up": f, "moe_down": f}
+
+
+def run_moe(wl, steps, warmup):
+    """Forwards of the MoE-MLP layer on resident inputs: ms per forward (device-synchronised wall
+    clock over `steps`), then the same number with per-kernel HIP events."""
+    import torch
+    from sparse_moe_query_amd import gqe
+    from sparse_moe_query_amd.runner import build_moe
+    layer, x, _ = build_moe(wl)
+    y = torch.empty_like(x)
+    for _ in range(warmup):
+        layer(x, y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer(x, y)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    gqe.gqe_moe_profile_enable(layer.h, True)
+    for _ in range(steps):
+        layer(x, y)
+    torch.cuda.synchronize()
+    kern, n = gqe.gqe_moe_profile_read_kernels(layer.h)
+    gqe.gqe_moe_profile_enable(layer.h, False)
+    km = {k: v / max(n, 1) for k, v in kern.items() if v > 0}
+    st = layer.stats()
+    layer.close()
+    return ms, km, st
+
+
+def moe_report(steps: int, warmup: int) -> dict:
+    """The top-k MoE-MLP (2 of 8 experts, d 768, d_ff 3072, 16384 tokens) and its skewed
+    16-expert variant: time per forward, tokens/s, expert-product rooflines (bf16 matrix core)."""
+    from sparse_moe_query_amd.inputs import MOE_WORKLOADS
+    out = {}
+    for name in ("moe_e8_k2_t16384", "moe_skew_e16_k2_t4096"):
+        wl = MOE_WORKLOADS[name]
+        log(f"[bench] {name}")
+        ms, km, st = run_moe(wl, steps, warmup)
+        fl = moe_flops(wl)
+        kr = {}
+        for k, f in fl.items():
+            if k in km:
+                a = f / (km[k] * 1e-3) / 1e12
+                kr[k] = dict(bound="mfma", achieved=a, peak=PEAK_BF16, unit="TFLOP/s", frac=a / PEAK_BF16,
+                             flops=f, kernel_ms=km[k], traffic=committed_traffic(k, name, "k_moe.hip"))
+        dom = max(kr, key=lambda k: kr[k]["kernel_ms"]) if kr else None
+        share = (st["counts"] / max(1, wl.tokens * wl.top_k)).tolist()
+        out[name] = dict(ms=ms, tokens_s=wl.tokens / (ms / 1e3), kernel_ms=km,
+                         tflops=sum(fl.values()) / (ms * 1e-3) / 1e12,
+                         roofline=dict(kr[dom], kernel=dom) if dom else None, kernels=kr,
+                         expert_share=share, aux=st["aux"],
+                         config=dict(dim=wl.dim, num_experts=wl.num_experts, top_k=wl.top_k, d_ff=wl.d_ff,
+                                     tokens=wl.tokens, activation=wl.activation,
+                                     router_bias_first=wl.router_bias_first))
+        log(f"[bench] {name}: {ms:.3f} ms, kernels {km}")
+    return out
+
+
 def cpu_baseline(wl, min_seconds=10.0):
     """The oracle as it stands, on whole sequences of the workload (all of their tokens), repeated
     over the batch until at least ``min_seconds`` of CPU work have been timed."""
@@ -359,6 +423,7 @@ def main():
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-moe", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="main workload only (for profilers)")
     ap.add_argument("--profile-workload", default=None,
                     help="run only this named workload (inputs.WORKLOADS, or NAME_gqa for its "
@@ -386,6 +451,14 @@ def main():
         wl, _, _, ms, kernel_ms = run_decode(name[:-4] if gqa else name, args.steps, args.warmup, gqa=gqa)
         print(json.dumps({"workload": wl.name, "ms_per_step": ms, "kernel_ms": kernel_ms,
                           "source_hash": source_hash("k_decode.hip")}), flush=True)
+        return
+    from sparse_moe_query_amd.inputs import MOE_WORKLOADS
+    if args.profile_workload in MOE_WORKLOADS:
+        if args.copy_calibration:
+            copy_calibration()
+        ms, km, _ = run_moe(MOE_WORKLOADS[args.profile_workload], args.steps, args.warmup)
+        print(json.dumps({"workload": args.profile_workload, "ms_per_step": ms, "kernel_ms": km,
+                          "source_hash": source_hash("k_moe.hip")}), flush=True)
         return
     if args.profile_workload == "backward_main_b8_s2048":
         if args.copy_calibration:
@@ -467,6 +540,8 @@ def main():
         result["long_context"] = long
     if not args.no_decode and not args.only_main:
         result["decode"] = decode_report(max(10, args.steps), args.warmup)
+    if not args.no_moe and not args.only_main:
+        result["moe_mlp"] = moe_report(max(10, args.steps), args.warmup)
     if not args.no_backward and not args.only_main:
         result["backward"] = backward_report(3, 1)
     if not args.no_cpu and not args.only_main:

@@ -333,6 +333,86 @@ void gqe_destroy(gqe_handle_t* h);
 /* Message of the last failing call on this thread ("" if none). */
 const char* gqe_last_error(void);
 
+/* ------------------------------------------------------------------ top-k MoE-MLP
+ * The mixture-of-experts MLP of the cseroadmap tutorial "Grouped-query attention and mixture of
+ * experts", section "Mixture of experts (MoE)" (its moe_layer sketch): a router scores all E experts
+ * with softmax(x W_r + b_r), keeps the top_k of largest probability (ties -> lower expert id) and
+ * mixes the chosen experts' outputs with the renormalised weights p / sum(p_selected):
+ *     y[t] = sum_r w[t, r] act(x[t] W1[e_r]) W2[e_r]
+ * Each expert is a two-layer MLP without biases (the page does not fix its form); act is GELU
+ * (0.5 h (1 + erf(h / sqrt 2))) or ReLU.  The hidden activation is stored in bf16, the expert
+ * outputs are mixed in float32 and y is rounded once to bf16.  Same conventions as above (caller-
+ * owned device buffers, asynchronous on `stream`, negative GQE_ERR_* codes, gqe_last_error). */
+typedef struct gqe_moe_handle gqe_moe_handle_t;
+
+#define GQE_ACT_GELU 0
+#define GQE_ACT_RELU 1
+
+typedef struct {
+    int32_t dim;         /* d: a multiple of 32 */
+    int32_t num_experts; /* E: 1..16 */
+    int32_t top_k;       /* 1..E */
+    int32_t d_ff;        /* hidden width of every expert: a multiple of 32 */
+    int32_t activation;  /* GQE_ACT_GELU or GQE_ACT_RELU */
+    int32_t dtype;       /* GQE_DTYPE_BF16 (the only supported type) */
+} gqe_moe_config_t;
+
+typedef struct {
+    const float* w_router; /* [d, E] float32 */
+    const float* b_router; /* [E] float32, or NULL (no bias, as in the tutorial's sketch) */
+    const void* w1;        /* [E, d, d_ff] bf16 */
+    const void* w2;        /* [E, d_ff, d] bf16 */
+} gqe_moe_weights_t;
+
+/* Validates the config (GQE_ERR_INVALID_CONFIG: E < 1, top_k outside 1..E, d or d_ff < 1, unknown
+ * activation; GQE_ERR_UNSUPPORTED: dtype other than bf16, E > 16, d or d_ff not a multiple of 32)
+ * and the weight pointers (16-byte aligned, w_router 4-byte), then allocates a host handle. */
+int gqe_moe_init(const gqe_moe_config_t* cfg, const gqe_moe_weights_t* w, gqe_moe_handle_t** out);
+
+/* Bytes of the device buffer gqe_moe_pack_weights fills (router weights in float64, expert weights
+ * transposed so that the reduction dimension is contiguous). */
+int gqe_moe_packed_weights_bytes(const gqe_moe_handle_t* h, size_t* bytes);
+
+/* Fills `packed` (device, 256-byte aligned, >= gqe_moe_packed_weights_bytes) from the weights
+ * given to gqe_moe_init; enqueued on `stream`.  Call again after changing the weights. */
+int gqe_moe_pack_weights(gqe_moe_handle_t* h, void* packed, size_t bytes, void* stream);
+
+/* Bytes of scratch a forward of `tokens` tokens needs (routing, bucketing, the hidden activations
+ * [tokens * top_k, d_ff] bf16 and the expert outputs [tokens * top_k, d] float32). */
+int gqe_moe_workspace_bytes(const gqe_moe_handle_t* h, int64_t tokens, size_t* bytes);
+
+/* y[tokens, d] (bf16, written) from x[tokens, d] (bf16); x and y device, 16-byte aligned, not
+ * overlapping; workspace 256-byte aligned.  route_idx / route_w: optional [tokens, top_k] int32 /
+ * float32 device outputs (expert ids best first, renormalised weights).  tokens = 0 is a no-op
+ * (x and y may then be NULL);
+ * tokens * top_k must stay below 2^31.  Errors: GQE_ERR_NULL_POINTER, GQE_ERR_MISALIGNED,
+ * GQE_ERR_SHAPE, GQE_ERR_WORKSPACE, GQE_ERR_STATE (weights not packed), GQE_ERR_HIP. */
+int gqe_moe_forward(gqe_moe_handle_t* h, const void* x, void* y, int64_t tokens, void* workspace,
+                    size_t ws_bytes, void* stream, int32_t* route_idx, float* route_w);
+
+/* Load statistics of the last forward (synchronises `stream`): tokens routed to each expert
+ * (counts[E], their shares are counts / (tokens * top_k)), the mean router probability of each
+ * expert (mean_prob[E]) and the balance loss E * sum_e share_e * mean_prob_e.  Any output may be
+ * NULL.  Errors: GQE_ERR_NULL_POINTER, GQE_ERR_STATE (no forward), GQE_ERR_HIP. */
+int gqe_moe_stats(gqe_moe_handle_t* h, void* stream, int64_t* counts, double* mean_prob, double* aux_loss);
+
+/* Byte offsets inside the workspace of a forward of `tokens` tokens, for stage-by-stage checks:
+ * offs[0] bucket offsets [E + 1] int32, offs[1] token of every bucket position [tokens * top_k]
+ * int32, offs[2] position of every (token, rank) [tokens, top_k] int32, offs[3] hidden
+ * activations [tokens * top_k, d_ff] bf16 in bucket order, offs[4] expert outputs
+ * [tokens * top_k, d] float32 in bucket order, offs[5] routing [tokens, top_k] int32,
+ * offs[6] renormalised weights [tokens, top_k] float32. */
+int gqe_moe_workspace_layout(const gqe_moe_handle_t* h, int64_t tokens, size_t offs[7]);
+
+/* Per-kernel timing as for the attention layer: slots 0 router, 1 router statistics, 2 bucketing,
+ * 3 up projection (W1 and the activation), 4 down projection (W2), 5 combine. */
+#define GQE_MOE_PROF_KERNELS 6
+int gqe_moe_profile_enable(gqe_moe_handle_t* h, int enable);
+int gqe_moe_profile_read_kernels(gqe_moe_handle_t* h, double kernel_ms[GQE_MOE_PROF_KERNELS], int64_t* forwards);
+
+/* Destroys the handle.  NULL is ignored. */
+void gqe_moe_destroy(gqe_moe_handle_t* h);
+
 #ifdef __cplusplus
 }
 #endif

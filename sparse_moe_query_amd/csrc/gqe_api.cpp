@@ -29,6 +29,11 @@ static int ok() {
     g_err[0] = 0;
     return GQE_OK;
 }
+// the same thread-local message for the other entry points of the library
+int gqe_set_error(int code, const char* msg) {
+    snprintf(g_err, sizeof(g_err), "%s", msg);
+    return code;
+}
 static bool misaligned(const void* p, size_t a) { return ((uintptr_t)p) % a != 0; }
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }

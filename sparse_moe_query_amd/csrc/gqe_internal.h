@@ -149,6 +149,34 @@ struct KernelMarks {
     }
 };
 
+// ---------------------------------------------------------------- top-k MoE-MLP
+struct MoeDims {
+    int d, E, k, dff, act, dtype;
+};
+struct MoePacked {
+    size_t wr64, br64;  // router (as the attention router's packed form, one group)
+    size_t w1t, w2t;    // expert weights transposed: [E][d_ff][d], [E][d][d_ff] bf16
+    size_t total;
+};
+struct MoePlan {
+    WorkPlan r;         // router and bucketing buffers (one group of E experts)
+    size_t offs, perm, inv;  // bucketing: [E + 1], [T k], [T k] int32
+    size_t H, Y;        // hidden [T k][d_ff] bf16, expert outputs [T k][d] f32, bucket order
+    size_t total;
+};
+// MoE timing slots (the router's own launcher records slots 0 and 1)
+enum { KM_MOE_ROUTER = 0, KM_MOE_STATS = 1, KM_MOE_BUCKET, KM_MOE_UP, KM_MOE_DOWN, KM_MOE_COMBINE, KM_MOE_COUNT };
+hipError_t launch_moe_pack(const MoeDims& M, const void* w1, const void* w2, void* packed, const MoePacked& pl,
+                           hipStream_t st);
+hipError_t launch_moe_experts(const MoeDims& M, const MoePlan& P, const void* x, void* y, const void* packed,
+                              const MoePacked& pl, char* ws, hipStream_t st, KernelMarks* km);
+// router weights packed in float64 as the router kernels read them
+hipError_t launch_pack_router(const GqeDims& D, const float* w_router, const float* b_router, size_t wr64_off,
+                              size_t br64_off, void* packed, hipStream_t st);
+
+// sets the message gqe_last_error returns on this thread; returns code (GQE_OK clears it)
+int gqe_set_error(int code, const char* msg);
+
 WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S, int64_t attn_slots);
 hipError_t launch_kn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km);
 bool router_uses_mfma(const GqeDims& D);

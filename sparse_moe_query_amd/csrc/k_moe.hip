@@ -1,0 +1,254 @@
+// Top-k mixture-of-experts MLP on gfx950 (cseroadmap tutorial "Grouped-query attention and mixture
+// of experts", section "Mixture of experts (MoE)": a router picks top_k of E expert MLPs per token
+// and mixes their outputs with the renormalised router weights).
+//
+//   router      the attention layer's router with one group of E experts (float64 logits, softmax,
+//               top-k with the lower index on ties, renormalised weights, per-expert statistics)
+//   bucketing   the global stable token-to-expert bucketing (histogram, scan, scatter, inverse)
+//   up          H[p] = act(x[perm[p]] W1[e])  for every bucket position p of expert e
+//   down        Y[p] = H[p] W2[e]
+//   combine     y[t] = sum_r w[t, r] Y[inv[t, r]]
+//
+// The two expert products are one grouped matrix-core GEMM kernel (moe_gemm_kernel): a work group
+// takes 128 consecutive bucket positions of one expert (so every row of the tile uses the same
+// weights; the tile table is walked on the device from the bucket offsets) and 256 output
+// features.  It computes C^T = W^T X^T with v_mfma_f32_32x32x16_bf16, the weights (pre-transposed
+// by the packing, k contiguous) as the A operand and the token rows as the B operand, so every lane
+// ends with four consecutive output features of one token: 8-byte bf16 stores of H, 16-byte float32
+// stores of Y.  Operands pass through LDS in k-slices of 32 (80-byte rows: the 16 rows that one
+// 16-byte fragment read serves per cycle fall in distinct banks), double-buffered: the next slice
+// is loaded into registers while the current one multiplies, one barrier per slice.  Each of the
+// four waves owns 128 features x 64 tokens (4 x 2 accumulator tiles of 32 x 32).
+#include "gqe_common.h"
+#include "gqe_internal.h"
+
+namespace {
+
+constexpr int kBF = 256;    // output features per tile
+constexpr int kBT = 128;    // bucket positions per tile
+constexpr int kBK = 32;     // k per LDS slice
+constexpr int kPitch = 40;  // bf16 per LDS row
+
+struct MoeGemmArgs {
+    const uint16_t* w;      // [E][NF][K] expert weights, k contiguous
+    const uint16_t* src;    // up: x [T][K]; down: H [P][K]
+    const int32_t* offs;    // [E + 1] bucket offsets
+    const int32_t* perm;    // [P] token of every bucket position (up)
+    void* out;              // up: H [P][NF] bf16; down: Y [P][NF] float32
+    int E, NF, K;
+};
+
+__device__ __forceinline__ float gelu(float v) { return 0.5f * v * (1.f + erff(v * 0.70710678118654752f)); }
+
+template <int MODE, int ACT>  // MODE 0: up (gathered x rows, activation, bf16 out); 1: down (float32 out)
+__global__ void __launch_bounds__(256, 2) moe_gemm_kernel(MoeGemmArgs a) {
+    __shared__ __align__(16) uint16_t Ws[2][kBF * kPitch];
+    __shared__ __align__(16) uint16_t Xs[2][kBT * kPitch];
+    // this work group's (expert, 128 positions): walk the experts' tile counts
+    int rem = blockIdx.x, e = 0, M = 0, p0 = 0;
+    for (; e < a.E; ++e) {
+        const int b0 = a.offs[e], b1 = a.offs[e + 1];
+        const int nt = (b1 - b0 + kBT - 1) / kBT;
+        if (rem < nt) {
+            p0 = b0 + rem * kBT;
+            M = min(kBT, b1 - p0);
+            break;
+        }
+        rem -= nt;
+    }
+    if (e == a.E) return;  // beyond the last tile (the grid is an upper bound)
+    const int f0 = blockIdx.y * kBF;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    const int wf = (w >> 1) * 128, wt = (w & 1) * 64;
+    // load slots: row r0 + 64 j of the tile, 16-byte chunk ch of the 64-byte k-slice
+    const int ch = tid & 3, r0 = tid >> 2;
+    const uint16_t* wrow[4];
+    bool wok[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int f = f0 + r0 + 64 * j;
+        wok[j] = f < a.NF;
+        wrow[j] = a.w + ((int64_t)e * a.NF + (wok[j] ? f : 0)) * a.K + ch * 8;
+    }
+    const uint16_t* xrow[2];
+    bool xok[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = r0 + 64 * j;
+        xok[j] = m < M;
+        const int64_t row = xok[j] ? (MODE == 0 ? (int64_t)a.perm[p0 + m] : (int64_t)(p0 + m)) : 0;
+        xrow[j] = a.src + row * a.K + ch * 8;
+    }
+    u32x4_t wr[4], xr[2];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            wr[j] = wok[j] ? *reinterpret_cast<const u32x4_t*>(wrow[j] + k0) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            xr[j] = xok[j] ? *reinterpret_cast<const u32x4_t*>(xrow[j] + k0) : u32x4_t{0u, 0u, 0u, 0u};
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4_t*>(&Ws[buf][(r0 + 64 * j) * kPitch + ch * 8]) = wr[j];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4_t*>(&Xs[buf][(r0 + 64 * j) * kPitch + ch * 8]) = xr[j];
+    };
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    const int nst = a.K / kBK;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int s = 0; s < nst; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < nst) gload((s + 1) * kBK);
+#pragma unroll
+        for (int kk = 0; kk < kBK; kk += 16) {
+            bf16x8_t af[4], bq[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                af[i] = *reinterpret_cast<const bf16x8_t*>(&Ws[buf][(wf + 32 * i + l32) * kPitch + kk + 8 * hi]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bq[j] = *reinterpret_cast<const bf16x8_t*>(&Xs[buf][(wt + 32 * j + l32) * kPitch + kk + 8 * hi]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bq[j], acc[i][j], 0, 0, 0);
+        }
+        if (s + 1 < nst) lstore(buf ^ 1);
+        __syncthreads();
+    }
+    // accumulator r of tile (i, j): feature 32 i + 8 (r / 4) + 4 hi + r % 4 of the wave's block,
+    // position 32 j + l32
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = wt + 32 * j + l32;
+        if (m >= M) continue;
+        const int64_t p = p0 + m;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int f = f0 + wf + 32 * i + 8 * q + 4 * hi;
+                if (f >= a.NF) continue;
+                float v[4];
+#pragma unroll
+                for (int z = 0; z < 4; ++z) v[z] = acc[i][j][4 * q + z];
+                if (MODE == 0) {
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) v[z] = ACT == GQE_ACT_RELU ? fmaxf(v[z], 0.f) : gelu(v[z]);
+                    *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(a.out) + p * a.NF + f) =
+                        u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                } else {
+                    *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.out) + p * a.NF + f) =
+                        f32x4_t{v[0], v[1], v[2], v[3]};
+                }
+            }
+    }
+}
+
+// y[t] = sum_r w[t, r] Y[inv[t, r]], thread per (token, 8 columns), rounded once to bf16
+__global__ void moe_combine_kernel(const float* __restrict__ Y, const int32_t* __restrict__ inv,
+                                   const float* __restrict__ wsel, uint16_t* __restrict__ y, int64_t T, int k, int d) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int c8 = d / 8;
+    if (q >= T * c8) return;
+    const int64_t t = q / c8;
+    const int c = (int)(q % c8) * 8;
+    float acc[8];
+#pragma unroll
+    for (int z = 0; z < 8; ++z) acc[z] = 0.f;
+    for (int r = 0; r < k; ++r) {
+        const int64_t p = inv[t * k + r];
+        const float wv = wsel[t * k + r];
+        const f32x4_t u = *reinterpret_cast<const f32x4_t*>(Y + p * d + c);
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(Y + p * d + c + 4);
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+            acc[z] += wv * u[z];
+            acc[4 + z] += wv * v[z];
+        }
+    }
+    *reinterpret_cast<u32x4_t*>(y + t * d + c) = u32x4_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                                         pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+}
+
+// dst[e][c][r] = src[e][r][c] (bf16), 64 x 64 tiles through LDS
+__global__ void moe_transpose_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int R, int C) {
+    __shared__ uint16_t tile[64][66];
+    const int e = blockIdx.z, r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    const uint16_t* s = src + (int64_t)e * R * C;
+    uint16_t* o = dst + (int64_t)e * R * C;
+    for (int i = threadIdx.x; i < 64 * 64; i += blockDim.x) {
+        const int rr = i >> 6, cc = i & 63;
+        if (r0 + rr < R && c0 + cc < C) tile[rr][cc] = s[(int64_t)(r0 + rr) * C + c0 + cc];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += blockDim.x) {
+        const int cc = i >> 6, rr = i & 63;
+        if (r0 + rr < R && c0 + cc < C) o[(int64_t)(c0 + cc) * R + r0 + rr] = tile[rr][cc];
+    }
+}
+
+template <int MODE>
+void gemm(const MoeGemmArgs& g, int act, int64_t P, hipStream_t st) {
+    const dim3 grid((unsigned)(ceil_div(P, kBT) + g.E), (unsigned)ceil_div(g.NF, kBF));
+    if (act == GQE_ACT_RELU) moe_gemm_kernel<MODE, GQE_ACT_RELU><<<grid, 256, 0, st>>>(g);
+    else moe_gemm_kernel<MODE, GQE_ACT_GELU><<<grid, 256, 0, st>>>(g);
+}
+
+}  // namespace
+
+hipError_t launch_moe_pack(const MoeDims& M, const void* w1, const void* w2, void* packed, const MoePacked& pl,
+                           hipStream_t st) {
+    char* pk = (char*)packed;
+    // W1 [E][d][d_ff] -> [E][d_ff][d]; W2 [E][d_ff][d] -> [E][d][d_ff]
+    moe_transpose_kernel<<<dim3((unsigned)ceil_div(M.dff, 64), (unsigned)ceil_div(M.d, 64), (unsigned)M.E), 256, 0,
+                           st>>>((const uint16_t*)w1, (uint16_t*)(pk + pl.w1t), M.d, M.dff);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    moe_transpose_kernel<<<dim3((unsigned)ceil_div(M.d, 64), (unsigned)ceil_div(M.dff, 64), (unsigned)M.E), 256, 0,
+                           st>>>((const uint16_t*)w2, (uint16_t*)(pk + pl.w2t), M.dff, M.d);
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_experts(const MoeDims& M, const MoePlan& P, const void* x, void* y, const void* packed,
+                              const MoePacked& pl, char* ws, hipStream_t st, KernelMarks* km) {
+    const char* pk = (const char*)packed;
+    const int64_t np = P.r.T * M.k;
+    MoeGemmArgs g{};
+    g.offs = (const int32_t*)(ws + P.offs);
+    g.perm = (const int32_t*)(ws + P.perm);
+    g.E = M.E;
+    if (km) km->begin(KM_MOE_UP);
+    g.w = (const uint16_t*)(pk + pl.w1t);
+    g.src = (const uint16_t*)x;
+    g.out = ws + P.H;
+    g.NF = M.dff;
+    g.K = M.d;
+    gemm<0>(g, M.act, np, st);
+    if (km) km->mark(KM_MOE_UP);
+    if (km) km->begin(KM_MOE_DOWN);
+    g.w = (const uint16_t*)(pk + pl.w2t);
+    g.src = (const uint16_t*)(ws + P.H);
+    g.out = ws + P.Y;
+    g.NF = M.d;
+    g.K = M.dff;
+    gemm<1>(g, M.act, np, st);
+    if (km) km->mark(KM_MOE_DOWN);
+    if (km) km->begin(KM_MOE_COMBINE);
+    const int64_t n = P.r.T * (M.d / 8);
+    moe_combine_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>(
+        (const float*)(ws + P.Y), (const int32_t*)(ws + P.inv), (const float*)(ws + P.r.wsel), (uint16_t*)y, P.r.T, M.k,
+        M.d);
+    if (km) km->mark(KM_MOE_COMBINE);
+    return hipGetLastError();
+}

@@ -115,15 +115,21 @@ __global__ void rope_table_kernel(double base, int dh, double* __restrict__ rev)
 
 }  // namespace
 
-hipError_t launch_pack(const GqeDims& D, const gqe_weights_t& w, const PackedLayout& pl,
-                       void* packed, bool mfma, hipStream_t st) {
+hipError_t launch_pack_router(const GqeDims& D, const float* w_router, const float* b_router, size_t wr64_off,
+                              size_t br64_off, void* packed, hipStream_t st) {
     char* pk = (char*)packed;
     const int Np = (int)round_up(D.N, 16);
     const int64_t m = (int64_t)D.d * Np + D.N;
-    pack_router_kernel<<<(unsigned)ceil_div(m, 256), 256, 0, st>>>(
-        w.w_router, w.b_router, D.d, D.N, Np, router_uses_mfma(D) ? 1 : 0, (double*)(pk + pl.wr64),
-        (double*)(pk + pl.br64));
-    hipError_t e = hipGetLastError();
+    pack_router_kernel<<<(unsigned)ceil_div(m, 256), 256, 0, st>>>(w_router, b_router, D.d, D.N, Np,
+                                                                   router_uses_mfma(D) ? 1 : 0,
+                                                                   (double*)(pk + wr64_off), (double*)(pk + br64_off));
+    return hipGetLastError();
+}
+
+hipError_t launch_pack(const GqeDims& D, const gqe_weights_t& w, const PackedLayout& pl,
+                       void* packed, bool mfma, hipStream_t st) {
+    char* pk = (char*)packed;
+    hipError_t e = launch_pack_router(D, w.w_router, w.b_router, pl.wr64, pl.br64, packed, st);
     if (e != hipSuccess) return e;
     rope_table_kernel<<<1, 64, 0, st>>>((double)D.rope, D.dh, (double*)(pk + pl.rope));
     e = hipGetLastError();

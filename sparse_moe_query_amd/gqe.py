@@ -27,7 +27,13 @@ EXPORTS = ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights", "gqe_work
            "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_bucket", "gqe_profile_enable",
            "gqe_profile_read", "gqe_profile_read_kernels", "gqe_attention_schedule", "gqe_kv_export",
            "gqe_decode_workspace_bytes", "gqe_decode", "gqe_backward_workspace_bytes", "gqe_backward",
-           "gqe_destroy", "gqe_last_error")
+           "gqe_destroy", "gqe_last_error") + (
+           "gqe_moe_init", "gqe_moe_packed_weights_bytes", "gqe_moe_pack_weights", "gqe_moe_workspace_bytes",
+           "gqe_moe_forward", "gqe_moe_stats", "gqe_moe_workspace_layout", "gqe_moe_profile_enable",
+           "gqe_moe_profile_read_kernels", "gqe_moe_destroy")
+ACTIVATIONS = {"gelu": 0, "relu": 1}
+# kernel timing slots of gqe_moe_profile_read_kernels
+MOE_KERNELS = ("moe_router", "moe_router_stats", "moe_bucket", "moe_up", "moe_down", "moe_combine")
 STAGES = ("router", "projection", "attention", "combine")
 # kernel timing slots of gqe_profile_read_kernels, in launch order
 KERNELS = ("router", "router_stats", "projection", "key_norms", "attention_prep", "attention", "attention_merge",
@@ -59,6 +65,14 @@ class Grads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in GRAD_FIELDS]
 
 
+class MoeConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("dim", "num_experts", "top_k", "d_ff", "activation", "dtype")]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_router", "b_router", "w1", "w2")]
+
+
 _lib = None
 
 
@@ -88,6 +102,17 @@ def lib():
         L.gqe_decode.argtypes = [P, P, P, I64, P, P, P, I64, P, SZ, P, P, P]
         L.gqe_backward_workspace_bytes.argtypes = [P, I64, I64, ctypes.POINTER(SZ)]
         L.gqe_backward.argtypes = [P, P, P, I64, I64, ctypes.c_double, P, P, SZ, ctypes.POINTER(Grads), P]
+        L.gqe_moe_init.argtypes = [ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeWeights), ctypes.POINTER(P)]
+        L.gqe_moe_packed_weights_bytes.argtypes = [P, ctypes.POINTER(SZ)]
+        L.gqe_moe_pack_weights.argtypes = [P, P, SZ, P]
+        L.gqe_moe_workspace_bytes.argtypes = [P, I64, ctypes.POINTER(SZ)]
+        L.gqe_moe_forward.argtypes = [P, P, P, I64, P, SZ, P, P, P]
+        L.gqe_moe_stats.argtypes = [P, P, P, P, P]
+        L.gqe_moe_workspace_layout.argtypes = [P, I64, P]
+        L.gqe_moe_profile_enable.argtypes = [P, ctypes.c_int]
+        L.gqe_moe_profile_read_kernels.argtypes = [P, P, P]
+        L.gqe_moe_destroy.argtypes = [P]
+        L.gqe_moe_destroy.restype = None
         L.gqe_destroy.argtypes = [P]
         L.gqe_destroy.restype = None
         L.gqe_last_error.argtypes = []
@@ -96,7 +121,9 @@ def lib():
                   "gqe_workspace_bytes", "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_bucket",
                   "gqe_profile_enable", "gqe_profile_read", "gqe_profile_read_kernels",
                   "gqe_attention_schedule", "gqe_kv_export", "gqe_decode_workspace_bytes", "gqe_decode",
-                  "gqe_backward_workspace_bytes", "gqe_backward"):
+                  "gqe_backward_workspace_bytes", "gqe_backward", "gqe_moe_init", "gqe_moe_packed_weights_bytes",
+                  "gqe_moe_pack_weights", "gqe_moe_workspace_bytes", "gqe_moe_forward", "gqe_moe_stats",
+                  "gqe_moe_workspace_layout", "gqe_moe_profile_enable", "gqe_moe_profile_read_kernels"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -244,7 +271,133 @@ def gqe_destroy(h):
         lib().gqe_destroy(h)
 
 
+# ------------------------------------------------------------------------- C names: MoE-MLP
+def gqe_moe_init(cfg: MoeConfig, weights: MoeWeights) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(lib().gqe_moe_init(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(h)))
+    return h
+
+
+def gqe_moe_packed_weights_bytes(h) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().gqe_moe_packed_weights_bytes(h, ctypes.byref(n)))
+    return n.value
+
+
+def gqe_moe_pack_weights(h, packed: torch.Tensor, stream=None):
+    _check(lib().gqe_moe_pack_weights(h, _ptr(packed), packed.numel() * packed.element_size(), _stream(stream)))
+
+
+def gqe_moe_workspace_bytes(h, tokens: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().gqe_moe_workspace_bytes(h, tokens, ctypes.byref(n)))
+    return n.value
+
+
+def gqe_moe_forward(h, x: torch.Tensor, y: torch.Tensor, tokens: int, ws: torch.Tensor, stream=None,
+                    route_idx: torch.Tensor | None = None, route_w: torch.Tensor | None = None):
+    _check(lib().gqe_moe_forward(h, _ptr(x), _ptr(y), tokens, _ptr(ws), ws.numel(), _stream(stream),
+                                 _ptr(route_idx), _ptr(route_w)))
+
+
+def gqe_moe_stats(h, n_experts: int, stream=None) -> dict:
+    counts = (ctypes.c_int64 * n_experts)()
+    mean = (ctypes.c_double * n_experts)()
+    aux = ctypes.c_double()
+    _check(lib().gqe_moe_stats(h, _stream(stream), counts, mean, ctypes.byref(aux)))
+    return dict(counts=np.array(counts[:], dtype=np.int64), mean_prob=np.array(mean[:]), aux=aux.value)
+
+
+def gqe_moe_workspace_layout(h, tokens: int):
+    offs = (ctypes.c_size_t * 7)()
+    _check(lib().gqe_moe_workspace_layout(h, tokens, offs))
+    return list(offs)
+
+
+def gqe_moe_profile_enable(h, enable: bool):
+    _check(lib().gqe_moe_profile_enable(h, int(enable)))
+
+
+def gqe_moe_profile_read_kernels(h):
+    ms = (ctypes.c_double * len(MOE_KERNELS))()
+    n = ctypes.c_int64()
+    _check(lib().gqe_moe_profile_read_kernels(h, ms, ctypes.byref(n)))
+    return dict(zip(MOE_KERNELS, ms[:])), n.value
+
+
+def gqe_moe_destroy(h):
+    lib().gqe_moe_destroy(h)
+
+
 # ------------------------------------------------------------------------- module wrapper
+class MoEMLP:
+    """Top-k mixture-of-experts MLP (the tutorial's moe_layer with expert MLPs): weights are device
+    tensors w_router [d, E] f32, b_router [E] f32 or None, w1 [E, d, d_ff] bf16, w2 [E, d_ff, d] bf16."""
+
+    WEIGHT_KEYS = ("w_router", "b_router", "w1", "w2")
+
+    def __init__(self, dim: int, num_experts: int, top_k: int, d_ff: int, activation: str = "gelu",
+                 weights: dict | None = None, stream=None):
+        if weights is None:
+            raise ValueError("weights (device tensors) are required")
+        self.dim, self.E, self.k, self.d_ff = dim, num_experts, top_k, d_ff
+        self.cfg = MoeConfig(dim, num_experts, top_k, d_ff, ACTIVATIONS[activation], DTYPES["bf16"])
+        self._w = {k: weights.get(k) for k in self.WEIGHT_KEYS}
+        self.weights = MoeWeights(*[_ptr(self._w[k]) for k in self.WEIGHT_KEYS])
+        self.h = gqe_moe_init(self.cfg, self.weights)
+        self.device = self._w["w1"].device
+        self.packed = torch.empty(max(gqe_moe_packed_weights_bytes(self.h), 256), dtype=torch.uint8,
+                                  device=self.device)
+        gqe_moe_pack_weights(self.h, self.packed, stream)
+        self._ws = None
+
+    def workspace(self, tokens: int) -> torch.Tensor:
+        nbytes = max(gqe_moe_workspace_bytes(self.h, tokens), 256)
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def __call__(self, x: torch.Tensor, y: torch.Tensor | None = None, stream=None, route_idx=None,
+                 route_w=None) -> torch.Tensor:
+        if x.dim() != 2 or x.shape[1] != self.dim or x.dtype != torch.bfloat16 or not x.is_contiguous():
+            raise ValueError("x must be a contiguous [tokens, dim] bf16 tensor")
+        if y is None:
+            y = torch.empty_like(x)
+        T = x.shape[0]
+        gqe_moe_forward(self.h, x, y, T, self.workspace(T), stream, route_idx, route_w)
+        return y
+
+    def stats(self, stream=None) -> dict:
+        return gqe_moe_stats(self.h, self.E, stream)
+
+    def intermediates(self, tokens: int) -> dict:
+        """Views of the last forward's bucketing, hidden activations and expert outputs."""
+        offs = gqe_moe_workspace_layout(self.h, tokens)
+        ws = self._ws
+        P = tokens * self.k
+
+        def view(off, shape, dt, es):
+            n = int(np.prod(shape))
+            return ws[off:off + n * es].view(dt).view(*shape)
+
+        return dict(offs=view(offs[0], (self.E + 1,), torch.int32, 4), perm=view(offs[1], (P,), torch.int32, 4),
+                    inv=view(offs[2], (tokens, self.k), torch.int32, 4),
+                    h=view(offs[3], (P, self.d_ff), torch.bfloat16, 2), Y=view(offs[4], (P, self.dim), torch.float32, 4),
+                    idx=view(offs[5], (tokens, self.k), torch.int32, 4),
+                    w=view(offs[6], (tokens, self.k), torch.float32, 4))
+
+    def close(self):
+        if self.h:
+            gqe_moe_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 class GQEAttention:
     """GQEAttention(dim, num_query_experts=16, num_kv_heads=8, top_k=1, head_dim=None,
     variant="gqe") as in the README; weights are device tensors in the C ABI layouts."""

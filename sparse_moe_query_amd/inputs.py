@@ -121,3 +121,57 @@ def make_inputs(wl: Workload) -> dict:
                     "w_o_shared"):
             out[key] = round_bf16(out[key])
     return out
+
+
+# ----------------------------------------------------------------------------- top-k MoE-MLP
+@dataclass(frozen=True)
+class MoeWorkload:
+    """A top-k MoE-MLP layer and its input: tokens x [T, dim] routed to top_k of num_experts
+    two-layer expert MLPs of hidden width d_ff."""
+    name: str
+    dim: int
+    num_experts: int
+    top_k: int
+    d_ff: int
+    tokens: int
+    activation: str = "gelu"
+    seed: int = 0
+    router_bias_first: float = 0.0    # > 0: bias added to expert 0's logit (skewed routing)
+    router_std: float | None = None   # router weight std (default 1/sqrt(dim): logits ~ N(0, 1))
+    router_bias: bool = False         # pass a (zero unless skewed) router bias to the layer
+
+    def with_(self, **kw) -> "MoeWorkload":
+        return replace(self, **kw)
+
+
+# 2 of 8 experts active (the tutorial's example) at the main setting's width and token count, a
+# skewed 16-expert layer, and a small ragged case.
+MOE_WORKLOADS = {
+    "moe_tiny": MoeWorkload("moe_tiny", 64, 4, 2, 128, 100),
+    "moe_e8_k2_t16384": MoeWorkload("moe_e8_k2_t16384", 768, 8, 2, 3072, 16384),
+    "moe_skew_e16_k2_t4096": MoeWorkload("moe_skew_e16_k2_t4096", 1024, 16, 2, 2048, 4096,
+                                         router_std=2.70 / np.sqrt(1024.0), router_bias_first=2.0,
+                                         router_bias=True),
+}
+
+
+def make_moe_inputs(wl: MoeWorkload) -> dict:
+    """Draw x and the weights for ``wl`` (float32 arrays, x / w1 / w2 bf16-exact):
+    x [T, d] ~ N(0, 1); w_router [d, E] ~ N(0, router_std^2); b_router [E] (None unless
+    ``router_bias``); w1 [E, d, d_ff] ~ N(0, 1/d); w2 [E, d_ff, d] ~ N(0, 1/d_ff)."""
+    d, E, dff = wl.dim, wl.num_experts, wl.d_ff
+    rng = np.random.default_rng(wl.seed)
+
+    def draw(shape, std):
+        return rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)
+
+    rstd = wl.router_std if wl.router_std is not None else 1.0 / np.sqrt(d)
+    out = {"x": round_bf16(draw((wl.tokens, d), 1.0)), "w_router": draw((d, E), rstd),
+           "w1": round_bf16(draw((E, d, dff), 1.0 / np.sqrt(d))),
+           "w2": round_bf16(draw((E, dff, d), 1.0 / np.sqrt(dff)))}
+    b = None
+    if wl.router_bias:
+        b = np.zeros(E, np.float32)
+        b[0] = np.float32(wl.router_bias_first)
+    out["b_router"] = b
+    return out

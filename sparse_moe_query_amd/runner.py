@@ -44,3 +44,19 @@ def run_layer(layer: GQEAttention, x: torch.Tensor, routing: bool = True) -> dic
         out["w"] = rw.cpu().numpy().reshape(B * S, layer.G, layer.k)
     out.update(layer.aux_stats())
     return out
+
+
+def build_moe(wl, inputs: dict | None = None, device: str = "cuda:0"):
+    """MoE-MLP layer of a MoeWorkload: returns (layer, x on the device, host inputs)."""
+    from .gqe import MoEMLP
+    from .inputs import make_moe_inputs
+    inputs = make_moe_inputs(wl) if inputs is None else inputs
+
+    def dev(a, dt):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dt)
+
+    w = dict(w_router=dev(inputs["w_router"], torch.float32), b_router=dev(inputs["b_router"], torch.float32),
+             w1=dev(inputs["w1"], torch.bfloat16), w2=dev(inputs["w2"], torch.bfloat16))
+    layer = MoEMLP(wl.dim, wl.num_experts, wl.top_k, wl.d_ff, wl.activation, weights=w)
+    x = dev(inputs["x"], torch.bfloat16)
+    return layer, x, inputs

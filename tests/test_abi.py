@@ -139,3 +139,67 @@ def test_decode_host_side_errors():
         assert e.value.code == -4
     finally:
         gqe.gqe_destroy(h)
+
+
+# ----------------------------------------------------------------------------- top-k MoE-MLP
+def _moe_cfg(**kw):
+    base = dict(dim=768, num_experts=8, top_k=2, d_ff=3072, activation=0, dtype=1)
+    base.update(kw)
+    return gqe.MoeConfig(*[base[f] for f, _ in gqe.MoeConfig._fields_])
+
+
+def _moe_weights(**kw):
+    base = {f: 0x20000 * (i + 1) for i, (f, _) in enumerate(gqe.MoeWeights._fields_)}
+    base.update(kw)
+    return gqe.MoeWeights(*[base[f] for f, _ in gqe.MoeWeights._fields_])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(num_experts=0), -1, "num_experts"),
+    (dict(top_k=0), -1, "top_k"),
+    (dict(top_k=9), -1, "top_k"),
+    (dict(dim=0), -1, "dim"),
+    (dict(d_ff=0), -1, "d_ff"),
+    (dict(activation=2), -1, "activation"),
+    (dict(dtype=0), -4, "bf16"),
+    (dict(num_experts=17, top_k=2), -4, "16"),
+    (dict(dim=100), -4, "multiples of 32"),
+    (dict(d_ff=3000), -4, "multiples of 32"),
+])
+def test_moe_init_rejects_bad_configs(kw, code, msg):
+    with pytest.raises(gqe.GqeError) as e:
+        gqe.gqe_moe_init(_moe_cfg(**kw), _moe_weights())
+    assert e.value.code == code
+    assert msg in str(e.value)
+
+
+def test_moe_host_side_errors_and_sizes():
+    with pytest.raises(gqe.GqeError) as e:
+        gqe.gqe_moe_init(_moe_cfg(), _moe_weights(w1=None))
+    assert e.value.code == -2
+    with pytest.raises(gqe.GqeError) as e:
+        gqe.gqe_moe_init(_moe_cfg(), _moe_weights(w2=0x20008))
+    assert e.value.code == -3
+    h = gqe.gqe_moe_init(_moe_cfg(), _moe_weights(b_router=None))
+    try:
+        d, E, k, dff, T = 768, 8, 2, 3072, 1000
+        packed = gqe.gqe_moe_packed_weights_bytes(h)
+        assert packed >= d * 16 * 8 + 2 * E * d * dff * 2
+        ws = gqe.gqe_moe_workspace_bytes(h, T)
+        assert ws >= T * k * (dff * 2 + d * 4)   # hidden bf16 + expert outputs float32
+        assert gqe.gqe_moe_workspace_bytes(h, 0) >= 0
+        offs = gqe.gqe_moe_workspace_layout(h, T)
+        assert all(o % 256 == 0 for o in offs) and len(set(offs)) == 7
+        with pytest.raises(gqe.GqeError) as e:
+            gqe.gqe_moe_workspace_bytes(h, -1)
+        assert e.value.code == -6
+        with pytest.raises(gqe.GqeError) as e:
+            gqe.gqe_moe_workspace_bytes(h, 1 << 30)   # tokens * top_k >= 2^31
+        assert e.value.code == -6
+        L = gqe.lib()
+        # forward before packing, stats before any forward: state errors, no device call
+        assert L.gqe_moe_forward(h, 0x1000, 0x2000, 4, 0x10000, 1 << 30, None, None, None) == -8
+        assert L.gqe_moe_stats(h, None, None, None, None) == -8
+        assert L.gqe_moe_forward(None, 0x1000, 0x2000, 4, 0x10000, 1 << 30, None, None, None) == -2
+    finally:
+        gqe.gqe_moe_destroy(h)

@@ -1,0 +1,143 @@
+"""GPU parity of the top-k MoE-MLP (gqe_moe_forward through the C ABI) against the oracle
+(``oracle/moe_oracle.py``), element by element, on seeded inputs.
+
+Tolerances follow from the arithmetic.  Routing: float64 logits on both sides, so the choices are
+bit-exact except at near ties (gap below 1e-6, where the GPU's choice is taken); weights within
+float32 rounding.  Hidden activations: the kernel rounds its float32 result once to bf16 and the
+oracle rounds the exact value, so they agree except where the exact value lies within float32
+accumulation error (~1e-6 relative) of a rounding boundary: there they differ by one bf16 ulp,
+at most 2^-7 relative, and such elements must be rare.  Output: the oracle mixes the bf16-rounded
+hidden activations exactly; the kernel sums in float32 and rounds y once to bf16 (half an ulp,
+at most 2^-8 relative), plus the effect of the rare one-ulp hidden differences and of float32
+accumulation, bounded by 2e-3 of the row's RMS."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as mo
+from sparse_moe_query_amd.inputs import MOE_WORKLOADS, MoeWorkload
+
+pytestmark = pytest.mark.gpu
+
+NEAR_TIE = 1e-6
+
+
+def _run(wl, sample=None):
+    from sparse_moe_query_amd.runner import build_moe
+    print(f"[gpu] moe {wl.name} T={wl.tokens} d={wl.dim} E={wl.num_experts} k={wl.top_k} d_ff={wl.d_ff} "
+          f"{wl.activation} bias={wl.router_bias_first}", flush=True)
+    layer, x, inp = build_moe(wl)
+    T, k = wl.tokens, wl.top_k
+    ridx = torch.full((max(T, 1), k), -1, dtype=torch.int32, device=x.device)
+    rw = torch.full((max(T, 1), k), -1.0, dtype=torch.float32, device=x.device)
+    y = layer(x, route_idx=ridx[:T], route_w=rw[:T])
+    torch.cuda.synchronize()
+    return layer, x, inp, y, ridx[:T].cpu().numpy(), rw[:T].cpu().numpy()
+
+
+def _routing(inp, k, gpu_idx, gpu_w, rows):
+    r = mo.router(inp["x"][rows].astype(np.float64), inp["w_router"], k, inp["b_router"])
+    srt = -np.sort(-r["logits"], axis=1)[:, :min(k + 1, r["logits"].shape[1])]
+    near = (np.min(srt[:, :-1] - srt[:, 1:], axis=1, initial=np.inf) < NEAR_TIE) if srt.shape[1] > 1 \
+        else np.zeros(len(rows), bool)
+    differ = np.any(gpu_idx != r["idx"], axis=1)
+    assert not (differ & ~near).any(), f"routing differs away from ties at rows {np.nonzero(differ & ~near)[0][:5]}"
+    same = ~differ
+    np.testing.assert_allclose(gpu_w[same], r["w"][same], rtol=2e-6, atol=1e-7)
+    return np.where(differ[:, None], gpu_idx, r["idx"]), int(differ.sum())
+
+
+def _check_y(wl, inp, y, gpu_idx, gpu_w, rows):
+    idx, ties = _routing(inp, wl.top_k, gpu_idx[rows], gpu_w[rows], rows)
+    ref = mo.forward(inp["x"][rows], inp, wl.top_k, wl.activation, idx=idx, hidden="bf16")
+    got = y[rows].float().cpu().numpy().astype(np.float64)
+    want = ref["y"]
+    rms = np.sqrt(np.mean(want ** 2, axis=1, keepdims=True))
+    err = np.abs(got - want)
+    bound = 2.0 ** -8 * np.abs(want) + 2e-3 * rms
+    worst = float(np.max(err / np.maximum(rms, 1e-30)))
+    print(f"[gpu]   y: max |err| / row RMS {worst:.2e}, near ties {ties}", flush=True)
+    assert np.all(err <= bound), f"y beyond 2^-8 |ref| + 2e-3 RMS: worst {worst:.3e}"
+    return ref
+
+
+CASES = [
+    MoeWorkload("moe_e8_k2_ragged", 256, 8, 2, 512, 333, seed=1),
+    MoeWorkload("moe_relu_e4_k1", 128, 4, 1, 256, 257, activation="relu", seed=2),
+    MoeWorkload("moe_all_active_e4", 64, 4, 4, 96, 130, seed=3),
+    MoeWorkload("moe_skew_e16_k2", 256, 16, 2, 256, 500, router_std=2.70 / 16.0, router_bias_first=2.0,
+                router_bias=True, seed=4),
+    MoeWorkload("moe_single_expert", 64, 1, 1, 64, 70, seed=5),
+    MoeWorkload("moe_one_token", 96, 8, 3, 160, 1, seed=6),
+    MOE_WORKLOADS["moe_tiny"],
+]
+
+
+@pytest.mark.parametrize("wl", CASES, ids=[w.name for w in CASES])
+def test_moe_matches_oracle(wl):
+    layer, x, inp, y, gi, gw = _run(wl)
+    rows = np.arange(wl.tokens)
+    ref = _check_y(wl, inp, y, gi, gw, rows)
+    # hidden activations in bucket order: position p holds (perm[p], the rank of its expert)
+    it = layer.intermediates(wl.tokens)
+    offs = it["offs"].cpu().numpy()
+    perm = it["perm"].cpu().numpy()
+    h = it["h"].float().cpu().numpy().astype(np.float64)
+    assert offs[0] == 0 and offs[-1] == wl.tokens * wl.top_k
+    mism = 0
+    for e in range(wl.num_experts):
+        for p in range(offs[e], offs[e + 1]):
+            t = perm[p]
+            r = int(np.nonzero(ref["idx"][t] == e)[0][0])
+            want = ref["h"][t, r]
+            diff = np.abs(h[p] - want)
+            assert np.all(diff <= 2.0 ** -7 * np.abs(want) + 1e-5 * np.max(np.abs(ref["h"]))), (e, p)
+            mism += int(np.count_nonzero(diff))
+    frac = mism / max(1, wl.tokens * wl.top_k * wl.d_ff)
+    print(f"[gpu]   hidden: one-ulp differences in {frac:.2e} of the elements", flush=True)
+    assert frac < 1e-2
+    # statistics of the router (counts exact, mean probabilities, balance loss)
+    st = layer.stats()
+    ost = mo.stats(mo.router(inp["x"].astype(np.float64), inp["w_router"], wl.top_k, inp["b_router"])["p"],
+                   ref["idx"], wl.num_experts)
+    np.testing.assert_array_equal(st["counts"], ost["counts"])
+    np.testing.assert_allclose(st["mean_prob"], ost["mean_p"], rtol=1e-5, atol=1e-7)
+    assert st["aux"] == pytest.approx(ost["aux"], rel=1e-5)
+    layer.close()
+
+
+def test_moe_zero_tokens_is_a_no_op():
+    wl = MOE_WORKLOADS["moe_tiny"]
+    layer, x, inp, y, gi, gw = _run(wl)
+    y0 = torch.full((1, wl.dim), 7.0, dtype=torch.bfloat16, device=x.device)
+    layer(x[:0], y=y0[:0])
+    torch.cuda.synchronize()
+    assert bool((y0 == 7.0).all())
+    assert layer.stats()["counts"].sum() == 0
+    layer.close()
+
+
+def test_moe_main_workload_sampled_rows():
+    """The full 2-of-8 workload (16384 tokens, d 768, d_ff 3072), in the launch configuration the
+    bench times: 96 sampled tokens against the oracle (routing and y), the statistics over all."""
+    wl = MOE_WORKLOADS["moe_e8_k2_t16384"]
+    layer, x, inp, y, gi, gw = _run(wl)
+    rows = np.sort(np.random.default_rng(0).choice(wl.tokens, 96, replace=False))
+    rows = np.unique(np.concatenate([rows, [0, wl.tokens - 1]]))
+    _check_y(wl, inp, y, gi, gw, rows)
+    r = mo.router(inp["x"].astype(np.float64), inp["w_router"], wl.top_k, inp["b_router"])
+    idx_full, _ = _routing(inp, wl.top_k, gi, gw, np.arange(wl.tokens))
+    ost = mo.stats(r["p"], idx_full, wl.num_experts)
+    st = layer.stats()
+    np.testing.assert_array_equal(st["counts"], ost["counts"])
+    assert st["aux"] == pytest.approx(ost["aux"], rel=1e-5)
+    layer.close()
+
+
+def test_moe_deterministic():
+    wl = CASES[0]
+    layer, x, inp, y, gi, gw = _run(wl)
+    y2 = layer(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    layer.close()
