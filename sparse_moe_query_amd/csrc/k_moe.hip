@@ -15,9 +15,10 @@
 // features.  It computes C^T = W^T X^T with v_mfma_f32_32x32x16_bf16, the weights (pre-transposed
 // by the packing, k contiguous) as the A operand and the token rows as the B operand, so every lane
 // ends with four consecutive output features of one token: 8-byte bf16 stores of H, 16-byte float32
-// stores of Y.  Operands pass through LDS in k-slices of 32 (80-byte rows: the 16 rows that one
-// 16-byte fragment read serves per cycle fall in distinct banks), double-buffered: the next slice
-// is loaded into registers while the current one multiplies, one barrier per slice.  Each of the
+// stores of Y.  Operands pass through LDS in k-slices of 32 (64-byte rows; the 16 rows that one
+// 16-byte fragment read serves per cycle fall in distinct banks by an XOR swizzle of the chunks),
+// loaded straight from global memory into a ring of three LDS stages (global_load_lds_dwordx4, no
+// registers), two slices ahead of the one that multiplies; one barrier per slice.  Each of the
 // four waves owns 128 features x 64 tokens (4 x 2 accumulator tiles of 32 x 32).
 #include "gqe_common.h"
 #include "gqe_internal.h"
@@ -26,8 +27,13 @@ namespace {
 
 constexpr int kBF = 256;    // output features per tile
 constexpr int kBT = 128;    // bucket positions per tile
-constexpr int kBK = 32;     // k per LDS slice
-constexpr int kPitch = 40;  // bf16 per LDS row
+constexpr int kBK = 32;     // k per LDS slice (64-byte rows of four 16-byte chunks)
+constexpr int kStages = 3;  // LDS ring: slices s + 1 and s + 2 load while slice s multiplies
+constexpr int kLoadsPerSlice = 6;  // direct-to-LDS load instructions per wave and slice
+
+// 16-byte chunk swizzle of 64-byte LDS rows: 16 consecutive rows reading the same chunk hit 16
+// distinct 4-bank groups (row r starts at bank 16 (r % 4); the chunk moves with r / 4).
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 struct MoeGemmArgs {
     const uint16_t* w;      // [E][NF][K] expert weights, k contiguous
@@ -36,16 +42,26 @@ struct MoeGemmArgs {
     const int32_t* perm;    // [P] token of every bucket position (up)
     void* out;              // up: H [P][NF] bf16; down: Y [P][NF] float32
     int E, NF, K;
+    int ntiles;             // upper bound of the 128-position tiles over all experts
 };
 
 __device__ __forceinline__ float gelu(float v) { return 0.5f * v * (1.f + erff(v * 0.70710678118654752f)); }
 
 template <int MODE, int ACT>  // MODE 0: up (gathered x rows, activation, bf16 out); 1: down (float32 out)
 __global__ void __launch_bounds__(256, 2) moe_gemm_kernel(MoeGemmArgs a) {
-    __shared__ __align__(16) uint16_t Ws[2][kBF * kPitch];
-    __shared__ __align__(16) uint16_t Xs[2][kBT * kPitch];
+    __shared__ __align__(1024) uint16_t Ws[kStages][kBF * kBK];
+    __shared__ __align__(1024) uint16_t Xs[kStages][kBT * kBK];
+    // XCD-aware order: work groups are dealt round-robin to the 8 XCDs, so group b runs on XCD
+    // b % 8; logical tile L = (b % 8) * per + b / 8 gives each XCD a contiguous run of tiles, with
+    // the feature tiles of one 128-position tile adjacent: the XCD's L2 holds that tile's token
+    // rows for all its feature tiles and the weights of about one expert at a time.
+    const int nft = (a.NF + kBF - 1) / kBF;
+    const int per = (int)((gridDim.x + 7) / 8);
+    const int L = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (L >= a.ntiles * nft) return;
+    const int ft = L % nft;
     // this work group's (expert, 128 positions): walk the experts' tile counts
-    int rem = blockIdx.x, e = 0, M = 0, p0 = 0;
+    int rem = L / nft, e = 0, M = 0, p0 = 0;
     for (; e < a.E; ++e) {
         const int b0 = a.offs[e], b1 = a.offs[e + 1];
         const int nt = (b1 - b0 + kBT - 1) / kBT;
@@ -57,42 +73,34 @@ __global__ void __launch_bounds__(256, 2) moe_gemm_kernel(MoeGemmArgs a) {
         rem -= nt;
     }
     if (e == a.E) return;  // beyond the last tile (the grid is an upper bound)
-    const int f0 = blockIdx.y * kBF;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    const int f0 = ft * kBF;
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
     const int wf = (w >> 1) * 128, wt = (w & 1) * 64;
-    // load slots: row r0 + 64 j of the tile, 16-byte chunk ch of the 64-byte k-slice
-    const int ch = tid & 3, r0 = tid >> 2;
-    const uint16_t* wrow[4];
-    bool wok[4];
+    // Direct global -> LDS loads: one wave instruction fills 16 rows of a stage (1 KB); lane q takes
+    // row q / 4 of them and the 16-byte slot q % 4, which holds chunk slot ^ swz(row).  Rows past
+    // the tile's end load a valid row (their results are never stored).
+    const uint16_t* wsrc[4];
+    const uint16_t* xsrc[2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int f = f0 + r0 + 64 * j;
-        wok[j] = f < a.NF;
-        wrow[j] = a.w + ((int64_t)e * a.NF + (wok[j] ? f : 0)) * a.K + ch * 8;
+        const int row = (w * 4 + j) * 16 + (lane >> 2);
+        const int f = f0 + row < a.NF ? f0 + row : f0;
+        wsrc[j] = a.w + ((int64_t)e * a.NF + f) * a.K + 8 * ((lane & 3) ^ swz(row));
     }
-    const uint16_t* xrow[2];
-    bool xok[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int m = r0 + 64 * j;
-        xok[j] = m < M;
-        const int64_t row = xok[j] ? (MODE == 0 ? (int64_t)a.perm[p0 + m] : (int64_t)(p0 + m)) : 0;
-        xrow[j] = a.src + row * a.K + ch * 8;
+        const int row = (w * 2 + j) * 16 + (lane >> 2);
+        const int m = row < M ? row : 0;
+        const int64_t src_row = MODE == 0 ? (int64_t)a.perm[p0 + m] : (int64_t)(p0 + m);
+        xsrc[j] = a.src + src_row * a.K + 8 * ((lane & 3) ^ swz(row));
     }
-    u32x4_t wr[4], xr[2];
-    auto gload = [&](int k0) {
+    auto issue = [&](int slice, int stage) {
+        const int k0 = slice * kBK;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            wr[j] = wok[j] ? *reinterpret_cast<const u32x4_t*>(wrow[j] + k0) : u32x4_t{0u, 0u, 0u, 0u};
+        for (int j = 0; j < 4; ++j) dma16(wsrc[j] + k0, &Ws[stage][(w * 4 + j) * 16 * kBK]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            xr[j] = xok[j] ? *reinterpret_cast<const u32x4_t*>(xrow[j] + k0) : u32x4_t{0u, 0u, 0u, 0u};
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4_t*>(&Ws[buf][(r0 + 64 * j) * kPitch + ch * 8]) = wr[j];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4_t*>(&Xs[buf][(r0 + 64 * j) * kPitch + ch * 8]) = xr[j];
+        for (int j = 0; j < 2; ++j) dma16(xsrc[j] + k0, &Xs[stage][(w * 2 + j) * 16 * kBK]);
     };
     f32x16_t acc[4][2];
 #pragma unroll
@@ -102,29 +110,36 @@ __global__ void __launch_bounds__(256, 2) moe_gemm_kernel(MoeGemmArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     const int nst = a.K / kBK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
+    issue(0, 0);
+    if (nst > 1) issue(1, 1);
     for (int s = 0; s < nst; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nst) gload((s + 1) * kBK);
+        // this wave's loads of slice s have landed (those of slice s + 1 may still fly); the
+        // barrier publishes every wave's and frees the stage of slice s - 1
+        if (s + 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_wait(kLoadsPerSlice));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+        __syncthreads();
+        if (s + 2 < nst) issue(s + 2, (s + 2) % kStages);
+        const int st = s % kStages;
 #pragma unroll
         for (int kk = 0; kk < kBK; kk += 16) {
+            const int c = kk / 8 + hi;  // 16-byte chunk of the fragment
             bf16x8_t af[4], bq[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const bf16x8_t*>(&Ws[buf][(wf + 32 * i + l32) * kPitch + kk + 8 * hi]);
+            for (int i = 0; i < 4; ++i) {
+                const int row = wf + 32 * i + l32;
+                af[i] = *reinterpret_cast<const bf16x8_t*>(&Ws[st][row * kBK + 8 * (c ^ swz(row))]);
+            }
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bq[j] = *reinterpret_cast<const bf16x8_t*>(&Xs[buf][(wt + 32 * j + l32) * kPitch + kk + 8 * hi]);
+            for (int j = 0; j < 2; ++j) {
+                const int row = wt + 32 * j + l32;
+                bq[j] = *reinterpret_cast<const bf16x8_t*>(&Xs[st][row * kBK + 8 * (c ^ swz(row))]);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bq[j], acc[i][j], 0, 0, 0);
         }
-        if (s + 1 < nst) lstore(buf ^ 1);
-        __syncthreads();
     }
     // accumulator r of tile (i, j): feature 32 i + 8 (r / 4) + 4 hi + r % 4 of the wave's block,
     // position 32 j + l32
@@ -200,9 +215,12 @@ __global__ void moe_transpose_kernel(const uint16_t* __restrict__ src, uint16_t*
 
 template <int MODE>
 void gemm(const MoeGemmArgs& g, int act, int64_t P, hipStream_t st) {
-    const dim3 grid((unsigned)(ceil_div(P, kBT) + g.E), (unsigned)ceil_div(g.NF, kBF));
-    if (act == GQE_ACT_RELU) moe_gemm_kernel<MODE, GQE_ACT_RELU><<<grid, 256, 0, st>>>(g);
-    else moe_gemm_kernel<MODE, GQE_ACT_GELU><<<grid, 256, 0, st>>>(g);
+    MoeGemmArgs a = g;
+    a.ntiles = (int)(ceil_div(P, kBT) + g.E);
+    const int64_t n = (int64_t)a.ntiles * ceil_div(g.NF, kBF);
+    const dim3 grid((unsigned)(8 * ceil_div(n, 8)));
+    if (act == GQE_ACT_RELU) moe_gemm_kernel<MODE, GQE_ACT_RELU><<<grid, 256, 0, st>>>(a);
+    else moe_gemm_kernel<MODE, GQE_ACT_GELU><<<grid, 256, 0, st>>>(a);
 }
 
 }  // namespace
