@@ -441,7 +441,9 @@ __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint
     constexpr int NC = DH / 16, P1 = DH + 8, P2 = 72;
     __shared__ __align__(16) uint16_t Qs[64 * P1], dOs[64 * P1], QsT[DH * P2], dOsT[DH * P2];
     __shared__ float lss[64], dds[64];
-    const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    // longest first: key block 0 (every query tile after it) of every (group, sequence) leads
+    const int kb = (int)(blockIdx.x / (a.G * a.B)), g = (int)(blockIdx.x % a.G), b = (int)(blockIdx.x / a.G % a.B);
+    const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, j4 = lane >> 4;
     const int64_t S = a.S;
     const int64_t key = (int64_t)kb * 64 + w * 16 + l16;  // this lane's key column
@@ -458,57 +460,80 @@ __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint
     }
     const int nqt = (int)ceil_div(S, 64);
     const uint16_t* Qg = reinterpret_cast<const uint16_t*>(a.Q);
-    for (int h = 0; h < a.H; ++h) {
-        if (group_of(a, h) != g) continue;  // uniform over the work group
-        for (int qt = kb; qt < nqt; ++qt) {
-            __syncthreads();
-            for (int i = tid; i < 64 * (DH / 8); i += 256) {
-                const int q = i / (DH / 8), c8 = i % (DH / 8);
-                const int64_t qp = (int64_t)qt * 64 + q;
-                u32x4_t vq = {0u, 0u, 0u, 0u}, vd = {0u, 0u, 0u, 0u};
-                if (qp < S) {
-                    vq = *reinterpret_cast<const u32x4_t*>(Qg + (((int64_t)b * a.H + h) * S + qp) * DH + 8 * c8);
-                    vd = *reinterpret_cast<const u32x4_t*>(dOb + (((int64_t)b * a.H + h) * a.S_pad + qp) * DH + 8 * c8);
-                }
-                *reinterpret_cast<u32x4_t*>(&Qs[q * P1 + 8 * c8]) = vq;
-                *reinterpret_cast<u32x4_t*>(&dOs[q * P1 + 8 * c8]) = vd;
+    // (head of the group, query tile) pairs in order; the next pair's Q, dO, log-sum-exp and D are
+    // loaded into registers while the current pair multiplies
+    const int nh = (g < a.G ? a.k : 0) + ((a.s && a.skv == g) ? 1 : 0);
+    const int ntl = nqt - kb, total = nh * ntl;
+    auto head = [&](int hi) { return hi < a.k ? g * a.k + hi : a.G * a.k; };
+    constexpr int NCH = 64 * (DH / 8), R = (NCH + 255) / 256;
+    u32x4_t pq[R], pd[R];
+    float pl = 0.f, pdd = 0.f;
+    auto fetch = [&](int it) {
+        const int h = head(it / ntl), qt = kb + it % ntl;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    QsT[(8 * c8 + e) * P2 + q] = (uint16_t)(vq[e >> 1] >> (16 * (e & 1)));
-                    dOsT[(8 * c8 + e) * P2 + q] = (uint16_t)(vd[e >> 1] >> (16 * (e & 1)));
-                }
+        for (int r = 0; r < R; ++r) {
+            const int i = tid + 256 * r;
+            const int q = i / (DH / 8), c8 = i % (DH / 8);
+            const int64_t qp = (int64_t)qt * 64 + q;
+            pq[r] = pd[r] = u32x4_t{0u, 0u, 0u, 0u};
+            if (i < NCH && qp < S) {
+                pq[r] = *reinterpret_cast<const u32x4_t*>(Qg + (((int64_t)b * a.H + h) * S + qp) * DH + 8 * c8);
+                pd[r] = *reinterpret_cast<const u32x4_t*>(dOb + (((int64_t)b * a.H + h) * a.S_pad + qp) * DH + 8 * c8);
             }
-            if (tid < 64) {
-                const int64_t qp = (int64_t)qt * 64 + tid;
-                const int64_t ti = (b * S + (qp < S ? qp : 0)) * a.H + h;
-                lss[tid] = a.lse[ti];
-                dds[tid] = a.Dd[ti];
+        }
+        if (tid < 64) {
+            const int64_t qp = (int64_t)qt * 64 + tid;
+            const int64_t ti = (b * S + (qp < S ? qp : 0)) * a.H + h;
+            pl = a.lse[ti];
+            pdd = a.Dd[ti];
+        }
+    };
+    if (total > 0) fetch(0);
+    for (int it = 0; it < total; ++it) {
+        const int qt = kb + it % ntl;
+        __syncthreads();  // the previous pair's products are done with the tiles
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = tid + 256 * r;
+            if (i >= NCH) continue;
+            const int q = i / (DH / 8), c8 = i % (DH / 8);
+            *reinterpret_cast<u32x4_t*>(&Qs[q * P1 + 8 * c8]) = pq[r];
+            *reinterpret_cast<u32x4_t*>(&dOs[q * P1 + 8 * c8]) = pd[r];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                QsT[(8 * c8 + e) * P2 + q] = (uint16_t)(pq[r][e >> 1] >> (16 * (e & 1)));
+                dOsT[(8 * c8 + e) * P2 + q] = (uint16_t)(pd[r][e >> 1] >> (16 * (e & 1)));
             }
-            __syncthreads();
+        }
+        if (tid < 64) {
+            lss[tid] = pl;
+            dds[tid] = pdd;
+        }
+        __syncthreads();
+        if (it + 1 < total) fetch(it + 1);
 #pragma unroll
-            for (int qs = 0; qs < 4; ++qs) {
-                const int q0 = qs * 16;
-                f32x4_t sacc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+        for (int qs = 0; qs < 4; ++qs) {
+            const int q0 = qs * 16;
+            f32x4_t sacc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    sacc = mma16(lds8(&Qs[(q0 + l16) * P1 + 16 * c + 4 * j4]), kf[c], sacc);
-                    dp = mma16(lds8(&dOs[(q0 + l16) * P1 + 16 * c + 4 * j4]), vf[c], dp);
-                }
-                float p[4], ds[4];
+            for (int c = 0; c < NC; ++c) {
+                sacc = mma16(lds8(&Qs[(q0 + l16) * P1 + 16 * c + 4 * j4]), kf[c], sacc);
+                dp = mma16(lds8(&dOs[(q0 + l16) * P1 + 16 * c + 4 * j4]), vf[c], dp);
+            }
+            float p[4], ds[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int qr = q0 + 4 * j4 + i;
-                    const int64_t qp = (int64_t)qt * 64 + qr;
-                    const bool on = kin && qp < S && qp >= key;
-                    p[i] = on ? __builtin_amdgcn_exp2f(sacc[i] - lss[qr]) : 0.f;
-                    ds[i] = on ? p[i] * (dp[i] - dds[qr]) : 0.f;
-                }
-                const s16x4_t pa = pack4(p), da = pack4(ds);
+            for (int i = 0; i < 4; ++i) {
+                const int qr = q0 + 4 * j4 + i;
+                const int64_t qp = (int64_t)qt * 64 + qr;
+                const bool on = kin && qp < S && qp >= key;
+                p[i] = on ? __builtin_amdgcn_exp2f(sacc[i] - lss[qr]) : 0.f;
+                ds[i] = on ? p[i] * (dp[i] - dds[qr]) : 0.f;
+            }
+            const s16x4_t pa = pack4(p), da = pack4(ds);
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    dv[c] = mma16(pa, lds8(&dOsT[(16 * c + l16) * P2 + q0 + 4 * j4]), dv[c]);
-                    dk[c] = mma16(da, lds8(&QsT[(16 * c + l16) * P2 + q0 + 4 * j4]), dk[c]);
-                }
+            for (int c = 0; c < NC; ++c) {
+                dv[c] = mma16(pa, lds8(&dOsT[(16 * c + l16) * P2 + q0 + 4 * j4]), dv[c]);
+                dk[c] = mma16(da, lds8(&QsT[(16 * c + l16) * P2 + q0 + 4 * j4]), dk[c]);
             }
         }
     }
@@ -540,7 +565,11 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
                                                           const uint16_t* __restrict__ dOb) {
     constexpr int NC = DH / 16, P1 = DH + 8, P2 = 72;
     __shared__ __align__(16) uint16_t Ks[64 * P1], Vs[64 * P1], KsT[DH * P2];
-    const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    // longest first: the last query block (every key tile before it) of every (head, sequence) leads
+    const int nqb = (int)ceil_div(a.S, 64);
+    const int qb = nqb - 1 - (int)(blockIdx.x / (a.H * a.B));
+    const int h = (int)(blockIdx.x % a.H), b = (int)(blockIdx.x / a.H % a.B);
+    const int tid = threadIdx.x;
     const int g = group_of(a, h);
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, j4 = lane >> 4;
     const int64_t S = a.S;
@@ -556,99 +585,117 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
     const float Dq = qin ? a.Dd[(b * S + qpos) * a.H + h] : 0.f;
     const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + ((int64_t)(b * a.G + g) * a.S_pad) * DH;
     const uint16_t* Vb = Vr + ((int64_t)(b * a.G + g) * a.S_pad) * DH;
-    auto stage = [&](int kt, bool full) {
-        __syncthreads();
-        for (int i = tid; i < 64 * (DH / 8); i += 256) {
+    const int ntile = qb + 1;
+    // pass 1 (iterations 0 .. ntile - 1): each lane folds its four keys of every sub-tile into
+    // (m, l); then the four lanes of a query column are combined into the row log-sum-exp L.
+    // pass 2 (ntile .. 2 ntile - 1): dS^T = P^T (dP^T - D), dq += dS K.  The next iteration's key
+    // (and value) tile is loaded into registers while the current one multiplies.
+    constexpr int NCH = 64 * (DH / 8), R = (NCH + 255) / 256;
+    u32x4_t pk[R], pv[R];
+    auto fetch = [&](int it) {
+        const int kt = it % ntile;
+        const bool full = it >= ntile;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = tid + 256 * r;
             const int kk = i / (DH / 8), c8 = i % (DH / 8);
             const int64_t kp = (int64_t)kt * 64 + kk;
-            u32x4_t vk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-            if (kp < S) {
-                vk = *reinterpret_cast<const u32x4_t*>(Kb + kp * DH + 8 * c8);
-                if (full) vv = *reinterpret_cast<const u32x4_t*>(Vb + kp * DH + 8 * c8);
-            }
-            *reinterpret_cast<u32x4_t*>(&Ks[kk * P1 + 8 * c8]) = vk;
-            if (full) {
-                *reinterpret_cast<u32x4_t*>(&Vs[kk * P1 + 8 * c8]) = vv;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) KsT[(8 * c8 + e) * P2 + kk] = (uint16_t)(vk[e >> 1] >> (16 * (e & 1)));
+            pk[r] = pv[r] = u32x4_t{0u, 0u, 0u, 0u};
+            if (i < NCH && kp < S) {
+                pk[r] = *reinterpret_cast<const u32x4_t*>(Kb + kp * DH + 8 * c8);
+                if (full) pv[r] = *reinterpret_cast<const u32x4_t*>(Vb + kp * DH + 8 * c8);
             }
         }
-        __syncthreads();
     };
-    const int ntile = qb + 1;
-    // pass 1: each lane folds its four keys of every sub-tile into (m, l); then the four lanes of a
-    // query column are combined
-    float m = -INFINITY, l = 0.f;
-    for (int kt = 0; kt < ntile; ++kt) {
-        stage(kt, false);
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub) {
-            const int k0 = sub * 16;
-            f32x4_t st = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < NC; ++c) st = mma16(lds8(&Ks[(k0 + l16) * P1 + 16 * c + 4 * j4]), qf[c], st);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t kp = (int64_t)kt * 64 + k0 + 4 * j4 + i;
-                if (kp <= qpos && kp < S) {
-                    const float mn = fmaxf(m, st[i]);
-                    l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(st[i] - mn);
-                    m = mn;
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int o = 0; o < 2; ++o) {
-        float mo, lo;
-        if (o == 0) {
-            const auto sm = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-            const auto sl = __builtin_amdgcn_permlane16_swap(__float_as_uint(l), __float_as_uint(l), false, false);
-            mo = (j4 & 1) ? __uint_as_float(sm[0]) : __uint_as_float(sm[1]);
-            lo = (j4 & 1) ? __uint_as_float(sl[0]) : __uint_as_float(sl[1]);
-        } else {
-            const auto sm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-            const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
-            mo = (j4 & 2) ? __uint_as_float(sm[0]) : __uint_as_float(sm[1]);
-            lo = (j4 & 2) ? __uint_as_float(sl[0]) : __uint_as_float(sl[1]);
-        }
-        if (mo != -INFINITY) {
-            if (m == -INFINITY) {
-                m = mo;
-                l = lo;
-            } else {
-                const float mn = fmaxf(m, mo);
-                l = l * __builtin_amdgcn_exp2f(m - mn) + lo * __builtin_amdgcn_exp2f(mo - mn);
-                m = mn;
-            }
-        }
-    }
-    const float L = m + __builtin_amdgcn_logf(l);
-    // pass 2
+    float m = -INFINITY, l = 0.f, L = 0.f;
     f32x4_t dq[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) dq[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int kt = 0; kt < ntile; ++kt) {
-        stage(kt, true);
+    fetch(0);
+    for (int it = 0; it < 2 * ntile; ++it) {
+        const int kt = it % ntile;
+        const bool full = it >= ntile;
+        __syncthreads();  // the previous tile's products are done
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub) {
-            const int k0 = sub * 16;
-            f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < R; ++r) {
+            const int i = tid + 256 * r;
+            if (i >= NCH) continue;
+            const int kk = i / (DH / 8), c8 = i % (DH / 8);
+            *reinterpret_cast<u32x4_t*>(&Ks[kk * P1 + 8 * c8]) = pk[r];
+            if (full) {
+                *reinterpret_cast<u32x4_t*>(&Vs[kk * P1 + 8 * c8]) = pv[r];
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                st = mma16(lds8(&Ks[(k0 + l16) * P1 + 16 * c + 4 * j4]), qf[c], st);
-                dpt = mma16(lds8(&Vs[(k0 + l16) * P1 + 16 * c + 4 * j4]), df[c], dpt);
+                for (int e = 0; e < 8; ++e) KsT[(8 * c8 + e) * P2 + kk] = (uint16_t)(pk[r][e >> 1] >> (16 * (e & 1)));
             }
-            float ds[4];
+        }
+        __syncthreads();
+        if (it + 1 < 2 * ntile) fetch(it + 1);
+        if (it == ntile) {  // first pass-2 tile: finish the log-sum-exp
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t kp = (int64_t)kt * 64 + k0 + 4 * j4 + i;
-                const bool on = qin && kp <= qpos && kp < S;
-                ds[i] = on ? __builtin_amdgcn_exp2f(st[i] - L) * (dpt[i] - Dq) : 0.f;
+            for (int o = 0; o < 2; ++o) {
+                float mo, lo;
+                if (o == 0) {
+                    const auto sm = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+                    const auto sl = __builtin_amdgcn_permlane16_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+                    mo = (j4 & 1) ? __uint_as_float(sm[0]) : __uint_as_float(sm[1]);
+                    lo = (j4 & 1) ? __uint_as_float(sl[0]) : __uint_as_float(sl[1]);
+                } else {
+                    const auto sm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+                    const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+                    mo = (j4 & 2) ? __uint_as_float(sm[0]) : __uint_as_float(sm[1]);
+                    lo = (j4 & 2) ? __uint_as_float(sl[0]) : __uint_as_float(sl[1]);
+                }
+                if (mo != -INFINITY) {
+                    if (m == -INFINITY) {
+                        m = mo;
+                        l = lo;
+                    } else {
+                        const float mn = fmaxf(m, mo);
+                        l = l * __builtin_amdgcn_exp2f(m - mn) + lo * __builtin_amdgcn_exp2f(mo - mn);
+                        m = mn;
+                    }
+                }
             }
-            const s16x4_t da = pack4(ds);
+            L = m + __builtin_amdgcn_logf(l);
+        }
+        if (!full) {
 #pragma unroll
-            for (int c = 0; c < NC; ++c) dq[c] = mma16(da, lds8(&KsT[(16 * c + l16) * P2 + k0 + 4 * j4]), dq[c]);
+            for (int sub = 0; sub < 4; ++sub) {
+                const int k0 = sub * 16;
+                f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NC; ++c) st = mma16(lds8(&Ks[(k0 + l16) * P1 + 16 * c + 4 * j4]), qf[c], st);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t kp = (int64_t)kt * 64 + k0 + 4 * j4 + i;
+                    if (kp <= qpos && kp < S) {
+                        const float mn = fmaxf(m, st[i]);
+                        l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(st[i] - mn);
+                        m = mn;
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int sub = 0; sub < 4; ++sub) {
+                const int k0 = sub * 16;
+                f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    st = mma16(lds8(&Ks[(k0 + l16) * P1 + 16 * c + 4 * j4]), qf[c], st);
+                    dpt = mma16(lds8(&Vs[(k0 + l16) * P1 + 16 * c + 4 * j4]), df[c], dpt);
+                }
+                float ds[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t kp = (int64_t)kt * 64 + k0 + 4 * j4 + i;
+                    const bool on = qin && kp <= qpos && kp < S;
+                    ds[i] = on ? __builtin_amdgcn_exp2f(st[i] - L) * (dpt[i] - Dq) : 0.f;
+                }
+                const s16x4_t da = pack4(ds);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) dq[c] = mma16(da, lds8(&KsT[(16 * c + l16) * P2 + k0 + 4 * j4]), dq[c]);
+            }
         }
     }
     // C layout: lane column = head dim 16 c + l16, rows = queries 16 w + 4 j4 + i
@@ -1251,9 +1298,10 @@ hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km
         // bf16: matrix cores
         const int64_t n = a.B * (a.G + a.H) * a.S_pad * a.dh;
         bwd_mprep_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>(a, a.vr, a.dob);
+        const dim3 gq1((unsigned)(nblk * a.H * a.B)), gk1((unsigned)(nblk * a.G * a.B));
 #define GQE_BWD_MFMA(DHV)                                                     \
-    bwd_dq_mfma_kernel<DHV><<<gq, 256, 0, st>>>(a, a.vr, a.dob);              \
-    bwd_dkv_mfma_kernel<DHV><<<gk, 256, 0, st>>>(a, a.vr, a.dob);
+    bwd_dq_mfma_kernel<DHV><<<gq1, 256, 0, st>>>(a, a.vr, a.dob);             \
+    bwd_dkv_mfma_kernel<DHV><<<gk1, 256, 0, st>>>(a, a.vr, a.dob);
         switch (a.dh / 16) {  // d_h: a multiple of 16, at most 128
             case 1: GQE_BWD_MFMA(16) break;
             case 2: GQE_BWD_MFMA(32) break;
