@@ -433,8 +433,9 @@ __global__ void bwd_mprep_kernel(BwdArgs a, uint16_t* __restrict__ Vr, uint16_t*
     }
 }
 
-// dk, dv of 64 keys (wave w: keys 16 w ..) of one (sequence, group) over the later queries of every
-// head of the group, query tiles of 64 staged in LDS row-major and transposed.
+// dk, dv of 128 keys (wave w: keys 32 w .. 32 w + 31, two 16-key column groups) of one (sequence,
+// group) over the later queries of every head of the group, query tiles of 64 staged in LDS
+// row-major and transposed; every fragment read from LDS feeds the products of both column groups.
 template <int DH>
 __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint16_t* __restrict__ Vr,
                                                            const uint16_t* __restrict__ dOb) {
@@ -446,30 +447,35 @@ __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, j4 = lane >> 4;
     const int64_t S = a.S;
-    const int64_t key = (int64_t)kb * 64 + w * 16 + l16;  // this lane's key column
-    const bool kin = key < S;
     const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + ((int64_t)(b * a.G + g) * a.S_pad) * DH;
     const uint16_t* Vb = Vr + ((int64_t)(b * a.G + g) * a.S_pad) * DH;
-    s16x4_t kf[NC], vf[NC];
-    f32x4_t dk[NC], dv[NC];
+    int64_t key[2];  // this lane's key column in each group
+    bool kin[2];
+    s16x4_t kf[2][NC], vf[2][NC];
+    f32x4_t dk[2][NC], dv[2][NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        kf[c] = kin ? gld8(Kb + key * DH + 16 * c + 4 * j4) : s16x4_t{0, 0, 0, 0};
-        vf[c] = kin ? gld8(Vb + key * DH + 16 * c + 4 * j4) : s16x4_t{0, 0, 0, 0};
-        dk[c] = dv[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 2; ++u) {
+        key[u] = (int64_t)kb * 128 + w * 32 + 16 * u + l16;
+        kin[u] = key[u] < S;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            kf[u][c] = kin[u] ? gld8(Kb + key[u] * DH + 16 * c + 4 * j4) : s16x4_t{0, 0, 0, 0};
+            vf[u][c] = kin[u] ? gld8(Vb + key[u] * DH + 16 * c + 4 * j4) : s16x4_t{0, 0, 0, 0};
+            dk[u][c] = dv[u][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
     }
     const int nqt = (int)ceil_div(S, 64);
     const uint16_t* Qg = reinterpret_cast<const uint16_t*>(a.Q);
     // (head of the group, query tile) pairs in order; the next pair's Q, dO, log-sum-exp and D are
     // loaded into registers while the current pair multiplies
-    const int nh = (g < a.G ? a.k : 0) + ((a.s && a.skv == g) ? 1 : 0);
-    const int ntl = nqt - kb, total = nh * ntl;
+    const int nh = a.k + ((a.s && a.skv == g) ? 1 : 0);
+    const int qt0 = 2 * kb, ntl = nqt - qt0, total = nh * ntl;
     auto head = [&](int hi) { return hi < a.k ? g * a.k + hi : a.G * a.k; };
     constexpr int NCH = 64 * (DH / 8), R = (NCH + 255) / 256;
     u32x4_t pq[R], pd[R];
     float pl = 0.f, pdd = 0.f;
     auto fetch = [&](int it) {
-        const int h = head(it / ntl), qt = kb + it % ntl;
+        const int h = head(it / ntl), qt = qt0 + it % ntl;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int i = tid + 256 * r;
@@ -490,7 +496,7 @@ __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint
     };
     if (total > 0) fetch(0);
     for (int it = 0; it < total; ++it) {
-        const int qt = kb + it % ntl;
+        const int qt = qt0 + it % ntl;
         __syncthreads();  // the previous pair's products are done with the tiles
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -514,48 +520,66 @@ __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint
 #pragma unroll
         for (int qs = 0; qs < 4; ++qs) {
             const int q0 = qs * 16;
-            f32x4_t sacc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+            s16x4_t qa[NC], da_[NC], qtb[NC], dtb[NC];
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                sacc = mma16(lds8(&Qs[(q0 + l16) * P1 + 16 * c + 4 * j4]), kf[c], sacc);
-                dp = mma16(lds8(&dOs[(q0 + l16) * P1 + 16 * c + 4 * j4]), vf[c], dp);
+                qa[c] = lds8(&Qs[(q0 + l16) * P1 + 16 * c + 4 * j4]);
+                da_[c] = lds8(&dOs[(q0 + l16) * P1 + 16 * c + 4 * j4]);
+                qtb[c] = lds8(&QsT[(16 * c + l16) * P2 + q0 + 4 * j4]);
+                dtb[c] = lds8(&dOsT[(16 * c + l16) * P2 + q0 + 4 * j4]);
             }
-            float p[4], ds[4];
+            float lq[4], dq4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int qr = q0 + 4 * j4 + i;
-                const int64_t qp = (int64_t)qt * 64 + qr;
-                const bool on = kin && qp < S && qp >= key;
-                p[i] = on ? __builtin_amdgcn_exp2f(sacc[i] - lss[qr]) : 0.f;
-                ds[i] = on ? p[i] * (dp[i] - dds[qr]) : 0.f;
+                lq[i] = lss[q0 + 4 * j4 + i];
+                dq4[i] = dds[q0 + 4 * j4 + i];
             }
-            const s16x4_t pa = pack4(p), da = pack4(ds);
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                dv[c] = mma16(pa, lds8(&dOsT[(16 * c + l16) * P2 + q0 + 4 * j4]), dv[c]);
-                dk[c] = mma16(da, lds8(&QsT[(16 * c + l16) * P2 + q0 + 4 * j4]), dk[c]);
+            for (int u = 0; u < 2; ++u) {
+                f32x4_t sacc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    sacc = mma16(qa[c], kf[u][c], sacc);
+                    dp = mma16(da_[c], vf[u][c], dp);
+                }
+                float p[4], ds[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t qp = (int64_t)qt * 64 + q0 + 4 * j4 + i;
+                    const bool on = kin[u] && qp < S && qp >= key[u];
+                    p[i] = on ? __builtin_amdgcn_exp2f(sacc[i] - lq[i]) : 0.f;
+                    ds[i] = on ? p[i] * (dp[i] - dq4[i]) : 0.f;
+                }
+                const s16x4_t pa = pack4(p), dsa = pack4(ds);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    dv[u][c] = mma16(pa, dtb[c], dv[u][c]);
+                    dk[u][c] = mma16(dsa, qtb[c], dk[u][c]);
+                }
             }
         }
     }
-    // C layout: lane column = head dim 16 c + l16, rows = keys 16 w + 4 j4 + i
+    // C layout: lane column = head dim 16 c + l16, rows = keys 32 w + 16 u + 4 j4 + i
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t kp = (int64_t)kb * 64 + w * 16 + 4 * j4 + i;
-            const int col = 16 * c + l16;
-            float kv = dk[c][i] * (1.f / kLog2e);
-            if (a.rope) {
-                const float other = swap_x1(kv);  // pair partner: the neighbouring column
-                float lo = (l16 & 1) ? other : kv, hi = (l16 & 1) ? kv : other;
-                rope_pair(lo, hi, -kp, a.rope[col >> 1]);
-                kv = (l16 & 1) ? hi : lo;
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t kp = (int64_t)kb * 128 + w * 32 + 16 * u + 4 * j4 + i;
+                const int col = 16 * c + l16;
+                float kv = dk[u][c][i] * (1.f / kLog2e);
+                if (a.rope) {
+                    const float other = swap_x1(kv);  // pair partner: the neighbouring column
+                    float lo = (l16 & 1) ? other : kv, hi = (l16 & 1) ? kv : other;
+                    rope_pair(lo, hi, -kp, a.rope[col >> 1]);
+                    kv = (l16 & 1) ? hi : lo;
+                }
+                if (kp < S) {
+                    a.dK[((b * S + kp) * a.G + g) * DH + col] = kv;
+                    a.dV[((b * S + kp) * a.G + g) * DH + col] = dv[u][c][i];
+                }
             }
-            if (kp < S) {
-                a.dK[((b * S + kp) * a.G + g) * DH + col] = kv;
-                a.dV[((b * S + kp) * a.G + g) * DH + col] = dv[c][i];
-            }
-        }
 }
 
 // dq of 64 queries (wave w: queries 16 w ..) of one (sequence, head): pass 1 the row log-sum-exp,
@@ -1298,7 +1322,7 @@ hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km
         // bf16: matrix cores
         const int64_t n = a.B * (a.G + a.H) * a.S_pad * a.dh;
         bwd_mprep_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>(a, a.vr, a.dob);
-        const dim3 gq1((unsigned)(nblk * a.H * a.B)), gk1((unsigned)(nblk * a.G * a.B));
+        const dim3 gq1((unsigned)(nblk * a.H * a.B)), gk1((unsigned)(ceil_div(a.S, 128) * a.G * a.B));
 #define GQE_BWD_MFMA(DHV)                                                     \
     bwd_dq_mfma_kernel<DHV><<<gq1, 256, 0, st>>>(a, a.vr, a.dob);             \
     bwd_dkv_mfma_kernel<DHV><<<gk1, 256, 0, st>>>(a, a.vr, a.dob);
