@@ -1127,11 +1127,15 @@ struct ProbWx {
 };
 
 // dx, dense part: K = [dK (G d_h) | dV (G d_h) | shared dq (d_h)] written (which = 0), then the
-// router logits' part, K = N, added (which = 1)
+// router logits' part, K = N, added (which = 1).  With `expand` the which = 0 product also takes
+// the routed query heads as N more d_h-wide segments, one per expert: a token's segment holds its
+// dq for that expert where it chose it and zeros elsewhere (n / k times the routed work, in one
+// pass over dx instead of one read-modify-write per (group, rank)).
 template <typename T>
 struct ProbDxDense {
     BwdArgs a;
     int which;
+    int expand;
     struct Sub {
         int M, N, K;
     };
@@ -1139,10 +1143,24 @@ struct ProbDxDense {
     __device__ bool begin(int, Sub& s) const {
         s.M = (int)a.T;
         s.N = a.d;
-        s.K = which ? (a.dense ? 0 : a.N) : kd();
+        s.K = which ? (a.dense ? 0 : a.N) : kd() + (expand ? a.N * a.dh : 0);
         return s.K > 0;
     }
+    // routed segment element kk' = e d_h + j: the head of token t that chose expert e, or -1
+    __device__ int routed_head(int t, int e) const {
+        const int g = e / a.n;
+        if (a.dense) return g * a.k + e % a.n;
+        const int32_t* id = a.idx + ((int64_t)t * a.G + g) * a.k;
+        for (int r = 0; r < a.k; ++r)
+            if (id[r] == e) return g * a.k + r;
+        return -1;
+    }
     __device__ float lda(const Sub&, int t, int kk) const {
+        if (!which && kk >= kd()) {
+            const int e = (kk - kd()) / a.dh, j = (kk - kd()) % a.dh;
+            const int h = routed_head(t, e);
+            return h < 0 ? 0.f : a.dQ[((int64_t)t * a.H + h) * a.dh + j];
+        }
         if (which) kk += kd();
         const int GD = a.G * a.dh;
         if (kk < GD) return a.dK[(int64_t)t * GD + kk];
@@ -1153,6 +1171,10 @@ struct ProbDxDense {
         return a.dl[(int64_t)t * a.N + kk];
     }
     __device__ float ldb(const Sub&, int kk, int i) const {
+        if (!which && kk >= kd()) {
+            const int e = (kk - kd()) / a.dh, j = (kk - kd()) % a.dh;
+            return ld<T>(a.wq, ((int64_t)e * a.d + i) * a.dh + j);
+        }
         if (which) kk += kd();
         const int GD = a.G * a.dh;
         if (kk < GD) return ld<T>(a.wk, (int64_t)i * GD + kk);
@@ -1166,6 +1188,17 @@ struct ProbDxDense {
     __device__ bool lda8(const Sub&, int t, int kk, float (&v)[8]) const {
         if (which) return false;
         const int GD = a.G * a.dh;
+        if (kk >= kd()) {
+            const int e = (kk - kd()) / a.dh, j = (kk - kd()) % a.dh;
+            const int h = routed_head(t, e);
+            if (h < 0) {
+#pragma unroll
+                for (int z = 0; z < 8; ++z) v[z] = 0.f;
+            } else {
+                ld8f(a.dQ + ((int64_t)t * a.H + h) * a.dh + j, v);
+            }
+            return true;
+        }
         if (kk < GD) ld8f(a.dK + (int64_t)t * GD + kk, v);
         else if (kk < 2 * GD) ld8f(a.dV + (int64_t)t * GD + kk - GD, v);
         else ld8f(a.dQ + ((int64_t)t * a.H + a.G * a.k) * a.dh + kk - 2 * GD, v);
@@ -1174,6 +1207,11 @@ struct ProbDxDense {
     __device__ bool ldb8(const Sub&, int kk, int i, float (&v)[8]) const {
         if (which) return false;
         const int GD = a.G * a.dh;
+        if (kk >= kd()) {
+            const int e = (kk - kd()) / a.dh, j = (kk - kd()) % a.dh;
+            ld8<T>(a.wq, ((int64_t)e * a.d + i) * a.dh + j, v);
+            return true;
+        }
         if (kk < GD) ld8<T>(a.wk, (int64_t)i * GD + kk, v);
         else if (kk < 2 * GD) ld8<T>(a.wv, (int64_t)i * GD + kk - GD, v);
         else ld8<T>(a.wqs, (int64_t)i * a.dh + kk - 2 * GD, v);
@@ -1369,11 +1407,14 @@ weights:
     }
     if (km) km->mark(KT_BWD_WGRAD);
     if (km) km->begin(KT_BWD_DX);
-    tgemm<ProbDxDense<T>, true, true>(mm, ProbDxDense<T>{a, 0}, nt, a.d, 1, st);
-    if (!a.dense) tgemm<ProbDxDense<T>, true, true>(false, ProbDxDense<T>{a, 1}, nt, a.d, 1, st);
-    for (int g = 0; g < a.G; ++g)
-        for (int r = 0; r < a.k; ++r)
-            tgemm<ProbDxRouted<T>, true, true>(mm, ProbDxRouted<T>{a, L, g, r}, nt, a.d, a.n, st);
+    // routed heads inside the dense product while that costs at most 4x their own work
+    const int expand = a.n <= 4 * a.k ? 1 : 0;
+    tgemm<ProbDxDense<T>, true, true>(mm, ProbDxDense<T>{a, 0, expand}, nt, a.d, 1, st);
+    if (!a.dense) tgemm<ProbDxDense<T>, true, true>(false, ProbDxDense<T>{a, 1, 0}, nt, a.d, 1, st);
+    if (!expand)
+        for (int g = 0; g < a.G; ++g)
+            for (int r = 0; r < a.k; ++r)
+                tgemm<ProbDxRouted<T>, true, true>(mm, ProbDxRouted<T>{a, L, g, r}, nt, a.d, a.n, st);
     if (km) km->mark(KT_BWD_DX);
     return hipGetLastError();
 }

@@ -83,6 +83,8 @@ CASES = [
     _wl("bwd_tiles_rope_dh64", k=2, dh=64, B=1, S=200, rope_base=10000.0, seed=13),
     _wl("bwd_dh128", d=512, N=4, G=2, dh=128, B=1, S=150, seed=14),
     _wl("bwd_dh16_k2", d=128, k=2, dh=16, B=2, S=130, seed=15),
+    # n = 8 > 4 k: the routed dx pieces run as their own per-(group, rank) products
+    _wl("bwd_n8_k1_routed_dx", N=16, G=2, k=1, dh=32, B=1, S=70, seed=16),
     Workload("bwd_tiny_f32", 64, 4, 2, 1, 16, 1, 32, dtype="f32", router_std=0.5, seed=8),
     Workload("bwd_f32_k2_rope", 64, 8, 2, 2, 16, 2, 24, dtype="f32", router_std=0.5, rope_base=500.0, seed=9),
 ]
