@@ -821,7 +821,11 @@ __device__ __forceinline__ u32x4_t pack8(const float (&v)[8]) {
 // accumulators, wave w owning the 32 x 32 quarter (w / 2, w % 2) of the 64 x 64 tile.
 template <class Prob, bool AK, bool BK>
 __global__ void __launch_bounds__(256) tgemm_mfma_kernel(Prob pr, int splits, float* part, int64_t pstride) {
-    constexpr int KC = 32, KP = 40;  // k chunk; LDS row pitch in bf16 (80 bytes: 16 rows hit distinct banks)
+    // k chunk: 32 for operands contiguous along k (one 16-byte vector per thread and operand), 128
+    // for operands contiguous along m and n (four k of eight m per thread).  LDS row pitch 40 / 136
+    // bf16 (80 / 272 bytes): the 8-byte fragment reads of 16 rows x 2 k-quads hit 64 distinct banks.
+    static_assert(AK == BK, "both operands contiguous along k, or neither");
+    constexpr int KC = AK ? 32 : 128, KP = AK ? 40 : 136, NQ = KC / 32;
     __shared__ __align__(16) uint16_t As[64 * KP];  // [m][k]
     __shared__ __align__(16) uint16_t Bs[64 * KP];  // [n][k]
     typename Prob::Sub sp;
@@ -839,42 +843,64 @@ __global__ void __launch_bounds__(256) tgemm_mfma_kernel(Prob pr, int splits, fl
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int k0 = kb; k0 < ke; k0 += KC) {
-        // 64 x 32 of A and of B, eight elements per thread: a vector load where the problem
-        // offers one for the whole run (lda8 / ldb8), else element by element
-        {
-            float v[8];
-            if (AK) {
-                const int m = tid >> 2, ka = (tid & 3) * 8;
+        // 64 x KC of A and of B.  Operands contiguous along k: eight neighbouring k of one row per
+        // load, one 16-byte LDS store.  Operands contiguous along m (n): eight neighbouring m of
+        // four neighbouring k per thread, regrouped in registers into eight 8-byte LDS stores of
+        // four k each.  Vector loads where the problem offers them for the whole run, else
+        // element by element (ragged edges).
+        if (AK) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                float v[8];
+                const int idx = tid + 256 * q, m = idx / (KC / 8), ka = (idx % (KC / 8)) * 8;
                 const bool in = m0 + m < sp.M;
                 if (!(in && k0 + ka + 8 <= ke && pr.lda8(sp, m0 + m, k0 + ka, v)))
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = (in && k0 + ka + e < ke) ? pr.lda(sp, m0 + m, k0 + ka + e) : 0.f;
                 *reinterpret_cast<u32x4_t*>(&As[m * KP + ka]) = pack8(v);
-            } else {
-                const int ka = tid >> 3, m8 = (tid & 7) * 8;
-                const bool in = k0 + ka < ke;
-                if (!(in && m0 + m8 + 8 <= sp.M && pr.lda8(sp, m0 + m8, k0 + ka, v)))
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = (in && m0 + m8 + e < sp.M) ? pr.lda(sp, m0 + m8 + e, k0 + ka) : 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) As[(m8 + e) * KP + ka] = bf16_bits(v[e]);
             }
-            if (BK) {
-                const int n = tid >> 2, kq = (tid & 3) * 8;
+        } else {
+            float v[4][8];
+            const int kq = (tid >> 3) * 4, m8 = (tid & 7) * 8;
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                const bool in = k0 + kq + z < ke;
+                if (!(in && m0 + m8 + 8 <= sp.M && pr.lda8(sp, m0 + m8, k0 + kq + z, v[z])))
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        v[z][e] = (in && m0 + m8 + e < sp.M) ? pr.lda(sp, m0 + m8 + e, k0 + kq + z) : 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                *reinterpret_cast<u32x2_t*>(&As[(m8 + e) * KP + kq]) =
+                    u32x2_t{pack_bf16x2(v[0][e], v[1][e]), pack_bf16x2(v[2][e], v[3][e])};
+        }
+        if (BK) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                float v[8];
+                const int idx = tid + 256 * q, n = idx / (KC / 8), kq = (idx % (KC / 8)) * 8;
                 const bool in = n0 + n < sp.N;
                 if (!(in && k0 + kq + 8 <= ke && pr.ldb8(sp, k0 + kq, n0 + n, v)))
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = (in && k0 + kq + e < ke) ? pr.ldb(sp, k0 + kq + e, n0 + n) : 0.f;
                 *reinterpret_cast<u32x4_t*>(&Bs[n * KP + kq]) = pack8(v);
-            } else {
-                const int kq = tid >> 3, n8 = (tid & 7) * 8;
-                const bool in = k0 + kq < ke;
-                if (!(in && n0 + n8 + 8 <= sp.N && pr.ldb8(sp, k0 + kq, n0 + n8, v)))
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = (in && n0 + n8 + e < sp.N) ? pr.ldb(sp, k0 + kq, n0 + n8 + e) : 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) Bs[(n8 + e) * KP + kq] = bf16_bits(v[e]);
             }
+        } else {
+            float v[4][8];
+            const int kq = (tid >> 3) * 4, n8 = (tid & 7) * 8;
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                const bool in = k0 + kq + z < ke;
+                if (!(in && n0 + n8 + 8 <= sp.N && pr.ldb8(sp, k0 + kq + z, n0 + n8, v[z])))
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        v[z][e] = (in && n0 + n8 + e < sp.N) ? pr.ldb(sp, k0 + kq + z, n0 + n8 + e) : 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                *reinterpret_cast<u32x2_t*>(&Bs[(n8 + e) * KP + kq]) =
+                    u32x2_t{pack_bf16x2(v[0][e], v[1][e]), pack_bf16x2(v[2][e], v[3][e])};
         }
         __syncthreads();
 #pragma unroll
