@@ -1326,14 +1326,20 @@ __global__ void __launch_bounds__(256) bwd_router_wgrad_kernel(BwdArgs a, int nc
         __syncthreads();
         const int nt = (int)min<int64_t>(kRgTok, t1 - tb);
         if (i <= a.d)
-            for (int tt = 0; tt < nt; ++tt) {
-                const float xv = i < a.d ? ld<T>(a.x, (tb + tt) * a.d + i) : 1.f;
+            for (int t8 = 0; t8 < nt; t8 += 8) {
+                // eight tokens' x loads in flight together (tokens past the chunk count as 0)
+                float xv[8];
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&dls[tt][4 * e4]);
+                for (int u = 0; u < 8; ++u)
+                    xv[u] = t8 + u < nt ? (i < a.d ? ld<T>(a.x, (tb + t8 + u) * a.d + i) : 1.f) : 0.f;
 #pragma unroll
-                    for (int z = 0; z < 4; ++z) acc[4 * e4 + z] += xv * v[z];
-                }
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4) {
+                        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&dls[t8 + u][4 * e4]);
+#pragma unroll
+                        for (int z = 0; z < 4; ++z) acc[4 * e4 + z] += xv[u] * v[z];
+                    }
             }
     }
     if (i <= a.d)
@@ -1342,15 +1348,23 @@ __global__ void __launch_bounds__(256) bwd_router_wgrad_kernel(BwdArgs a, int nc
             if (e < ne) part[((int64_t)c * (a.d + 1) + i) * a.N + e0 + e] = acc[e];
 }
 
+// eight lanes per output element, each adding every eighth chunk in chunk order, then the eight
+// partial sums added in lane order (a fixed order: the result does not depend on the schedule)
 __global__ void bwd_router_wgrad_reduce(BwdArgs a, int nchunk, const float* __restrict__ part) {
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (i, e)
+    const int64_t q = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 3;  // (i, e)
+    const int sl = threadIdx.x & 7;
     const int64_t n = (int64_t)(a.d + 1) * a.N;
-    if (q >= n) return;
     float v = 0.f;
-    for (int c = 0; c < nchunk; ++c) v += part[(int64_t)c * n + q];
+    if (q < n)
+        for (int c = sl; c < nchunk; c += 8) v += part[(int64_t)c * n + q];
+    // lanes 8 j .. 8 j + 7: add lane 0's partial first, then lanes 1 .. 7, in that order
+    float tot = 0.f;
+#pragma unroll
+    for (int o = 0; o < 8; ++o) tot += __shfl(v, (threadIdx.x & ~7) + o);
+    if (q >= n || sl != 0) return;
     const int i = (int)(q / a.N), e = (int)(q % a.N);
-    if (i < a.d) a.dwr[(int64_t)i * a.N + e] = v;
-    else a.dbr[e] = v;
+    if (i < a.d) a.dwr[(int64_t)i * a.N + e] = tot;
+    else a.dbr[e] = tot;
 }
 
 template <class Prob, bool AK, bool BK>
@@ -1429,7 +1443,8 @@ weights:
         const int nchunk = (int)std::min<int64_t>(kRouterChunks, ceil_div(a.T, kRgTok));
         const dim3 gr((unsigned)ceil_div(a.d + 1, 256), (unsigned)ceil_div(a.N, 16), (unsigned)nchunk);
         bwd_router_wgrad_kernel<T><<<gr, 256, 0, st>>>(a, nchunk, a.part);
-        bwd_router_wgrad_reduce<<<(unsigned)ceil_div((int64_t)(a.d + 1) * a.N, 256), 256, 0, st>>>(a, nchunk, a.part);
+        bwd_router_wgrad_reduce<<<(unsigned)ceil_div((int64_t)(a.d + 1) * a.N * 8, 256), 256, 0, st>>>(a, nchunk,
+                                                                                                     a.part);
     }
     if (km) km->mark(KT_BWD_WGRAD);
     if (km) km->begin(KT_BWD_DX);
