@@ -65,9 +65,11 @@ struct BwdArgs {
     float* dl;              // [T][N]
     float* cf;              // [T][H]: output coefficient of each routed head (p for weighted_concat, else 1)
     float* wn;              // [T][H]: renormalised weight of each routed head (variant gqe)
-    float* dQ;              // [T][H][dh] (before the rotation)
-    float* dK;              // [T][G][dh] (before the rotation)
-    float* dV;              // [T][G][dh]
+    // query / key / value gradients, float32 for float32 layers and bf16 for bf16 layers (the
+    // matrix-core products that read them round to bf16 anyway)
+    void* dQ;               // [T][H][dh] (before the rotation)
+    void* dK;               // [T][G][dh] (before the rotation)
+    void* dV;               // [T][G][dh]
     float* part;            // split-K partial sums of the weight gradients
     uint16_t* vr;           // bf16 path: V row-major [B][G][S_pad][dh]
     uint16_t* dob;          // bf16 path: dO in bf16 [B][H][S_pad][dh]
@@ -107,6 +109,28 @@ __device__ __forceinline__ void ld8(const void* p, int64_t i, float (&v)[8]) {
     }
 }
 __device__ __forceinline__ void ld8f(const float* p, float (&v)[8]) { ld8<float>(p, 0, v); }
+// the storage type of dQ, dK, dV for layers of type T
+template <typename T>
+struct GradT {
+    typedef float type;
+};
+template <>
+struct GradT<bf16_t> {
+    typedef bf16_t type;
+};
+template <typename T>
+__device__ __forceinline__ float gread(const void* p, int64_t i) {
+    return ld<typename GradT<T>::type>(p, i);
+}
+template <typename T>
+__device__ __forceinline__ void gread8(const void* p, int64_t i, float (&v)[8]) {
+    ld8<typename GradT<T>::type>(p, i, v);
+}
+template <typename T>
+__device__ __forceinline__ void gwrite(void* p, int64_t i, float v) {
+    typedef typename GradT<T>::type G;
+    reinterpret_cast<G*>(p)[i] = from_f32<G>(v);
+}
 __device__ __forceinline__ float dot4(const f32x4_t& u, const f32x4_t& v) {
     return u[0] * v[0] + u[1] * v[1] + u[2] * v[2] + u[3] * v[3];
 }
@@ -310,7 +334,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < DQ; i += 2) rope_pair(dq[i], dq[i + 1], -s, a.rope[(d0 + i) >> 1]);
 #pragma unroll
-    for (int i = 0; i < DQ; ++i) a.dQ[(t * a.H + h) * dh + d0 + i] = dq[i];
+    for (int i = 0; i < DQ; ++i) gwrite<T>(a.dQ, (t * a.H + h) * dh + d0 + i, dq[i]);
     if (qd == 0) a.lse[t * a.H + h] = L;
 }
 
@@ -391,8 +415,8 @@ __global__ void __launch_bounds__(256) bwd_dkv_kernel(BwdArgs a) {
     const int64_t t = b * a.S + j;
 #pragma unroll
     for (int i = 0; i < DQ; ++i) {
-        a.dK[(t * a.G + g) * dh + d0 + i] = dk[i];
-        a.dV[(t * a.G + g) * dh + d0 + i] = dv[i];
+        gwrite<T>(a.dK, (t * a.G + g) * dh + d0 + i, dk[i]);
+        gwrite<T>(a.dV, (t * a.G + g) * dh + d0 + i, dv[i]);
     }
 }
 
@@ -576,8 +600,8 @@ __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint
                     kv = (l16 & 1) ? hi : lo;
                 }
                 if (kp < S) {
-                    a.dK[((b * S + kp) * a.G + g) * DH + col] = kv;
-                    a.dV[((b * S + kp) * a.G + g) * DH + col] = dv[u][c][i];
+                    gwrite<bf16_t>(a.dK, ((b * S + kp) * a.G + g) * DH + col, kv);
+                    gwrite<bf16_t>(a.dV, ((b * S + kp) * a.G + g) * DH + col, dv[u][c][i]);
                 }
             }
 }
@@ -737,7 +761,7 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
                 rope_pair(lo, hi, -qr, a.rope[col >> 1]);
                 v = (l16 & 1) ? hi : lo;
             }
-            if (qr < S) a.dQ[((b * S + qr) * a.H + h) * DH + col] = v;
+            if (qr < S) gwrite<bf16_t>(a.dQ, ((b * S + qr) * a.H + h) * DH + col, v);
         }
     if (j4 == 0 && qin) a.lse[(b * S + qpos) * a.H + h] = L;
 }
@@ -1121,27 +1145,36 @@ struct ProbWx {
         ld8<T>(a.x, tok(s, k) * a.d + i, v);
         return true;
     }
-    __device__ const float* grow(const Sub& s, int k) const {  // the gradient row of token list entry k
+    // the gradient row of token list entry k: buffer and element offset
+    __device__ const void* grow(const Sub& s, int k, int64_t& off) const {
         const int ebase = 2 * a.G + a.s;
         const int64_t t = tok(s, k);
-        if (s.hb < a.G) return a.dK + (t * a.G + s.hb) * a.dh;
-        if (s.hb < 2 * a.G) return a.dV + (t * a.G + s.hb - a.G) * a.dh;
-        if (s.hb < ebase) return a.dQ + (t * a.H + a.G * a.k) * a.dh;
+        if (s.hb < a.G) {
+            off = (t * a.G + s.hb) * a.dh;
+            return a.dK;
+        }
+        if (s.hb < 2 * a.G) {
+            off = (t * a.G + s.hb - a.G) * a.dh;
+            return a.dV;
+        }
+        if (s.hb < ebase) {
+            off = (t * a.H + a.G * a.k) * a.dh;
+            return a.dQ;
+        }
         const int h = s.g * a.k + (a.dense ? s.e % a.n : L.rank[s.base + k]);
-        return a.dQ + (t * a.H + h) * a.dh;
+        off = (t * a.H + h) * a.dh;
+        return a.dQ;
     }
     __device__ bool ldb8(const Sub& s, int k, int j, float (&v)[8]) const {
-        ld8f(grow(s, k) + j, v);
+        int64_t off;
+        const void* p = grow(s, k, off);
+        gread8<T>(p, off + j, v);
         return true;
     }
     __device__ float ldb(const Sub& s, int k, int j) const {
-        const int ebase = 2 * a.G + a.s;
-        const int64_t t = tok(s, k);
-        if (s.hb < a.G) return a.dK[(t * a.G + s.hb) * a.dh + j];
-        if (s.hb < 2 * a.G) return a.dV[(t * a.G + s.hb - a.G) * a.dh + j];
-        if (s.hb < ebase) return a.dQ[(t * a.H + a.G * a.k) * a.dh + j];
-        const int h = s.g * a.k + (a.dense ? s.e % a.n : L.rank[s.base + k]);
-        return a.dQ[(t * a.H + h) * a.dh + j];
+        int64_t off;
+        const void* p = grow(s, k, off);
+        return gread<T>(p, off + j);
     }
     __device__ void store(const Sub& s, int i, int j, float v) const {
         const int ebase = 2 * a.G + a.s;
@@ -1185,14 +1218,14 @@ struct ProbDxDense {
         if (!which && kk >= kd()) {
             const int e = (kk - kd()) / a.dh, j = (kk - kd()) % a.dh;
             const int h = routed_head(t, e);
-            return h < 0 ? 0.f : a.dQ[((int64_t)t * a.H + h) * a.dh + j];
+            return h < 0 ? 0.f : gread<T>(a.dQ, ((int64_t)t * a.H + h) * a.dh + j);
         }
         if (which) kk += kd();
         const int GD = a.G * a.dh;
-        if (kk < GD) return a.dK[(int64_t)t * GD + kk];
-        if (kk < 2 * GD) return a.dV[(int64_t)t * GD + kk - GD];
+        if (kk < GD) return gread<T>(a.dK, (int64_t)t * GD + kk);
+        if (kk < 2 * GD) return gread<T>(a.dV, (int64_t)t * GD + kk - GD);
         kk -= 2 * GD;
-        if (a.s && kk < a.dh) return a.dQ[((int64_t)t * a.H + a.G * a.k) * a.dh + kk];
+        if (a.s && kk < a.dh) return gread<T>(a.dQ, ((int64_t)t * a.H + a.G * a.k) * a.dh + kk);
         kk -= a.s * a.dh;
         return a.dl[(int64_t)t * a.N + kk];
     }
@@ -1221,13 +1254,13 @@ struct ProbDxDense {
 #pragma unroll
                 for (int z = 0; z < 8; ++z) v[z] = 0.f;
             } else {
-                ld8f(a.dQ + ((int64_t)t * a.H + h) * a.dh + j, v);
+                gread8<T>(a.dQ, ((int64_t)t * a.H + h) * a.dh + j, v);
             }
             return true;
         }
-        if (kk < GD) ld8f(a.dK + (int64_t)t * GD + kk, v);
-        else if (kk < 2 * GD) ld8f(a.dV + (int64_t)t * GD + kk - GD, v);
-        else ld8f(a.dQ + ((int64_t)t * a.H + a.G * a.k) * a.dh + kk - 2 * GD, v);
+        if (kk < GD) gread8<T>(a.dK, (int64_t)t * GD + kk, v);
+        else if (kk < 2 * GD) gread8<T>(a.dV, (int64_t)t * GD + kk - GD, v);
+        else gread8<T>(a.dQ, ((int64_t)t * a.H + a.G * a.k) * a.dh + kk - 2 * GD, v);
         return true;
     }
     __device__ bool ldb8(const Sub&, int kk, int i, float (&v)[8]) const {
@@ -1279,7 +1312,7 @@ struct ProbDxRouted {
     __device__ float lda(const Sub& s, int m, int j) const {
         const int64_t t = tok(s, m);
         if (!mine(s, m)) return 0.f;
-        return a.dQ[(t * a.H + g * a.k + r) * a.dh + j];
+        return gread<T>(a.dQ, (t * a.H + g * a.k + r) * a.dh + j);
     }
     __device__ float ldb(const Sub& s, int j, int i) const { return ld<T>(a.wq, ((int64_t)s.e * a.d + i) * a.dh + j); }
     __device__ bool lda8(const Sub& s, int m, int j, float (&v)[8]) const {
@@ -1287,7 +1320,7 @@ struct ProbDxRouted {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = 0.f;
         } else {
-            ld8f(a.dQ + (tok(s, m) * a.H + g * a.k + r) * a.dh + j, v);
+            gread8<T>(a.dQ, (tok(s, m) * a.H + g * a.k + r) * a.dh + j, v);
         }
         return true;
     }
@@ -1491,9 +1524,9 @@ hipError_t launch_backward(const GqeDims& D, const WorkPlan& P, const BwdPlan& B
     a.dl = (float*)(ws + BP.dl);
     a.cf = (float*)(ws + BP.cf);
     a.wn = (float*)(ws + BP.wn);
-    a.dQ = (float*)(ws + BP.dQ);
-    a.dK = (float*)(ws + BP.dK);
-    a.dV = (float*)(ws + BP.dV);
+    a.dQ = ws + BP.dQ;
+    a.dK = ws + BP.dK;
+    a.dV = ws + BP.dV;
     a.part = (float*)(ws + BP.part);
     a.vr = (uint16_t*)(ws + BP.vr);
     a.dob = (uint16_t*)(ws + BP.dob);
