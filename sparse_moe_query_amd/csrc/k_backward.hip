@@ -109,6 +109,10 @@ __device__ __forceinline__ void ld8(const void* p, int64_t i, float (&v)[8]) {
     }
 }
 __device__ __forceinline__ void ld8f(const float* p, float (&v)[8]) { ld8<float>(p, 0, v); }
+__device__ __forceinline__ uint16_t bf16_bits(float v) { return (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu); }
+__device__ __forceinline__ u32x4_t pack8(const float (&v)[8]) {
+    return u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+}
 // the storage type of dQ, dK, dV for layers of type T
 template <typename T>
 struct GradT {
@@ -442,18 +446,36 @@ __device__ __forceinline__ float swap_x1(float v) {  // the value of lane ^ 1
 }
 
 // row-major V and bf16 dO (rows past the sequence zero) for the matrix-core kernels
+// thread per eight head dims of one row: V rows gathered from V^T with neighbouring threads on
+// neighbouring keys (coalesced reads), dO rows converted with neighbouring threads on neighbouring
+// dims; one 16-byte store each
 __global__ void bwd_mprep_kernel(BwdArgs a, uint16_t* __restrict__ Vr, uint16_t* __restrict__ dOb) {
-    const int64_t nv = a.B * a.G * a.S_pad * a.dh, no = a.B * a.H * a.S_pad * a.dh;
+    const int c8n = a.dh / 8;
+    const int64_t nv = a.B * a.G * a.S_pad * c8n, no = a.B * a.H * a.S_pad * c8n;
     const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (q < nv) {
-        const int c = (int)(q % a.dh);
-        const int64_t r = q / a.dh, s = r % a.S_pad, bg = r / a.S_pad;
-        Vr[q] = s < a.S ? reinterpret_cast<const uint16_t*>(a.Vt)[(bg * a.dh + c) * a.S_pad + vt_pos(s)] : 0;
+        const int64_t s = q % a.S_pad, rem = q / a.S_pad;
+        const int c8 = (int)(rem % c8n);
+        const int64_t bg = rem / c8n;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (s < a.S) {
+            const uint16_t* src = reinterpret_cast<const uint16_t*>(a.Vt) + (bg * a.dh + 8 * c8) * a.S_pad + vt_pos(s);
+#pragma unroll
+            for (int e = 0; e < 8; e += 2)
+                v[e >> 1] = (uint32_t)src[(int64_t)e * a.S_pad] | ((uint32_t)src[(int64_t)(e + 1) * a.S_pad] << 16);
+        }
+        *reinterpret_cast<u32x4_t*>(Vr + (bg * a.S_pad + s) * a.dh + 8 * c8) = v;
     } else if (q < nv + no) {
         const int64_t i = q - nv;
-        const int c = (int)(i % a.dh);
-        const int64_t r = i / a.dh, s = r % a.S_pad, bh = r / a.S_pad, b = bh / a.H, h = bh % a.H;
-        dOb[i] = s < a.S ? (uint16_t)(pack_bf16x2(a.dO[((b * a.S + s) * a.H + h) * a.dh + c], 0.f) & 0xffffu) : 0;
+        const int c8 = (int)(i % c8n);
+        const int64_t r = i / c8n, s = r % a.S_pad, bh = r / a.S_pad, b = bh / a.H, h = bh % a.H;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (s < a.S) {
+            float f[8];
+            ld8f(a.dO + ((b * a.S + s) * a.H + h) * a.dh + 8 * c8, f);
+            v = pack8(f);
+        }
+        *reinterpret_cast<u32x4_t*>(dOb + (bh * a.S_pad + s) * a.dh + 8 * c8) = v;
     }
 }
 
@@ -835,10 +857,6 @@ __global__ void __launch_bounds__(256) tgemm_reduce_kernel(Prob pr, int splits, 
     pr.store(sp, (int)(e / sp.N), (int)(e % sp.N), v);
 }
 
-__device__ __forceinline__ uint16_t bf16_bits(float v) { return (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu); }
-__device__ __forceinline__ u32x4_t pack8(const float (&v)[8]) {
-    return u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-}
 
 // The same sub-problems on matrix cores (bf16 layers): operands rounded once to bf16 as they are
 // staged (k chunks of 32, rows k-contiguous in LDS for both A and B), 16x16x16 products into float32
@@ -1431,7 +1449,7 @@ hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km
     const dim3 gq(nblk, (unsigned)a.H, (unsigned)a.B), gk(nblk, (unsigned)a.G, (unsigned)a.B);
     if (sizeof(T) == 2) {
         // bf16: matrix cores
-        const int64_t n = a.B * (a.G + a.H) * a.S_pad * a.dh;
+        const int64_t n = a.B * (a.G + a.H) * a.S_pad * (a.dh / 8);
         bwd_mprep_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>(a, a.vr, a.dob);
         const dim3 gq1((unsigned)(nblk * a.H * a.B)), gk1((unsigned)(ceil_div(a.S, 128) * a.G * a.B));
 #define GQE_BWD_MFMA(DHV)                                                     \
