@@ -593,8 +593,8 @@ static BwdPlan make_bwd_plan(const GqeDims& D, int64_t B, int64_t S) {
         // (input side, 2G + s + N + 1 sub-problems) or d_h x d (output side, N + G + 1)
         const size_t in_side = (size_t)(2 * D.G + D.s + D.N) * D.d * D.dh;
         const size_t out_side = (size_t)(D.N + D.G + D.s) * D.dh * D.d;
-        const size_t router_side = (size_t)kRouterChunks * (D.d + 1) * D.N / 8 + 1;
-        P.part = take(8 * std::max(std::max(in_side, out_side), router_side) * 4);
+        const size_t router_side = (size_t)kRouterChunks * (D.d + 1) * D.N;
+        P.part = take(std::max((size_t)kWgradSplits * std::max(in_side, out_side), router_side) * 4);
     }
     const size_t S_pad = (size_t)round_up(S, GQE_KV_TILE);
     P.vr = take((size_t)B * D.G * S_pad * D.dh * 2);

@@ -13,6 +13,8 @@
 #define GQE_ATTN_MAX_CHUNKS 32   // key-range chunks an attention item may be split into
 // token chunks of the backward's router weight gradient (its partial sums share the split-K buffer)
 constexpr int kRouterChunks = 128;
+// split-K pieces of the backward's weight gradients (sums over the tokens)
+constexpr int kWgradSplits = 16;
 #define GQE_DEC_MAX_HEADS 8      // decode: active query heads of one KV group
 #define GQE_DEC_MAX_SLOTS 192    // decode: output-projection slots of one token
 #define GQE_DEC_MAX_SLOT_DIMS 8192  // decode: slots x d_h of one token

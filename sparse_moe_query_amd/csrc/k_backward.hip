@@ -40,7 +40,6 @@
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kWgradSplits = 8;  // split-K pieces of the weight gradients (sums over the tokens)
 
 struct BwdArgs {
     const void* x;          // [T][d]
