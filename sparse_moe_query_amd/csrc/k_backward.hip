@@ -108,6 +108,11 @@ __device__ __forceinline__ void ld8(const void* p, int64_t i, float (&v)[8]) {
     }
 }
 __device__ __forceinline__ void ld8f(const float* p, float (&v)[8]) { ld8<float>(p, 0, v); }
+// element e of lo and of hi (eight bf16 each) as one bf16 pair
+__device__ __forceinline__ uint32_t bf16_pair(const u32x4_t& lo, const u32x4_t& hi, int e) {
+    const uint32_t a = (lo[e >> 1] >> (16 * (e & 1))) & 0xffffu, b = (hi[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+    return a | (b << 16);
+}
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu); }
 __device__ __forceinline__ u32x4_t pack8(const float (&v)[8]) {
     return u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
@@ -516,18 +521,20 @@ __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint
     const int nh = a.k + ((a.s && a.skv == g) ? 1 : 0);
     const int qt0 = 2 * kb, ntl = nqt - qt0, total = nh * ntl;
     auto head = [&](int hi) { return hi < a.k ? g * a.k + hi : a.G * a.k; };
-    constexpr int NCH = 64 * (DH / 8), R = (NCH + 255) / 256;
+    // staging: thread = (four neighbouring rows, one 8-dim chunk); R = the four rows
+    constexpr int NQC = 16 * (DH / 8), R = 4;
+    static_assert(NQC <= 256, "d_h <= 128");
+    const int rq = (tid / (DH / 8)) * 4, cq = tid % (DH / 8);
     u32x4_t pq[R], pd[R];
     float pl = 0.f, pdd = 0.f;
     auto fetch = [&](int it) {
         const int h = head(it / ntl), qt = qt0 + it % ntl;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int i = tid + 256 * r;
-            const int q = i / (DH / 8), c8 = i % (DH / 8);
+            const int q = rq + r, c8 = cq;
             const int64_t qp = (int64_t)qt * 64 + q;
             pq[r] = pd[r] = u32x4_t{0u, 0u, 0u, 0u};
-            if (i < NCH && qp < S) {
+            if (tid < NQC && qp < S) {
                 pq[r] = *reinterpret_cast<const u32x4_t*>(Qg + (((int64_t)b * a.H + h) * S + qp) * DH + 8 * c8);
                 pd[r] = *reinterpret_cast<const u32x4_t*>(dOb + (((int64_t)b * a.H + h) * a.S_pad + qp) * DH + 8 * c8);
             }
@@ -543,17 +550,19 @@ __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint
     for (int it = 0; it < total; ++it) {
         const int qt = qt0 + it % ntl;
         __syncthreads();  // the previous pair's products are done with the tiles
+        if (tid < NQC) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int i = tid + 256 * r;
-            if (i >= NCH) continue;
-            const int q = i / (DH / 8), c8 = i % (DH / 8);
-            *reinterpret_cast<u32x4_t*>(&Qs[q * P1 + 8 * c8]) = pq[r];
-            *reinterpret_cast<u32x4_t*>(&dOs[q * P1 + 8 * c8]) = pd[r];
+            for (int r = 0; r < R; ++r) {
+                *reinterpret_cast<u32x4_t*>(&Qs[(rq + r) * P1 + 8 * cq]) = pq[r];
+                *reinterpret_cast<u32x4_t*>(&dOs[(rq + r) * P1 + 8 * cq]) = pd[r];
+            }
+            // transposed: dim 8 cq + e, rows rq .. rq + 3 in one 8-byte store
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                QsT[(8 * c8 + e) * P2 + q] = (uint16_t)(pq[r][e >> 1] >> (16 * (e & 1)));
-                dOsT[(8 * c8 + e) * P2 + q] = (uint16_t)(pd[r][e >> 1] >> (16 * (e & 1)));
+                *reinterpret_cast<u32x2_t*>(&QsT[(8 * cq + e) * P2 + rq]) =
+                    u32x2_t{bf16_pair(pq[0], pq[1], e), bf16_pair(pq[2], pq[3], e)};
+                *reinterpret_cast<u32x2_t*>(&dOsT[(8 * cq + e) * P2 + rq]) =
+                    u32x2_t{bf16_pair(pd[0], pd[1], e), bf16_pair(pd[2], pd[3], e)};
             }
         }
         if (tid < 64) {
@@ -659,18 +668,20 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
     // (m, l); then the four lanes of a query column are combined into the row log-sum-exp L.
     // pass 2 (ntile .. 2 ntile - 1): dS^T = P^T (dP^T - D), dq += dS K.  The next iteration's key
     // (and value) tile is loaded into registers while the current one multiplies.
-    constexpr int NCH = 64 * (DH / 8), R = (NCH + 255) / 256;
+    // staging: thread = (four neighbouring rows, one 8-dim chunk); R = the four rows
+    constexpr int NQC = 16 * (DH / 8), R = 4;
+    static_assert(NQC <= 256, "d_h <= 128");
+    const int rq = (tid / (DH / 8)) * 4, cq = tid % (DH / 8);
     u32x4_t pk[R], pv[R];
     auto fetch = [&](int it) {
         const int kt = it % ntile;
         const bool full = it >= ntile;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int i = tid + 256 * r;
-            const int kk = i / (DH / 8), c8 = i % (DH / 8);
+            const int kk = rq + r, c8 = cq;
             const int64_t kp = (int64_t)kt * 64 + kk;
             pk[r] = pv[r] = u32x4_t{0u, 0u, 0u, 0u};
-            if (i < NCH && kp < S) {
+            if (tid < NQC && kp < S) {
                 pk[r] = *reinterpret_cast<const u32x4_t*>(Kb + kp * DH + 8 * c8);
                 if (full) pv[r] = *reinterpret_cast<const u32x4_t*>(Vb + kp * DH + 8 * c8);
             }
@@ -685,17 +696,17 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
         const int kt = it % ntile;
         const bool full = it >= ntile;
         __syncthreads();  // the previous tile's products are done
+        if (tid < NQC) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int i = tid + 256 * r;
-            if (i >= NCH) continue;
-            const int kk = i / (DH / 8), c8 = i % (DH / 8);
-            *reinterpret_cast<u32x4_t*>(&Ks[kk * P1 + 8 * c8]) = pk[r];
-            if (full) {
-                *reinterpret_cast<u32x4_t*>(&Vs[kk * P1 + 8 * c8]) = pv[r];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) KsT[(8 * c8 + e) * P2 + kk] = (uint16_t)(pk[r][e >> 1] >> (16 * (e & 1)));
+            for (int r = 0; r < R; ++r) {
+                *reinterpret_cast<u32x4_t*>(&Ks[(rq + r) * P1 + 8 * cq]) = pk[r];
+                if (full) *reinterpret_cast<u32x4_t*>(&Vs[(rq + r) * P1 + 8 * cq]) = pv[r];
             }
+            if (full)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    *reinterpret_cast<u32x2_t*>(&KsT[(8 * cq + e) * P2 + rq]) =
+                        u32x2_t{bf16_pair(pk[0], pk[1], e), bf16_pair(pk[2], pk[3], e)};
         }
         __syncthreads();
         if (it + 1 < 2 * ntile) fetch(it + 1);
