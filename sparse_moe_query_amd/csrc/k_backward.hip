@@ -877,7 +877,7 @@ __global__ void __launch_bounds__(256) tgemm_mfma_kernel(Prob pr, int splits, fl
     // for operands contiguous along m and n (four k of eight m per thread).  LDS row pitch 40 / 136
     // bf16 (80 / 272 bytes): the 8-byte fragment reads of 16 rows x 2 k-quads hit 64 distinct banks.
     static_assert(AK == BK, "both operands contiguous along k, or neither");
-    constexpr int KC = AK ? 32 : 128, KP = AK ? 40 : 136, NQ = KC / 32;
+    constexpr int KC = AK ? 32 : 64, KP = AK ? 40 : 72, NQ = KC / 32;
     __shared__ __align__(16) uint16_t As[64 * KP];  // [m][k]
     __shared__ __align__(16) uint16_t Bs[64 * KP];  // [n][k]
     typename Prob::Sub sp;
@@ -912,10 +912,10 @@ __global__ void __launch_bounds__(256) tgemm_mfma_kernel(Prob pr, int splits, fl
                 *reinterpret_cast<u32x4_t*>(&As[m * KP + ka]) = pack8(v);
             }
         } else {
-            float v[4][8];
-            const int kq = (tid >> 3) * 4, m8 = (tid & 7) * 8;
+            float v[2][8];
+            const int kq = (tid >> 3) * 2, m8 = (tid & 7) * 8;
 #pragma unroll
-            for (int z = 0; z < 4; ++z) {
+            for (int z = 0; z < 2; ++z) {
                 const bool in = k0 + kq + z < ke;
                 if (!(in && m0 + m8 + 8 <= sp.M && pr.lda8(sp, m0 + m8, k0 + kq + z, v[z])))
 #pragma unroll
@@ -924,8 +924,7 @@ __global__ void __launch_bounds__(256) tgemm_mfma_kernel(Prob pr, int splits, fl
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<u32x2_t*>(&As[(m8 + e) * KP + kq]) =
-                    u32x2_t{pack_bf16x2(v[0][e], v[1][e]), pack_bf16x2(v[2][e], v[3][e])};
+                *reinterpret_cast<uint32_t*>(&As[(m8 + e) * KP + kq]) = pack_bf16x2(v[0][e], v[1][e]);
         }
         if (BK) {
 #pragma unroll
@@ -939,10 +938,10 @@ __global__ void __launch_bounds__(256) tgemm_mfma_kernel(Prob pr, int splits, fl
                 *reinterpret_cast<u32x4_t*>(&Bs[n * KP + kq]) = pack8(v);
             }
         } else {
-            float v[4][8];
-            const int kq = (tid >> 3) * 4, n8 = (tid & 7) * 8;
+            float v[2][8];
+            const int kq = (tid >> 3) * 2, n8 = (tid & 7) * 8;
 #pragma unroll
-            for (int z = 0; z < 4; ++z) {
+            for (int z = 0; z < 2; ++z) {
                 const bool in = k0 + kq + z < ke;
                 if (!(in && n0 + n8 + 8 <= sp.N && pr.ldb8(sp, k0 + kq + z, n0 + n8, v[z])))
 #pragma unroll
@@ -951,8 +950,7 @@ __global__ void __launch_bounds__(256) tgemm_mfma_kernel(Prob pr, int splits, fl
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<u32x2_t*>(&Bs[(n8 + e) * KP + kq]) =
-                    u32x2_t{pack_bf16x2(v[0][e], v[1][e]), pack_bf16x2(v[2][e], v[3][e])};
+                *reinterpret_cast<uint32_t*>(&Bs[(n8 + e) * KP + kq]) = pack_bf16x2(v[0][e], v[1][e]);
         }
         __syncthreads();
 #pragma unroll
