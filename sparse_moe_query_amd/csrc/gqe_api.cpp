@@ -584,6 +584,7 @@ static BwdPlan make_bwd_plan(const GqeDims& D, int64_t B, int64_t S) {
     P.dQ = take(T * D.H * D.dh * 4);
     P.dK = take(T * D.G * D.dh * 4);
     P.dV = take(T * D.G * D.dh * 4);
+    P.kvp = take(4 * T * D.dh * 4);
     P.offs = take((size_t)(D.N + 1) * 4);
     P.perm = take(T * D.G * D.k * 4);
     P.inv = take(T * D.G * D.k * 4);

@@ -72,6 +72,7 @@ struct DecodePlan {
 struct BwdPlan {
     int NS;                           // output-projection slots of one token
     size_t U, dO, Dd, lse, dl, cf, wn, dQ, dK, dV;
+    size_t kvp;                       // bf16 attention: float32 dK / dV partials of the shared head's group
     size_t offs, perm, inv, rank;     // token lists of the routed experts (bucketing) and choice ranks
     size_t part;                      // split-K partial sums of the weight gradients
     size_t vr, dob;                   // bf16 attention: row-major V and bf16 dO

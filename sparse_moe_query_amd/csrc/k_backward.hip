@@ -72,6 +72,8 @@ struct BwdArgs {
     float* part;            // split-K partial sums of the weight gradients
     uint16_t* vr;           // bf16 path: V row-major [B][G][S_pad][dh]
     uint16_t* dob;          // bf16 path: dO in bf16 [B][H][S_pad][dh]
+    float* kvp;             // bf16 path: [4][T][dh] float32 dK / dV of the shared head's group, split
+                            // into its routed heads' part and the shared head's part
     // outputs (float32)
     float *dx, *dwr, *dbr, *dwq, *dwqs, *dwk, *dwv, *dwo, *dwor, *dwos;
     double aux_coef;
@@ -493,7 +495,14 @@ __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint
     __shared__ __align__(16) uint16_t Qs[64 * P1], dOs[64 * P1], QsT[DH * P2], dOsT[DH * P2];
     __shared__ float lss[64], dds[64];
     // longest first: key block 0 (every query tile after it) of every (group, sequence) leads
-    const int kb = (int)(blockIdx.x / (a.G * a.B)), g = (int)(blockIdx.x % a.G), b = (int)(blockIdx.x / a.G % a.B);
+    // one work group per (key block, group, sequence), and one more per (key block, sequence) for
+    // the shared head: the shared head's group would otherwise carry twice the work of the others
+    // on the longest (first) key blocks; the two parts of that group go to float32 partials
+    const int GS = a.G + a.s;
+    const int kb = (int)(blockIdx.x / (GS * a.B)), gi = (int)(blockIdx.x % GS), b = (int)(blockIdx.x / GS % a.B);
+    const bool shared_part = gi == a.G;
+    const int g = shared_part ? a.skv : gi;
+    const bool split = a.s && g == a.skv;
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, j4 = lane >> 4;
     const int64_t S = a.S;
@@ -518,9 +527,9 @@ __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint
     const uint16_t* Qg = reinterpret_cast<const uint16_t*>(a.Q);
     // (head of the group, query tile) pairs in order; the next pair's Q, dO, log-sum-exp and D are
     // loaded into registers while the current pair multiplies
-    const int nh = a.k + ((a.s && a.skv == g) ? 1 : 0);
+    const int nh = shared_part ? 1 : a.k;
     const int qt0 = 2 * kb, ntl = nqt - qt0, total = nh * ntl;
-    auto head = [&](int hi) { return hi < a.k ? g * a.k + hi : a.G * a.k; };
+    auto head = [&](int hi) { return shared_part ? a.G * a.k : g * a.k + hi; };
     // staging: thread = (four neighbouring rows, one 8-dim chunk); R = the four rows
     constexpr int NQC = 16 * (DH / 8), R = 4;
     static_assert(NQC <= 256, "d_h <= 128");
@@ -630,10 +639,28 @@ __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint
                     kv = (l16 & 1) ? hi : lo;
                 }
                 if (kp < S) {
-                    gwrite<bf16_t>(a.dK, ((b * S + kp) * a.G + g) * DH + col, kv);
-                    gwrite<bf16_t>(a.dV, ((b * S + kp) * a.G + g) * DH + col, dv[u][c][i]);
+                    if (split) {
+                        const int64_t T = a.T, o = (b * S + kp) * DH + col;
+                        a.kvp[(shared_part ? 1 : 0) * T * DH + o] = kv;
+                        a.kvp[(shared_part ? 3 : 2) * T * DH + o] = dv[u][c][i];
+                    } else {
+                        gwrite<bf16_t>(a.dK, ((b * S + kp) * a.G + g) * DH + col, kv);
+                        gwrite<bf16_t>(a.dV, ((b * S + kp) * a.G + g) * DH + col, dv[u][c][i]);
+                    }
                 }
             }
+}
+
+// the shared head's group: dK = routed part + shared part, dV likewise, rounded once to bf16
+__global__ void bwd_kv_sum_kernel(BwdArgs a) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t n = a.T * a.dh;
+    if (q >= n) return;
+    const int64_t t = q / a.dh;
+    const int c = (int)(q % a.dh);
+    const int64_t o = (t * a.G + a.skv) * a.dh + c;
+    gwrite<bf16_t>(a.dK, o, a.kvp[q] + a.kvp[n + q]);
+    gwrite<bf16_t>(a.dV, o, a.kvp[2 * n + q] + a.kvp[3 * n + q]);
 }
 
 // dq of 64 queries (wave w: queries 16 w ..) of one (sequence, head): pass 1 the row log-sum-exp,
@@ -1459,7 +1486,7 @@ hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km
         // bf16: matrix cores
         const int64_t n = a.B * (a.G + a.H) * a.S_pad * (a.dh / 8);
         bwd_mprep_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>(a, a.vr, a.dob);
-        const dim3 gq1((unsigned)(nblk * a.H * a.B)), gk1((unsigned)(ceil_div(a.S, 128) * a.G * a.B));
+        const dim3 gq1((unsigned)(nblk * a.H * a.B)), gk1((unsigned)(ceil_div(a.S, 128) * (a.G + a.s) * a.B));
 #define GQE_BWD_MFMA(DHV)                                                     \
     bwd_dq_mfma_kernel<DHV><<<gq1, 256, 0, st>>>(a, a.vr, a.dob);             \
     bwd_dkv_mfma_kernel<DHV><<<gk1, 256, 0, st>>>(a, a.vr, a.dob);
@@ -1474,6 +1501,7 @@ hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km
             default: GQE_BWD_MFMA(128) break;
         }
 #undef GQE_BWD_MFMA
+        if (a.s) bwd_kv_sum_kernel<<<(unsigned)ceil_div(a.T * a.dh, 256), 256, 0, st>>>(a);
         if (km) km->mark(KT_BWD_ATTN);
         goto weights;
     }
@@ -1556,6 +1584,7 @@ hipError_t launch_backward(const GqeDims& D, const WorkPlan& P, const BwdPlan& B
     a.part = (float*)(ws + BP.part);
     a.vr = (uint16_t*)(ws + BP.vr);
     a.dob = (uint16_t*)(ws + BP.dob);
+    a.kvp = (float*)(ws + BP.kvp);
     a.dx = gr.dx;
     a.dwr = gr.d_router;
     a.dbr = gr.d_router_bias;
