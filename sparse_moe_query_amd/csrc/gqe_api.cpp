@@ -590,7 +590,7 @@ static BwdPlan make_bwd_plan(const GqeDims& D, int64_t B, int64_t S) {
     P.inv = take(T * D.G * D.k * 4);
     P.rank = take(T * D.G * D.k * 4);
     {
-        // split-K partials: 8 pieces of every weight-gradient sub-problem, each at most (d + 1) x max(d_h, N)
+        // split-K partials: kWgradSplits pieces of every weight-gradient sub-problem, each at most (d + 1) x max(d_h, N)
         // (input side, 2G + s + N + 1 sub-problems) or d_h x d (output side, N + G + 1)
         const size_t in_side = (size_t)(2 * D.G + D.s + D.N) * D.d * D.dh;
         const size_t out_side = (size_t)(D.N + D.G + D.s) * D.dh * D.d;

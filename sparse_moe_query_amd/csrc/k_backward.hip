@@ -896,13 +896,14 @@ __global__ void __launch_bounds__(256) tgemm_reduce_kernel(Prob pr, int splits, 
 
 
 // The same sub-problems on matrix cores (bf16 layers): operands rounded once to bf16 as they are
-// staged (k chunks of 32, rows k-contiguous in LDS for both A and B), 16x16x16 products into float32
-// accumulators, wave w owning the 32 x 32 quarter (w / 2, w % 2) of the 64 x 64 tile.
+// staged (rows k-contiguous in LDS for both A and B), 16x16x16 products into float32 accumulators,
+// wave w owning the 32 x 32 quarter (w / 2, w % 2) of the 64 x 64 tile.
 template <class Prob, bool AK, bool BK>
 __global__ void __launch_bounds__(256) tgemm_mfma_kernel(Prob pr, int splits, float* part, int64_t pstride) {
-    // k chunk: 32 for operands contiguous along k (one 16-byte vector per thread and operand), 128
-    // for operands contiguous along m and n (four k of eight m per thread).  LDS row pitch 40 / 136
-    // bf16 (80 / 272 bytes): the 8-byte fragment reads of 16 rows x 2 k-quads hit 64 distinct banks.
+    // k chunk: 32 for operands contiguous along k (one 16-byte vector per thread and operand), 64
+    // for operands contiguous along m and n (two tokens of eight rows per thread).  LDS row pitch
+    // 40 / 72 bf16 (80 / 144 bytes): the 8-byte fragment reads of 16 rows x 2 k-quads hit distinct
+    // banks.
     static_assert(AK == BK, "both operands contiguous along k, or neither");
     constexpr int KC = AK ? 32 : 64, KP = AK ? 40 : 72, NQ = KC / 32;
     __shared__ __align__(16) uint16_t As[64 * KP];  // [m][k]

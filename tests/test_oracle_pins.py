@@ -343,6 +343,78 @@ def test_identical_experts_equal_single_expert(variant):
     np.testing.assert_allclose(out2["y"], out["y"], rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("k", [2, 3])
+def test_identical_experts_renormalised_slot_at_k_above_one(k):
+    """Tutorial 'Mixture of experts' (identical experts make the mixture one expert) at k >= 2,
+    variant gqe, n = 4 > k: every chosen expert of a group then gives the same head output o, so
+    the hard-concat part is k o W_o[g] and the renormalised slot is (sum_r w_r) o W_oR[g] = o W_oR[g]
+    -- the layer must equal the k = 1 layer whose expert projection is k W_o[g], whatever the
+    routing.  A slot weighted by the raw probabilities (their sum is below 1 when k < n), by 1 per
+    choice, or by any weights not summing to one fails this."""
+    wl = _wl(d=32, N=8, G=2, k=k, dh=8, B=2, S=9, variant="gqe", rstd=0.1, seed=3)
+    w = make_inputs(wl)
+    for g in range(2):
+        w["w_q"][g * 4:(g + 1) * 4] = w["w_q"][g * 4]
+        w["w_o"][g * 4:(g + 1) * 4] = w["w_o"][g * 4]
+    out, _ = _fwd(wl, w)
+    p_sel = np.take_along_axis(out["p"].reshape(wl.tokens, 2, 4), out["idx"] % 4, axis=2).sum(axis=2)
+    assert np.mean(p_sel) < 0.95  # raw probabilities of the chosen experts do not sum to one
+    w1 = dict(w)
+    w1["w_o"] = float(k) * w["w_o"].astype(np.float64)  # exact: no float32 rounding of 3 W_o
+    one, _ = _fwd(wl.with_(top_k=1), w1)
+    np.testing.assert_allclose(out["y"], one["y"], rtol=1e-11, atol=1e-13)
+    w2 = dict(w)
+    w2["w_router"] = np.random.default_rng(17).standard_normal(w["w_router"].shape).astype(np.float32)
+    out2, _ = _fwd(wl, w2)
+    assert np.any(out2["idx"] != out["idx"])
+    np.testing.assert_allclose(out2["y"], out["y"], rtol=1e-11, atol=1e-13)
+
+
+def test_weighted_concat_pairs_each_probability_with_its_expert():
+    """README 'Ablations' (weighted_concat: each selected expert's slot scaled by its router
+    probability) at k = 2 of n = 4, one position per sequence: every head output is then v_0 of
+    its group, so with W_o[e] = c_e M (distinct scalars c_e) the output is
+    (sum_r p[e_r] c_{e_r}) v_0 M -- the scalar, recovered from y, checks that each probability is
+    paired with its own expert's projection.  The router's p and idx are pinned on their own."""
+    wl = _wl(d=32, N=4, G=1, k=2, dh=8, B=7, S=1, variant="weighted_concat", shared=False,
+             rstd=0.1, seed=5)
+    w = make_inputs(wl)
+    c = np.array([1.0, 8.0, 64.0, 512.0], np.float32)  # powers of two: c_e M is exact
+    w["w_o"] = c[:, None, None] * w["w_o"][0][None]
+    out, _ = _fwd(wl, w)
+    base, _ = _fwd(wl.with_(variant="hard_concat", top_k=1, num_query_experts=1),
+                   dict(w, w_q=w["w_q"][:1], w_o=w["w_o"][:1], w_router=w["w_router"][:, :1],
+                        b_router=w["b_router"][:1]))  # one expert, coefficient 1: v_0 M
+    T = wl.tokens
+    scal = np.einsum("td,td->t", out["y"], base["y"]) / np.einsum("td,td->t", base["y"], base["y"])
+    want = (out["p"][np.arange(T)[:, None], out["idx"][:, 0, :]] * c[out["idx"][:, 0, :]]).sum(axis=1)
+    np.testing.assert_allclose(scal, want, rtol=1e-10)
+
+
+@pytest.mark.parametrize("k,n,G", [(2, 4, 1), (3, 4, 2), (2, 3, 2)])
+def test_gqe_slot_is_weighted_mix_divided_by_selected_mass(k, n, G):
+    """Explainer 'Output Construction' (renormalised weighted-sum slot) against README
+    'Ablations' (weighted_concat): with W_o[e] = W_oR[g] for every expert of group g and no shared
+    head, weighted_concat gives sum_g sum_r p_r o_r W_oR[g]; the gqe slot alone (W_o = 0) gives
+    sum_g sum_r (p_r / sum_sel p) o_r W_oR[g].  With one group the two differ exactly by the factor
+    sum_sel p per token; with several groups, zeroing every W_oR but one isolates each group."""
+    N = n * G
+    wl = _wl(d=32, N=N, G=G, k=k, dh=8, B=2, S=11, variant="gqe", shared=False, rstd=0.1, seed=7)
+    w = make_inputs(wl)
+    for gsel in range(G):
+        wg = dict(w)
+        wg["w_o_rslot"] = w["w_o_rslot"].copy()
+        wg["w_o_rslot"][np.arange(G) != gsel] = 0
+        wg["w_o"] = np.repeat(wg["w_o_rslot"], n, axis=0)
+        yw, _ = _fwd(wl.with_(variant="weighted_concat"), wg)
+        wz = dict(wg, w_o=np.zeros_like(wg["w_o"]))
+        ys, _ = _fwd(wl, wz)
+        T = wl.tokens
+        p_sel = yw["p"][np.arange(T)[:, None], yw["idx"][:, gsel, :]].sum(axis=1)
+        assert np.mean(p_sel) < 0.95
+        np.testing.assert_allclose(ys["y"] * p_sel[:, None], yw["y"], rtol=1e-10, atol=1e-14)
+
+
 def test_weighted_concat_scales_slot_by_router_probability():
     """README 'Ablations': weighted_concat has no renormalised slot; each selected expert's
     slot is weighted by its router probability.  With one group's projection kept and the
