@@ -10,6 +10,8 @@ and trained weights are not available, so seeded Gaussians of the same shapes st
   every time, so the three output variants of one seed share identical weights;
 * x ~ N(0, 1); projection weights ~ N(0, 0.02^2); router weights ~ N(0, router_std^2);
 * an optional +bias on local expert 0 of each group;
+* optional stress settings for peaked attention: a larger std of the query and key projections
+  (``qk_std``) and a ramp that scales x up along the sequence (``x_ramp``);
 * then round-to-nearest-even to bf16 for bf16 workloads (the router stays fp32).
 """
 from __future__ import annotations
@@ -51,6 +53,8 @@ class Workload:
     router_bias_first: float = 0.0    # added to local expert 0 of every group
     dense_gqa: bool = False           # all-active GQA baseline on the same weights
     rope_base: float = 0.0            # rotary position embedding base (0: none, as on the pages)
+    qk_std: float = 0.02              # std of the query and key projections (W_q, W_qs, W_k)
+    x_ramp: float = 0.0               # x[b, s] scaled by 1 + x_ramp * s / (S - 1): growing norms
 
     @property
     def dh(self) -> int:
@@ -104,14 +108,17 @@ def make_inputs(wl: Workload) -> dict:
     out = {
         "x": draw((wl.batch, wl.seq, d), 1.0),
         "w_router": draw((d, N), rstd),
-        "w_q": draw((N, d, dh), 0.02),
-        "w_q_shared": draw((d, dh), 0.02),
-        "w_k": draw((d, G * dh), 0.02),
+        "w_q": draw((N, d, dh), wl.qk_std),
+        "w_q_shared": draw((d, dh), wl.qk_std),
+        "w_k": draw((d, G * dh), wl.qk_std),
         "w_v": draw((d, G * dh), 0.02),
         "w_o": draw((N, dh, d), 0.02),
         "w_o_rslot": draw((G, dh, d), 0.02),
         "w_o_shared": draw((dh, d), 0.02),
     }
+    if wl.x_ramp:
+        ramp = 1.0 + wl.x_ramp * np.arange(wl.seq, dtype=np.float32) / np.float32(max(wl.seq - 1, 1))
+        out["x"] = out["x"] * ramp.astype(np.float32)[None, :, None]
     b = np.zeros(N, np.float32)
     if wl.router_bias_first:
         b[:: N // G] = np.float32(wl.router_bias_first)

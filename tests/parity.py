@@ -18,6 +18,9 @@ Bars (from the measurement plan):
 """
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 
 from oracle import gqe_oracle as go
@@ -25,6 +28,21 @@ from oracle import gqe_oracle as go
 NEAR_TIE = 1e-6
 Y_TOL = {"f32": 1e-4, "bf16": 2e-2}
 Y_STORAGE_U = {"f32": 0.0, "bf16": 2.0 ** -8}   # storage rounding of one output element
+
+
+# Every GPU comparison appends its error figures here (one JSON object per line), so the raw and
+# global figures behind each pass are on record next to the bar that was applied.
+RECORD = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out",
+                      "parity_errors.jsonl")
+
+
+def record(entry: dict) -> None:
+    try:
+        os.makedirs(os.path.dirname(RECORD), exist_ok=True)
+        with open(RECORD, "a") as f:
+            f.write(json.dumps(entry) + "\n")
+    except OSError:
+        pass
 
 
 def oracle_cfg(wl) -> go.OracleConfig:
@@ -133,6 +151,10 @@ def compare(wl, gpu: dict, inputs: dict, rows=None, want_qo=False) -> dict:
                y_err_global=rel_err(gpu["y"][rows], y_ref), rows=int(len(rows)), K=K, V=V)
     if want_qo:
         rep["q_ref"], rep["o_ref"] = res[1], res[2]
+    record(dict(kind="forward", workload=wl.name, B=B, S=S, d=wl.dim, N=N, G=G, k=k, dh=wl.dh,
+                variant=wl.variant, dtype=wl.dtype, rows=int(len(rows)), near_ties=rep["near_ties"],
+                y_err=rep["y_err"], y_err_raw=rep["y_err_raw"], y_err_global=rep["y_err_global"],
+                bar=Y_TOL[wl.dtype]))
     assert np.all(np.isfinite(gpu["y"][rows])), "non-finite GPU output"
     assert err <= Y_TOL[wl.dtype], f"{wl.name}: y max-abs error {err:.3e} x token RMS > {Y_TOL[wl.dtype]}"
     return rep
@@ -155,5 +177,8 @@ def compare_decode(wl, y, idx, w, inputs: dict, pos) -> dict:
     assert np.all(np.isfinite(y)), "non-finite GPU output"
     err = rel_err_rows(y, ref["y"], Y_STORAGE_U[wl.dtype])
     rep.update(y_err=err, y_err_raw=rel_err_rows(y, ref["y"]))
+    record(dict(kind="decode", workload=wl.name, B=len(pos), dh=wl.dh, k=wl.top_k, dtype=wl.dtype,
+                near_ties=rep["near_ties"], y_err=rep["y_err"], y_err_raw=rep["y_err_raw"],
+                bar=Y_TOL[wl.dtype]))
     assert err <= Y_TOL[wl.dtype], f"{wl.name} decode: y max-abs error {err:.3e} x token RMS > {Y_TOL[wl.dtype]}"
     return rep

@@ -66,6 +66,7 @@ def _check(wl, aux_coef=0.01, seed=11):
             bad.append(k)
     print(f"[gpu]   gradient errors (max |diff| / max |grad|): " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()),
           flush=True)
+    parity.record(dict(kind="backward", workload=wl.name, B=wl.batch, S=wl.seq, dtype=wl.dtype, errors=errs))
     assert not bad, f"{wl.name}: {bad} beyond {G_TOL[wl.dtype]}"
     return errs
 
@@ -85,6 +86,9 @@ CASES = [
     _wl("bwd_dh16_k2", d=128, k=2, dh=16, B=2, S=130, seed=15),
     # n = 8 > 4 k: the routed dx pieces run as their own per-(group, rank) products
     _wl("bwd_n8_k1_routed_dx", N=16, G=2, k=1, dh=32, B=1, S=70, seed=16),
+    # the main setting's per-sequence shape (d 768, N 16, G 8, k 1, d_h 48, S 2048): the full-size
+    # tiling, the split-K pieces over many token chunks, the key-block order over 32 key blocks
+    _wl("bwd_main_setting_s2048", d=768, N=16, G=8, k=1, dh=48, B=1, S=2048, seed=17),
     Workload("bwd_tiny_f32", 64, 4, 2, 1, 16, 1, 32, dtype="f32", router_std=0.5, seed=8),
     Workload("bwd_f32_k2_rope", 64, 8, 2, 2, 16, 2, 24, dtype="f32", router_std=0.5, rope_base=500.0, seed=9),
 ]

@@ -230,3 +230,52 @@ def test_rope_parity(wl):
     """Optional rotary position embedding: every token against the oracle (rotation in float64)."""
     rows = None if wl.tokens <= 1000 else parity.sample_rows(wl.batch, wl.seq, n=96, seed=3)
     _run(wl, rows=rows)
+
+
+# Peaked attention: query and key projections with std 0.2 (ten times the default) put
+# max|q| * max|k| far above the range where the kernel may skip the running maximum (64 in log2
+# units), so every key tile takes the online-softmax step; a ramp that scales x up along the
+# sequence makes the scores grow along the keys, so the running maximum keeps rising by more than
+# the lazy threshold (2^8) and the accumulators are rescaled.  Shapes where the schedule splits
+# items, so the merge combines chunks with non-zero offsets.  Every token is checked.
+PEAKED = [
+    _small("peaked_dh48_k1", B=1, S=1000, qk_std=0.2, seed=30),
+    _small("peaked_dh48_k1_ramp", B=1, S=1000, qk_std=0.2, x_ramp=3.0, seed=31),
+    _small("peaked_dh48_k2", d=512, N=16, G=4, k=2, dh=48, B=1, S=1000, qk_std=0.2, x_ramp=1.0, seed=32),
+    _small("peaked_dh32_k2", d=256, N=8, G=4, k=2, dh=32, B=1, S=1000, qk_std=0.2, seed=33),
+    _small("peaked_dh32_k1_ramp", d=384, N=8, G=4, k=1, dh=32, B=1, S=1000, qk_std=0.2, x_ramp=3.0, seed=34),
+    _small("peaked_dh64_k2_ramp", d=1024, k=2, dh=64, B=1, S=1000, qk_std=0.2, x_ramp=3.0, seed=35),
+    _small("peaked_dh64_k1", d=1024, k=1, dh=64, B=1, S=1000, qk_std=0.2, seed=36),
+]
+
+FAST_BOUND = 64.0   # log2 units: the kernel skips the running maximum only below this bound
+
+
+@pytest.mark.parametrize("wl", PEAKED, ids=[w.name for w in PEAKED])
+def test_online_softmax_branch(wl):
+    from sparse_moe_query_amd import gqe
+    layer, x, inp, gpu, rep = _run(wl, want_qo=True)
+    B, S, dh = wl.batch, wl.seq, wl.dh
+    jobs, merges, nslots, chunk = gqe.gqe_attention_schedule(layer.h, B, S)
+    assert chunk > 0 and len(merges) > 0, "the shape must split attention items"
+    inter = layer.intermediates(B, S)
+    q = inter["q"].float().cpu().numpy().astype(np.float64)          # [B, H, S, dh], log2 units
+    knt = inter["knt"].cpu().numpy().astype(np.float64)[:, :, :(S + 63) // 64]
+    qn = np.sqrt((q ** 2).sum(-1))
+    # every query norm times every tile's largest key norm exceeds the bound: no tile of any wave
+    # can take the fast path (the kernel's per-wave query bound is at least the largest norm)
+    assert qn.min() * knt.min() > FAST_BOUND, (qn.min(), knt.min())
+    og = inter["o"].float().cpu().numpy().reshape(B * S, -1, dh)
+    assert parity.rel_err_rows(og, rep["o_ref"], parity.Y_STORAGE_U[wl.dtype]) <= 2e-2
+    if wl.x_ramp:
+        # scores of late queries rise along the keys by more than the lazy threshold (2^8)
+        k = inter["k"].float().cpu().numpy().astype(np.float64)[0, 0, :S]   # group 0, batch 0
+        rises = 0
+        for pos in (S - 1, S // 2, S - 200):
+            s = k[:pos + 1] @ q[0, 0, pos]
+            tiles = [s[i:i + 64].max() for i in range(0, pos + 1, 64)]
+            rises += int(np.max(np.maximum.accumulate(tiles)) - tiles[0] > 8.0)
+        assert rises > 0
+    print(f"[gpu] {wl.name}: y_err={rep['y_err']:.2e} raw {rep['y_err_raw']:.2e} chunks cap {chunk}, "
+          f"{len(merges)} merged items, min|q|*min knt = {qn.min() * knt.min():.1f}", flush=True)
+    layer.close()
