@@ -118,9 +118,11 @@ def check_routing(cfg, r: dict, gpu_idx, gpu_w):
     return idx_used, int(len(tie_pairs))
 
 
-def compare(wl, gpu: dict, inputs: dict, rows=None, want_qo=False) -> dict:
+def compare(wl, gpu: dict, inputs: dict, rows=None, want_qo=False, check_y=True) -> dict:
     """Check a GPU forward (run_layer output) against the oracle; returns a report and raises
-    AssertionError on any violation."""
+    AssertionError on any violation.  check_y=False records the output errors without holding
+    them to the bar (stress inputs whose output is ill-conditioned in the storage precision are
+    checked stage by stage instead)."""
     cfg = oracle_cfg(wl)
     B, S, T = wl.batch, wl.seq, wl.tokens
     G, k, n, N = wl.num_kv_heads, wl.top_k, wl.num_query_experts // wl.num_kv_heads, \
@@ -156,8 +158,27 @@ def compare(wl, gpu: dict, inputs: dict, rows=None, want_qo=False) -> dict:
                 y_err=rep["y_err"], y_err_raw=rep["y_err_raw"], y_err_global=rep["y_err_global"],
                 bar=Y_TOL[wl.dtype]))
     assert np.all(np.isfinite(gpu["y"][rows])), "non-finite GPU output"
-    assert err <= Y_TOL[wl.dtype], f"{wl.name}: y max-abs error {err:.3e} x token RMS > {Y_TOL[wl.dtype]}"
+    if check_y:
+        assert err <= Y_TOL[wl.dtype], f"{wl.name}: y max-abs error {err:.3e} x token RMS > {Y_TOL[wl.dtype]}"
     return rep
+
+
+def attention_from_stored(q, k, vt_rows, G: int, kper: int, skv: int, S: int):
+    """Causal softmax attention in float64 over the kernel's own stored operands: q [B, H, S, d_h]
+    (already in log2 units, i.e. multiplied by log2(e)/sqrt(d_h)), k [B, G, >=S, d_h],
+    v [B, G, >=S, d_h].  Head v < G*kper attends group v // kper, the shared head group skv.
+    Returns O [B, S, H, d_h].  Isolates the attention kernel from the rounding of its inputs."""
+    B, H, _, dh = q.shape
+    out = np.zeros((B, S, H, dh))
+    mask = np.triu(np.ones((S, S), bool), 1)
+    for b in range(B):
+        for h in range(H):
+            g = h // kper if h < G * kper else skv
+            s = q[b, h, :S] @ k[b, g, :S].T
+            s[mask] = -np.inf
+            p = np.exp2(s - s.max(axis=1, keepdims=True))
+            out[b, :, h] = (p @ vt_rows[b, g, :S]) / p.sum(axis=1, keepdims=True)
+    return out
 
 
 def compare_decode(wl, y, idx, w, inputs: dict, pos) -> dict:

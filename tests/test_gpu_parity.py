@@ -242,7 +242,7 @@ PEAKED = [
     _small("peaked_dh48_k1", B=1, S=1000, qk_std=0.2, seed=30),
     _small("peaked_dh48_k1_ramp", B=1, S=1000, qk_std=0.2, x_ramp=3.0, seed=31),
     _small("peaked_dh48_k2", d=512, N=16, G=4, k=2, dh=48, B=1, S=1000, qk_std=0.2, x_ramp=1.0, seed=32),
-    _small("peaked_dh32_k2", d=256, N=8, G=4, k=2, dh=32, B=1, S=1000, qk_std=0.2, seed=33),
+    _small("peaked_dh32_k2", d=256, N=8, G=4, k=2, dh=32, B=1, S=1000, qk_std=0.3, seed=33),
     _small("peaked_dh32_k1_ramp", d=384, N=8, G=4, k=1, dh=32, B=1, S=1000, qk_std=0.2, x_ramp=3.0, seed=34),
     _small("peaked_dh64_k2_ramp", d=1024, k=2, dh=64, B=1, S=1000, qk_std=0.2, x_ramp=3.0, seed=35),
     _small("peaked_dh64_k1", d=1024, k=1, dh=64, B=1, S=1000, qk_std=0.2, seed=36),
@@ -253,9 +253,22 @@ FAST_BOUND = 64.0   # log2 units: the kernel skips the running maximum only belo
 
 @pytest.mark.parametrize("wl", PEAKED, ids=[w.name for w in PEAKED])
 def test_online_softmax_branch(wl):
+    """Scores this peaked make the output ill-conditioned in bf16: rounding q and k once to bf16
+    (the layer's storage precision, 2^-9 relative) moves a score by up to |q| |k| 2^-8, about one
+    unit of log2 here, which re-weights the softmax by tens of percent.  So the stages are
+    checked one by one: Q, K, V against the oracle within one rounding, the attention output
+    against float64 softmax attention over the kernel's own stored bf16 Q, K, V (the check of
+    the online-softmax branch), routing and statistics exactly; the end-to-end output error is
+    recorded, not held to the bar."""
     from sparse_moe_query_amd import gqe
-    layer, x, inp, gpu, rep = _run(wl, want_qo=True)
-    B, S, dh = wl.batch, wl.seq, wl.dh
+    from sparse_moe_query_amd.gqe import vt_unpermute
+    from sparse_moe_query_amd.runner import build_layer, run_layer
+    print(f"[gpu] {wl.name} B={wl.batch} S={wl.seq} d={wl.dim} N={wl.num_query_experts} "
+          f"G={wl.num_kv_heads} k={wl.top_k} dh={wl.dh} qk_std={wl.qk_std} x_ramp={wl.x_ramp}", flush=True)
+    layer, x, inp = build_layer(wl)
+    gpu = run_layer(layer, x)
+    rep = parity.compare(wl, gpu, inp, want_qo=True, check_y=False)
+    B, S, dh, G = wl.batch, wl.seq, wl.dh, wl.num_kv_heads
     jobs, merges, nslots, chunk = gqe.gqe_attention_schedule(layer.h, B, S)
     assert chunk > 0 and len(merges) > 0, "the shape must split attention items"
     inter = layer.intermediates(B, S)
@@ -265,8 +278,25 @@ def test_online_softmax_branch(wl):
     # every query norm times every tile's largest key norm exceeds the bound: no tile of any wave
     # can take the fast path (the kernel's per-wave query bound is at least the largest norm)
     assert qn.min() * knt.min() > FAST_BOUND, (qn.min(), knt.min())
-    og = inter["o"].float().cpu().numpy().reshape(B * S, -1, dh)
-    assert parity.rel_err_rows(og, rep["o_ref"], parity.Y_STORAGE_U[wl.dtype]) <= 2e-2
+    H = q.shape[1]
+    # stored Q, K, V = the exact values rounded once
+    qscale = np.float32(1.4426950408889634 / np.sqrt(dh))
+    qg = q.transpose(0, 2, 1, 3).reshape(B * S, H, dh) / qscale
+    assert parity.within_rounding(qg, rep["q_ref"], wl.dtype)
+    kg = inter["k"].float().cpu().numpy().astype(np.float64)
+    vg = vt_unpermute(inter["vt"]).float().cpu().numpy().astype(np.float64).transpose(0, 1, 3, 2)
+    Kx = rep["K"].reshape(B, S, G, dh).transpose(0, 2, 1, 3)
+    Vx = rep["V"].reshape(B, S, G, dh).transpose(0, 2, 1, 3)
+    assert parity.within_rounding(kg[:, :, :S], Kx, wl.dtype)
+    assert parity.within_rounding(vg[:, :, :S], Vx, wl.dtype)
+    # the attention output against float64 attention over the stored operands: the kernel's own
+    # roundings are P to bf16 (2^-9 relative, the same P forms the row sums) and O to bf16
+    og = inter["o"].float().cpu().numpy().astype(np.float64).reshape(B, S, H, dh)
+    oref = parity.attention_from_stored(q, kg, vg, G, wl.top_k, wl.shared_kv_group, S)
+    o_err = parity.rel_err_rows(og, oref, parity.Y_STORAGE_U[wl.dtype])
+    parity.record(dict(kind="attention_stage", workload=wl.name, o_err=o_err, o_err_raw=parity.rel_err_rows(og, oref),
+                       bar=1e-2))
+    assert o_err <= 1e-2, f"attention output {o_err:.3e} x row RMS from float64 attention over the stored operands"
     if wl.x_ramp:
         # scores of late queries rise along the keys by more than the lazy threshold (2^8)
         k = inter["k"].float().cpu().numpy().astype(np.float64)[0, 0, :S]   # group 0, batch 0
@@ -276,6 +306,7 @@ def test_online_softmax_branch(wl):
             tiles = [s[i:i + 64].max() for i in range(0, pos + 1, 64)]
             rises += int(np.max(np.maximum.accumulate(tiles)) - tiles[0] > 8.0)
         assert rises > 0
-    print(f"[gpu] {wl.name}: y_err={rep['y_err']:.2e} raw {rep['y_err_raw']:.2e} chunks cap {chunk}, "
+    print(f"[gpu] {wl.name}: attention stage {o_err:.2e}; end to end y_err={rep['y_err']:.2e} "
+          f"raw {rep['y_err_raw']:.2e} (recorded); chunk cap {chunk}, "
           f"{len(merges)} merged items, min|q|*min knt = {qn.min() * knt.min():.1f}", flush=True)
     layer.close()
