@@ -17,10 +17,9 @@
  *  - Device pointers are plain addresses in the memory of the current HIP device.  All
  *    tensors are dense and row-major in the "x @ W" convention; shapes are given per argument.
  *  - Ownership: the caller owns every device buffer (x, y, weights, packed weights, workspace,
- *    routing outputs) and the stream.  The library owns the opaque host handle and, per
- *    (device, batch, seq) it has run, a small device table of the attention work schedule
- *    (8 int32 per work group), allocated and copied synchronously on the first gqe_forward of
- *    that shape and freed by gqe_destroy.
+ *    routing outputs) and the stream.  The library owns only the opaque host handle; it
+ *    allocates no device memory and copies nothing between host and device in gqe_forward
+ *    (the attention work schedule is rebuilt in the workspace by a kernel of every forward).
  *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
  *    enqueued asynchronously; only gqe_aux_stats synchronises.
  *  - A handle is not re-entrant: calls that use one handle (or one workspace) must not overlap
@@ -138,8 +137,10 @@ int gqe_packed_weights_bytes(const gqe_handle_t* h, size_t* bytes);
 int gqe_pack_weights(gqe_handle_t* h, void* packed, size_t bytes, void* stream);
 
 /* Bytes of scratch that gqe_forward needs for a [batch, seq] input (routing decisions,
- * per-expert statistics, Q/K/V, head outputs and the float32 partial results of attention items
- * that the schedule splits along the key range).  batch >= 1, seq >= 1.  Host only. */
+ * per-expert statistics, Q/K/V, head outputs, the attention work schedule and the float32
+ * partial results of attention items that the schedule splits along the key range).
+ * batch >= 1, seq >= 1, batch * seq <= 2^28.  Host only.  Errors: GQE_ERR_NULL_POINTER,
+ * GQE_ERR_SHAPE, GQE_ERR_UNSUPPORTED (an attention work item longer than 8191 key tiles). */
 int gqe_workspace_bytes(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t* bytes);
 
 /* The forward pass y = GQE(x) (README "Usage": y = attn(x)).
@@ -151,9 +152,10 @@ int gqe_workspace_bytes(const gqe_handle_t* h, int64_t batch, int64_t seq, size_
  *             group (descending router logit; ties -> lower id).  NULL to skip.
  *  route_w    optional [batch, seq, G, k] float32: renormalised weight p / sum(p_selected)
  *             of each choice.  NULL to skip.
- * Enqueues all kernels on `stream` and returns.  Requires gqe_pack_weights first (else
+ * Enqueues all kernels on `stream` and returns; no device allocation, no host-device copy, no
+ * synchronisation (it may be captured in a HIP graph).  Requires gqe_pack_weights first (else
  * GQE_ERR_STATE).  Errors: NULL/misaligned pointers, GQE_ERR_SHAPE, GQE_ERR_WORKSPACE,
- * GQE_ERR_HIP (launch failure). */
+ * GQE_ERR_UNSUPPORTED, GQE_ERR_HIP (launch failure). */
 int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t seq,
                 void* workspace, size_t ws_bytes, void* stream, int32_t* route_idx,
                 float* route_w);
@@ -178,10 +180,12 @@ int gqe_aux_stats(gqe_handle_t* h, void* stream, int64_t* counts, double* mean_p
  * swapped), offs[3] O_act [B, S, H_act, d_h], offs[4] route_idx [T, G, k] int32, offs[5]
  * route_w [T, G, k] f32, offs[6] p_sel [T, G, k] f32, offs[7] statistics (counts [N] int64,
  * mean probability [N] f64, aux f64), offs[8] key norms [B, G, S_pad] f32, offs[9] largest key
- * norm of every 64-key tile [B, G, S_pad / 64] f32; dims[0] = H_act, dims[1] = S_pad,
- * dims[2] = matrix-core stages (1 projection, 2 attention, 4 combine).  Errors:
+ * norm of every 64-key tile [B, G, S_pad / 64] f32, offs[10] the attention jobs [dims[3]][8]
+ * int32 and offs[11] the merge records [.][8] int32 (the tables gqe_attention_schedule returns,
+ * as the forward built them); dims[0] = H_act, dims[1] = S_pad, dims[2] = matrix-core stages
+ * (1 projection, 2 attention, 4 combine), dims[3] = attention jobs.  Errors:
  * GQE_ERR_NULL_POINTER, GQE_ERR_SHAPE. */
-int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t offs[10],
+int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t offs[12],
                          int64_t dims[4]);
 
 /* Token-to-expert bucketing of the last forward's routing: the global form of the gather the
@@ -201,11 +205,12 @@ int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size
 int gqe_bucket(gqe_handle_t* h, void* stream, int32_t* offs, int32_t* perm, int32_t* inv);
 
 /* The work schedule of the matrix-core attention for a [batch, seq] forward (host only, no device
- * call; the same tables gqe_forward uploads).  The causal attention of item (batch b, group g,
+ * call; the same tables gqe_forward builds in its workspace).  The causal attention of item (batch b, group g,
  * positions p0 .. p0+np-1, the nh active heads of the group at each position: 256 / nh positions
  * per item) reads the key tiles 0 .. (last position)/64; long items are split into chunks of
  * consecutive key tiles whose float32 partial results a merge kernel combines (online-softmax
- * merge over disjoint key ranges).
+ * merge over disjoint key ranges).  Order: jobs by key-tile count, longest first; equal counts in
+ * the order group, item, chunk; the batch's B sequences of one (group, item, chunk) in a row.
  *  jobs    NULL or [max_jobs][8] int32, dispatch order: b, g, nh, p0, np, kt0, kt1 (key tiles
  *          [kt0, kt1)), partial slot (-1: the job covers the whole item and writes O itself)
  *  merges  NULL or [max_merges][8] int32: b, g, nh, p0, np, first slot, chunks, 0
@@ -317,17 +322,18 @@ int gqe_backward(gqe_handle_t* h, const void* x, const void* dy, int64_t batch, 
  * and of gqe_backward:
  *   12 output-side gradients (dy W_slot^T, head outputs, router logits)   13 attention
  *   14 weight gradients     15 input gradient dx
+ * and 16 the attention schedule builder of gqe_forward.
  * gqe_profile_read_kernels waits for the recorded events, returns the summed milliseconds per
  * kernel slot (0 for slots not launched) and the number of forwards they cover, and starts a new
  * accumulation.  gqe_profile_read does the same summed per stage (0 router = slots 0+1,
- * 1 projections = 2+3+8, 2 attention = 4+5+6+9+10, 3 combine = 7+11).  Not re-entrant; errors as
+ * 1 projections = 2+3+8, 2 attention = 16+4+5+6+9+10, 3 combine = 7+11).  Not re-entrant; errors as
  * GQE_ERR_NULL_POINTER / GQE_ERR_HIP. */
-#define GQE_PROF_KERNELS 16
+#define GQE_PROF_KERNELS 17
 int gqe_profile_enable(gqe_handle_t* h, int enable);
 int gqe_profile_read(gqe_handle_t* h, double stage_ms[4], int64_t* forwards);
 int gqe_profile_read_kernels(gqe_handle_t* h, double kernel_ms[GQE_PROF_KERNELS], int64_t* forwards);
 
-/* Destroys the handle and frees the device schedule tables it owns.  NULL is ignored. */
+/* Destroys the handle.  NULL is ignored. */
 void gqe_destroy(gqe_handle_t* h);
 
 /* Message of the last failing call on this thread ("" if none). */

@@ -12,7 +12,10 @@
 // scheduling).  A job costs its key tiles plus a fixed start/finish cost (tile units); splitting
 // adds the partial write per chunk and a merge kernel.  The candidate with the shortest simulated
 // time wins; it is a pure function of (config, batch, seq), so the workspace size that depends on
-// it is reproducible without a device.
+// it is reproducible without a device.  The tables themselves (dispatch order, slots, merges: the
+// canonical order defined in gqe_internal.h) are built on the device by every forward
+// (k_sched.hip) from the chunk cap; plan_attention builds the same tables on the host for
+// gqe_attention_schedule.
 #include <algorithm>
 #include <cmath>
 #include <functional>
@@ -52,10 +55,6 @@ std::vector<ItemT> make_items(const GqeDims& D, int64_t B, int64_t S) {
     return it;
 }
 
-int chunks_of(int kt, int C) {
-    if (C <= 0 || kt <= C) return 1;
-    return std::min<int>((kt + C - 1) / C, GQE_ATTN_MAX_CHUNKS);
-}
 
 // Simulated finish time (tile units) of jobs dispatched in the given order.
 double simulate(const std::vector<double>& cost) {
@@ -78,14 +77,17 @@ double evaluate(const std::vector<ItemT>& items, int C, int64_t* nslots) {
     cost.reserve(items.size() * 2);
     int64_t slots = 0;
     for (const ItemT& t : items) {
-        const int nc = chunks_of(t.kt, C);
+        const int nc = attn_chunks_of(t.kt, C);
         if (nc == 1) {
             cost.push_back(t.kt + kJobFixed);
             continue;
         }
         slots += nc;
-        for (int i = 0; i < nc; ++i)
-            cost.push_back((double)((int64_t)(i + 1) * t.kt / nc - (int64_t)i * t.kt / nc) + kJobFixed + kChunkExtra);
+        for (int i = 0; i < nc; ++i) {
+            int a, e;
+            attn_chunk_range(t.kt, nc, i, &a, &e);
+            cost.push_back((double)(e - a) + kJobFixed + kChunkExtra);
+        }
     }
     std::sort(cost.begin(), cost.end(), std::greater<double>());
     double t = simulate(cost);
@@ -96,8 +98,9 @@ double evaluate(const std::vector<ItemT>& items, int C, int64_t* nslots) {
 
 }  // namespace
 
-AttnSchedule plan_attention(const GqeDims& D, int64_t B, int64_t S, bool tables) {
-    AttnSchedule sc;
+// Chunk cap and sizes (no tables).
+AttnCounts attn_counts(const GqeDims& D, int64_t B, int64_t S) {
+    AttnCounts n;
     const std::vector<ItemT> items = make_items(D, B, S);
     int max_kt = 0;
     for (const ItemT& t : items) max_kt = std::max(max_kt, t.kt);
@@ -105,7 +108,6 @@ AttnSchedule plan_attention(const GqeDims& D, int64_t B, int64_t S, bool tables)
     int64_t ns = 0;
     double best = evaluate(items, 0, &ns);
     int bestC = 0;
-    int64_t bestN = 0;
     std::vector<int> caps;
     for (int c = 4; c < max_kt; c = c < 8 ? c + 2 : c + c / 2) caps.push_back(c);
     std::reverse(caps.begin(), caps.end());
@@ -114,36 +116,80 @@ AttnSchedule plan_attention(const GqeDims& D, int64_t B, int64_t S, bool tables)
         if (t < best * (1.0 - kMinGain)) {
             best = t;
             bestC = C;
-            bestN = ns;
         }
     }
-    sc.chunk = bestC;
-    sc.nslots = bestN;
-    if (!tables) return sc;
+    n.chunk = bestC;
+    // the templates of one sequence (every sequence has the same items)
+    for (int g = 0; g < D.G; ++g) {
+        const int nh = attn_item_nh(g, D.k, D.s, D.skv);
+        const int ni = attn_items_of_group(S, nh);
+        n.items += ni;
+        for (int i = 0; i < ni; ++i) {
+            int p0, np;
+            const int kt = attn_item_tiles(S, nh, i, &p0, &np);
+            const int nc = attn_chunks_of(kt, bestC);
+            n.tpl += nc;
+            for (int c = 0; c < nc; ++c) {
+                int a, e;
+                attn_chunk_range(kt, nc, c, &a, &e);
+                n.maxlen = std::max(n.maxlen, e - a);
+            }
+            if (nc > 1) {
+                n.nmerges += B;
+                n.nslots += B * nc;
+            }
+        }
+    }
+    n.njobs = B * n.tpl;
+    return n;
+}
 
-    struct J {
-        AttnJob j;
-        int len;
-        size_t order;
+// The tables in the canonical order (gqe_internal.h): templates sorted by length, longest first,
+// ties by template number; B jobs per template.
+AttnSchedule plan_attention(const GqeDims& D, int64_t B, int64_t S) {
+    AttnSchedule sc;
+    sc.n = attn_counts(D, B, S);
+    const int C = sc.n.chunk;
+    struct Tpl {
+        int g, nh, p0, np, kt0, kt1, nc, c;
+        int64_t ss;  // first slot index / B of the item (split items)
     };
-    std::vector<J> jobs;
-    jobs.reserve(items.size() + (size_t)bestN);
-    int32_t slot = 0;
-    for (const ItemT& t : items) {
-        const int nc = chunks_of(t.kt, bestC);
-        if (nc == 1) {
-            jobs.push_back(J{AttnJob{t.b, t.g, t.nh, t.p0, t.np, 0, t.kt, -1}, t.kt, jobs.size()});
-            continue;
+    std::vector<Tpl> tpl;
+    tpl.reserve(sc.n.tpl);
+    int64_t ss = 0, mi = 0;
+    sc.merges.resize((size_t)sc.n.nmerges);
+    for (int g = 0; g < D.G; ++g) {
+        const int nh = attn_item_nh(g, D.k, D.s, D.skv);
+        const int ni = attn_items_of_group(S, nh);
+        for (int i = 0; i < ni; ++i) {
+            int p0, np;
+            const int kt = attn_item_tiles(S, nh, i, &p0, &np);
+            const int nc = attn_chunks_of(kt, C);
+            for (int c = 0; c < nc; ++c) {
+                int a, e;
+                attn_chunk_range(kt, nc, c, &a, &e);
+                tpl.push_back(Tpl{g, nh, p0, np, a, e, nc, c, nc > 1 ? ss : -1});
+            }
+            if (nc > 1) {
+                for (int64_t b = 0; b < B; ++b)
+                    sc.merges[(size_t)(B * mi + b)] =
+                        AttnMerge{(int32_t)b, g, nh, p0, np, (int32_t)(B * ss + b * nc), nc, 0};
+                ss += nc;
+                mi += 1;
+            }
         }
-        sc.merges.push_back(AttnMerge{t.b, t.g, t.nh, t.p0, t.np, slot, nc, 0});
-        for (int i = 0; i < nc; ++i) {
-            const int a = (int)((int64_t)i * t.kt / nc), e = (int)((int64_t)(i + 1) * t.kt / nc);
-            jobs.push_back(J{AttnJob{t.b, t.g, t.nh, t.p0, t.np, a, e, slot + i}, e - a, jobs.size()});
-        }
-        slot += nc;
     }
-    std::stable_sort(jobs.begin(), jobs.end(), [](const J& x, const J& y) { return x.len > y.len; });
-    sc.jobs.reserve(jobs.size());
-    for (const J& x : jobs) sc.jobs.push_back(x.j);
+    std::vector<int> order(tpl.size());
+    for (size_t t = 0; t < tpl.size(); ++t) order[t] = (int)t;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int x, int y) { return tpl[x].kt1 - tpl[x].kt0 > tpl[y].kt1 - tpl[y].kt0; });
+    sc.jobs.reserve((size_t)sc.n.njobs);
+    for (int t : order) {
+        const Tpl& x = tpl[t];
+        for (int64_t b = 0; b < B; ++b) {
+            const int32_t part = x.ss >= 0 ? (int32_t)(B * x.ss + b * x.nc + x.c) : -1;
+            sc.jobs.push_back(AttnJob{(int32_t)b, x.g, x.nh, x.p0, x.np, x.kt0, x.kt1, part});
+        }
+    }
     return sc;
 }

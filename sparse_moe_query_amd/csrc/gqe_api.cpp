@@ -38,7 +38,7 @@ static bool misaligned(const void* p, size_t a) { return ((uintptr_t)p) % a != 0
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S, int64_t attn_slots) {
+WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S, const AttnCounts& ac) {
     WorkPlan P;
     P.B = B;
     P.S = S;
@@ -67,9 +67,13 @@ WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S, int64_t attn_slots) {
     P.o = take((size_t)B * S * D.H * D.dh * es);
     P.kn = take((size_t)B * D.G * P.S_pad * 4);
     P.knt = take((size_t)B * D.G * (P.S_pad / GQE_KV_TILE) * 4);
-    P.nslots = attn_slots;
-    P.part_o = take((size_t)attn_slots * GQE_ATTN_COLS * D.dh * 4);
-    P.part_ml = take((size_t)attn_slots * GQE_ATTN_COLS * 2 * 4);
+    P.ac = ac;
+    P.nslots = ac.nslots;
+    P.part_o = take((size_t)ac.nslots * GQE_ATTN_COLS * D.dh * 4);
+    P.part_ml = take((size_t)ac.nslots * GQE_ATTN_COLS * 2 * 4);
+    P.sched_jobs = take((size_t)ac.njobs * sizeof(AttnJob));
+    P.sched_merges = take((size_t)ac.nmerges * sizeof(AttnMerge));
+    P.sched_scratch = take(ac.njobs > 0 ? attn_sched_scratch_bytes(ac) : 0);
     P.total = off;
     return P;
 }
@@ -176,43 +180,29 @@ static bool mfma_supported(const GqeDims& D) {
     return true;
 }
 
-// Partial-result slots of the attention schedule for [B, S] (0 on the scalar attention path).
-static int64_t attn_slots(const gqe_handle* h, int64_t B, int64_t S) {
-    if (!h->mfma_attn) return 0;
-    for (const AttnSchedDev& c : h->sched)
-        if (c.B == B && c.S == S) return c.nslots;
-    return plan_attention(h->D, B, S, false).nslots;
+// Sizes of the attention schedule for [B, S] (all zero on the scalar attention path).  The chunk
+// cap comes from a host simulation of the dispatch; the last few shapes are cached in the handle
+// (host memory only).
+static AttnCounts attn_counts_for(const gqe_handle* h, int64_t B, int64_t S) {
+    if (!h->mfma_attn) return AttnCounts{};
+    for (const gqe_handle::CountEntry& c : h->count_cache)
+        if (c.B == B && c.S == S) return c.c;
+    const AttnCounts ac = attn_counts(h->D, B, S);
+    gqe_handle::CountEntry& slot = h->count_cache[h->count_next];
+    slot.B = B;
+    slot.S = S;
+    slot.c = ac;
+    h->count_next = (h->count_next + 1) % gqe_handle::kCountCache;
+    return ac;
 }
 
-// The device copy of the attention schedule for [B, S] on the current device: built on the host
-// and uploaded on first use (synchronous copy), then reused.
-static int attn_schedule(gqe_handle* h, int64_t B, int64_t S, const AttnSchedDev** out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail(GQE_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
-    for (const AttnSchedDev& c : h->sched)
-        if (c.device == dev && c.B == B && c.S == S) {
-            *out = &c;
-            return GQE_OK;
-        }
-    const AttnSchedule sc = plan_attention(h->D, B, S, true);
-    AttnSchedDev d{dev, B, S, nullptr, nullptr, (int)sc.jobs.size(), (int)sc.merges.size(), sc.nslots};
-    if (sc.jobs.empty() || sc.jobs.size() > 0x7fffffffu)
-        return fail(GQE_ERR_SHAPE, "attention schedule has %zu jobs", sc.jobs.size());
-    e = hipMalloc((void**)&d.jobs, sc.jobs.size() * sizeof(AttnJob));
-    if (e == hipSuccess) e = hipMemcpy(d.jobs, sc.jobs.data(), sc.jobs.size() * sizeof(AttnJob), hipMemcpyHostToDevice);
-    if (e == hipSuccess && !sc.merges.empty()) {
-        e = hipMalloc((void**)&d.merges, sc.merges.size() * sizeof(AttnMerge));
-        if (e == hipSuccess)
-            e = hipMemcpy(d.merges, sc.merges.data(), sc.merges.size() * sizeof(AttnMerge), hipMemcpyHostToDevice);
-    }
-    if (e != hipSuccess) {
-        if (d.jobs) (void)hipFree(d.jobs);
-        if (d.merges) (void)hipFree(d.merges);
-        return fail(GQE_ERR_HIP, "upload of the attention schedule failed: %s", hipGetErrorString(e));
-    }
-    h->sched.push_back(d);
-    *out = &h->sched.back();
+// The device schedule builder keeps per-length counters in LDS and the job index in 32 bits.
+static int attn_counts_supported(const AttnCounts& ac) {
+    if (ac.maxlen >= 8192)
+        return fail(GQE_ERR_UNSUPPORTED, "an attention work item of %d key tiles exceeds the schedule builder's 8191",
+                    ac.maxlen);
+    if (ac.njobs > 0x7fffffff || ac.nslots > 0x7fffffff)
+        return fail(GQE_ERR_SHAPE, "attention schedule of %lld jobs exceeds 2^31", (long long)ac.njobs);
     return GQE_OK;
 }
 
@@ -330,14 +320,17 @@ int gqe_workspace_bytes(const gqe_handle_t* h, int64_t batch, int64_t seq, size_
     if (!h || !bytes) return fail(GQE_ERR_NULL_POINTER, "handle and bytes must be non-NULL");
     if (batch < 1 || seq < 1 || batch * seq > ((int64_t)1 << 28))
         return fail(GQE_ERR_SHAPE, "batch and seq must be >= 1 with batch*seq <= 2^28");
-    *bytes = make_plan(h->D, batch, seq, attn_slots(h, batch, seq)).total;
+    const AttnCounts ac = attn_counts_for(h, batch, seq);
+    const int rc = attn_counts_supported(ac);
+    if (rc != GQE_OK) return rc;
+    *bytes = make_plan(h->D, batch, seq, ac).total;
     return ok();
 }
 
-int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t offs[10], int64_t dims[4]) {
+int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t offs[12], int64_t dims[4]) {
     if (!h || !offs || !dims) return fail(GQE_ERR_NULL_POINTER, "handle, offs and dims must be non-NULL");
     if (batch < 1 || seq < 1 || batch * seq > ((int64_t)1 << 28)) return fail(GQE_ERR_SHAPE, "bad batch/seq");
-    WorkPlan P = make_plan(h->D, batch, seq, attn_slots(h, batch, seq));
+    WorkPlan P = make_plan(h->D, batch, seq, attn_counts_for(h, batch, seq));
     offs[0] = P.q;
     offs[1] = P.kk;
     offs[2] = P.vt;
@@ -348,10 +341,12 @@ int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size
     offs[7] = P.stats;
     offs[8] = P.kn;
     offs[9] = P.knt;
+    offs[10] = P.sched_jobs;
+    offs[11] = P.sched_merges;
     dims[0] = h->D.H;
     dims[1] = P.S_pad;
     dims[2] = (h->mfma_proj ? 1 : 0) | (h->mfma_attn ? 2 : 0) | (h->mfma_combine ? 4 : 0);
-    dims[3] = 0;
+    dims[3] = P.ac.njobs;
     return ok();
 }
 
@@ -372,12 +367,12 @@ int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t 
     const char* xb = (const char*)x;
     const char* yb = (const char*)y;
     if (xb < yb + xbytes && yb < xb + xbytes) return fail(GQE_ERR_INVALID_CONFIG, "x and y must not alias");
-    const AttnSchedDev* sched = nullptr;
-    if (h->mfma_attn) {
-        const int rc = attn_schedule(h, batch, seq, &sched);
+    const AttnCounts ac = attn_counts_for(h, batch, seq);
+    {
+        const int rc = attn_counts_supported(ac);
         if (rc != GQE_OK) return rc;
     }
-    WorkPlan P = make_plan(D, batch, seq, sched ? sched->nslots : 0);
+    WorkPlan P = make_plan(D, batch, seq, ac);
     if (ws_bytes < P.total) return fail(GQE_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, P.total);
     hipStream_t st = (hipStream_t)stream;
     char* ws = (char*)workspace;
@@ -389,16 +384,22 @@ int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t 
         if (rc != GQE_OK) return rc;
         km = &marks;
     }
+    // the attention schedule first: it depends only on the shape, and is built in the workspace
+    if (h->mfma_attn) {
+        if (km) km->begin(KT_ATTN_SCHED);
+        e = launch_attn_sched(D, P, ws, st);
+        if (km) km->mark(KT_ATTN_SCHED);
+    }
     // with the matrix-core projection, its last work group finalizes the router statistics and
     // (S % 64 == 0) its key blocks write the per-tile key-norm maxima the attention reads
-    if (!D.dense) e = launch_router(D, P, x, h->packed, h->pl, ws, route_idx, route_w, st, km, !h->mfma_proj);
+    if (e == hipSuccess && !D.dense) e = launch_router(D, P, x, h->packed, h->pl, ws, route_idx, route_w, st, km, !h->mfma_proj);
     if (e == hipSuccess)
         e = h->mfma_proj ? launch_proj_mfma(D, P, x, h->packed, h->pl, ws, st, km)
                          : launch_proj_simple(D, P, h->w, x, (const double*)((const char*)h->packed + h->pl.rope), ws, st,
                                               km);
     if (e == hipSuccess && !h->mfma_proj && h->mfma_attn) e = launch_kn_simple(D, P, ws, st, km);
     if (e == hipSuccess)
-        e = h->mfma_attn ? launch_attn_mfma(D, P, *sched, ws, st, km, !(h->mfma_proj && P.S % 64 == 0))
+        e = h->mfma_attn ? launch_attn_mfma(D, P, ws, st, km, !(h->mfma_proj && P.S % 64 == 0))
                          : launch_attn_simple(D, P, ws, st, km);
     if (e == hipSuccess)
         e = h->mfma_combine ? launch_combine_mfma(D, P, h->packed, h->pl, y, ws, st, km)
@@ -464,11 +465,11 @@ int gqe_attention_schedule(const gqe_handle_t* h, int64_t batch, int64_t seq, in
     if (!h || !counts) return fail(GQE_ERR_NULL_POINTER, "handle and counts must be non-NULL");
     if (batch < 1 || seq < 1 || batch * seq > ((int64_t)1 << 28)) return fail(GQE_ERR_SHAPE, "bad batch/seq");
     if (!h->mfma_attn) return fail(GQE_ERR_STATE, "this configuration runs the scalar attention path (no schedule)");
-    const AttnSchedule sc = plan_attention(h->D, batch, seq, true);
+    const AttnSchedule sc = plan_attention(h->D, batch, seq);
     counts[0] = (int64_t)sc.jobs.size();
     counts[1] = (int64_t)sc.merges.size();
-    counts[2] = sc.nslots;
-    counts[3] = sc.chunk;
+    counts[2] = sc.n.nslots;
+    counts[3] = sc.n.chunk;
     if (jobs) {
         if (max_jobs < counts[0]) return fail(GQE_ERR_WORKSPACE, "jobs buffer holds %lld < %lld records",
                                               (long long)max_jobs, (long long)counts[0]);
@@ -684,7 +685,7 @@ int gqe_profile_read(gqe_handle_t* h, double stage_ms[4], int64_t* forwards) {
     if (rc != GQE_OK) return rc;
     stage_ms[0] = k[KT_ROUTER] + k[KT_ROUTER_STATS];
     stage_ms[1] = k[KT_PROJ] + k[KT_KEYNORM] + k[KT_DEC_PROJ];
-    stage_ms[2] = k[KT_ATTN_PREP] + k[KT_ATTN] + k[KT_ATTN_MERGE] + k[KT_DEC_ATTN] + k[KT_DEC_MERGE];
+    stage_ms[2] = k[KT_ATTN_SCHED] + k[KT_ATTN_PREP] + k[KT_ATTN] + k[KT_ATTN_MERGE] + k[KT_DEC_ATTN] + k[KT_DEC_MERGE];
     stage_ms[3] = k[KT_COMBINE] + k[KT_DEC_COMBINE];
     return ok();
 }
@@ -692,14 +693,6 @@ int gqe_profile_read(gqe_handle_t* h, double stage_ms[4], int64_t* forwards) {
 void gqe_destroy(gqe_handle_t* h) {
     if (!h) return;
     for (hipEvent_t e : h->prof_ev) (void)hipEventDestroy(e);
-    for (AttnSchedDev& c : h->sched) {
-        int cur = 0;
-        const bool other = hipGetDevice(&cur) == hipSuccess && cur != c.device;
-        if (other) (void)hipSetDevice(c.device);
-        if (c.jobs) (void)hipFree(c.jobs);
-        if (c.merges) (void)hipFree(c.merges);
-        if (other) (void)hipSetDevice(cur);
-    }
     delete h;
 }
 

@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "../../include/gqe.h"
+#include "gqe_common.h"
 
 #define GQE_ATTN_COLS 256        // query columns (position, head) of one attention work item
 #define GQE_ATTN_MAX_CHUNKS 32   // key-range chunks an attention item may be split into
@@ -39,6 +40,72 @@ struct PackedLayout {
                          // W_o[e] + W_oR[g] (the renormalised weight is exactly 1), no own slot
 };
 
+// One attention work group: item (batch b, group g, nh heads per position, positions
+// [p0, p0 + np)) restricted to key tiles [kt0, kt1); part = partial-result slot, or -1 when the
+// job covers the whole item and writes O itself.  Eight int32 per job on the device.
+struct AttnJob {
+    int32_t b, g, nh, p0, np, kt0, kt1, part;
+};
+// One merge work group: the item's nc chunks sit in slots slot0 .. slot0 + nc - 1.
+struct AttnMerge {
+    int32_t b, g, nh, p0, np, slot0, nc, pad;
+};
+
+// ---------------------------------------------------------------- attention work schedule
+// Items of one sequence: group g carries nh = k heads per position (k + 1 in the shared head's
+// group); an item is 256 / nh consecutive positions, items i = 0 .. ceil(S / (256 / nh)) - 1 in
+// group order.  Item (g, i) reads key tiles [0, kt), kt = (last position) / 64 + 1; with a chunk
+// cap C > 0 an item longer than C tiles is cut into nc = min(ceil(kt / C), 32) chunks, chunk c
+// covering tiles [c kt / nc, (c + 1) kt / nc).  A template is one (g, i, c); templates are
+// numbered group-major, then item, then chunk.  Dispatch order: templates sorted by length
+// (kt1 - kt0) descending, ties by template number, and each template's B sequences in a row
+// (job = B rank + b).  Split item (g, i) of sequence b owns partial slots B ss + b nc + c, where ss
+// is the number of chunks of the split items before it, and merge record B mi + b, where mi is the
+// number of split items before it.  The host planner (attn_sched.cpp) and the device builder
+// (k_sched.hip) both follow this definition, so the table gqe_forward builds in the workspace
+// equals the one gqe_attention_schedule returns.
+__host__ __device__ inline int attn_item_nh(int g, int k, int s, int skv) { return k + ((s && g == skv) ? 1 : 0); }
+__host__ __device__ inline int attn_items_of_group(int64_t S, int nh) {
+    const int P = GQE_ATTN_COLS / nh;
+    return (int)((S + P - 1) / P);
+}
+__host__ __device__ inline int attn_item_tiles(int64_t S, int nh, int i, int* p0, int* np) {
+    const int P = GQE_ATTN_COLS / nh;
+    const int64_t a = (int64_t)i * P;
+    const int64_t n = S - a < P ? S - a : P;
+    *p0 = (int)a;
+    *np = (int)n;
+    return (int)((a + n - 1) / GQE_KV_TILE + 1);
+}
+__host__ __device__ inline int attn_chunks_of(int kt, int C) {
+    if (C <= 0 || kt <= C) return 1;
+    const int nc = (kt + C - 1) / C;
+    return nc < GQE_ATTN_MAX_CHUNKS ? nc : GQE_ATTN_MAX_CHUNKS;
+}
+__host__ __device__ inline void attn_chunk_range(int kt, int nc, int c, int* kt0, int* kt1) {
+    *kt0 = (int)((int64_t)c * kt / nc);
+    *kt1 = (int)((int64_t)(c + 1) * kt / nc);
+}
+
+// Sizes of the schedule of a [B, S] forward (a pure function of the config, B and S).
+struct AttnCounts {
+    int chunk = 0;          // chunk cap C in key tiles (0: no item split)
+    int items = 0;          // items of one sequence (all groups)
+    int tpl = 0;            // templates of one sequence
+    int maxlen = 0;         // longest template in key tiles
+    int64_t njobs = 0;      // B tpl
+    int64_t nmerges = 0;    // B x split items of one sequence
+    int64_t nslots = 0;     // B x chunks of the split items of one sequence
+};
+AttnCounts attn_counts(const GqeDims& D, int64_t B, int64_t S);
+
+struct AttnSchedule {
+    std::vector<AttnJob> jobs;      // dispatch order
+    std::vector<AttnMerge> merges;
+    AttnCounts n;
+};
+AttnSchedule plan_attention(const GqeDims& D, int64_t B, int64_t S);
+
 // Byte offsets into the caller's workspace for one [B, S] forward.
 struct WorkPlan {
     int64_t B, S, T, S_pad;
@@ -53,6 +120,10 @@ struct WorkPlan {
     size_t knt;                       // per-64-key-tile maximum norm [B][G][S_pad/64] f32
     size_t part_o, part_ml;           // attention partials [nslots][256][d_h] / [nslots][256][2] f32
     int64_t nslots;
+    // the attention schedule, built on the device by every forward (matrix-core attention only):
+    // jobs [njobs][8], merges [nmerges][8] int32, and the builder's scratch
+    AttnCounts ac;
+    size_t sched_jobs, sched_merges, sched_scratch;
     size_t total;
 };
 
@@ -79,34 +150,6 @@ struct BwdPlan {
     size_t total;
 };
 
-// One attention work group: item (batch b, group g, nh heads per position, positions
-// [p0, p0 + np)) restricted to key tiles [kt0, kt1); part = partial-result slot, or -1 when the
-// job covers the whole item and writes O itself.  Eight int32 per job on the device.
-struct AttnJob {
-    int32_t b, g, nh, p0, np, kt0, kt1, part;
-};
-// One merge work group: the item's nc chunks sit in slots slot0 .. slot0 + nc - 1.
-struct AttnMerge {
-    int32_t b, g, nh, p0, np, slot0, nc, pad;
-};
-struct AttnSchedule {
-    std::vector<AttnJob> jobs;      // dispatch order
-    std::vector<AttnMerge> merges;
-    int64_t nslots = 0;             // partial-result slots
-    int chunk = 0;                  // chunk cap in key tiles (0: no item split)
-};
-// tables = false: only nslots and chunk (for workspace sizing)
-AttnSchedule plan_attention(const GqeDims& D, int64_t B, int64_t S, bool tables);
-
-// Device copy of a schedule, owned by the handle (one per (device, batch, seq) run).
-struct AttnSchedDev {
-    int device;
-    int64_t B, S;
-    AttnJob* jobs;
-    AttnMerge* merges;
-    int njobs, nmerges;
-    int64_t nslots;
-};
 
 struct gqe_handle {
     gqe_config_t cfg;
@@ -125,14 +168,21 @@ struct gqe_handle {
     std::vector<hipEvent_t> prof_ev;     // 2 * KT_COUNT events per recorded forward
     std::vector<uint32_t> prof_mask;     // kernel slots recorded by each forward
     size_t prof_used = 0;                // forwards recorded
-    std::vector<AttnSchedDev> sched;     // attention schedules uploaded so far
+    // schedule sizes of the last shapes seen (host memory only; the tables live in the workspace)
+    static constexpr int kCountCache = 8;
+    struct CountEntry {
+        int64_t B = 0, S = 0;
+        AttnCounts c;
+    };
+    mutable CountEntry count_cache[kCountCache];
+    mutable int count_next = 0;
 };
 
 // Kernel timing slots, in launch order (GQE_PROF_KERNELS in gqe.h).
 enum {
     KT_ROUTER = 0, KT_ROUTER_STATS, KT_PROJ, KT_KEYNORM, KT_ATTN_PREP, KT_ATTN, KT_ATTN_MERGE, KT_COMBINE,
     KT_DEC_PROJ, KT_DEC_ATTN, KT_DEC_MERGE, KT_DEC_COMBINE,
-    KT_BWD_OUT, KT_BWD_ATTN, KT_BWD_WGRAD, KT_BWD_DX, KT_COUNT
+    KT_BWD_OUT, KT_BWD_ATTN, KT_BWD_WGRAD, KT_BWD_DX, KT_ATTN_SCHED, KT_COUNT
 };
 
 // Records events on the stream right before and right after each kernel a launcher enqueues
@@ -180,7 +230,11 @@ hipError_t launch_pack_router(const GqeDims& D, const float* w_router, const flo
 // sets the message gqe_last_error returns on this thread; returns code (GQE_OK clears it)
 int gqe_set_error(int code, const char* msg);
 
-WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S, int64_t attn_slots);
+WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S, const AttnCounts& ac);
+// Builds the attention schedule of P (jobs, merges) in the workspace on the stream.
+hipError_t launch_attn_sched(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st);
+// Scratch bytes the device schedule builder needs.
+size_t attn_sched_scratch_bytes(const AttnCounts& ac);
 hipError_t launch_kn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km);
 bool router_uses_mfma(const GqeDims& D);
 PackedLayout make_packed_layout(const GqeDims& D, bool mfma);
@@ -203,8 +257,7 @@ hipError_t launch_combine_simple(const GqeDims& D, const WorkPlan& P, const gqe_
 hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x,
                             const void* packed, const PackedLayout& pl, char* ws,
                             hipStream_t st, KernelMarks* km);
-hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, const AttnSchedDev& sc, char* ws, hipStream_t st,
-                            KernelMarks* km, bool prep);
+hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km, bool prep);
 int decode_units(const GqeDims& D);
 int decode_chunk(const GqeDims& D);
 hipError_t launch_kv_export(const GqeDims& D, const WorkPlan& P, const char* ws, void* kc, void* vc, int64_t s_max,

@@ -4,8 +4,9 @@
 // head attend to the group's dense, unchanged KV head.  A work item is (batch b, group g, block of
 // positions); its 256 query columns are all (position, head) pairs of the group's active heads, so
 // every K/V tile staged in LDS serves the k routed heads (+ the shared head for its group) at once.
-// A work group runs one job of the host-built schedule: an item, or a chunk of consecutive key
-// tiles of a long item (its unnormalised partial result is combined by attn_merge_kernel).
+// A work group runs one job of the schedule (built in the workspace by k_sched.hip): an item, or a
+// chunk of consecutive key tiles of a long item (its unnormalised partial result is combined by
+// attn_merge_kernel).
 //
 // Per wave: 64 query columns (two 32-column tiles), 64-key tiles.
 //   S^T = K Q^T     v_mfma_f32_32x32x16_bf16 (d_h = 48 needs no padding: 3 k-steps of 16).  The
@@ -217,7 +218,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
     const_i32_ptr jb = (const_i32_ptr)(a.jobs + 8 * (int64_t)blockIdx.x);
     const int ib = jb[0], ig = jb[1], NH = jb[2], p0 = jb[3], np = jb[4];
     const int kt0 = jb[5], kt_end = jb[6], part = jb[7];
-    if (kt_end <= kt0) return;  // padding of the schedule's XCD lists
+    if (kt_end <= kt0) return;  // an empty job does nothing
     const int S = (int)a.S;  // the host limits a call to 2^28 tokens
     const int last_pos = min(p0 + np, S) - 1;  // last query position of the item
 
@@ -616,14 +617,13 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(const int32_t* __restri
 
 }  // namespace
 
-hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, const AttnSchedDev& sc, char* ws, hipStream_t st,
-                            KernelMarks* km, bool prep) {
+hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km, bool prep) {
     AttnArgs a{};
     a.Q = (const bf16_t*)(ws + P.q);
     a.K = (const bf16_t*)(ws + P.kk);
     a.Vt = (const bf16_t*)(ws + P.vt);
     a.knt = (const float*)(ws + P.knt);
-    a.jobs = (const int32_t*)sc.jobs;
+    a.jobs = (const int32_t*)(ws + P.sched_jobs);
     a.O = (bf16_t*)(ws + P.o);
     a.part_o = (float*)(ws + P.part_o);
     a.part_ml = (float*)(ws + P.part_ml);
@@ -632,7 +632,7 @@ hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, const AttnSched
     a.G = D.G;
     a.H = D.H;
     a.k = D.k;
-    if (sc.njobs <= 0 || sc.nslots != P.nslots) return hipErrorInvalidValue;
+    if (P.ac.njobs <= 0) return hipErrorInvalidValue;
     if (prep) {
         const int64_t BG = P.B * D.G;
         const int64_t work = BG * (P.S_pad / 64) + BG * D.dh * (P.S_pad - P.S);
@@ -647,7 +647,7 @@ hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, const AttnSched
         if (e != hipSuccess) return e;
     }
     if (km) km->begin(KT_ATTN);
-    const unsigned grid = (unsigned)sc.njobs;
+    const unsigned grid = (unsigned)P.ac.njobs;
     switch (D.dh) {
         case 32: attn_fwd_kernel<32><<<grid, 256, 0, st>>>(a); break;
         case 48: attn_fwd_kernel<48><<<grid, 256, 0, st>>>(a); break;
@@ -655,14 +655,14 @@ hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, const AttnSched
         default: return hipErrorInvalidValue;
     }
     if (km) km->mark(KT_ATTN);
-    if (sc.nmerges > 0) {
+    if (P.ac.nmerges > 0) {
         {
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
         if (km) km->begin(KT_ATTN_MERGE);
-        const unsigned mgrid = (unsigned)sc.nmerges * 4;
-        const int32_t* mj = (const int32_t*)sc.merges;
+        const unsigned mgrid = (unsigned)P.ac.nmerges * 4;
+        const int32_t* mj = (const int32_t*)(ws + P.sched_merges);
         switch (D.dh) {
             case 32: attn_merge_kernel<32><<<mgrid, 256, 0, st>>>(mj, a.part_o, a.part_ml, a.O, P.S, D.G, D.H, D.k); break;
             case 48: attn_merge_kernel<48><<<mgrid, 256, 0, st>>>(mj, a.part_o, a.part_ml, a.O, P.S, D.G, D.H, D.k); break;

@@ -38,7 +38,7 @@ STAGES = ("router", "projection", "attention", "combine")
 # kernel timing slots of gqe_profile_read_kernels, in launch order
 KERNELS = ("router", "router_stats", "projection", "key_norms", "attention_prep", "attention", "attention_merge",
            "combine", "decode_projection", "decode_attention", "decode_merge", "decode_combine",
-           "backward_output", "backward_attention", "backward_weights", "backward_dx")
+           "backward_output", "backward_attention", "backward_weights", "backward_dx", "attention_schedule")
 GRAD_FIELDS = ("dx", "d_router", "d_router_bias", "d_q", "d_q_shared", "d_k", "d_v", "d_o", "d_o_rslot",
                "d_o_shared")
 
@@ -196,7 +196,7 @@ def gqe_aux_stats(h, n_experts: int, stream=None) -> dict:
 
 
 def gqe_workspace_layout(h, batch: int, seq: int):
-    offs = (ctypes.c_size_t * 10)()
+    offs = (ctypes.c_size_t * 12)()
     dims = (ctypes.c_int64 * 4)()
     _check(lib().gqe_workspace_layout(h, batch, seq, offs, dims))
     return list(offs), list(dims)
@@ -551,6 +551,8 @@ class GQEAttention:
             psel=view(offs[6], (T, self.G, self.k), torch.float32, 4),
             kn=view(offs[8], (batch, self.G, S_pad), torch.float32, 4),
             knt=view(offs[9], (batch, self.G, S_pad // 64), torch.float32, 4),
+            jobs=view(offs[10], (dims[3], 8), torch.int32, 4),
+            merges_offset=offs[11],
             matrix_core=bool(dims[2]),
         )
 

@@ -99,3 +99,48 @@ def test_long_items_are_split_at_16k():
     assert chunk > 0 and len(merges) > 0
     assert (jobs[:, 6] - jobs[:, 5]).max() < 256
 
+
+
+def _canonical(G, k, shared, skv, B, S, chunk):
+    """The dispatch order written out from its definition: templates (group, item, chunk) in that
+    order, sorted by key-tile count (longest first, ties keep template order), each repeated for
+    the B sequences; split items own B ss + b nc + c slots and merge record B mi + b."""
+    tpl, merges, ss, mi = [], [], 0, 0
+    for g in range(G):
+        nh = k + (1 if shared and g == skv else 0)
+        P = COLS // nh
+        for i in range((S + P - 1) // P):
+            p0, np_ = i * P, min(P, S - i * P)
+            kt = (p0 + np_ - 1) // TILE + 1
+            nc = 1 if chunk <= 0 or kt <= chunk else min(-(-kt // chunk), 32)
+            for c in range(nc):
+                tpl.append((g, nh, p0, np_, c * kt // nc, (c + 1) * kt // nc, nc, c, ss if nc > 1 else -1))
+            if nc > 1:
+                merges += [(b, g, nh, p0, np_, B * ss + b * nc, nc, 0) for b in range(B)]
+                ss += nc
+                mi += 1
+    order = sorted(range(len(tpl)), key=lambda t: (-(tpl[t][5] - tpl[t][4]), t))
+    jobs = []
+    for t in order:
+        g, nh, p0, np_, a, e, nc, c, s0 = tpl[t]
+        for b in range(B):
+            jobs.append((b, g, nh, p0, np_, a, e, B * s0 + b * nc + c if s0 >= 0 else -1))
+    return np.array(jobs, np.int32).reshape(-1, 8), np.array(merges, np.int32).reshape(-1, 8)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_schedule_follows_its_canonical_order(case):
+    """The tables equal the order written out from its definition (the device builder of every
+    forward writes the same tables; a GPU test compares them bit for bit)."""
+    c = dict(d=768, N=16, G=8, k=1, dh=48, shared=1, skv=0, dense=0, variant=0)
+    c.update(case)
+    B, S = c.pop("B"), c.pop("S")
+    h = _handle(**c)
+    try:
+        jobs, merges, nslots, chunk = gqe.gqe_attention_schedule(h, B, S)
+    finally:
+        gqe.gqe_destroy(h)
+    k = c["N"] // c["G"] if c["dense"] else c["k"]
+    ej, em = _canonical(c["G"], k, c["shared"] and not c["dense"], c["skv"], B, S, chunk)
+    np.testing.assert_array_equal(jobs, ej)
+    np.testing.assert_array_equal(merges.reshape(-1, 8), em)
