@@ -140,7 +140,7 @@ int gqe_pack_weights(gqe_handle_t* h, void* packed, size_t bytes, void* stream);
  * per-expert statistics, Q/K/V, head outputs, the attention work schedule and the float32
  * partial results of attention items that the schedule splits along the key range).
  * batch >= 1, seq >= 1, batch * seq <= 2^28.  Host only.  Errors: GQE_ERR_NULL_POINTER,
- * GQE_ERR_SHAPE, GQE_ERR_UNSUPPORTED (an attention work item longer than 8191 key tiles). */
+ * GQE_ERR_SHAPE. */
 int gqe_workspace_bytes(const gqe_handle_t* h, int64_t batch, int64_t seq, size_t* bytes);
 
 /* The forward pass y = GQE(x) (README "Usage": y = attn(x)).
@@ -155,7 +155,7 @@ int gqe_workspace_bytes(const gqe_handle_t* h, int64_t batch, int64_t seq, size_
  * Enqueues all kernels on `stream` and returns; no device allocation, no host-device copy, no
  * synchronisation (it may be captured in a HIP graph).  Requires gqe_pack_weights first (else
  * GQE_ERR_STATE).  Errors: NULL/misaligned pointers, GQE_ERR_SHAPE, GQE_ERR_WORKSPACE,
- * GQE_ERR_UNSUPPORTED, GQE_ERR_HIP (launch failure). */
+ * GQE_ERR_HIP (launch failure). */
 int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t seq,
                 void* workspace, size_t ws_bytes, void* stream, int32_t* route_idx,
                 float* route_w);
@@ -322,7 +322,8 @@ int gqe_backward(gqe_handle_t* h, const void* x, const void* dy, int64_t batch, 
  * and of gqe_backward:
  *   12 output-side gradients (dy W_slot^T, head outputs, router logits)   13 attention
  *   14 weight gradients     15 input gradient dx
- * and 16 the attention schedule builder of gqe_forward.
+ * and 16 the attention schedule builder of gqe_forward when it runs as a kernel of its own (the
+ * all-active GQA configuration; otherwise it runs inside the router launch, slot 0).
  * gqe_profile_read_kernels waits for the recorded events, returns the summed milliseconds per
  * kernel slot (0 for slots not launched) and the number of forwards they cover, and starts a new
  * accumulation.  gqe_profile_read does the same summed per stage (0 router = slots 0+1,

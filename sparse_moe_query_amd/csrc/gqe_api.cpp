@@ -196,11 +196,8 @@ static AttnCounts attn_counts_for(const gqe_handle* h, int64_t B, int64_t S) {
     return ac;
 }
 
-// The device schedule builder keeps per-length counters in LDS and the job index in 32 bits.
+// Job and slot numbers are 32-bit.
 static int attn_counts_supported(const AttnCounts& ac) {
-    if (ac.maxlen >= 8192)
-        return fail(GQE_ERR_UNSUPPORTED, "an attention work item of %d key tiles exceeds the schedule builder's 8191",
-                    ac.maxlen);
     if (ac.njobs > 0x7fffffff || ac.nslots > 0x7fffffff)
         return fail(GQE_ERR_SHAPE, "attention schedule of %lld jobs exceeds 2^31", (long long)ac.njobs);
     return GQE_OK;
@@ -384,15 +381,18 @@ int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t 
         if (rc != GQE_OK) return rc;
         km = &marks;
     }
-    // the attention schedule first: it depends only on the shape, and is built in the workspace
-    if (h->mfma_attn) {
+    // the attention schedule depends only on the shape and is built in the workspace: by the first
+    // work group of the router launch, or (no router: the all-active GQA baseline) by a kernel of
+    // its own
+    if (h->mfma_attn && D.dense) {
         if (km) km->begin(KT_ATTN_SCHED);
         e = launch_attn_sched(D, P, ws, st);
         if (km) km->mark(KT_ATTN_SCHED);
     }
     // with the matrix-core projection, its last work group finalizes the router statistics and
     // (S % 64 == 0) its key blocks write the per-tile key-norm maxima the attention reads
-    if (e == hipSuccess && !D.dense) e = launch_router(D, P, x, h->packed, h->pl, ws, route_idx, route_w, st, km, !h->mfma_proj);
+    if (e == hipSuccess && !D.dense)
+        e = launch_router(D, P, x, h->packed, h->pl, ws, route_idx, route_w, st, km, !h->mfma_proj, h->mfma_attn);
     if (e == hipSuccess)
         e = h->mfma_proj ? launch_proj_mfma(D, P, x, h->packed, h->pl, ws, st, km)
                          : launch_proj_simple(D, P, h->w, x, (const double*)((const char*)h->packed + h->pl.rope), ws, st,

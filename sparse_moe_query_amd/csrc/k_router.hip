@@ -19,6 +19,9 @@
 // four partial sums are added in a fixed order; two blocks fit one CU (68 KB of LDS each).
 // Generic path (any d, N <= 64): one token per lane, float64 FMAs with the weights as wave-uniform
 // scalar operands.
+// In the layer's forward the first work group of the launch builds the attention work schedule
+// instead (attn_sched_dev.h), overlapping the routing of the others.
+#include "attn_sched_dev.h"
 #include "gqe_common.h"
 #include "gqe_internal.h"
 #include "gqe_stats.h"
@@ -46,6 +49,10 @@ struct RouterArgs {
     float* rw;
     int32_t* part_cnt;
     double* part_psum;
+    // when set, work group 0 builds the attention schedule (its LDS: the reduction buffer) and
+    // work group b + 1 routes token block b
+    int sched_here;
+    SchedArgs sched;
 };
 
 template <typename Tin>
@@ -114,7 +121,7 @@ __device__ void select_one(const RouterArgs& a, double* l, int64_t tt, int g, in
 // The selection compares the float64 logits; the probabilities are formed from the float64
 // differences l - max with the float32 exponential (relative error ~1e-7), and overwrite the
 // logits of the same (token, group).  Per-block statistics follow.
-__device__ void select_and_stats(const RouterArgs& a, double (*lg)[65], int* cnt, int64_t t0, int nthreads) {
+__device__ void select_and_stats(const RouterArgs& a, double (*lg)[65], int* cnt, int64_t t0, int nthreads, int blk) {
     const int G = a.G;
     for (int q = threadIdx.x; q < kTok * G; q += nthreads) {
         const int tok = q / G, g = q % G;
@@ -139,8 +146,8 @@ __device__ void select_and_stats(const RouterArgs& a, double (*lg)[65], int* cnt
         const int e = threadIdx.x;
         double s = 0.0;
         for (int j = 0; j < kJ; ++j) s += gs[j][e];
-        a.part_psum[(int64_t)blockIdx.x * a.N + e] = s;
-        a.part_cnt[(int64_t)blockIdx.x * a.N + e] = cnt[e];
+        a.part_psum[(int64_t)blk * a.N + e] = s;
+        a.part_cnt[(int64_t)blk * a.N + e] = cnt[e];
     }
 }
 
@@ -150,9 +157,14 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(RouterArgs a) {
     __shared__ double red[kW][kTok][17];
     __shared__ double lg[kTok][65];
     __shared__ int cnt[64];
+    if (a.sched_here && blockIdx.x == 0) {
+        attn_sched_block<64 * kW>(a.sched, reinterpret_cast<unsigned char*>(&red[0][0][0]), (int)sizeof(red));
+        return;
+    }
+    const int blk = (int)blockIdx.x - a.sched_here;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t t0 = (int64_t)blockIdx.x * kTok;
+    const int64_t t0 = (int64_t)blk * kTok;
     if (threadIdx.x < 64) cnt[threadIdx.x] = 0;
 
     const int dq = a.d / kW;            // multiple of 8 (d % 64 == 0)
@@ -228,7 +240,7 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(RouterArgs a) {
         lg[tok][e] = v + a.br[e];
     }
     __syncthreads();
-    select_and_stats(a, lg, cnt, t0, 64 * kW);
+    select_and_stats(a, lg, cnt, t0, 64 * kW, blk);
 }
 
 template <typename Tin>
@@ -236,9 +248,14 @@ __global__ void __launch_bounds__(256) router_valu_kernel(RouterArgs a) {
     __shared__ double red[4][kTok][17];
     __shared__ double lg[kTok][65];
     __shared__ int cnt[64];
+    if (a.sched_here && blockIdx.x == 0) {
+        attn_sched_block<256>(a.sched, reinterpret_cast<unsigned char*>(&red[0][0][0]), (int)sizeof(red));
+        return;
+    }
+    const int blk = (int)blockIdx.x - a.sched_here;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t t0 = (int64_t)blockIdx.x * kTok;
+    const int64_t t0 = (int64_t)blk * kTok;
     const int64_t t = t0 + lane;
     const bool valid = t < a.T;
     if (threadIdx.x < 64) cnt[threadIdx.x] = 0;
@@ -265,7 +282,7 @@ __global__ void __launch_bounds__(256) router_valu_kernel(RouterArgs a) {
         }
         __syncthreads();
     }
-    select_and_stats(a, lg, cnt, t0, 256);
+    select_and_stats(a, lg, cnt, t0, 256, blk);
 }
 
 // One token per block (few tokens, e.g. a decode step): thread (expert column e, hidden slice)
@@ -366,7 +383,7 @@ hipError_t launch_router_tokens(const GqeDims& D, int64_t T, const void* x, cons
 
 hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, const void* packed,
                          const PackedLayout& pl, char* ws, int32_t* route_idx, float* route_w,
-                         hipStream_t st, KernelMarks* km, bool finalize) {
+                         hipStream_t st, KernelMarks* km, bool finalize, bool build_sched) {
     const char* pk = (const char*)packed;
     RouterArgs a{};
     a.x = x;
@@ -387,7 +404,9 @@ hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, con
     a.rw = route_w;
     a.part_cnt = (int32_t*)(ws + P.part_cnt);
     a.part_psum = (double*)(ws + P.part_psum);
-    const dim3 grid((unsigned)P.nblk_router);
+    a.sched_here = build_sched ? 1 : 0;
+    if (build_sched) a.sched = make_sched_args(D, P, ws);
+    const dim3 grid((unsigned)(P.nblk_router + a.sched_here));
     const bool bf = D.dtype == GQE_DTYPE_BF16;
     if (km) km->begin(KT_ROUTER);
     if (router_uses_mfma(D)) {
