@@ -160,6 +160,22 @@ int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t 
                 void* workspace, size_t ws_bytes, void* stream, int32_t* route_idx,
                 float* route_w);
 
+/* The same forward pass for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The workspace is not passed in:
+ * the library holds one static device array of GQE_STATIC_SCRATCH_BYTES (64 MiB) per GPU it runs
+ * on, until the process ends (enough for the main setting, 8 x 2048 tokens at d = 768, N = 16,
+ * G = 8, d_h = 48).  The caller still owns x, y and the routing outputs.  Allocates nothing, copies
+ * nothing, enqueues on `stream` and returns.  Every call on one GPU (any handle) shares that GPU's
+ * array, which keeps the last call's contents: gqe_aux_stats, gqe_bucket and gqe_kv_export of this
+ * handle read it until the next call on that GPU (gqe_backward needs the workspace of a
+ * gqe_forward); calls that overlap on one GPU race.
+ * Errors: as gqe_forward, and GQE_ERR_WORKSPACE when the shape needs more than
+ * GQE_STATIC_SCRATCH_BYTES (gqe_workspace_bytes tells), GQE_ERR_HIP when the array's device address
+ * cannot be looked up. */
+#define GQE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int gqe_forward_static(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t seq, void* stream,
+                       int32_t* route_idx, float* route_w);
+
 /* Load-balancing statistics of the last gqe_forward on this handle (README "Algorithm
  * Overview": Switch-style auxiliary loss; "Usage": loss = lm_loss + 0.01 *
  * collect_aux_loss(attn)).  Synchronises `stream`, then copies to host memory:

@@ -349,13 +349,25 @@ int gqe_workspace_layout(const gqe_handle_t* h, int64_t batch, int64_t seq, size
 
 int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t seq, void* workspace,
                 size_t ws_bytes, void* stream, int32_t* route_idx, float* route_w) {
-    if (!h || !x || !y || !workspace) return fail(GQE_ERR_NULL_POINTER, "handle, x, y and workspace must be non-NULL");
+    return gqe_forward_impl(h, x, y, batch, seq, workspace, ws_bytes, stream, route_idx, route_w, nullptr);
+}
+
+}  // extern "C"
+
+// The forward pass on a given workspace.  When ws_for is given, it is called after every
+// argument check with the workspace size the shape needs and returns the workspace to use (or
+// NULL, having set the error message and code).
+int gqe_forward_impl(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t seq, void* workspace,
+                     size_t ws_bytes, void* stream, int32_t* route_idx, float* route_w,
+                     void* (*ws_for)(size_t need, size_t* have, int* code)) {
+    if (!h || !x || !y || (!workspace && !ws_for))
+        return fail(GQE_ERR_NULL_POINTER, "handle, x, y and workspace must be non-NULL");
     if (!h->packed) return fail(GQE_ERR_STATE, "gqe_pack_weights must run before gqe_forward");
     if (batch < 1 || seq < 1 || batch * seq > ((int64_t)1 << 28))
         return fail(GQE_ERR_SHAPE, "batch and seq must be >= 1 with batch*seq <= 2^28 (got %lld x %lld)",
                     (long long)batch, (long long)seq);
     if (misaligned(x, 16) || misaligned(y, 16)) return fail(GQE_ERR_MISALIGNED, "x and y must be 16-byte aligned");
-    if (misaligned(workspace, 256)) return fail(GQE_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    if (workspace && misaligned(workspace, 256)) return fail(GQE_ERR_MISALIGNED, "workspace must be 256-byte aligned");
     if ((route_idx && misaligned(route_idx, 4)) || (route_w && misaligned(route_w, 4)))
         return fail(GQE_ERR_MISALIGNED, "routing outputs must be 4-byte aligned");
     const GqeDims& D = h->D;
@@ -370,6 +382,11 @@ int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t 
         if (rc != GQE_OK) return rc;
     }
     WorkPlan P = make_plan(D, batch, seq, ac);
+    if (ws_for) {
+        int code = GQE_ERR_WORKSPACE;
+        workspace = ws_for(P.total, &ws_bytes, &code);
+        if (!workspace) return code;   // ws_for set the message
+    }
     if (ws_bytes < P.total) return fail(GQE_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, P.total);
     hipStream_t st = (hipStream_t)stream;
     char* ws = (char*)workspace;
@@ -411,6 +428,8 @@ int gqe_forward(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t 
     h->last_plan = P;
     return ok();
 }
+
+extern "C" {
 
 int gqe_aux_stats(gqe_handle_t* h, void* stream, int64_t* counts, double* mean_prob, double* aux_loss,
                   int32_t* active_heads) {

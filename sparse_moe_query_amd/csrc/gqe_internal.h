@@ -229,6 +229,12 @@ hipError_t launch_pack_router(const GqeDims& D, const float* w_router, const flo
 
 // sets the message gqe_last_error returns on this thread; returns code (GQE_OK clears it)
 int gqe_set_error(int code, const char* msg);
+// gqe_forward with an optional workspace provider (called after the argument checks with the
+// bytes the shape needs; returns the workspace and its size, or NULL after setting the error
+// message and its code)
+int gqe_forward_impl(gqe_handle_t* h, const void* x, void* y, int64_t batch, int64_t seq, void* workspace,
+                     size_t ws_bytes, void* stream, int32_t* route_idx, float* route_w,
+                     void* (*ws_for)(size_t need, size_t* have, int* code));
 
 WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S, const AttnCounts& ac);
 // Builds the attention schedule of P (jobs, merges) in the workspace on the stream.

@@ -24,7 +24,7 @@ ERRORS = {0: "GQE_OK", -1: "GQE_ERR_INVALID_CONFIG", -2: "GQE_ERR_NULL_POINTER",
           -3: "GQE_ERR_MISALIGNED", -4: "GQE_ERR_UNSUPPORTED", -5: "GQE_ERR_WORKSPACE",
           -6: "GQE_ERR_SHAPE", -7: "GQE_ERR_HIP", -8: "GQE_ERR_STATE"}
 EXPORTS = ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights", "gqe_workspace_bytes",
-           "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_bucket", "gqe_profile_enable",
+           "gqe_forward", "gqe_forward_static", "gqe_aux_stats", "gqe_workspace_layout", "gqe_bucket", "gqe_profile_enable",
            "gqe_profile_read", "gqe_profile_read_kernels", "gqe_attention_schedule", "gqe_kv_export",
            "gqe_decode_workspace_bytes", "gqe_decode", "gqe_backward_workspace_bytes", "gqe_backward",
            "gqe_destroy", "gqe_last_error") + (
@@ -90,6 +90,7 @@ def lib():
         L.gqe_pack_weights.argtypes = [P, P, SZ, P]
         L.gqe_workspace_bytes.argtypes = [P, I64, I64, ctypes.POINTER(SZ)]
         L.gqe_forward.argtypes = [P, P, P, I64, I64, P, SZ, P, P, P]
+        L.gqe_forward_static.argtypes = [P, P, P, I64, I64, P, P, P]
         L.gqe_aux_stats.argtypes = [P, P, P, P, P, P]
         L.gqe_workspace_layout.argtypes = [P, I64, I64, P, P]
         L.gqe_bucket.argtypes = [P, P, P, P, P]
@@ -118,7 +119,7 @@ def lib():
         L.gqe_last_error.argtypes = []
         L.gqe_last_error.restype = ctypes.c_char_p
         for f in ("gqe_init", "gqe_packed_weights_bytes", "gqe_pack_weights",
-                  "gqe_workspace_bytes", "gqe_forward", "gqe_aux_stats", "gqe_workspace_layout", "gqe_bucket",
+                  "gqe_workspace_bytes", "gqe_forward", "gqe_forward_static", "gqe_aux_stats", "gqe_workspace_layout", "gqe_bucket",
                   "gqe_profile_enable", "gqe_profile_read", "gqe_profile_read_kernels",
                   "gqe_attention_schedule", "gqe_kv_export", "gqe_decode_workspace_bytes", "gqe_decode",
                   "gqe_backward_workspace_bytes", "gqe_backward", "gqe_moe_init", "gqe_moe_packed_weights_bytes",
@@ -177,6 +178,16 @@ def gqe_forward(h, x: torch.Tensor, y: torch.Tensor, batch: int, seq: int,
     _check(lib().gqe_forward(h, _ptr(x), _ptr(y), batch, seq, _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream),
                              _ptr(route_idx), _ptr(route_w)))
+
+
+def gqe_forward_static(h, x: torch.Tensor, y: torch.Tensor, batch: int, seq: int, stream=None,
+                       route_idx=None, route_w=None):
+    """The forward on the library's static per-GPU scratch (no workspace argument)."""
+    _check(lib().gqe_forward_static(h, _ptr(x), _ptr(y), batch, seq, _stream(stream), _ptr(route_idx),
+                                    _ptr(route_w)))
+
+
+STATIC_SCRATCH_BYTES = 64 << 20
 
 
 def gqe_bucket(h, offs: torch.Tensor, perm: torch.Tensor, inv: torch.Tensor, stream=None):
