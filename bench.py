@@ -380,11 +380,38 @@ def moe_report(steps: int, warmup: int) -> dict:
     return out
 
 
-def cpu_baseline(wl, min_seconds=10.0):
-    """The oracle as it stands, on whole sequences of the workload (all of their tokens), repeated
-    over the batch until at least ``min_seconds`` of CPU work have been timed."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_seconds(wl, b: int = 0) -> float:
+    """Wall-clock seconds of the oracle forward of sequence b of the workload (all its tokens;
+    input generation excluded)."""
     from oracle import gqe_oracle as go
     from sparse_moe_query_amd.inputs import make_inputs
+    inp = make_inputs(wl)
+    cfg = go.OracleConfig(wl.dim, wl.num_query_experts, wl.num_kv_heads, wl.top_k, wl.dh,
+                          wl.variant, wl.shared_head, wl.shared_kv_group)
+    x = inp["x"].reshape(wl.batch, wl.seq, wl.dim)
+    t0 = time.perf_counter()
+    go.forward(cfg, 1, wl.seq, x[b % wl.batch], inp)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(wl, min_seconds=10.0):
+    """The oracle as it stands, on whole sequences of the workload (all of their tokens), repeated
+    over the batch until at least ``min_seconds`` of CPU work have been timed; then the per-config
+    plan on bounded samples (one whole sequence per run): the tiny float32 layer as the median of 3
+    runs; the skewed k = 2 layer and each ablation variant once (a median of 3 at these lengths
+    would add minutes of CPU time to every run)."""
+    from oracle import gqe_oracle as go
+    from sparse_moe_query_amd.inputs import WORKLOADS, make_inputs
     inp = make_inputs(wl)
     cfg = go.OracleConfig(wl.dim, wl.num_query_experts, wl.num_kv_heads, wl.top_k, wl.dh,
                           wl.variant, wl.shared_head, wl.shared_kv_group)
@@ -398,9 +425,43 @@ def cpu_baseline(wl, min_seconds=10.0):
         done += wl.seq
         b += 1
     threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    plan = {}
+    for name, runs in (("tiny_fp32", 3), ("k2_skew_b4_s4096", 1), ("ablation_gqe_b2_s8192", 1),
+                       ("ablation_weighted_b2_s8192", 1), ("ablation_hard_b2_s8192", 1)):
+        w = WORKLOADS[name]
+        t = sorted(_oracle_seconds(w, r) for r in range(runs))[runs // 2]
+        plan[name] = dict(tokens_s=w.seq / t, seconds_per_sequence=t, runs=runs, seq=w.seq)
     return dict(value=done / elapsed, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"{b} whole sequences of the workload (seq {wl.seq}, all tokens, cycling over its "
-                       f"batch of {wl.batch}), fp64 plain loops, {elapsed:.1f} s")
+                       f"batch of {wl.batch}), fp64 plain loops, {elapsed:.1f} s",
+                cpu_model=cpu_model(), per_config=plan)
+
+
+def config_report(steps: int) -> dict:
+    """The skewed k = 2 layer and the three output variants of the ablation sweep, each timed as
+    the main workload is, beside the all-active GQA run of the same kernels on the same inputs
+    (the ablation variants share their weights, so one GQA run serves the three)."""
+    from sparse_moe_query_amd.inputs import WORKLOADS, gqa_of
+    out = {}
+    gqa_cache = {}
+    for name in ("k2_skew_b4_s4096", "ablation_gqe_b2_s8192", "ablation_weighted_b2_s8192", "ablation_hard_b2_s8192"):
+        wl = WORKLOADS[name]
+        log(f"[bench] {name}")
+        ms, kern, _ = run_workload(wl, steps, 2)
+        g = gqa_of(wl)
+        key = (g.dim, g.seed, g.batch, g.seq, g.head_dim, g.top_k)
+        if key not in gqa_cache:
+            log(f"[bench] {name} gqa")
+            gqa_cache[key] = run_workload(g, steps, 2)[:2]
+        g_ms, g_kern = gqa_cache[key]
+        a = algorithmic(wl)
+        at = a["attention"]["flops"] / (attn_step_ms(kern) * 1e-3) / 1e12
+        out[name] = dict(tokens_s=wl.tokens / (ms / 1e3), ms=ms, kernel_ms=kern, layer_gflop=a["layer_flops"] / 1e9,
+                         layer_tflops=a["layer_flops"] / (ms * 1e-3) / 1e12, attn_tflops=at,
+                         attn_frac_peak=at / PEAK_BF16, gqa_ms=g_ms, gqa_kernel_ms=g_kern,
+                         speedup_layer=g_ms / ms, speedup_attention=attn_step_ms(g_kern) / attn_step_ms(kern))
+        log(f"[bench] {name}: {ms:.3f} ms (GQA {g_ms:.3f} ms), attn {at:.0f} TFLOP/s")
+    return out
 
 
 def copy_calibration(nbytes=256 << 20, reps=3):
@@ -538,6 +599,8 @@ def main():
                               speedup_attention=attn_step_ms(g_kern) / attn_step_ms(l_kern))
             log(f"[bench] {name}: {l_ms:.3f} ms (GQA {g_ms:.3f} ms) attn {at:.0f} TFLOP/s")
         result["long_context"] = long
+    if not args.no_long and not args.only_main:
+        result["configs"] = config_report(max(5, args.steps // 3))
     if not args.no_decode and not args.only_main:
         result["decode"] = decode_report(max(10, args.steps), args.warmup)
     if not args.no_moe and not args.only_main:
