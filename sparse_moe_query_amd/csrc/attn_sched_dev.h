@@ -10,11 +10,12 @@
 //   1  per item of one sequence: its chunk count nc; exclusive scans give the first template of
 //      every item, its first partial slot (chunks of the split items before it) and its merge
 //      number (split items before it)
-//   2  per template: its item, and the sort key (longest first, then template number)
-//   3  bitonic sort of the keys (in LDS when they fit, else in the workspace)
-//   4  rank of every template = its position in the sorted keys
-//   5  per (template, sequence): its job record at B rank + b; per (split item, sequence): its
-//      merge record
+//   2  per template: its item, and the sort key (longest first)
+//   3  a stable radix sort of the template numbers by key (equal keys keep template order)
+//   4  per (sorted position p, sequence b): the job record of the template at p goes to B p + b;
+//      per (split item, sequence): its merge record
+// The per-item and per-template arrays live in LDS when they fit (the usual case), else in the
+// workspace.
 #pragma once
 
 #include "gqe_common.h"
@@ -23,22 +24,17 @@
 struct SchedArgs {
     AttnJob* jobs;
     AttnMerge* merges;
-    int32_t* tstart;   // [items + 1] first template of every item
-    int32_t* sstart;   // [items + 1] chunks of the split items before it (slots / B)
-    int32_t* mstart;   // [items + 1] split items before it (merges / B)
-    int32_t* tf;       // [tpl] item of every template
-    int32_t* rank;     // [tpl] dispatch rank of every template
-    uint64_t* gkeys;   // [npow2] sort keys when they do not fit in LDS
+    int32_t* gscratch;  // the same arrays as in LDS, when they do not fit there
     int64_t B, S;
-    int G, k, s, skv, C, items, tpl, maxlen, npow2;
+    int G, k, s, skv, C, items, tpl;
+    int nbits;         // bits of the longest template length (the sort key is maxlen - length)
+    int maxlen;
 };
 
-// Scratch bytes of the builder in the workspace (int32 prefix arrays, item and rank of every
-// template, sort keys).
-__host__ __device__ inline int sched_npow2(int tpl) {
-    int n = 2;
-    while (n < tpl) n <<= 1;
-    return n;
+// Bytes of the builder's arrays: tstart, sstart, mstart [items + 1], then tf, key, idx, tmp and
+// pre [tpl] (int32 each).
+__host__ __device__ inline size_t sched_array_bytes(int items, int tpl) {
+    return ((size_t)3 * (items + 1) + (size_t)5 * tpl) * 4;
 }
 
 namespace sched_dev {
@@ -96,28 +92,20 @@ __device__ void block_scan(int n, Ld ld, St st, int* lds_tot, int (&tot)[NV]) {
     }
 }
 
-}  // namespace sched_dev
-
-// The whole builder, by one work group of NT threads; lds: at least kHeader + 8 bytes of LDS
-// (keys live there when kHeader + 8 npow2 <= lds_bytes).
+// The builder on arrays at `arr` (LDS or workspace; the two instantiations keep the accesses in
+// their own address space).
 template <int NT>
-__device__ void attn_sched_block(const SchedArgs& a, unsigned char* lds, int lds_bytes) {
-    using namespace sched_dev;
-    int* goff = reinterpret_cast<int*>(lds);            // [65]
-    int* lds_tot = reinterpret_cast<int*>(lds) + 68;    // [NT / 64 * 3]
-    const bool keys_lds = kHeader + 8 * a.npow2 <= lds_bytes;
-    uint64_t* keys = keys_lds ? reinterpret_cast<uint64_t*>(lds + kHeader) : a.gkeys;
+__device__ __forceinline__ void build(const SchedArgs& a, int* goff, int* lds_tot, int32_t* arr) {
     const int tid = threadIdx.x;
     const int G = a.G;
-    if (tid == 0) {
-        int acc = 0;
-        for (int g = 0; g < G; ++g) {
-            goff[g] = acc;
-            acc += attn_items_of_group(a.S, attn_item_nh(g, a.k, a.s, a.skv));
-        }
-        goff[G] = acc;
-    }
-    __syncthreads();
+    int32_t* tstart = arr;
+    int32_t* sstart = tstart + (a.items + 1);
+    int32_t* mstart = sstart + (a.items + 1);
+    int32_t* tf = mstart + (a.items + 1);
+    int32_t* key = tf + a.tpl;
+    int32_t* idx = key + a.tpl;
+    int32_t* tmp = idx + a.tpl;
+    int32_t* pre = tmp + a.tpl;
     // item f -> group, geometry, chunk count
     auto item = [&](int f, int& g, int& nh, int& p0, int& np, int& kt, int& nc) {
         int lo = 0, hi = G - 1;  // the last group with goff[g] <= f
@@ -145,84 +133,114 @@ __device__ void attn_sched_block(const SchedArgs& a, unsigned char* lds, int lds
                 v[2] = nc > 1 ? 1 : 0;
             },
             [&](int f, int (&o)[3]) {
-                a.tstart[f] = o[0];
-                a.sstart[f] = o[1];
-                a.mstart[f] = o[2];
+                tstart[f] = o[0];
+                sstart[f] = o[1];
+                mstart[f] = o[2];
             },
             lds_tot, tot);
         if (tid == 0) {
-            a.tstart[a.items] = tot[0];
-            a.sstart[a.items] = tot[1];
-            a.mstart[a.items] = tot[2];
+            tstart[a.items] = tot[0];
+            sstart[a.items] = tot[1];
+            mstart[a.items] = tot[2];
         }
     }
     __threadfence_block();
     __syncthreads();
 
-    // ---- 2: the templates of every item and their sort keys (longest first, then number)
+    // ---- 2: the templates of every item: their item and sort key (longest first)
     for (int f = tid; f < a.items; f += NT) {
         int g, nh, p0, np, kt, nc;
         item(f, g, nh, p0, np, kt, nc);
-        const int t0 = a.tstart[f];
+        const int t0 = tstart[f];
         for (int c = 0; c < nc; ++c) {
             int k0, k1;
             attn_chunk_range(kt, nc, c, &k0, &k1);
-            a.tf[t0 + c] = f;
-            keys[t0 + c] = ((uint64_t)(uint32_t)(a.maxlen - (k1 - k0)) << 32) | (uint32_t)(t0 + c);
+            tf[t0 + c] = f;
+            key[t0 + c] = a.maxlen - (k1 - k0);
+            idx[t0 + c] = t0 + c;
         }
     }
-    for (int t = a.tpl + tid; t < a.npow2; t += NT) keys[t] = ~0ull;
     __threadfence_block();
     __syncthreads();
 
-    // ---- 3: bitonic sort, ascending
-    const int n = a.npow2;
-    for (int size = 2; size <= n; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < (n >> 1); i += NT) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const uint64_t x = keys[lo], y = keys[hi];
-                const bool up = (lo & size) == 0;
-                if ((x > y) == up) {
-                    keys[lo] = y;
-                    keys[hi] = x;
-                }
-            }
-            __threadfence_block();
-            __syncthreads();
+    // ---- 3: stable LSD radix sort of the template numbers by key, two bits per pass (a stable
+    // four-way split: a block scan of the digit flags, then a scatter)
+    for (int shift = 0; shift < a.nbits; shift += 2) {
+        int tot[4];
+        block_scan<NT, 4>(
+            a.tpl,
+            [&](int i, int (&v)[4]) {
+                const int dgt = (key[idx[i]] >> shift) & 3;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = dgt == q ? 1 : 0;
+            },
+            [&](int i, int (&o)[4]) {
+                const int dgt = (key[idx[i]] >> shift) & 3;
+                pre[i] = dgt == 0 ? o[0] : dgt == 1 ? o[1] : dgt == 2 ? o[2] : o[3];
+            },
+            lds_tot, tot);
+        const int s1 = tot[0], s2 = s1 + tot[1], s3 = s2 + tot[2];
+        for (int i = tid; i < a.tpl; i += NT) {
+            const int t = idx[i];
+            const int dgt = (key[t] >> shift) & 3;
+            tmp[(dgt == 0 ? 0 : dgt == 1 ? s1 : dgt == 2 ? s2 : s3) + pre[i]] = t;
         }
+        __threadfence_block();
+        __syncthreads();
+        int32_t* x = idx;
+        idx = tmp;
+        tmp = x;
     }
 
-    // ---- 4: ranks
-    for (int p = tid; p < a.tpl; p += NT) a.rank[(uint32_t)keys[p]] = p;
-    __threadfence_block();
-    __syncthreads();
-
-    // ---- 5: job records (template t, sequence b) -> position B rank + b; merge records
-    const int64_t B = a.B;
-    const int64_t nj = B * a.tpl;
-    for (int64_t j = tid; j < nj; j += NT) {
-        const int t = (int)(j / B);
-        const int b = (int)(j - (int64_t)t * B);
-        const int f = a.tf[t];
+    // ---- 4: job records (sorted position p, sequence b) -> B p + b; merge records
+    const int B = (int)a.B;   // B tpl < 2^31 (checked on the host)
+    const int nj = B * a.tpl;
+    for (int j = tid; j < nj; j += NT) {
+        const int p = j / B;
+        const int b = j - p * B;
+        const int t = idx[p];
+        const int f = tf[t];
         int g, nh, p0, np, kt, nc;
         item(f, g, nh, p0, np, kt, nc);
-        const int c = t - a.tstart[f];
+        const int c = t - tstart[f];
         int k0, k1;
         attn_chunk_range(kt, nc, c, &k0, &k1);
-        const int part = nc > 1 ? (int)(B * a.sstart[f] + (int64_t)b * nc + c) : -1;
-        a.jobs[B * a.rank[t] + b] = AttnJob{b, g, nh, p0, np, k0, k1, part};
+        const int part = nc > 1 ? B * sstart[f] + b * nc + c : -1;
+        a.jobs[j] = AttnJob{b, g, nh, p0, np, k0, k1, part};
     }
-    const int64_t nm = B * a.items;
-    for (int64_t j = tid; j < nm; j += NT) {
-        const int f = (int)(j / B);
-        const int b = (int)(j - (int64_t)f * B);
+    const int nm = B * a.items;
+    for (int j = tid; j < nm; j += NT) {
+        const int f = j / B;
+        const int b = j - f * B;
         int g, nh, p0, np, kt, nc;
         item(f, g, nh, p0, np, kt, nc);
         if (nc <= 1) continue;
-        a.merges[B * a.mstart[f] + b] = AttnMerge{b, g, nh, p0, np, (int)(B * a.sstart[f] + (int64_t)b * nc), nc, 0};
+        a.merges[B * mstart[f] + b] = AttnMerge{b, g, nh, p0, np, B * sstart[f] + b * nc, nc, 0};
     }
+}
+
+}  // namespace sched_dev
+
+// The whole builder, by one work group of NT threads; lds: LDS scratch of lds_bytes (the
+// arrays live there when kHeader + their bytes fit).
+template <int NT>
+__device__ __forceinline__ void attn_sched_block(const SchedArgs& a, unsigned char* lds, int lds_bytes) {
+    using namespace sched_dev;
+    int* goff = reinterpret_cast<int*>(lds);            // [65]
+    int* lds_tot = reinterpret_cast<int*>(lds) + 68;    // [NT / 64 * 3]
+    if (threadIdx.x < 64) {
+        // lane g: the items of group g; the wave's exclusive scan gives the first item of each
+        const int g = threadIdx.x;
+        const int cnt = g < a.G ? attn_items_of_group(a.S, attn_item_nh(g, a.k, a.s, a.skv)) : 0;
+        const int inc = sched_dev::wave_incl_scan(cnt, g);
+        if (g < a.G) goff[g] = inc - cnt;
+        if (g == a.G - 1) goff[a.G] = inc;
+    }
+    __syncthreads();
+    if ((size_t)kHeader + sched_array_bytes(a.items, a.tpl) <= (size_t)lds_bytes)
+        build<NT>(a, goff, lds_tot, reinterpret_cast<int32_t*>(lds + kHeader));
+    else
+        build<NT>(a, goff, lds_tot, a.gscratch);
 }
 
 // Host: the builder's arguments for the forward of plan P (workspace ws).

@@ -399,9 +399,9 @@ int gqe_forward_impl(gqe_handle_t* h, const void* x, void* y, int64_t batch, int
         km = &marks;
     }
     // the attention schedule depends only on the shape and is built in the workspace: by the first
-    // work group of the router launch, or (no router: the all-active GQA baseline) by a kernel of
-    // its own
-    if (h->mfma_attn && D.dense) {
+    // work group of the matrix-core projection launch, overlapping the projections, or else by a
+    // kernel of its own
+    if (h->mfma_attn && !h->mfma_proj) {
         if (km) km->begin(KT_ATTN_SCHED);
         e = launch_attn_sched(D, P, ws, st);
         if (km) km->mark(KT_ATTN_SCHED);
@@ -409,9 +409,9 @@ int gqe_forward_impl(gqe_handle_t* h, const void* x, void* y, int64_t batch, int
     // with the matrix-core projection, its last work group finalizes the router statistics and
     // (S % 64 == 0) its key blocks write the per-tile key-norm maxima the attention reads
     if (e == hipSuccess && !D.dense)
-        e = launch_router(D, P, x, h->packed, h->pl, ws, route_idx, route_w, st, km, !h->mfma_proj, h->mfma_attn);
+        e = launch_router(D, P, x, h->packed, h->pl, ws, route_idx, route_w, st, km, !h->mfma_proj);
     if (e == hipSuccess)
-        e = h->mfma_proj ? launch_proj_mfma(D, P, x, h->packed, h->pl, ws, st, km)
+        e = h->mfma_proj ? launch_proj_mfma(D, P, x, h->packed, h->pl, ws, st, km, h->mfma_attn)
                          : launch_proj_simple(D, P, h->w, x, (const double*)((const char*)h->packed + h->pl.rope), ws, st,
                                               km);
     if (e == hipSuccess && !h->mfma_proj && h->mfma_attn) e = launch_kn_simple(D, P, ws, st, km);

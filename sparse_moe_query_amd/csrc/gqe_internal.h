@@ -67,24 +67,26 @@ struct AttnMerge {
 __host__ __device__ inline int attn_item_nh(int g, int k, int s, int skv) { return k + ((s && g == skv) ? 1 : 0); }
 __host__ __device__ inline int attn_items_of_group(int64_t S, int nh) {
     const int P = GQE_ATTN_COLS / nh;
-    return (int)((S + P - 1) / P);
+    return ((int)S + P - 1) / P;  // S < 2^28: 32-bit arithmetic (no 64-bit division on the device)
 }
+// positions are below 2^28, so the item geometry fits int
 __host__ __device__ inline int attn_item_tiles(int64_t S, int nh, int i, int* p0, int* np) {
     const int P = GQE_ATTN_COLS / nh;
-    const int64_t a = (int64_t)i * P;
-    const int64_t n = S - a < P ? S - a : P;
-    *p0 = (int)a;
-    *np = (int)n;
-    return (int)((a + n - 1) / GQE_KV_TILE + 1);
+    const int a = i * P;
+    const int n = (int)S - a < P ? (int)S - a : P;
+    *p0 = a;
+    *np = n;
+    return (a + n - 1) / GQE_KV_TILE + 1;
 }
 __host__ __device__ inline int attn_chunks_of(int kt, int C) {
     if (C <= 0 || kt <= C) return 1;
     const int nc = (kt + C - 1) / C;
     return nc < GQE_ATTN_MAX_CHUNKS ? nc : GQE_ATTN_MAX_CHUNKS;
 }
+// (c + 1) kt < 2^31: c < 32 chunks and kt <= 2^22 key tiles (at most 2^28 positions)
 __host__ __device__ inline void attn_chunk_range(int kt, int nc, int c, int* kt0, int* kt1) {
-    *kt0 = (int)((int64_t)c * kt / nc);
-    *kt1 = (int)((int64_t)(c + 1) * kt / nc);
+    *kt0 = c * kt / nc;
+    *kt1 = (c + 1) * kt / nc;
 }
 
 // Sizes of the schedule of a [B, S] forward (a pure function of the config, B and S).
@@ -250,7 +252,7 @@ hipError_t launch_pack(const GqeDims& D, const gqe_weights_t& w, const PackedLay
                        void* packed, bool mfma, hipStream_t st);
 hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, const void* packed,
                          const PackedLayout& pl, char* ws, int32_t* route_idx, float* route_w,
-                         hipStream_t st, KernelMarks* km, bool finalize, bool build_sched = false);
+                         hipStream_t st, KernelMarks* km, bool finalize);
 // Router for a handful of tokens (one block per token; no balance statistics).
 hipError_t launch_router_tokens(const GqeDims& D, int64_t T, const void* x, const void* packed,
                                 const PackedLayout& pl, int32_t* idx, float* wsel, float* psel, int32_t* route_idx,
@@ -260,9 +262,10 @@ hipError_t launch_proj_simple(const GqeDims& D, const WorkPlan& P, const gqe_wei
 hipError_t launch_attn_simple(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km);
 hipError_t launch_combine_simple(const GqeDims& D, const WorkPlan& P, const gqe_weights_t& w,
                                  void* y, char* ws, hipStream_t st, KernelMarks* km);
+// build_sched: the launch's first work group also builds the attention schedule
 hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x,
                             const void* packed, const PackedLayout& pl, char* ws,
-                            hipStream_t st, KernelMarks* km);
+                            hipStream_t st, KernelMarks* km, bool build_sched);
 hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipStream_t st, KernelMarks* km, bool prep);
 int decode_units(const GqeDims& D);
 int decode_chunk(const GqeDims& D);

@@ -21,6 +21,7 @@
 //   epilogue   queries are stored multiplied by log2(e)/sqrt(d_h) (the attention scale, folded in
 //              before the single rounding to bf16); every key's norm is stored for the attention
 //              kernel's range test
+#include "attn_sched_dev.h"
 #include "gqe_common.h"
 #include "gqe_internal.h"
 #include "gqe_stats.h"
@@ -50,6 +51,9 @@ struct ProjArgs {
     const double* part_psum;
     char* stats;
     int64_t nblk_router;
+    // when set, work group 0 builds the attention work schedule and work group L + 1 runs job L
+    int sched_here;
+    SchedArgs sched;
 };
 
 // Element offset of (row, 16-byte chunk c) in an LDS stage of [rows][64] bf16 whose chunks are
@@ -88,8 +92,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
     constexpr int CB = DH / 16;
     constexpr int LX = kBM * kKC * 2 / 1024 / 4;       // 1 KB x segments per wave per stage
     constexpr int LW = 4 * DH * kKC * 2 / 1024 / 4;    // 1 KB weight segments per wave per stage
-    __shared__ __align__(1024) uint16_t xs[2][kBM * kKC];
-    __shared__ __align__(1024) uint16_t wls[2][4 * DH * kKC];
+    // one LDS buffer: two x stages and two weight stages (or, in the schedule-building work
+    // group, the builder's arrays)
+    __shared__ __align__(1024) uint16_t lds_all[2 * kBM * kKC + 2 * 4 * DH * kKC];
+    if (a.sched_here && blockIdx.x == 0) {
+        attn_sched_block<256>(a.sched, reinterpret_cast<unsigned char*>(lds_all), (int)sizeof(lds_all));
+        return;
+    }
+    uint16_t (*xs)[kBM * kKC] = reinterpret_cast<uint16_t (*)[kBM * kKC]>(lds_all);
+    uint16_t (*wls)[4 * DH * kKC] = reinterpret_cast<uint16_t (*)[4 * DH * kKC]>(lds_all + 2 * kBM * kKC);
     // per wave: gathered tile rows (| rank << 8); lives in x stage 1 until the first slice is
     // loaded into it (each lane keeps the entries it needs in registers)
     uint16_t (*rows)[kBM] = reinterpret_cast<uint16_t (*)[kBM]>(&xs[1][0]);
@@ -97,7 +108,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     // XCD-aware order: the items of one token tile run on one XCD so its x tile stays in L2
-    const int L = blockIdx.x;
+    const int L = (int)blockIdx.x - a.sched_here;
     int tile, job;
     if (a.ntiles % 8 == 0) {
         const int xcd = L % 8, i = L / 8;
@@ -309,7 +320,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
 }  // namespace
 
 hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x, const void* packed,
-                            const PackedLayout& pl, char* ws, hipStream_t st, KernelMarks* km) {
+                            const PackedLayout& pl, char* ws, hipStream_t st, KernelMarks* km, bool build_sched) {
     ProjArgs a{};
     a.x = (const bf16_t*)x;
     a.wproj = (const bf16_t*)((const char*)packed + pl.wproj);
@@ -342,7 +353,9 @@ hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x, 
     a.njobs = (a.HB + 3) / 4;
     a.ntiles = (int)ceil_div(P.T, kBM);
     if (D.d % kKC != 0) return hipErrorInvalidValue;
-    const unsigned grid = (unsigned)((int64_t)a.ntiles * a.njobs);
+    a.sched_here = build_sched ? 1 : 0;
+    if (build_sched) a.sched = make_sched_args(D, P, ws);
+    const unsigned grid = (unsigned)((int64_t)a.ntiles * a.njobs + a.sched_here);
     if (km) km->begin(KT_PROJ);
     switch (D.dh) {
         case 32: proj_kernel<32><<<grid, 256, 0, st>>>(a); break;

@@ -19,9 +19,6 @@
 // four partial sums are added in a fixed order; two blocks fit one CU (68 KB of LDS each).
 // Generic path (any d, N <= 64): one token per lane, float64 FMAs with the weights as wave-uniform
 // scalar operands.
-// In the layer's forward the first work group of the launch builds the attention work schedule
-// instead (attn_sched_dev.h), overlapping the routing of the others.
-#include "attn_sched_dev.h"
 #include "gqe_common.h"
 #include "gqe_internal.h"
 #include "gqe_stats.h"
@@ -49,10 +46,6 @@ struct RouterArgs {
     float* rw;
     int32_t* part_cnt;
     double* part_psum;
-    // when set, work group 0 builds the attention schedule (its LDS: the reduction buffer) and
-    // work group b + 1 routes token block b
-    int sched_here;
-    SchedArgs sched;
 };
 
 template <typename Tin>
@@ -157,11 +150,7 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(RouterArgs a) {
     __shared__ double red[kW][kTok][17];
     __shared__ double lg[kTok][65];
     __shared__ int cnt[64];
-    if (a.sched_here && blockIdx.x == 0) {
-        attn_sched_block<64 * kW>(a.sched, reinterpret_cast<unsigned char*>(&red[0][0][0]), (int)sizeof(red));
-        return;
-    }
-    const int blk = (int)blockIdx.x - a.sched_here;
+    const int blk = (int)blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t t0 = (int64_t)blk * kTok;
@@ -248,11 +237,7 @@ __global__ void __launch_bounds__(256) router_valu_kernel(RouterArgs a) {
     __shared__ double red[4][kTok][17];
     __shared__ double lg[kTok][65];
     __shared__ int cnt[64];
-    if (a.sched_here && blockIdx.x == 0) {
-        attn_sched_block<256>(a.sched, reinterpret_cast<unsigned char*>(&red[0][0][0]), (int)sizeof(red));
-        return;
-    }
-    const int blk = (int)blockIdx.x - a.sched_here;
+    const int blk = (int)blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t t0 = (int64_t)blk * kTok;
@@ -383,7 +368,7 @@ hipError_t launch_router_tokens(const GqeDims& D, int64_t T, const void* x, cons
 
 hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, const void* packed,
                          const PackedLayout& pl, char* ws, int32_t* route_idx, float* route_w,
-                         hipStream_t st, KernelMarks* km, bool finalize, bool build_sched) {
+                         hipStream_t st, KernelMarks* km, bool finalize) {
     const char* pk = (const char*)packed;
     RouterArgs a{};
     a.x = x;
@@ -404,9 +389,7 @@ hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, con
     a.rw = route_w;
     a.part_cnt = (int32_t*)(ws + P.part_cnt);
     a.part_psum = (double*)(ws + P.part_psum);
-    a.sched_here = build_sched ? 1 : 0;
-    if (build_sched) a.sched = make_sched_args(D, P, ws);
-    const dim3 grid((unsigned)(P.nblk_router + a.sched_here));
+    const dim3 grid((unsigned)P.nblk_router);
     const bool bf = D.dtype == GQE_DTYPE_BF16;
     if (km) km->begin(KT_ROUTER);
     if (router_uses_mfma(D)) {

@@ -6,7 +6,7 @@
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kLds = sched_dev::kHeader + 8 * 8192;
+constexpr int kLds = sched_dev::kHeader + 64 * 1024;
 
 __global__ void __launch_bounds__(kThreads) attn_sched_kernel(SchedArgs a) {
     __shared__ __align__(16) unsigned char lds[kLds];
@@ -15,24 +15,14 @@ __global__ void __launch_bounds__(kThreads) attn_sched_kernel(SchedArgs a) {
 
 }  // namespace
 
-size_t attn_sched_scratch_bytes(const AttnCounts& ac) {
-    return (size_t)(3 * (ac.items + 1) + 2 * ac.tpl) * 4 + 64 + (size_t)sched_npow2(ac.tpl) * 8;
-}
+size_t attn_sched_scratch_bytes(const AttnCounts& ac) { return sched_array_bytes(ac.items, ac.tpl) + 64; }
 
 SchedArgs make_sched_args(const GqeDims& D, const WorkPlan& P, char* ws) {
     const AttnCounts& ac = P.ac;
     SchedArgs a{};
     a.jobs = (AttnJob*)(ws + P.sched_jobs);
     a.merges = (AttnMerge*)(ws + P.sched_merges);
-    int32_t* sc = (int32_t*)(ws + P.sched_scratch);
-    a.tstart = sc;
-    a.sstart = a.tstart + (ac.items + 1);
-    a.mstart = a.sstart + (ac.items + 1);
-    a.tf = a.mstart + (ac.items + 1);
-    a.rank = a.tf + ac.tpl;
-    // 8-byte aligned keys after the int32 arrays
-    const size_t koff = ((size_t)(3 * (ac.items + 1) + 2 * ac.tpl) * 4 + 63) & ~(size_t)63;
-    a.gkeys = (uint64_t*)(ws + P.sched_scratch + koff);
+    a.gscratch = (int32_t*)(ws + P.sched_scratch);
     a.B = P.B;
     a.S = P.S;
     a.G = D.G;
@@ -43,7 +33,9 @@ SchedArgs make_sched_args(const GqeDims& D, const WorkPlan& P, char* ws) {
     a.items = ac.items;
     a.tpl = ac.tpl;
     a.maxlen = ac.maxlen;
-    a.npow2 = sched_npow2(ac.tpl);
+    int nb = 1;
+    while ((1 << nb) <= ac.maxlen) ++nb;
+    a.nbits = nb;
     return a;
 }
 
