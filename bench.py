@@ -95,6 +95,21 @@ def committed_traffic(kernel: str, workload: str, source: str | None = None):
     return float(m_bytes.group(1))
 
 
+def committed_mfma_busy(kernel: str, workload: str):
+    """Measured matrix-core busy fraction of ``kernel`` on ``workload`` (SQ_VALU_MFMA_BUSY_CYCLES over
+    the SIMDs' active cycles) from profiles/counters_<kernel>_<workload>.md, if that summary was taken
+    on the current source."""
+    path = os.path.join(ROOT, "profiles", f"counters_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source hash:\s*([0-9a-f]+)", text)
+    m_busy = re.search(r"mfma_busy:\s*([0-9.eE+-]+)", text)
+    if not m_hash or not m_busy or m_hash.group(1) != source_hash(KERNEL_SOURCES[kernel][0]):
+        return None
+    return float(m_busy.group(1))
+
+
 def run_workload(wl, steps, warmup, profile=True):
     import torch
     from sparse_moe_query_amd import gqe
@@ -551,6 +566,8 @@ def main():
     kernels = {k: roofline(k, kernel_ms[k], alg, main_wl.name, mrg(k)) for k in KERNEL_SOURCES if kernel_ms.get(k, 0) > 0}
     kernels = {k: {kk: v[kk] for kk in ("kernel_ms", "achieved", "frac", "algorithmic_hbm_frac", "traffic")}
                for k, v in kernels.items()}
+    for k in kernels:
+        kernels[k]["mfma_busy"] = committed_mfma_busy(k, main_wl.name)
 
     result = {
         "metric": "GQE prefill tokens/s + attn TFLOP/s (% MFMA peak), d=768 N=16 G=8 k=1",
@@ -594,6 +611,7 @@ def main():
             gat = ga["attention"]["flops"] / (attn_step_ms(g_kern) * 1e-3) / 1e12
             long[name] = dict(tokens_s=wl.tokens / (l_ms / 1e3), ms=l_ms, kernel_ms=l_kern,
                               attn_tflops=at, attn_frac_peak=at / PEAK_BF16,
+                              attn_mfma_busy=committed_mfma_busy("attention", name),
                               gqa_ms=g_ms, gqa_kernel_ms=g_kern, gqa_attn_tflops=gat,
                               speedup_layer=g_ms / l_ms,
                               speedup_attention=attn_step_ms(g_kern) / attn_step_ms(l_kern))
