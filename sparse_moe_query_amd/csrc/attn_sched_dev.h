@@ -39,7 +39,9 @@ __host__ __device__ inline size_t sched_array_bytes(int items, int tpl) {
 
 namespace sched_dev {
 
-constexpr int kHeader = 512;  // LDS bytes for the group offsets and the scan's wave totals
+// LDS bytes for the group offsets (ints [0, 65)) and the scan's wave totals (ints [68, 68 + 4 NT/64),
+// up to 1024 threads)
+constexpr int kHeader = 1024;
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
@@ -227,7 +229,8 @@ template <int NT>
 __device__ __forceinline__ void attn_sched_block(const SchedArgs& a, unsigned char* lds, int lds_bytes) {
     using namespace sched_dev;
     int* goff = reinterpret_cast<int*>(lds);            // [65]
-    int* lds_tot = reinterpret_cast<int*>(lds) + 68;    // [NT / 64 * 3]
+    static_assert(68 + 4 * (NT / 64) <= kHeader / 4, "scan totals must fit the header");
+    int* lds_tot = reinterpret_cast<int*>(lds) + 68;    // [NT / 64 * 4]
     if (threadIdx.x < 64) {
         // lane g: the items of group g; the wave's exclusive scan gives the first item of each
         const int g = threadIdx.x;

@@ -1,5 +1,5 @@
-// Final reduction of the router's per-block expert statistics (one 256-thread block; LDS scratch
-// passed in): counts, mean in-group probability, and the Switch-style balance loss.
+// Final reduction of the router's per-block expert statistics (one work group of at least 256
+// threads, all of which call it; LDS scratch passed in: ps and pc 256 entries each, fp 64): counts, mean in-group probability, and the Switch-style balance loss.
 //
 // GQE README "Algorithm Overview": a Switch-style load-balancing auxiliary loss.  With T tokens
 // and k choices per group: f_e = count_e / (T k), P_e = (1/T) sum_t p_e(t), per group
@@ -18,17 +18,20 @@ __device__ __forceinline__ void stats_finalize_block(const int32_t* __restrict__
     double* mean = reinterpret_cast<double*>(stats + 8 * N);
     double* aux = reinterpret_cast<double*>(stats + 16 * N);
     const int J = 256 / N;
+    const bool mine = threadIdx.x < 256;  // larger work groups: the other threads only meet the barriers
     const int e = threadIdx.x % N, j = threadIdx.x / N;
     double s = 0.0;
     int64_t c = 0;
-    if (j < J) {
+    if (mine && j < J) {
         for (int64_t b = j; b < nblk; b += J) {
             c += part_cnt[b * N + e];
             s += part_psum[b * N + e];
         }
     }
-    ps[threadIdx.x] = s;
-    pc[threadIdx.x] = c;
+    if (mine) {
+        ps[threadIdx.x] = s;
+        pc[threadIdx.x] = c;
+    }
     __syncthreads();
     if (threadIdx.x < N) {
         double tot = 0.0;

@@ -4,20 +4,25 @@
 // group), the always-on shared query head is dense, and only the selected query-head experts are
 // computed.  All of them read the same token rows, so one kernel does them all:
 //
-//   work item = (tile of 128 tokens, 4 head blocks); head block = d_h output columns of one of
-//               K_g, V_g, the shared query head, or routed expert e; one wave per head block
-//   pipeline   per 64-wide slice of the hidden dimension, the x tile (128 x 64) and the four head
+//   work item = (tile of 256 tokens, 4 head blocks); head block = d_h output columns of one of
+//               K_g, V_g, the shared query head, or routed expert e.  Eight waves: wave w computes
+//               head block w & 3 on half w >> 2 of the head block's rows
+//   pipeline   per 64-wide slice of the hidden dimension, the x tile (256 x 64) and the four head
 //              blocks' weights (4 d_h x 64, pre-transposed by gqe_pack_weights) go straight from
 //              global memory into LDS (global_load_lds_dwordx4 into XOR-swizzled 16-byte chunks,
 //              so fragment reads are bank-conflict free); two LDS stages, the next slice in
-//              flight while the current one multiplies; the x tile is shared by the four waves
-//   routed     tile-local token-to-expert bucketing: for its expert e the wave scans the tile's
-//              routing decisions with a ballot (histogram = popcount, exclusive prefix = masked
-//              popcount) and gathers the matching rows into a contiguous LDS slice; only those
-//              rows are multiplied (no capacity, no dropped tokens; empty slices do no work)
-//   products   v_mfma_f32_16x16x32_bf16 computing C^T = W^T x^T, one straight-line body for every
-//              wave; each lane ends with four consecutive head-dim values of one token (K/Q rows
-//              are stored as 8-byte vectors, V goes to V^T [dim][key], keys slotted by vt_pos)
+//              flight while the current one multiplies.  The x tile is shared by the eight waves
+//              and each head block's weights by two, so a 256-token tile halves the global reads
+//              per product of a 128-token one
+//   rows       a dense head block's rows are the tile's tokens, 128 per wave.  A routed expert's
+//              rows are the tile's tokens routed to it: tile-local bucketing scans the routing
+//              decisions with a ballot (histogram = popcount, exclusive prefix = masked popcount)
+//              into a contiguous row list, split between the head block's two waves in whole
+//              16-row blocks.  A wave multiplies only the 16-row blocks that hold rows (no
+//              capacity, no dropped tokens; an expert with no rows in the tile does no products)
+//   products   v_mfma_f32_16x16x32_bf16 computing C^T = W^T x^T; each lane ends with four
+//              consecutive head-dim values of one token (K/Q rows are stored as 8-byte vectors,
+//              V goes to V^T [dim][key], keys slotted by vt_pos)
 //   epilogue   queries are stored multiplied by log2(e)/sqrt(d_h) (the attention scale, folded in
 //              before the single rounding to bf16); every key's norm is stored for the attention
 //              kernel's range test
@@ -28,8 +33,9 @@
 
 namespace {
 
-constexpr int kBM = 128;   // tokens per tile
+constexpr int kBM = 256;   // tokens per tile
 constexpr int kKC = 64;    // hidden-dim slice per LDS stage (8 chunks of 16 bytes per row)
+constexpr int kWaves = 8;  // wave w: head block w & 3 of the item, row half w >> 2
 
 struct ProjArgs {
     const bf16_t* x;
@@ -62,13 +68,13 @@ struct ProjArgs {
 // distinct bank groups.
 __device__ __forceinline__ int swz64(int row, int c) { return (row * 8 + (c ^ ((row >> 1) & 7))) * 8; }
 
-// One 64-wide slice of the hidden dimension for one wave: C^T += W^T x^T over the eight row
-// blocks myrow[] of the x stage and the wave's d_h weight rows.  Every wave runs this same
-// straight-line body (routed slices too, on their gathered rows; padding rows are not stored),
-// so the accumulators stay in place across the loop.
-template <int DH>
+// One 64-wide slice of the hidden dimension for one wave: C^T += W^T x^T over the row blocks
+// xrow[] of the x stage and the wave's d_h weight rows.  FULL: all eight row blocks hold rows
+// (straight-line body); otherwise only the first nrb (wave-uniform) are multiplied.  The
+// accumulators are indexed by constants either way, so they stay in registers.
+template <int DH, bool FULL>
 __device__ __forceinline__ void mma_slice(f32x4_t (&acc)[8][DH / 16], const uint16_t* xb, const uint16_t* wb,
-                                          const int (&xrow)[8], int wrow, int lane) {
+                                          const int (&xrow)[8], int wrow, int lane, int nrb) {
     constexpr int CB = DH / 16;
 #pragma unroll
     for (int ks = 0; ks < kKC / 32; ++ks) {
@@ -79,6 +85,7 @@ __device__ __forceinline__ void mma_slice(f32x4_t (&acc)[8][DH / 16], const uint
             wf[cb] = *reinterpret_cast<const bf16x8_t*>(wb + swz64(wrow + 16 * cb + (lane & 15), c));
 #pragma unroll
         for (int rb = 0; rb < 8; ++rb) {
+            if (!FULL && rb >= nrb) break;
             const bf16x8_t xf = *reinterpret_cast<const bf16x8_t*>(xb + swz64(xrow[rb], c));
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
@@ -88,25 +95,29 @@ __device__ __forceinline__ void mma_slice(f32x4_t (&acc)[8][DH / 16], const uint
 }
 
 template <int DH>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) proj_kernel(ProjArgs a) {
+__global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) proj_kernel(ProjArgs a) {
     constexpr int CB = DH / 16;
-    constexpr int LX = kBM * kKC * 2 / 1024 / 4;       // 1 KB x segments per wave per stage
-    constexpr int LW = 4 * DH * kKC * 2 / 1024 / 4;    // 1 KB weight segments per wave per stage
+    constexpr int NT = kWaves * 64;
+    constexpr int LX = kBM * kKC * 2 / 1024 / kWaves;       // 1 KB x segments per wave per stage
+    constexpr int LW = 4 * DH * kKC * 2 / 1024 / kWaves;    // 1 KB weight segments per wave per stage
+    static_assert(LX * 1024 * kWaves == kBM * kKC * 2 && LW * 1024 * kWaves == 4 * DH * kKC * 2, "whole segments");
     // one LDS buffer: two x stages and two weight stages (or, in the schedule-building work
     // group, the builder's arrays)
     __shared__ __align__(1024) uint16_t lds_all[2 * kBM * kKC + 2 * 4 * DH * kKC];
     if (a.sched_here && blockIdx.x == 0) {
-        attn_sched_block<256>(a.sched, reinterpret_cast<unsigned char*>(lds_all), (int)sizeof(lds_all));
+        attn_sched_block<NT>(a.sched, reinterpret_cast<unsigned char*>(lds_all), (int)sizeof(lds_all));
         return;
     }
     uint16_t (*xs)[kBM * kKC] = reinterpret_cast<uint16_t (*)[kBM * kKC]>(lds_all);
     uint16_t (*wls)[4 * DH * kKC] = reinterpret_cast<uint16_t (*)[4 * DH * kKC]>(lds_all + 2 * kBM * kKC);
-    // per wave: gathered tile rows (| rank << 8); lives in x stage 1 until the first slice is
-    // loaded into it (each lane keeps the entries it needs in registers)
+    // per head block: its row list (row | rank << 8) and row count; they live in x stage 1 until
+    // the first slice is loaded into it (each lane keeps the entries it needs in registers)
     uint16_t (*rows)[kBM] = reinterpret_cast<uint16_t (*)[kBM]>(&xs[1][0]);
+    int* rcount = reinterpret_cast<int*>(&xs[1][4 * kBM]);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int slot = w & 3, half = w >> 2;
     // XCD-aware order: the items of one token tile run on one XCD so its x tile stays in L2
     const int L = (int)blockIdx.x - a.sched_here;
     int tile, job;
@@ -121,7 +132,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
     tile = __builtin_amdgcn_readfirstlane(tile);  // keep the tile's addresses in scalar registers
     job = __builtin_amdgcn_readfirstlane(job);
     const int64_t t0 = (int64_t)tile * kBM;
-    const int hb = job * 4 + w;
+    const int hb0 = job * 4;
+    const int hb = hb0 + slot;
     const bool active = hb < a.HB;
     const int GD = a.G;
     // head block kinds: [0,G) K_g, [G,2G) V_g, 2G shared query (if s), then expert e
@@ -130,22 +142,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
     const bool is_expert = active && hb >= ebase;
     const int e = hb - ebase;
     const int g_of = is_expert ? e / a.n : (hb < GD ? hb : hb - GD);
+    const bool routed = is_expert && !a.dense;
 
     // ---- stage loader: each wave moves LX segments of the x tile (rows past the last token
-    // repeat it) and LW segments of the weights (a head block past the last one reads block 0)
-    // per-lane byte offsets are loop invariant; the slice index moves the (scalar) bases
-    const int hb0 = job * 4;
+    // repeat it) and LW segments of the weights (a head block past the last one reads block 0);
+    // per-lane byte offsets are loop invariant, the slice index moves the (scalar) bases
     uint32_t xoff[LX], woff[LW];
 #pragma unroll
     for (int i = 0; i < LX; ++i) {
-        const int q = (w + 4 * i) * 64 + lane;
+        const int q = (w + kWaves * i) * 64 + lane;
         const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
         const int64_t rem = a.T - 1 - t0;
         xoff[i] = (uint32_t)(((r < rem ? r : rem) * a.d + 8 * c) * 2);
     }
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
-        const int q = (w + 4 * i) * 64 + lane;
+        const int q = (w + kWaves * i) * 64 + lane;
         const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
         int h = hb0 + r / DH;
         if (h >= a.HB) h = 0;
@@ -154,21 +166,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
     const bf16_t* xbase = a.x + t0 * a.d;
     auto issue = [&](int kc, int stage) {
 #pragma unroll
-        for (int i = 0; i < LX; ++i) dma16(xbase + kc * kKC, xoff[i], &xs[stage][(w + 4 * i) * 512]);
+        for (int i = 0; i < LX; ++i) dma16(xbase + kc * kKC, xoff[i], &xs[stage][(w + kWaves * i) * 512]);
 #pragma unroll
-        for (int i = 0; i < LW; ++i) dma16(a.wproj + kc * kKC, woff[i], &wls[stage][(w + 4 * i) * 512]);
+        for (int i = 0; i < LW; ++i) dma16(a.wproj + kc * kKC, woff[i], &wls[stage][(w + kWaves * i) * 512]);
     };
     issue(0, 0);
 
-    // ---- rows of this wave (tile-local bucketing for a routed expert)
-    int nrows;
-    if (is_expert && !a.dense) {
-        // padding entries (past the slice) point at row 0 so every LDS read stays in the tile
-        rows[w][lane] = 0;
-        rows[w][lane + 64] = 0;
+    // ---- row lists: the first wave of each routed head block buckets the tile's decisions
+    if (routed && half == 0) {
         int base = 0;
-        for (int half = 0; half < kBM / 64; ++half) {
-            const int row = half * 64 + lane;
+        for (int part = 0; part < kBM / 64; ++part) {
+            const int row = part * 64 + lane;
             const int64_t t = t0 + row;
             int rank = -1;
             if (t < a.T) {
@@ -178,16 +186,37 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
             }
             const uint64_t m = __builtin_amdgcn_ballot_w64(rank >= 0);
             const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-            if (rank >= 0) rows[w][base + pre] = (uint16_t)(row | (rank << 8));
+            if (rank >= 0) rows[slot][base + pre] = (uint16_t)(row | (rank << 8));
             base += __builtin_popcountll(m);
         }
-        nrows = base;
-    } else {
-        const int64_t rem = a.T - t0;
-        nrows = active ? (int)(rem < kBM ? rem : kBM) : 0;
-        const int rank = is_expert ? e % a.n : 0;  // all-active GQA: expert j of a group is head j
-        for (int i = lane; i < kBM; i += 64) rows[w][i] = (uint16_t)(i | (rank << 8));
+        // padding entries (past the list) point at row 0 so every LDS read stays in the tile
+        for (int i = base + lane; i < kBM; i += 64) rows[slot][i] = 0;
+        if (lane == 0) rcount[slot] = base;
     }
+    __syncthreads();  // row lists visible
+    int nrows;
+    int myrow[8], xrow[8];  // row | rank << 8, and the row alone, of the lane's row in each row block
+    if (routed) {
+        // the head block's list split in whole 16-row blocks: half 0 takes the first
+        // 16 * ceil(cnt / 32) entries (at most 128), half 1 the rest
+        const int cnt = rcount[slot];
+        const int split = min(cnt, 16 * ((cnt + 31) / 32));
+        const int first = half ? split : 0;
+        nrows = half ? cnt - split : split;
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb) {
+            const int i = first + 16 * rb + (lane & 15);
+            myrow[rb] = rows[slot][i < kBM ? i : 0];
+        }
+    } else {
+        const int64_t rem = a.T - t0 - 128 * half;
+        nrows = active ? (int)(rem < 0 ? 0 : (rem < 128 ? rem : 128)) : 0;
+        const int rank = is_expert ? e % a.n : 0;  // all-active GQA: expert j of a group is head j
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb) myrow[rb] = (128 * half + 16 * rb + (lane & 15)) | (rank << 8);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) xrow[rb] = myrow[rb] & 0xff;
     nrows = __builtin_amdgcn_readfirstlane(nrows);
     const int nrb = (nrows + 15) / 16;
 
@@ -198,22 +227,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
         for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const int nk = a.d / kKC;
-    // my gathered entry for each row block (lane's row = rows[16 rb + lane % 16]); rows[] is
-    // written and read by its own wave only, the barrier below frees stage 1 for the loads
-    int myrow[8], xrow[8];  // row | rank << 8, and the row alone
-#pragma unroll
-    for (int rb = 0; rb < 8; ++rb) {
-        myrow[rb] = rows[w][16 * rb + (lane & 15)];
-        xrow[rb] = myrow[rb] & 0xff;
-    }
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
-    __syncthreads();  // stage 0 visible, stage 1 free
+    __syncthreads();  // stage 0 visible; the row lists are read, stage 1 is free
 
-    // ---- epilogue: acc[rb][cb] lane holds row 16 rb + (lane & 15) of the slice, head dims
+    // ---- epilogue: acc[rb][cb] lane holds row block rb's row of this lane, head dims
     // 16 cb + 4 (lane >> 4) + 0..3
-    auto epilogue = [&](f32x4_t (&acc)[8][DH / 16], const int (&myrow)[8], int nrows, int nrb) {
+    auto epilogue = [&]() {
         const uint32_t S = (uint32_t)a.S;  // the host limits a call to 2^28 tokens
-        float kmx[2] = {0.f, 0.f};  // K blocks: largest squared norm of each 64-token half
+        float kmx[2] = {0.f, 0.f};  // K blocks: largest squared norm of each 64-token quarter
         // rotary embedding of query and key blocks: this lane's pairs are head dims
         // 16 cb + 4 (lane >> 4) + {0, 1} and {2, 3}, i.e. pairs 8 cb + 2 (lane >> 4) + {0, 1}
         const bool rot = a.rope != nullptr && !is_v;
@@ -222,7 +243,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
         for (int cb = 0; cb < DH / 16; ++cb)
 #pragma unroll
             for (int p = 0; p < 2; ++p) rev[cb][p] = rot ? a.rope[8 * cb + 2 * (lane >> 4) + p] : 0.0;
-    #pragma unroll
+#pragma unroll
         for (int rb = 0; rb < 8; ++rb) {
             if (rb >= nrb) continue;
             const int li = 16 * rb + (lane & 15);
@@ -233,9 +254,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
             if (hb < GD) {
                 // key: also its norm (the four lane groups hold complementary dims)
                 float ss = 0.f;
-    #pragma unroll
+#pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 4; ++i) ss += acc[rb][cb][i] * acc[rb][cb][i];
                 ss += __shfl_xor(ss, 16);
                 ss += __shfl_xor(ss, 32);
@@ -246,7 +267,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
                 kmx[rb >> 2] = __builtin_fmaxf(kmx[rb >> 2], ss);
                 if ((lane >> 4) == 0) a.kn[((int64_t)b * a.G + hb) * a.S_pad + sp] = sqrtf(ss);
                 bf16_t* dst = a.K + (((int64_t)b * a.G + hb) * a.S_pad + sp) * DH;
-    #pragma unroll
+#pragma unroll
                 for (int cb = 0; cb < CB; ++cb) {
                     const f32x4_t v = acc[rb][cb];
                     u32x2_t pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -259,9 +280,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
                 // V^T [dim][key]: this lane's token is one key of four consecutive dim rows
                 const int g = hb - GD;
                 uint16_t* dst = reinterpret_cast<uint16_t*>(a.Vt) + ((int64_t)b * a.G + g) * DH * a.S_pad + vt_pos(sp);
-    #pragma unroll
+#pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 4; i += 2) {
                         const uint32_t pk = pack_bf16x2(acc[rb][cb][i], acc[rb][cb][i + 1]);
                         dst[(int64_t)(16 * cb + 4 * (lane >> 4) + i) * a.S_pad] = (uint16_t)(pk & 0xffffu);
@@ -276,7 +297,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
             if (rot)
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) rope_quad(acc[rb][cb], sp, rev[cb][0], rev[cb][1]);
-    #pragma unroll
+#pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
                 const f32x4_t v = acc[rb][cb] * qs;
                 u32x2_t pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -284,13 +305,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
             }
         }
         if (hb < GD && a.knt_here) {
-            // S % 64 == 0: the two 64-token halves of the tile are whole 64-key tiles
+            // S % 64 == 0: the two 64-token quarters of this wave's half are whole 64-key tiles
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 float m = kmx[h];
 #pragma unroll
                 for (int o = 1; o < 16; o <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
-                const int64_t t = t0 + 64 * h;
+                const int64_t t = t0 + 128 * half + 64 * h;
                 if (lane == 0 && t < a.T) {
                     const uint32_t b = (uint32_t)t / S, sp = (uint32_t)t - b * S;
                     a.knt[((int64_t)b * a.G + hb) * (a.S_pad / 64) + sp / 64] = sqrtf(m);
@@ -299,14 +320,20 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) p
         }
     };
 
-    for (int kc = 0; kc < nk; ++kc) {
-        const int stage = kc & 1;
-        if (kc + 1 < nk) issue(kc + 1, stage ^ 1);
-        mma_slice<DH>(acc, xs[stage], wls[stage], xrow, w * DH, lane);
-        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
-        __syncthreads();
-    }
-    if (active) epilogue(acc, myrow, nrows, nrb);
+    // ---- main loop: the same barriers for every wave; a wave with all eight row blocks runs
+    // the straight-line body
+    auto run = [&](auto full) {
+        for (int kc = 0; kc < nk; ++kc) {
+            const int stage = kc & 1;
+            if (kc + 1 < nk) issue(kc + 1, stage ^ 1);
+            if (nrb > 0) mma_slice<DH, decltype(full)::value>(acc, xs[stage], wls[stage], xrow, slot * DH, lane, nrb);
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+            __syncthreads();
+        }
+    };
+    if (nrb == 8) run(std::true_type{});
+    else run(std::false_type{});
+    if (active) epilogue();
     if (a.stats_here && blockIdx.x == gridDim.x - 1) {
         // the x stages are free now: LDS scratch of the statistics finalize
         __syncthreads();
@@ -358,9 +385,9 @@ hipError_t launch_proj_mfma(const GqeDims& D, const WorkPlan& P, const void* x, 
     const unsigned grid = (unsigned)((int64_t)a.ntiles * a.njobs + a.sched_here);
     if (km) km->begin(KT_PROJ);
     switch (D.dh) {
-        case 32: proj_kernel<32><<<grid, 256, 0, st>>>(a); break;
-        case 48: proj_kernel<48><<<grid, 256, 0, st>>>(a); break;
-        case 64: proj_kernel<64><<<grid, 256, 0, st>>>(a); break;
+        case 32: proj_kernel<32><<<grid, kWaves * 64, 0, st>>>(a); break;
+        case 48: proj_kernel<48><<<grid, kWaves * 64, 0, st>>>(a); break;
+        case 64: proj_kernel<64><<<grid, kWaves * 64, 0, st>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     if (km) km->mark(KT_PROJ);

@@ -56,6 +56,9 @@ SMALL = [
     _small("long_k2_dh64", d=1024, k=2, dh=64, B=1, S=700, seed=10),
     _small("long_dh32_k2", d=256, N=8, G=4, k=2, dh=32, B=2, S=900, seed=11),
     _small("long_gqa", B=1, S=800, k=2, variant="hard_concat", shared_head=False, dense_gqa=True, seed=12),
+    # bf16 with a hidden size that is not a multiple of 64: scalar projection and combine, matrix-core
+    # attention on a schedule built by its own kernel
+    _small("bf16_d96_scalar_proj", d=96, N=8, G=4, k=1, dh=32, B=2, S=700, seed=13),
 ]
 
 

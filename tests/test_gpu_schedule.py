@@ -27,6 +27,8 @@ SHAPES = [
     _small("sched_single", B=4, S=1),
     _small("sched_group3", B=2, S=700, shared_kv_group=3),
     _small("sched_dh32_k2", d=256, N=8, G=4, k=2, dh=32, B=2, S=900),
+    # hidden size not a multiple of 64: scalar projection, so the schedule kernel of its own
+    _small("sched_own_kernel", d=96, N=8, G=4, k=1, dh=32, B=2, S=900),
 ]
 
 
