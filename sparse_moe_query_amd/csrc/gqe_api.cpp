@@ -620,6 +620,10 @@ static BwdPlan make_bwd_plan(const GqeDims& D, int64_t B, int64_t S) {
     const size_t S_pad = (size_t)round_up(S, GQE_KV_TILE);
     P.vr = take((size_t)B * D.G * S_pad * D.dh * 2);
     P.dob = take((size_t)B * D.H * S_pad * D.dh * 2);
+    if (D.dtype == GQE_DTYPE_BF16) {
+        P.wg_gr = take(T * D.N * D.dh * 2);
+        P.wg_ocat = take(T * (D.N + D.G + D.s) * D.dh * 2);
+    }
     P.total = off;
     return P;
 }

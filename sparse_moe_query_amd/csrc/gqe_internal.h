@@ -16,6 +16,7 @@
 constexpr int kRouterChunks = 128;
 // split-K pieces of the backward's weight gradients (sums over the tokens)
 constexpr int kWgradSplits = 16;
+constexpr int kWgSplits = 8;      // token pieces of the bf16 weight-gradient products
 #define GQE_DEC_MAX_HEADS 8      // decode: active query heads of one KV group
 #define GQE_DEC_MAX_SLOTS 192    // decode: output-projection slots of one token
 #define GQE_DEC_MAX_SLOT_DIMS 8192  // decode: slots x d_h of one token
@@ -149,6 +150,7 @@ struct BwdPlan {
     size_t offs, perm, inv, rank;     // token lists of the routed experts (bucketing) and choice ranks
     size_t part;                      // split-K partial sums of the weight gradients
     size_t vr, dob;                   // bf16 attention: row-major V and bf16 dO
+    size_t wg_gr, wg_ocat;            // bf16 weight gradients: zero-expanded routed query gradients and slot vectors
     size_t total;
 };
 

@@ -74,6 +74,8 @@ struct BwdArgs {
     uint16_t* dob;          // bf16 path: dO in bf16 [B][H][S_pad][dh]
     float* kvp;             // bf16 path: [4][T][dh] float32 dK / dV of the shared head's group, split
                             // into its routed heads' part and the shared head's part
+    uint16_t* wg_gr;        // bf16 path: zero-expanded routed query gradients [T][N][dh]
+    uint16_t* wg_ocat;      // bf16 path: zero-expanded output-slot vectors [T][N + G + s][dh]
     // outputs (float32)
     float *dx, *dwr, *dbr, *dwq, *dwqs, *dwk, *dwv, *dwo, *dwor, *dwos;
     double aux_coef;
@@ -1454,6 +1456,233 @@ __global__ void bwd_router_wgrad_reduce(BwdArgs a, int nchunk, const float* __re
     else a.dbr[e] = tot;
 }
 
+// ---------------------------------------------------------------- token-contracted products (bf16)
+// C[m][n] = sum_t A[t][m] B[t][n] with A and B token-major (the weight gradients: x^T g and
+// slot^T dy), for bf16 layers.  Work group = 128 x 128 tile of C and a range of tokens (ordered
+// split-K); per 32 tokens the two 32 x 128 operand tiles go straight from global memory into LDS
+// (global_load_lds_dwordx4, token rows as they are, 16-byte chunks XOR-swizzled by the row), three
+// stages deep.  The matrix core wants eight consecutive tokens per lane for one column, which
+// ds_read_b64_tr_b16 delivers from the token-major tile: within 16 lanes, lane i receives halfword
+// i % 4 of the 8-byte pieces addressed by lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4, so
+// lane j addressing row kk + j / 4, column c0 + 4 (j % 4) hands lane i the four tokens kk .. kk + 3
+// of column c0 + i.  Four waves, each a 64 x 64 quarter in 16 x 16 blocks, v_mfma_f32_16x16x32_bf16.
+struct WgJob {
+    const uint16_t* A;  // [T][lda], columns [0, M) used
+    const uint16_t* B;  // [T][ldb], columns [0, N) used
+    int lda, ldb, M, N;
+    int tiles_n, tile0;  // 128-column tiles of N; first tile of the job in the launch
+    int64_t part;        // float offset of the job's partial sums [split][M][N]
+    float* dst;          // reduce: destination
+    int mode;            // 0: dst[m N + n]; 1: dst[((n / dh) M + m) dh + n % dh] (per-expert blocks)
+};
+constexpr int kWgMaxJobs = 4;
+struct WgArgs {
+    WgJob job[kWgMaxJobs];
+    int njobs, ntiles;
+    int64_t T;
+    int splits, kc;  // token range per split (a multiple of 32)
+    int dh;
+    float* part;
+};
+
+__device__ __forceinline__ int wg_swz(int r) { return 2 * (r & 3) + 8 * ((r >> 3) & 1); }
+
+__global__ void __launch_bounds__(256) wg_gemm_kernel(WgArgs a) {
+    constexpr int BM = 128, BN = 128, KC = 32, NST = 3;
+    __shared__ __align__(1024) uint16_t As[NST][KC * BM];
+    __shared__ __align__(1024) uint16_t Bs[NST][KC * BN];
+    int t = blockIdx.x, jn = 0;
+    for (int q = 1; q < a.njobs; ++q)
+        if (t >= a.job[q].tile0) jn = q;
+    const WgJob& J = a.job[jn];
+    t -= J.tile0;
+    const int m0 = (t / J.tiles_n) * BM, n0 = (t % J.tiles_n) * BN;
+    const int piece = blockIdx.y;
+    const int64_t kb = (int64_t)piece * a.kc, ke = min(a.T, kb + a.kc);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // LDS destinations of the loads are scalar
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (kb < ke) {
+        // loads: wave w fills 1 KB segments w and w + 4 of each operand tile (4 token rows each);
+        // lane: row 4 seg + lane / 16, LDS chunk lane % 16 holding global chunk (lane % 16) ^ swz(row);
+        // columns past M (N) read column 0 of the row, tokens past the range read the range's last
+        int aoff[2], boff[2], rowv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int seg = w + 4 * h, r = 4 * seg + (lane >> 4), c = (lane & 15) ^ wg_swz(r);
+            rowv[h] = r;
+            aoff[h] = (m0 + 8 * c < J.M) ? m0 + 8 * c : 0;
+            boff[h] = (n0 + 8 * c < J.N) ? n0 + 8 * c : 0;
+        }
+        auto issue = [&](int64_t k0, int stage) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t tok = min(k0 + rowv[h], ke - 1);
+                dma16(J.A + tok * J.lda + aoff[h], &As[stage][(w + 4 * h) * 512]);
+                dma16(J.B + tok * J.ldb + boff[h], &Bs[stage][(w + 4 * h) * 512]);
+            }
+        };
+        const int nchunk = (int)((ke - kb + KC - 1) / KC);
+        issue(kb, 0);
+        if (nchunk > 1) issue(kb + KC, 1);
+        // fragment addresses (element offsets in a stage): lane j of its 16-lane group addresses
+        // token row 8 q + 4 h + j / 4 (q = lane / 16, h = read), column base + 4 (j % 4)
+        const int q = lane >> 4, gi = lane & 15;
+        const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+        auto faddr = [&](int col0, int h) {
+            const int r = 8 * q + 4 * h + (gi >> 2);
+            const int col = col0 + 4 * (gi & 3);
+            return r * 128 + 8 * ((col >> 3) ^ wg_swz(r)) + (col & 7);
+        };
+        typedef __attribute__((address_space(3))) s16x4_t* lds_s4;
+        for (int c = 0; c < nchunk; ++c) {
+            const int stage = c % NST;
+            if (c + 2 < nchunk) {
+                issue(kb + (int64_t)(c + 2) * KC, (c + 2) % NST);
+                __builtin_amdgcn_s_waitcnt(vmcnt_wait(8));   // chunk c landed, c + 1 and c + 2 in flight
+            } else if (c + 1 < nchunk) {
+                __builtin_amdgcn_s_waitcnt(vmcnt_wait(4));
+            } else {
+                __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+            }
+            __syncthreads();
+            bf16x8_t af[4], bfr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&As[stage][faddr(wm + 16 * i, 0)]));
+                const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&As[stage][faddr(wm + 16 * i, 1)]));
+                af[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                const s16x4_t lb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&Bs[stage][faddr(wn + 16 * i, 0)]));
+                const s16x4_t hb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&Bs[stage][faddr(wn + 16 * i, 1)]));
+                bfr[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lb, hb, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+            const int64_t k0 = kb + (int64_t)c * KC;
+            if (k0 + KC > ke) {
+                // the range's last, partial chunk: tokens past its end (rows re-read from the last
+                // token) contribute nothing
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (k0 + 8 * q + e >= ke) bfr[i][e] = (__bf16)0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            __syncthreads();  // the stage is free for the load three chunks on
+        }
+    }
+    // C layout: lane holds rows 4 (lane / 16) + 0..3 of each 16 x 16 block, column lane % 16
+    float* pp = a.part + J.part + (int64_t)piece * J.M * J.N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + ((w >> 1) * 64) + 16 * i + 4 * (lane >> 4) + r;
+                const int n = n0 + ((w & 1) * 64) + 16 * j + (lane & 15);
+                if (m < J.M && n < J.N) pp[(int64_t)m * J.N + n] = acc[i][j][r];
+            }
+}
+
+// The split-K pieces of every element added in piece order, then stored (blockIdx.y = job).
+__global__ void __launch_bounds__(256) wg_reduce_kernel(WgArgs a) {
+    const WgJob& J = a.job[blockIdx.y];
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t MN = (int64_t)J.M * J.N;
+    if (e >= MN) return;
+    float v = 0.f;
+    for (int p = 0; p < a.splits; ++p) v += a.part[J.part + p * MN + e];
+    const int m = (int)(e / J.N), n = (int)(e % J.N);
+    if (J.mode == 0) J.dst[e] = v;
+    else J.dst[((int64_t)(n / a.dh) * J.M + m) * a.dh + n % a.dh] = v;
+}
+
+// Zero-expanded operands of the weight gradients (bf16, token-major).  gr: [T][N][d_h], expert e's
+// block holds the token's query gradient for e where it chose e, zeros elsewhere.  ocat: [T][NO][d_h]
+// with NO = N + (G if the renormalised slot) + s: the expert slots (coefficient times the head
+// output where chosen, zeros elsewhere), the renormalised group slots (sum_r w_r o_r), the shared
+// head's output.  Thread = (token, block, eight head dims).
+template <typename T>
+__global__ void __launch_bounds__(256) wg_expand_kernel(BwdArgs a, uint16_t* __restrict__ gr, uint16_t* __restrict__ ocat,
+                                                        int nslot) {
+    const int u8 = a.dh / 8;
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int nb = a.N + nslot;
+    if (q >= a.T * nb * u8) return;
+    const int j = (int)(q % u8) * 8;
+    const int blk = (int)((q / u8) % nb);
+    const int64_t t = q / ((int64_t)u8 * nb);
+    if (blk < a.N) {
+        // expert e: the choice rank r with idx[t][g][r] == e (all-active GQA: head e % n)
+        const int e = blk, g = e / a.n;
+        int r = -1;
+        if (a.dense) r = e % a.n;
+        else
+            for (int rr = 0; rr < a.k; ++rr)
+                if (a.idx[(t * a.G + g) * a.k + rr] == e) r = rr;
+        u32x4_t gv = {0u, 0u, 0u, 0u}, ov = {0u, 0u, 0u, 0u};
+        if (r >= 0) {
+            const int h = g * a.k + r;
+            gv = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.dQ) + (t * a.H + h) * a.dh + j);
+            float o[8];
+            ld8<bf16_t>(a.O, (t * a.H + h) * a.dh + j, o);
+            const float c = a.cf[t * a.H + h];
+#pragma unroll
+            for (int z = 0; z < 8; ++z) o[z] *= c;
+            ov = pack8(o);
+        }
+        *reinterpret_cast<u32x4_t*>(gr + (t * a.N + e) * a.dh + j) = gv;
+        *reinterpret_cast<u32x4_t*>(ocat + (t * (a.N + nslot) + e) * a.dh + j) = ov;
+        return;
+    }
+    const int sl = blk - a.N;
+    float o[8];
+    if (sl < nslot - a.s) {
+        // renormalised slot of group sl
+#pragma unroll
+        for (int z = 0; z < 8; ++z) o[z] = 0.f;
+        for (int r = 0; r < a.k; ++r) {
+            const int h = sl * a.k + r;
+            float v[8];
+            ld8<bf16_t>(a.O, (t * a.H + h) * a.dh + j, v);
+            const float c = a.wn[t * a.H + h];
+#pragma unroll
+            for (int z = 0; z < 8; ++z) o[z] += c * v[z];
+        }
+    } else {
+        ld8<bf16_t>(a.O, (t * a.H + a.G * a.k) * a.dh + j, o);
+    }
+    *reinterpret_cast<u32x4_t*>(ocat + (t * (a.N + nslot) + blk) * a.dh + j) = pack8(o);
+}
+
+// Launches one token-contracted product set (jobs in order) and its reduce.
+hipError_t wg_launch(WgArgs wa, hipStream_t st) {
+    int tiles = 0;
+    int64_t off = 0;
+    for (int i = 0; i < wa.njobs; ++i) {
+        WgJob& J = wa.job[i];
+        J.tiles_n = (int)ceil_div(J.N, 128);
+        J.tile0 = tiles;
+        tiles += (int)ceil_div(J.M, 128) * J.tiles_n;
+        J.part = off;
+        off += (int64_t)wa.splits * J.M * J.N;
+    }
+    wa.ntiles = tiles;
+    wg_gemm_kernel<<<dim3((unsigned)tiles, (unsigned)wa.splits), 256, 0, st>>>(wa);
+    int64_t mn = 0;
+    for (int i = 0; i < wa.njobs; ++i) mn = std::max(mn, (int64_t)wa.job[i].M * wa.job[i].N);
+    wg_reduce_kernel<<<dim3((unsigned)ceil_div(mn, 256), (unsigned)wa.njobs), 256, 0, st>>>(wa);
+    return hipGetLastError();
+}
+
 template <class Prob, bool AK, bool BK>
 void tgemm(bool mfma, const Prob& p, int maxM, int maxN, int nsub, hipStream_t st, int splits = 1,
            float* part = nullptr) {
@@ -1523,10 +1752,47 @@ hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km
     if (km) km->mark(KT_BWD_ATTN);
 weights:
     if (km) km->begin(KT_BWD_WGRAD);
-    // weight gradients reduce over the tokens: split-K pieces (kWgradSplits) summed in order
-    tgemm<ProbWo<T>, false, false>(mm, ProbWo<T>{a, L}, a.dh, a.d, nsm, st, kWgradSplits, a.part);
-    const int nwx = 2 * a.G + a.s + a.N;  // head blocks and experts (the router has its own kernel)
-    tgemm<ProbWx<T>, false, false>(mm, ProbWx<T>{a, L}, a.d, a.dh, nwx, st, kWgradSplits, a.part);
+    // weight gradients reduce over the tokens: split-K pieces summed in order
+    if (mm && a.d % 8 == 0) {
+        // bf16: two token-contracted products over zero-expanded operands (routed experts as
+        // blocks that are zero where the token did not choose them)
+        const int nslot = (rslot ? a.G : 0) + a.s;
+        const int64_t nth = a.T * (a.N + nslot) * (a.dh / 8);
+        wg_expand_kernel<T><<<blocks(nth), 256, 0, st>>>(a, a.wg_gr, a.wg_ocat, nslot);
+        WgArgs wa{};
+        wa.T = a.T;
+        wa.splits = kWgSplits;
+        wa.kc = (int)round_up(ceil_div(a.T, kWgSplits), 32);
+        wa.dh = a.dh;
+        wa.part = a.part;
+        const int no = (a.N + nslot) * a.dh;  // slot columns of a token
+        const uint16_t* dyb = reinterpret_cast<const uint16_t*>(a.dy);
+        const uint16_t* xb = reinterpret_cast<const uint16_t*>(a.x);
+        // output side: dW_o / dW_oR / dW_os [slot d_h][d] = slot^T dy
+        wa.job[0] = WgJob{a.wg_ocat, dyb, no, a.d, a.N * a.dh, a.d, 0, 0, 0, a.dwo, 0};
+        wa.njobs = 1;
+        if (rslot) wa.job[wa.njobs++] = WgJob{a.wg_ocat + a.N * a.dh, dyb, no, a.d, a.G * a.dh, a.d, 0, 0, 0, a.dwor, 0};
+        if (a.s) wa.job[wa.njobs++] = WgJob{a.wg_ocat + (no - a.dh), dyb, no, a.d, a.dh, a.d, 0, 0, 0, a.dwos, 0};
+        hipError_t e = wg_launch(wa, st);
+        if (e != hipSuccess) return e;
+        // input side: dW_k, dW_v [d][G d_h], dW_qs [d][d_h] = x^T g; dW_q [N][d][d_h] from the
+        // zero-expanded routed gradients
+        const uint16_t* dKb = reinterpret_cast<const uint16_t*>(a.dK);
+        const uint16_t* dVb = reinterpret_cast<const uint16_t*>(a.dV);
+        const uint16_t* dQb = reinterpret_cast<const uint16_t*>(a.dQ);
+        const int gd = a.G * a.dh;
+        wa.job[0] = WgJob{xb, dKb, a.d, gd, a.d, gd, 0, 0, 0, a.dwk, 0};
+        wa.job[1] = WgJob{xb, dVb, a.d, gd, a.d, gd, 0, 0, 0, a.dwv, 0};
+        wa.job[2] = WgJob{xb, a.wg_gr, a.d, a.N * a.dh, a.d, a.N * a.dh, 0, 0, 0, a.dwq, 1};
+        wa.njobs = 3;
+        if (a.s) wa.job[wa.njobs++] = WgJob{xb, dQb + a.G * a.k * a.dh, a.d, a.H * a.dh, a.d, a.dh, 0, 0, 0, a.dwqs, 0};
+        e = wg_launch(wa, st);
+        if (e != hipSuccess) return e;
+    } else {
+        tgemm<ProbWo<T>, false, false>(mm, ProbWo<T>{a, L}, a.dh, a.d, nsm, st, kWgradSplits, a.part);
+        const int nwx = 2 * a.G + a.s + a.N;  // head blocks and experts (the router has its own kernel)
+        tgemm<ProbWx<T>, false, false>(mm, ProbWx<T>{a, L}, a.d, a.dh, nwx, st, kWgradSplits, a.part);
+    }
     if (!a.dense) {
         const int nchunk = (int)std::min<int64_t>(kRouterChunks, ceil_div(a.T, kRgTok));
         const dim3 gr((unsigned)ceil_div(a.d + 1, 256), (unsigned)ceil_div(a.N, 16), (unsigned)nchunk);
@@ -1586,6 +1852,8 @@ hipError_t launch_backward(const GqeDims& D, const WorkPlan& P, const BwdPlan& B
     a.vr = (uint16_t*)(ws + BP.vr);
     a.dob = (uint16_t*)(ws + BP.dob);
     a.kvp = (float*)(ws + BP.kvp);
+    a.wg_gr = (uint16_t*)(ws + BP.wg_gr);
+    a.wg_ocat = (uint16_t*)(ws + BP.wg_ocat);
     a.dx = gr.dx;
     a.dwr = gr.d_router;
     a.dbr = gr.d_router_bias;
