@@ -594,7 +594,8 @@ static BwdPlan make_bwd_plan(const GqeDims& D, int64_t B, int64_t S) {
     };
     const size_t T = (size_t)(B * S);
     P.NS = D.G * D.k + ((!D.dense && D.variant == GQE_VARIANT_GQE) ? D.G : 0) + D.s;
-    P.U = take(T * P.NS * D.dh * 4);
+    P.NSX = D.N + ((!D.dense && D.variant == GQE_VARIANT_GQE) ? D.G : 0) + D.s;
+    P.U = take(T * std::max(P.NS, P.NSX) * D.dh * 4);
     P.dO = take(T * D.H * D.dh * 4);
     P.Dd = take(T * D.H * 4);
     P.lse = take(T * D.H * 4);
@@ -621,7 +622,10 @@ static BwdPlan make_bwd_plan(const GqeDims& D, int64_t B, int64_t S) {
     P.vr = take((size_t)B * D.G * S_pad * D.dh * 2);
     P.dob = take((size_t)B * D.H * S_pad * D.dh * 2);
     if (D.dtype == GQE_DTYPE_BF16) {
-        P.wg_gr = take(T * D.N * D.dh * 2);
+        const size_t kp = (size_t)round_up((int64_t)(2 * D.G + D.s + D.N) * D.dh, 64);
+        P.wg_gcat = take(T * kp * 2);
+        P.wg_wcat = take((size_t)D.d * kp * 2);
+        P.wg_wslot = take((size_t)P.NSX * D.dh * D.d * 2);
         P.wg_ocat = take(T * (D.N + D.G + D.s) * D.dh * 2);
     }
     P.total = off;

@@ -137,6 +137,7 @@ struct DecodePlan {
     int64_t B, s_max, NC;             // NC = key chunks per cache row
     int C, MH;                        // keys per chunk, largest active head count of a group
     int NS;                           // output-projection slots of one token
+    int NSX;                          // every output slot (N experts + group slots + shared)
     size_t qd, part, od, yp;          // queries [B][H][dh], chunk partials [B][G][NC][MH][dh+2], O [B][H][dh],
                                       // per-slot output rows [B][NS][d] (all f32)
     size_t total;
@@ -145,12 +146,15 @@ struct DecodePlan {
 // Byte offsets into the caller's backward workspace for a [B, S] forward (all float32).
 struct BwdPlan {
     int NS;                           // output-projection slots of one token
+    int NSX;                          // every output slot (N experts + group slots + shared)
     size_t U, dO, Dd, lse, dl, cf, wn, dQ, dK, dV;
     size_t kvp;                       // bf16 attention: float32 dK / dV partials of the shared head's group
     size_t offs, perm, inv, rank;     // token lists of the routed experts (bucketing) and choice ranks
     size_t part;                      // split-K partial sums of the weight gradients
     size_t vr, dob;                   // bf16 attention: row-major V and bf16 dO
-    size_t wg_gr, wg_ocat;            // bf16 weight gradients: zero-expanded routed query gradients and slot vectors
+    size_t wg_gcat, wg_wcat, wg_ocat; // bf16 weight / input gradients: concatenated gradients (routed experts
+                                      // zero-expanded), matching weights, slot vectors
+    size_t wg_wslot;                  // bf16: the output-slot weights in one matrix
     size_t total;
 };
 

@@ -57,7 +57,7 @@ struct BwdArgs {
     const float* probs;     // [T][N] the forward's in-group router probabilities
     const double* rope;     // rotary frequencies (cycles per position) or null
     // backward workspace
-    float* U;               // [T][NS][dh]
+    float* U;               // [T][NS][dh] (slot order: see wgp)
     float* dO;              // [T][H][dh]
     float* Dd;              // [T][H]
     float* lse;             // [T][H]
@@ -74,13 +74,18 @@ struct BwdArgs {
     uint16_t* dob;          // bf16 path: dO in bf16 [B][H][S_pad][dh]
     float* kvp;             // bf16 path: [4][T][dh] float32 dK / dV of the shared head's group, split
                             // into its routed heads' part and the shared head's part
-    uint16_t* wg_gr;        // bf16 path: zero-expanded routed query gradients [T][N][dh]
+    uint16_t* wg_gcat;      // bf16 path: concatenated gradients, routed experts zero-expanded [T][kp]
+    uint16_t* wg_wcat;      // bf16 path: the matching input-side weights [d][kp]
+    uint16_t* wg_wslot;     // bf16 path: the output-slot weights [NS dh][d]
     uint16_t* wg_ocat;      // bf16 path: zero-expanded output-slot vectors [T][N + G + s][dh]
     // outputs (float32)
     float *dx, *dwr, *dbr, *dwq, *dwqs, *dwk, *dwv, *dwo, *dwor, *dwos;
     double aux_coef;
     int64_t B, S, T, S_pad;
     int d, N, G, k, n, dh, H, s, skv, variant, dense, NS, Np;
+    // bf16 whole-product path (see run): U holds every expert's slot ([N experts | G group slots |
+    // shared], NS = N + G + s) instead of the token's chosen ones ([G k ranks | G | s])
+    int wgp;
 };
 
 template <typename T>
@@ -156,11 +161,22 @@ __device__ __forceinline__ int expert_of(const BwdArgs& a, int64_t t, int h) {
 __device__ __forceinline__ int group_of(const BwdArgs& a, int h) { return h < a.G * a.k ? h / a.k : a.skv; }
 
 // ---------------------------------------------------------------- head-output and router gradients
-// thread per (token, group); group 0 also handles the shared head.
+// Sum over the four lanes of a quad (DPP row permutations xor 1, xor 2).
+__device__ __forceinline__ float quad_add(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false));
+    return v;
+}
+
+// Four lanes per (token, group), each a quarter of the head dims (four elements in every 16; the
+// dot products summed over the quad); group 0 also handles the shared head.  Every lane of a quad
+// forms the router gradients (n <= 16 values), its first lane stores them.
 template <typename T>
 __global__ void bwd_route_kernel(BwdArgs a) {
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= a.T * a.G) return;
+    const int64_t q = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 2;
+    const int qd = threadIdx.x & 3;
+    const bool lead = qd == 0;
+    if (q >= a.T * a.G) return;  // whole quads leave together (T G quads, blocks of 64 quads)
     const int64_t t = q / a.G;
     const int g = (int)(q % a.G);
     const int n = a.n, k = a.k, dh = a.dh, H = a.H, nr = a.G * a.k;
@@ -169,30 +185,37 @@ __global__ void bwd_route_kernel(BwdArgs a) {
     // rows of d_h (a multiple of 16) read and written four elements at a time
     const float* Ut = a.U + t * a.NS * dh;
     auto U4 = [&](int slot, int j) { return *reinterpret_cast<const f32x4_t*>(Ut + slot * dh + j); };
+    // U slots: the routed heads' (by choice rank, or by expert on the whole-product path), then the
+    // renormalised group slots, then the shared head
+    const int ub = a.wgp ? a.N : nr;
     auto O4 = [&](int h, int j) { return ld4<T>(a.O, ((b * a.S + s) * H + h) * dh + j); };
     auto dO4 = [&](int h, int j) -> f32x4_t& { return *reinterpret_cast<f32x4_t*>(a.dO + (t * H + h) * dh + j); };
     if (g == 0 && a.s) {  // shared head: do = dy W_os^T
-        const int hs = nr, ls = nr + (rslot ? a.G : 0);
+        const int hs = nr, ls = ub + (rslot ? a.G : 0);
         float D = 0.f;
-        for (int j = 0; j < dh; j += 4) {
+        for (int j = 4 * qd; j < dh; j += 16) {
             const f32x4_t v = U4(ls, j);
             dO4(hs, j) = v;
             D += dot4(v, O4(hs, j));
         }
-        a.Dd[t * H + hs] = D;
+        D = quad_add(D);
+        if (lead) a.Dd[t * H + hs] = D;
     }
     if (a.dense) {  // all-active GQA: hard concatenation, no router
         for (int r = 0; r < k; ++r) {
             const int h = g * k + r;
             float D = 0.f;
-            for (int j = 0; j < dh; j += 4) {
-                const f32x4_t v = U4(h, j);
+            for (int j = 4 * qd; j < dh; j += 16) {
+                const f32x4_t v = U4(a.wgp ? g * n + r : h, j);
                 dO4(h, j) = v;
                 D += dot4(v, O4(h, j));
             }
-            a.Dd[t * H + h] = D;
-            a.cf[t * H + h] = 1.f;
-            a.wn[t * H + h] = 0.f;
+            D = quad_add(D);
+            if (lead) {
+                a.Dd[t * H + h] = D;
+                a.cf[t * H + h] = 1.f;
+                a.wn[t * H + h] = 0.f;
+            }
         }
         return;
     }
@@ -211,9 +234,9 @@ __global__ void bwd_route_kernel(BwdArgs a) {
         const float coef = a.variant == GQE_VARIANT_WEIGHTED_CONCAT ? p[jr] : 1.f;
         const float w = p[jr] / psel;
         float D = 0.f, ou = 0.f, ov = 0.f;
-        for (int j = 0; j < dh; j += 4) {
-            const f32x4_t u = U4(h, j);
-            const f32x4_t v = rslot ? U4(nr + g, j) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 4 * qd; j < dh; j += 16) {
+            const f32x4_t u = U4(a.wgp ? id[r] : h, j);
+            const f32x4_t v = rslot ? U4(ub + g, j) : f32x4_t{0.f, 0.f, 0.f, 0.f};
             const f32x4_t o = O4(h, j);
             const f32x4_t dov = coef * u + w * v;
             dO4(h, j) = dov;
@@ -221,9 +244,14 @@ __global__ void bwd_route_kernel(BwdArgs a) {
             ou += dot4(o, u);
             ov += dot4(o, v);
         }
-        a.Dd[t * H + h] = D;
-        a.cf[t * H + h] = coef;
-        a.wn[t * H + h] = w;
+        D = quad_add(D);
+        ou = quad_add(ou);
+        ov = quad_add(ov);
+        if (lead) {
+            a.Dd[t * H + h] = D;
+            a.cf[t * H + h] = coef;
+            a.wn[t * H + h] = w;
+        }
         if (a.variant == GQE_VARIANT_WEIGHTED_CONCAT) dp[jr] += ou;
         dw[r] = ov;
     }
@@ -239,7 +267,8 @@ __global__ void bwd_route_kernel(BwdArgs a) {
     }
     float sdp = 0.f;
     for (int jj = 0; jj < n; ++jj) sdp += p[jj] * dp[jj];
-    for (int jj = 0; jj < n; ++jj) a.dl[t * a.N + g * n + jj] = p[jj] * (dp[jj] - sdp);
+    if (lead)
+        for (int jj = 0; jj < n; ++jj) a.dl[t * a.N + g * n + jj] = p[jj] * (dp[jj] - sdp);
 }
 
 // ---------------------------------------------------------------- attention
@@ -1605,63 +1634,230 @@ __global__ void __launch_bounds__(256) wg_reduce_kernel(WgArgs a) {
     else J.dst[((int64_t)(n / a.dh) * J.M + m) * a.dh + n % a.dh] = v;
 }
 
-// Zero-expanded operands of the weight gradients (bf16, token-major).  gr: [T][N][d_h], expert e's
-// block holds the token's query gradient for e where it chose e, zeros elsewhere.  ocat: [T][NO][d_h]
-// with NO = N + (G if the renormalised slot) + s: the expert slots (coefficient times the head
-// output where chosen, zeros elsewhere), the renormalised group slots (sum_r w_r o_r), the shared
-// head's output.  Thread = (token, block, eight head dims).
+// Token-major bf16 operands of the weight and input gradients, with the routed experts
+// zero-expanded (an expert's block is zero where the token did not choose it).  gcat: [T][kp], the
+// concatenated gradients [dK (G d_h) | dV (G d_h) | shared dq (s d_h) | routed dq per expert (N d_h) |
+// zeros up to kp]; ocat: [T][N + nslot][d_h], the output-slot vectors: expert slots (coefficient times
+// the head output where chosen), the renormalised group slots (sum_r w_r o_r), the shared head's
+// output.  Thread = (token, eight columns).
 template <typename T>
-__global__ void __launch_bounds__(256) wg_expand_kernel(BwdArgs a, uint16_t* __restrict__ gr, uint16_t* __restrict__ ocat,
-                                                        int nslot) {
-    const int u8 = a.dh / 8;
+__global__ void __launch_bounds__(256) wg_expand_kernel(BwdArgs a, uint16_t* __restrict__ gcat, int kp,
+                                                        uint16_t* __restrict__ ocat, int nslot) {
+    const int ng = kp / 8, no = (a.N + nslot) * a.dh / 8;
     const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int nb = a.N + nslot;
-    if (q >= a.T * nb * u8) return;
-    const int j = (int)(q % u8) * 8;
-    const int blk = (int)((q / u8) % nb);
-    const int64_t t = q / ((int64_t)u8 * nb);
-    if (blk < a.N) {
-        // expert e: the choice rank r with idx[t][g][r] == e (all-active GQA: head e % n)
-        const int e = blk, g = e / a.n;
-        int r = -1;
-        if (a.dense) r = e % a.n;
-        else
-            for (int rr = 0; rr < a.k; ++rr)
-                if (a.idx[(t * a.G + g) * a.k + rr] == e) r = rr;
-        u32x4_t gv = {0u, 0u, 0u, 0u}, ov = {0u, 0u, 0u, 0u};
-        if (r >= 0) {
-            const int h = g * a.k + r;
-            gv = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.dQ) + (t * a.H + h) * a.dh + j);
-            float o[8];
-            ld8<bf16_t>(a.O, (t * a.H + h) * a.dh + j, o);
-            const float c = a.cf[t * a.H + h];
-#pragma unroll
-            for (int z = 0; z < 8; ++z) o[z] *= c;
-            ov = pack8(o);
+    if (q >= a.T * (ng + no)) return;
+    const int64_t t = q / (ng + no);
+    const int u = (int)(q % (ng + no));
+    const uint16_t* dQ = reinterpret_cast<const uint16_t*>(a.dQ);
+    const int GD = a.G * a.dh, kd = 2 * GD + a.s * a.dh;
+    // the head of token t that chose expert e (all-active GQA: head e % n of its group), or -1
+    auto routed_head = [&](int e) {
+        const int g = e / a.n;
+        if (a.dense) return g * a.k + e % a.n;
+        const int32_t* id = a.idx + (t * a.G + g) * a.k;
+        int h = -1;
+        for (int r = 0; r < a.k; ++r)
+            if (id[r] == e) h = g * a.k + r;
+        return h;
+    };
+    if (u < ng) {
+        const int c = 8 * u;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (c < GD) v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.dK) + t * GD + c);
+        else if (c < 2 * GD) v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.dV) + t * GD + c - GD);
+        else if (c < kd) v = *reinterpret_cast<const u32x4_t*>(dQ + (t * a.H + a.G * a.k) * a.dh + c - 2 * GD);
+        else if (c < kd + a.N * a.dh) {
+            const int e = (c - kd) / a.dh, j = (c - kd) % a.dh;
+            const int h = routed_head(e);
+            if (h >= 0) v = *reinterpret_cast<const u32x4_t*>(dQ + (t * a.H + h) * a.dh + j);
         }
-        *reinterpret_cast<u32x4_t*>(gr + (t * a.N + e) * a.dh + j) = gv;
-        *reinterpret_cast<u32x4_t*>(ocat + (t * (a.N + nslot) + e) * a.dh + j) = ov;
+        *reinterpret_cast<u32x4_t*>(gcat + t * kp + c) = v;
         return;
     }
-    const int sl = blk - a.N;
+    const int c = 8 * (u - ng);
+    const int blk = c / a.dh, j = c % a.dh;
     float o[8];
-    if (sl < nslot - a.s) {
-        // renormalised slot of group sl
+    if (blk < a.N) {
+        const int h = routed_head(blk);
+        if (h < 0) {
+#pragma unroll
+            for (int z = 0; z < 8; ++z) o[z] = 0.f;
+        } else {
+            ld8<bf16_t>(a.O, (t * a.H + h) * a.dh + j, o);
+            const float cf = a.cf[t * a.H + h];
+#pragma unroll
+            for (int z = 0; z < 8; ++z) o[z] *= cf;
+        }
+    } else if (blk - a.N < nslot - a.s) {
+        const int g = blk - a.N;
 #pragma unroll
         for (int z = 0; z < 8; ++z) o[z] = 0.f;
         for (int r = 0; r < a.k; ++r) {
-            const int h = sl * a.k + r;
+            const int h = g * a.k + r;
             float v[8];
             ld8<bf16_t>(a.O, (t * a.H + h) * a.dh + j, v);
-            const float c = a.wn[t * a.H + h];
+            const float w = a.wn[t * a.H + h];
 #pragma unroll
-            for (int z = 0; z < 8; ++z) o[z] += c * v[z];
+            for (int z = 0; z < 8; ++z) o[z] += w * v[z];
         }
     } else {
         ld8<bf16_t>(a.O, (t * a.H + a.G * a.k) * a.dh + j, o);
     }
-    *reinterpret_cast<u32x4_t*>(ocat + (t * (a.N + nslot) + blk) * a.dh + j) = pack8(o);
+    *reinterpret_cast<u32x4_t*>(ocat + t * (a.N + nslot) * a.dh + c) = pack8(o);
 }
+
+// The input-side weights transposed to match gcat: wcat[i][kk] = the weight that multiplies gcat
+// column kk in dx[t][i] (W_k, W_v, W_qs, then W_q of every expert; zeros up to kp).  Thread = (i,
+// eight columns).
+__global__ void __launch_bounds__(256) wg_wcat_kernel(BwdArgs a, uint16_t* __restrict__ wcat, int kp) {
+    const int ng = kp / 8;
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= (int64_t)a.d * ng) return;
+    const int i = (int)(q / ng), c = 8 * (int)(q % ng);
+    const int GD = a.G * a.dh, kd = 2 * GD + a.s * a.dh;
+    const uint16_t* src = nullptr;
+    if (c < GD) src = reinterpret_cast<const uint16_t*>(a.wk) + (int64_t)i * GD + c;
+    else if (c < 2 * GD) src = reinterpret_cast<const uint16_t*>(a.wv) + (int64_t)i * GD + c - GD;
+    else if (c < kd) src = reinterpret_cast<const uint16_t*>(a.wqs) + (int64_t)i * a.dh + c - 2 * GD;
+    else if (c < kd + a.N * a.dh) {
+        const int e = (c - kd) / a.dh, j = (c - kd) % a.dh;
+        src = reinterpret_cast<const uint16_t*>(a.wq) + ((int64_t)e * a.d + i) * a.dh + j;
+    }
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (src) {
+        // two 8-byte halves (the weights are only assumed 8-byte aligned, as by ld8)
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(src), hi = *reinterpret_cast<const u32x2_t*>(src + 4);
+        v = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    }
+    *reinterpret_cast<u32x4_t*>(wcat + (int64_t)i * kp + c) = v;
+}
+
+// The output-slot weights as one [NS d_h][d] matrix: W_o of every expert, W_oR of every group (when
+// the renormalised slot exists), W_os.  Thread = (row, eight columns).
+__global__ void __launch_bounds__(256) wg_wslot_kernel(BwdArgs a, uint16_t* __restrict__ wsl) {
+    const int ng = a.d / 8;
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= (int64_t)a.NS * a.dh * ng) return;
+    const int row = (int)(q / ng), c = 8 * (int)(q % ng);
+    const int ro = a.N * a.dh, rg = (a.NS - a.N - a.s) * a.dh;
+    const uint16_t* src;
+    if (row < ro) src = reinterpret_cast<const uint16_t*>(a.wo) + (int64_t)row * a.d + c;
+    else if (row < ro + rg) src = reinterpret_cast<const uint16_t*>(a.wor) + (int64_t)(row - ro) * a.d + c;
+    else src = reinterpret_cast<const uint16_t*>(a.wos) + (int64_t)(row - ro - rg) * a.d + c;
+    const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(src), hi = *reinterpret_cast<const u32x2_t*>(src + 4);
+    *reinterpret_cast<u32x4_t*>(wsl + (int64_t)row * a.d + c) = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// dx = gcat wcat^T + dl W_r^T (float32 result, written): the first product on bf16 operands, both
+// contiguous along the contraction, so the tiles go straight into LDS (64-wide slices, XOR-swizzled
+// 16-byte chunks, two stages) and the fragments are plain 16-byte LDS reads; 128 x 128 tiles of dx,
+// four waves of 64 x 64 in v_mfma_f32_16x16x32_bf16 (kp is a multiple of 64).  The router's term
+// (float32 logit gradients and router weights, nr <= 64 columns; nr = 0: none) is added in the same
+// accumulators by v_mfma_f32_16x16x4_f32 from float32 tiles staged in the freed LDS.
+__global__ void __launch_bounds__(256, 2) dx_gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                                                         float* __restrict__ C, int64_t M, int N, int kp,
+                                                         const float* __restrict__ dl, const float* __restrict__ wr,
+                                                         int nr) {
+    constexpr int BM = 128, BN = 128, KC = 64;
+    __shared__ __align__(1024) uint16_t As[2][BM * KC];
+    __shared__ __align__(1024) uint16_t Bs[2][BN * KC];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tiles_n = (N + BN - 1) / BN;
+    const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * BM;
+    const int n0 = (int)(blockIdx.x % tiles_n) * BN;
+    // loads: 16 segments of 1 KB per operand tile (8 rows of 8 chunks each), wave w takes
+    // segments w, w + 4, w + 8, w + 12; LDS chunk p of row r holds global chunk p ^ ((r >> 1) & 7)
+    uint32_t aoff[4], boff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int qq = (w + 4 * i) * 64 + lane;
+        const int r = qq >> 3, c = (qq & 7) ^ ((r >> 1) & 7);
+        const int64_t ra = min(m0 + r, M - 1) - m0;
+        const int rb = min(n0 + r, N - 1) - n0;
+        aoff[i] = (uint32_t)((ra * kp + 8 * c) * 2);
+        boff[i] = (uint32_t)(((int64_t)rb * kp + 8 * c) * 2);
+    }
+    const uint16_t* abase = A + m0 * kp;
+    const uint16_t* bbase = B + (int64_t)n0 * kp;
+    auto issue = [&](int kc, int stage) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(abase + kc * KC, aoff[i], &As[stage][(w + 4 * i) * 512]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(bbase + kc * KC, boff[i], &Bs[stage][(w + 4 * i) * 512]);
+    };
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+    auto swz = [](int row, int c) { return (row * 8 + (c ^ ((row >> 1) & 7))) * 8; };
+    const int nk = kp / KC;
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+    __syncthreads();
+    for (int kc = 0; kc < nk; ++kc) {
+        const int stage = kc & 1;
+        if (kc + 1 < nk) issue(kc + 1, stage ^ 1);
+#pragma unroll
+        for (int ks = 0; ks < KC / 32; ++ks) {
+            const int c = 4 * ks + (lane >> 4);
+            bf16x8_t af[4], bfr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                af[i] = *reinterpret_cast<const bf16x8_t*>(&As[stage][swz(wm + 16 * i + (lane & 15), c)]);
+                bfr[i] = *reinterpret_cast<const bf16x8_t*>(&Bs[stage][swz(wn + 16 * i + (lane & 15), c)]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+        __syncthreads();
+    }
+    if (nr > 0) {
+        // dl [128 tokens][nr4] and W_r [128 columns][nr4] of the tile in float32 (zero past the
+        // edges and past nr), then k-steps of four router columns
+        const int nr4 = (nr + 3) & ~3;
+        float* dls = reinterpret_cast<float*>(&As[0][0]);
+        float* wrs = reinterpret_cast<float*>(&Bs[0][0]);
+        for (int q = tid; q < BM * nr4; q += 256) {
+            const int r = q / nr4, e = q % nr4;
+            dls[q] = (m0 + r < M && e < nr) ? dl[(m0 + r) * nr + e] : 0.f;
+            wrs[q] = (n0 + r < N && e < nr) ? wr[(int64_t)(n0 + r) * nr + e] : 0.f;
+        }
+        __syncthreads();
+        for (int e0 = 0; e0 < nr4; e0 += 4) {
+            float af[4], bq[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                af[i] = dls[(wm + 16 * i + (lane & 15)) * nr4 + e0 + (lane >> 4)];
+                bq[i] = wrs[(wn + 16 * i + (lane & 15)) * nr4 + e0 + (lane >> 4)];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bq[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    // lane: rows (tokens) 4 (lane / 16) + 0..3 of each 16 x 16 block, column lane % 16
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t m = m0 + wm + 16 * i + 4 * (lane >> 4) + r;
+                const int n = n0 + wn + 16 * j + (lane & 15);
+                if (m < M && n < N) C[m * N + n] = acc[i][j][r];
+            }
+}
+
+// Columns of gcat / wcat: the concatenated input-side blocks rounded up to whole 64-wide slices.
+int wg_kp(const BwdArgs& a) { return (int)round_up((int64_t)(2 * a.G + a.s + a.N) * a.dh, 64); }
 
 // Launches one token-contracted product set (jobs in order) and its reduce.
 hipError_t wg_launch(WgArgs wa, hipStream_t st) {
@@ -1706,8 +1902,21 @@ hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km
     // bf16 layers: the GEMM-shaped steps on matrix cores, except the router's (float32 weights and
     // logit gradients stay float32)
     const bool mm = sizeof(T) == 2;
-    tgemm<ProbU<T>, true, true>(mm, ProbU<T>{a, L}, nt, a.dh, nsm, st);
-    bwd_route_kernel<T><<<blocks(a.T * a.G), 256, 0, st>>>(a);
+    // bf16: the output-slot, weight and input gradients as whole products over zero-expanded
+    // operands (conditions in launch_backward)
+    const bool wgp = a.wgp != 0;
+    if (wgp) {
+        // U = dy W_slots^T for every slot of every token (the experts zero-expanded: slots the token
+        // did not choose are computed and not read), one product
+        const int nso = a.NS * a.dh;
+        wg_wslot_kernel<<<blocks((int64_t)nso * (a.d / 8)), 256, 0, st>>>(a, a.wg_wslot);
+        const unsigned tiles = (unsigned)(ceil_div(a.T, 128) * ceil_div(nso, 128));
+        dx_gemm_kernel<<<tiles, 256, 0, st>>>(reinterpret_cast<const uint16_t*>(a.dy), a.wg_wslot, a.U, a.T, nso, a.d,
+                                              nullptr, nullptr, 0);
+    } else {
+        tgemm<ProbU<T>, true, true>(mm, ProbU<T>{a, L}, nt, a.dh, nsm, st);
+    }
+    bwd_route_kernel<T><<<blocks(4 * a.T * a.G), 256, 0, st>>>(a);
     if (km) km->mark(KT_BWD_OUT);
     if (km) km->begin(KT_BWD_ATTN);
     const unsigned nblk = (unsigned)ceil_div(a.S, 64);
@@ -1753,12 +1962,13 @@ hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km
 weights:
     if (km) km->begin(KT_BWD_WGRAD);
     // weight gradients reduce over the tokens: split-K pieces summed in order
-    if (mm && a.d % 8 == 0) {
+    if (wgp) {
         // bf16: two token-contracted products over zero-expanded operands (routed experts as
         // blocks that are zero where the token did not choose them)
         const int nslot = (rslot ? a.G : 0) + a.s;
-        const int64_t nth = a.T * (a.N + nslot) * (a.dh / 8);
-        wg_expand_kernel<T><<<blocks(nth), 256, 0, st>>>(a, a.wg_gr, a.wg_ocat, nslot);
+        const int kp = wg_kp(a);
+        const int64_t nth = a.T * (kp / 8 + (a.N + nslot) * a.dh / 8);
+        wg_expand_kernel<T><<<blocks(nth), 256, 0, st>>>(a, a.wg_gcat, kp, a.wg_ocat, nslot);
         WgArgs wa{};
         wa.T = a.T;
         wa.splits = kWgSplits;
@@ -1777,15 +1987,13 @@ weights:
         if (e != hipSuccess) return e;
         // input side: dW_k, dW_v [d][G d_h], dW_qs [d][d_h] = x^T g; dW_q [N][d][d_h] from the
         // zero-expanded routed gradients
-        const uint16_t* dKb = reinterpret_cast<const uint16_t*>(a.dK);
-        const uint16_t* dVb = reinterpret_cast<const uint16_t*>(a.dV);
-        const uint16_t* dQb = reinterpret_cast<const uint16_t*>(a.dQ);
         const int gd = a.G * a.dh;
-        wa.job[0] = WgJob{xb, dKb, a.d, gd, a.d, gd, 0, 0, 0, a.dwk, 0};
-        wa.job[1] = WgJob{xb, dVb, a.d, gd, a.d, gd, 0, 0, 0, a.dwv, 0};
-        wa.job[2] = WgJob{xb, a.wg_gr, a.d, a.N * a.dh, a.d, a.N * a.dh, 0, 0, 0, a.dwq, 1};
+        const uint16_t* gc = a.wg_gcat;
+        wa.job[0] = WgJob{xb, gc, a.d, kp, a.d, gd, 0, 0, 0, a.dwk, 0};
+        wa.job[1] = WgJob{xb, gc + gd, a.d, kp, a.d, gd, 0, 0, 0, a.dwv, 0};
+        wa.job[2] = WgJob{xb, gc + 2 * gd + a.s * a.dh, a.d, kp, a.d, a.N * a.dh, 0, 0, 0, a.dwq, 1};
         wa.njobs = 3;
-        if (a.s) wa.job[wa.njobs++] = WgJob{xb, dQb + a.G * a.k * a.dh, a.d, a.H * a.dh, a.d, a.dh, 0, 0, 0, a.dwqs, 0};
+        if (a.s) wa.job[wa.njobs++] = WgJob{xb, gc + 2 * gd, a.d, kp, a.d, a.dh, 0, 0, 0, a.dwqs, 0};
         e = wg_launch(wa, st);
         if (e != hipSuccess) return e;
     } else {
@@ -1802,14 +2010,24 @@ weights:
     }
     if (km) km->mark(KT_BWD_WGRAD);
     if (km) km->begin(KT_BWD_DX);
-    // routed heads inside the dense product while that costs at most 4x their own work
-    const int expand = a.n <= 4 * a.k ? 1 : 0;
-    tgemm<ProbDxDense<T>, true, true>(mm, ProbDxDense<T>{a, 0, expand}, nt, a.d, 1, st);
-    if (!a.dense) tgemm<ProbDxDense<T>, true, true>(false, ProbDxDense<T>{a, 1, 0}, nt, a.d, 1, st);
-    if (!expand)
-        for (int g = 0; g < a.G; ++g)
-            for (int r = 0; r < a.k; ++r)
-                tgemm<ProbDxRouted<T>, true, true>(mm, ProbDxRouted<T>{a, L, g, r}, nt, a.d, a.n, st);
+    if (wgp) {
+        // bf16: dx = gcat wcat^T + dl W_r^T in one kernel (gcat from the weights stage)
+        const int kp = wg_kp(a);
+        wg_wcat_kernel<<<blocks((int64_t)a.d * (kp / 8)), 256, 0, st>>>(a, a.wg_wcat, kp);
+        const unsigned tiles = (unsigned)(ceil_div(a.T, 128) * ceil_div(a.d, 128));
+        dx_gemm_kernel<<<tiles, 256, 0, st>>>(a.wg_gcat, a.wg_wcat, a.dx, a.T, a.d, kp, a.dl, a.wr,
+                                              a.dense ? 0 : a.N);
+    } else {
+        // routed heads inside the dense product while that costs at most 4x their own work
+        const int expand = a.n <= 4 * a.k ? 1 : 0;
+        tgemm<ProbDxDense<T>, true, true>(mm, ProbDxDense<T>{a, 0, expand}, nt, a.d, 1, st);
+        if (!a.dense) tgemm<ProbDxDense<T>, true, true>(false, ProbDxDense<T>{a, 1, 0}, nt, a.d, 1, st);
+        if (!expand)
+            for (int g = 0; g < a.G; ++g)
+                for (int r = 0; r < a.k; ++r)
+                    tgemm<ProbDxRouted<T>, true, true>(mm, ProbDxRouted<T>{a, L, g, r}, nt, a.d, a.n, st);
+    
+    }
     if (km) km->mark(KT_BWD_DX);
     return hipGetLastError();
 }
@@ -1852,7 +2070,9 @@ hipError_t launch_backward(const GqeDims& D, const WorkPlan& P, const BwdPlan& B
     a.vr = (uint16_t*)(ws + BP.vr);
     a.dob = (uint16_t*)(ws + BP.dob);
     a.kvp = (float*)(ws + BP.kvp);
-    a.wg_gr = (uint16_t*)(ws + BP.wg_gr);
+    a.wg_gcat = (uint16_t*)(ws + BP.wg_gcat);
+    a.wg_wcat = (uint16_t*)(ws + BP.wg_wcat);
+    a.wg_wslot = (uint16_t*)(ws + BP.wg_wslot);
     a.wg_ocat = (uint16_t*)(ws + BP.wg_ocat);
     a.dx = gr.dx;
     a.dwr = gr.d_router;
@@ -1880,7 +2100,11 @@ hipError_t launch_backward(const GqeDims& D, const WorkPlan& P, const BwdPlan& B
     a.skv = D.skv;
     a.variant = D.variant;
     a.dense = D.dense;
-    a.NS = BP.NS;
+    // bf16 whole products over zero-expanded operands while the routed part costs at most 4x its
+    // own work (n <= 4k), the router term fits the dx product's epilogue (N <= 64) and the hidden
+    // size tiles the 64-wide slices of the U and dx products (d % 64 == 0)
+    a.wgp = (D.dtype == GQE_DTYPE_BF16 && D.d % 64 == 0 && D.n <= 4 * D.k && D.N <= 64) ? 1 : 0;
+    a.NS = a.wgp ? BP.NSX : BP.NS;
     a.Np = (int)round_up(D.N, 16);
     Lists L{(const int32_t*)(ws + BP.offs), (const int32_t*)(ws + BP.perm), (const int32_t*)(ws + BP.rank)};
     if (!D.dense) {
