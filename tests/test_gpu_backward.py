@@ -86,6 +86,9 @@ CASES = [
     _wl("bwd_dh16_k2", d=128, k=2, dh=16, B=2, S=130, seed=15),
     # n = 8 > 4 k: the routed dx pieces run as their own per-(group, rank) products
     _wl("bwd_n8_k1_routed_dx", N=16, G=2, k=1, dh=32, B=1, S=70, seed=16),
+    # bf16 with a hidden size that is not a multiple of 64: the per-block tiled products instead of
+    # the whole zero-expanded ones
+    _wl("bwd_bf16_d96_tiled", d=96, N=8, G=4, k=1, dh=32, B=1, S=90, seed=18),
     # the main setting's per-sequence shape (d 768, N 16, G 8, k 1, d_h 48, S 2048): the full-size
     # tiling, the split-K pieces over many token chunks, the key-block order over 32 key blocks
     _wl("bwd_main_setting_s2048", d=768, N=16, G=8, k=1, dh=48, B=1, S=2048, seed=17),
