@@ -477,6 +477,21 @@ __device__ __forceinline__ s16x4_t pack4(const float (&v)[4]) {
     return __builtin_bit_cast(s16x4_t, u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
 }
 __device__ __forceinline__ s16x4_t lds8(const uint16_t* p) { return *reinterpret_cast<const s16x4_t*>(p); }
+// sixteen bytes (eight bf16) from LDS or global memory, and two four-element pieces joined
+__device__ __forceinline__ bf16x8_t ld16b(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+__device__ __forceinline__ bf16x8_t join8(const s16x4_t& lo, const s16x4_t& hi) {
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+__device__ __forceinline__ f32x4_t mma32(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// c + A B for a 16 x 16 x 16 product whose sum c a 16 x 16 x 32 product may have just written: the
+// 16 x 16 x 16 product goes to its own zero accumulator and the two are added on the vector ALU.
+// Chained through the accumulator operand instead (no wait states between the two in the generated
+// code), the pair gave wrong sums on gfx950 in the parity tests.
+__device__ __forceinline__ f32x4_t mma16_add(const s16x4_t& a, const s16x4_t& b, const f32x4_t& c) {
+    return c + mma16(a, b, f32x4_t{0.f, 0.f, 0.f, 0.f});
+}
 __device__ __forceinline__ s16x4_t gld8(const uint16_t* p) { return *reinterpret_cast<const s16x4_t*>(p); }
 __device__ __forceinline__ float swap_x1(float v) {  // the value of lane ^ 1
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));
@@ -519,10 +534,15 @@ __global__ void bwd_mprep_kernel(BwdArgs a, uint16_t* __restrict__ Vr, uint16_t*
 // dk, dv of 128 keys (wave w: keys 32 w .. 32 w + 31, two 16-key column groups) of one (sequence,
 // group) over the later queries of every head of the group, query tiles of 64 staged in LDS
 // row-major and transposed; every fragment read from LDS feeds the products of both column groups.
+// 16 x 16 products in v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x16_bf16 for a last 16 head dims):
+// the score products contract the head dims, the gradient products P^T dO and dS^T Q contract 32
+// queries at a time -- the lane's four queries of two consecutive 16-query blocks, the transposed
+// tiles read in the same order.
 template <int DH>
 __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint16_t* __restrict__ Vr,
                                                            const uint16_t* __restrict__ dOb) {
-    constexpr int NC = DH / 16, P1 = DH + 8, P2 = 72;
+    constexpr int NC = DH / 16, N32 = DH / 32, R16 = (DH % 32) / 16, P1 = DH + 8, P2 = 72;
+    constexpr int F32 = N32 > 0 ? N32 : 1;
     __shared__ __align__(16) uint16_t Qs[64 * P1], dOs[64 * P1], QsT[DH * P2], dOsT[DH * P2];
     __shared__ float lss[64], dds[64];
     // longest first: key block 0 (every query tile after it) of every (group, sequence) leads
@@ -541,18 +561,27 @@ __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint
     const uint16_t* Vb = Vr + ((int64_t)(b * a.G + g) * a.S_pad) * DH;
     int64_t key[2];  // this lane's key column in each group
     bool kin[2];
-    s16x4_t kf[2][NC], vf[2][NC];
+    // key and value fragments of the score products: head dims 32 c + 8 j4 .. + 7, and of a last
+    // 16 (R16) dims 32 N32 + 4 j4 .. + 3
+    bf16x8_t kf[2][F32], vf[2][F32];
+    s16x4_t kt16[2], vt16[2];
     f32x4_t dk[2][NC], dv[2][NC];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         key[u] = (int64_t)kb * 128 + w * 32 + 16 * u + l16;
         kin[u] = key[u] < S;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            kf[u][c] = kin[u] ? gld8(Kb + key[u] * DH + 16 * c + 4 * j4) : s16x4_t{0, 0, 0, 0};
-            vf[u][c] = kin[u] ? gld8(Vb + key[u] * DH + 16 * c + 4 * j4) : s16x4_t{0, 0, 0, 0};
-            dk[u][c] = dv[u][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < N32; ++c) {
+            kf[u][c] = kin[u] ? ld16b(Kb + key[u] * DH + 32 * c + 8 * j4) : bf16x8_t{};
+            vf[u][c] = kin[u] ? ld16b(Vb + key[u] * DH + 32 * c + 8 * j4) : bf16x8_t{};
         }
+        kt16[u] = vt16[u] = s16x4_t{0, 0, 0, 0};
+        if (R16 && kin[u]) {
+            kt16[u] = gld8(Kb + key[u] * DH + 32 * N32 + 4 * j4);
+            vt16[u] = gld8(Vb + key[u] * DH + 32 * N32 + 4 * j4);
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) dk[u][c] = dv[u][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     const int nqt = (int)ceil_div(S, 64);
     const uint16_t* Qg = reinterpret_cast<const uint16_t*>(a.Q);
@@ -611,44 +640,68 @@ __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint
         }
         __syncthreads();
         if (it + 1 < total) fetch(it + 1);
+        // pairs of 16-query blocks: queries qp .. qp + 31 of the tile
 #pragma unroll
-        for (int qs = 0; qs < 4; ++qs) {
-            const int q0 = qs * 16;
-            s16x4_t qa[NC], da_[NC], qtb[NC], dtb[NC];
+        for (int qp = 0; qp < 64; qp += 32) {
+            bf16x8_t qa[2][F32], da_[2][F32];
+            s16x4_t qa16[2], da16[2];
+            float lq[2][4], dq4[2][4];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int q0 = qp + 16 * h2;
+#pragma unroll
+                for (int c = 0; c < N32; ++c) {
+                    qa[h2][c] = ld16b(&Qs[(q0 + l16) * P1 + 32 * c + 8 * j4]);
+                    da_[h2][c] = ld16b(&dOs[(q0 + l16) * P1 + 32 * c + 8 * j4]);
+                }
+                qa16[h2] = da16[h2] = s16x4_t{0, 0, 0, 0};
+                if (R16) {
+                    qa16[h2] = lds8(&Qs[(q0 + l16) * P1 + 32 * N32 + 4 * j4]);
+                    da16[h2] = lds8(&dOs[(q0 + l16) * P1 + 32 * N32 + 4 * j4]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    lq[h2][i] = lss[q0 + 4 * j4 + i];
+                    dq4[h2][i] = dds[q0 + 4 * j4 + i];
+                }
+            }
+            // transposed Q and dO: head dim 16 c + l16, the lane's queries of both blocks
+            bf16x8_t qtb[NC], dtb[NC];
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                qa[c] = lds8(&Qs[(q0 + l16) * P1 + 16 * c + 4 * j4]);
-                da_[c] = lds8(&dOs[(q0 + l16) * P1 + 16 * c + 4 * j4]);
-                qtb[c] = lds8(&QsT[(16 * c + l16) * P2 + q0 + 4 * j4]);
-                dtb[c] = lds8(&dOsT[(16 * c + l16) * P2 + q0 + 4 * j4]);
-            }
-            float lq[4], dq4[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                lq[i] = lss[q0 + 4 * j4 + i];
-                dq4[i] = dds[q0 + 4 * j4 + i];
+                const int r = (16 * c + l16) * P2 + qp + 4 * j4;
+                qtb[c] = join8(lds8(&QsT[r]), lds8(&QsT[r + 16]));
+                dtb[c] = join8(lds8(&dOsT[r]), lds8(&dOsT[r + 16]));
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                f32x4_t sacc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+                float p[8], ds[8];
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c = 0; c < N32; ++c) {
+                        sacc = mma32(qa[h2][c], kf[u][c], sacc);
+                        dp = mma32(da_[h2][c], vf[u][c], dp);
+                    }
+                    if (R16) {
+                        sacc = mma16_add(qa16[h2], kt16[u], sacc);
+                        dp = mma16_add(da16[h2], vt16[u], dp);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int64_t qpos = (int64_t)qt * 64 + qp + 16 * h2 + 4 * j4 + i;
+                        const bool on = kin[u] && qpos < S && qpos >= key[u];
+                        p[4 * h2 + i] = on ? __builtin_amdgcn_exp2f(sacc[i] - lq[h2][i]) : 0.f;
+                        ds[4 * h2 + i] = on ? p[4 * h2 + i] * (dp[i] - dq4[h2][i]) : 0.f;
+                    }
+                }
+                const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, pack8(p));
+                const bf16x8_t dsa = __builtin_bit_cast(bf16x8_t, pack8(ds));
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    sacc = mma16(qa[c], kf[u][c], sacc);
-                    dp = mma16(da_[c], vf[u][c], dp);
-                }
-                float p[4], ds[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t qp = (int64_t)qt * 64 + q0 + 4 * j4 + i;
-                    const bool on = kin[u] && qp < S && qp >= key[u];
-                    p[i] = on ? __builtin_amdgcn_exp2f(sacc[i] - lq[i]) : 0.f;
-                    ds[i] = on ? p[i] * (dp[i] - dq4[i]) : 0.f;
-                }
-                const s16x4_t pa = pack4(p), dsa = pack4(ds);
-#pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    dv[u][c] = mma16(pa, dtb[c], dv[u][c]);
-                    dk[u][c] = mma16(dsa, qtb[c], dk[u][c]);
+                    dv[u][c] = mma32(pa, dtb[c], dv[u][c]);
+                    dk[u][c] = mma32(dsa, qtb[c], dk[u][c]);
                 }
             }
         }
@@ -699,7 +752,8 @@ __global__ void bwd_kv_sum_kernel(BwdArgs a) {
 template <int DH>
 __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint16_t* __restrict__ Vr,
                                                           const uint16_t* __restrict__ dOb) {
-    constexpr int NC = DH / 16, P1 = DH + 8, P2 = 72;
+    constexpr int NC = DH / 16, N32 = DH / 32, R16 = (DH % 32) / 16, P1 = DH + 8, P2 = 72;
+    constexpr int F32 = N32 > 0 ? N32 : 1;
     __shared__ __align__(16) uint16_t Ks[64 * P1], Vs[64 * P1], KsT[DH * P2];
     // longest first: the last query block (every key tile before it) of every (head, sequence) leads
     const int nqb = (int)ceil_div(a.S, 64);
@@ -712,11 +766,22 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
     const int64_t qpos = (int64_t)qb * 64 + w * 16 + l16;  // this lane's query column
     const bool qin = qpos < S;
     const uint16_t* Qg = reinterpret_cast<const uint16_t*>(a.Q);
-    s16x4_t qf[NC], df[NC];
+    // query and dO fragments of the score products: head dims 32 c + 8 j4 .. + 7, and of a last 16
+    // (R16) dims 32 N32 + 4 j4 .. + 3
+    bf16x8_t qf[F32], df[F32];
+    s16x4_t qf16 = {0, 0, 0, 0}, df16 = {0, 0, 0, 0};
+    {
+        const uint16_t* qrow = Qg + (((int64_t)b * a.H + h) * S + qpos) * DH;
+        const uint16_t* drow = dOb + (((int64_t)b * a.H + h) * a.S_pad + qpos) * DH;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        qf[c] = qin ? gld8(Qg + (((int64_t)b * a.H + h) * S + qpos) * DH + 16 * c + 4 * j4) : s16x4_t{0, 0, 0, 0};
-        df[c] = qin ? gld8(dOb + (((int64_t)b * a.H + h) * a.S_pad + qpos) * DH + 16 * c + 4 * j4) : s16x4_t{0, 0, 0, 0};
+        for (int c = 0; c < N32; ++c) {
+            qf[c] = qin ? ld16b(qrow + 32 * c + 8 * j4) : bf16x8_t{};
+            df[c] = qin ? ld16b(drow + 32 * c + 8 * j4) : bf16x8_t{};
+        }
+        if (R16 && qin) {
+            qf16 = gld8(qrow + 32 * N32 + 4 * j4);
+            df16 = gld8(drow + 32 * N32 + 4 * j4);
+        }
     }
     const float Dq = qin ? a.Dd[(b * S + qpos) * a.H + h] : 0.f;
     const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + ((int64_t)(b * a.G + g) * a.S_pad) * DH;
@@ -725,7 +790,10 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
     // pass 1 (iterations 0 .. ntile - 1): each lane folds its four keys of every sub-tile into
     // (m, l); then the four lanes of a query column are combined into the row log-sum-exp L.
     // pass 2 (ntile .. 2 ntile - 1): dS^T = P^T (dP^T - D), dq += dS K.  The next iteration's key
-    // (and value) tile is loaded into registers while the current one multiplies.
+    // (and value) tile is loaded into registers while the current one multiplies.  16 x 16 products in
+    // v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x16_bf16 for a last 16 head dims); dq += dS K
+    // contracts 32 keys at a time (the lane's four keys of two consecutive 16-key sub-tiles, K^T read
+    // in the same order).
     // staging: thread = (four neighbouring rows, one 8-dim chunk); R = the four rows
     constexpr int NQC = 16 * (DH / 8), R = 4;
     static_assert(NQC <= 256, "d_h <= 128");
@@ -796,13 +864,19 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
             }
             L = m + __builtin_amdgcn_logf(l);
         }
+        // S^T (rows keys k0 + 4 j4 + i, column the lane's query) of one 16-key sub-tile
+        auto scores = [&](const uint16_t* Tl, int k0, const bf16x8_t (&f)[F32], const s16x4_t& f16) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < N32; ++c) acc = mma32(ld16b(&Tl[(k0 + l16) * P1 + 32 * c + 8 * j4]), f[c], acc);
+            if (R16) acc = mma16_add(lds8(&Tl[(k0 + l16) * P1 + 32 * N32 + 4 * j4]), f16, acc);
+            return acc;
+        };
         if (!full) {
 #pragma unroll
             for (int sub = 0; sub < 4; ++sub) {
                 const int k0 = sub * 16;
-                f32x4_t st = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c = 0; c < NC; ++c) st = mma16(lds8(&Ks[(k0 + l16) * P1 + 16 * c + 4 * j4]), qf[c], st);
+                const f32x4_t st = scores(Ks, k0, qf, qf16);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int64_t kp = (int64_t)kt * 64 + k0 + 4 * j4 + i;
@@ -815,24 +889,25 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
             }
         } else {
 #pragma unroll
-            for (int sub = 0; sub < 4; ++sub) {
-                const int k0 = sub * 16;
-                f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
+            for (int sp = 0; sp < 64; sp += 32) {
+                float ds[8];
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const int k0 = sp + 16 * h2;
+                    const f32x4_t st = scores(Ks, k0, qf, qf16), dpt = scores(Vs, k0, df, df16);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int64_t kp = (int64_t)kt * 64 + k0 + 4 * j4 + i;
+                        const bool on = qin && kp <= qpos && kp < S;
+                        ds[4 * h2 + i] = on ? __builtin_amdgcn_exp2f(st[i] - L) * (dpt[i] - Dq) : 0.f;
+                    }
+                }
+                const bf16x8_t da = __builtin_bit_cast(bf16x8_t, pack8(ds));
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    st = mma16(lds8(&Ks[(k0 + l16) * P1 + 16 * c + 4 * j4]), qf[c], st);
-                    dpt = mma16(lds8(&Vs[(k0 + l16) * P1 + 16 * c + 4 * j4]), df[c], dpt);
+                    const int r = (16 * c + l16) * P2 + sp + 4 * j4;
+                    dq[c] = mma32(da, join8(lds8(&KsT[r]), lds8(&KsT[r + 16])), dq[c]);
                 }
-                float ds[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t kp = (int64_t)kt * 64 + k0 + 4 * j4 + i;
-                    const bool on = qin && kp <= qpos && kp < S;
-                    ds[i] = on ? __builtin_amdgcn_exp2f(st[i] - L) * (dpt[i] - Dq) : 0.f;
-                }
-                const s16x4_t da = pack4(ds);
-#pragma unroll
-                for (int c = 0; c < NC; ++c) dq[c] = mma16(da, lds8(&KsT[(16 * c + l16) * P2 + k0 + 4 * j4]), dq[c]);
             }
         }
     }
