@@ -65,6 +65,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
     __shared__ __align__(1024) uint16_t ol[2][kBM * PO * 8];
     __shared__ __align__(16) uint8_t rj[kBM * kGKMax];  // expert index inside the group, per choice
     __shared__ float rc[COEF ? kBM * kGKMax : 1]; // p (weighted_concat) or w (gqe) per choice
+    __shared__ __align__(16) uint16_t zr[C8 * 8];   // a zero token row: unchosen tokens read it
+    static_assert(COEF || KH == 1, "the select-only form handles one head per unit");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -122,6 +124,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
     issue_o(0);
     issue_w(0);
     if (a.NS > 1) issue_w(1);
+    if (tid < C8) *reinterpret_cast<u32x4_t*>(&zr[8 * tid]) = u32x4_t{0u, 0u, 0u, 0u};
 
     // ---- routing of the tile's tokens (routed mode): expert index inside the group per choice
     if (!a.dense) {
@@ -171,7 +174,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
     int unit = 0, u = 0;  // position of the stage: unit, slot inside the unit (wave-uniform)
     for (int st = 0; st < a.NS; ++st) {
         const bool routed = unit < a.NUM && !a.dense;
-        if (routed && u == 0) {
+        if (!COEF && routed && u == 0) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) jr[i][0] = rj[(trow0 + 32 * i) * kGKMax + unit];
+        }
+        if (COEF && routed && u == 0) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -189,11 +196,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
             if (u < a.n) kind = a.variant == GQE_VARIANT_WEIGHTED_CONCAT ? 2 : 1;
             else kind = KH == 1 ? 0 : 2;
         }
+        // token rows of this slot's fragments: the select-only form points an unchosen token at
+        // the zero row, so its fragments need no per-element select
+        const uint16_t* const ob = ol[unit & 1];
+        const uint16_t* tb[2];
+        const bool sel = routed && u < a.n;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            tb[i] = (!COEF && sel && jr[i][0] != u) ? zr : ob + (trow0 + 32 * i) * PO * 8;
         int off[2];
         bool valid[2];
         float coef[2][KH];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; COEF && i < 2; ++i) {
             off[i] = 0;
             valid[i] = true;
             if (kind == 1) {
@@ -215,25 +230,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
         const bool o_next = u == 0 && unit + 1 < NU;
         const bool ahead = st + 2 < a.NS;
         const uint16_t* wb = wl[st % 3];
-        const uint16_t* ob = ol[unit & 1];
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            bf16x8_t wf[2], tf[2];
+        auto frag = [&](int kk, bf16x8_t (&wf)[2], bf16x8_t (&tf)[2]) {
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
                 wf[cb] = *reinterpret_cast<const bf16x8_t*>(wb + ((wcol0 + 32 * cb) * PW + 2 * kk + hsel) * 8);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const uint16_t* orow_p = ob + ((trow0 + 32 * i) * PO + 2 * kk + hsel) * 8;
-                if (!COEF || kind != 2) {
-                    u32x4_t v = *reinterpret_cast<const u32x4_t*>(orow_p + off[i] * 8);
+                if (!COEF) {
+                    tf[i] = *reinterpret_cast<const bf16x8_t*>(tb[i] + (2 * kk + hsel) * 8);
+                } else if (kind != 2) {
+                    u32x4_t v = *reinterpret_cast<const u32x4_t*>(tb[i] + (2 * kk + hsel + off[i]) * 8);
                     if (!valid[i]) v = u32x4_t{0u, 0u, 0u, 0u};
                     tf[i] = __builtin_bit_cast(bf16x8_t, v);
                 } else {
                     float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int r = 0; r < KH; ++r) {
-                        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(orow_p + r * C8 * 8);
+                        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(tb[i] + (2 * kk + hsel + r * C8) * 8);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             f[2 * e] += coef[i][r] * __uint_as_float(v[e] << 16);
@@ -245,11 +258,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
                     tf[i] = __builtin_bit_cast(bf16x8_t, pk);
                 }
             }
+        };
+        bf16x8_t wf[2][2], tf[2][2];
+        frag(0, wf[0], tf[0]);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            if (kk + 1 < KS) frag(kk + 1, wf[(kk + 1) & 1], tf[(kk + 1) & 1]);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb)
-                    acc[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb], tf[i], acc[i][cb], 0, 0, 0);
+                    acc[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk & 1][cb], tf[kk & 1][i], acc[i][cb], 0, 0, 0);
             if (kk == 0 && o_next) issue_o(unit + 1);
             if (kk == 1 && ahead) issue_w(st + 2);
         }
