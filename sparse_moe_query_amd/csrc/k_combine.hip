@@ -11,9 +11,9 @@
 // the layer output is y = A @ W_stack, W_stack = [W_o[g*n..g*n+n-1]; W_oR[g] for g; W_os].
 // A is never materialised: its fragments are formed in registers from the head outputs.
 //
-// Work item: 128 tokens x 128 output columns; four waves in 2 x 2, each 64 x 64 = 2 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16 computing y^T = W_stack^T A^T (every lane stores four consecutive
-// output columns).  The reduction runs slot by slot (one stage = d_h rows of W_stack):
+// Work item: 128 tokens x 128 output columns; eight waves in 2 x 4, each 64 tokens x 32 columns =
+// 2 blocks of v_mfma_f32_32x32x16_bf16 computing y^T = W_stack^T A^T (every lane stores four
+// consecutive output columns); two work groups per CU, four waves per SIMD.  The reduction runs slot by slot (one stage = d_h rows of W_stack):
 //   W_stack   pre-packed per (column tile, slot) as the exact LDS image ([128 cols][odd pitch]
 //             16-byte chunks, zero pad chunk) and copied by global_load_lds_dwordx4 into a ring
 //             of three stages, two slots ahead of the one being multiplied
@@ -34,6 +34,10 @@ namespace {
 
 constexpr int kBM = 128;
 constexpr int kBN = 128;
+constexpr int kWaves = 8;           // 2 x 4: waves along the tokens x along the output columns
+constexpr int kWN = 4;
+constexpr int kCB = kBN / kWN / 32;  // 32-column blocks per wave
+constexpr int kThreads = 64 * kWaves;
 constexpr int kGKMax = 16;  // routing entries per token staged in LDS (groups x choices)
 
 __host__ __device__ constexpr int odd_pitch(int chunks) { return (chunks & 1) ? chunks : chunks + 1; }
@@ -54,12 +58,12 @@ struct CombArgs {
 };
 
 template <int DH, int KH, bool COEF>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) combine_kernel(CombArgs a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) combine_kernel(CombArgs a) {
     constexpr int C8 = DH / 8;                // 16-byte chunks per head row
     constexpr int PW = odd_pitch(C8);         // W_stack stage pitch (chunks per output column)
     constexpr int PO = odd_pitch(KH * C8);    // O stage pitch (chunks per token)
-    constexpr int SEGW = kBN * PW * 16 / 1024, LW = (SEGW + 3) / 4;
-    constexpr int SEGO = kBM * PO * 16 / 1024, LO = (SEGO + 3) / 4;
+    constexpr int SEGW = kBN * PW * 16 / 1024, LW = (SEGW + kWaves - 1) / kWaves;
+    constexpr int SEGO = kBM * PO * 16 / 1024, LO = (SEGO + kWaves - 1) / kWaves;
     constexpr int KS = DH / 16;
     __shared__ __align__(1024) uint16_t wl[3][kBN * PW * 8];
     __shared__ __align__(1024) uint16_t ol[2][kBM * PO * 8];
@@ -70,7 +74,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w / kWN, wn = w % kWN;
     const int ncol = a.d / kBN;
     const int ntile = (int)ceil_div(a.T, kBM);
     // XCD-aware: the column tiles of one token tile run on one XCD (they share the O rows)
@@ -95,7 +99,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
         const bf16_t* src = wtile + (int64_t)st * kBN * PW * 8;
 #pragma unroll
         for (int i = 0; i < LW; ++i) {
-            const int seg = min(w + 4 * i, SEGW - 1);
+            const int seg = min(w + kWaves * i, SEGW - 1);
             dma16(src, (uint32_t)(seg * 1024 + 16 * lane), &wl[st % 3][seg * 512]);
         }
     };
@@ -105,7 +109,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
     int ochk[LO];
 #pragma unroll
     for (int i = 0; i < LO; ++i) {
-        const int q = min(w + 4 * i, SEGO - 1) * 64 + lane;
+        const int q = min(w + kWaves * i, SEGO - 1) * 64 + lane;
         const int64_t rmax = a.T - 1 - t0;
         const int r = q / PO;
         orow[i] = (uint32_t)((r < rmax ? r : rmax) * a.H * DH * 2);
@@ -117,7 +121,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
 #pragma unroll
         for (int i = 0; i < LO; ++i) {
             const int c = ochk[i] < nh * C8 ? ochk[i] : 0;
-            dma16(base, orow[i] + 16 * c, &ol[unit & 1][(min(w + 4 * i, SEGO - 1)) * 512]);
+            dma16(base, orow[i] + 16 * c, &ol[unit & 1][(min(w + kWaves * i, SEGO - 1)) * 512]);
         }
     };
 
@@ -129,7 +133,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
     // ---- routing of the tile's tokens (routed mode): expert index inside the group per choice
     if (!a.dense) {
         const int GK = a.G * a.k;
-        for (int q = tid; q < kBM * GK; q += 256) {
+        for (int q = tid; q < kBM * GK; q += kThreads) {
             const int row = q / GK, e = q % GK;
             const int64_t t = t0 + row;
             uint8_t j = 0xff;
@@ -147,14 +151,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
     else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
     __syncthreads();
 
-    f32x16_t acc[2][2];
+    f32x16_t acc[2][kCB];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+        for (int j = 0; j < kCB; ++j) acc[i][j] = f32x16_t{};
 
     const int trow0 = 64 * wm + (lane & 31);          // token rows trow0, trow0 + 32
-    const int wcol0 = 64 * wn + (lane & 31);          // output columns wcol0, wcol0 + 32
+    const int wcol0 = 32 * kCB * wn + (lane & 31);    // output columns wcol0 (+ 32)
     const int hsel = lane >> 5;                       // which 8 of the 16 reduction rows
     // the choices of the lane's two tokens for every group (one byte each), kept in registers
     u32x4_t jw[2];
@@ -230,9 +234,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
         const bool o_next = u == 0 && unit + 1 < NU;
         const bool ahead = st + 2 < a.NS;
         const uint16_t* wb = wl[st % 3];
-        auto frag = [&](int kk, bf16x8_t (&wf)[2], bf16x8_t (&tf)[2]) {
+        auto frag = [&](int kk, bf16x8_t (&wf)[kCB], bf16x8_t (&tf)[2]) {
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
+            for (int cb = 0; cb < kCB; ++cb)
                 wf[cb] = *reinterpret_cast<const bf16x8_t*>(wb + ((wcol0 + 32 * cb) * PW + 2 * kk + hsel) * 8);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -259,7 +263,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
                 }
             }
         };
-        bf16x8_t wf[2][2], tf[2][2];
+        bf16x8_t wf[2][kCB], tf[2][2];
         frag(0, wf[0], tf[0]);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
@@ -267,7 +271,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int cb = 0; cb < 2; ++cb)
+                for (int cb = 0; cb < kCB; ++cb)
                     acc[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk & 1][cb], tf[kk & 1][i], acc[i][cb], 0, 0, 0);
             if (kk == 0 && o_next) issue_o(unit + 1);
             if (kk == 1 && ahead) issue_w(st + 2);
@@ -293,14 +297,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
         }
     }
 
-    // ---- epilogue: acc[i][cb] is y^T for token trow0 + 32 i, columns 64 wn + 32 cb + rows
+    // ---- epilogue: acc[i][cb] is y^T for token trow0 + 32 i, columns 32 (kCB wn + cb) + rows
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int64_t t = t0 + trow0 + 32 * i;
         if (t >= a.T) continue;
-        bf16_t* yr = a.y + t * a.d + ct * kBN + 64 * wn;
+        bf16_t* yr = a.y + t * a.d + ct * kBN + 32 * kCB * wn;
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+        for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int col = 32 * cb + 8 * q + 4 * hsel;
@@ -314,10 +318,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) c
 template <int DH>
 hipError_t launch_dh(const CombArgs& a, bool coef, unsigned grid, hipStream_t st) {
     if (a.KHU == 1) {
-        if (coef) combine_kernel<DH, 1, true><<<grid, 256, 0, st>>>(a);
-        else combine_kernel<DH, 1, false><<<grid, 256, 0, st>>>(a);
+        if (coef) combine_kernel<DH, 1, true><<<grid, kThreads, 0, st>>>(a);
+        else combine_kernel<DH, 1, false><<<grid, kThreads, 0, st>>>(a);
     } else {
-        combine_kernel<DH, 2, true><<<grid, 256, 0, st>>>(a);
+        combine_kernel<DH, 2, true><<<grid, kThreads, 0, st>>>(a);
     }
     return hipGetLastError();
 }
