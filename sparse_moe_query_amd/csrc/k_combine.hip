@@ -65,8 +65,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
     constexpr int SEGW = kBN * PW * 16 / 1024, LW = (SEGW + kWaves - 1) / kWaves;
     constexpr int SEGO = kBM * PO * 16 / 1024, LO = (SEGO + kWaves - 1) / kWaves;
     constexpr int KS = DH / 16;
-    __shared__ __align__(1024) uint16_t wl[3][kBN * PW * 8];
-    __shared__ __align__(1024) uint16_t ol[2][kBM * PO * 8];
+    constexpr int WST = kBN * PW * 8, OST = kBM * PO * 8;  // stage sizes (bf16)
+    // W ring (three stages) and O double buffer in one array: the epilogue reuses all of it
+    __shared__ __align__(1024) uint16_t lbuf[3 * WST + 2 * OST];
+    uint16_t* const wl = lbuf;
+    uint16_t* const ol = lbuf + 3 * WST;
     __shared__ __align__(16) uint8_t rj[kBM * kGKMax];  // expert index inside the group, per choice
     __shared__ float rc[COEF ? kBM * kGKMax : 1]; // p (weighted_concat) or w (gqe) per choice
     __shared__ __align__(16) uint16_t zr[C8 * 8];   // a zero token row: unchosen tokens read it
@@ -100,7 +103,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
 #pragma unroll
         for (int i = 0; i < LW; ++i) {
             const int seg = min(w + kWaves * i, SEGW - 1);
-            dma16(src, (uint32_t)(seg * 1024 + 16 * lane), &wl[st % 3][seg * 512]);
+            dma16(src, (uint32_t)(seg * 1024 + 16 * lane), wl + (st % 3) * WST + seg * 512);
         }
     };
     // O rows: chunk slot q of the stage = (token row q / PO, chunk q % PO); rows past the last
@@ -121,7 +124,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
 #pragma unroll
         for (int i = 0; i < LO; ++i) {
             const int c = ochk[i] < nh * C8 ? ochk[i] : 0;
-            dma16(base, orow[i] + 16 * c, &ol[unit & 1][(min(w + kWaves * i, SEGO - 1)) * 512]);
+            dma16(base, orow[i] + 16 * c, ol + (unit & 1) * OST + min(w + kWaves * i, SEGO - 1) * 512);
         }
     };
 
@@ -202,7 +205,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
         }
         // token rows of this slot's fragments: the select-only form points an unchosen token at
         // the zero row, so its fragments need no per-element select
-        const uint16_t* const ob = ol[unit & 1];
+        const uint16_t* const ob = ol + (unit & 1) * OST;
         const uint16_t* tb[2];
         const bool sel = routed && u < a.n;
 #pragma unroll
@@ -233,7 +236,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
         // work: the next unit's rows when this unit starts, then the slot two ahead
         const bool o_next = u == 0 && unit + 1 < NU;
         const bool ahead = st + 2 < a.NS;
-        const uint16_t* wb = wl[st % 3];
+        const uint16_t* wb = wl + (st % 3) * WST;
         auto frag = [&](int kk, bf16x8_t (&wf)[kCB], bf16x8_t (&tf)[2]) {
 #pragma unroll
             for (int cb = 0; cb < kCB; ++cb)
@@ -297,21 +300,34 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
         }
     }
 
-    // ---- epilogue: acc[i][cb] is y^T for token trow0 + 32 i, columns 32 (kCB wn + cb) + rows
+    // ---- epilogue: acc[i][cb] is y^T for token trow0 + 32 i, columns 32 (kCB wn + cb) + rows.
+    // The tile goes through LDS (the stage buffers are free: the last slot's barrier is behind
+    // every wave's reads of them, and no copy is in flight) so that y is written as whole 256-byte token rows:
+    // stored straight from the accumulators, every store instruction would write 16-byte pieces of
+    // 32 different rows.
+    constexpr int YP = kBN + 8;  // row pitch in bf16 (272 bytes: consecutive rows 4 banks apart)
+    static_assert(kBM * YP <= 3 * WST + 2 * OST, "the output tile fits in the stage buffers");
+    uint16_t* ys = lbuf;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int64_t t = t0 + trow0 + 32 * i;
-        if (t >= a.T) continue;
-        bf16_t* yr = a.y + t * a.d + ct * kBN + 32 * kCB * wn;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int col = 32 * cb + 8 * q + 4 * hsel;
-                u32x2_t pk = {pack_bf16x2(acc[i][cb][4 * q], acc[i][cb][4 * q + 1]),
-                              pack_bf16x2(acc[i][cb][4 * q + 2], acc[i][cb][4 * q + 3])};
-                *reinterpret_cast<u32x2_t*>(yr + col) = pk;
+                const int col = 32 * kCB * wn + 32 * cb + 8 * q + 4 * hsel;
+                *reinterpret_cast<u32x2_t*>(&ys[(trow0 + 32 * i) * YP + col]) =
+                    u32x2_t{pack_bf16x2(acc[i][cb][4 * q], acc[i][cb][4 * q + 1]),
+                            pack_bf16x2(acc[i][cb][4 * q + 2], acc[i][cb][4 * q + 3])};
             }
+    __syncthreads();
+    constexpr int CH = kBN / 8;  // 16-byte chunks per token row of the tile
+#pragma unroll
+    for (int it = 0; it < kBM * CH / kThreads; ++it) {
+        const int q = tid + kThreads * it, row = q / CH, ch = q % CH;
+        const int64_t t = t0 + row;
+        if (t < a.T)
+            *reinterpret_cast<u32x4_t*>(a.y + t * a.d + ct * kBN + 8 * ch) =
+                *reinterpret_cast<const u32x4_t*>(&ys[row * YP + 8 * ch]);
     }
 }
 
