@@ -525,6 +525,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
         }
         return;
     }
+    // The normalised bf16 tile of the wave's 64 query columns goes through a wave-private LDS
+    // region (the K / V stages are free: the loop's last barrier is behind every wave's reads and
+    // no load is in flight) so that each (token, head) row of O is written in 16-byte pieces;
+    // from the accumulators a lane holds one head dim of a row, and every store would write
+    // 2-byte elements of two rows.
+    constexpr int SP = DH + 8;  // staging pitch (bf16): 16-byte aligned rows
+    static_assert(2 * kQW * SP <= NSTAGE * TILE_K && 2 * kQW * SP <= NSTAGE * TILE_V, "staging fits");
+    uint16_t* const ost = (w < 2 ? &ks_lds[0][0] : &vs_lds[0][0]) + (w & 1) * kQW * SP;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
         float ltot = 0.f;  // !ONES: the full row sum of the lane's column (both key halves)
@@ -538,17 +546,25 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
             const int row = 8 * (j >> 2) + 4 * hsel + (j & 3);
             const float lrow_sum = ONES ? __shfl(oacc[qt][CBS < NCB ? CBS : 0][j], CS + 32 * hsel) : __shfl(ltot, row);
             const float sc = 1.0f / lrow_sum;
-            const int c = w * kQW + qt * 32 + row;
-            const int p = c / NH, h = c % NH;
-            const int pos = p0 + p;
-            if (p >= np || pos >= S) continue;
-            const int v = h < a.k ? ig * a.k + h : a.G * a.k;
-            bf16_t* orow = a.O + (((int64_t)ib * S + pos) * a.H + v) * DH;
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 const int n = 32 * cb + lrow;
-                if (n < DH) orow[n] = from_f32<bf16_t>(oacc[qt][cb][j] * sc);
+                if (n < DH) ost[(qt * 32 + row) * SP + n] = from_f32<bf16_t>(oacc[qt][cb][j] * sc).bits;
             }
+        }
+    }
+    __syncthreads();
+    constexpr int C8 = DH / 8;  // 16-byte pieces per row
+#pragma unroll
+    for (int it = 0; it < C8; ++it) {
+        const int q = lane + 64 * it, r = q / C8, ch = q - r * C8;
+        const int c = w * kQW + r;
+        const int p = c / NH, h = c - p * NH;
+        const int pos = p0 + p;
+        if (p < np && pos < S) {
+            const int v = h < a.k ? ig * a.k + h : a.G * a.k;
+            *reinterpret_cast<u32x4_t*>(a.O + (((int64_t)ib * S + pos) * a.H + v) * DH + 8 * ch) =
+                *reinterpret_cast<const u32x4_t*>(&ost[r * SP + 8 * ch]);
         }
     }
 }

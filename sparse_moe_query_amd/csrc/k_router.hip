@@ -10,13 +10,14 @@
 // the lower local index.
 //
 // Fast path (d % 64 == 0, N <= 16): v_mfma_f64_16x16x4_f64 (full-rate fp64 on gfx950).  A block
-// owns 64 tokens; wave w of 4 sums the w-th quarter of the hidden dimension for all of them, its
-// x and weight loads issued three 32-wide chunks at a time ahead of the products.  Each lane
+// owns 64 tokens; wave w of 8 (two per SIMD, so one wave's conversions overlap the other's
+// products) sums the w-th eighth of the hidden dimension for all of them, its x and weight loads
+// issued three 32-wide chunks at a time ahead of the products.  Each lane
 // loads eight consecutive hidden values of one token with one 16-byte load; the k index of the
 // MFMA is permuted accordingly (k-step s of lane group q covers hidden index 8q + s), and the
 // router weights are pre-permuted into exactly that lane order ([octet of 8 hidden indices]
 // [column][8], by gqe_pack_weights), so the B operands are 64 contiguous bytes per lane.  The
-// four partial sums are added in a fixed order; two blocks fit one CU (68 KB of LDS each).
+// eight partial sums are added in a fixed order (103 KB of LDS: one block per CU).
 // Generic path (any d, N <= 64): one token per lane, float64 FMAs with the weights as wave-uniform
 // scalar operands.
 #include "gqe_common.h"
@@ -145,8 +146,8 @@ __device__ void select_and_stats(const RouterArgs& a, double (*lg)[65], int* cnt
 }
 
 template <typename Tin>
-__global__ void __launch_bounds__(256) router_mfma_kernel(RouterArgs a) {
-    constexpr int kW = 4;  // waves; wave w sums the w-th quarter of the hidden dimension
+__global__ void __launch_bounds__(512) router_mfma_kernel(RouterArgs a) {
+    constexpr int kW = 8;  // waves; wave w sums the w-th eighth of the hidden dimension
     __shared__ double red[kW][kTok][17];
     __shared__ double lg[kTok][65];
     __shared__ int cnt[64];
@@ -393,8 +394,8 @@ hipError_t launch_router(const GqeDims& D, const WorkPlan& P, const void* x, con
     const bool bf = D.dtype == GQE_DTYPE_BF16;
     if (km) km->begin(KT_ROUTER);
     if (router_uses_mfma(D)) {
-        if (bf) router_mfma_kernel<bf16_t><<<grid, 256, 0, st>>>(a);
-        else router_mfma_kernel<float><<<grid, 256, 0, st>>>(a);
+        if (bf) router_mfma_kernel<bf16_t><<<grid, 512, 0, st>>>(a);
+        else router_mfma_kernel<float><<<grid, 512, 0, st>>>(a);
     } else {
         if (bf) router_valu_kernel<bf16_t><<<grid, 256, 0, st>>>(a);
         else router_valu_kernel<float><<<grid, 256, 0, st>>>(a);
