@@ -71,6 +71,8 @@ WorkPlan make_plan(const GqeDims& D, int64_t B, int64_t S, const AttnCounts& ac)
     P.nslots = ac.nslots;
     P.part_o = take((size_t)ac.nslots * GQE_ATTN_COLS * D.dh * 4);
     P.part_ml = take((size_t)ac.nslots * GQE_ATTN_COLS * 2 * 4);
+    P.lse = take((size_t)P.T * D.H * 4);
+    P.lse_ok = false;
     P.sched_jobs = take((size_t)ac.njobs * sizeof(AttnJob));
     P.sched_merges = take((size_t)ac.nmerges * sizeof(AttnMerge));
     P.sched_scratch = take(ac.njobs > 0 ? attn_sched_scratch_bytes(ac) : 0);
@@ -426,6 +428,7 @@ int gqe_forward_impl(gqe_handle_t* h, const void* x, void* y, int64_t batch, int
     h->ran = true;
     h->last_ws = workspace;
     h->last_plan = P;
+    h->last_plan.lse_ok = h->mfma_attn;
     return ok();
 }
 

@@ -122,6 +122,8 @@ struct WorkPlan {
     size_t kn;                        // per-key norms [B][G][S_pad] f32
     size_t knt;                       // per-64-key-tile maximum norm [B][G][S_pad/64] f32
     size_t part_o, part_ml;           // attention partials [nslots][256][d_h] / [nslots][256][2] f32
+    size_t lse;                       // [T][H] f32 row log-sum-exp (log2 units) of the attention
+    bool lse_ok;                      // the last forward wrote lse (matrix-core attention)
     int64_t nslots;
     // the attention schedule, built on the device by every forward (matrix-core attention only):
     // jobs [njobs][8], merges [nmerges][8] int32, and the builder's scratch

@@ -49,6 +49,7 @@ struct AttnArgs {
     bf16_t* O;
     float* part_o;        // partial results of split items: [slot][256 columns][d_h]
     float* part_ml;       //   and their (running offset m, row sum l) [slot][256 columns][2]
+    float* lse;           // row log-sum-exp m + log2(l) of every stored query row [T][H] (the backward's)
     int64_t S, S_pad;
     int G, H, k;
 };
@@ -530,7 +531,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
     // no load is in flight) so that each (token, head) row of O is written in 16-byte pieces;
     // from the accumulators a lane holds one head dim of a row, and every store would write
     // 2-byte elements of two rows.
-    constexpr int SP = DH + 8;  // staging pitch (bf16): 16-byte aligned rows
+    constexpr int SP = DH + 8;  // staging pitch (bf16): 16-byte aligned rows; the pad holds l and m
     static_assert(2 * kQW * SP <= NSTAGE * TILE_K && 2 * kQW * SP <= NSTAGE * TILE_V, "staging fits");
     uint16_t* const ost = (w < 2 ? &ks_lds[0][0] : &vs_lds[0][0]) + (w & 1) * kQW * SP;
 #pragma unroll
@@ -551,8 +552,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
                 const int n = 32 * cb + lrow;
                 if (n < DH) ost[(qt * 32 + row) * SP + n] = from_f32<bf16_t>(oacc[qt][cb][j] * sc).bits;
             }
+            // the row sum goes to the row's pad (elements DH, DH + 1), for the log-sum-exp
+            if (lrow == 0) *reinterpret_cast<float*>(&ost[(qt * 32 + row) * SP + DH]) = lrow_sum;
         }
     }
+    // the offset of each column (lanes 0..31 hold those of both query tiles) beside its row sum
+    if (lane < 32)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) *reinterpret_cast<float*>(&ost[(qt * 32 + lane) * SP + DH + 2]) = mrun[qt];
     __syncthreads();
     constexpr int C8 = DH / 8;  // 16-byte pieces per row
 #pragma unroll
@@ -563,21 +570,33 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnArgs a) {
         const int pos = p0 + p;
         if (p < np && pos < S) {
             const int v = h < a.k ? ig * a.k + h : a.G * a.k;
-            *reinterpret_cast<u32x4_t*>(a.O + (((int64_t)ib * S + pos) * a.H + v) * DH + 8 * ch) =
-                *reinterpret_cast<const u32x4_t*>(&ost[r * SP + 8 * ch]);
+            const int64_t orow = ((int64_t)ib * S + pos) * a.H + v;
+            *reinterpret_cast<u32x4_t*>(a.O + orow * DH + 8 * ch) = *reinterpret_cast<const u32x4_t*>(&ost[r * SP + 8 * ch]);
+        }
+    }
+    {
+        // the row log-sum-exp m + log2(l) of the lane's row, kept for the backward
+        const int c = w * kQW + lane;
+        const int p = c / NH, h = c - p * NH;
+        const int pos = p0 + p;
+        if (p < np && pos < S) {
+            const float l = *reinterpret_cast<const float*>(&ost[lane * SP + DH]);
+            const float m = *reinterpret_cast<const float*>(&ost[lane * SP + DH + 2]);
+            a.lse[((int64_t)ib * S + pos) * a.H + (h < a.k ? ig * a.k + h : a.G * a.k)] = m + __builtin_amdgcn_logf(l);
         }
     }
 }
 
 // Combines the key-range chunks of one split item: per query column, M = max_i m_i,
 // l = sum_i l_i 2^(m_i - M), O = sum_i O_i 2^(m_i - M) / l -- the online-softmax merge of partial
-// results over disjoint key ranges -- then one rounding to bf16.  Four work groups per item, 64
+// results over disjoint key ranges -- then one rounding to bf16, and the row log-sum-exp
+// M + log2(l) for the backward.  Four work groups per item, 64
 // columns each; every thread keeps all its 16-byte loads of a chunk in flight.
 template <int DH>
 __global__ void __launch_bounds__(256) attn_merge_kernel(const int32_t* __restrict__ merges,
                                                          const float* __restrict__ part_o,
                                                          const float* __restrict__ part_ml, bf16_t* __restrict__ O,
-                                                         int64_t S, int G, int H, int k) {
+                                                         float* __restrict__ lse, int64_t S, int G, int H, int k) {
     constexpr int CPB = kCols / 4;          // columns per work group
     constexpr int NV = CPB * DH / 4 / 256;  // 16-byte vectors per thread per chunk
     static_assert(CPB * DH % 1024 == 0, "whole vectors per thread");
@@ -599,6 +618,9 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(const int32_t* __restri
         }
         const float inv = l > 0.f ? 1.0f / l : 0.f;  // l > 0 for every column that is stored
         for (int i = 0; i < nc; ++i) coef[i][threadIdx.x] *= inv;
+        const int p = c / nh, h = c - p * nh;
+        const int64_t pos = p0 + p;
+        if (p < np && pos < S) lse[((int64_t)b * S + pos) * H + (h < k ? g * k + h : G * k)] = M + __builtin_amdgcn_logf(l);
     }
     __syncthreads();
     f32x4_t acc[NV];
@@ -643,6 +665,7 @@ hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipSt
     a.O = (bf16_t*)(ws + P.o);
     a.part_o = (float*)(ws + P.part_o);
     a.part_ml = (float*)(ws + P.part_ml);
+    a.lse = (float*)(ws + P.lse);
     a.S = P.S;
     a.S_pad = P.S_pad;
     a.G = D.G;
@@ -680,9 +703,9 @@ hipError_t launch_attn_mfma(const GqeDims& D, const WorkPlan& P, char* ws, hipSt
         const unsigned mgrid = (unsigned)P.ac.nmerges * 4;
         const int32_t* mj = (const int32_t*)(ws + P.sched_merges);
         switch (D.dh) {
-            case 32: attn_merge_kernel<32><<<mgrid, 256, 0, st>>>(mj, a.part_o, a.part_ml, a.O, P.S, D.G, D.H, D.k); break;
-            case 48: attn_merge_kernel<48><<<mgrid, 256, 0, st>>>(mj, a.part_o, a.part_ml, a.O, P.S, D.G, D.H, D.k); break;
-            case 64: attn_merge_kernel<64><<<mgrid, 256, 0, st>>>(mj, a.part_o, a.part_ml, a.O, P.S, D.G, D.H, D.k); break;
+            case 32: attn_merge_kernel<32><<<mgrid, 256, 0, st>>>(mj, a.part_o, a.part_ml, a.O, a.lse, P.S, D.G, D.H, D.k); break;
+            case 48: attn_merge_kernel<48><<<mgrid, 256, 0, st>>>(mj, a.part_o, a.part_ml, a.O, a.lse, P.S, D.G, D.H, D.k); break;
+            case 64: attn_merge_kernel<64><<<mgrid, 256, 0, st>>>(mj, a.part_o, a.part_ml, a.O, a.lse, P.S, D.G, D.H, D.k); break;
             default: return hipErrorInvalidValue;
         }
         if (km) km->mark(KT_ATTN_MERGE);

@@ -60,7 +60,8 @@ struct BwdArgs {
     float* U;               // [T][NS][dh] (slot order: see wgp)
     float* dO;              // [T][H][dh]
     float* Dd;              // [T][H]
-    float* lse;             // [T][H]
+    float* lse;             // [T][H]: row log-sum-exp (log2 units); the forward's when lse_fwd
+    int lse_fwd;            // bf16 matrix-core attention: lse was written by the forward
     float* dl;              // [T][N]
     float* cf;              // [T][H]: output coefficient of each routed head (p for weighted_concat, else 1)
     float* wn;              // [T][H]: renormalised weight of each routed head (variant gqe)
@@ -789,6 +790,7 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
     const int ntile = qb + 1;
     // pass 1 (iterations 0 .. ntile - 1): each lane folds its four keys of every sub-tile into
     // (m, l); then the four lanes of a query column are combined into the row log-sum-exp L.
+    // Skipped when the forward's attention stored L (the same scores, with its row sums).
     // pass 2 (ntile .. 2 ntile - 1): dS^T = P^T (dP^T - D), dq += dS K.  The next iteration's key
     // (and value) tile is loaded into registers while the current one multiplies.  16 x 16 products in
     // v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x16_bf16 for a last 16 head dims); dq += dS K
@@ -817,8 +819,11 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
     f32x4_t dq[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) dq[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    fetch(0);
-    for (int it = 0; it < 2 * ntile; ++it) {
+    // with the forward's log-sum-exp the first pass is skipped
+    const int it0 = a.lse_fwd ? ntile : 0;
+    if (a.lse_fwd) L = qin ? a.lse[(b * S + qpos) * a.H + h] : 0.f;
+    fetch(it0);
+    for (int it = it0; it < 2 * ntile; ++it) {
         const int kt = it % ntile;
         const bool full = it >= ntile;
         __syncthreads();  // the previous tile's products are done
@@ -836,7 +841,7 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
         }
         __syncthreads();
         if (it + 1 < 2 * ntile) fetch(it + 1);
-        if (it == ntile) {  // first pass-2 tile: finish the log-sum-exp
+        if (it == ntile && !a.lse_fwd) {  // first pass-2 tile: finish the log-sum-exp
 #pragma unroll
             for (int o = 0; o < 2; ++o) {
                 float mo, lo;
@@ -928,7 +933,7 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
             }
             if (qr < S) gwrite<bf16_t>(a.dQ, ((b * S + qr) * a.H + h) * DH + col, v);
         }
-    if (j4 == 0 && qin) a.lse[(b * S + qpos) * a.H + h] = L;
+    if (j4 == 0 && qin && !a.lse_fwd) a.lse[(b * S + qpos) * a.H + h] = L;
 }
 
 // ---------------------------------------------------------------- tiled float32 GEMM
@@ -2135,6 +2140,12 @@ hipError_t launch_backward(const GqeDims& D, const WorkPlan& P, const BwdPlan& B
     a.dO = (float*)(ws + BP.dO);
     a.Dd = (float*)(ws + BP.Dd);
     a.lse = (float*)(ws + BP.lse);
+    if (D.dtype == GQE_DTYPE_BF16 && P.lse_ok) {
+        // the forward's attention stored every row's log-sum-exp: the query-block kernel skips its
+        // first pass and both attention kernels read it from the forward workspace
+        a.lse = const_cast<float*>(reinterpret_cast<const float*>(fws + P.lse));
+        a.lse_fwd = 1;
+    }
     a.dl = (float*)(ws + BP.dl);
     a.cf = (float*)(ws + BP.cf);
     a.wn = (float*)(ws + BP.wn);
