@@ -147,7 +147,8 @@ int gqe_workspace_bytes(const gqe_handle_t* h, int64_t batch, int64_t seq, size_
  *  x          [batch, seq, d] device, cfg.dtype; not aliased with y.
  *  y          [batch, seq, d] device, cfg.dtype (written).
  *  workspace  device, >= gqe_workspace_bytes(batch, seq), 256-byte aligned; also holds the
- *             routing statistics read later by gqe_aux_stats.
+ *             routing statistics read later by gqe_aux_stats and what gqe_backward reads (routing,
+ *             Q, K, V^T, O and, on the matrix-core attention path, every query row's log-sum-exp).
  *  route_idx  optional [batch, seq, G, k] int32: global expert id of the r-th choice of each
  *             group (descending router logit; ties -> lower id).  NULL to skip.
  *  route_w    optional [batch, seq, G, k] float32: renormalised weight p / sum(p_selected)
@@ -317,7 +318,8 @@ int gqe_backward_workspace_bytes(const gqe_handle_t* h, int64_t batch, int64_t s
 /* The backward pass of the last gqe_forward on this handle.
  *  x, dy          [batch, seq, d] device, cfg.dtype; x the forward's input, dy the loss gradient.
  *  aux_coef       weight of the balance loss in L (the README's 0.01; 0 for none).
- *  fwd_workspace  the workspace of that forward (routing, statistics, Q, K, V^T, O), unchanged.
+ *  fwd_workspace  the workspace of that forward (routing, statistics, Q, K, V^T, O, the row
+ *                 log-sum-exp of its matrix-core attention), unchanged.
  *  workspace      device, >= gqe_backward_workspace_bytes(batch, seq), 256-byte aligned.
  * Enqueued on `stream`.  Supported: n = N/G <= 16, head_dim a multiple of 16, head_dim <= 128.
  * Errors: GQE_ERR_NULL_POINTER, GQE_ERR_STATE (no forward of this shape on this workspace),
