@@ -641,6 +641,8 @@ __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint
         }
         __syncthreads();
         if (it + 1 < total) fetch(it + 1);
+        // a query tile wholly after the block's last key and inside the sequence masks nothing
+        const bool inside = (int64_t)qt * 64 >= (int64_t)kb * 128 + 128 && (int64_t)qt * 64 + 64 <= S;
         // pairs of 16-query blocks: queries qp .. qp + 31 of the tile
 #pragma unroll
         for (int qp = 0; qp < 64; qp += 32) {
@@ -689,12 +691,20 @@ __global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint
                         sacc = mma16_add(qa16[h2], kt16[u], sacc);
                         dp = mma16_add(da16[h2], vt16[u], dp);
                     }
+                    if (inside) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int64_t qpos = (int64_t)qt * 64 + qp + 16 * h2 + 4 * j4 + i;
-                        const bool on = kin[u] && qpos < S && qpos >= key[u];
-                        p[4 * h2 + i] = on ? __builtin_amdgcn_exp2f(sacc[i] - lq[h2][i]) : 0.f;
-                        ds[4 * h2 + i] = on ? p[4 * h2 + i] * (dp[i] - dq4[h2][i]) : 0.f;
+                        for (int i = 0; i < 4; ++i) {
+                            p[4 * h2 + i] = __builtin_amdgcn_exp2f(sacc[i] - lq[h2][i]);
+                            ds[4 * h2 + i] = p[4 * h2 + i] * (dp[i] - dq4[h2][i]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int64_t qpos = (int64_t)qt * 64 + qp + 16 * h2 + 4 * j4 + i;
+                            const bool on = kin[u] && qpos < S && qpos >= key[u];
+                            p[4 * h2 + i] = on ? __builtin_amdgcn_exp2f(sacc[i] - lq[h2][i]) : 0.f;
+                            ds[4 * h2 + i] = on ? p[4 * h2 + i] * (dp[i] - dq4[h2][i]) : 0.f;
+                        }
                     }
                 }
                 const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, pack8(p));
@@ -893,6 +903,8 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
                 }
             }
         } else {
+            // a key tile wholly before the query block masks nothing but the rows past the end
+            const bool inside = kt < qb;
 #pragma unroll
             for (int sp = 0; sp < 64; sp += 32) {
                 float ds[8];
@@ -900,11 +912,16 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
                 for (int h2 = 0; h2 < 2; ++h2) {
                     const int k0 = sp + 16 * h2;
                     const f32x4_t st = scores(Ks, k0, qf, qf16), dpt = scores(Vs, k0, df, df16);
+                    if (inside) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int64_t kp = (int64_t)kt * 64 + k0 + 4 * j4 + i;
-                        const bool on = qin && kp <= qpos && kp < S;
-                        ds[4 * h2 + i] = on ? __builtin_amdgcn_exp2f(st[i] - L) * (dpt[i] - Dq) : 0.f;
+                        for (int i = 0; i < 4; ++i) ds[4 * h2 + i] = qin ? __builtin_amdgcn_exp2f(st[i] - L) * (dpt[i] - Dq) : 0.f;
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int64_t kp = (int64_t)kt * 64 + k0 + 4 * j4 + i;
+                            const bool on = qin && kp <= qpos && kp < S;
+                            ds[4 * h2 + i] = on ? __builtin_amdgcn_exp2f(st[i] - L) * (dpt[i] - Dq) : 0.f;
+                        }
                     }
                 }
                 const bf16x8_t da = __builtin_bit_cast(bf16x8_t, pack8(ds));
