@@ -1845,50 +1845,60 @@ __global__ void __launch_bounds__(256) wg_wslot_kernel(BwdArgs a, uint16_t* __re
     *reinterpret_cast<u32x4_t*>(wsl + (int64_t)row * a.d + c) = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// dx = gcat wcat^T + dl W_r^T (float32 result, written): the first product on bf16 operands, both
-// contiguous along the contraction, so the tiles go straight into LDS (64-wide slices, XOR-swizzled
-// 16-byte chunks, two stages) and the fragments are plain 16-byte LDS reads; 128 x 128 tiles of dx,
-// four waves of 64 x 64 in v_mfma_f32_16x16x32_bf16 (kp is a multiple of 64).  The router's term
+// C = A B^T (+ dl W_r^T) in float32 for bf16 A [M][kp] and B [N][kp], both contiguous along the
+// contraction (the U and dx products): 256 x (64 NB) tiles, eight waves of 128 x 16 NB in
+// v_mfma_f32_16x16x32_bf16, the operand tiles copied straight into LDS in 64-wide slices
+// (XOR-swizzled 16-byte chunks, two stages).  Against 128 x 128 tiles this re-reads each operand
+// fewer times: these products are bound by their global -> LDS copies, not by the matrix cores.
+// NB is chosen per product so that the tiles fill the CUs in the fewest rounds.  The router's term
 // (float32 logit gradients and router weights, nr <= 64 columns; nr = 0: none) is added in the same
 // accumulators by v_mfma_f32_16x16x4_f32 from float32 tiles staged in the freed LDS.
-__global__ void __launch_bounds__(256, 2) dx_gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-                                                         float* __restrict__ C, int64_t M, int N, int kp,
-                                                         const float* __restrict__ dl, const float* __restrict__ wr,
-                                                         int nr) {
-    constexpr int BM = 128, BN = 128, KC = 64;
+template <int NB>
+__global__ void __launch_bounds__(512, 1) bt_gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                                                       float* __restrict__ C, int64_t M, int N, int kp,
+                                                       const float* __restrict__ dl, const float* __restrict__ wr,
+                                                       int nr) {
+    constexpr int BM = 256, BN = 64 * NB, KC = 64;
+    constexpr int SA = BM * KC / 512, SB = BN * KC / 512;  // 1 KB segments per operand tile
     __shared__ __align__(1024) uint16_t As[2][BM * KC];
     __shared__ __align__(1024) uint16_t Bs[2][BN * KC];
+    static_assert(SA % 8 == 0 && SB % 8 == 0, "whole segments per wave");
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tiles_n = (N + BN - 1) / BN;
     const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * BM;
     const int n0 = (int)(blockIdx.x % tiles_n) * BN;
-    // loads: 16 segments of 1 KB per operand tile (8 rows of 8 chunks each), wave w takes
-    // segments w, w + 4, w + 8, w + 12; LDS chunk p of row r holds global chunk p ^ ((r >> 1) & 7)
-    uint32_t aoff[4], boff[4];
+    // segment s: rows 8 s .. 8 s + 7, eight chunks each; wave w takes segments w, w + 8, ...;
+    // LDS chunk p of row r holds global chunk p ^ ((r >> 1) & 7); rows past the edge repeat the last
+    uint32_t aoff[SA / 8], boff[SB / 8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int qq = (w + 4 * i) * 64 + lane;
+    for (int i = 0; i < SA / 8; ++i) {
+        const int qq = (w + 8 * i) * 64 + lane;
         const int r = qq >> 3, c = (qq & 7) ^ ((r >> 1) & 7);
         const int64_t ra = min(m0 + r, M - 1) - m0;
-        const int rb = min(n0 + r, N - 1) - n0;
         aoff[i] = (uint32_t)((ra * kp + 8 * c) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < SB / 8; ++i) {
+        const int qq = (w + 8 * i) * 64 + lane;
+        const int r = qq >> 3, c = (qq & 7) ^ ((r >> 1) & 7);
+        const int rb = min(n0 + r, N - 1) - n0;
         boff[i] = (uint32_t)(((int64_t)rb * kp + 8 * c) * 2);
     }
     const uint16_t* abase = A + m0 * kp;
     const uint16_t* bbase = B + (int64_t)n0 * kp;
     auto issue = [&](int kc, int stage) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16(abase + kc * KC, aoff[i], &As[stage][(w + 4 * i) * 512]);
+        for (int i = 0; i < SA / 8; ++i) dma16(abase + kc * KC, aoff[i], &As[stage][(w + 8 * i) * 512]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16(bbase + kc * KC, boff[i], &Bs[stage][(w + 4 * i) * 512]);
+        for (int i = 0; i < SB / 8; ++i) dma16(bbase + kc * KC, boff[i], &Bs[stage][(w + 8 * i) * 512]);
     };
-    f32x4_t acc[4][4];
+    f32x4_t acc[8][NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int wm = (w >> 2) * 128, wn = (w & 3) * 16 * NB;
     auto swz = [](int row, int c) { return (row * 8 + (c ^ ((row >> 1) & 7))) * 8; };
     const int nk = kp / KC;
     issue(0, 0);
@@ -1900,51 +1910,53 @@ __global__ void __launch_bounds__(256, 2) dx_gemm_kernel(const uint16_t* __restr
 #pragma unroll
         for (int ks = 0; ks < KC / 32; ++ks) {
             const int c = 4 * ks + (lane >> 4);
-            bf16x8_t af[4], bfr[4];
+            bf16x8_t bfr[NB];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                af[i] = *reinterpret_cast<const bf16x8_t*>(&As[stage][swz(wm + 16 * i + (lane & 15), c)]);
-                bfr[i] = *reinterpret_cast<const bf16x8_t*>(&Bs[stage][swz(wn + 16 * i + (lane & 15), c)]);
+            for (int j = 0; j < NB; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[stage][swz(wn + 16 * j + (lane & 15), c)]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&As[stage][swz(wm + 16 * i + (lane & 15), c)]);
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
         __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
         __syncthreads();
     }
     if (nr > 0) {
-        // dl [128 tokens][nr4] and W_r [128 columns][nr4] of the tile in float32 (zero past the
+        // dl [256 tokens][nr4] and W_r [BN columns][nr4] of the tile in float32 (zero past the
         // edges and past nr), then k-steps of four router columns
         const int nr4 = (nr + 3) & ~3;
         float* dls = reinterpret_cast<float*>(&As[0][0]);
         float* wrs = reinterpret_cast<float*>(&Bs[0][0]);
-        for (int q = tid; q < BM * nr4; q += 256) {
+        for (int q = tid; q < BM * nr4; q += 512) {
             const int r = q / nr4, e = q % nr4;
             dls[q] = (m0 + r < M && e < nr) ? dl[(m0 + r) * nr + e] : 0.f;
+        }
+        for (int q = tid; q < BN * nr4; q += 512) {
+            const int r = q / nr4, e = q % nr4;
             wrs[q] = (n0 + r < N && e < nr) ? wr[(int64_t)(n0 + r) * nr + e] : 0.f;
         }
         __syncthreads();
         for (int e0 = 0; e0 < nr4; e0 += 4) {
-            float af[4], bq[4];
+            float bq[NB];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                af[i] = dls[(wm + 16 * i + (lane & 15)) * nr4 + e0 + (lane >> 4)];
-                bq[i] = wrs[(wn + 16 * i + (lane & 15)) * nr4 + e0 + (lane >> 4)];
+            for (int j = 0; j < NB; ++j) bq[j] = wrs[(wn + 16 * j + (lane & 15)) * nr4 + e0 + (lane >> 4)];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float af = dls[(wm + 16 * i + (lane & 15)) * nr4 + e0 + (lane >> 4)];
+#pragma unroll
+                for (int j = 0; j < NB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af, bq[j], acc[i][j], 0, 0, 0);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bq[j], acc[i][j], 0, 0, 0);
         }
     }
     // lane: rows (tokens) 4 (lane / 16) + 0..3 of each 16 x 16 block, column lane % 16
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t m = m0 + wm + 16 * i + 4 * (lane >> 4) + r;
@@ -1952,6 +1964,44 @@ __global__ void __launch_bounds__(256, 2) dx_gemm_kernel(const uint16_t* __restr
                 if (m < M && n < N) C[m * N + n] = acc[i][j][r];
             }
 }
+
+// CUs of the current device (cached per device)
+int device_cus() {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// C [M][N] = A B^T (+ dl W_r^T) with the tile width that fills the CUs in the fewest rounds (time of
+// a round taken as proportional to the tile width; ties to the wider tile)
+hipError_t launch_bt_gemm(const uint16_t* A, const uint16_t* B, float* C, int64_t M, int N, int kp, const float* dl,
+                          const float* wr, int nr, hipStream_t st) {
+    const int64_t cus = device_cus(), tm = ceil_div(M, 256);
+    int nb = 3;
+    double best = 1e300;
+    for (int b = 2; b <= 5; ++b) {
+        const double cost = (double)ceil_div(tm * ceil_div(N, 64 * b), cus) * b;
+        if (cost <= best) {
+            best = cost;
+            nb = b;
+        }
+    }
+    const unsigned tiles = (unsigned)(tm * ceil_div(N, 64 * nb));
+    switch (nb) {
+        case 2: bt_gemm_kernel<2><<<tiles, 512, 0, st>>>(A, B, C, M, N, kp, dl, wr, nr); break;
+        case 3: bt_gemm_kernel<3><<<tiles, 512, 0, st>>>(A, B, C, M, N, kp, dl, wr, nr); break;
+        case 4: bt_gemm_kernel<4><<<tiles, 512, 0, st>>>(A, B, C, M, N, kp, dl, wr, nr); break;
+        default: bt_gemm_kernel<5><<<tiles, 512, 0, st>>>(A, B, C, M, N, kp, dl, wr, nr); break;
+    }
+    return hipGetLastError();
+}
+
 
 // Columns of gcat / wcat: the concatenated input-side blocks rounded up to whole 64-wide slices.
 int wg_kp(const BwdArgs& a) { return (int)round_up((int64_t)(2 * a.G + a.s + a.N) * a.dh, 64); }
@@ -2007,9 +2057,7 @@ hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km
         // did not choose are computed and not read), one product
         const int nso = a.NS * a.dh;
         wg_wslot_kernel<<<blocks((int64_t)nso * (a.d / 8)), 256, 0, st>>>(a, a.wg_wslot);
-        const unsigned tiles = (unsigned)(ceil_div(a.T, 128) * ceil_div(nso, 128));
-        dx_gemm_kernel<<<tiles, 256, 0, st>>>(reinterpret_cast<const uint16_t*>(a.dy), a.wg_wslot, a.U, a.T, nso, a.d,
-                                              nullptr, nullptr, 0);
+        launch_bt_gemm(reinterpret_cast<const uint16_t*>(a.dy), a.wg_wslot, a.U, a.T, nso, a.d, nullptr, nullptr, 0, st);
     } else {
         tgemm<ProbU<T>, true, true>(mm, ProbU<T>{a, L}, nt, a.dh, nsm, st);
     }
@@ -2111,9 +2159,7 @@ weights:
         // bf16: dx = gcat wcat^T + dl W_r^T in one kernel (gcat from the weights stage)
         const int kp = wg_kp(a);
         wg_wcat_kernel<<<blocks((int64_t)a.d * (kp / 8)), 256, 0, st>>>(a, a.wg_wcat, kp);
-        const unsigned tiles = (unsigned)(ceil_div(a.T, 128) * ceil_div(a.d, 128));
-        dx_gemm_kernel<<<tiles, 256, 0, st>>>(a.wg_gcat, a.wg_wcat, a.dx, a.T, a.d, kp, a.dl, a.wr,
-                                              a.dense ? 0 : a.N);
+        launch_bt_gemm(a.wg_gcat, a.wg_wcat, a.dx, a.T, a.d, kp, a.dl, a.wr, a.dense ? 0 : a.N, st);
     } else {
         // routed heads inside the dense product while that costs at most 4x their own work
         const int expand = a.n <= 4 * a.k ? 1 : 0;
