@@ -539,8 +539,11 @@ __global__ void bwd_mprep_kernel(BwdArgs a, uint16_t* __restrict__ Vr, uint16_t*
 // the score products contract the head dims, the gradient products P^T dO and dS^T Q contract 32
 // queries at a time -- the lane's four queries of two consecutive 16-query blocks, the transposed
 // tiles read in the same order.
+// Two waves per SIMD up to d_h = 48 (the compiler fits the registers in 256 with a few dwords of
+// spill; one wave per SIMD left the matrix core idle during every wait); larger head dims keep one
+// wave per SIMD (their spills at 256 registers are larger).
 template <int DH>
-__global__ void __launch_bounds__(256) bwd_dkv_mfma_kernel(BwdArgs a, const uint16_t* __restrict__ Vr,
+__global__ void __launch_bounds__(256, DH <= 48 ? 2 : 1) bwd_dkv_mfma_kernel(BwdArgs a, const uint16_t* __restrict__ Vr,
                                                            const uint16_t* __restrict__ dOb) {
     constexpr int NC = DH / 16, N32 = DH / 32, R16 = (DH % 32) / 16, P1 = DH + 8, P2 = 72;
     constexpr int F32 = N32 > 0 ? N32 : 1;
