@@ -761,23 +761,26 @@ __global__ void bwd_kv_sum_kernel(BwdArgs a) {
     gwrite<bf16_t>(a.dV, o, a.kvp[2 * n + q] + a.kvp[3 * n + q]);
 }
 
-// dq of 64 queries (wave w: queries 16 w ..) of one (sequence, head): pass 1 the row log-sum-exp,
+constexpr int kDqWaves = 8;  // waves of the query-block kernel (16 queries each)
+
+// dq of 16 kDqWaves queries (wave w: queries 16 w ..) of one (sequence, head): pass 1 the row log-sum-exp,
 // pass 2 dS^T = P^T (dP^T - D) and dq += dS K over the causal key tiles.
 template <int DH>
-__global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint16_t* __restrict__ Vr,
-                                                          const uint16_t* __restrict__ dOb) {
+__global__ void __launch_bounds__(64 * kDqWaves) bwd_dq_mfma_kernel(BwdArgs a, const uint16_t* __restrict__ Vr,
+                                                                    const uint16_t* __restrict__ dOb) {
     constexpr int NC = DH / 16, N32 = DH / 32, R16 = (DH % 32) / 16, P1 = DH + 8, P2 = 72;
     constexpr int F32 = N32 > 0 ? N32 : 1;
+    constexpr int QB = 16 * kDqWaves;  // queries per work group, 16 per wave
     __shared__ __align__(16) uint16_t Ks[64 * P1], Vs[64 * P1], KsT[DH * P2];
     // longest first: the last query block (every key tile before it) of every (head, sequence) leads
-    const int nqb = (int)ceil_div(a.S, 64);
+    const int nqb = (int)ceil_div(a.S, QB);
     const int qb = nqb - 1 - (int)(blockIdx.x / (a.H * a.B));
     const int h = (int)(blockIdx.x % a.H), b = (int)(blockIdx.x / a.H % a.B);
     const int tid = threadIdx.x;
     const int g = group_of(a, h);
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, j4 = lane >> 4;
     const int64_t S = a.S;
-    const int64_t qpos = (int64_t)qb * 64 + w * 16 + l16;  // this lane's query column
+    const int64_t qpos = (int64_t)qb * QB + w * 16 + l16;  // this lane's query column
     const bool qin = qpos < S;
     const uint16_t* Qg = reinterpret_cast<const uint16_t*>(a.Q);
     // query and dO fragments of the score products: head dims 32 c + 8 j4 .. + 7, and of a last 16
@@ -800,7 +803,7 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
     const float Dq = qin ? a.Dd[(b * S + qpos) * a.H + h] : 0.f;
     const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + ((int64_t)(b * a.G + g) * a.S_pad) * DH;
     const uint16_t* Vb = Vr + ((int64_t)(b * a.G + g) * a.S_pad) * DH;
-    const int ntile = qb + 1;
+    const int ntile = (int)((min((int64_t)qb * QB + QB, S) - 1) / 64) + 1;  // key tiles up to the last query
     // pass 1 (iterations 0 .. ntile - 1): each lane folds its four keys of every sub-tile into
     // (m, l); then the four lanes of a query column are combined into the row log-sum-exp L.
     // Skipped when the forward's attention stored L (the same scores, with its row sums).
@@ -907,7 +910,7 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
             }
         } else {
             // a key tile wholly before the query block masks nothing but the rows past the end
-            const bool inside = kt < qb;
+            const bool inside = (int64_t)kt * 64 + 64 <= (int64_t)qb * QB;
 #pragma unroll
             for (int sp = 0; sp < 64; sp += 32) {
                 float ds[8];
@@ -942,7 +945,7 @@ __global__ void __launch_bounds__(256) bwd_dq_mfma_kernel(BwdArgs a, const uint1
     for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t qr = (int64_t)qb * 64 + w * 16 + 4 * j4 + i;
+            const int64_t qr = (int64_t)qb * QB + w * 16 + 4 * j4 + i;
             const int col = 16 * c + l16;
             float v = dq[c][i] * sc;
             if (a.rope) {
@@ -2073,9 +2076,10 @@ hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km
         // bf16: matrix cores
         const int64_t n = a.B * (a.G + a.H) * a.S_pad * (a.dh / 8);
         bwd_mprep_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>(a, a.vr, a.dob);
-        const dim3 gq1((unsigned)(nblk * a.H * a.B)), gk1((unsigned)(ceil_div(a.S, 128) * (a.G + a.s) * a.B));
+        const dim3 gq1((unsigned)(ceil_div(a.S, 16 * kDqWaves) * a.H * a.B)),
+            gk1((unsigned)(ceil_div(a.S, 128) * (a.G + a.s) * a.B));
 #define GQE_BWD_MFMA(DHV)                                                     \
-    bwd_dq_mfma_kernel<DHV><<<gq1, 256, 0, st>>>(a, a.vr, a.dob);             \
+    bwd_dq_mfma_kernel<DHV><<<gq1, 64 * kDqWaves, 0, st>>>(a, a.vr, a.dob);   \
     bwd_dkv_mfma_kernel<DHV><<<gk1, 256, 0, st>>>(a, a.vr, a.dob);
         switch (a.dh / 16) {  // d_h: a multiple of 16, at most 128
             case 1: GQE_BWD_MFMA(16) break;
