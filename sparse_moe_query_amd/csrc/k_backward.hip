@@ -1524,7 +1524,8 @@ struct ProbDxRouted {
 // Router weight and bias gradients, dW_r[i][e] = sum_t x_t[i] dl_t[e] and db_r[e] = sum_t dl_t[e]
 // (row i = d, where x counts as 1), in float32: work group = (256 rows i, 16 experts, token chunk);
 // the chunk's logit gradients pass through LDS 128 tokens at a time and every lane reads them as
-// a broadcast; per-chunk partial sums are added in chunk order.
+// a broadcast; per-chunk partial sums ([chunk][expert][row]: neighbouring lanes store neighbouring
+// rows) are added in chunk order.
 constexpr int kRgTok = 128;
 template <typename T>
 __global__ void __launch_bounds__(256) bwd_router_wgrad_kernel(BwdArgs a, int nchunk, float* __restrict__ part) {
@@ -1566,13 +1567,13 @@ __global__ void __launch_bounds__(256) bwd_router_wgrad_kernel(BwdArgs a, int nc
     if (i <= a.d)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-            if (e < ne) part[((int64_t)c * (a.d + 1) + i) * a.N + e0 + e] = acc[e];
+            if (e < ne) part[((int64_t)c * a.N + e0 + e) * (a.d + 1) + i] = acc[e];
 }
 
 // eight lanes per output element, each adding every eighth chunk in chunk order, then the eight
 // partial sums added in lane order (a fixed order: the result does not depend on the schedule)
 __global__ void bwd_router_wgrad_reduce(BwdArgs a, int nchunk, const float* __restrict__ part) {
-    const int64_t q = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 3;  // (i, e)
+    const int64_t q = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 3;  // e (d + 1) + i
     const int sl = threadIdx.x & 7;
     const int64_t n = (int64_t)(a.d + 1) * a.N;
     float v = 0.f;
@@ -1583,7 +1584,7 @@ __global__ void bwd_router_wgrad_reduce(BwdArgs a, int nchunk, const float* __re
 #pragma unroll
     for (int o = 0; o < 8; ++o) tot += __shfl(v, (threadIdx.x & ~7) + o);
     if (q >= n || sl != 0) return;
-    const int i = (int)(q / a.N), e = (int)(q % a.N);
+    const int e = (int)(q / (a.d + 1)), i = (int)(q % (a.d + 1));
     if (i < a.d) a.dwr[(int64_t)i * a.N + e] = tot;
     else a.dbr[e] = tot;
 }
