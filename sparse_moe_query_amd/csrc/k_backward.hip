@@ -1747,11 +1747,11 @@ __global__ void __launch_bounds__(256) wg_reduce_kernel(WgArgs a) {
 template <typename T>
 __global__ void __launch_bounds__(256) wg_expand_kernel(BwdArgs a, uint16_t* __restrict__ gcat, int kp,
                                                         uint16_t* __restrict__ ocat, int nslot) {
+    // work group: four tokens (blockIdx.y) x 64 consecutive 16-byte chunks of their rows (blockIdx.x)
     const int ng = kp / 8, no = (a.N + nslot) * a.dh / 8;
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (q >= a.T * (ng + no)) return;
-    const int64_t t = q / (ng + no);
-    const int u = (int)(q % (ng + no));
+    const int64_t t = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int u = (int)blockIdx.x * 64 + (int)(threadIdx.x & 63);
+    if (t >= a.T || u >= ng + no) return;
     const uint16_t* dQ = reinterpret_cast<const uint16_t*>(a.dQ);
     const int GD = a.G * a.dh, kd = 2 * GD + a.s * a.dh;
     // the head of token t that chose expert e (all-active GQA: head e % n of its group), or -1
@@ -2120,8 +2120,9 @@ weights:
         // blocks that are zero where the token did not choose them)
         const int nslot = (rslot ? a.G : 0) + a.s;
         const int kp = wg_kp(a);
-        const int64_t nth = a.T * (kp / 8 + (a.N + nslot) * a.dh / 8);
-        wg_expand_kernel<T><<<blocks(nth), 256, 0, st>>>(a, a.wg_gcat, kp, a.wg_ocat, nslot);
+        const int nch = kp / 8 + (a.N + nslot) * a.dh / 8;  // 16-byte chunks of a token's two rows
+        const dim3 ge((unsigned)ceil_div(nch, 64), (unsigned)ceil_div(a.T, 4));
+        wg_expand_kernel<T><<<ge, 256, 0, st>>>(a, a.wg_gcat, kp, a.wg_ocat, nslot);
         WgArgs wa{};
         wa.T = a.T;
         wa.splits = kWgSplits;
