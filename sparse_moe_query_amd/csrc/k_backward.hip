@@ -594,11 +594,17 @@ __global__ void __launch_bounds__(256, DH <= 48 ? 2 : 1) bwd_dkv_mfma_kernel(Bwd
     const int nh = shared_part ? 1 : a.k;
     const int qt0 = 2 * kb, ntl = nqt - qt0, total = nh * ntl;
     auto head = [&](int hi) { return shared_part ? a.G * a.k : g * a.k + hi; };
-    // staging: thread = (four neighbouring rows, one 8-dim chunk); R = the four rows
+    // staging: thread = (four neighbouring rows, one 8-dim chunk); R = the four rows.  Up to d_h = 64
+    // (SPLIT) waves 0-1 stage Q and waves 2-3 dO, each with its transposed copy, so a staging thread
+    // does half the work and holds half the prefetch registers; above, every staging thread does both
     constexpr int NQC = 16 * (DH / 8), R = 4;
+    constexpr bool SPLIT = NQC <= 128;
     static_assert(NQC <= 256, "d_h <= 128");
-    const int rq = (tid / (DH / 8)) * 4, cq = tid % (DH / 8);
-    u32x4_t pq[R], pd[R];
+    const bool dorole = SPLIT && tid >= 128;  // this thread stages dO (wave-uniform)
+    const int sid = SPLIT ? (tid & 127) : tid;
+    const bool stager = sid < NQC;
+    const int rq = (sid / (DH / 8)) * 4, cq = sid % (DH / 8);
+    u32x4_t pq[R], pd[SPLIT ? 1 : R];
     float pl = 0.f, pdd = 0.f;
     auto fetch = [&](int it) {
         const int h = head(it / ntl), qt = qt0 + it % ntl;
@@ -606,10 +612,17 @@ __global__ void __launch_bounds__(256, DH <= 48 ? 2 : 1) bwd_dkv_mfma_kernel(Bwd
         for (int r = 0; r < R; ++r) {
             const int q = rq + r, c8 = cq;
             const int64_t qp = (int64_t)qt * 64 + q;
-            pq[r] = pd[r] = u32x4_t{0u, 0u, 0u, 0u};
-            if (tid < NQC && qp < S) {
-                pq[r] = *reinterpret_cast<const u32x4_t*>(Qg + (((int64_t)b * a.H + h) * S + qp) * DH + 8 * c8);
-                pd[r] = *reinterpret_cast<const u32x4_t*>(dOb + (((int64_t)b * a.H + h) * a.S_pad + qp) * DH + 8 * c8);
+            pq[r] = u32x4_t{0u, 0u, 0u, 0u};
+            if (!SPLIT) pd[SPLIT ? 0 : r] = u32x4_t{0u, 0u, 0u, 0u};
+            if (stager && qp < S) {
+                const uint16_t* qsrc = Qg + (((int64_t)b * a.H + h) * S + qp) * DH + 8 * c8;
+                const uint16_t* dsrc = dOb + (((int64_t)b * a.H + h) * a.S_pad + qp) * DH + 8 * c8;
+                if (SPLIT) {
+                    pq[r] = *reinterpret_cast<const u32x4_t*>(dorole ? dsrc : qsrc);
+                } else {
+                    pq[r] = *reinterpret_cast<const u32x4_t*>(qsrc);
+                    pd[SPLIT ? 0 : r] = *reinterpret_cast<const u32x4_t*>(dsrc);
+                }
             }
         }
         if (tid < 64) {
@@ -623,19 +636,30 @@ __global__ void __launch_bounds__(256, DH <= 48 ? 2 : 1) bwd_dkv_mfma_kernel(Bwd
     for (int it = 0; it < total; ++it) {
         const int qt = qt0 + it % ntl;
         __syncthreads();  // the previous pair's products are done with the tiles
-        if (tid < NQC) {
+        if (stager) {
+            if (SPLIT) {
+                uint16_t* const rowm = dorole ? dOs : Qs;
+                uint16_t* const tr = dorole ? dOsT : QsT;
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                *reinterpret_cast<u32x4_t*>(&Qs[(rq + r) * P1 + 8 * cq]) = pq[r];
-                *reinterpret_cast<u32x4_t*>(&dOs[(rq + r) * P1 + 8 * cq]) = pd[r];
-            }
-            // transposed: dim 8 cq + e, rows rq .. rq + 3 in one 8-byte store
+                for (int r = 0; r < R; ++r) *reinterpret_cast<u32x4_t*>(&rowm[(rq + r) * P1 + 8 * cq]) = pq[r];
+                // transposed: dim 8 cq + e, rows rq .. rq + 3 in one 8-byte store
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                *reinterpret_cast<u32x2_t*>(&QsT[(8 * cq + e) * P2 + rq]) =
-                    u32x2_t{bf16_pair(pq[0], pq[1], e), bf16_pair(pq[2], pq[3], e)};
-                *reinterpret_cast<u32x2_t*>(&dOsT[(8 * cq + e) * P2 + rq]) =
-                    u32x2_t{bf16_pair(pd[0], pd[1], e), bf16_pair(pd[2], pd[3], e)};
+                for (int e = 0; e < 8; ++e)
+                    *reinterpret_cast<u32x2_t*>(&tr[(8 * cq + e) * P2 + rq]) =
+                        u32x2_t{bf16_pair(pq[0], pq[1], e), bf16_pair(pq[2], pq[3], e)};
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    *reinterpret_cast<u32x4_t*>(&Qs[(rq + r) * P1 + 8 * cq]) = pq[r];
+                    *reinterpret_cast<u32x4_t*>(&dOs[(rq + r) * P1 + 8 * cq]) = pd[SPLIT ? 0 : r];
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    *reinterpret_cast<u32x2_t*>(&QsT[(8 * cq + e) * P2 + rq]) =
+                        u32x2_t{bf16_pair(pq[0], pq[1], e), bf16_pair(pq[2], pq[3], e)};
+                    *reinterpret_cast<u32x2_t*>(&dOsT[(8 * cq + e) * P2 + rq]) =
+                        u32x2_t{bf16_pair(pd[0], pd[SPLIT ? 0 : 1], e), bf16_pair(pd[SPLIT ? 0 : 2], pd[SPLIT ? 0 : 3], e)};
+                }
             }
         }
         if (tid < 64) {
@@ -2064,7 +2088,9 @@ hipError_t run(const BwdArgs& a, const Lists& L, hipStream_t st, KernelMarks* km
         // did not choose are computed and not read), one product
         const int nso = a.NS * a.dh;
         wg_wslot_kernel<<<blocks((int64_t)nso * (a.d / 8)), 256, 0, st>>>(a, a.wg_wslot);
-        launch_bt_gemm(reinterpret_cast<const uint16_t*>(a.dy), a.wg_wslot, a.U, a.T, nso, a.d, nullptr, nullptr, 0, st);
+        const hipError_t e = launch_bt_gemm(reinterpret_cast<const uint16_t*>(a.dy), a.wg_wslot, a.U, a.T, nso, a.d,
+                                            nullptr, nullptr, 0, st);
+        if (e != hipSuccess) return e;
     } else {
         tgemm<ProbU<T>, true, true>(mm, ProbU<T>{a, L}, nt, a.dh, nsm, st);
     }
@@ -2168,7 +2194,8 @@ weights:
         // bf16: dx = gcat wcat^T + dl W_r^T in one kernel (gcat from the weights stage)
         const int kp = wg_kp(a);
         wg_wcat_kernel<<<blocks((int64_t)a.d * (kp / 8)), 256, 0, st>>>(a, a.wg_wcat, kp);
-        launch_bt_gemm(a.wg_gcat, a.wg_wcat, a.dx, a.T, a.d, kp, a.dl, a.wr, a.dense ? 0 : a.N, st);
+        const hipError_t e = launch_bt_gemm(a.wg_gcat, a.wg_wcat, a.dx, a.T, a.d, kp, a.dl, a.wr, a.dense ? 0 : a.N, st);
+        if (e != hipSuccess) return e;
     } else {
         // routed heads inside the dense product while that costs at most 4x their own work
         const int expand = a.n <= 4 * a.k ? 1 : 0;
