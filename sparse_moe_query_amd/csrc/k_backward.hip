@@ -836,11 +836,17 @@ __global__ void __launch_bounds__(64 * kDqWaves) bwd_dq_mfma_kernel(BwdArgs a, c
     // v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x16_bf16 for a last 16 head dims); dq += dS K
     // contracts 32 keys at a time (the lane's four keys of two consecutive 16-key sub-tiles, K^T read
     // in the same order).
-    // staging: thread = (four neighbouring rows, one 8-dim chunk); R = the four rows
+    // staging: thread = (four neighbouring rows, one 8-dim chunk); R = the four rows.  Up to d_h = 64
+    // (SPLIT) threads 0 .. 127 stage K and its transposed copy and threads 128 .. 255 stage V
+    // (pass 2); above, every staging thread does both
     constexpr int NQC = 16 * (DH / 8), R = 4;
+    constexpr bool SPLIT = NQC <= 128 && 64 * kDqWaves >= 256;
     static_assert(NQC <= 256, "d_h <= 128");
-    const int rq = (tid / (DH / 8)) * 4, cq = tid % (DH / 8);
-    u32x4_t pk[R], pv[R];
+    const bool vrole = SPLIT && tid >= 128 && tid < 256;  // this thread stages V (wave-uniform)
+    const int sid = SPLIT ? (tid & 127) : tid;
+    const bool stager = (SPLIT ? tid < 256 : true) && sid < NQC;
+    const int rq = (sid / (DH / 8)) * 4, cq = sid % (DH / 8);
+    u32x4_t pk[R], pv[SPLIT ? 1 : R];
     auto fetch = [&](int it) {
         const int kt = it % ntile;
         const bool full = it >= ntile;
@@ -848,10 +854,15 @@ __global__ void __launch_bounds__(64 * kDqWaves) bwd_dq_mfma_kernel(BwdArgs a, c
         for (int r = 0; r < R; ++r) {
             const int kk = rq + r, c8 = cq;
             const int64_t kp = (int64_t)kt * 64 + kk;
-            pk[r] = pv[r] = u32x4_t{0u, 0u, 0u, 0u};
-            if (tid < NQC && kp < S) {
-                pk[r] = *reinterpret_cast<const u32x4_t*>(Kb + kp * DH + 8 * c8);
-                if (full) pv[r] = *reinterpret_cast<const u32x4_t*>(Vb + kp * DH + 8 * c8);
+            pk[r] = u32x4_t{0u, 0u, 0u, 0u};
+            if (!SPLIT) pv[SPLIT ? 0 : r] = u32x4_t{0u, 0u, 0u, 0u};
+            if (stager && kp < S) {
+                if (SPLIT) {
+                    if (!vrole || full) pk[r] = *reinterpret_cast<const u32x4_t*>((vrole ? Vb : Kb) + kp * DH + 8 * c8);
+                } else {
+                    pk[r] = *reinterpret_cast<const u32x4_t*>(Kb + kp * DH + 8 * c8);
+                    if (full) pv[SPLIT ? 0 : r] = *reinterpret_cast<const u32x4_t*>(Vb + kp * DH + 8 * c8);
+                }
             }
         }
     };
@@ -867,13 +878,14 @@ __global__ void __launch_bounds__(64 * kDqWaves) bwd_dq_mfma_kernel(BwdArgs a, c
         const int kt = it % ntile;
         const bool full = it >= ntile;
         __syncthreads();  // the previous tile's products are done
-        if (tid < NQC) {
+        if (stager && (!vrole || full)) {
+            uint16_t* const rowm = vrole ? Vs : Ks;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                *reinterpret_cast<u32x4_t*>(&Ks[(rq + r) * P1 + 8 * cq]) = pk[r];
-                if (full) *reinterpret_cast<u32x4_t*>(&Vs[(rq + r) * P1 + 8 * cq]) = pv[r];
+                *reinterpret_cast<u32x4_t*>(&rowm[(rq + r) * P1 + 8 * cq]) = pk[r];
+                if (!SPLIT && full) *reinterpret_cast<u32x4_t*>(&Vs[(rq + r) * P1 + 8 * cq]) = pv[SPLIT ? 0 : r];
             }
-            if (full)
+            if (full && !vrole)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     *reinterpret_cast<u32x2_t*>(&KsT[(8 * cq + e) * P2 + rq]) =
