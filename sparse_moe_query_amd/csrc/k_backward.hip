@@ -534,7 +534,8 @@ __global__ void bwd_mprep_kernel(BwdArgs a, uint16_t* __restrict__ Vr, uint16_t*
 
 // dk, dv of 128 keys (wave w: keys 32 w .. 32 w + 31, two 16-key column groups) of one (sequence,
 // group) over the later queries of every head of the group, query tiles of 64 staged in LDS
-// row-major and transposed; every fragment read from LDS feeds the products of both column groups.
+// row-major (the gradient products read them transposed with ds_read_b64_tr_b16); every fragment
+// read from LDS feeds the products of both column groups.
 // 16 x 16 products in v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x16_bf16 for a last 16 head dims):
 // the score products contract the head dims, the gradient products P^T dO and dS^T Q contract 32
 // queries at a time -- the lane's four queries of two consecutive 16-query blocks, the transposed
@@ -547,7 +548,7 @@ __global__ void __launch_bounds__(256, DH <= 48 ? 2 : 1) bwd_dkv_mfma_kernel(Bwd
                                                            const uint16_t* __restrict__ dOb) {
     constexpr int NC = DH / 16, N32 = DH / 32, R16 = (DH % 32) / 16, P1 = DH + 8, P2 = 72;
     constexpr int F32 = N32 > 0 ? N32 : 1;
-    __shared__ __align__(16) uint16_t Qs[64 * P1], dOs[64 * P1], QsT[DH * P2], dOsT[DH * P2];
+    __shared__ __align__(16) uint16_t Qs[64 * P1], dOs[64 * P1];
     __shared__ float lss[64], dds[64];
     // longest first: key block 0 (every query tile after it) of every (group, sequence) leads
     // one work group per (key block, group, sequence), and one more per (key block, sequence) for
@@ -639,26 +640,13 @@ __global__ void __launch_bounds__(256, DH <= 48 ? 2 : 1) bwd_dkv_mfma_kernel(Bwd
         if (stager) {
             if (SPLIT) {
                 uint16_t* const rowm = dorole ? dOs : Qs;
-                uint16_t* const tr = dorole ? dOsT : QsT;
 #pragma unroll
                 for (int r = 0; r < R; ++r) *reinterpret_cast<u32x4_t*>(&rowm[(rq + r) * P1 + 8 * cq]) = pq[r];
-                // transposed: dim 8 cq + e, rows rq .. rq + 3 in one 8-byte store
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    *reinterpret_cast<u32x2_t*>(&tr[(8 * cq + e) * P2 + rq]) =
-                        u32x2_t{bf16_pair(pq[0], pq[1], e), bf16_pair(pq[2], pq[3], e)};
             } else {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     *reinterpret_cast<u32x4_t*>(&Qs[(rq + r) * P1 + 8 * cq]) = pq[r];
                     *reinterpret_cast<u32x4_t*>(&dOs[(rq + r) * P1 + 8 * cq]) = pd[SPLIT ? 0 : r];
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    *reinterpret_cast<u32x2_t*>(&QsT[(8 * cq + e) * P2 + rq]) =
-                        u32x2_t{bf16_pair(pq[0], pq[1], e), bf16_pair(pq[2], pq[3], e)};
-                    *reinterpret_cast<u32x2_t*>(&dOsT[(8 * cq + e) * P2 + rq]) =
-                        u32x2_t{bf16_pair(pd[0], pd[SPLIT ? 0 : 1], e), bf16_pair(pd[SPLIT ? 0 : 2], pd[SPLIT ? 0 : 3], e)};
                 }
             }
         }
@@ -695,13 +683,20 @@ __global__ void __launch_bounds__(256, DH <= 48 ? 2 : 1) bwd_dkv_mfma_kernel(Bwd
                     dq4[h2][i] = dds[q0 + 4 * j4 + i];
                 }
             }
-            // transposed Q and dO: head dim 16 c + l16, the lane's queries of both blocks
+            // Q and dO transposed on the read (ds_read_b64_tr_b16): lane j of a 16-lane group
+            // addresses row row0 + j / 4, columns col0 + 4 (j % 4) .. + 3, and lane i receives rows
+            // row0 .. row0 + 3 of column col0 + i -- head dim 16 c + l16, the lane's four queries of
+            // each of the two blocks
+            typedef __attribute__((address_space(3))) s16x4_t* lds_s4;
+            auto trq = [&](const uint16_t* T, int row0, int col0) {
+                return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s4)(&T[(row0 + (l16 >> 2)) * P1 + col0 + 4 * (l16 & 3)]));
+            };
             bf16x8_t qtb[NC], dtb[NC];
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const int r = (16 * c + l16) * P2 + qp + 4 * j4;
-                qtb[c] = join8(lds8(&QsT[r]), lds8(&QsT[r + 16]));
-                dtb[c] = join8(lds8(&dOsT[r]), lds8(&dOsT[r + 16]));
+                qtb[c] = join8(trq(Qs, qp + 4 * j4, 16 * c), trq(Qs, qp + 16 + 4 * j4, 16 * c));
+                dtb[c] = join8(trq(dOs, qp + 4 * j4, 16 * c), trq(dOs, qp + 16 + 4 * j4, 16 * c));
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
