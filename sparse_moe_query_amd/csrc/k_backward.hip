@@ -546,7 +546,7 @@ __global__ void bwd_mprep_kernel(BwdArgs a, uint16_t* __restrict__ Vr, uint16_t*
 template <int DH>
 __global__ void __launch_bounds__(256, DH <= 48 ? 2 : 1) bwd_dkv_mfma_kernel(BwdArgs a, const uint16_t* __restrict__ Vr,
                                                            const uint16_t* __restrict__ dOb) {
-    constexpr int NC = DH / 16, N32 = DH / 32, R16 = (DH % 32) / 16, P1 = DH + 8, P2 = 72;
+    constexpr int NC = DH / 16, N32 = DH / 32, R16 = (DH % 32) / 16, P1 = DH + 8;
     constexpr int F32 = N32 > 0 ? N32 : 1;
     __shared__ __align__(16) uint16_t Qs[64 * P1], dOs[64 * P1];
     __shared__ float lss[64], dds[64];
@@ -596,8 +596,8 @@ __global__ void __launch_bounds__(256, DH <= 48 ? 2 : 1) bwd_dkv_mfma_kernel(Bwd
     const int qt0 = 2 * kb, ntl = nqt - qt0, total = nh * ntl;
     auto head = [&](int hi) { return shared_part ? a.G * a.k : g * a.k + hi; };
     // staging: thread = (four neighbouring rows, one 8-dim chunk); R = the four rows.  Up to d_h = 64
-    // (SPLIT) waves 0-1 stage Q and waves 2-3 dO, each with its transposed copy, so a staging thread
-    // does half the work and holds half the prefetch registers; above, every staging thread does both
+    // (SPLIT) waves 0-1 stage Q and waves 2-3 dO, so a staging thread does half the work and holds
+    // half the prefetch registers; above, every staging thread does both
     constexpr int NQC = 16 * (DH / 8), R = 4;
     constexpr bool SPLIT = NQC <= 128;
     static_assert(NQC <= 256, "d_h <= 128");
@@ -787,10 +787,10 @@ constexpr int kDqWaves = 8;  // waves of the query-block kernel (16 queries each
 template <int DH>
 __global__ void __launch_bounds__(64 * kDqWaves) bwd_dq_mfma_kernel(BwdArgs a, const uint16_t* __restrict__ Vr,
                                                                     const uint16_t* __restrict__ dOb) {
-    constexpr int NC = DH / 16, N32 = DH / 32, R16 = (DH % 32) / 16, P1 = DH + 8, P2 = 72;
+    constexpr int NC = DH / 16, N32 = DH / 32, R16 = (DH % 32) / 16, P1 = DH + 8;
     constexpr int F32 = N32 > 0 ? N32 : 1;
     constexpr int QB = 16 * kDqWaves;  // queries per work group, 16 per wave
-    __shared__ __align__(16) uint16_t Ks[64 * P1], Vs[64 * P1], KsT[DH * P2];
+    __shared__ __align__(16) uint16_t Ks[64 * P1], Vs[64 * P1];
     // longest first: the last query block (every key tile before it) of every (head, sequence) leads
     const int nqb = (int)ceil_div(a.S, QB);
     const int qb = nqb - 1 - (int)(blockIdx.x / (a.H * a.B));
@@ -829,10 +829,10 @@ __global__ void __launch_bounds__(64 * kDqWaves) bwd_dq_mfma_kernel(BwdArgs a, c
     // pass 2 (ntile .. 2 ntile - 1): dS^T = P^T (dP^T - D), dq += dS K.  The next iteration's key
     // (and value) tile is loaded into registers while the current one multiplies.  16 x 16 products in
     // v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x16_bf16 for a last 16 head dims); dq += dS K
-    // contracts 32 keys at a time (the lane's four keys of two consecutive 16-key sub-tiles, K^T read
-    // in the same order).
+    // contracts 32 keys at a time (the lane's four keys of two consecutive 16-key sub-tiles, K read
+    // transposed in the same order with ds_read_b64_tr_b16).
     // staging: thread = (four neighbouring rows, one 8-dim chunk); R = the four rows.  Up to d_h = 64
-    // (SPLIT) threads 0 .. 127 stage K and its transposed copy and threads 128 .. 255 stage V
+    // (SPLIT) threads 0 .. 127 stage K and threads 128 .. 255 stage V
     // (pass 2); above, every staging thread does both
     constexpr int NQC = 16 * (DH / 8), R = 4;
     constexpr bool SPLIT = NQC <= 128 && 64 * kDqWaves >= 256;
@@ -880,11 +880,6 @@ __global__ void __launch_bounds__(64 * kDqWaves) bwd_dq_mfma_kernel(BwdArgs a, c
                 *reinterpret_cast<u32x4_t*>(&rowm[(rq + r) * P1 + 8 * cq]) = pk[r];
                 if (!SPLIT && full) *reinterpret_cast<u32x4_t*>(&Vs[(rq + r) * P1 + 8 * cq]) = pv[SPLIT ? 0 : r];
             }
-            if (full && !vrole)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    *reinterpret_cast<u32x2_t*>(&KsT[(8 * cq + e) * P2 + rq]) =
-                        u32x2_t{bf16_pair(pk[0], pk[1], e), bf16_pair(pk[2], pk[3], e)};
         }
         __syncthreads();
         if (it + 1 < 2 * ntile) fetch(it + 1);
@@ -916,6 +911,12 @@ __global__ void __launch_bounds__(64 * kDqWaves) bwd_dq_mfma_kernel(BwdArgs a, c
             }
             L = m + __builtin_amdgcn_logf(l);
         }
+        typedef __attribute__((address_space(3))) s16x4_t* lds_s4;
+        // lane j of a 16-lane group addresses key row0 + j / 4, dims col0 + 4 (j % 4) .. + 3; lane i
+        // receives keys row0 .. row0 + 3 of dim col0 + i
+        auto trk = [&](int row0, int col0) {
+            return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&Ks[(row0 + (l16 >> 2)) * P1 + col0 + 4 * (l16 & 3)]));
+        };
         // S^T (rows keys k0 + 4 j4 + i, column the lane's query) of one 16-key sub-tile
         auto scores = [&](const uint16_t* Tl, int k0, const bf16x8_t (&f)[F32], const s16x4_t& f16) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -962,11 +963,11 @@ __global__ void __launch_bounds__(64 * kDqWaves) bwd_dq_mfma_kernel(BwdArgs a, c
                     }
                 }
                 const bf16x8_t da = __builtin_bit_cast(bf16x8_t, pack8(ds));
+                // K transposed on the read (ds_read_b64_tr_b16): head dim 16 c + l16, the lane's
+                // four keys of each of the two 16-key sub-tiles
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    const int r = (16 * c + l16) * P2 + sp + 4 * j4;
-                    dq[c] = mma32(da, join8(lds8(&KsT[r]), lds8(&KsT[r + 16])), dq[c]);
-                }
+                for (int c = 0; c < NC; ++c)
+                    dq[c] = mma32(da, join8(trk(sp + 4 * j4, 16 * c), trk(sp + 16 + 4 * j4, 16 * c)), dq[c]);
             }
         }
     }
