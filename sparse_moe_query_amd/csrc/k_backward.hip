@@ -118,12 +118,6 @@ __device__ __forceinline__ void ld8(const void* p, int64_t i, float (&v)[8]) {
     }
 }
 __device__ __forceinline__ void ld8f(const float* p, float (&v)[8]) { ld8<float>(p, 0, v); }
-// element e of lo and of hi (eight bf16 each) as one bf16 pair
-__device__ __forceinline__ uint32_t bf16_pair(const u32x4_t& lo, const u32x4_t& hi, int e) {
-    const uint32_t a = (lo[e >> 1] >> (16 * (e & 1))) & 0xffffu, b = (hi[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-    return a | (b << 16);
-}
-__device__ __forceinline__ uint16_t bf16_bits(float v) { return (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu); }
 __device__ __forceinline__ u32x4_t pack8(const float (&v)[8]) {
     return u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
 }
@@ -153,12 +147,6 @@ __device__ __forceinline__ float dot4(const f32x4_t& u, const f32x4_t& v) {
     return u[0] * v[0] + u[1] * v[1] + u[2] * v[2] + u[3] * v[3];
 }
 
-// routed head h = g k + r of token t -> expert; the shared head -> -1
-__device__ __forceinline__ int expert_of(const BwdArgs& a, int64_t t, int h) {
-    if (h >= a.G * a.k) return -1;
-    const int g = h / a.k, r = h % a.k;
-    return a.dense ? g * a.n + r : a.idx[(t * a.G + g) * a.k + r];
-}
 __device__ __forceinline__ int group_of(const BwdArgs& a, int h) { return h < a.G * a.k ? h / a.k : a.skv; }
 
 // ---------------------------------------------------------------- head-output and router gradients
@@ -473,9 +461,6 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4_t mma16(const s16x4_t& a, const s16x4_t& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ s16x4_t pack4(const float (&v)[4]) {
-    return __builtin_bit_cast(s16x4_t, u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
 }
 __device__ __forceinline__ s16x4_t lds8(const uint16_t* p) { return *reinterpret_cast<const s16x4_t*>(p); }
 // sixteen bytes (eight bf16) from LDS or global memory, and two four-element pieces joined
