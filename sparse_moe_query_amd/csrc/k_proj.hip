@@ -68,13 +68,25 @@ struct ProjArgs {
 // distinct bank groups.
 __device__ __forceinline__ int swz64(int row, int c) { return (row * 8 + (c ^ ((row >> 1) & 7))) * 8; }
 
-// One 64-wide slice of the hidden dimension for one wave: C^T += W^T x^T over the row blocks
-// xrow[] of the x stage and the wave's d_h weight rows.  FULL: all eight row blocks hold rows
-// (straight-line body); otherwise only the first nrb (wave-uniform) are multiplied.  The
-// accumulators are indexed by constants either way, so they stay in registers.
-template <int DH, bool FULL>
+// Compile-time loop: f(integral_constant<int, I>) for I = B .. E - 1, so array indices derived from
+// I are constants whatever the unroller decides (the accumulators stay in registers).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// One 64-wide slice of the hidden dimension for one wave: C^T += W^T x^T over the first NRB row
+// blocks xrow[] of the x stage and the wave's d_h weight rows.  The x fragments are read two row
+// blocks ahead of their products into a three-entry ring (the scheduling barriers pin that order:
+// left alone, the compiler reads each fragment right before its products), and the row-block count
+// is a template argument, so the body is straight-line code whose LDS waits count exactly the
+// reads in flight (with a run-time count every conditional read made the compiler wait for all).
+template <int DH, int NRB>
 __device__ __forceinline__ void mma_slice(f32x4_t (&acc)[8][DH / 16], const uint16_t* xb, const uint16_t* wb,
-                                          const int (&xrow)[8], int wrow, int lane, int nrb) {
+                                          const int (&xrow)[8], int wrow, int lane) {
     constexpr int CB = DH / 16;
 #pragma unroll
     for (int ks = 0; ks < kKC / 32; ++ks) {
@@ -83,14 +95,20 @@ __device__ __forceinline__ void mma_slice(f32x4_t (&acc)[8][DH / 16], const uint
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
             wf[cb] = *reinterpret_cast<const bf16x8_t*>(wb + swz64(wrow + 16 * cb + (lane & 15), c));
-#pragma unroll
-        for (int rb = 0; rb < 8; ++rb) {
-            if (!FULL && rb >= nrb) break;
-            const bf16x8_t xf = *reinterpret_cast<const bf16x8_t*>(xb + swz64(xrow[rb], c));
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-                acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[cb], xf, acc[rb][cb], 0, 0, 0);
-        }
+        auto xfrag = [&](int rb) { return *reinterpret_cast<const bf16x8_t*>(xb + swz64(xrow[rb], c)); };
+        bf16x8_t xq[3];
+        xq[0] = xfrag(0);
+        if constexpr (NRB > 1) xq[1] = xfrag(1);
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, NRB>([&](auto rbc) {
+            constexpr int rb = decltype(rbc)::value;
+            if constexpr (rb + 2 < NRB) xq[(rb + 2) % 3] = xfrag(rb + 2);
+            static_for<0, CB>([&](auto cbc) {
+                constexpr int cb = decltype(cbc)::value;
+                acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[cb], xq[rb % 3], acc[rb][cb], 0, 0, 0);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
     }
 }
 
@@ -320,19 +338,29 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
         }
     };
 
-    // ---- main loop: the same barriers for every wave; a wave with all eight row blocks runs
-    // the straight-line body
-    auto run = [&](auto full) {
+    // ---- main loop: the same barriers for every wave; the loop is specialised on the wave's
+    // row-block count (one copy per count, chosen once)
+    auto run = [&](auto nrbc) {
+        constexpr int NRB = decltype(nrbc)::value;
         for (int kc = 0; kc < nk; ++kc) {
             const int stage = kc & 1;
             if (kc + 1 < nk) issue(kc + 1, stage ^ 1);
-            if (nrb > 0) mma_slice<DH, decltype(full)::value>(acc, xs[stage], wls[stage], xrow, slot * DH, lane, nrb);
+            if constexpr (NRB > 0) mma_slice<DH, NRB>(acc, xs[stage], wls[stage], xrow, slot * DH, lane);
             __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
             __syncthreads();
         }
     };
-    if (nrb == 8) run(std::true_type{});
-    else run(std::false_type{});
+    switch (nrb) {
+        case 0: run(std::integral_constant<int, 0>{}); break;
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        case 4: run(std::integral_constant<int, 4>{}); break;
+        case 5: run(std::integral_constant<int, 5>{}); break;
+        case 6: run(std::integral_constant<int, 6>{}); break;
+        case 7: run(std::integral_constant<int, 7>{}); break;
+        default: run(std::integral_constant<int, 8>{}); break;
+    }
     if (active) epilogue();
     if (a.stats_here && blockIdx.x == gridDim.x - 1) {
         // the x stages are free now: LDS scratch of the statistics finalize
