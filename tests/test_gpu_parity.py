@@ -56,6 +56,10 @@ SMALL = [
     _small("long_k2_dh64", d=1024, k=2, dh=64, B=1, S=700, seed=10),
     _small("long_dh32_k2", d=256, N=8, G=4, k=2, dh=32, B=2, S=900, seed=11),
     _small("long_gqa", B=1, S=800, k=2, variant="hard_concat", shared_head=False, dense_gqa=True, seed=12),
+    # routing skewed toward local expert 0 (about 85 % and 76 % of the tokens) and a ragged last
+    # tile: the projection's routed and dense waves multiply every row-block count from 1 to 8
+    _small("skew_k1_partial_tile", B=2, S=242, router_bias_first=1.5, seed=14),
+    _small("skew_k1_dh32", d=256, N=8, G=4, k=1, dh=32, B=1, S=300, router_bias_first=1.0, seed=15),
     # bf16 with a hidden size that is not a multiple of 64: scalar projection and combine, matrix-core
     # attention on a schedule built by its own kernel
     _small("bf16_d96_scalar_proj", d=96, N=8, G=4, k=1, dh=32, B=2, S=700, seed=13),
