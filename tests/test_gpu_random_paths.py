@@ -1,19 +1,22 @@
-"""GPU parity of the backward pass and of decode over seeded draws of the layer's configuration.
+"""GPU parity of the backward pass, of decode and of the top-k MoE-MLP over seeded draws of the
+layer's configuration.
 
 As in test_gpu_random_configs.py, the parameters and shapes come from fixed seeds (the same cases
 every run), restricted to what each entry point supports: the backward takes head dims that are
 multiples of 16 and at most 16 experts per group; decode takes 16-byte cache rows, at most eight
-active heads per group and at most 8192 slot dims per token.  The checks are those of the
-hand-picked cases (tests/test_gpu_backward.py, tests/test_gpu_decode.py).
+active heads per group and at most 8192 slot dims per token; the MoE-MLP takes bf16, at most 16
+experts and sizes that are multiples of 32.  The checks are those of the hand-picked cases
+(tests/test_gpu_backward.py, tests/test_gpu_decode.py, tests/test_gpu_moe.py).
 """
 from __future__ import annotations
 
 import numpy as np
 import pytest
 
-from sparse_moe_query_amd.inputs import Workload
+from sparse_moe_query_amd.inputs import MoeWorkload, Workload
 from tests.test_gpu_backward import _check as check_backward
 from tests.test_gpu_decode import _decode_steps
+from tests.test_gpu_moe import test_moe_matches_oracle as check_moe
 
 pytestmark = pytest.mark.gpu
 
@@ -68,3 +71,23 @@ def test_random_decode(wl):
     lens = sorted(int(v) for v in r.integers(0, max(1, wl.seq - 2), size=wl.batch))
     lens[0] = 0
     _decode_steps(wl, lens, 2, wl.seq)
+
+
+def _moe_draw(i: int) -> MoeWorkload:
+    r = np.random.default_rng(8300 + i)
+    E = int(r.integers(1, 17))
+    k = int(r.integers(1, min(E, 4) + 1))
+    d = int(r.choice([64, 96, 128, 192, 256, 320]))
+    dff = int(r.choice([32, 64, 96, 160, 256, 512]))
+    T = int(r.integers(1, 601))
+    act = str(r.choice(["gelu", "relu"]))
+    return MoeWorkload(f"rmoe{i:02d}_d{d}_E{E}_k{k}_ff{dff}_T{T}_{act}", d, E, k, dff, T, activation=act,
+                       seed=500 + i)
+
+
+MOE = [_moe_draw(i) for i in range(8)]
+
+
+@pytest.mark.parametrize("wl", MOE, ids=[w.name for w in MOE])
+def test_random_moe(wl):
+    check_moe(wl)
