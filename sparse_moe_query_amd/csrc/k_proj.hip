@@ -135,7 +135,7 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int slot = w & 3, half = w >> 2;
+    const int half = w >> 2;
     // XCD-aware order: the items of one token tile run on one XCD so its x tile stays in L2
     const int L = (int)blockIdx.x - a.sched_here;
     int tile, job;
@@ -151,6 +151,10 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
     job = __builtin_amdgcn_readfirstlane(job);
     const int64_t t0 = (int64_t)tile * kBM;
     const int hb0 = job * 4;
+    // a job holding only the last head block (an expert) spreads it over all eight waves,
+    // 32 rows each, instead of leaving six of them idle
+    const bool single = hb0 + 1 == a.HB && hb0 >= 2 * a.G + a.s;
+    const int slot = single ? 0 : (w & 3);
     const int hb = hb0 + slot;
     const bool active = hb < a.HB;
     const int GD = a.G;
@@ -188,50 +192,63 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
         for (int i = 0; i < LW; ++i) dma16(a.wproj + kc * kKC, woff[i], &wls[stage][(w + kWaves * i) * 512]);
     };
-    issue(0, 0);
-
-    // ---- row lists: the first wave of each routed head block buckets the tile's decisions
-    if (routed && half == 0) {
-        int base = 0;
-        for (int part = 0; part < kBM / 64; ++part) {
-            const int row = part * 64 + lane;
-            const int64_t t = t0 + row;
-            int rank = -1;
-            if (t < a.T) {
-                const int32_t* id = a.idx + (t * a.G + g_of) * a.k;
-                for (int r = 0; r < a.k; ++r)
-                    if (id[r] == e) rank = r;
+    // ---- row lists, built before the first copies are issued so that their index loads wait for
+    // nothing else: the first wave of each routed head block buckets the tile's decisions; the
+    // tile's four index entries per lane are loaded together, one choice rank at a time
+    if (routed && (single ? w == 0 : half == 0)) {
+        constexpr int NP = kBM / 64;
+        int rank[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) rank[p] = -1;
+        for (int r = 0; r < a.k; ++r) {
+            int32_t id[NP];
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int64_t t = t0 + p * 64 + lane;
+                const int64_t tc = t < a.T ? t : a.T - 1;  // in bounds; masked below
+                id[p] = a.idx[(tc * a.G + g_of) * a.k + r];
+                if (t >= a.T) id[p] = -1;
             }
-            const uint64_t m = __builtin_amdgcn_ballot_w64(rank >= 0);
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+                if (id[p] == e) rank[p] = r;
+        }
+        int base = 0;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const uint64_t m = __builtin_amdgcn_ballot_w64(rank[p] >= 0);
             const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-            if (rank >= 0) rows[slot][base + pre] = (uint16_t)(row | (rank << 8));
+            if (rank[p] >= 0) rows[slot][base + pre] = (uint16_t)((p * 64 + lane) | (rank[p] << 8));
             base += __builtin_popcountll(m);
         }
         // padding entries (past the list) point at row 0 so every LDS read stays in the tile
         for (int i = base + lane; i < kBM; i += 64) rows[slot][i] = 0;
         if (lane == 0) rcount[slot] = base;
     }
+    issue(0, 0);
     __syncthreads();  // row lists visible
     int nrows;
     int myrow[8], xrow[8];  // row | rank << 8, and the row alone, of the lane's row in each row block
     if (routed) {
         // the head block's list split in whole 16-row blocks: half 0 takes the first
-        // 16 * ceil(cnt / 32) entries (at most 128), half 1 the rest
+        // 16 * ceil(cnt / 32) entries (at most 128), half 1 the rest; in a single-block job
+        // wave w takes entries 32 w .. 32 w + 31
         const int cnt = rcount[slot];
         const int split = min(cnt, 16 * ((cnt + 31) / 32));
-        const int first = half ? split : 0;
-        nrows = half ? cnt - split : split;
+        const int first = single ? 32 * w : (half ? split : 0);
+        nrows = single ? max(0, min(32, cnt - first)) : (half ? cnt - split : split);
 #pragma unroll
         for (int rb = 0; rb < 8; ++rb) {
             const int i = first + 16 * rb + (lane & 15);
             myrow[rb] = rows[slot][i < kBM ? i : 0];
         }
     } else {
-        const int64_t rem = a.T - t0 - 128 * half;
-        nrows = active ? (int)(rem < 0 ? 0 : (rem < 128 ? rem : 128)) : 0;
+        const int r0 = single ? 32 * w : 128 * half, rmax = single ? 32 : 128;
+        const int64_t rem = a.T - t0 - r0;
+        nrows = active ? (int)(rem < 0 ? 0 : (rem < rmax ? rem : rmax)) : 0;
         const int rank = is_expert ? e % a.n : 0;  // all-active GQA: expert j of a group is head j
 #pragma unroll
-        for (int rb = 0; rb < 8; ++rb) myrow[rb] = (128 * half + 16 * rb + (lane & 15)) | (rank << 8);
+        for (int rb = 0; rb < 8; ++rb) myrow[rb] = ((r0 + 16 * rb + (lane & 15)) & 0xff) | (rank << 8);
     }
 #pragma unroll
     for (int rb = 0; rb < 8; ++rb) xrow[rb] = myrow[rb] & 0xff;
