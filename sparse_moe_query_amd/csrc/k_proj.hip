@@ -150,15 +150,19 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
     tile = __builtin_amdgcn_readfirstlane(tile);  // keep the tile's addresses in scalar registers
     job = __builtin_amdgcn_readfirstlane(job);
     const int64_t t0 = (int64_t)tile * kBM;
-    const int hb0 = job * 4;
-    // a job holding only the last head block (an expert) spreads it over all eight waves,
-    // 32 rows each, instead of leaving six of them idle
-    const bool single = hb0 + 1 == a.HB && hb0 >= 2 * a.G + a.s;
-    const int slot = single ? 0 : (w & 3);
-    const int hb = hb0 + slot;
-    const bool active = hb < a.HB;
     const int GD = a.G;
-    // head block kinds: [0,G) K_g, [G,2G) V_g, 2G shared query (if s), then expert e
+    // head block kinds: [0,G) K_g, [G,2G) V_g, 2G shared query (if s), then expert e. Jobs take
+    // them in the order K, V, experts, shared query: the dense shared block comes last, alone
+    // in the last job when 4 j + 1 blocks leave one over, instead of sharing a job (and a SIMD's
+    // two waves) with routed blocks that hold about half as many rows
+    auto hb_at = [&](int p) { return (a.s && p >= 2 * GD) ? (p == a.HB - 1 ? 2 * GD : p + 1) : p; };
+    const int p0 = job * 4;
+    // a job holding only the last head block (not a K block, whose epilogue keeps per-half key
+    // norms) spreads it over all eight waves, 32 rows each, instead of leaving six of them idle
+    const bool single = p0 + 1 == a.HB && hb_at(p0) >= GD;
+    const int slot = single ? 0 : (w & 3);
+    const bool active = p0 + slot < a.HB;
+    const int hb = active ? hb_at(p0 + slot) : a.HB;
     const int ebase = 2 * GD + a.s;
     const bool is_v = active && hb >= GD && hb < 2 * GD;
     const bool is_expert = active && hb >= ebase;
@@ -181,8 +185,8 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
     for (int i = 0; i < LW; ++i) {
         const int q = (w + kWaves * i) * 64 + lane;
         const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
-        int h = hb0 + r / DH;
-        if (h >= a.HB) h = 0;
+        const int pw = p0 + r / DH;
+        const int h = pw < a.HB ? hb_at(pw) : 0;
         woff[i] = (uint32_t)(((h * DH + r % DH) * a.d + 8 * c) * 2);
     }
     const bf16_t* xbase = a.x + t0 * a.d;
