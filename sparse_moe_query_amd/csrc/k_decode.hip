@@ -294,9 +294,27 @@ __global__ void __launch_bounds__(256) dec_proj_kernel(DecArgs a) {
     const T* X = (const T*)a.x;
     for (int c0 = 0; c0 < d; c0 += CH) {
         const int nc = d - c0 < CH ? d - c0 : CH;
-        for (int i = tid; i < kTok * CH; i += 256) {
-            const int t = i / CH, c = i - t * CH;
-            xs[t][c] = (t < ntok && c < nc) ? to_f32(X[(int64_t)(list[t] & 0xffffff) * d + c0 + c]) : 0.f;
+        // the chunk of the token rows, 16 bytes per load (d is a multiple of E), every load of the
+        // thread issued before the first is used: one memory round trip per chunk
+        constexpr int NV = kTok * kDC / E / 256;
+        const int vr = CH / E;  // 16-byte units per staged row
+        u32x4_t xv[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int i = tid + 256 * j;
+            const int t = i / vr, c = (i - t * vr) * E;
+            xv[j] = u32x4_t{0u, 0u, 0u, 0u};
+            if (t < ntok && c < nc) xv[j] = load16(X + (int64_t)(list[t] & 0xffffff) * d + c0 + c);
+        }
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int i = tid + 256 * j;
+            const int t = i / vr, c = (i - t * vr) * E;
+            if (t >= kTok) continue;
+            float f[E];
+            widen16(xv[j], f);
+#pragma unroll
+            for (int q = 0; q < E; ++q) xs[t][c + q] = f[q];  // zero past the tokens and the chunk
         }
         __syncthreads();
         if (uact) {
@@ -545,7 +563,7 @@ __global__ void __launch_bounds__(64) dec_merge_kernel(DecArgs a) {
 template <typename T>
 __global__ void __launch_bounds__(64) dec_oproj_kernel(DecArgs a) {
     constexpr int E = 16 / (int)sizeof(T);
-    __shared__ float vs[kTok][128 + kOprojRows];
+    __shared__ __align__(16) float vs[kTok][128 + kOprojRows];
     __shared__ int list[kTok];
     __shared__ int wcount[1];
     const int sm = blockIdx.x, tg = blockIdx.y, lane = threadIdx.x;
@@ -584,24 +602,65 @@ __global__ void __launch_bounds__(64) dec_oproj_kernel(DecArgs a) {
     const int ntok = token_group(a, kind == 0 && !a.dense, e, g, kind == 0 ? e % a.n : 0, tg, list, wcount);
     if (ntok <= 0) return;
     constexpr int VW = 128 + kOprojRows;  // slot vector row (zero past d_h)
-    for (int i = lane; i < kTok * VW; i += 64) {
-        const int t = i / VW, jj = i - t * VW;
-        float v = 0.f;
-        if (t < ntok && jj < dh) {
+    static_assert(VW % 4 == 0, "float4 units");
+    // the slot vectors in float4 units (d_h is a multiple of 4), lane i taking units i, i + 64, ...;
+    // every load of a lane is issued before the first is used (the renormalised slot: once per
+    // choice rank), so the staging costs one memory round trip instead of one per element
+    constexpr int VU = VW / 4, NI = (kTok * VU + 63) / 64;
+    const bool wc = !a.dense && a.variant == GQE_VARIANT_WEIGHTED_CONCAT;
+    f32x4_t vv[NI];
+    const float* orow[NI];  // the unit's source in the token's head outputs (null: zero)
+    int64_t selr[NI];       // the token's routing entries
+    int rk[NI];
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+        const int i = lane + 64 * n, t = i / VU, j = (i - t * VU) * 4;
+        vv[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        orow[n] = nullptr;
+        selr[n] = 0;
+        rk[n] = 0;
+        if (t < ntok && j < dh) {
             const int tk = list[t];
-            const int b = tk & 0xffffff, r = tk >> 24;
-            const float* o = a.od + (int64_t)b * a.H * dh;
-            const int64_t sel = ((int64_t)b * G + g) * a.k;
-            if (kind == 0) {
-                const float coef = (!a.dense && a.variant == GQE_VARIANT_WEIGHTED_CONCAT) ? a.psel[sel + r] : 1.f;
-                v = coef * o[(g * kr + r) * dh + jj];
-            } else if (kind == 1) {
-                for (int q = 0; q < a.k; ++q) v += a.wsel[sel + q] * o[(g * a.k + q) * dh + jj];
-            } else {
-                v = o[nr * dh + jj];
+            const int b = tk & 0xffffff;
+            rk[n] = tk >> 24;
+            selr[n] = ((int64_t)b * G + g) * a.k;
+            orow[n] = a.od + (int64_t)b * a.H * dh + j;
+        }
+    }
+    if (kind == 1) {
+        for (int q = 0; q < a.k; ++q) {
+            f32x4_t ov[NI];
+            float wq[NI];
+#pragma unroll
+            for (int n = 0; n < NI; ++n) {
+                ov[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                wq[n] = 0.f;
+                if (orow[n]) {
+                    ov[n] = *reinterpret_cast<const f32x4_t*>(orow[n] + (g * a.k + q) * dh);
+                    wq[n] = a.wsel[selr[n] + q];
+                }
+            }
+#pragma unroll
+            for (int n = 0; n < NI; ++n) vv[n] += wq[n] * ov[n];
+        }
+    } else {
+        float cf[NI];
+#pragma unroll
+        for (int n = 0; n < NI; ++n) {
+            cf[n] = 1.f;
+            if (orow[n]) {
+                vv[n] = *reinterpret_cast<const f32x4_t*>(orow[n] + (kind == 0 ? (g * kr + rk[n]) * dh : nr * dh));
+                if (kind == 0 && wc) cf[n] = a.psel[selr[n] + rk[n]];
             }
         }
-        vs[t][jj] = v;  // rows past d_h are zero
+#pragma unroll
+        for (int n = 0; n < NI; ++n)
+            if (kind == 0 && wc) vv[n] *= cf[n];
+    }
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+        const int i = lane + 64 * n, t = i / VU, j = (i - t * VU) * 4;
+        if (t < kTok) *reinterpret_cast<f32x4_t*>(&vs[t][j]) = vv[n];  // zero past d_h and the tokens
     }
     __syncthreads();
     if (!cact) return;
