@@ -554,19 +554,24 @@ __global__ void __launch_bounds__(64) dec_merge_kernel(DecArgs a) {
 }
 
 // ---------------------------------------------------------------- output projection per weight slot
-// Work group (one wave) = (weight slot, up to 8 tokens that use it, 64 column units of 16 bytes):
+// Work group (four waves) = (weight slot, up to 8 tokens that use it, 64 column units of 16 bytes):
 // slot = W_o of routed expert e (the tokens that chose it), W_oR of group g (variant gqe) or the
 // shared head's W_os (every token).  Each token's slot vector (its head output, times the
 // raw router probability for weighted_concat; the renormalised mix sum_r w_r o_r for W_oR) times the
-// slot's d_h x d block, each weight row read once for the group of tokens.  Writes the token's
-// float32 partial row of that slot; dec_ysum_kernel adds a token's slots in a fixed order.
+// slot's d_h x d block, each weight row read once for the group of tokens: the waves take the
+// 12-row batches of the block round-robin, and their partial sums meet in LDS in wave order.  Writes
+// the token's float32 partial row of that slot; dec_ysum_kernel adds a token's slots in a fixed
+// order.
 template <typename T>
-__global__ void __launch_bounds__(64) dec_oproj_kernel(DecArgs a) {
+__global__ void __launch_bounds__(256) dec_oproj_kernel(DecArgs a) {
     constexpr int E = 16 / (int)sizeof(T);
+    constexpr int NWV = 4;  // waves
     __shared__ __align__(16) float vs[kTok][128 + kOprojRows];
+    __shared__ __align__(16) float red[NWV][kTok][64 * E];  // the waves' partial sums
     __shared__ int list[kTok];
-    __shared__ int wcount[1];
-    const int sm = blockIdx.x, tg = blockIdx.y, lane = threadIdx.x;
+    __shared__ int wcount[NWV];
+    const int sm = blockIdx.x, tg = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = a.G, dh = a.dh, d = a.d;
     const int kr = a.dense ? a.n : a.k;
     const bool rslot = !a.dense && a.variant == GQE_VARIANT_GQE;
@@ -587,9 +592,11 @@ __global__ void __launch_bounds__(64) dec_oproj_kernel(DecArgs a) {
     const T* W = kind == 0 ? (const T*)a.wo + (int64_t)e * dh * d
                            : (kind == 1 ? (const T*)a.wor + (int64_t)g * dh * d : (const T*)a.wos);
     const T* wp = W + (cact ? cu * E : 0);
-    // weight rows in batches of kOprojRows, the next batch in flight while one is used; the
-    // first is issued before the token selection (rows past d_h repeat the last)
+    // weight rows in batches of kOprojRows, batch b taken by wave b % 4, a wave's next batch in
+    // flight while one is used; its first is issued before the token selection (rows past d_h
+    // repeat the last; they meet zero slot values)
     constexpr int RB = kOprojRows;
+    const int nb = (dh + RB - 1) / RB;
     u32x4_t wv[2][RB];
     auto issue = [&](int buf, int j0) {
 #pragma unroll
@@ -598,7 +605,7 @@ __global__ void __launch_bounds__(64) dec_oproj_kernel(DecArgs a) {
             wv[buf][i] = load16(wp + (int64_t)j * d);
         }
     };
-    issue(0, 0);
+    if (w < nb) issue(0, w * RB);
     const int ntok = token_group(a, kind == 0 && !a.dense, e, g, kind == 0 ? e % a.n : 0, tg, list, wcount);
     if (ntok <= 0) return;
     constexpr int VW = 128 + kOprojRows;  // slot vector row (zero past d_h)
@@ -606,7 +613,7 @@ __global__ void __launch_bounds__(64) dec_oproj_kernel(DecArgs a) {
     // the slot vectors in float4 units (d_h is a multiple of 4), lane i taking units i, i + 64, ...;
     // every load of a lane is issued before the first is used (the renormalised slot: once per
     // choice rank), so the staging costs one memory round trip instead of one per element
-    constexpr int VU = VW / 4, NI = (kTok * VU + 63) / 64;
+    constexpr int VU = VW / 4, NI = (kTok * VU + 64 * NWV - 1) / (64 * NWV);
     const bool wc = !a.dense && a.variant == GQE_VARIANT_WEIGHTED_CONCAT;
     f32x4_t vv[NI];
     const float* orow[NI];  // the unit's source in the token's head outputs (null: zero)
@@ -614,7 +621,7 @@ __global__ void __launch_bounds__(64) dec_oproj_kernel(DecArgs a) {
     int rk[NI];
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
-        const int i = lane + 64 * n, t = i / VU, j = (i - t * VU) * 4;
+        const int i = tid + 64 * NWV * n, t = i / VU, j = (i - t * VU) * 4;
         vv[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         orow[n] = nullptr;
         selr[n] = 0;
@@ -659,11 +666,10 @@ __global__ void __launch_bounds__(64) dec_oproj_kernel(DecArgs a) {
     }
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
-        const int i = lane + 64 * n, t = i / VU, j = (i - t * VU) * 4;
+        const int i = tid + 64 * NWV * n, t = i / VU, j = (i - t * VU) * 4;
         if (t < kTok) *reinterpret_cast<f32x4_t*>(&vs[t][j]) = vv[n];  // zero past d_h and the tokens
     }
     __syncthreads();
-    if (!cact) return;
     float acc[kTok][E];
 #pragma unroll
     for (int t = 0; t < kTok; ++t)
@@ -682,27 +688,36 @@ __global__ void __launch_bounds__(64) dec_oproj_kernel(DecArgs a) {
             }
         }
     };
-    for (int j0 = 0; j0 < dh; j0 += 2 * RB) {
-        if (j0 + RB < dh) issue(1, j0 + RB);
-        use(wv[0], j0);
-        if (j0 + 2 * RB < dh) issue(0, j0 + 2 * RB);
-        if (j0 + RB < dh) use(wv[1], j0 + RB);
+    for (int b = w; b < nb; b += 2 * NWV) {
+        if (b + NWV < nb) issue(1, (b + NWV) * RB);
+        use(wv[0], b * RB);
+        if (b + 2 * NWV < nb) issue(0, (b + 2 * NWV) * RB);
+        if (b + NWV < nb) use(wv[1], (b + NWV) * RB);
     }
-    for (int t = 0; t < ntok; ++t) {
+    // partial sums through LDS; wave w then adds the four partials (in wave order) of tokens
+    // 2 w and 2 w + 1 and writes them
+#pragma unroll
+    for (int t = 0; t < kTok; ++t)
+#pragma unroll
+        for (int q = 0; q < E; q += 4)
+            *reinterpret_cast<f32x4_t*>(&red[w][t][lane * E + q]) =
+                f32x4_t{acc[t][q], acc[t][q + 1], acc[t][q + 2], acc[t][q + 3]};
+    __syncthreads();
+    static_assert(kTok == 2 * NWV, "two tokens per wave");
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int t = 2 * w + h;
+        if (t >= ntok || !cact) continue;
         const int tk = list[t];
         const int b = tk & 0xffffff, r = tk >> 24;
         const int ls = kind == 0 ? g * kr + r : (kind == 1 ? nr + g : nr + (rslot ? G : 0));
         float* dst = a.yp + ((int64_t)b * a.NS + ls) * d + cu * E;
 #pragma unroll
         for (int q = 0; q < E; q += 4) {
-            float acc4[4];
-            for (int z = 0; z < 4; ++z) {
-                acc4[z] = acc[0][q + z];
+            f32x4_t v = *reinterpret_cast<const f32x4_t*>(&red[0][t][lane * E + q]);
 #pragma unroll
-                for (int tt = 1; tt < kTok; ++tt)
-                    if (t == tt) acc4[z] = acc[tt][q + z];
-            }
-            *reinterpret_cast<f32x4_t*>(dst + q) = f32x4_t{acc4[0], acc4[1], acc4[2], acc4[3]};
+            for (int p = 1; p < NWV; ++p) v += *reinterpret_cast<const f32x4_t*>(&red[p][t][lane * E + q]);
+            *reinterpret_cast<f32x4_t*>(dst + q) = v;
         }
     }
 }
@@ -833,8 +848,8 @@ hipError_t launch_decode(const GqeDims& D, const DecodePlan& P, const gqe_weight
     const int E = bf ? 8 : 4;
     const unsigned nsm = (unsigned)(D.N + ((!D.dense && D.variant == GQE_VARIANT_GQE) ? D.G : 0) + D.s);
     const dim3 go(nsm, tgroups, (unsigned)ceil_div(D.d / E, 64));
-    if (bf) dec_oproj_kernel<bf16_t><<<go, 64, 0, st>>>(a);
-    else dec_oproj_kernel<float><<<go, 64, 0, st>>>(a);
+    if (bf) dec_oproj_kernel<bf16_t><<<go, 256, 0, st>>>(a);
+    else dec_oproj_kernel<float><<<go, 256, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 gy((unsigned)ceil_div(D.d / 4, 256), (unsigned)P.B);
     if (bf) dec_ysum_kernel<bf16_t><<<gy, 256, 0, st>>>(a);
