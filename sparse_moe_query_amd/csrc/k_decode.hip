@@ -22,9 +22,11 @@
 //                      heads of the group, then chunk maximum, exp2, row sums and P.V; writes a
 //                      float32 partial result (O, maximum, row sum) per head
 //   dec_merge_kernel   one wave per (token, head): online-softmax merge of the chunk partials
-//   dec_combine_kernel work group = (token, 256 output columns): the variant's output
-//                      construction (routed slots, renormalised slot, shared head) fused with the
-//                      output projection, weights in their "x @ W" layout
+//   dec_oproj_kernel   work group = (weight slot, up to 8 tokens that use it, 512 output columns):
+//                      the variant's output construction (routed slots, renormalised slot, shared
+//                      head) fused with the output projection, weights in their "x @ W" layout;
+//                      a float32 partial row per (token, slot)
+//   dec_ysum_kernel    a token's slot rows added in slot order
 //
 // A sequence whose position is outside [0, s_max) is not processed: nothing is written to the
 // cache, and its output row is NaN.
