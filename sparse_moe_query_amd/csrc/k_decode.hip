@@ -528,25 +528,30 @@ __global__ void __launch_bounds__(64) dec_merge_kernel(DecArgs a) {
     const int nch = (int)(((int64_t)p + a.C) / a.C);
     const int64_t cs = (int64_t)a.MH * (dh + 2);
     const float* base = a.part + (((int64_t)b * a.G + g) * a.NC * a.MH + h) * (dh + 2);
-    float M = -INFINITY;
-    for (int c = lane; c < nch; c += 64) M = fmaxf(M, base[c * cs + dh]);
+    // the lane's first chunk's (m, l), loaded together and kept: with at most 64 chunks (every
+    // cache up to 64 C positions) nothing is read twice
+    const float m0 = lane < nch ? base[lane * cs + dh] : -INFINITY;
+    const float l0 = lane < nch ? base[lane * cs + dh + 1] : 0.f;
+    float M = m0;
+    for (int c = lane + 64; c < nch; c += 64) M = fmaxf(M, base[c * cs + dh]);
     M = wave_max(M);
-    float l = 0.f;
-    for (int c = lane; c < nch; c += 64) l += base[c * cs + dh + 1] * __builtin_amdgcn_exp2f(base[c * cs + dh] - M);
+    const float e0 = lane < nch ? __builtin_amdgcn_exp2f(m0 - M) : 0.f;
+    float l = l0 * e0;
+    for (int c = lane + 64; c < nch; c += 64) l += base[c * cs + dh + 1] * __builtin_amdgcn_exp2f(base[c * cs + dh] - M);
     const float inv = 1.f / wave_sum(l);
     float o0 = 0.f, o1 = 0.f;
     for (int cb = 0; cb < nch; cb += 64) {
         const int c = cb + lane;
-        scl[lane] = c < nch ? __builtin_amdgcn_exp2f(base[c * cs + dh] - M) * inv : 0.f;
+        scl[lane] = cb == 0 ? e0 * inv : (c < nch ? __builtin_amdgcn_exp2f(base[c * cs + dh] - M) * inv : 0.f);
         __syncthreads();
         const int n = nch - cb < 64 ? nch - cb : 64;
         const float* pc = base + cb * cs;
         if (lane < dh) {
-#pragma unroll 8
+#pragma unroll 16
             for (int i = 0; i < n; ++i) o0 += pc[i * cs + lane] * scl[i];
         }
         if (lane + 64 < dh) {
-#pragma unroll 8
+#pragma unroll 16
             for (int i = 0; i < n; ++i) o1 += pc[i * cs + lane + 64] * scl[i];
         }
         __syncthreads();
